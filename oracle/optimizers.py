@@ -1,0 +1,347 @@
+"""Plain fp64 NumPy oracle for one optimizer step of Adafactor, CAME and LAMB.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the
+bench's CPU-baseline leg may import this module; the library never does, and it
+shares no code, constant table or helper with the HIP path.
+
+Everything is done in float64 with whole-array NumPy operations in the order the
+method states, and the second-moment estimate of the factored path is
+*materialised* as a full array (the HIP path never builds it). States are plain
+dicts of float64 arrays named as on the Colossal-AI distributed-optimizers page
+("Colossal-AI 分布式优化器全解析", blog.gitcode.com; section "Step 3"):
+``exp_avg``, ``exp_avg_sq_row``, ``exp_avg_sq_col``, ``exp_avg_sq``. CAME's
+confidence statistics, which the page describes but does not name, are
+``exp_avg_res_row`` / ``exp_avg_res_col``; LAMB's moments are ``exp_avg`` /
+``exp_avg_sq``.
+
+Functions take and return new arrays; nothing is modified in place. ``t`` is the
+1-based index of the step being taken (the counter is incremented before use).
+
+Sources (the pages), by function:
+
+* Adafactor: the page's section "Step 3" (defaults, relative step size and its
+  ValueError texts, optional first moment, factored-vs-full rule with the row
+  and column statistic shapes), the note after "Step 5" (beta2t = 1 - step **
+  decay_rate, RMS clipping by clip_threshold, scale_parameter), and the "four
+  optimizers" table (second moment approximated by row * col).
+* CAME: the "four optimizers" table (confidence matrix on top of Adafactor's
+  factorisation, three betas) and the "DistributedCAME" paragraph of the "other
+  optimizers' key parameters" section (defaults). The step order follows the CAME
+  paper the page cites (arXiv:2307.02047).
+* LAMB: the "four optimizers" table (layer-wise trust ratio) and the
+  "DistributedLAMB" paragraph (defaults, validation). The step follows the LAMB
+  paper the page cites (arXiv:1904.00962).
+
+Readings where the pages are silent are listed, with reasons, in the design notes
+of this repository; each is marked "reading" at the line that applies it.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+Array = np.ndarray
+State = Dict[str, Array]
+
+# ----------------------------------------------------------------------------- defaults
+
+# Page "Step 3": the distributed Adafactor's defaults, aligned with Hugging Face's.
+ADAFACTOR_DEFAULTS = dict(lr=None, eps=(1e-30, 1e-3), clip_threshold=1.0, decay_rate=-0.8,
+                          beta1=None, weight_decay=0.0, scale_parameter=True,
+                          relative_step=True, warmup_init=False)
+# Page "DistributedCAME" paragraph.
+CAME_DEFAULTS = dict(lr=None, eps=(1e-30, 1e-16), clip_threshold=1.0,
+                     betas=(0.9, 0.999, 0.9999), weight_decay=0.0)
+# Page "DistributedLAMB" paragraph.
+LAMB_DEFAULTS = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-6, weight_decay=0.0,
+                     bias_correction=True)
+
+# Error texts printed on the page ("Step 3").
+MSG_LR_WITH_RELATIVE = "Cannot combine manual lr and relative_step=True options"
+MSG_WARMUP_NEEDS_RELATIVE = "warmup_init=True requires relative_step=True"
+
+
+def _hp(defaults: dict, hp: Optional[dict]) -> dict:
+    out = dict(defaults)
+    if hp:
+        unknown = set(hp) - set(defaults)
+        if unknown:
+            raise TypeError(f"unknown hyperparameters: {sorted(unknown)}")
+        out.update(hp)
+    return out
+
+
+def rms(a: Array) -> float:
+    """Root mean square over every element of the tensor (population RMS)."""
+    a = np.asarray(a, dtype=np.float64)
+    if a.size == 0:
+        return 0.0
+    return math.sqrt(float(np.mean(a * a)))
+
+
+def is_factored(shape: Tuple[int, ...]) -> bool:
+    """Page "Step 3": factored = len(param_shape) >= 2."""
+    return len(shape) >= 2
+
+
+# ----------------------------------------------------------------------------- Adafactor
+
+def adafactor_hparams(hp: Optional[dict] = None) -> dict:
+    """Defaults merged with ``hp`` and validated as the page states ("Step 3")."""
+    h = _hp(ADAFACTOR_DEFAULTS, hp)
+    if h["lr"] is not None and h["relative_step"]:
+        raise ValueError(MSG_LR_WITH_RELATIVE)
+    if h["warmup_init"] and not h["relative_step"]:
+        raise ValueError(MSG_WARMUP_NEEDS_RELATIVE)
+    if h["lr"] is None and not h["relative_step"]:
+        # reading: without a relative step there is no learning rate at all.
+        raise ValueError("lr is required when relative_step=False")
+    return h
+
+
+def adafactor_step_size(h: dict, t: int) -> float:
+    """rho_t. Page "Step 3": with relative_step the rate is min(1e-2, 1/sqrt(step)),
+    and warmup_init replaces the 1e-2 by 1e-6 * step (reading: the linear ramp sits
+    inside the same min). Without relative_step it is the given lr."""
+    if h["relative_step"]:
+        cap = 1e-6 * t if h["warmup_init"] else 1e-2
+        return min(cap, 1.0 / math.sqrt(t))
+    return float(h["lr"])
+
+
+def adafactor_beta2t(h: dict, t: int) -> float:
+    """Note after "Step 5": beta2t = 1 - step ** decay_rate."""
+    return 1.0 - math.pow(t, h["decay_rate"])
+
+
+def adafactor_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None) -> State:
+    """Zero state with the shapes of page "Step 3": row statistic over shape[:-1],
+    column statistic over shape[:-2] + shape[-1:], full statistic for 1-D, and
+    ``exp_avg`` only when beta1 is set."""
+    h = adafactor_hparams(hp)
+    shape = tuple(shape)
+    st: State = {}
+    if h["beta1"] is not None:
+        st["exp_avg"] = np.zeros(shape)
+    if is_factored(shape):
+        st["exp_avg_sq_row"] = np.zeros(shape[:-1])
+        st["exp_avg_sq_col"] = np.zeros(shape[:-2] + shape[-1:])
+    else:
+        st["exp_avg_sq"] = np.zeros(shape)
+    return st
+
+
+def adafactor_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int
+                          ) -> Tuple[Array, State]:
+    """One Adafactor step of one tensor; returns (new parameter, new state)."""
+    h = adafactor_hparams(hp)
+    if t < 1:
+        raise ValueError("step must be >= 1")
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    eps1, eps2 = h["eps"]
+
+    # Learning rate: relative step, scaled by the parameter's RMS before this
+    # step's update (reading: the RMS is taken when the rate is computed).
+    alpha = adafactor_step_size(h, t)
+    if h["scale_parameter"]:
+        alpha *= max(eps2, rms(x))
+
+    b2 = adafactor_beta2t(h, t)
+    q = g * g + eps1  # reading: eps1 enters with the squared gradient
+    new = {}
+    if is_factored(x.shape):
+        row = b2 * state["exp_avg_sq_row"] + (1.0 - b2) * q.mean(axis=-1)
+        col = b2 * state["exp_avg_sq_col"] + (1.0 - b2) * q.mean(axis=-2)
+        new["exp_avg_sq_row"], new["exp_avg_sq_col"] = row, col
+        # "row * col" estimate, normalised by the row statistic's mean over each
+        # matrix (the leading dims are independent matrices), materialised in full.
+        v_hat = row[..., :, None] * col[..., None, :] / row.mean(axis=-1)[..., None, None]
+    else:
+        v = b2 * state["exp_avg_sq"] + (1.0 - b2) * q
+        new["exp_avg_sq"] = v
+        v_hat = v
+    u = g / np.sqrt(v_hat)
+    # RMS clipping (note after "Step 5"): divide by max(1, RMS(u) / clip_threshold).
+    u = u / max(1.0, rms(u) / h["clip_threshold"])
+    u = alpha * u
+    if h["beta1"] is not None:
+        # reading: the first moment averages the clipped, lr-scaled update.
+        m = h["beta1"] * state["exp_avg"] + (1.0 - h["beta1"]) * u
+        new["exp_avg"] = m
+        delta = m
+    else:
+        delta = u
+    # reading: decoupled weight decay on the pre-update parameter, scaled by alpha.
+    x_new = x - h["weight_decay"] * alpha * x - delta
+    return x_new, new
+
+
+def adafactor_step(xs: Sequence[Array], gs: Sequence[Array], states: Sequence[State],
+                   hp: Optional[dict], t: int) -> Tuple[List[Array], List[State]]:
+    """A step over a list: every statistic is per tensor, so each is independent."""
+    out_x, out_s = [], []
+    for x, g, st in zip(xs, gs, states):
+        a, b = adafactor_step_tensor(x, g, st, hp, t)
+        out_x.append(a)
+        out_s.append(b)
+    return out_x, out_s
+
+
+# ----------------------------------------------------------------------------- CAME
+
+def came_hparams(hp: Optional[dict] = None) -> dict:
+    h = _hp(CAME_DEFAULTS, hp)
+    if h["lr"] is None:
+        # reading: CAME has no relative step, so the lr must be supplied.
+        raise ValueError("CAME requires an explicit lr")
+    if h["lr"] < 0:
+        raise ValueError(f"Invalid learning rate: {h['lr']}")
+    for i, b in enumerate(h["betas"]):
+        if not 0.0 <= b < 1.0:
+            raise ValueError(f"Invalid beta parameter at index {i}: {b}")
+    return h
+
+
+def came_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None) -> State:
+    """Zero state: first moment, factored (or full) squared-gradient statistic and,
+    for factored tensors, the factored confidence statistic."""
+    shape = tuple(shape)
+    st: State = {"exp_avg": np.zeros(shape)}
+    if is_factored(shape):
+        st["exp_avg_sq_row"] = np.zeros(shape[:-1])
+        st["exp_avg_sq_col"] = np.zeros(shape[:-2] + shape[-1:])
+        st["exp_avg_res_row"] = np.zeros(shape[:-1])
+        st["exp_avg_res_col"] = np.zeros(shape[:-2] + shape[-1:])
+    else:
+        st["exp_avg_sq"] = np.zeros(shape)
+    return st
+
+
+def _factored_estimate(row: Array, col: Array) -> Array:
+    """row_i * col_j / mean_i(row_i) per matrix, materialised."""
+    return row[..., :, None] * col[..., None, :] / row.mean(axis=-1)[..., None, None]
+
+
+def came_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int
+                     ) -> Tuple[Array, State]:
+    """One CAME step of one tensor; returns (new parameter, new state)."""
+    h = came_hparams(hp)
+    if t < 1:
+        raise ValueError("step must be >= 1")
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    eps1, eps2 = h["eps"]
+    beta1, beta2, beta3 = h["betas"]
+    lr = float(h["lr"])
+    new = {}
+
+    # Squared-gradient statistic: Adafactor's factorisation with a constant beta2
+    # (reading: no decay schedule and no bias correction).
+    q = g * g + eps1
+    fac = is_factored(x.shape)
+    if fac:
+        row = beta2 * state["exp_avg_sq_row"] + (1.0 - beta2) * q.mean(axis=-1)
+        col = beta2 * state["exp_avg_sq_col"] + (1.0 - beta2) * q.mean(axis=-2)
+        new["exp_avg_sq_row"], new["exp_avg_sq_col"] = row, col
+        v_hat = _factored_estimate(row, col)
+    else:
+        v = beta2 * state["exp_avg_sq"] + (1.0 - beta2) * q
+        new["exp_avg_sq"] = v
+        v_hat = v
+    u = g / np.sqrt(v_hat)
+    u = u / max(1.0, rms(u) / h["clip_threshold"])
+
+    m = beta1 * state["exp_avg"] + (1.0 - beta1) * u
+    new["exp_avg"] = m
+
+    if fac:
+        # Instability of the update against its running mean, factored the same
+        # way; its reconstruction is the confidence that scales the step.
+        e = (u - m) ** 2 + eps2
+        rrow = beta3 * state["exp_avg_res_row"] + (1.0 - beta3) * e.mean(axis=-1)
+        rcol = beta3 * state["exp_avg_res_col"] + (1.0 - beta3) * e.mean(axis=-2)
+        new["exp_avg_res_row"], new["exp_avg_res_col"] = rrow, rcol
+        s = _factored_estimate(rrow, rcol)
+        delta = m / np.sqrt(s)
+    else:
+        # reading: a full 1-D statistic carries no factorisation error to correct.
+        delta = m
+    x_new = x - lr * h["weight_decay"] * x - lr * delta
+    return x_new, new
+
+
+def came_step(xs, gs, states, hp, t):
+    out_x, out_s = [], []
+    for x, g, st in zip(xs, gs, states):
+        a, b = came_step_tensor(x, g, st, hp, t)
+        out_x.append(a)
+        out_s.append(b)
+    return out_x, out_s
+
+
+# ----------------------------------------------------------------------------- LAMB
+
+def lamb_hparams(hp: Optional[dict] = None) -> dict:
+    """Defaults merged with ``hp``; the page says the constructor validates lr, eps
+    and betas (reading: lr >= 0, eps >= 0, 0 <= beta < 1)."""
+    h = _hp(LAMB_DEFAULTS, hp)
+    if not h["lr"] >= 0.0:
+        raise ValueError(f"Invalid learning rate: {h['lr']}")
+    if not h["eps"] >= 0.0:
+        raise ValueError(f"Invalid epsilon value: {h['eps']}")
+    for i, b in enumerate(h["betas"]):
+        if not 0.0 <= b < 1.0:
+            raise ValueError(f"Invalid beta parameter at index {i}: {b}")
+    return h
+
+
+def lamb_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None) -> State:
+    shape = tuple(shape)
+    return {"exp_avg": np.zeros(shape), "exp_avg_sq": np.zeros(shape)}
+
+
+def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int
+                     ) -> Tuple[Array, State]:
+    """One LAMB step of one tensor (the whole tensor is one layer for the trust ratio)."""
+    h = lamb_hparams(hp)
+    if t < 1:
+        raise ValueError("step must be >= 1")
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    beta1, beta2 = h["betas"]
+    m = beta1 * state["exp_avg"] + (1.0 - beta1) * g
+    v = beta2 * state["exp_avg_sq"] + (1.0 - beta2) * g * g
+    if h["bias_correction"]:
+        m_hat = m / (1.0 - beta1 ** t)
+        v_hat = v / (1.0 - beta2 ** t)
+    else:
+        m_hat, v_hat = m, v
+    # reading: eps outside the square root; decay added to the Adam direction.
+    d = m_hat / (np.sqrt(v_hat) + h["eps"]) + h["weight_decay"] * x
+    x_norm = float(np.sqrt(np.sum(x * x)))
+    d_norm = float(np.sqrt(np.sum(d * d)))
+    # reading: identity scaling of the parameter norm; ratio 1 when either norm is 0.
+    trust = x_norm / d_norm if (x_norm > 0.0 and d_norm > 0.0) else 1.0
+    x_new = x - h["lr"] * trust * d
+    return x_new, {"exp_avg": m, "exp_avg_sq": v}
+
+
+def lamb_step(xs, gs, states, hp, t):
+    out_x, out_s = [], []
+    for x, g, st in zip(xs, gs, states):
+        a, b = lamb_step_tensor(x, g, st, hp, t)
+        out_x.append(a)
+        out_s.append(b)
+    return out_x, out_s
+
+
+# ----------------------------------------------------------------------------- dispatch
+
+STEP = {"adafactor": adafactor_step, "came": came_step, "lamb": lamb_step}
+STEP_TENSOR = {"adafactor": adafactor_step_tensor, "came": came_step_tensor,
+               "lamb": lamb_step_tensor}
+INIT_STATE = {"adafactor": adafactor_init_state, "came": came_init_state,
+              "lamb": lamb_init_state}

@@ -1,0 +1,237 @@
+"""Seeded synthetic workloads for the optimizer step.
+
+This module holds shapes, initial parameter values and gradient draws only: no
+optimizer arithmetic. Both the fp64 oracle (through the tests and the bench's CPU
+leg) and the HIP library are fed from here, so a parity check always compares the
+two on the same bits.
+
+Shapes are model architectures (a Llama-7B decoder stack and BERT-large), not data
+items: the optimizer step sees only parameter and gradient tensors, so synthetic
+gradients with the statistics described below stand in for real training
+gradients.
+
+Random streams. Every tensor k of a workload draws from its own torch generator
+seeded with ``seed * 2**20 + k * 2**8 + stream``; stream 0 is the initial value,
+stream 1 the fixed per-tensor gradient scales, stream 2 + s the N(0, 1) noise of
+step s (0-based). A generator lives on the device the tensors are made on, so the
+CPU and a GPU draw different (but each reproducible) values; parity tests copy
+the GPU's draws to the host for the oracle.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class TensorSpec:
+    name: str
+    shape: Tuple[int, ...]
+    kind: str  # "weight" (N(0, 0.02) init), "norm" (ones), "bias" (zeros)
+
+    @property
+    def numel(self) -> int:
+        return math.prod(self.shape)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    optimizer: str  # "adafactor" | "came" | "lamb"
+    hparams: Dict[str, object]
+    specs: Tuple[TensorSpec, ...]
+    grad_dtype: torch.dtype
+    grad_std: float
+    grad_scaling: str  # "row": per-row scale; "rowcol": row x col scales; "none"
+    steps: int
+    seed: int = 0
+
+    @property
+    def numel(self) -> int:
+        return sum(s.numel for s in self.specs)
+
+
+# ----------------------------------------------------------------------------- shapes
+
+def llama_layer_specs(prefix: str = "", hidden: int = 4096, ffn: int = 11008) -> List[TensorSpec]:
+    """One Llama decoder layer in parameter order: attention q, k, v, o, MLP gate,
+    up, down, then the two RMSNorm weights."""
+    h, f = hidden, ffn
+    return [
+        TensorSpec(prefix + "self_attn.q_proj.weight", (h, h), "weight"),
+        TensorSpec(prefix + "self_attn.k_proj.weight", (h, h), "weight"),
+        TensorSpec(prefix + "self_attn.v_proj.weight", (h, h), "weight"),
+        TensorSpec(prefix + "self_attn.o_proj.weight", (h, h), "weight"),
+        TensorSpec(prefix + "mlp.gate_proj.weight", (f, h), "weight"),
+        TensorSpec(prefix + "mlp.up_proj.weight", (f, h), "weight"),
+        TensorSpec(prefix + "mlp.down_proj.weight", (h, f), "weight"),
+        TensorSpec(prefix + "input_layernorm.weight", (h,), "norm"),
+        TensorSpec(prefix + "post_attention_layernorm.weight", (h,), "norm"),
+    ]
+
+
+def llama_specs(layers: int = 32, hidden: int = 4096, ffn: int = 11008, vocab: int = 32000) -> List[TensorSpec]:
+    """A Llama causal LM in parameter order: embedding, decoder layers, final norm, lm_head."""
+    out = [TensorSpec("model.embed_tokens.weight", (vocab, hidden), "weight")]
+    for i in range(layers):
+        out += llama_layer_specs(f"model.layers.{i}.", hidden, ffn)
+    out.append(TensorSpec("model.norm.weight", (hidden,), "norm"))
+    out.append(TensorSpec("lm_head.weight", (vocab, hidden), "weight"))
+    return out
+
+
+def bert_specs(layers: int = 24, hidden: int = 1024, ffn: int = 4096, vocab: int = 30522,
+               max_pos: int = 512) -> List[TensorSpec]:
+    """A BERT encoder in parameter order: word and position embeddings and their
+    LayerNorm, then per layer q, k, v, o (+ biases), FFN in/out (+ biases) and two
+    LayerNorms (weight and bias each)."""
+    h, f = hidden, ffn
+    out = [
+        TensorSpec("embeddings.word_embeddings.weight", (vocab, h), "weight"),
+        TensorSpec("embeddings.position_embeddings.weight", (max_pos, h), "weight"),
+        TensorSpec("embeddings.LayerNorm.weight", (h,), "norm"),
+        TensorSpec("embeddings.LayerNorm.bias", (h,), "bias"),
+    ]
+    for i in range(layers):
+        p = f"encoder.layer.{i}."
+        for n in ("attention.self.query", "attention.self.key", "attention.self.value",
+                  "attention.output.dense"):
+            out.append(TensorSpec(p + n + ".weight", (h, h), "weight"))
+            out.append(TensorSpec(p + n + ".bias", (h,), "bias"))
+        out.append(TensorSpec(p + "attention.output.LayerNorm.weight", (h,), "norm"))
+        out.append(TensorSpec(p + "attention.output.LayerNorm.bias", (h,), "bias"))
+        out.append(TensorSpec(p + "intermediate.dense.weight", (f, h), "weight"))
+        out.append(TensorSpec(p + "intermediate.dense.bias", (f,), "bias"))
+        out.append(TensorSpec(p + "output.dense.weight", (h, f), "weight"))
+        out.append(TensorSpec(p + "output.dense.bias", (h,), "bias"))
+        out.append(TensorSpec(p + "output.LayerNorm.weight", (h,), "norm"))
+        out.append(TensorSpec(p + "output.LayerNorm.bias", (h,), "bias"))
+    return out
+
+
+# ----------------------------------------------------------------------------- workloads
+
+_AF_DEFAULT: Dict[str, object] = {}
+_AF_BETA1 = {"beta1": 0.9}
+_CAME = {"lr": 2e-4, "betas": (0.9, 0.999, 0.9999), "eps": (1e-30, 1e-16),
+         "clip_threshold": 1.0, "weight_decay": 0.0}
+_LAMB = {"lr": 1e-3, "betas": (0.9, 0.999), "eps": 1e-6, "weight_decay": 0.01,
+         "bias_correction": True}
+
+
+def _wl(name, opt, hp, specs, gdt, gstd, scaling, steps):
+    return Workload(name, opt, dict(hp), tuple(specs), gdt, gstd, scaling, steps)
+
+
+WORKLOADS: Dict[str, Workload] = {}
+
+
+def _register(w: Workload) -> None:
+    WORKLOADS[w.name] = w
+
+
+# The five measured configurations.
+_register(_wl("adafactor_small", "adafactor", _AF_DEFAULT,
+              [TensorSpec("weight", (256, 512), "weight"), TensorSpec("bias", (512,), "bias")],
+              torch.float32, 1.0, "row", 10))
+_register(_wl("adafactor_llama_layer", "adafactor", _AF_BETA1, llama_layer_specs(),
+              torch.bfloat16, 1e-3, "rowcol", 20))
+_register(_wl("adafactor_llama7b", "adafactor", _AF_BETA1, llama_specs(),
+              torch.bfloat16, 1e-3, "rowcol", 5))
+_register(_wl("came_llama_layer", "came", _CAME, llama_layer_specs(),
+              torch.bfloat16, 1e-3, "rowcol", 20))
+_register(_wl("lamb_bert_large", "lamb", _LAMB, bert_specs(),
+              torch.float32, 1e-2, "none", 20))
+
+# Scaled-down versions of the same structure (ragged widths included) that the
+# oracle runs element by element in seconds.
+_register(_wl("adafactor_llama_mini", "adafactor", _AF_BETA1,
+              llama_specs(layers=2, hidden=256, ffn=688, vocab=1000),
+              torch.bfloat16, 1e-3, "rowcol", 10))
+_register(_wl("came_llama_mini", "came", _CAME,
+              llama_specs(layers=2, hidden=256, ffn=688, vocab=1000),
+              torch.bfloat16, 1e-3, "rowcol", 10))
+_register(_wl("lamb_bert_mini", "lamb", _LAMB,
+              bert_specs(layers=2, hidden=128, ffn=512, vocab=3001, max_pos=64),
+              torch.float32, 1e-2, "none", 10))
+
+
+def custom(name: str, optimizer: str, shapes: Sequence[Tuple[int, ...]], *, hparams=None,
+           grad_dtype=torch.float32, grad_std=1.0, grad_scaling="row", steps=3,
+           kinds: Optional[Sequence[str]] = None, seed: int = 0) -> Workload:
+    """An ad-hoc workload over the given shapes (edge cases in tests)."""
+    specs = []
+    for i, shp in enumerate(shapes):
+        kind = kinds[i] if kinds else ("weight" if len(shp) >= 2 else "norm")
+        specs.append(TensorSpec(f"t{i}", tuple(int(s) for s in shp), kind))
+    return Workload(name, optimizer, dict(hparams or {}), tuple(specs), grad_dtype, grad_std,
+                    grad_scaling, steps, seed)
+
+
+# ----------------------------------------------------------------------------- draws
+
+def _gen(wl: Workload, k: int, stream: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed * (1 << 20) + k * (1 << 8) + stream)
+    return g
+
+
+def init_params(wl: Workload, device="cpu") -> List[torch.Tensor]:
+    """fp32 parameters: 2-D+ weights N(0, 0.02) (std 0.02), norm weights 1, biases 0."""
+    out = []
+    for k, s in enumerate(wl.specs):
+        if s.kind == "weight":
+            t = torch.empty(s.shape, dtype=torch.float32, device=device)
+            t.normal_(0.0, 0.02, generator=_gen(wl, k, 0, device))
+        elif s.kind == "norm":
+            t = torch.ones(s.shape, dtype=torch.float32, device=device)
+        else:
+            t = torch.zeros(s.shape, dtype=torch.float32, device=device)
+        out.append(t)
+    return out
+
+
+def _log_uniform(n: int, gen: torch.Generator, device) -> torch.Tensor:
+    u = torch.empty(n, dtype=torch.float32, device=device).uniform_(-2.0, 2.0, generator=gen)
+    return torch.pow(10.0, u)
+
+
+def grad_scales(wl: Workload, device="cpu") -> List[Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]]:
+    """Per-tensor fixed scales, drawn once: 10**U(-2, 2) over rows (dim -2) and,
+    for "rowcol", over columns (dim -1). 1-D tensors get one scale per element."""
+    out = []
+    for k, s in enumerate(wl.specs):
+        if wl.grad_scaling == "none":
+            out.append((None, None))
+            continue
+        gen = _gen(wl, k, 1, device)
+        if len(s.shape) < 2:
+            out.append((_log_uniform(max(s.numel, 1), gen, device).reshape(s.shape), None))
+            continue
+        a = _log_uniform(s.shape[-2], gen, device)
+        b = _log_uniform(s.shape[-1], gen, device) if wl.grad_scaling == "rowcol" else None
+        out.append((a, b))
+    return out
+
+
+def grads(wl: Workload, step_index: int, scales, device="cpu") -> List[torch.Tensor]:
+    """Gradients of 0-based step ``step_index``: std * z * row_scale * col_scale,
+    z ~ N(0, 1) redrawn each step, computed in fp32 then cast to the grad dtype."""
+    out = []
+    for k, s in enumerate(wl.specs):
+        z = torch.empty(s.shape, dtype=torch.float32, device=device)
+        z.normal_(0.0, 1.0, generator=_gen(wl, k, 2 + step_index, device))
+        g = z * wl.grad_std
+        a, b = scales[k]
+        if a is not None:
+            if len(s.shape) < 2:
+                g = g * a
+            else:
+                g = g * a.unsqueeze(-1)
+                if b is not None:
+                    g = g * b
+        out.append(g.to(wl.grad_dtype).contiguous())
+    return out
