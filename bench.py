@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Optimizer-step benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one library call over the whole tensor list of the workload (default:
+Adafactor with beta1 = 0.9 over a Llama-7B-shaped list, 291 tensors, 6.74e9 fp32
+parameters, bf16 gradients), with parameters, states, gradients and workspace
+resident in HBM before timing. W untimed steps, then exactly K steps between two
+hipEvents on the stream (synchronised on both sides). One JSON line on stdout:
+
+* ``value``: optimizer-step throughput in parameters per second (whole job).
+* ``hbm``: the step's compulsory bytes (read G once, read and write the parameter
+  and every full-size state once) over the step time, against 8 TB/s.
+* ``roofline``: the dominant pass (the apply pass for Adafactor), its algorithmic
+  bytes per launch over its average duration, timed with hipEvents that the
+  library records between its passes on the same stream during the timed steps.
+* ``cpu_baseline``: the fp64 oracle (single-threaded NumPy) on a bounded sample of
+  the same workload, one step, in parameters per second.
+
+With more than one GPU requested it exits: the step has no cross-GPU work to
+measure here (see the design notes on sharding).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def _bytes_per_param(wl, spec, numel) -> dict:
+    """Algorithmic bytes of one tensor: whole step, and per pass."""
+    gb = 2 if str(wl.grad_dtype).endswith("bfloat16") else 4
+    fac = len(spec.shape) >= 2 and wl.optimizer != "lamb"
+    n = numel
+    if fac:
+        lead = math.prod(spec.shape[:-2]) if len(spec.shape) > 2 else 1
+        rc = lead * (spec.shape[-2] + spec.shape[-1])
+    else:
+        rc = 0
+    if wl.optimizer == "adafactor":
+        mom = wl.hparams.get("beta1") is not None
+        step = n * (gb + 8 + (8 if mom else 0) + (0 if fac else 8)) + 8 * rc
+        apply = n * (gb + 8 + (8 if mom else 0) + (0 if fac else 4)) + 4 * rc
+        return {"step": step, "adafactor_apply": apply}
+    if wl.optimizer == "came":
+        step = n * (gb + 8 + 8 + (0 if fac else 8)) + 16 * rc
+        mom = n * (gb + 8 + (0 if fac else 12)) + 4 * rc   # G, M rw (1-D: also V read, X rw)
+        app = (n * 12 + 4 * rc) if fac else 0               # M read, X rw
+        return {"step": step, "came_mom": mom, "came_apply": app}
+    step = n * (gb + 8 + 8 + 8)
+    return {"step": step, "lamb_moments": n * (gb + 4 + 16), "lamb_apply": n * 16}
+
+
+def algorithmic_bytes(wl) -> dict:
+    tot: dict = {}
+    for s in wl.specs:
+        for k, v in _bytes_per_param(wl, s, s.numel).items():
+            tot[k] = tot.get(k, 0) + v
+    return tot
+
+
+def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
+    """One oracle step over a bounded sample of the workload's tensors, on the host."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+
+    # Sample: the workload's tensors in list order, stopping near ~120M parameters
+    # (about 10-30 s of single-threaded fp64 NumPy), at least one tensor.
+    idx, tot = [], 0
+    for k, s in enumerate(wl.specs):
+        if idx and tot + s.numel > 120_000_000:
+            break
+        idx.append(k)
+        tot += s.numel
+    xs = [p.double().numpy() for p in workloads.init_params(wl, "cpu", idx)]
+    sc = workloads.grad_scales(wl, "cpu", idx)
+    gs = [g.to(torch.float64).numpy() for g in workloads.grads(wl, 0, sc, "cpu", idx)]
+    hp = dict(wl.hparams)
+    st = [oracle.INIT_STATE[wl.optimizer](x.shape, hp) for x in xs]
+    t0 = time.perf_counter()
+    done = 0
+    for k in range(len(xs)):
+        oracle.STEP_TENSOR[wl.optimizer](xs[k], gs[k], st[k], hp, 1)
+        done += xs[k].size
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    names = [wl.specs[idx[k]].name for k in range(len(xs))]
+    return {"value": done / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"one fp64 step over {done} parameters of the same workload "
+                      f"({len(names)} tensors from '{names[0]}' on, freshly allocated), "
+                      f"{dt:.1f} s, single-threaded NumPy"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="adafactor_llama7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with the dominant pass's rocprofv3 FETCH_SIZE/WRITE_SIZE (KiB per "
+                         "dispatch) and the copy-kernel scale factor")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the optimizer step on one GPU; the step exchanges nothing between "
+              "GPUs (each data-parallel rank runs the same step on its own copy), so there is no "
+              "multi-GPU figure to take here. Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    from memory_efficient_optimizers_amd import _lib
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    _lib.load()
+    wl = workloads.WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+
+    params = workloads.init_params(wl, dev)
+    scales = workloads.grad_scales(wl, dev)
+    grads = workloads.grads(wl, 0, scales, dev)
+    del scales
+    hp = dict(wl.hparams)
+    beta1 = hp.get("beta1") is not None
+    states = [_lib.init_state(wl.optimizer, p, beta1=beta1) for p in params]
+    hps = {"adafactor": _lib.adafactor_hparams, "came": _lib.came_hparams,
+           "lamb": _lib.lamb_hparams}[wl.optimizer](**hp)
+    wsize = getattr(_lib, f"meo_{wl.optimizer}_workspace_size")(params, grads)
+    ws = _lib.workspace(wsize, dev)
+    call = _lib.PreparedStep(wl.optimizer, hps, params, grads, states, ws)
+    stream = torch.cuda.current_stream()
+    numel = wl.numel
+
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        call(t, stream)
+    torch.cuda.synchronize()
+
+    _lib.meo_profile_enable(True)
+    _lib.meo_profile_collect()  # drop anything recorded before
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        t += 1
+        call(t, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    _lib.meo_profile_enable(False)
+    passes = _lib.meo_profile_collect()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_step = total_ms / args.steps
+    value = numel / (ms_step / 1e3)
+
+    ab = algorithmic_bytes(wl)
+    step_gbps = ab["step"] / (ms_step / 1e3) / 1e9
+    dominant = max((k for k in passes if k in ab), key=lambda k: passes[k]["ms"])
+    avg_ms = passes[dominant]["ms"] / passes[dominant]["launches"]
+    achieved = ab[dominant] / (avg_ms / 1e3) / 1e9
+    traffic = None
+    if args.traffic:
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("kernel") == dominant:
+            traffic = tr.get("bytes_per_launch")
+
+    out = {
+        "metric": "optimizer-step params/s + achieved HBM GB/s (% peak), 7B-shaped Adafactor",
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "optimizer": wl.optimizer, "tensors": len(wl.specs),
+                   "params": numel, "grad_dtype": str(wl.grad_dtype).replace("torch.", ""),
+                   "param_state_dtype": "float32",
+                   "hparams": {k: (list(v) if isinstance(v, tuple) else v) for k, v in hp.items()}},
+        "hbm": {"step_bytes": ab["step"], "achieved": step_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": step_gbps / HBM_PEAK_GBPS},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "bytes_per_launch": ab[dominant], "avg_ms": avg_ms},
+        "passes_ms_per_step": {k: v["ms"] / args.steps for k, v in passes.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

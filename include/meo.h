@@ -1,0 +1,246 @@
+/*
+ * meo.h -- C ABI of the fused optimizer-step library for AMD MI355X (gfx950).
+ *
+ * One call runs one optimizer step over a list of parameter tensors:
+ *
+ *   meo_adafactor_step  Adafactor with the factored second moment (row and column
+ *                       statistics for tensors of two or more dims, a full
+ *                       statistic for 1-D tensors), RMS clipping, relative step
+ *                       size, parameter scaling, weight decay and an optional
+ *                       first moment.
+ *   meo_came_step       CAME: Adafactor's factored statistic plus a factored
+ *                       confidence statistic of the update's instability.
+ *   meo_lamb_step       LAMB: Adam moments with a per-tensor trust ratio.
+ *
+ * Source of the method: the Colossal-AI distributed-optimizers page
+ * ("Colossal-AI 分布式优化器全解析", blog.gitcode.com): section "Step 3" (Adafactor
+ * defaults, relative step and its errors, optional first moment, the factored
+ * rule and the statistic shapes), the note after "Step 5" (beta2t schedule, RMS
+ * clipping, scale_parameter), the "four optimizers" table (row * col
+ * factorisation, CAME's confidence matrix, LAMB's layer-wise trust ratio), and
+ * the DistributedLAMB / DistributedCAME paragraphs (defaults, validation).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor, state and workspace pointers are DEVICE pointers owned by the
+ *   caller. Parameters and states are float32 and updated in place; gradients
+ *   are read only. Every buffer is contiguous and row-major (last dim
+ *   innermost). Buffers must not alias one another. fp32 buffers need 4-byte
+ *   alignment and bf16 ones 2-byte alignment; 16-byte alignment (and, for
+ *   factored tensors, cols % 8 == 0) selects the vectorised path.
+ * - `stream` is a hipStream_t (NULL = the default stream). The step is enqueued
+ *   asynchronously on it and never synchronises the host; results are valid
+ *   once the stream reaches that point. Calls that overlap on different streams
+ *   must not share a workspace.
+ * - `step` is the 1-based index of the step being taken (the caller increments
+ *   its counter before the call); all tensors of one call share it.
+ * - Every argument is validated on the host before anything is enqueued: a
+ *   failing call leaves every tensor untouched. Return value: MEO_OK, or a
+ *   negative MEO_E* code with a message available from meo_last_error().
+ * - Tensors with zero elements are skipped.
+ * - `workspace` is device scratch of at least meo_*_workspace_size() bytes,
+ *   256-byte aligned, valid only while the enqueued work runs; no value is kept
+ *   in it between calls.
+ * - The library keeps a small cache of device-side launch tables keyed on the
+ *   tensor list (shapes and pointers). Building a table allocates device memory
+ *   and copies to it synchronously, once per distinct list;
+ *   meo_release_plans() frees the cache.
+ */
+#ifndef MEO_H
+#define MEO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MEO_VERSION 1
+
+/* Return codes. */
+#define MEO_OK          0
+#define MEO_EINVAL     (-1) /* hyperparameter or step out of range            */
+#define MEO_ESHAPE     (-2) /* inconsistent batch/rows/cols/ndim or too large */
+#define MEO_EDTYPE     (-3) /* unsupported dtype                              */
+#define MEO_ENULL      (-4) /* required pointer is NULL                       */
+#define MEO_EWORKSPACE (-5) /* workspace NULL, misaligned or too small        */
+#define MEO_EALIGN     (-6) /* tensor pointer misaligned for its dtype        */
+#define MEO_EHIP       (-7) /* HIP runtime error while enqueueing             */
+
+/* Element types. */
+#define MEO_F32  0
+#define MEO_BF16 1
+
+/*
+ * One parameter tensor and its gradient, viewed as [batch, rows, cols]:
+ * ndim >= 2 -> rows = size of dim -2, cols = size of dim -1, batch = product of
+ * the leading dims; the Adafactor/CAME statistics are factored per matrix
+ * (page "Step 3": factored = len(param_shape) >= 2).
+ * ndim 0 or 1 -> batch = rows = 1, cols = numel; full (unfactored) statistic.
+ * LAMB ignores the view and treats the tensor as one flat layer.
+ */
+typedef struct meo_tensor {
+    void*       param;       /* float32 [batch*rows*cols], updated in place   */
+    const void* grad;        /* grad_dtype [batch*rows*cols], read only        */
+    int64_t     batch;
+    int64_t     rows;
+    int64_t     cols;
+    int32_t     ndim;        /* the tensor's number of dims (0, 1, 2, ...)     */
+    int32_t     param_dtype; /* MEO_F32                                        */
+    int32_t     grad_dtype;  /* MEO_F32 or MEO_BF16                            */
+    int32_t     reserved;    /* set to 0                                       */
+} meo_tensor;
+
+/* ------------------------------------------------------------------ Adafactor */
+
+/* Hyperparameters. Defaults (meo_adafactor_defaults) are the page's, section
+ * "Step 3": lr = None (has_lr = 0), eps = (1e-30, 1e-3), clip_threshold = 1.0,
+ * decay_rate = -0.8, beta1 = None (has_beta1 = 0), weight_decay = 0.0,
+ * scale_parameter = 1, relative_step = 1, warmup_init = 0.
+ * The learning rate is min(1e-2, 1/sqrt(step)) with relative_step (1e-2 becomes
+ * 1e-6*step with warmup_init), else lr; with scale_parameter it is multiplied by
+ * max(eps2, RMS(param)). beta2t = 1 - step**decay_rate (note after "Step 5").
+ * Errors (MEO_EINVAL): has_lr with relative_step ("Cannot combine manual lr and
+ * relative_step=True options"), warmup_init without relative_step
+ * ("warmup_init=True requires relative_step=True"), neither lr nor
+ * relative_step, clip_threshold <= 0, negative eps, non-finite values. */
+typedef struct meo_adafactor_hparams {
+    double  lr;
+    double  eps1;
+    double  eps2;
+    double  clip_threshold;
+    double  decay_rate;
+    double  beta1;
+    double  weight_decay;
+    int32_t has_lr;
+    int32_t has_beta1;
+    int32_t scale_parameter;
+    int32_t relative_step;
+    int32_t warmup_init;
+    int32_t reserved;
+} meo_adafactor_hparams;
+
+/* Per-tensor state, float32, caller-allocated, zero before the first step.
+ * Names follow the page ("Step 3"). */
+typedef struct meo_adafactor_state {
+    float* exp_avg;        /* [numel]; required iff has_beta1, else ignored     */
+    float* exp_avg_sq_row; /* [batch*rows]; factored tensors only               */
+    float* exp_avg_sq_col; /* [batch*cols]; factored tensors only               */
+    float* exp_avg_sq;     /* [numel]; 1-D tensors only                          */
+} meo_adafactor_state;
+
+void   meo_adafactor_defaults(meo_adafactor_hparams* hp);
+size_t meo_adafactor_workspace_size(int32_t n, const meo_tensor* tensors);
+int    meo_adafactor_validate(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
+                              const meo_tensor* tensors, const meo_adafactor_state* states);
+int    meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
+                          const meo_tensor* tensors, const meo_adafactor_state* states,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------- CAME */
+
+/* Hyperparameters. Defaults (meo_came_defaults) are the page's DistributedCAME
+ * paragraph: eps = (1e-30, 1e-16), clip_threshold = 1.0,
+ * betas = (0.9, 0.999, 0.9999), weight_decay = 0.0. The page's lr default is
+ * None, but CAME has no relative step, so lr must be given (has_lr = 1).
+ * beta2 is constant (no decay schedule); no bias correction. Errors
+ * (MEO_EINVAL): no lr, lr < 0, a beta outside [0, 1), clip_threshold <= 0,
+ * negative eps, non-finite values. */
+typedef struct meo_came_hparams {
+    double  lr;
+    double  eps1;
+    double  eps2;
+    double  clip_threshold;
+    double  beta1;
+    double  beta2;
+    double  beta3;
+    double  weight_decay;
+    int32_t has_lr;
+    int32_t reserved;
+} meo_came_hparams;
+
+/* Per-tensor state, float32, zero before the first step. The confidence
+ * statistic is factored like the squared-gradient one. */
+typedef struct meo_came_state {
+    float* exp_avg;         /* [numel], always required                          */
+    float* exp_avg_sq_row;  /* [batch*rows]; factored only                       */
+    float* exp_avg_sq_col;  /* [batch*cols]; factored only                       */
+    float* exp_avg_res_row; /* [batch*rows]; factored only                       */
+    float* exp_avg_res_col; /* [batch*cols]; factored only                       */
+    float* exp_avg_sq;      /* [numel]; 1-D only                                  */
+} meo_came_state;
+
+void   meo_came_defaults(meo_came_hparams* hp);
+size_t meo_came_workspace_size(int32_t n, const meo_tensor* tensors);
+int    meo_came_validate(const meo_came_hparams* hp, int64_t step, int32_t n,
+                         const meo_tensor* tensors, const meo_came_state* states);
+int    meo_came_step(const meo_came_hparams* hp, int64_t step, int32_t n,
+                     const meo_tensor* tensors, const meo_came_state* states,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------- LAMB */
+
+/* Hyperparameters. Defaults (meo_lamb_defaults) are the page's DistributedLAMB
+ * paragraph: lr = 1e-3, betas = (0.9, 0.999), eps = 1e-6, weight_decay = 0,
+ * bias_correction = 1. The page says lr, eps and betas are validated: MEO_EINVAL
+ * for lr < 0, eps < 0, a beta outside [0, 1), or non-finite values.
+ * Per tensor: m, v Adam moments (bias-corrected if asked), direction
+ * d = m_hat / (sqrt(v_hat) + eps) + weight_decay * param, trust ratio
+ * ||param|| / ||d|| (1 when either is 0), param -= lr * ratio * d. */
+typedef struct meo_lamb_hparams {
+    double  lr;
+    double  beta1;
+    double  beta2;
+    double  eps;
+    double  weight_decay;
+    int32_t bias_correction;
+    int32_t reserved;
+} meo_lamb_hparams;
+
+typedef struct meo_lamb_state {
+    float* exp_avg;    /* [numel] */
+    float* exp_avg_sq; /* [numel] */
+} meo_lamb_state;
+
+void   meo_lamb_defaults(meo_lamb_hparams* hp);
+size_t meo_lamb_workspace_size(int32_t n, const meo_tensor* tensors);
+int    meo_lamb_validate(const meo_lamb_hparams* hp, int64_t step, int32_t n,
+                         const meo_tensor* tensors, const meo_lamb_state* states);
+int    meo_lamb_step(const meo_lamb_hparams* hp, int64_t step, int32_t n,
+                     const meo_tensor* tensors, const meo_lamb_state* states,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------- utilities */
+
+/* Message of the last failing call on this thread ("" if none). The pointer
+ * stays valid until the next call on the same thread. */
+const char* meo_last_error(void);
+
+/* Frees the cached launch tables. Waits for the device first. */
+void meo_release_plans(void);
+
+/* MEO_VERSION of the built library. */
+int meo_version(void);
+
+/* ----------------------------------------------------------- pass timing
+ * For measurement only. While enabled (meo_profile_enable(1)), every step call
+ * also records a hipEvent on its stream before its first pass and after each
+ * pass, so that the time of each pass can be read back. The events sit between
+ * the passes' launches; they add no device work to the passes themselves.
+ * Pass ids are 0 .. MEO_NUM_PASSES-1, named by meo_pass_name().
+ * meo_profile_collect() waits for the recorded events, adds each pass's
+ * elapsed milliseconds into total_ms[id] and its launch count into
+ * launches[id] (both arrays of MEO_NUM_PASSES entries, caller-owned host
+ * memory, zeroed by the caller), and forgets the events. Returns MEO_OK or
+ * MEO_EHIP. Not for use under graph capture. */
+#define MEO_NUM_PASSES 9
+int         meo_profile_enable(int on);
+const char* meo_pass_name(int id);
+int         meo_profile_collect(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEO_H */

@@ -1,0 +1,369 @@
+"""ctypes binding of libmeo.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does nothing
+but turn torch tensors into the C structs (device pointers and sizes), pass the
+current HIP stream, and turn a negative return code into ``MeoError``. All
+arithmetic of the step runs in the library's HIP kernels. The library must be
+built (``python -m memory_efficient_optimizers_amd.build``); without it every call
+raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+import torch  # loaded first: the library binds to the HIP runtime torch has loaded
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmeo.so")
+
+c_int32, c_int64, c_double, c_void_p, c_size_t = (ctypes.c_int32, ctypes.c_int64, ctypes.c_double,
+                                                  ctypes.c_void_p, ctypes.c_size_t)
+c_float_p = ctypes.POINTER(ctypes.c_float)
+
+MEO_OK, MEO_EINVAL, MEO_ESHAPE, MEO_EDTYPE, MEO_ENULL, MEO_EWORKSPACE, MEO_EALIGN, MEO_EHIP = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+MEO_F32, MEO_BF16 = 0, 1
+ERROR_NAMES = {MEO_EINVAL: "MEO_EINVAL", MEO_ESHAPE: "MEO_ESHAPE", MEO_EDTYPE: "MEO_EDTYPE",
+               MEO_ENULL: "MEO_ENULL", MEO_EWORKSPACE: "MEO_EWORKSPACE", MEO_EALIGN: "MEO_EALIGN",
+               MEO_EHIP: "MEO_EHIP"}
+EXPORTS = [
+    "meo_adafactor_defaults", "meo_adafactor_workspace_size", "meo_adafactor_validate",
+    "meo_adafactor_step", "meo_came_defaults", "meo_came_workspace_size", "meo_came_validate",
+    "meo_came_step", "meo_lamb_defaults", "meo_lamb_workspace_size", "meo_lamb_validate",
+    "meo_lamb_step", "meo_last_error", "meo_release_plans", "meo_version", "meo_profile_enable",
+    "meo_pass_name", "meo_profile_collect",
+]
+MEO_NUM_PASSES = 9
+
+
+class MeoError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {message}")
+        self.code = code
+        self.message = message
+
+
+class meo_tensor(ctypes.Structure):
+    _fields_ = [("param", c_void_p), ("grad", c_void_p), ("batch", c_int64), ("rows", c_int64),
+                ("cols", c_int64), ("ndim", c_int32), ("param_dtype", c_int32),
+                ("grad_dtype", c_int32), ("reserved", c_int32)]
+
+
+class meo_adafactor_hparams(ctypes.Structure):
+    _fields_ = [("lr", c_double), ("eps1", c_double), ("eps2", c_double),
+                ("clip_threshold", c_double), ("decay_rate", c_double), ("beta1", c_double),
+                ("weight_decay", c_double), ("has_lr", c_int32), ("has_beta1", c_int32),
+                ("scale_parameter", c_int32), ("relative_step", c_int32),
+                ("warmup_init", c_int32), ("reserved", c_int32)]
+
+
+class meo_adafactor_state(ctypes.Structure):
+    _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq_row", c_void_p), ("exp_avg_sq_col", c_void_p),
+                ("exp_avg_sq", c_void_p)]
+
+
+class meo_came_hparams(ctypes.Structure):
+    _fields_ = [("lr", c_double), ("eps1", c_double), ("eps2", c_double),
+                ("clip_threshold", c_double), ("beta1", c_double), ("beta2", c_double),
+                ("beta3", c_double), ("weight_decay", c_double), ("has_lr", c_int32),
+                ("reserved", c_int32)]
+
+
+class meo_came_state(ctypes.Structure):
+    _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq_row", c_void_p), ("exp_avg_sq_col", c_void_p),
+                ("exp_avg_res_row", c_void_p), ("exp_avg_res_col", c_void_p),
+                ("exp_avg_sq", c_void_p)]
+
+
+class meo_lamb_hparams(ctypes.Structure):
+    _fields_ = [("lr", c_double), ("beta1", c_double), ("beta2", c_double), ("eps", c_double),
+                ("weight_decay", c_double), ("bias_correction", c_int32), ("reserved", c_int32)]
+
+
+class meo_lamb_state(ctypes.Structure):
+    _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq", c_void_p)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Loads libmeo.so once and declares the signatures; raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m memory_efficient_optimizers_amd.build`")
+    lib = ctypes.CDLL(path)
+    T = ctypes.POINTER(meo_tensor)
+    for opt, hp, st in (("adafactor", meo_adafactor_hparams, meo_adafactor_state),
+                        ("came", meo_came_hparams, meo_came_state),
+                        ("lamb", meo_lamb_hparams, meo_lamb_state)):
+        getattr(lib, f"meo_{opt}_defaults").argtypes = [ctypes.POINTER(hp)]
+        getattr(lib, f"meo_{opt}_defaults").restype = None
+        getattr(lib, f"meo_{opt}_workspace_size").argtypes = [c_int32, T]
+        getattr(lib, f"meo_{opt}_workspace_size").restype = c_size_t
+        getattr(lib, f"meo_{opt}_validate").argtypes = [ctypes.POINTER(hp), c_int64, c_int32, T,
+                                                        ctypes.POINTER(st)]
+        getattr(lib, f"meo_{opt}_validate").restype = ctypes.c_int
+        getattr(lib, f"meo_{opt}_step").argtypes = [ctypes.POINTER(hp), c_int64, c_int32, T,
+                                                    ctypes.POINTER(st), c_void_p, c_size_t, c_void_p]
+        getattr(lib, f"meo_{opt}_step").restype = ctypes.c_int
+    lib.meo_last_error.argtypes = []
+    lib.meo_last_error.restype = ctypes.c_char_p
+    lib.meo_release_plans.argtypes = []
+    lib.meo_release_plans.restype = None
+    lib.meo_version.argtypes = []
+    lib.meo_version.restype = ctypes.c_int
+    lib.meo_profile_enable.argtypes = [ctypes.c_int]
+    lib.meo_profile_enable.restype = ctypes.c_int
+    lib.meo_pass_name.argtypes = [ctypes.c_int]
+    lib.meo_pass_name.restype = ctypes.c_char_p
+    lib.meo_profile_collect.argtypes = [ctypes.POINTER(c_double), ctypes.POINTER(c_int64)]
+    lib.meo_profile_collect.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != MEO_OK:
+        msg = load().meo_last_error().decode("utf-8", "replace")
+        raise MeoError(rc, msg)
+
+
+# ----------------------------------------------------------------------------- marshalling
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def tensor_struct(param: torch.Tensor, grad: torch.Tensor) -> meo_tensor:
+    """[batch, rows, cols] view of a parameter and its gradient (see meo.h)."""
+    if param.dtype != torch.float32:
+        raise TypeError("parameters must be float32")
+    if grad.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("gradients must be float32 or bfloat16")
+    if not (param.is_contiguous() and grad.is_contiguous()):
+        raise ValueError("parameter and gradient must be contiguous")
+    if grad.shape != param.shape:
+        raise ValueError(f"gradient shape {tuple(grad.shape)} != parameter shape {tuple(param.shape)}")
+    shape = tuple(param.shape)
+    if len(shape) >= 2:
+        batch = 1
+        for s in shape[:-2]:
+            batch *= s
+        rows, cols = shape[-2], shape[-1]
+    else:
+        batch, rows, cols = 1, 1, param.numel()
+    return meo_tensor(param.data_ptr(), grad.data_ptr(), batch, rows, cols, len(shape), MEO_F32,
+                      MEO_BF16 if grad.dtype == torch.bfloat16 else MEO_F32, 0)
+
+
+def _tensors(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor]):
+    if len(params) != len(grads):
+        raise ValueError("params and grads differ in length")
+    arr = (meo_tensor * max(len(params), 1))()
+    for i, (p, g) in enumerate(zip(params, grads)):
+        arr[i] = tensor_struct(p, g)
+    return arr
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ws(workspace: Optional[torch.Tensor]):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def _states(cls, keys, states: Sequence[Dict[str, torch.Tensor]]):
+    arr = (cls * max(len(states), 1))()
+    for i, st in enumerate(states):
+        arr[i] = cls(*[_ptr(st.get(k)) for k in keys])
+    return arr
+
+
+ADAFACTOR_KEYS = ["exp_avg", "exp_avg_sq_row", "exp_avg_sq_col", "exp_avg_sq"]
+CAME_KEYS = ["exp_avg", "exp_avg_sq_row", "exp_avg_sq_col", "exp_avg_res_row", "exp_avg_res_col",
+             "exp_avg_sq"]
+LAMB_KEYS = ["exp_avg", "exp_avg_sq"]
+
+
+# ----------------------------------------------------------------------------- hparams
+
+def adafactor_hparams(lr=None, eps=(1e-30, 1e-3), clip_threshold=1.0, decay_rate=-0.8, beta1=None,
+                      weight_decay=0.0, scale_parameter=True, relative_step=True,
+                      warmup_init=False) -> meo_adafactor_hparams:
+    return meo_adafactor_hparams(0.0 if lr is None else float(lr), float(eps[0]), float(eps[1]),
+                                 float(clip_threshold), float(decay_rate),
+                                 0.0 if beta1 is None else float(beta1), float(weight_decay),
+                                 int(lr is not None), int(beta1 is not None), int(bool(scale_parameter)),
+                                 int(bool(relative_step)), int(bool(warmup_init)), 0)
+
+
+def came_hparams(lr=None, eps=(1e-30, 1e-16), clip_threshold=1.0, betas=(0.9, 0.999, 0.9999),
+                 weight_decay=0.0) -> meo_came_hparams:
+    return meo_came_hparams(0.0 if lr is None else float(lr), float(eps[0]), float(eps[1]),
+                            float(clip_threshold), float(betas[0]), float(betas[1]), float(betas[2]),
+                            float(weight_decay), int(lr is not None), 0)
+
+
+def lamb_hparams(lr=1e-3, betas=(0.9, 0.999), eps=1e-6, weight_decay=0.0,
+                 bias_correction=True) -> meo_lamb_hparams:
+    return meo_lamb_hparams(float(lr), float(betas[0]), float(betas[1]), float(eps),
+                            float(weight_decay), int(bool(bias_correction)), 0)
+
+
+def meo_adafactor_defaults() -> meo_adafactor_hparams:
+    hp = meo_adafactor_hparams()
+    load().meo_adafactor_defaults(ctypes.byref(hp))
+    return hp
+
+
+def meo_came_defaults() -> meo_came_hparams:
+    hp = meo_came_hparams()
+    load().meo_came_defaults(ctypes.byref(hp))
+    return hp
+
+
+def meo_lamb_defaults() -> meo_lamb_hparams:
+    hp = meo_lamb_hparams()
+    load().meo_lamb_defaults(ctypes.byref(hp))
+    return hp
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def meo_adafactor_workspace_size(params, grads) -> int:
+    return int(load().meo_adafactor_workspace_size(len(params), _tensors(params, grads)))
+
+
+def meo_came_workspace_size(params, grads) -> int:
+    return int(load().meo_came_workspace_size(len(params), _tensors(params, grads)))
+
+
+def meo_lamb_workspace_size(params, grads) -> int:
+    return int(load().meo_lamb_workspace_size(len(params), _tensors(params, grads)))
+
+
+def meo_adafactor_validate(hp, step, params, grads, states) -> None:
+    _check(load().meo_adafactor_validate(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+                                         _states(meo_adafactor_state, ADAFACTOR_KEYS, states)))
+
+
+def meo_came_validate(hp, step, params, grads, states) -> None:
+    _check(load().meo_came_validate(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+                                    _states(meo_came_state, CAME_KEYS, states)))
+
+
+def meo_lamb_validate(hp, step, params, grads, states) -> None:
+    _check(load().meo_lamb_validate(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+                                    _states(meo_lamb_state, LAMB_KEYS, states)))
+
+
+def meo_adafactor_step(hp, step, params, grads, states, workspace=None, stream=None) -> None:
+    ws, nb = _ws(workspace)
+    _check(load().meo_adafactor_step(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+                                     _states(meo_adafactor_state, ADAFACTOR_KEYS, states), ws, nb,
+                                     _stream(stream)))
+
+
+def meo_came_step(hp, step, params, grads, states, workspace=None, stream=None) -> None:
+    ws, nb = _ws(workspace)
+    _check(load().meo_came_step(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+                                _states(meo_came_state, CAME_KEYS, states), ws, nb, _stream(stream)))
+
+
+def meo_lamb_step(hp, step, params, grads, states, workspace=None, stream=None) -> None:
+    ws, nb = _ws(workspace)
+    _check(load().meo_lamb_step(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+                                _states(meo_lamb_state, LAMB_KEYS, states), ws, nb, _stream(stream)))
+
+
+def meo_last_error() -> str:
+    return load().meo_last_error().decode("utf-8", "replace")
+
+
+def meo_release_plans() -> None:
+    load().meo_release_plans()
+
+
+def meo_version() -> int:
+    return int(load().meo_version())
+
+
+def meo_profile_enable(on: bool) -> None:
+    _check(load().meo_profile_enable(int(bool(on))))
+
+
+def meo_pass_name(i: int) -> str:
+    return load().meo_pass_name(i).decode()
+
+
+def meo_profile_collect() -> Dict[str, Dict[str, float]]:
+    """{pass name: {"ms": total milliseconds, "launches": count}} since the last collect."""
+    ms = (c_double * MEO_NUM_PASSES)()
+    n = (c_int64 * MEO_NUM_PASSES)()
+    _check(load().meo_profile_collect(ms, n))
+    return {meo_pass_name(i): {"ms": ms[i], "launches": int(n[i])} for i in range(MEO_NUM_PASSES) if n[i]}
+
+
+class PreparedStep:
+    """The C arguments of one optimizer's step over a fixed list, marshalled once:
+    repeated calls (a training loop, a benchmark) then only pass the step index and
+    the stream. The tensors must stay alive and in place."""
+
+    _KIND = {"adafactor": (meo_adafactor_state, ADAFACTOR_KEYS),
+             "came": (meo_came_state, CAME_KEYS), "lamb": (meo_lamb_state, LAMB_KEYS)}
+
+    def __init__(self, optimizer: str, hp, params, grads, states, workspace=None):
+        cls, keys = self._KIND[optimizer]
+        self.fn = getattr(load(), f"meo_{optimizer}_step")
+        self.hp = hp
+        self.n = len(params)
+        self.tensors = _tensors(params, grads)
+        self.states = _states(cls, keys, states)
+        self.ws, self.ws_bytes = _ws(workspace)
+        self._keep = (list(params), list(grads), list(states), workspace)
+
+    def __call__(self, step: int, stream=None) -> None:
+        _check(self.fn(ctypes.byref(self.hp), step, self.n, self.tensors, self.states, self.ws,
+                       self.ws_bytes, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- state allocation
+
+def init_state(optimizer: str, param: torch.Tensor, *, beta1: bool = True) -> Dict[str, torch.Tensor]:
+    """Zero fp32 state tensors for one parameter, with the shapes of meo.h."""
+    z = lambda shape: torch.zeros(shape, dtype=torch.float32, device=param.device)  # noqa: E731
+    shape = tuple(param.shape)
+    st: Dict[str, torch.Tensor] = {}
+    if optimizer == "lamb":
+        return {"exp_avg": z(shape), "exp_avg_sq": z(shape)}
+    if optimizer == "came" or beta1:
+        st["exp_avg"] = z(shape)
+    if len(shape) >= 2:
+        st["exp_avg_sq_row"] = z(shape[:-1])
+        st["exp_avg_sq_col"] = z(shape[:-2] + shape[-1:])
+        if optimizer == "came":
+            st["exp_avg_res_row"] = z(shape[:-1])
+            st["exp_avg_res_col"] = z(shape[:-2] + shape[-1:])
+    else:
+        st["exp_avg_sq"] = z(shape)
+    return st
+
+
+def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    """A device scratch buffer of at least ``nbytes`` (torch allocations are 256-byte aligned)."""
+    if nbytes <= 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)

@@ -1,0 +1,688 @@
+// C ABI of the optimizer-step library: validation, launch tables, pass sequences.
+//
+// Host-side schedule values are computed in fp64 from the rules on the
+// Colossal-AI distributed-optimizers page: the relative step size
+// min(1e-2, 1/sqrt(step)) (1e-6*step with warmup_init) and its errors from
+// section "Step 3", beta2t = 1 - step**decay_rate from the note after "Step 5";
+// CAME and LAMB defaults and checks from the DistributedCAME / DistributedLAMB
+// paragraphs. Everything per element runs in the HIP passes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <list>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/meo.h"
+#include "internal.h"
+
+using namespace meo;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+
+enum Op { kOpAdafactor = 0, kOpCame = 1, kOpLamb = 2 };
+
+// Uniform view of the per-tensor state pointers of the three optimizers.
+struct StatePtrs {
+    float* m = nullptr;
+    float* v = nullptr;
+    float* r = nullptr;
+    float* c = nullptr;
+    float* rr = nullptr;
+    float* rc = nullptr;
+};
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align64(int64_t f) { return (f + 63) / 64 * 64; }  // floats -> 256-byte multiple
+
+bool is_factored(int op, const meo_tensor& t) { return op != kOpLamb && t.ndim >= 2; }
+
+bool overflow_numel(const meo_tensor& t, int64_t* numel) {
+    __int128 n = static_cast<__int128>(t.batch) * t.rows * t.cols;
+    if (n > (static_cast<__int128>(1) << 62)) return true;
+    *numel = static_cast<int64_t>(n);
+    return false;
+}
+
+// Geometry and workspace layout of one tensor (pointer-independent).
+struct Geo {
+    int64_t numel = 0;
+    int32_t factored = 0, B = 1, H = 1, W = 1, tr = 1, tc = 0, nrc = 0, ncc = 0;
+    int64_t ntiles = 0, fin_items = 0;
+    int64_t rowpart = 0, colpart = 0, sumr = 0, tilepart = 0, bscal = 0, scal = 0;
+};
+
+// Fills geometry and workspace offsets; returns the workspace size in floats.
+// Tensors are assumed validated.
+int64_t layout(int op, int32_t n, const meo_tensor* ts, std::vector<Geo>* out) {
+    int64_t off = 0;
+    if (out) out->assign(n, Geo());
+    for (int32_t k = 0; k < n; ++k) {
+        Geo g;
+        overflow_numel(ts[k], &g.numel);
+        if (g.numel > 0) {
+            g.factored = is_factored(op, ts[k]);
+            if (g.factored) {
+                g.B = static_cast<int32_t>(ts[k].batch);
+                g.H = static_cast<int32_t>(ts[k].rows);
+                g.W = static_cast<int32_t>(ts[k].cols);
+                g.tr = static_cast<int32_t>(ceil_div(g.H, kTileRows));
+                g.tc = static_cast<int32_t>(ceil_div(g.W, kTileCols));
+                g.ntiles = static_cast<int64_t>(g.B) * g.tr * g.tc;
+                g.nrc = static_cast<int32_t>(ceil_div(g.H, kFinChunk));
+                g.ncc = static_cast<int32_t>(ceil_div(g.W, kFinChunk));
+                g.fin_items = static_cast<int64_t>(g.B) * (g.nrc + g.ncc);
+                g.rowpart = off; off = align64(off + static_cast<int64_t>(g.B) * g.tc * g.H);
+                g.colpart = off; off = align64(off + static_cast<int64_t>(g.B) * g.tr * g.W);
+                g.sumr = off;    off = align64(off + static_cast<int64_t>(g.B) * g.nrc);
+            } else {
+                g.ntiles = ceil_div(g.numel, kFlatTile);
+                g.tc = static_cast<int32_t>(g.ntiles);
+            }
+            g.tilepart = off; off = align64(off + 2 * g.ntiles);
+            g.bscal = off;    off = align64(off + 2 * static_cast<int64_t>(g.B));
+            g.scal = off;     off = align64(off + kScalSlots);
+        }
+        if (out) (*out)[k] = g;
+    }
+    return off;
+}
+
+// ----------------------------------------------------------------------------- validation
+
+bool finite(double v) { return std::isfinite(v); }
+
+int check_tensors(int op, int64_t step, int32_t n, const meo_tensor* ts, const void* states) {
+    if (step < 1) return fail(MEO_EINVAL, "step must be >= 1 (1-based index of the step being taken)");
+    if (n < 0) return fail(MEO_EINVAL, "negative tensor count");
+    if (n == 0) return MEO_OK;
+    if (!ts) return fail(MEO_ENULL, "tensors is NULL");
+    if (!states) return fail(MEO_ENULL, "states is NULL");
+    int64_t total_tiles = 0, total_fin = 0;
+    for (int32_t k = 0; k < n; ++k) {
+        const meo_tensor& t = ts[k];
+        const std::string who = "tensor " + std::to_string(k) + ": ";
+        if (t.batch < 0 || t.rows < 0 || t.cols < 0 || t.ndim < 0)
+            return fail(MEO_ESHAPE, who + "negative batch, rows, cols or ndim");
+        int64_t numel;
+        if (overflow_numel(t, &numel)) return fail(MEO_ESHAPE, who + "too many elements");
+        if (t.ndim <= 1 && numel > 0 && (t.batch != 1 || t.rows != 1))
+            return fail(MEO_ESHAPE, who + "a tensor with ndim <= 1 must have batch == rows == 1");
+        if (t.param_dtype != MEO_F32) return fail(MEO_EDTYPE, who + "param_dtype must be MEO_F32");
+        if (t.grad_dtype != MEO_F32 && t.grad_dtype != MEO_BF16)
+            return fail(MEO_EDTYPE, who + "grad_dtype must be MEO_F32 or MEO_BF16");
+        if (numel == 0) continue;
+        if (!t.param) return fail(MEO_ENULL, who + "param is NULL");
+        if (!t.grad) return fail(MEO_ENULL, who + "grad is NULL");
+        if (reinterpret_cast<uintptr_t>(t.param) % 4) return fail(MEO_EALIGN, who + "param not 4-byte aligned");
+        if (reinterpret_cast<uintptr_t>(t.grad) % (t.grad_dtype == MEO_BF16 ? 2 : 4))
+            return fail(MEO_EALIGN, who + "grad misaligned for its dtype");
+        const bool fac = is_factored(op, t);
+        if (fac) {
+            if (t.batch > kMaxDim || t.rows > kMaxDim || t.cols > kMaxDim)
+                return fail(MEO_ESHAPE, who + "batch, rows or cols exceed 2^31 - 1");
+            const int64_t tiles = t.batch * ceil_div(t.rows, kTileRows) * ceil_div(t.cols, kTileCols);
+            if (tiles > kMaxDim) return fail(MEO_ESHAPE, who + "too many tiles");
+            total_tiles += tiles;
+            total_fin += t.batch * (ceil_div(t.rows, kFinChunk) + ceil_div(t.cols, kFinChunk));
+        } else {
+            total_tiles += ceil_div(numel, kFlatTile);
+        }
+        // states
+        StatePtrs sp;
+        if (op == kOpAdafactor) {
+            const auto& s = static_cast<const meo_adafactor_state*>(states)[k];
+            sp.m = s.exp_avg; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col; sp.v = s.exp_avg_sq;
+        } else if (op == kOpCame) {
+            const auto& s = static_cast<const meo_came_state*>(states)[k];
+            sp.m = s.exp_avg; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col;
+            sp.rr = s.exp_avg_res_row; sp.rc = s.exp_avg_res_col; sp.v = s.exp_avg_sq;
+        } else {
+            const auto& s = static_cast<const meo_lamb_state*>(states)[k];
+            sp.m = s.exp_avg; sp.v = s.exp_avg_sq;
+        }
+        const float* need[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+        const char* names[6] = {"", "", "", "", "", ""};
+        int nn = 0;
+        if (op == kOpLamb) {
+            need[nn] = sp.m; names[nn++] = "exp_avg";
+            need[nn] = sp.v; names[nn++] = "exp_avg_sq";
+        } else {
+            if (fac) {
+                need[nn] = sp.r; names[nn++] = "exp_avg_sq_row";
+                need[nn] = sp.c; names[nn++] = "exp_avg_sq_col";
+                if (op == kOpCame) {
+                    need[nn] = sp.rr; names[nn++] = "exp_avg_res_row";
+                    need[nn] = sp.rc; names[nn++] = "exp_avg_res_col";
+                }
+            } else {
+                need[nn] = sp.v; names[nn++] = "exp_avg_sq";
+            }
+        }
+        for (int i = 0; i < nn; ++i) {
+            if (!need[i]) return fail(MEO_ENULL, who + names[i] + " is NULL");
+            if (reinterpret_cast<uintptr_t>(need[i]) % 4) return fail(MEO_EALIGN, who + names[i] + " misaligned");
+        }
+    }
+    if (total_tiles > 0xffffffffLL || total_fin > 0xffffffffLL)
+        return fail(MEO_ESHAPE, "the tensor list needs more than 2^32 blocks in one pass");
+    return MEO_OK;
+}
+
+int check_adafactor_hp(const meo_adafactor_hparams* hp) {
+    if (!hp) return fail(MEO_ENULL, "hparams is NULL");
+    if (hp->has_lr && hp->relative_step)
+        return fail(MEO_EINVAL, "Cannot combine manual lr and relative_step=True options");
+    if (hp->warmup_init && !hp->relative_step)
+        return fail(MEO_EINVAL, "warmup_init=True requires relative_step=True");
+    if (!hp->has_lr && !hp->relative_step) return fail(MEO_EINVAL, "lr is required when relative_step=False");
+    if (hp->has_lr && !(finite(hp->lr) && hp->lr >= 0.0)) return fail(MEO_EINVAL, "Invalid learning rate");
+    if (!(finite(hp->eps1) && hp->eps1 >= 0.0 && finite(hp->eps2) && hp->eps2 >= 0.0))
+        return fail(MEO_EINVAL, "eps must be finite and >= 0");
+    if (!(finite(hp->clip_threshold) && hp->clip_threshold > 0.0))
+        return fail(MEO_EINVAL, "clip_threshold must be finite and > 0");
+    if (!finite(hp->decay_rate)) return fail(MEO_EINVAL, "decay_rate must be finite");
+    if (hp->has_beta1 && !finite(hp->beta1)) return fail(MEO_EINVAL, "beta1 must be finite");
+    if (!finite(hp->weight_decay)) return fail(MEO_EINVAL, "weight_decay must be finite");
+    return MEO_OK;
+}
+
+int check_came_hp(const meo_came_hparams* hp) {
+    if (!hp) return fail(MEO_ENULL, "hparams is NULL");
+    if (!hp->has_lr) return fail(MEO_EINVAL, "CAME requires an explicit lr");
+    if (!(finite(hp->lr) && hp->lr >= 0.0)) return fail(MEO_EINVAL, "Invalid learning rate");
+    const double b[3] = {hp->beta1, hp->beta2, hp->beta3};
+    for (int i = 0; i < 3; ++i)
+        if (!(b[i] >= 0.0 && b[i] < 1.0))
+            return fail(MEO_EINVAL, "Invalid beta parameter at index " + std::to_string(i));
+    if (!(finite(hp->eps1) && hp->eps1 >= 0.0 && finite(hp->eps2) && hp->eps2 >= 0.0))
+        return fail(MEO_EINVAL, "eps must be finite and >= 0");
+    if (!(finite(hp->clip_threshold) && hp->clip_threshold > 0.0))
+        return fail(MEO_EINVAL, "clip_threshold must be finite and > 0");
+    if (!finite(hp->weight_decay)) return fail(MEO_EINVAL, "weight_decay must be finite");
+    return MEO_OK;
+}
+
+int check_lamb_hp(const meo_lamb_hparams* hp) {
+    if (!hp) return fail(MEO_ENULL, "hparams is NULL");
+    if (!(finite(hp->lr) && hp->lr >= 0.0)) return fail(MEO_EINVAL, "Invalid learning rate");
+    if (!(finite(hp->eps) && hp->eps >= 0.0)) return fail(MEO_EINVAL, "Invalid epsilon value");
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return fail(MEO_EINVAL, "Invalid beta parameter at index 0");
+    if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return fail(MEO_EINVAL, "Invalid beta parameter at index 1");
+    if (!finite(hp->weight_decay)) return fail(MEO_EINVAL, "weight_decay must be finite");
+    return MEO_OK;
+}
+
+int check_workspace(int op, int32_t n, const meo_tensor* ts, void* ws, size_t bytes) {
+    const int64_t need = layout(op, n, ts, nullptr) * static_cast<int64_t>(sizeof(float));
+    if (need == 0) return MEO_OK;
+    if (!ws) return fail(MEO_EWORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MEO_EWORKSPACE, "workspace not 256-byte aligned");
+    if (bytes < static_cast<size_t>(need))
+        return fail(MEO_EWORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+    return MEO_OK;
+}
+
+// ----------------------------------------------------------------------------- plan cache
+
+struct Plan {
+    std::vector<uint8_t> key;
+    int device = 0;
+    void* mem = nullptr;  // [n TDesc][n+1 tile0][n+1 fin0]
+    int32_t n = 0;
+    int64_t tiles = 0, fin_items = 0;
+    const TDesc* desc = nullptr;
+    const int64_t* tile0 = nullptr;
+    const int64_t* fin0 = nullptr;
+};
+
+std::mutex g_mu;
+std::list<Plan*> g_plans;  // most recently used first
+constexpr size_t kMaxPlans = 16;
+
+void free_plan(Plan* p) {
+    int cur = 0;
+    hipGetDevice(&cur);
+    if (cur != p->device) hipSetDevice(p->device);
+    hipFree(p->mem);  // waits for work still using it
+    if (cur != p->device) hipSetDevice(cur);
+    delete p;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Builds (or finds) the launch table for this list. Returns nullptr with g_err set
+// on a HIP failure.
+Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int has_m, int* rc) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        *rc = fail(MEO_EHIP, "hipGetDevice failed");
+        return nullptr;
+    }
+    std::vector<uint8_t> key(sizeof(int) * 4 + n * (sizeof(meo_tensor) + sizeof(StatePtrs)));
+    {
+        uint8_t* w = key.data();
+        const int hdr[4] = {op, n, dev, has_m};
+        std::memcpy(w, hdr, sizeof hdr); w += sizeof hdr;
+        std::memcpy(w, ts, n * sizeof(meo_tensor)); w += n * sizeof(meo_tensor);
+        std::memcpy(w, sp, n * sizeof(StatePtrs));
+    }
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (auto it = g_plans.begin(); it != g_plans.end(); ++it) {
+        if ((*it)->key == key) {
+            Plan* p = *it;
+            g_plans.erase(it);
+            g_plans.push_front(p);
+            return p;
+        }
+    }
+    std::vector<Geo> geo;
+    layout(op, n, ts, &geo);
+    std::vector<TDesc> desc;
+    std::vector<int64_t> tile0(1, 0), fin0(1, 0);
+    for (int32_t k = 0; k < n; ++k) {
+        const Geo& g = geo[k];
+        if (g.numel == 0) continue;
+        TDesc d;
+        std::memset(&d, 0, sizeof d);
+        d.x = static_cast<float*>(ts[k].param);
+        d.g = ts[k].grad;
+        d.m = has_m ? sp[k].m : nullptr;
+        d.v = sp[k].v; d.r = sp[k].r; d.c = sp[k].c; d.rr = sp[k].rr; d.rc = sp[k].rc;
+        d.numel = g.numel;
+        d.tile0 = tile0.back();
+        d.fin0 = fin0.back();
+        d.rowpart = g.rowpart; d.colpart = g.colpart; d.sumr = g.sumr;
+        d.tilepart = g.tilepart; d.bscal = g.bscal; d.scal = g.scal;
+        d.B = g.B; d.H = g.H; d.W = g.W;
+        d.factored = g.factored;
+        d.gbf16 = ts[k].grad_dtype == MEO_BF16;
+        bool vec = aligned16(d.x) && aligned16(d.g) && (!d.m || aligned16(d.m));
+        if (g.factored) vec = vec && (g.W % kVec == 0);
+        else vec = vec && (!d.v || aligned16(d.v));
+        d.vec = vec;
+        d.tr = g.tr; d.tc = g.tc;
+        d.ntiles = static_cast<int32_t>(g.ntiles);
+        d.nrc = g.nrc; d.ncc = g.ncc;
+        desc.push_back(d);
+        tile0.push_back(tile0.back() + g.ntiles);
+        fin0.push_back(fin0.back() + g.fin_items);
+    }
+    const int32_t m = static_cast<int32_t>(desc.size());
+    const size_t bytes_desc = m * sizeof(TDesc);
+    const size_t bytes_pre = (m + 1) * sizeof(int64_t);
+    std::vector<uint8_t> host(bytes_desc + 2 * bytes_pre);
+    if (m) std::memcpy(host.data(), desc.data(), bytes_desc);
+    std::memcpy(host.data() + bytes_desc, tile0.data(), bytes_pre);
+    std::memcpy(host.data() + bytes_desc + bytes_pre, fin0.data(), bytes_pre);
+    Plan* p = new Plan;
+    p->key = std::move(key);
+    p->device = dev;
+    p->n = m;
+    p->tiles = tile0.back();
+    p->fin_items = fin0.back();
+    if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
+        hipMemcpy(p->mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+        if (p->mem) hipFree(p->mem);
+        delete p;
+        *rc = fail(MEO_EHIP, "could not allocate or upload the launch table");
+        return nullptr;
+    }
+    uint8_t* base = static_cast<uint8_t*>(p->mem);
+    p->desc = reinterpret_cast<const TDesc*>(base);
+    p->tile0 = reinterpret_cast<const int64_t*>(base + bytes_desc);
+    p->fin0 = reinterpret_cast<const int64_t*>(base + bytes_desc + bytes_pre);
+    g_plans.push_front(p);
+    while (g_plans.size() > kMaxPlans) {
+        free_plan(g_plans.back());
+        g_plans.pop_back();
+    }
+    return p;
+}
+
+std::vector<StatePtrs> state_ptrs(int op, int32_t n, const void* states) {
+    std::vector<StatePtrs> out(n);
+    for (int32_t k = 0; k < n; ++k) {
+        StatePtrs& sp = out[k];
+        if (op == kOpAdafactor) {
+            const auto& s = static_cast<const meo_adafactor_state*>(states)[k];
+            sp.m = s.exp_avg; sp.v = s.exp_avg_sq; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col;
+        } else if (op == kOpCame) {
+            const auto& s = static_cast<const meo_came_state*>(states)[k];
+            sp.m = s.exp_avg; sp.v = s.exp_avg_sq; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col;
+            sp.rr = s.exp_avg_res_row; sp.rc = s.exp_avg_res_col;
+        } else {
+            const auto& s = static_cast<const meo_lamb_state*>(states)[k];
+            sp.m = s.exp_avg; sp.v = s.exp_avg_sq;
+        }
+    }
+    return out;
+}
+
+// ----------------------------------------------------------------------------- pass timing
+
+enum Pass { kPassStats = 0, kPassFinalize, kPassRms, kPassScalars, kPassAfApply, kPassCameMom,
+            kPassCameApply, kPassLambMoments, kPassLambApply, kPassCount };
+static_assert(kPassCount == MEO_NUM_PASSES, "pass table");
+const char* const kPassNames[kPassCount] = {"stats", "finalize", "rms", "scalars", "adafactor_apply",
+                                            "came_mom", "came_apply", "lamb_moments", "lamb_apply"};
+
+struct ProfRec { int pass; hipEvent_t a, b; };
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Records an event after each pass of one step call when profiling is on.
+class PassTimer {
+  public:
+    explicit PassTimer(hipStream_t s) : s_(s) {
+        std::lock_guard<std::mutex> lock(g_prof_mu);
+        on_ = g_prof_on;
+        if (on_) {
+            last_ = take_event();
+            if (!last_ || hipEventRecord(last_, s_) != hipSuccess) on_ = false;
+        }
+    }
+    void mark(int pass) {
+        if (!on_) return;
+        std::lock_guard<std::mutex> lock(g_prof_mu);
+        hipEvent_t e = take_event();
+        if (!e || hipEventRecord(e, s_) != hipSuccess) { on_ = false; return; }
+        g_prof.push_back(ProfRec{pass, last_, e});
+        last_ = e;
+    }
+  private:
+    hipStream_t s_;
+    bool on_ = false;
+    hipEvent_t last_ = nullptr;
+};
+
+int launch_status(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MEO_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+    return MEO_OK;
+}
+
+}  // namespace
+
+// ============================================================================= exports
+
+extern "C" {
+
+const char* meo_last_error(void) { return g_err.c_str(); }
+
+int meo_version(void) { return MEO_VERSION; }
+
+int meo_profile_enable(int on) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof_on = on != 0;
+    return MEO_OK;
+}
+
+const char* meo_pass_name(int id) { return (id >= 0 && id < kPassCount) ? kPassNames[id] : ""; }
+
+int meo_profile_collect(double* total_ms, int64_t* launches) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    int rc = MEO_OK;
+    std::vector<hipEvent_t> seen;
+    for (const ProfRec& r : g_prof) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+            rc = fail(MEO_EHIP, "could not read pass timing events");
+        } else {
+            if (total_ms) total_ms[r.pass] += ms;
+            if (launches) launches[r.pass] += 1;
+        }
+        seen.push_back(r.a);
+        seen.push_back(r.b);
+    }
+    std::sort(seen.begin(), seen.end());
+    seen.erase(std::unique(seen.begin(), seen.end()), seen.end());
+    for (hipEvent_t e : seen) g_event_pool.push_back(e);
+    g_prof.clear();
+    return rc;
+}
+
+void meo_release_plans(void) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (Plan* p : g_plans) free_plan(p);
+    g_plans.clear();
+}
+
+// ----------------------------------------------------------------------------- Adafactor
+
+void meo_adafactor_defaults(meo_adafactor_hparams* hp) {
+    if (!hp) return;
+    std::memset(hp, 0, sizeof *hp);
+    hp->lr = 0.0;
+    hp->has_lr = 0;
+    hp->eps1 = 1e-30;
+    hp->eps2 = 1e-3;
+    hp->clip_threshold = 1.0;
+    hp->decay_rate = -0.8;
+    hp->beta1 = 0.0;
+    hp->has_beta1 = 0;
+    hp->weight_decay = 0.0;
+    hp->scale_parameter = 1;
+    hp->relative_step = 1;
+    hp->warmup_init = 0;
+}
+
+size_t meo_adafactor_workspace_size(int32_t n, const meo_tensor* ts) {
+    if (n <= 0 || !ts) return 0;
+    return static_cast<size_t>(layout(kOpAdafactor, n, ts, nullptr)) * sizeof(float);
+}
+
+int meo_adafactor_validate(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                           const meo_adafactor_state* st) {
+    g_err.clear();
+    int rc = check_adafactor_hp(hp);
+    if (rc) return rc;
+    rc = check_tensors(kOpAdafactor, step, n, ts, st);
+    if (rc) return rc;
+    if (hp->has_beta1)
+        for (int32_t k = 0; k < n; ++k) {
+            int64_t numel;
+            overflow_numel(ts[k], &numel);
+            if (numel > 0 && !st[k].exp_avg)
+                return fail(MEO_ENULL, "tensor " + std::to_string(k) + ": exp_avg is NULL but beta1 is set");
+            if (numel > 0 && reinterpret_cast<uintptr_t>(st[k].exp_avg) % 4)
+                return fail(MEO_EALIGN, "tensor " + std::to_string(k) + ": exp_avg misaligned");
+        }
+    return MEO_OK;
+}
+
+int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                       const meo_adafactor_state* st, void* ws, size_t ws_bytes, void* stream) {
+    int rc = meo_adafactor_validate(hp, step, n, ts, st);
+    if (rc) return rc;
+    if (n == 0) return MEO_OK;
+    rc = check_workspace(kOpAdafactor, n, ts, ws, ws_bytes);
+    if (rc) return rc;
+    const std::vector<StatePtrs> sp = state_ptrs(kOpAdafactor, n, st);
+    Plan* p = get_plan(kOpAdafactor, n, ts, sp.data(), hp->has_beta1, &rc);
+    if (!p) return rc;
+    if (p->n == 0) return MEO_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const Table t{p->desc, p->tile0, p->fin0, static_cast<float*>(ws), p->n};
+
+    const double tt = static_cast<double>(step);
+    double rho;
+    if (hp->relative_step) rho = std::fmin(hp->warmup_init ? 1e-6 * tt : 1e-2, 1.0 / std::sqrt(tt));
+    else rho = hp->lr;
+    const double b2 = 1.0 - std::pow(tt, hp->decay_rate);
+
+    PassTimer pt(s);
+    launch_stats(t, p->tiles, StatsArgs{static_cast<float>(hp->eps1), static_cast<float>(b2),
+                                        static_cast<float>(1.0 - b2), 1}, s);
+    pt.mark(kPassStats);
+    launch_finalize(t, p->fin_items, FinArgs{b2, 0}, s);
+    pt.mark(kPassFinalize);
+    launch_rms(t, p->tiles, 1, s);
+    pt.mark(kPassRms);
+    launch_scalars(t, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, rho, hp->eps2, hp->clip_threshold,
+                                     hp->weight_decay, 0.0}, s);
+    pt.mark(kPassScalars);
+    launch_af_apply(t, p->tiles, AfApplyArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1),
+                                             hp->has_beta1}, s);
+    pt.mark(kPassAfApply);
+    return launch_status("adafactor step launch");
+}
+
+// ----------------------------------------------------------------------------- CAME
+
+void meo_came_defaults(meo_came_hparams* hp) {
+    if (!hp) return;
+    std::memset(hp, 0, sizeof *hp);
+    hp->lr = 0.0;
+    hp->has_lr = 0;
+    hp->eps1 = 1e-30;
+    hp->eps2 = 1e-16;
+    hp->clip_threshold = 1.0;
+    hp->beta1 = 0.9;
+    hp->beta2 = 0.999;
+    hp->beta3 = 0.9999;
+    hp->weight_decay = 0.0;
+}
+
+size_t meo_came_workspace_size(int32_t n, const meo_tensor* ts) {
+    if (n <= 0 || !ts) return 0;
+    return static_cast<size_t>(layout(kOpCame, n, ts, nullptr)) * sizeof(float);
+}
+
+int meo_came_validate(const meo_came_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                      const meo_came_state* st) {
+    g_err.clear();
+    int rc = check_came_hp(hp);
+    if (rc) return rc;
+    rc = check_tensors(kOpCame, step, n, ts, st);
+    if (rc) return rc;
+    for (int32_t k = 0; k < n; ++k) {
+        int64_t numel;
+        overflow_numel(ts[k], &numel);
+        if (numel > 0 && !st[k].exp_avg) return fail(MEO_ENULL, "tensor " + std::to_string(k) + ": exp_avg is NULL");
+        if (numel > 0 && reinterpret_cast<uintptr_t>(st[k].exp_avg) % 4)
+            return fail(MEO_EALIGN, "tensor " + std::to_string(k) + ": exp_avg misaligned");
+    }
+    return MEO_OK;
+}
+
+int meo_came_step(const meo_came_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                  const meo_came_state* st, void* ws, size_t ws_bytes, void* stream) {
+    int rc = meo_came_validate(hp, step, n, ts, st);
+    if (rc) return rc;
+    if (n == 0) return MEO_OK;
+    rc = check_workspace(kOpCame, n, ts, ws, ws_bytes);
+    if (rc) return rc;
+    const std::vector<StatePtrs> sp = state_ptrs(kOpCame, n, st);
+    Plan* p = get_plan(kOpCame, n, ts, sp.data(), 1, &rc);
+    if (!p) return rc;
+    if (p->n == 0) return MEO_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const Table t{p->desc, p->tile0, p->fin0, static_cast<float*>(ws), p->n};
+
+    PassTimer pt(s);
+    launch_stats(t, p->tiles, StatsArgs{static_cast<float>(hp->eps1), static_cast<float>(hp->beta2),
+                                        static_cast<float>(1.0 - hp->beta2), 0}, s);
+    pt.mark(kPassStats);
+    launch_finalize(t, p->fin_items, FinArgs{hp->beta2, 0}, s);
+    pt.mark(kPassFinalize);
+    launch_rms(t, p->tiles, 0, s);
+    pt.mark(kPassRms);
+    launch_scalars(t, p->n, ScalArgs{kScalCame1, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay, hp->lr}, s);
+    pt.mark(kPassScalars);
+    launch_came_mom(t, p->tiles, CameArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1),
+                                          static_cast<float>(hp->eps2), static_cast<float>(hp->lr)}, s);
+    pt.mark(kPassCameMom);
+    launch_finalize(t, p->fin_items, FinArgs{hp->beta3, 1}, s);
+    pt.mark(kPassFinalize);
+    launch_scalars(t, p->n, ScalArgs{kScalCame2, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay, hp->lr}, s);
+    pt.mark(kPassScalars);
+    launch_came_apply(t, p->tiles, s);
+    pt.mark(kPassCameApply);
+    return launch_status("came step launch");
+}
+
+// ----------------------------------------------------------------------------- LAMB
+
+void meo_lamb_defaults(meo_lamb_hparams* hp) {
+    if (!hp) return;
+    std::memset(hp, 0, sizeof *hp);
+    hp->lr = 1e-3;
+    hp->beta1 = 0.9;
+    hp->beta2 = 0.999;
+    hp->eps = 1e-6;
+    hp->weight_decay = 0.0;
+    hp->bias_correction = 1;
+}
+
+size_t meo_lamb_workspace_size(int32_t n, const meo_tensor* ts) {
+    if (n <= 0 || !ts) return 0;
+    return static_cast<size_t>(layout(kOpLamb, n, ts, nullptr)) * sizeof(float);
+}
+
+int meo_lamb_validate(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                      const meo_lamb_state* st) {
+    g_err.clear();
+    int rc = check_lamb_hp(hp);
+    if (rc) return rc;
+    return check_tensors(kOpLamb, step, n, ts, st);
+}
+
+int meo_lamb_step(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                  const meo_lamb_state* st, void* ws, size_t ws_bytes, void* stream) {
+    int rc = meo_lamb_validate(hp, step, n, ts, st);
+    if (rc) return rc;
+    if (n == 0) return MEO_OK;
+    rc = check_workspace(kOpLamb, n, ts, ws, ws_bytes);
+    if (rc) return rc;
+    const std::vector<StatePtrs> sp = state_ptrs(kOpLamb, n, st);
+    Plan* p = get_plan(kOpLamb, n, ts, sp.data(), 1, &rc);
+    if (!p) return rc;
+    if (p->n == 0) return MEO_OK;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const Table t{p->desc, p->tile0, p->fin0, static_cast<float*>(ws), p->n};
+
+    const double tt = static_cast<double>(step);
+    const double bc1 = hp->bias_correction ? 1.0 - std::pow(hp->beta1, tt) : 1.0;
+    const double bc2 = hp->bias_correction ? 1.0 - std::pow(hp->beta2, tt) : 1.0;
+    const LambArgs la{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1),
+                      static_cast<float>(hp->beta2), static_cast<float>(1.0 - hp->beta2),
+                      static_cast<float>(1.0 / bc1), static_cast<float>(1.0 / bc2),
+                      static_cast<float>(hp->eps), static_cast<float>(hp->weight_decay)};
+    PassTimer pt(s);
+    launch_lamb_moments(t, p->tiles, la, s);
+    pt.mark(kPassLambMoments);
+    launch_scalars(t, p->n, ScalArgs{kScalLamb, 0, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
+    pt.mark(kPassScalars);
+    launch_lamb_apply(t, p->tiles, la, s);
+    pt.mark(kPassLambApply);
+    return launch_status("lamb step launch");
+}
+
+}  // extern "C"

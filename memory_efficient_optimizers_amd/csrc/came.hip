@@ -1,0 +1,151 @@
+// CAME passes beyond the shared Adafactor-style statistics.
+//
+// The page (Colossal-AI distributed optimizers, "four optimizers" table and the
+// DistributedCAME paragraph) describes CAME as Adafactor's factorisation plus a
+// confidence matrix tracked with a third beta; the step order is that of the CAME
+// paper it cites (arXiv:2307.02047):
+//
+//   k_came_mom    u = G / sqrt(V_hat) / kappa (rebuilt on the fly),
+//                 M <- beta1 M + (1 - beta1) u, stored;
+//                 factored: row and column sums of E = (u - M)^2 + eps2 per tile
+//                 (the instability), folded into the confidence statistics by the
+//                 shared finalize pass with beta3;
+//                 1-D: the step is M itself, X <- X - lr wd X - lr M.
+//   k_came_apply  factored: X <- X - lr wd X - M * rsqrt(S_ij) * lr with
+//                 S_ij = Rs_i Cs_j / mean(Rs) rebuilt on the fly.
+#include "internal.h"
+
+namespace meo {
+
+__global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
+    __shared__ __align__(16) float lds[kWaves * kTileCols];
+    const int64_t tile = blockIdx.x;
+    const int k = find_tensor(t.tile0, t.n, tile);
+    const TDesc d = t.desc[k];
+    const int64_t lt = tile - d.tile0;
+    float* ws = t.ws;
+    const bool vec = d.vec, bf = d.gbf16;
+    const float b1 = a.beta1, omb1 = a.omb1;
+
+    if (d.factored) {
+        const TileRC p = tile_rc(d, lt);
+        const int lane = threadIdx.x & 63;
+        const float coef = ws[d.bscal + p.b];
+        const int64_t mat = static_cast<int64_t>(p.b) * d.H * d.W;
+        float cf[kVec], cs[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            cf[e] = e < p.valid ? rsqrtf(d.c[static_cast<int64_t>(p.b) * d.W + p.col + e]) : 0.0f;
+            cs[e] = 0.0f;
+        }
+        const float* rrow = d.r + static_cast<int64_t>(p.b) * d.H;
+        float* rowpart = ws + d.rowpart + (static_cast<int64_t>(p.b) * d.tc + p.ct) * d.H;
+        for (int i0 = 0; i0 < p.nrows; i0 += 4) {
+            float g[4][kVec], m[4][kVec];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i0 + i < p.nrows) {
+                    const int64_t off = mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col;
+                    load_g8(d.g, off, p.valid, vec, bf, g[i]);
+                    load_f8(d.m + off, p.valid, vec, m[i]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i0 + i < p.nrows) {
+                    const int row = p.row0 + i0 + i;
+                    const int64_t off = mat + static_cast<int64_t>(row) * d.W + p.col;
+                    const float rf = rsqrtf(rrow[row]) * coef;
+                    float rs = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        const float u = (g[i][e] * cf[e]) * rf;
+                        m[i][e] = fmaf(b1, m[i][e], omb1 * u);
+                        const float du = u - m[i][e];
+                        const float q = e < p.valid ? fmaf(du, du, a.eps2) : 0.0f;
+                        cs[e] += q;
+                        rs += q;
+                    }
+                    store_f8(d.m + off, p.valid, vec, m[i]);
+                    rs = wave_sum(rs);
+                    if (lane == 0) rowpart[row] = rs;
+                }
+            }
+        }
+        write_colpart(d, ws, p, cs, lds);
+    } else {
+        const float coef = ws[d.bscal];
+        const float decay = ws[d.scal + kSlotDecay];
+        const float lr = a.lr;
+        const int64_t base = lt * kFlatTile;
+        for (int it = 0; it < kFlatIters; ++it) {
+            const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
+            const int valid = clamp_valid(d.numel - i);
+            if (valid == 0) break;
+            float g[kVec], v[kVec], x[kVec], m[kVec];
+            load_g8(d.g, i, valid, vec, bf, g);
+            load_f8(d.v + i, valid, vec, v);
+            load_f8(d.x + i, valid, vec, x);
+            load_f8(d.m + i, valid, vec, m);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+                const float u = e < valid ? (g[e] * rsqrtf(v[e])) * coef : 0.0f;
+                m[e] = fmaf(b1, m[e], omb1 * u);
+                x[e] = fmaf(-decay, x[e], x[e]) - lr * m[e];
+            }
+            store_f8(d.m + i, valid, vec, m);
+            store_f8(d.x + i, valid, vec, x);
+        }
+    }
+}
+
+void launch_came_mom(const Table& t, int64_t tiles, const CameArgs& a, hipStream_t s) {
+    if (tiles > 0) hipLaunchKernelGGL(k_came_mom, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t, a);
+}
+
+__global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
+    const int64_t tile = blockIdx.x;
+    const int k = find_tensor(t.tile0, t.n, tile);
+    const TDesc d = t.desc[k];
+    if (!d.factored) return;  // 1-D tensors were finished by k_came_mom
+    const int64_t lt = tile - d.tile0;
+    const float* ws = t.ws;
+    const bool vec = d.vec;
+    const TileRC p = tile_rc(d, lt);
+    const float coef = ws[d.bscal + d.B + p.b];
+    const float decay = ws[d.scal + kSlotDecay];
+    const int64_t mat = static_cast<int64_t>(p.b) * d.H * d.W;
+    float sc[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e)
+        sc[e] = e < p.valid ? rsqrtf(d.rc[static_cast<int64_t>(p.b) * d.W + p.col + e]) : 0.0f;
+    const float* rrow = d.rr + static_cast<int64_t>(p.b) * d.H;
+    for (int i0 = 0; i0 < p.nrows; i0 += 4) {
+        float x[4][kVec], m[4][kVec];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i0 + i < p.nrows) {
+                const int64_t off = mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col;
+                load_f8(d.x + off, p.valid, vec, x[i]);
+                load_f8(d.m + off, p.valid, vec, m[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i0 + i < p.nrows) {
+                const int row = p.row0 + i0 + i;
+                const int64_t off = mat + static_cast<int64_t>(row) * d.W + p.col;
+                const float sr = rsqrtf(rrow[row]) * coef;
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) x[i][e] = fmaf(-decay, x[i][e], x[i][e]) - (m[i][e] * sc[e]) * sr;
+                store_f8(d.x + off, p.valid, vec, x[i]);
+            }
+        }
+    }
+}
+
+void launch_came_apply(const Table& t, int64_t tiles, hipStream_t s) {
+    if (tiles > 0) hipLaunchKernelGGL(k_came_apply, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t);
+}
+
+}  // namespace meo

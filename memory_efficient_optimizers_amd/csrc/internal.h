@@ -1,0 +1,286 @@
+// Internal structures and device helpers of the optimizer-step library.
+//
+// Work decomposition shared by every pass:
+//   * A factored tensor, viewed as [B, H, W], is cut into tiles of kTileRows rows
+//     x kTileCols columns inside one matrix. A block of 256 threads (4 wave64s)
+//     owns one tile: each lane owns 8 adjacent columns (one 16-byte bf16 or two
+//     16-byte fp32 loads per row), each wave owns kRowsPerWave rows.
+//   * A flat tensor (1-D Adafactor/CAME tensors, every LAMB tensor) is cut into
+//     tiles of kFlatTile consecutive elements; each thread owns 8 adjacent
+//     elements per iteration.
+//   * The tiles of every tensor in a call form one grid; a block finds its tensor
+//     by binary search over the prefix sums of tile counts (launch table).
+// Every cross-block reduction is two-stage with a fixed order, so results are
+// bitwise reproducible and independent of what else is in the list.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace meo {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kLanes = 64;
+constexpr int kVec = 8;                       // elements per lane per row/iteration
+constexpr int kTileCols = kLanes * kVec;      // 512
+constexpr int kRowsPerWave = 16;
+constexpr int kTileRows = kWaves * kRowsPerWave;  // 64
+constexpr int kFlatIters = 16;
+constexpr int kFlatTile = kThreads * kVec * kFlatIters;  // 32768
+constexpr int kFinChunk = 256;                // rows or columns per finalize block
+constexpr int kScalSlots = 8;                 // floats of per-tensor scalars
+
+// Per-tensor scalar slots in the workspace.
+enum ScalSlot { kSlotAlpha = 0, kSlotCoef = 1, kSlotDecay = 2, kSlotRmsU = 3, kSlotRmsX = 4,
+                kSlotNormD = 5 };
+
+// Device-side descriptor of one tensor of the call (built on the host, cached).
+struct TDesc {
+    float* x;         // parameter
+    const void* g;    // gradient (fp32 or bf16)
+    float* m;         // first moment (nullable)
+    float* v;         // full second moment (1-D Adafactor/CAME; LAMB)
+    float* r;         // factored row statistic [B*H]
+    float* c;         // factored column statistic [B*W]
+    float* rr;        // CAME confidence row statistic [B*H]
+    float* rc;        // CAME confidence column statistic [B*W]
+    int64_t numel;
+    int64_t tile0;    // first global tile of this tensor
+    int64_t fin0;     // first finalize item of this tensor
+    // workspace offsets, in floats
+    int64_t rowpart;  // [B][tc][H]   row sums per column tile
+    int64_t colpart;  // [B][tr][W]   column sums per row tile
+    int64_t sumr;     // [B][nrc]     sums of the new row statistic per finalize chunk
+    int64_t tilepart; // [ntiles][2]  per-tile partial sums for the per-tensor scalars
+    int64_t bscal;    // [2][B]       per-matrix coefficients
+    int64_t scal;     // [kScalSlots] per-tensor scalars
+    int32_t B, H, W;
+    int32_t factored; // 1: [B,H,W] factored statistics; 0: flat
+    int32_t gbf16;    // gradient dtype is bf16
+    int32_t vec;      // 16-byte vector accesses are valid
+    int32_t tr, tc;   // tiles per matrix along rows / columns (flat: tr = 1, tc = ntiles)
+    int32_t ntiles;
+    int32_t nrc, ncc; // finalize chunks per matrix along rows / columns
+    int32_t pad;
+};
+
+// Launch table of one call, device-resident.
+struct Table {
+    const TDesc* desc;
+    const int64_t* tile0;  // [n+1] prefix sums of tile counts
+    const int64_t* fin0;   // [n+1] prefix sums of finalize items
+    float* ws;             // workspace base
+    int32_t n;
+};
+
+// ----------------------------------------------------------------------------- helpers
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Largest k in [0, n) with pre[k] <= t (pre is non-decreasing, pre[n] > t).
+__device__ __forceinline__ int find_tensor(const int64_t* __restrict__ pre, int n, int64_t t) {
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (pre[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Sum of two per-thread values over the block, in a fixed order; result valid in
+// thread 0. `lds` must hold 2 * kWaves floats.
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* lds) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    a = wave_sum(a);
+    b = wave_sum(b);
+    if (lane == 0) { lds[w] = a; lds[kWaves + w] = b; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        a = (lds[0] + lds[1]) + (lds[2] + lds[3]);
+        b = (lds[4] + lds[5]) + (lds[6] + lds[7]);
+    }
+}
+
+__device__ __forceinline__ double block_sum_d(double a, double* lds) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    a = wave_sum(a);
+    if (lane == 0) lds[w] = a;
+    __syncthreads();
+    return (lds[0] + lds[1]) + (lds[2] + lds[3]);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 8 gradient values starting at element `i` of `g`; `valid` (0..8) of them are in
+// range, the rest read as 0. Vector loads only when all 8 are valid and `vec`.
+__device__ __forceinline__ void load_g8(const void* __restrict__ g, int64_t i, int valid,
+                                        bool vec, bool bf16, float* f) {
+    if (bf16) {
+        const uint16_t* p = static_cast<const uint16_t*>(g) + i;
+        if (vec && valid == kVec) {
+            uint4 u = *reinterpret_cast<const uint4*>(p);
+            f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+            f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e)
+                f[e] = e < valid ? __uint_as_float(static_cast<uint32_t>(p[e]) << 16) : 0.0f;
+        }
+    } else {
+        const float* p = static_cast<const float*>(g) + i;
+        if (vec && valid == kVec) {
+            float4 a = *reinterpret_cast<const float4*>(p);
+            float4 b = *reinterpret_cast<const float4*>(p + 4);
+            f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+            f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) f[e] = e < valid ? p[e] : 0.0f;
+        }
+    }
+}
+
+__device__ __forceinline__ void load_f8(const float* __restrict__ p, int valid, bool vec, float* f) {
+    if (vec && valid == kVec) {
+        float4 a = *reinterpret_cast<const float4*>(p);
+        float4 b = *reinterpret_cast<const float4*>(p + 4);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) f[e] = e < valid ? p[e] : 0.0f;
+    }
+}
+
+__device__ __forceinline__ void store_f8(float* __restrict__ p, int valid, bool vec, const float* f) {
+    if (vec && valid == kVec) {
+        *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e)
+            if (e < valid) p[e] = f[e];
+    }
+}
+
+__device__ __forceinline__ int clamp_valid(int64_t remaining) {
+    return remaining >= kVec ? kVec : (remaining > 0 ? static_cast<int>(remaining) : 0);
+}
+
+// ----------------------------------------------------------------------------- tile helpers
+
+// Mean over the rows of matrix b of the (already updated) row statistic, from the
+// per-chunk sums written by the finalize pass. Every lane of the calling wave gets
+// the same value, and every caller the same bits (fixed order).
+__device__ __forceinline__ double row_mean(const TDesc& d, const float* __restrict__ ws, int b) {
+    const int lane = threadIdx.x & 63;
+    const float* sr = ws + d.sumr + static_cast<int64_t>(b) * d.nrc;
+    double s = 0.0;
+    for (int j = lane; j < d.nrc; j += kLanes) s += static_cast<double>(sr[j]);
+    return wave_sum(s) / static_cast<double>(d.H);
+}
+
+struct TileRC {   // this thread's position inside a factored tile
+    int b, rt, ct, col, valid, row0, nrows;
+};
+
+__device__ __forceinline__ TileRC tile_rc(const TDesc& d, int64_t lt) {
+    TileRC p;
+    const int per = d.tr * d.tc;
+    p.b = static_cast<int>(lt / per);
+    const int rem = static_cast<int>(lt - static_cast<int64_t>(p.b) * per);
+    p.rt = rem / d.tc;
+    p.ct = rem - p.rt * d.tc;
+    const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    p.col = p.ct * kTileCols + lane * kVec;
+    p.valid = clamp_valid(static_cast<int64_t>(d.W) - p.col);
+    p.row0 = p.rt * kTileRows + w * kRowsPerWave;
+    p.nrows = min(kRowsPerWave, d.H - p.row0);
+    return p;
+}
+
+// Column partial sums of one tile: the 4 waves' per-lane sums are combined in a
+// fixed order through LDS (kWaves * kTileCols floats) and written to
+// colpart[b][rt][col].
+__device__ __forceinline__ void write_colpart(const TDesc& d, float* __restrict__ ws, const TileRC& p,
+                                              const float* cs, float* lds) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float* l = lds + w * kTileCols + lane * kVec;
+    *reinterpret_cast<float4*>(l) = make_float4(cs[0], cs[1], cs[2], cs[3]);
+    *reinterpret_cast<float4*>(l + 4) = make_float4(cs[4], cs[5], cs[6], cs[7]);
+    __syncthreads();
+    float* out = ws + d.colpart + (static_cast<int64_t>(p.b) * d.tr + p.rt) * d.W;
+    for (int cc = threadIdx.x; cc < kTileCols; cc += kThreads) {
+        const int cg = p.ct * kTileCols + cc;
+        if (cg < d.W)
+            out[cg] = (lds[cc] + lds[kTileCols + cc]) + (lds[2 * kTileCols + cc] + lds[3 * kTileCols + cc]);
+    }
+}
+
+__device__ __forceinline__ float sum8(const float* a) {
+    return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
+// ----------------------------------------------------------------------------- launchers
+
+// Arguments of the shared passes.
+struct StatsArgs {      // factored statistics of Q = G^2 + eps1; 1-D full statistic
+    float eps1;
+    float beta;         // EMA weight of the old 1-D statistic (beta2t or beta2); 0: not read
+    float omb;          // 1 - beta, rounded from fp64
+    int32_t need_x;     // 1-D tiles also accumulate sum(x^2)
+};
+struct FinArgs {        // row/column finalize: s <- beta*s + (1-beta)*mean(partials)
+    double beta;        // 0: the old statistic is not read
+    int32_t which;      // 0: squared-gradient statistic (r, c); 1: CAME confidence (rr, rc)
+};
+enum ScalMode { kScalAdafactor = 0, kScalCame1 = 1, kScalCame2 = 2, kScalLamb = 3 };
+struct ScalArgs {
+    int32_t mode;
+    int32_t scale_parameter;
+    double rho;         // Adafactor base step size
+    double eps2;        // Adafactor floor of RMS(param)
+    double clip;        // clip threshold
+    double wd;          // weight decay
+    double lr;          // CAME / LAMB learning rate
+};
+struct AfApplyArgs {
+    float beta1, omb1;
+    int32_t has_beta1;
+};
+struct CameArgs {
+    float beta1, omb1;
+    float eps2;
+    float lr;
+};
+struct LambArgs {
+    float beta1, omb1, beta2, omb2;
+    float inv_bc1, inv_bc2;  // 1 / (1 - beta^t), or 1 without bias correction
+    float eps, wd;
+};
+
+void launch_stats(const Table& t, int64_t tiles, const StatsArgs& a, hipStream_t s);
+void launch_finalize(const Table& t, int64_t items, const FinArgs& a, hipStream_t s);
+void launch_rms(const Table& t, int64_t tiles, int32_t need_x, hipStream_t s);
+void launch_scalars(const Table& t, int32_t n, const ScalArgs& a, hipStream_t s);
+void launch_af_apply(const Table& t, int64_t tiles, const AfApplyArgs& a, hipStream_t s);
+void launch_came_mom(const Table& t, int64_t tiles, const CameArgs& a, hipStream_t s);
+void launch_came_apply(const Table& t, int64_t tiles, hipStream_t s);
+void launch_lamb_moments(const Table& t, int64_t tiles, const LambArgs& a, hipStream_t s);
+void launch_lamb_apply(const Table& t, int64_t tiles, const LambArgs& a, hipStream_t s);
+
+}  // namespace meo

@@ -1,0 +1,91 @@
+// LAMB passes. The page (Colossal-AI distributed optimizers, "four optimizers"
+// table and the DistributedLAMB paragraph) describes a layer-wise update scaled
+// by a trust ratio of parameter and update norms; the per-tensor step is that of
+// the LAMB paper it cites (arXiv:1904.00962):
+//
+//   k_lamb_moments  M <- b1 M + (1-b1) G, V <- b2 V + (1-b2) G^2 (stored);
+//                   d = (M / bc1) / (sqrt(V / bc2) + eps) + wd X; per-tile sums of
+//                   X^2 and d^2.
+//   (k_scalars)     ratio = ||X|| / ||d|| (1 if either is 0), coef = lr * ratio.
+//   k_lamb_apply    d recomputed from the stored M, V and X; X <- X - coef d.
+//
+// Every tensor is one flat layer, whatever its number of dims.
+#include "internal.h"
+
+namespace meo {
+
+__device__ __forceinline__ float lamb_dir(float m, float v, float x, const LambArgs& a) {
+    return (m * a.inv_bc1) / (sqrtf(v * a.inv_bc2) + a.eps) + a.wd * x;
+}
+
+__global__ __launch_bounds__(kThreads) void k_lamb_moments(Table t, LambArgs a) {
+    __shared__ float lds[2 * kWaves];
+    const int64_t tile = blockIdx.x;
+    const int k = find_tensor(t.tile0, t.n, tile);
+    const TDesc d = t.desc[k];
+    const int64_t lt = tile - d.tile0;
+    const bool vec = d.vec, bf = d.gbf16;
+    const int64_t base = lt * kFlatTile;
+    float sx[kVec], sd[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) { sx[e] = 0.0f; sd[e] = 0.0f; }
+    for (int it = 0; it < kFlatIters; ++it) {
+        const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
+        const int valid = clamp_valid(d.numel - i);
+        if (valid == 0) break;
+        float g[kVec], x[kVec], m[kVec], v[kVec];
+        load_g8(d.g, i, valid, vec, bf, g);
+        load_f8(d.x + i, valid, vec, x);
+        load_f8(d.m + i, valid, vec, m);
+        load_f8(d.v + i, valid, vec, v);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            m[e] = fmaf(a.beta1, m[e], a.omb1 * g[e]);
+            v[e] = fmaf(a.beta2, v[e], a.omb2 * (g[e] * g[e]));
+            const float dd = e < valid ? lamb_dir(m[e], v[e], x[e], a) : 0.0f;
+            sx[e] = fmaf(x[e], x[e], sx[e]);
+            sd[e] = fmaf(dd, dd, sd[e]);
+        }
+        store_f8(d.m + i, valid, vec, m);
+        store_f8(d.v + i, valid, vec, v);
+    }
+    float tx = sum8(sx), td = sum8(sd);
+    block_sum2(tx, td, lds);
+    if (threadIdx.x == 0) {
+        float* tp = t.ws + d.tilepart + 2 * lt;
+        tp[0] = tx;
+        tp[1] = td;
+    }
+}
+
+void launch_lamb_moments(const Table& t, int64_t tiles, const LambArgs& a, hipStream_t s) {
+    if (tiles > 0) hipLaunchKernelGGL(k_lamb_moments, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t, a);
+}
+
+__global__ __launch_bounds__(kThreads) void k_lamb_apply(Table t, LambArgs a) {
+    const int64_t tile = blockIdx.x;
+    const int k = find_tensor(t.tile0, t.n, tile);
+    const TDesc d = t.desc[k];
+    const int64_t lt = tile - d.tile0;
+    const bool vec = d.vec;
+    const float coef = t.ws[d.bscal];
+    const int64_t base = lt * kFlatTile;
+    for (int it = 0; it < kFlatIters; ++it) {
+        const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
+        const int valid = clamp_valid(d.numel - i);
+        if (valid == 0) break;
+        float x[kVec], m[kVec], v[kVec];
+        load_f8(d.x + i, valid, vec, x);
+        load_f8(d.m + i, valid, vec, m);
+        load_f8(d.v + i, valid, vec, v);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) x[e] = x[e] - coef * lamb_dir(m[e], v[e], x[e], a);
+        store_f8(d.x + i, valid, vec, x);
+    }
+}
+
+void launch_lamb_apply(const Table& t, int64_t tiles, const LambArgs& a, hipStream_t s) {
+    if (tiles > 0) hipLaunchKernelGGL(k_lamb_apply, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t, a);
+}
+
+}  // namespace meo

@@ -1,0 +1,158 @@
+"""torch.optim front ends over the C ABI: Adafactor, CAME and Lamb.
+
+Each class owns its state tensors (fp32, on the parameter's device, named as on
+the Colossal-AI distributed-optimizers page: ``step``, ``exp_avg``,
+``exp_avg_sq_row``, ``exp_avg_sq_col``, ``exp_avg_sq``; CAME adds
+``exp_avg_res_row`` / ``exp_avg_res_col``) and a device workspace, and hands
+every parameter with a gradient to one library call per parameter group (and per
+step count, should parameters have taken different numbers of steps). The update
+itself runs in the HIP kernels; ``state_dict()`` / ``load_state_dict()`` work as
+for any torch optimizer.
+"""
+from __future__ import annotations
+
+from collections import defaultdict
+from typing import Dict, List, Optional, Tuple
+
+import torch
+
+from . import _lib
+
+
+class _MeoOptimizer(torch.optim.Optimizer):
+    _kind = ""
+
+    def __init__(self, params, defaults):
+        super().__init__(params, defaults)
+        self._workspace: Dict[torch.device, torch.Tensor] = {}
+
+    def _ws(self, nbytes: int, device) -> Optional[torch.Tensor]:
+        if nbytes <= 0:
+            return None
+        ws = self._workspace.get(device)
+        if ws is None or ws.numel() < nbytes:
+            ws = _lib.workspace(nbytes, device)
+            self._workspace[device] = ws
+        return ws
+
+    def _state_for(self, p: torch.Tensor, group) -> Dict[str, torch.Tensor]:
+        raise NotImplementedError
+
+    def _call(self, group, step: int, params, grads, states, ws):
+        raise NotImplementedError
+
+    def _wsize(self, params, grads) -> int:
+        raise NotImplementedError
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        for group in self.param_groups:
+            buckets: Dict[Tuple[torch.device, int], List[torch.Tensor]] = defaultdict(list)
+            for p in group["params"]:
+                if p.grad is None:
+                    continue
+                if p.grad.is_sparse:
+                    raise RuntimeError(f"{type(self).__name__} does not support sparse gradients")
+                st = self.state[p]
+                if len(st) == 0:
+                    st["step"] = 0
+                    st.update(self._state_for(p, group))
+                st["step"] += 1
+                buckets[(p.device, st["step"])].append(p)
+            for (device, step), ps in buckets.items():
+                grads = [p.grad if p.grad.is_contiguous() else p.grad.contiguous() for p in ps]
+                states = [self.state[p] for p in ps]
+                ws = self._ws(self._wsize(ps, grads), device)
+                with torch.cuda.device(device):
+                    self._call(group, step, ps, grads, states, ws)
+        return loss
+
+
+class Adafactor(_MeoOptimizer):
+    """Adafactor with the page's defaults ("Step 3"): lr=None, eps=(1e-30, 1e-3),
+    clip_threshold=1.0, decay_rate=-0.8, beta1=None, weight_decay=0.0,
+    scale_parameter=True, relative_step=True, warmup_init=False."""
+
+    _kind = "adafactor"
+
+    def __init__(self, params, lr=None, eps=(1e-30, 1e-3), clip_threshold=1.0, decay_rate=-0.8,
+                 beta1=None, weight_decay=0.0, scale_parameter=True, relative_step=True,
+                 warmup_init=False):
+        if lr is not None and relative_step:
+            raise ValueError("Cannot combine manual lr and relative_step=True options")
+        if warmup_init and not relative_step:
+            raise ValueError("warmup_init=True requires relative_step=True")
+        defaults = dict(lr=lr, eps=eps, clip_threshold=clip_threshold, decay_rate=decay_rate,
+                        beta1=beta1, weight_decay=weight_decay, scale_parameter=scale_parameter,
+                        relative_step=relative_step, warmup_init=warmup_init)
+        super().__init__(params, defaults)
+
+    def _state_for(self, p, group):
+        return _lib.init_state("adafactor", p, beta1=group["beta1"] is not None)
+
+    def _wsize(self, params, grads):
+        return _lib.meo_adafactor_workspace_size(params, grads)
+
+    def _call(self, group, step, params, grads, states, ws):
+        hp = _lib.adafactor_hparams(**{k: group[k] for k in self.defaults})
+        _lib.meo_adafactor_step(hp, step, params, grads, states, ws)
+
+
+class CAME(_MeoOptimizer):
+    """CAME with the page's defaults (DistributedCAME paragraph):
+    eps=(1e-30, 1e-16), clip_threshold=1.0, betas=(0.9, 0.999, 0.9999),
+    weight_decay=0.0; lr must be given."""
+
+    _kind = "came"
+
+    def __init__(self, params, lr=None, eps=(1e-30, 1e-16), clip_threshold=1.0,
+                 betas=(0.9, 0.999, 0.9999), weight_decay=0.0):
+        if lr is None:
+            raise ValueError("CAME requires an explicit lr")
+        defaults = dict(lr=lr, eps=eps, clip_threshold=clip_threshold, betas=betas,
+                        weight_decay=weight_decay)
+        super().__init__(params, defaults)
+
+    def _state_for(self, p, group):
+        return _lib.init_state("came", p)
+
+    def _wsize(self, params, grads):
+        return _lib.meo_came_workspace_size(params, grads)
+
+    def _call(self, group, step, params, grads, states, ws):
+        hp = _lib.came_hparams(**{k: group[k] for k in self.defaults})
+        _lib.meo_came_step(hp, step, params, grads, states, ws)
+
+
+class Lamb(_MeoOptimizer):
+    """LAMB with the page's defaults (DistributedLAMB paragraph): lr=1e-3,
+    betas=(0.9, 0.999), eps=1e-6, weight_decay=0, bias_correction=True."""
+
+    _kind = "lamb"
+
+    def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-6, weight_decay=0.0,
+                 bias_correction=True):
+        if not lr >= 0.0:
+            raise ValueError(f"Invalid learning rate: {lr}")
+        if not eps >= 0.0:
+            raise ValueError(f"Invalid epsilon value: {eps}")
+        for i, b in enumerate(betas):
+            if not 0.0 <= b < 1.0:
+                raise ValueError(f"Invalid beta parameter at index {i}: {b}")
+        defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay,
+                        bias_correction=bias_correction)
+        super().__init__(params, defaults)
+
+    def _state_for(self, p, group):
+        return _lib.init_state("lamb", p)
+
+    def _wsize(self, params, grads):
+        return _lib.meo_lamb_workspace_size(params, grads)
+
+    def _call(self, group, step, params, grads, states, ws):
+        hp = _lib.lamb_hparams(**{k: group[k] for k in self.defaults})
+        _lib.meo_lamb_step(hp, step, params, grads, states, ws)

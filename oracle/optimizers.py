@@ -86,6 +86,12 @@ def is_factored(shape: Tuple[int, ...]) -> bool:
     return len(shape) >= 2
 
 
+def _untouched(x: Array, state: State) -> Tuple[Array, State]:
+    """reading: a tensor with no elements has nothing to update; its statistics
+    (means over zero entries) are left as they were."""
+    return np.array(x, dtype=np.float64), {k: np.array(v) for k, v in state.items()}
+
+
 # ----------------------------------------------------------------------------- Adafactor
 
 def adafactor_hparams(hp: Optional[dict] = None) -> dict:
@@ -141,6 +147,8 @@ def adafactor_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], 
         raise ValueError("step must be >= 1")
     x = np.asarray(x, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
+    if x.size == 0:
+        return _untouched(x, state)
     eps1, eps2 = h["eps"]
 
     # Learning rate: relative step, scaled by the parameter's RMS before this
@@ -233,6 +241,8 @@ def came_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
         raise ValueError("step must be >= 1")
     x = np.asarray(x, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
+    if x.size == 0:
+        return _untouched(x, state)
     eps1, eps2 = h["eps"]
     beta1, beta2, beta3 = h["betas"]
     lr = float(h["lr"])
@@ -311,6 +321,8 @@ def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
         raise ValueError("step must be >= 1")
     x = np.asarray(x, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
+    if x.size == 0:
+        return _untouched(x, state)
     beta1, beta2 = h["betas"]
     m = beta1 * state["exp_avg"] + (1.0 - beta1) * g
     v = beta2 * state["exp_avg_sq"] + (1.0 - beta2) * g * g

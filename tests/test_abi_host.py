@@ -1,0 +1,179 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, and validates arguments (codes and page messages) before any
+device work. No compute call is made, so these run without a GPU: validation
+only inspects pointers, never dereferences them."""
+import json
+import os
+import re
+
+import pytest
+import torch
+
+from memory_efficient_optimizers_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "meo.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmeo.so is not built: run `python -m memory_efficient_optimizers_amd.build`")
+    return _lib.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(meo_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert _lib.meo_version() == 1
+
+
+def test_defaults_are_the_pages(lib):
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "page_defaults.json")))
+    a = _lib.meo_adafactor_defaults()
+    g = gold["adafactor"]
+    assert (a.has_lr, a.has_beta1) == (0, 0)
+    assert (a.eps1, a.eps2) == tuple(g["eps"])
+    assert a.clip_threshold == g["clip_threshold"] and a.decay_rate == g["decay_rate"]
+    assert a.weight_decay == g["weight_decay"]
+    assert (a.scale_parameter, a.relative_step, a.warmup_init) == (1, 1, 0)
+    c = _lib.meo_came_defaults()
+    g = gold["came"]
+    assert c.has_lr == 0 and (c.eps1, c.eps2) == tuple(g["eps"])
+    assert (c.beta1, c.beta2, c.beta3) == tuple(g["betas"])
+    assert c.clip_threshold == g["clip_threshold"] and c.weight_decay == g["weight_decay"]
+    l = _lib.meo_lamb_defaults()
+    g = gold["lamb"]
+    assert l.lr == g["lr"] and (l.beta1, l.beta2) == tuple(g["betas"]) and l.eps == g["eps"]
+    assert l.weight_decay == g["weight_decay"] and l.bias_correction == 1
+
+
+def _mk(shapes, gdt=torch.float32):
+    ps = [torch.zeros(s, dtype=torch.float32) for s in shapes]
+    gs = [torch.zeros(s, dtype=gdt) for s in shapes]
+    return ps, gs
+
+
+def _af_states(ps, beta1=False):
+    return [_lib.init_state("adafactor", p, beta1=beta1) for p in ps]
+
+
+def _code(fn, *a):
+    with pytest.raises(_lib.MeoError) as e:
+        fn(*a)
+    return e.value.code, e.value.message
+
+
+def test_adafactor_validation(lib):
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "page_defaults.json")))["messages"]
+    ps, gs = _mk([(4, 8), (8,)])
+    st = _af_states(ps)
+    _lib.meo_adafactor_validate(_lib.adafactor_hparams(), 1, ps, gs, st)
+    code, msg = _code(_lib.meo_adafactor_validate, _lib.adafactor_hparams(lr=1e-3), 1, ps, gs, st)
+    assert code == _lib.MEO_EINVAL and msg == gold["lr_with_relative_step"]
+    code, msg = _code(_lib.meo_adafactor_validate,
+                      _lib.adafactor_hparams(lr=1e-3, relative_step=False, warmup_init=True), 1, ps, gs, st)
+    assert code == _lib.MEO_EINVAL and msg == gold["warmup_needs_relative_step"]
+    assert _code(_lib.meo_adafactor_validate, _lib.adafactor_hparams(relative_step=False), 1,
+                 ps, gs, st)[0] == _lib.MEO_EINVAL
+    assert _code(_lib.meo_adafactor_validate, _lib.adafactor_hparams(clip_threshold=0.0), 1,
+                 ps, gs, st)[0] == _lib.MEO_EINVAL
+    assert _code(_lib.meo_adafactor_validate, _lib.adafactor_hparams(), 0, ps, gs, st)[0] == _lib.MEO_EINVAL
+    # beta1 set but no first moment
+    assert _code(_lib.meo_adafactor_validate, _lib.adafactor_hparams(beta1=0.9), 1,
+                 ps, gs, st)[0] == _lib.MEO_ENULL
+    # factored tensor without its row statistic
+    bad = [dict(s) for s in st]
+    del bad[0]["exp_avg_sq_row"]
+    assert _code(_lib.meo_adafactor_validate, _lib.adafactor_hparams(), 1, ps, gs, bad)[0] == _lib.MEO_ENULL
+    # 1-D tensor without its full statistic
+    bad = [dict(s) for s in st]
+    del bad[1]["exp_avg_sq"]
+    assert _code(_lib.meo_adafactor_validate, _lib.adafactor_hparams(), 1, ps, gs, bad)[0] == _lib.MEO_ENULL
+
+
+def test_tensor_checks(lib):
+    ps, gs = _mk([(4, 8)])
+    st = _af_states(ps)
+    hp = ctypes_hp = _lib.adafactor_hparams()
+    t = _lib._tensors(ps, gs)
+    sts = _lib._states(_lib.meo_adafactor_state, _lib.ADAFACTOR_KEYS, st)
+
+    def val(tensors):
+        return lib.meo_adafactor_validate(_lib.ctypes.byref(ctypes_hp), 1, 1, tensors, sts)
+
+    t[0].grad_dtype = 7
+    assert val(t) == _lib.MEO_EDTYPE
+    t[0].grad_dtype = _lib.MEO_F32
+    t[0].param_dtype = _lib.MEO_BF16
+    assert val(t) == _lib.MEO_EDTYPE
+    t[0].param_dtype = _lib.MEO_F32
+    t[0].rows = -1
+    assert val(t) == _lib.MEO_ESHAPE
+    t[0].rows = 4
+    t[0].ndim = 1  # 1-D view must have rows == 1
+    assert val(t) == _lib.MEO_ESHAPE
+    t[0].ndim = 2
+    t[0].param = t[0].param + 2
+    assert val(t) == _lib.MEO_EALIGN
+    t[0].param = None
+    assert val(t) == _lib.MEO_ENULL
+    assert "param is NULL" in _lib.meo_last_error()
+    assert lib.meo_adafactor_validate(_lib.ctypes.byref(hp), 1, 1, None, sts) == _lib.MEO_ENULL
+    # a zero-element tensor needs no pointers and is skipped
+    t[0].rows = 0
+    assert val(t) == _lib.MEO_OK
+
+
+def test_workspace_checks(lib):
+    ps, gs = _mk([(100, 600), (33,)])
+    need = _lib.meo_adafactor_workspace_size(ps, gs)
+    assert need > 0 and need % 256 == 0
+    ps2, gs2 = _mk([(100, 600), (33,), (5000, 7)])
+    assert _lib.meo_adafactor_workspace_size(ps2, gs2) > need
+    st = _af_states(ps)
+    hp = _lib.adafactor_hparams()
+    # the workspace is checked before any device work: too small / missing
+    small = torch.empty(need - 256, dtype=torch.uint8)
+    assert _code(_lib.meo_adafactor_step, hp, 1, ps, gs, st, small, 0)[0] == _lib.MEO_EWORKSPACE
+    assert _code(_lib.meo_adafactor_step, hp, 1, ps, gs, st, None, 0)[0] == _lib.MEO_EWORKSPACE
+    assert _lib.meo_lamb_workspace_size(ps, gs) > 0
+    assert _lib.meo_came_workspace_size(ps, gs) > 0
+
+
+def test_came_validation(lib):
+    ps, gs = _mk([(4, 8), (8,)], torch.bfloat16)
+    st = [_lib.init_state("came", p) for p in ps]
+    _lib.meo_came_validate(_lib.came_hparams(lr=2e-4), 1, ps, gs, st)
+    assert _code(_lib.meo_came_validate, _lib.came_hparams(), 1, ps, gs, st)[0] == _lib.MEO_EINVAL
+    assert _code(_lib.meo_came_validate, _lib.came_hparams(lr=1e-3, betas=(0.9, 0.999, 1.0)), 1,
+                 ps, gs, st)[0] == _lib.MEO_EINVAL
+    bad = [dict(s) for s in st]
+    del bad[0]["exp_avg_res_col"]
+    assert _code(_lib.meo_came_validate, _lib.came_hparams(lr=1e-3), 1, ps, gs, bad)[0] == _lib.MEO_ENULL
+
+
+def test_lamb_validation(lib):
+    ps, gs = _mk([(4, 8), (8,)])
+    st = [_lib.init_state("lamb", p) for p in ps]
+    _lib.meo_lamb_validate(_lib.lamb_hparams(), 1, ps, gs, st)
+    for bad in (dict(lr=-1.0), dict(eps=-1.0), dict(betas=(1.0, 0.999)), dict(betas=(0.9, 1.5))):
+        assert _code(_lib.meo_lamb_validate, _lib.lamb_hparams(**bad), 1, ps, gs, st)[0] == _lib.MEO_EINVAL
+    bad = [dict(s) for s in st]
+    del bad[1]["exp_avg"]
+    assert _code(_lib.meo_lamb_validate, _lib.lamb_hparams(), 1, ps, gs, bad)[0] == _lib.MEO_ENULL
+
+
+def test_empty_list_is_a_noop(lib):
+    assert lib.meo_adafactor_step(_lib.ctypes.byref(_lib.adafactor_hparams()), 1, 0, None, None, None, 0,
+                                  None) == _lib.MEO_OK

@@ -1,0 +1,226 @@
+"""Parity of the HIP library with the fp64 oracle, through the C ABI.
+
+Small and scaled-down workloads are compared element by element after every
+chained step; the full-size workloads run as the bench runs them (one call over
+the whole tensor list) and are compared on a sample of whole tensors, which the
+oracle recomputes alone (every statistic is per tensor, so a tensor's result does
+not depend on the rest of the list). Bar: floored relative error <= 1e-5 on
+every fp32 output (tests/harness.py).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.harness import TOL_F32, Run, floored_rel_err, lib_hp, lib_states, lib_step, lib_workspace, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from memory_efficient_optimizers_amd import _lib
+    _lib.load()
+
+
+def _chain(wl, steps, check_every=1, hp=None):
+    run = Run(wl, hp=hp)
+    worst = (0.0, "")
+    for s in range(steps):
+        run.step()
+        if (s + 1) % check_every == 0 or s + 1 == steps:
+            err, name = run.worst()
+            print(f"  {wl.name} step {s + 1}: worst {err:.3e} at {name}", flush=True)
+            assert err <= TOL_F32, f"step {s + 1}: {name} err {err:.3e}"
+            worst = max(worst, (err, name))
+    return run, worst
+
+
+# ----------------------------------------------------------------------------- small / mini workloads
+
+def test_adafactor_small_all_steps():
+    """Adafactor defaults on a 256x512 weight + 512 bias, fp32 grads, 10 steps."""
+    wl = workloads.WORKLOADS["adafactor_small"]
+    _chain(wl, wl.steps)
+
+
+@pytest.mark.parametrize("name", ["adafactor_llama_mini", "came_llama_mini", "lamb_bert_mini"])
+def test_scaled_down_workloads_chained(name):
+    wl = workloads.WORKLOADS[name]
+    _chain(wl, wl.steps, check_every=3)
+
+
+EDGE_SHAPES = [(1, 1000), (1000, 1), (37, 1001), (3,), (), (2, 3, 70, 130), (0, 5), (65, 513),
+               (129, 1024), (1, 8), (700, 8), (5000,), (40000,)]
+
+
+@pytest.mark.parametrize("gdt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("opt,hp", [
+    ("adafactor", {}),
+    ("adafactor", {"beta1": 0.9, "weight_decay": 0.1}),
+    ("adafactor", {"scale_parameter": False, "clip_threshold": 0.3, "beta1": 0.5}),
+    ("adafactor", {"relative_step": False, "lr": 3e-3, "decay_rate": -0.6}),
+    ("adafactor", {"warmup_init": True}),
+    ("came", {"lr": 2e-4}),
+    ("came", {"lr": 1e-3, "weight_decay": 0.05, "clip_threshold": 0.5}),
+    ("lamb", {"lr": 1e-3, "weight_decay": 0.01}),
+    ("lamb", {"lr": 2e-3, "bias_correction": False}),
+])
+def test_edge_shapes(opt, hp, gdt):
+    """Unit dims, odd widths (scalar path), tiny and 0-d tensors, leading batch
+    dims, an empty tensor, ragged tiles on both axes, long 1-D tensors."""
+    wl = workloads.custom(f"edge_{opt}", opt, EDGE_SHAPES, hparams=hp, grad_dtype=gdt,
+                          grad_std=1.0, grad_scaling="rowcol", steps=4)
+    _chain(wl, 4)
+
+
+@pytest.mark.parametrize("opt,hp", [("adafactor", {"beta1": 0.9, "weight_decay": 0.2}),
+                                    ("came", {"lr": 2e-4, "weight_decay": 0.1}),
+                                    ("lamb", {"weight_decay": 0.01})])
+def test_zero_gradients(opt, hp):
+    """All-zero gradients and a zero row inside a nonzero gradient stay finite and
+    match the oracle (eps1 keeps the estimate positive)."""
+    wl = workloads.custom(f"zero_{opt}", opt, [(64, 512), (300,), (70, 96)], hparams=hp, steps=3)
+    run = Run(wl)
+    for s in range(3):
+        gs = run.grads(s)
+        gs[0].zero_()
+        gs[1].zero_()
+        gs[2][5].zero_()
+        gs[2][:, 7].zero_()
+        run.step(gs)
+        for p in run.params:
+            assert torch.isfinite(p).all()
+        err, name = run.worst()
+        assert err <= TOL_F32, (s, name, err)
+
+
+def test_resume_at_step_40000():
+    """A resumed run at step 40000: relative step 1/sqrt(t) = 5e-3 < 1e-2 and
+    beta2t close to 1."""
+    wl = workloads.custom("resume", "adafactor", [(128, 640), (640,)], hparams={"beta1": 0.9}, steps=6)
+    run = Run(wl)
+    for s in range(3):
+        run.step()
+    run.t = 39999
+    for s in range(3, 6):
+        run.step()
+        err, name = run.worst()
+        assert err <= TOL_F32, (run.t, name, err)
+
+
+# ----------------------------------------------------------------------------- invariants of the library
+
+@pytest.mark.parametrize("name", ["adafactor_llama_mini", "came_llama_mini", "lamb_bert_mini"])
+def test_bitwise_deterministic_and_list_independent(name):
+    """Two runs give identical bits, and a step over the list gives the same bits
+    as a step over each tensor alone."""
+    wl = workloads.WORKLOADS[name]
+    opt, hp = wl.optimizer, dict(wl.hparams)
+    scales = workloads.grad_scales(wl, "cuda")
+    results = []
+    for mode in ("list", "list", "single"):
+        ps = workloads.init_params(wl, "cuda")
+        sts = lib_states(opt, ps, hp)
+        hps = lib_hp(opt, hp)
+        for t in range(1, 4):
+            gs = workloads.grads(wl, t - 1, scales, "cuda")
+            if mode == "list":
+                lib_step(opt, hps, t, ps, gs, sts, lib_workspace(opt, ps, gs))
+            else:
+                for k in range(len(ps)):
+                    lib_step(opt, hps, t, [ps[k]], [gs[k]], [sts[k]], lib_workspace(opt, [ps[k]], [gs[k]]))
+        torch.cuda.synchronize()
+        results.append([p.clone() for p in ps] + [v.clone() for st in sts for v in st.values()])
+    for a, b in zip(results[0], results[1]):
+        assert torch.equal(a, b)
+    for a, b in zip(results[0], results[2]):
+        assert torch.equal(a, b)
+
+
+def test_optimizer_classes_match_binding():
+    from memory_efficient_optimizers_amd import CAME, Adafactor, Lamb
+    for cls, opt, hp in ((Adafactor, "adafactor", {"beta1": 0.9}), (CAME, "came", {"lr": 2e-4}),
+                         (Lamb, "lamb", {"weight_decay": 0.01})):
+        wl = workloads.custom(f"cls_{opt}", opt, [(96, 520), (520,), (3, 17, 40)], hparams=hp)
+        scales = workloads.grad_scales(wl, "cuda")
+        ref = Run(wl)
+        ps = [torch.nn.Parameter(p.clone()) for p in workloads.init_params(wl, "cuda")]
+        o = cls(ps, **hp)
+        for t in range(3):
+            gs = workloads.grads(wl, t, scales, "cuda")
+            ref.step([g.clone() for g in gs], oracle_too=False)
+            for p, g in zip(ps, gs):
+                p.grad = g
+            o.step()
+        torch.cuda.synchronize()
+        for p, q in zip(ps, ref.params):
+            assert torch.equal(p.detach(), q)
+        assert o.state[ps[0]]["step"] == 3
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("name", ["adafactor_llama_layer", "came_llama_layer"])
+def test_full_llama_layer(name):
+    """One Llama-7B decoder layer (202M parameters, bf16 grads), 2 chained steps,
+    every element of every tensor against the oracle."""
+    wl = workloads.WORKLOADS[name]
+    _chain(wl, 2)
+
+
+def _sampled_full(wl, sample_idx, steps):
+    """One library call over the whole list per step (the bench's launch shape);
+    the oracle follows only the sampled tensors."""
+    dev = "cuda"
+    opt, hp = wl.optimizer, dict(wl.hparams)
+    ps = workloads.init_params(wl, dev)
+    sts = lib_states(opt, ps, hp)
+    hps = lib_hp(opt, hp)
+    scales = workloads.grad_scales(wl, dev)
+    ox = {k: to64(ps[k]) for k in sample_idx}
+    ost = {k: oracle.INIT_STATE[opt](tuple(ps[k].shape), hp) for k in sample_idx}
+    ws = None
+    for t in range(1, steps + 1):
+        gs = workloads.grads(wl, t - 1, scales, dev)
+        if ws is None:
+            ws = lib_workspace(opt, ps, gs)
+        lib_step(opt, hps, t, ps, gs, sts, ws)
+        torch.cuda.synchronize()
+        for k in sample_idx:
+            ox[k], ost[k] = oracle.STEP_TENSOR[opt](ox[k], to64(gs[k]), ost[k], hp, t)
+            errs = {"param": floored_rel_err(to64(ps[k]), ox[k])}
+            for key, arr in ost[k].items():
+                errs[key] = floored_rel_err(to64(sts[k][key]), arr)
+            worst = max(errs, key=errs.get)
+            print(f"  {wl.name} step {t} {wl.specs[k].name}: worst {errs[worst]:.3e} ({worst})", flush=True)
+            assert errs[worst] <= TOL_F32, (t, wl.specs[k].name, worst, errs[worst])
+        del gs
+
+
+def test_full_llama7b_sampled():
+    """The 7B list (291 tensors, 6.74e9 parameters) in one call per step. Step 1:
+    the embedding, the last gate projection and the final norm checked in full;
+    then three chained steps on a q projection and the final norm."""
+    wl = workloads.WORKLOADS["adafactor_llama7b"]
+    names = [s.name for s in wl.specs]
+    _sampled_full(wl, [0, names.index("model.layers.31.mlp.gate_proj.weight"),
+                       names.index("model.norm.weight")], 1)
+    _sampled_full(wl, [names.index("model.layers.17.self_attn.q_proj.weight"),
+                       names.index("model.norm.weight")], 3)
+
+
+def test_full_bert_large_lamb_sampled():
+    """BERT-large list (388 tensors) in one call per step; word embeddings, an
+    FFN weight and bias and a LayerNorm weight checked in full."""
+    wl = workloads.WORKLOADS["lamb_bert_large"]
+    names = [s.name for s in wl.specs]
+    idx = [0, names.index("encoder.layer.11.intermediate.dense.weight"),
+           names.index("encoder.layer.11.intermediate.dense.bias"),
+           names.index("encoder.layer.23.output.LayerNorm.weight")]
+    _sampled_full(wl, idx, 3)

@@ -179,10 +179,16 @@ def _gen(wl: Workload, k: int, stream: int, device) -> torch.Generator:
     return g
 
 
-def init_params(wl: Workload, device="cpu") -> List[torch.Tensor]:
-    """fp32 parameters: 2-D+ weights N(0, 0.02) (std 0.02), norm weights 1, biases 0."""
+def _pick(wl: Workload, indices):
+    ks = range(len(wl.specs)) if indices is None else indices
+    return [(k, wl.specs[k]) for k in ks]
+
+
+def init_params(wl: Workload, device="cpu", indices=None) -> List[torch.Tensor]:
+    """fp32 parameters: 2-D+ weights N(0, 0.02) (std 0.02), norm weights 1, biases 0.
+    ``indices`` selects tensors (same draws as in the full list)."""
     out = []
-    for k, s in enumerate(wl.specs):
+    for k, s in _pick(wl, indices):
         if s.kind == "weight":
             t = torch.empty(s.shape, dtype=torch.float32, device=device)
             t.normal_(0.0, 0.02, generator=_gen(wl, k, 0, device))
@@ -199,11 +205,12 @@ def _log_uniform(n: int, gen: torch.Generator, device) -> torch.Tensor:
     return torch.pow(10.0, u)
 
 
-def grad_scales(wl: Workload, device="cpu") -> List[Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]]:
+def grad_scales(wl: Workload, device="cpu", indices=None
+                ) -> List[Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]]:
     """Per-tensor fixed scales, drawn once: 10**U(-2, 2) over rows (dim -2) and,
     for "rowcol", over columns (dim -1). 1-D tensors get one scale per element."""
     out = []
-    for k, s in enumerate(wl.specs):
+    for k, s in _pick(wl, indices):
         if wl.grad_scaling == "none":
             out.append((None, None))
             continue
@@ -217,15 +224,16 @@ def grad_scales(wl: Workload, device="cpu") -> List[Tuple[Optional[torch.Tensor]
     return out
 
 
-def grads(wl: Workload, step_index: int, scales, device="cpu") -> List[torch.Tensor]:
+def grads(wl: Workload, step_index: int, scales, device="cpu", indices=None) -> List[torch.Tensor]:
     """Gradients of 0-based step ``step_index``: std * z * row_scale * col_scale,
-    z ~ N(0, 1) redrawn each step, computed in fp32 then cast to the grad dtype."""
+    z ~ N(0, 1) redrawn each step, computed in fp32 then cast to the grad dtype.
+    ``scales`` must come from grad_scales with the same ``indices``."""
     out = []
-    for k, s in enumerate(wl.specs):
+    for j, (k, s) in enumerate(_pick(wl, indices)):
         z = torch.empty(s.shape, dtype=torch.float32, device=device)
         z.normal_(0.0, 1.0, generator=_gen(wl, k, 2 + step_index, device))
         g = z * wl.grad_std
-        a, b = scales[k]
+        a, b = scales[j]
         if a is not None:
             if len(s.shape) < 2:
                 g = g * a
