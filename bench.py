@@ -100,6 +100,26 @@ def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
                       f"{dt:.1f} s, single-threaded NumPy"}
 
 
+def copy_calibration(torch, args) -> int:
+    n = 1 << 30  # fp32 elements: 4 GiB read + 4 GiB written per copy
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(max(args.warmup, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbps = 2 * 4 * n / (ms / 1e3) / 1e9
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "ms": ms, "GBps": gbps,
+                      "frac_of_peak": gbps / HBM_PEAK_GBPS}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +127,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="adafactor_llama7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the step: time a plain device copy of 4 GiB (torch's copy kernel), "
+                         "the reference for achievable bandwidth and for scaling rocprofv3 byte counters")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with the dominant pass's rocprofv3 FETCH_SIZE/WRITE_SIZE (KiB per "
                          "dispatch) and the copy-kernel scale factor")
@@ -125,6 +148,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        return copy_calibration(torch, args)
     _lib.load()
     wl = workloads.WORKLOADS[args.workload]
     dev = "cuda"

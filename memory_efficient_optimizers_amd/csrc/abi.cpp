@@ -241,12 +241,12 @@ int check_workspace(int op, int32_t n, const meo_tensor* ts, void* ws, size_t by
 struct Plan {
     std::vector<uint8_t> key;
     int device = 0;
-    void* mem = nullptr;  // [n TDesc][n+1 tile0][n+1 fin0]
+    void* mem = nullptr;  // [n TDesc][tiles int32][finalize items int32]
     int32_t n = 0;
     int64_t tiles = 0, fin_items = 0;
     const TDesc* desc = nullptr;
-    const int64_t* tile0 = nullptr;
-    const int64_t* fin0 = nullptr;
+    const int32_t* tile_tensor = nullptr;
+    const int32_t* fin_tensor = nullptr;
 };
 
 std::mutex g_mu;
@@ -255,10 +255,10 @@ constexpr size_t kMaxPlans = 16;
 
 void free_plan(Plan* p) {
     int cur = 0;
-    hipGetDevice(&cur);
-    if (cur != p->device) hipSetDevice(p->device);
-    hipFree(p->mem);  // waits for work still using it
-    if (cur != p->device) hipSetDevice(cur);
+    (void)hipGetDevice(&cur);
+    if (cur != p->device) (void)hipSetDevice(p->device);
+    (void)hipFree(p->mem);  // waits for work still using it
+    if (cur != p->device) (void)hipSetDevice(cur);
     delete p;
 }
 
@@ -322,29 +322,35 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
         fin0.push_back(fin0.back() + g.fin_items);
     }
     const int32_t m = static_cast<int32_t>(desc.size());
-    const size_t bytes_desc = m * sizeof(TDesc);
-    const size_t bytes_pre = (m + 1) * sizeof(int64_t);
-    std::vector<uint8_t> host(bytes_desc + 2 * bytes_pre);
-    if (m) std::memcpy(host.data(), desc.data(), bytes_desc);
-    std::memcpy(host.data() + bytes_desc, tile0.data(), bytes_pre);
-    std::memcpy(host.data() + bytes_desc + bytes_pre, fin0.data(), bytes_pre);
+    const int64_t tiles = tile0.back(), items = fin0.back();
+    const size_t bytes_desc = (m * sizeof(TDesc) + 255) / 256 * 256;
+    const size_t bytes_tiles = (tiles * sizeof(int32_t) + 255) / 256 * 256;
+    const size_t bytes_fin = std::max<size_t>(items * sizeof(int32_t), 4);
+    std::vector<uint8_t> host(bytes_desc + bytes_tiles + bytes_fin, 0);
+    if (m) std::memcpy(host.data(), desc.data(), m * sizeof(TDesc));
+    int32_t* tt = reinterpret_cast<int32_t*>(host.data() + bytes_desc);
+    int32_t* ft = reinterpret_cast<int32_t*>(host.data() + bytes_desc + bytes_tiles);
+    for (int32_t k = 0; k < m; ++k) {
+        for (int64_t i = tile0[k]; i < tile0[k + 1]; ++i) tt[i] = k;
+        for (int64_t i = fin0[k]; i < fin0[k + 1]; ++i) ft[i] = k;
+    }
     Plan* p = new Plan;
     p->key = std::move(key);
     p->device = dev;
     p->n = m;
-    p->tiles = tile0.back();
-    p->fin_items = fin0.back();
+    p->tiles = tiles;
+    p->fin_items = items;
     if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
         hipMemcpy(p->mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
-        if (p->mem) hipFree(p->mem);
+        if (p->mem) (void)hipFree(p->mem);
         delete p;
         *rc = fail(MEO_EHIP, "could not allocate or upload the launch table");
         return nullptr;
     }
     uint8_t* base = static_cast<uint8_t*>(p->mem);
     p->desc = reinterpret_cast<const TDesc*>(base);
-    p->tile0 = reinterpret_cast<const int64_t*>(base + bytes_desc);
-    p->fin0 = reinterpret_cast<const int64_t*>(base + bytes_desc + bytes_pre);
+    p->tile_tensor = reinterpret_cast<const int32_t*>(base + bytes_desc);
+    p->fin_tensor = reinterpret_cast<const int32_t*>(base + bytes_desc + bytes_tiles);
     g_plans.push_front(p);
     while (g_plans.size() > kMaxPlans) {
         free_plan(g_plans.back());
@@ -529,7 +535,7 @@ int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
     if (!p) return rc;
     if (p->n == 0) return MEO_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const Table t{p->desc, p->tile0, p->fin0, static_cast<float*>(ws), p->n};
+    const Table t{p->desc, p->tile_tensor, p->fin_tensor, static_cast<float*>(ws), p->n};
 
     const double tt = static_cast<double>(step);
     double rho;
@@ -604,7 +610,7 @@ int meo_came_step(const meo_came_hparams* hp, int64_t step, int32_t n, const meo
     if (!p) return rc;
     if (p->n == 0) return MEO_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const Table t{p->desc, p->tile0, p->fin0, static_cast<float*>(ws), p->n};
+    const Table t{p->desc, p->tile_tensor, p->fin_tensor, static_cast<float*>(ws), p->n};
 
     PassTimer pt(s);
     launch_stats(t, p->tiles, StatsArgs{static_cast<float>(hp->eps1), static_cast<float>(hp->beta2),
@@ -666,7 +672,7 @@ int meo_lamb_step(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo
     if (!p) return rc;
     if (p->n == 0) return MEO_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const Table t{p->desc, p->tile0, p->fin0, static_cast<float*>(ws), p->n};
+    const Table t{p->desc, p->tile_tensor, p->fin_tensor, static_cast<float*>(ws), p->n};
 
     const double tt = static_cast<double>(step);
     const double bc1 = hp->bias_correction ? 1.0 - std::pow(hp->beta1, tt) : 1.0;

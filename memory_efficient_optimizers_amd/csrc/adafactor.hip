@@ -13,22 +13,22 @@ namespace meo {
 
 __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
     const int64_t tile = blockIdx.x;
-    const int k = find_tensor(t.tile0, t.n, tile);
+    const int k = tensor_of(t.tile_tensor, tile);
     const TDesc d = t.desc[k];
     const int64_t lt = tile - d.tile0;
     const float* ws = t.ws;
-    const float decay = ws[d.scal + kSlotDecay];
+    const float decay = ldf(ws + d.scal + kSlotDecay);
     const bool vec = d.vec, bf = d.gbf16, mom = a.has_beta1;
     const float b1 = a.beta1, omb1 = a.omb1;
 
     if (d.factored) {
         const TileRC p = tile_rc(d, lt);
-        const float coef = ws[d.bscal + p.b];
+        const float coef = ldf(ws + d.bscal + p.b);
         const int64_t mat = static_cast<int64_t>(p.b) * d.H * d.W;
         float cf[kVec];
 #pragma unroll
         for (int e = 0; e < kVec; ++e)
-            cf[e] = e < p.valid ? rsqrtf(d.c[static_cast<int64_t>(p.b) * d.W + p.col + e]) : 0.0f;
+            cf[e] = e < p.valid ? rsqrtf(ldf(d.c + static_cast<int64_t>(p.b) * d.W + p.col + e)) : 0.0f;
         const float* rrow = d.r + static_cast<int64_t>(p.b) * d.H;
         for (int i0 = 0; i0 < p.nrows; i0 += 4) {
             float g[4][kVec], x[4][kVec], m[4][kVec];
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
             for (int i = 0; i < 4; ++i) {
                 if (i0 + i < p.nrows) {
                     const int64_t off = mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col;
-                    const float rf = rsqrtf(rrow[p.row0 + i0 + i]) * coef;
+                    const float rf = rsqrtf(ldf(rrow + p.row0 + i0 + i)) * coef;
 #pragma unroll
                     for (int e = 0; e < kVec; ++e) {
                         const float u = (g[i][e] * cf[e]) * rf;
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
             }
         }
     } else {
-        const float coef = ws[d.bscal];
+        const float coef = ldf(ws + d.bscal);
         const int64_t base = lt * kFlatTile;
         for (int it = 0; it < kFlatIters; ++it) {
             const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;

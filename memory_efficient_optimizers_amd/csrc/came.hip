@@ -20,7 +20,7 @@ namespace meo {
 __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
     __shared__ __align__(16) float lds[kWaves * kTileCols];
     const int64_t tile = blockIdx.x;
-    const int k = find_tensor(t.tile0, t.n, tile);
+    const int k = tensor_of(t.tile_tensor, tile);
     const TDesc d = t.desc[k];
     const int64_t lt = tile - d.tile0;
     float* ws = t.ws;
@@ -30,12 +30,12 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
     if (d.factored) {
         const TileRC p = tile_rc(d, lt);
         const int lane = threadIdx.x & 63;
-        const float coef = ws[d.bscal + p.b];
+        const float coef = ldf(ws + d.bscal + p.b);
         const int64_t mat = static_cast<int64_t>(p.b) * d.H * d.W;
         float cf[kVec], cs[kVec];
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
-            cf[e] = e < p.valid ? rsqrtf(d.c[static_cast<int64_t>(p.b) * d.W + p.col + e]) : 0.0f;
+            cf[e] = e < p.valid ? rsqrtf(ldf(d.c + static_cast<int64_t>(p.b) * d.W + p.col + e)) : 0.0f;
             cs[e] = 0.0f;
         }
         const float* rrow = d.r + static_cast<int64_t>(p.b) * d.H;
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
                 if (i0 + i < p.nrows) {
                     const int row = p.row0 + i0 + i;
                     const int64_t off = mat + static_cast<int64_t>(row) * d.W + p.col;
-                    const float rf = rsqrtf(rrow[row]) * coef;
+                    const float rf = rsqrtf(ldf(rrow + row)) * coef;
                     float rs = 0.0f;
 #pragma unroll
                     for (int e = 0; e < kVec; ++e) {
@@ -68,14 +68,14 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
                     }
                     store_f8(d.m + off, p.valid, vec, m[i]);
                     rs = wave_sum(rs);
-                    if (lane == 0) rowpart[row] = rs;
+                    if (lane == 0) stf(rowpart + row, rs);
                 }
             }
         }
         write_colpart(d, ws, p, cs, lds);
     } else {
-        const float coef = ws[d.bscal];
-        const float decay = ws[d.scal + kSlotDecay];
+        const float coef = ldf(ws + d.bscal);
+        const float decay = ldf(ws + d.scal + kSlotDecay);
         const float lr = a.lr;
         const int64_t base = lt * kFlatTile;
         for (int it = 0; it < kFlatIters; ++it) {
@@ -105,20 +105,20 @@ void launch_came_mom(const Table& t, int64_t tiles, const CameArgs& a, hipStream
 
 __global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
     const int64_t tile = blockIdx.x;
-    const int k = find_tensor(t.tile0, t.n, tile);
+    const int k = tensor_of(t.tile_tensor, tile);
     const TDesc d = t.desc[k];
     if (!d.factored) return;  // 1-D tensors were finished by k_came_mom
     const int64_t lt = tile - d.tile0;
     const float* ws = t.ws;
     const bool vec = d.vec;
     const TileRC p = tile_rc(d, lt);
-    const float coef = ws[d.bscal + d.B + p.b];
-    const float decay = ws[d.scal + kSlotDecay];
+    const float coef = ldf(ws + d.bscal + d.B + p.b);
+    const float decay = ldf(ws + d.scal + kSlotDecay);
     const int64_t mat = static_cast<int64_t>(p.b) * d.H * d.W;
     float sc[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e)
-        sc[e] = e < p.valid ? rsqrtf(d.rc[static_cast<int64_t>(p.b) * d.W + p.col + e]) : 0.0f;
+        sc[e] = e < p.valid ? rsqrtf(ldf(d.rc + static_cast<int64_t>(p.b) * d.W + p.col + e)) : 0.0f;
     const float* rrow = d.rr + static_cast<int64_t>(p.b) * d.H;
     for (int i0 = 0; i0 < p.nrows; i0 += 4) {
         float x[4][kVec], m[4][kVec];
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
             if (i0 + i < p.nrows) {
                 const int row = p.row0 + i0 + i;
                 const int64_t off = mat + static_cast<int64_t>(row) * d.W + p.col;
-                const float sr = rsqrtf(rrow[row]) * coef;
+                const float sr = rsqrtf(ldf(rrow + row)) * coef;
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) x[i][e] = fmaf(-decay, x[i][e], x[i][e]) - (m[i][e] * sc[e]) * sr;
                 store_f8(d.x + off, p.valid, vec, x[i]);

@@ -68,9 +68,9 @@ struct TDesc {
 // Launch table of one call, device-resident.
 struct Table {
     const TDesc* desc;
-    const int64_t* tile0;  // [n+1] prefix sums of tile counts
-    const int64_t* fin0;   // [n+1] prefix sums of finalize items
-    float* ws;             // workspace base
+    const int32_t* tile_tensor;  // [tiles] tensor index of every tile
+    const int32_t* fin_tensor;   // [finalize items] tensor index of every finalize item
+    float* ws;                   // workspace base
     int32_t n;
 };
 
@@ -78,14 +78,9 @@ struct Table {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Largest k in [0, n) with pre[k] <= t (pre is non-decreasing, pre[n] > t).
-__device__ __forceinline__ int find_tensor(const int64_t* __restrict__ pre, int n, int64_t t) {
-    int lo = 0, hi = n;
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (pre[mid] <= t) lo = mid; else hi = mid;
-    }
-    return lo;
+// Tensor index of a block's tile: one scalar load from the launch table.
+__device__ __forceinline__ int tensor_of(const int32_t* __restrict__ table, int64_t item) {
+    return table[item];
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -125,57 +120,95 @@ __device__ __forceinline__ double block_sum_d(double a, double* lds) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Pointers read from the launch table are generic; every tensor lives in device
+// global memory, so accesses go through address-space-1 pointers (global_load /
+// global_store instead of flat_*).
+#define MEO_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const MEO_GLOBAL T* gld(const void* p) {
+    return (const MEO_GLOBAL T*)(p);
+}
+template <typename T>
+__device__ __forceinline__ MEO_GLOBAL T* gst(void* p) {
+    return (MEO_GLOBAL T*)(p);
+}
+
+// 16-byte loads; NT marks data read once (non-temporal hint).
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_u4(const void* p) {
+    if (NT) return __builtin_nontemporal_load(gld<u32x4>(p));
+    return *gld<u32x4>(p);
+}
+template <bool NT>
+__device__ __forceinline__ f32x4 ld_f4(const void* p) {
+    if (NT) return __builtin_nontemporal_load(gld<f32x4>(p));
+    return *gld<f32x4>(p);
+}
+
 // 8 gradient values starting at element `i` of `g`; `valid` (0..8) of them are in
 // range, the rest read as 0. Vector loads only when all 8 are valid and `vec`.
+template <bool NT = false>
 __device__ __forceinline__ void load_g8(const void* __restrict__ g, int64_t i, int valid,
                                         bool vec, bool bf16, float* f) {
     if (bf16) {
         const uint16_t* p = static_cast<const uint16_t*>(g) + i;
         if (vec && valid == kVec) {
-            uint4 u = *reinterpret_cast<const uint4*>(p);
+            const u32x4 u = ld_u4<NT>(p);
             f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
             f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
         } else {
+            const MEO_GLOBAL uint16_t* q = gld<uint16_t>(p);
 #pragma unroll
             for (int e = 0; e < kVec; ++e)
-                f[e] = e < valid ? __uint_as_float(static_cast<uint32_t>(p[e]) << 16) : 0.0f;
+                f[e] = e < valid ? __uint_as_float(static_cast<uint32_t>(q[e]) << 16) : 0.0f;
         }
     } else {
         const float* p = static_cast<const float*>(g) + i;
         if (vec && valid == kVec) {
-            float4 a = *reinterpret_cast<const float4*>(p);
-            float4 b = *reinterpret_cast<const float4*>(p + 4);
+            const f32x4 a = ld_f4<NT>(p);
+            const f32x4 b = ld_f4<NT>(p + 4);
             f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
             f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
         } else {
+            const MEO_GLOBAL float* q = gld<float>(p);
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) f[e] = e < valid ? p[e] : 0.0f;
+            for (int e = 0; e < kVec; ++e) f[e] = e < valid ? q[e] : 0.0f;
         }
     }
 }
 
+template <bool NT = false>
 __device__ __forceinline__ void load_f8(const float* __restrict__ p, int valid, bool vec, float* f) {
     if (vec && valid == kVec) {
-        float4 a = *reinterpret_cast<const float4*>(p);
-        float4 b = *reinterpret_cast<const float4*>(p + 4);
+        const f32x4 a = ld_f4<NT>(p);
+        const f32x4 b = ld_f4<NT>(p + 4);
         f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
         f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
     } else {
+        const MEO_GLOBAL float* q = gld<float>(p);
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) f[e] = e < valid ? p[e] : 0.0f;
+        for (int e = 0; e < kVec; ++e) f[e] = e < valid ? q[e] : 0.0f;
     }
 }
 
 __device__ __forceinline__ void store_f8(float* __restrict__ p, int valid, bool vec, const float* f) {
     if (vec && valid == kVec) {
-        *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
-        *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+        *gst<f32x4>(p) = f32x4{f[0], f[1], f[2], f[3]};
+        *gst<f32x4>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
     } else {
+        MEO_GLOBAL float* q = gst<float>(p);
 #pragma unroll
         for (int e = 0; e < kVec; ++e)
-            if (e < valid) p[e] = f[e];
+            if (e < valid) q[e] = f[e];
     }
 }
+
+// Scalar helpers for state vectors read through generic pointers.
+__device__ __forceinline__ float ldf(const float* p) { return *gld<float>(p); }
+__device__ __forceinline__ void stf(float* p, float v) { *gst<float>(p) = v; }
 
 __device__ __forceinline__ int clamp_valid(int64_t remaining) {
     return remaining >= kVec ? kVec : (remaining > 0 ? static_cast<int>(remaining) : 0);
@@ -190,7 +223,7 @@ __device__ __forceinline__ double row_mean(const TDesc& d, const float* __restri
     const int lane = threadIdx.x & 63;
     const float* sr = ws + d.sumr + static_cast<int64_t>(b) * d.nrc;
     double s = 0.0;
-    for (int j = lane; j < d.nrc; j += kLanes) s += static_cast<double>(sr[j]);
+    for (int j = lane; j < d.nrc; j += kLanes) s += static_cast<double>(ldf(sr + j));
     return wave_sum(s) / static_cast<double>(d.H);
 }
 
@@ -227,7 +260,7 @@ __device__ __forceinline__ void write_colpart(const TDesc& d, float* __restrict_
     for (int cc = threadIdx.x; cc < kTileCols; cc += kThreads) {
         const int cg = p.ct * kTileCols + cc;
         if (cg < d.W)
-            out[cg] = (lds[cc] + lds[kTileCols + cc]) + (lds[2 * kTileCols + cc] + lds[3 * kTileCols + cc]);
+            stf(out + cg, (lds[cc] + lds[kTileCols + cc]) + (lds[2 * kTileCols + cc] + lds[3 * kTileCols + cc]));
     }
 }
 

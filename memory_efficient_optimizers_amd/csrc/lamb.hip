@@ -21,7 +21,7 @@ __device__ __forceinline__ float lamb_dir(float m, float v, float x, const LambA
 __global__ __launch_bounds__(kThreads) void k_lamb_moments(Table t, LambArgs a) {
     __shared__ float lds[2 * kWaves];
     const int64_t tile = blockIdx.x;
-    const int k = find_tensor(t.tile0, t.n, tile);
+    const int k = tensor_of(t.tile_tensor, tile);
     const TDesc d = t.desc[k];
     const int64_t lt = tile - d.tile0;
     const bool vec = d.vec, bf = d.gbf16;
@@ -53,8 +53,8 @@ __global__ __launch_bounds__(kThreads) void k_lamb_moments(Table t, LambArgs a) 
     block_sum2(tx, td, lds);
     if (threadIdx.x == 0) {
         float* tp = t.ws + d.tilepart + 2 * lt;
-        tp[0] = tx;
-        tp[1] = td;
+        stf(tp, tx);
+        stf(tp + 1, td);
     }
 }
 
@@ -64,11 +64,11 @@ void launch_lamb_moments(const Table& t, int64_t tiles, const LambArgs& a, hipSt
 
 __global__ __launch_bounds__(kThreads) void k_lamb_apply(Table t, LambArgs a) {
     const int64_t tile = blockIdx.x;
-    const int k = find_tensor(t.tile0, t.n, tile);
+    const int k = tensor_of(t.tile_tensor, tile);
     const TDesc d = t.desc[k];
     const int64_t lt = tile - d.tile0;
     const bool vec = d.vec;
-    const float coef = t.ws[d.bscal];
+    const float coef = ldf(t.ws + d.bscal);
     const int64_t base = lt * kFlatTile;
     for (int it = 0; it < kFlatIters; ++it) {
         const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;

@@ -39,7 +39,7 @@ __device__ void stats_factored(const TDesc& d, int64_t lt, float* __restrict__ w
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (i0 + i < p.nrows)
-                load_g8(d.g, mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, bf, g[i]);
+                load_g8<true>(d.g, mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, bf, g[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (i0 + i < p.nrows) {
@@ -51,7 +51,7 @@ __device__ void stats_factored(const TDesc& d, int64_t lt, float* __restrict__ w
                     rs += q;
                 }
                 rs = wave_sum(rs);
-                if (lane == 0) rowpart[p.row0 + i0 + i] = rs;
+                if (lane == 0) stf(rowpart + p.row0 + i0 + i, rs);
             }
         }
     }
@@ -92,15 +92,15 @@ __device__ void stats_flat(const TDesc& d, int64_t lt, float* __restrict__ ws, c
     block_sum2(tu, tx, lds);
     if (threadIdx.x == 0) {
         float* tp = ws + d.tilepart + 2 * lt;
-        tp[0] = tu;
-        tp[1] = tx;
+        stf(tp, tu);
+        stf(tp + 1, tx);
     }
 }
 
 __global__ __launch_bounds__(kThreads) void k_stats(Table t, StatsArgs a) {
     __shared__ __align__(16) float lds[kWaves * kTileCols];
     const int64_t tile = blockIdx.x;
-    const int k = find_tensor(t.tile0, t.n, tile);
+    const int k = tensor_of(t.tile_tensor, tile);
     const TDesc d = t.desc[k];
     const int64_t lt = tile - d.tile0;
     if (d.factored) stats_factored(d, lt, t.ws, a, lds);
@@ -117,7 +117,7 @@ void launch_stats(const Table& t, int64_t tiles, const StatsArgs& a, hipStream_t
 __global__ __launch_bounds__(kThreads) void k_finalize(Table t, FinArgs a) {
     __shared__ double lds[kWaves];
     const int64_t item = blockIdx.x;
-    const int k = find_tensor(t.fin0, t.n, item);
+    const int k = tensor_of(t.fin_tensor, item);
     const TDesc d = t.desc[k];
     const int64_t li = item - d.fin0;
     const int per = d.nrc + d.ncc;
@@ -133,26 +133,26 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Table t, FinArgs a) {
         if (row < d.H) {
             const float* rp = ws + d.rowpart + static_cast<int64_t>(b) * d.tc * d.H + row;
             double s = 0.0;
-            for (int ct = 0; ct < d.tc; ++ct) s += static_cast<double>(rp[static_cast<int64_t>(ct) * d.H]);
+            for (int ct = 0; ct < d.tc; ++ct) s += static_cast<double>(ldf(rp + static_cast<int64_t>(ct) * d.H));
             float* dst = rs + static_cast<int64_t>(b) * d.H + row;
             const double mean = s / static_cast<double>(d.W);
-            rnew = beta != 0.0 ? beta * static_cast<double>(*dst) + omb * mean : mean;
+            rnew = beta != 0.0 ? beta * static_cast<double>(ldf(dst)) + omb * mean : mean;
             const float r32 = static_cast<float>(rnew);
-            *dst = r32;
+            stf(dst, r32);
             rnew = static_cast<double>(r32);  // the mean is taken over the stored values
         }
         const double tot = block_sum_d(rnew, lds);
-        if (threadIdx.x == 0) ws[d.sumr + static_cast<int64_t>(b) * d.nrc + j] = static_cast<float>(tot);
+        if (threadIdx.x == 0) stf(ws + d.sumr + static_cast<int64_t>(b) * d.nrc + j, static_cast<float>(tot));
     } else {
         const int col = (j - d.nrc) * kFinChunk + threadIdx.x;
         if (col < d.W) {
             const float* cp = ws + d.colpart + static_cast<int64_t>(b) * d.tr * d.W + col;
             double s = 0.0;
-            for (int rt = 0; rt < d.tr; ++rt) s += static_cast<double>(cp[static_cast<int64_t>(rt) * d.W]);
+            for (int rt = 0; rt < d.tr; ++rt) s += static_cast<double>(ldf(cp + static_cast<int64_t>(rt) * d.W));
             float* dst = cs + static_cast<int64_t>(b) * d.W + col;
             const double mean = s / static_cast<double>(d.H);
-            const double cnew = beta != 0.0 ? beta * static_cast<double>(*dst) + omb * mean : mean;
-            *dst = static_cast<float>(cnew);
+            const double cnew = beta != 0.0 ? beta * static_cast<double>(ldf(dst)) + omb * mean : mean;
+            stf(dst, static_cast<float>(cnew));
         }
     }
 }
@@ -166,7 +166,7 @@ void launch_finalize(const Table& t, int64_t items, const FinArgs& a, hipStream_
 __global__ __launch_bounds__(kThreads) void k_rms(Table t, int32_t need_x) {
     __shared__ float lds[2 * kWaves];
     const int64_t tile = blockIdx.x;
-    const int k = find_tensor(t.tile0, t.n, tile);
+    const int k = tensor_of(t.tile_tensor, tile);
     const TDesc d = t.desc[k];
     if (!d.factored) return;  // flat tensors finished their sums in k_stats
     const int64_t lt = tile - d.tile0;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_rms(Table t, int32_t need_x) {
     float cf[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e)
-        cf[e] = e < p.valid ? rsqrtf(d.c[static_cast<int64_t>(p.b) * d.W + p.col + e]) : 0.0f;
+        cf[e] = e < p.valid ? rsqrtf(ldf(d.c + static_cast<int64_t>(p.b) * d.W + p.col + e)) : 0.0f;
     const float* rrow = d.r + static_cast<int64_t>(p.b) * d.H;
     float su[kVec], sx[kVec];
 #pragma unroll
@@ -188,11 +188,11 @@ __global__ __launch_bounds__(kThreads) void k_rms(Table t, int32_t need_x) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (i0 + i < p.nrows)
-                load_g8(d.g, mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, bf, g[i]);
+                load_g8<true>(d.g, mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, bf, g[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (i0 + i < p.nrows) {
-                const float rf = rsqrtf(rrow[p.row0 + i0 + i]) * sm;
+                const float rf = rsqrtf(ldf(rrow + p.row0 + i0 + i)) * sm;
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) {
                     const float u = (g[i][e] * cf[e]) * rf;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void k_rms(Table t, int32_t need_x) {
             for (int i = 0; i < 8; ++i) {
                 if (i0 + i < p.nrows) {
                     float x[kVec];
-                    load_f8(d.x + mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, x);
+                    load_f8<true>(d.x + mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, x);
 #pragma unroll
                     for (int e = 0; e < kVec; ++e) sx[e] = fmaf(x[e], x[e], sx[e]);
                 }
@@ -216,8 +216,8 @@ __global__ __launch_bounds__(kThreads) void k_rms(Table t, int32_t need_x) {
     block_sum2(tu, tx, lds);
     if (threadIdx.x == 0) {
         float* tp = t.ws + d.tilepart + 2 * lt;
-        tp[0] = tu;
-        tp[1] = tx;
+        stf(tp, tu);
+        stf(tp + 1, tx);
     }
 }
 
@@ -233,8 +233,8 @@ __device__ __forceinline__ void tile_sums(const TDesc& d, const float* __restric
     double a = 0.0, b = 0.0;
     const float* tp = ws + d.tilepart;
     for (int j = threadIdx.x; j < d.ntiles; j += kThreads) {
-        a += static_cast<double>(tp[2 * j]);
-        b += static_cast<double>(tp[2 * j + 1]);
+        a += static_cast<double>(ldf(tp + 2 * j));
+        b += static_cast<double>(ldf(tp + 2 * j + 1));
     }
     su = block_sum_d(a, lds);
     __syncthreads();
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_scalars(Table t, ScalArgs a) {
         if (!d.factored) return;
         for (int b = w; b < d.B; b += kWaves) {
             const double mr = row_mean(d, ws, b);
-            if ((threadIdx.x & 63) == 0) bs[d.B + b] = static_cast<float>(a.lr * sqrt(mr));
+            if ((threadIdx.x & 63) == 0) stf(bs + d.B + b, static_cast<float>(a.lr * sqrt(mr)));
         }
         return;
     }
@@ -269,9 +269,9 @@ __global__ __launch_bounds__(kThreads) void k_scalars(Table t, ScalArgs a) {
         const double xn = sqrt(su), dn = sqrt(sx);
         const double trust = (xn > 0.0 && dn > 0.0) ? xn / dn : 1.0;
         if (threadIdx.x == 0) {
-            bs[0] = static_cast<float>(a.lr * trust);
-            scal[kSlotRmsX] = static_cast<float>(xn);
-            scal[kSlotNormD] = static_cast<float>(dn);
+            stf(bs + 0, static_cast<float>(a.lr * trust));
+            stf(scal + kSlotRmsX, static_cast<float>(xn));
+            stf(scal + kSlotNormD, static_cast<float>(dn));
         }
         return;
     }
@@ -281,23 +281,23 @@ __global__ __launch_bounds__(kThreads) void k_scalars(Table t, ScalArgs a) {
     if (a.mode == kScalAdafactor) {
         const double rms_x = sqrt(sx / n);
         alpha = a.rho * (a.scale_parameter ? fmax(a.eps2, rms_x) : 1.0);
-        if (threadIdx.x == 0) scal[kSlotRmsX] = static_cast<float>(rms_x);
+        if (threadIdx.x == 0) stf(scal + kSlotRmsX, static_cast<float>(rms_x));
     }
     const double coef = alpha / kappa;
     if (threadIdx.x == 0) {
-        scal[kSlotAlpha] = static_cast<float>(alpha);
-        scal[kSlotCoef] = static_cast<float>(coef);
-        scal[kSlotRmsU] = static_cast<float>(rms_u);
+        stf(scal + kSlotAlpha, static_cast<float>(alpha));
+        stf(scal + kSlotCoef, static_cast<float>(coef));
+        stf(scal + kSlotRmsU, static_cast<float>(rms_u));
         // Decoupled weight decay: Adafactor scales it by alpha, CAME by lr.
-        scal[kSlotDecay] = static_cast<float>(a.mode == kScalAdafactor ? a.wd * alpha : a.wd * a.lr);
+        stf(scal + kSlotDecay, static_cast<float>(a.mode == kScalAdafactor ? a.wd * alpha : a.wd * a.lr));
     }
     if (d.factored) {
         for (int b = w; b < d.B; b += kWaves) {
             const double mr = row_mean(d, ws, b);
-            if ((threadIdx.x & 63) == 0) bs[b] = static_cast<float>(coef * sqrt(mr));
+            if ((threadIdx.x & 63) == 0) stf(bs + b, static_cast<float>(coef * sqrt(mr)));
         }
     } else if (threadIdx.x == 0) {
-        bs[0] = static_cast<float>(coef);
+        stf(bs + 0, static_cast<float>(coef));
     }
 }
 

@@ -1,12 +1,20 @@
 """Shared helpers of the GPU parity tests: run the library and the oracle on the
 same seeded inputs and compare.
 
-Tolerance: for every output tensor (parameter and each state),
-    err = max_i |a_i - b_i| / max(|b_i|, 1e-2 * RMS(b))
-with a = the library's fp32 result and b = the oracle's fp64 result; the bar is
-1e-5 for fp32 outputs. The floor 1e-2 * RMS(b) only matters where a value
-crosses zero by cancellation (a parameter or first moment near 0), where an
-elementwise relative error has no meaning.
+Tolerance (the bar is a relative error of 1e-5 on every fp32 output tensor):
+
+* positive statistics (``exp_avg_sq*``, ``exp_avg_res*``): plain elementwise
+  relative error, max_i |a_i - b_i| / |b_i|. Every term of these averages is
+  positive, so nothing cancels and each element must hold 1e-5 on its own.
+* signed outputs (the parameter and ``exp_avg``): max_i |a_i - b_i| /
+  max(|b_i|, RMS(b)). These are sums of terms of both signs (an EMA of the
+  update, a parameter minus its step) and cross zero; fp32 storage and
+  arithmetic leave an absolute error of a few ulps of the *terms*, which are of
+  the order of the tensor's RMS, so near a zero crossing the error is measured
+  against that scale. (A plain fp32 run of the oracle's own arithmetic reaches
+  8e-5 if the floor is 1e-2 * RMS instead, and ~1e-6 with this one.)
+
+Here a = the library's fp32 result and b = the oracle's fp64 result.
 """
 from __future__ import annotations
 
@@ -23,15 +31,24 @@ from memory_efficient_optimizers_amd import _lib
 TOL_F32 = 1e-5
 
 
-def floored_rel_err(a, b) -> float:
+POSITIVE_KEYS = ("exp_avg_sq_row", "exp_avg_sq_col", "exp_avg_sq", "exp_avg_res_row", "exp_avg_res_col")
+
+
+def floored_rel_err(a, b, floor: float = 1.0) -> float:
+    """max_i |a_i - b_i| / max(|b_i|, floor * RMS(b)) (a zero denominator counts as 1)."""
     a = np.asarray(a, dtype=np.float64).reshape(-1)
     b = np.asarray(b, dtype=np.float64).reshape(-1)
     if b.size == 0:
         return 0.0
-    r = math.sqrt(float(np.mean(b * b)))
-    den = np.maximum(np.abs(b), 1e-2 * r)
+    r = math.sqrt(float(np.mean(b * b))) if floor > 0 else 0.0
+    den = np.maximum(np.abs(b), floor * r)
     den = np.where(den > 0, den, 1.0)
     return float(np.max(np.abs(a - b) / den))
+
+
+def output_err(key: str, a, b) -> float:
+    """The error of one output tensor under the rule above."""
+    return floored_rel_err(a, b, 0.0 if key in POSITIVE_KEYS else 1.0)
 
 
 def to64(t: torch.Tensor) -> np.ndarray:
@@ -100,9 +117,9 @@ class Run:
         torch.cuda.synchronize()
         out = {}
         for k, spec in enumerate(self.wl.specs):
-            out[f"{spec.name}:param"] = floored_rel_err(to64(self.params[k]), self.ox[k])
+            out[f"{spec.name}:param"] = output_err("param", to64(self.params[k]), self.ox[k])
             for key, arr in self.ost[k].items():
-                out[f"{spec.name}:{key}"] = floored_rel_err(to64(self.states[k][key]), arr)
+                out[f"{spec.name}:{key}"] = output_err(key, to64(self.states[k][key]), arr)
         return out
 
     def worst(self):
