@@ -178,15 +178,16 @@ def main() -> int:
 
     _lib.meo_profile_enable(True)
     _lib.meo_profile_collect()  # drop anything recorded before
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         t += 1
         call(t, stream)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
+    ev0, ev1 = evs[0], evs[-1]
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     _lib.meo_profile_enable(False)
     passes = _lib.meo_profile_collect()
     total_ms = ev0.elapsed_time(ev1)
@@ -195,7 +196,7 @@ def main() -> int:
 
     ab = algorithmic_bytes(wl)
     step_gbps = ab["step"] / (ms_step / 1e3) / 1e9
-    dominant = max((k for k in passes if k in ab), key=lambda k: passes[k]["ms"])
+    dominant = max((k for k in passes if k in ab), key=lambda k: passes[k]["ms"])  # the apply pass
     avg_ms = passes[dominant]["ms"] / passes[dominant]["launches"]
     achieved = ab[dominant] / (avg_ms / 1e3) / 1e9
     traffic = None
@@ -213,6 +214,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "step_ms": {"min": min(step_ms), "median": sorted(step_ms)[len(step_ms) // 2], "max": max(step_ms)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -35,7 +35,7 @@ EXPORTS = [
     "meo_lamb_step", "meo_last_error", "meo_release_plans", "meo_version", "meo_profile_enable",
     "meo_pass_name", "meo_profile_collect",
 ]
-MEO_NUM_PASSES = 9
+MEO_NUM_PASSES = 11
 
 
 class MeoError(RuntimeError):

@@ -17,7 +17,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/meo.h"
+#include "meo.h"
 #include "internal.h"
 
 using namespace meo;
@@ -57,13 +57,17 @@ bool overflow_numel(const meo_tensor& t, int64_t* numel) {
     return false;
 }
 
-// Geometry and workspace layout of one tensor (pointer-independent).
+// Geometry and workspace layout of one tensor. It depends on the shapes and on the
+// alignment of param and grad (which decides the statistics mode), not on states.
 struct Geo {
     int64_t numel = 0;
-    int32_t factored = 0, B = 1, H = 1, W = 1, tr = 1, tc = 0, nrc = 0, ncc = 0;
-    int64_t ntiles = 0, fin_items = 0;
-    int64_t rowpart = 0, colpart = 0, sumr = 0, tilepart = 0, bscal = 0, scal = 0;
+    int32_t mode = kFlat, cls = 0, B = 1, H = 1, W = 1, tr = 1, tc = 0, strips = 0, nrc = 0, ncc = 0;
+    int64_t tiles = 0;  // 2-D tiles (factored) or flat tiles
+    int32_t xchunks = 0;
+    int64_t rowpart = 0, colpart = 0, sumr = 0, tilepart = 0, xpart = 0, bscal = 0, scal = 0;
 };
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Fills geometry and workspace offsets; returns the workspace size in floats.
 // Tensors are assumed validated.
@@ -74,27 +78,42 @@ int64_t layout(int op, int32_t n, const meo_tensor* ts, std::vector<Geo>* out) {
         Geo g;
         overflow_numel(ts[k], &g.numel);
         if (g.numel > 0) {
-            g.factored = is_factored(op, ts[k]);
-            if (g.factored) {
+            if (is_factored(op, ts[k])) {
                 g.B = static_cast<int32_t>(ts[k].batch);
                 g.H = static_cast<int32_t>(ts[k].rows);
                 g.W = static_cast<int32_t>(ts[k].cols);
+                const bool rc_ok = g.W % kVec == 0 && g.W <= kRcMaxCols1 && aligned16(ts[k].param) &&
+                                   aligned16(ts[k].grad);
+                g.mode = rc_ok ? kRowComplete : kTiled;
+                g.cls = g.W <= kRcMaxCols0 ? 0 : 1;
                 g.tr = static_cast<int32_t>(ceil_div(g.H, kTileRows));
                 g.tc = static_cast<int32_t>(ceil_div(g.W, kTileCols));
-                g.ntiles = static_cast<int64_t>(g.B) * g.tr * g.tc;
+                g.strips = static_cast<int32_t>(ceil_div(g.H, kStripRows));
+                g.tiles = static_cast<int64_t>(g.B) * g.tr * g.tc;
                 g.nrc = static_cast<int32_t>(ceil_div(g.H, kFinChunk));
                 g.ncc = static_cast<int32_t>(ceil_div(g.W, kFinChunk));
-                g.fin_items = static_cast<int64_t>(g.B) * (g.nrc + g.ncc);
-                g.rowpart = off; off = align64(off + static_cast<int64_t>(g.B) * g.tc * g.H);
-                g.colpart = off; off = align64(off + static_cast<int64_t>(g.B) * g.tr * g.W);
-                g.sumr = off;    off = align64(off + static_cast<int64_t>(g.B) * g.nrc);
+                const bool tiled_stats = g.mode == kTiled || op == kOpCame;  // CAME's confidence is tiled
+                const int64_t B = g.B;
+                const int64_t colrows = std::max<int64_t>(tiled_stats ? g.tr : 0,
+                                                          g.mode == kRowComplete ? 2 * int64_t{g.strips} : 0);
+                const int64_t tparts = std::max<int64_t>(g.mode == kTiled ? g.tiles : 0,
+                                                         g.mode == kRowComplete ? B * g.strips : 0);
+                g.rowpart = off; off = align64(off + (tiled_stats ? B * g.tc * g.H : 0));
+                g.colpart = off; off = align64(off + B * colrows * g.W);
+                g.sumr = off;    off = align64(off + B * std::max(g.nrc, g.ncc));
+                g.tilepart = off; off = align64(off + 2 * tparts);
+                if (g.mode == kRowComplete) {
+                    g.xchunks = static_cast<int32_t>(ceil_div(g.numel, kFlatTile));
+                    g.xpart = off; off = align64(off + g.xchunks);
+                }
             } else {
-                g.ntiles = ceil_div(g.numel, kFlatTile);
-                g.tc = static_cast<int32_t>(g.ntiles);
+                g.mode = kFlat;
+                g.tiles = ceil_div(g.numel, kFlatTile);
+                g.tc = static_cast<int32_t>(g.tiles);
+                g.tilepart = off; off = align64(off + 2 * g.tiles);
             }
-            g.tilepart = off; off = align64(off + 2 * g.ntiles);
-            g.bscal = off;    off = align64(off + 2 * static_cast<int64_t>(g.B));
-            g.scal = off;     off = align64(off + kScalSlots);
+            g.bscal = off; off = align64(off + 2 * static_cast<int64_t>(g.B));
+            g.scal = off;  off = align64(off + kScalSlots);
         }
         if (out) (*out)[k] = g;
     }
@@ -238,15 +257,17 @@ int check_workspace(int op, int32_t n, const meo_tensor* ts, void* ws, size_t by
 
 // ----------------------------------------------------------------------------- plan cache
 
+// Item tables of the launches of one call.
+enum List { kListRc0 = 0, kListRc1, kListTiled, kListAll, kListFin1, kListFin2, kListCount };
+
 struct Plan {
     std::vector<uint8_t> key;
     int device = 0;
-    void* mem = nullptr;  // [n TDesc][tiles int32][finalize items int32]
+    void* mem = nullptr;  // [n TDesc][item tables]
     int32_t n = 0;
-    int64_t tiles = 0, fin_items = 0;
     const TDesc* desc = nullptr;
-    const int32_t* tile_tensor = nullptr;
-    const int32_t* fin_tensor = nullptr;
+    const int2* items[kListCount] = {};
+    int64_t count[kListCount] = {};
 };
 
 std::mutex g_mu;
@@ -261,8 +282,6 @@ void free_plan(Plan* p) {
     if (cur != p->device) (void)hipSetDevice(cur);
     delete p;
 }
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Builds (or finds) the launch table for this list. Returns nullptr with g_err set
 // on a HIP failure.
@@ -292,10 +311,11 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
     std::vector<Geo> geo;
     layout(op, n, ts, &geo);
     std::vector<TDesc> desc;
-    std::vector<int64_t> tile0(1, 0), fin0(1, 0);
+    std::vector<int2> lists[kListCount];
     for (int32_t k = 0; k < n; ++k) {
         const Geo& g = geo[k];
         if (g.numel == 0) continue;
+        const int32_t id = static_cast<int32_t>(desc.size());
         TDesc d;
         std::memset(&d, 0, sizeof d);
         d.x = static_cast<float*>(ts[k].param);
@@ -303,43 +323,62 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
         d.m = has_m ? sp[k].m : nullptr;
         d.v = sp[k].v; d.r = sp[k].r; d.c = sp[k].c; d.rr = sp[k].rr; d.rc = sp[k].rc;
         d.numel = g.numel;
-        d.tile0 = tile0.back();
-        d.fin0 = fin0.back();
         d.rowpart = g.rowpart; d.colpart = g.colpart; d.sumr = g.sumr;
-        d.tilepart = g.tilepart; d.bscal = g.bscal; d.scal = g.scal;
+        d.tilepart = g.tilepart; d.xpart = g.xpart; d.bscal = g.bscal; d.scal = g.scal;
+        d.xchunks = g.xchunks;
         d.B = g.B; d.H = g.H; d.W = g.W;
-        d.factored = g.factored;
+        d.mode = g.mode;
         d.gbf16 = ts[k].grad_dtype == MEO_BF16;
         bool vec = aligned16(d.x) && aligned16(d.g) && (!d.m || aligned16(d.m));
-        if (g.factored) vec = vec && (g.W % kVec == 0);
+        if (g.mode != kFlat) vec = vec && (g.W % kVec == 0);
         else vec = vec && (!d.v || aligned16(d.v));
         d.vec = vec;
-        d.tr = g.tr; d.tc = g.tc;
-        d.ntiles = static_cast<int32_t>(g.ntiles);
+        d.tr = g.tr; d.tc = g.tc; d.strips = g.strips;
         d.nrc = g.nrc; d.ncc = g.ncc;
         desc.push_back(d);
-        tile0.push_back(tile0.back() + g.ntiles);
-        fin0.push_back(fin0.back() + g.fin_items);
+        auto add = [&](int list, int64_t count) {
+            for (int64_t i = 0; i < count; ++i) lists[list].push_back(make_int2(id, static_cast<int>(i)));
+        };
+        if (g.mode == kFlat) {
+            add(kListAll, g.tiles);
+            if (op != kOpLamb) add(kListRc0, g.tiles);
+        } else {
+            add(kListAll, g.tiles);
+            if (g.mode == kRowComplete) {
+                // Strips interleaved with the chunks that stream X for sum(X^2), so
+                // that barrier-free streaming runs beside the strips' row reductions.
+                std::vector<int2>& L = lists[g.cls == 0 ? kListRc0 : kListRc1];
+                const int64_t ns = static_cast<int64_t>(g.B) * g.strips, nx = g.xchunks;
+                int64_t is = 0, ix = 0;
+                while (is < ns || ix < nx) {
+                    if (is < ns) L.push_back(make_int2(id, static_cast<int>(is++)));
+                    const int64_t want = (is * nx + ns - 1) / ns;  // x chunks due after `is` strips
+                    while (ix < nx && (ix < want || is == ns)) L.push_back(make_int2(id, static_cast<int>(-1 - ix++)));
+                }
+                add(kListFin1, static_cast<int64_t>(g.B) * g.ncc);
+            } else {
+                add(kListTiled, g.tiles);
+                add(kListFin1, static_cast<int64_t>(g.B) * (g.nrc + g.ncc));
+            }
+            if (op == kOpCame) add(kListFin2, static_cast<int64_t>(g.B) * (g.nrc + g.ncc));
+        }
     }
     const int32_t m = static_cast<int32_t>(desc.size());
-    const int64_t tiles = tile0.back(), items = fin0.back();
-    const size_t bytes_desc = (m * sizeof(TDesc) + 255) / 256 * 256;
-    const size_t bytes_tiles = (tiles * sizeof(int32_t) + 255) / 256 * 256;
-    const size_t bytes_fin = std::max<size_t>(items * sizeof(int32_t), 4);
-    std::vector<uint8_t> host(bytes_desc + bytes_tiles + bytes_fin, 0);
-    if (m) std::memcpy(host.data(), desc.data(), m * sizeof(TDesc));
-    int32_t* tt = reinterpret_cast<int32_t*>(host.data() + bytes_desc);
-    int32_t* ft = reinterpret_cast<int32_t*>(host.data() + bytes_desc + bytes_tiles);
-    for (int32_t k = 0; k < m; ++k) {
-        for (int64_t i = tile0[k]; i < tile0[k + 1]; ++i) tt[i] = k;
-        for (int64_t i = fin0[k]; i < fin0[k + 1]; ++i) ft[i] = k;
+    size_t offs[kListCount + 1];
+    size_t total = (m * sizeof(TDesc) + 255) / 256 * 256;
+    for (int l = 0; l < kListCount; ++l) {
+        offs[l] = total;
+        total += (lists[l].size() * sizeof(int2) + 255) / 256 * 256;
     }
+    total = std::max<size_t>(total, 256);
+    std::vector<uint8_t> host(total, 0);
+    if (m) std::memcpy(host.data(), desc.data(), m * sizeof(TDesc));
+    for (int l = 0; l < kListCount; ++l)
+        if (!lists[l].empty()) std::memcpy(host.data() + offs[l], lists[l].data(), lists[l].size() * sizeof(int2));
     Plan* p = new Plan;
     p->key = std::move(key);
     p->device = dev;
     p->n = m;
-    p->tiles = tiles;
-    p->fin_items = items;
     if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
         hipMemcpy(p->mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
         if (p->mem) (void)hipFree(p->mem);
@@ -349,8 +388,10 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
     }
     uint8_t* base = static_cast<uint8_t*>(p->mem);
     p->desc = reinterpret_cast<const TDesc*>(base);
-    p->tile_tensor = reinterpret_cast<const int32_t*>(base + bytes_desc);
-    p->fin_tensor = reinterpret_cast<const int32_t*>(base + bytes_desc + bytes_tiles);
+    for (int l = 0; l < kListCount; ++l) {
+        p->items[l] = reinterpret_cast<const int2*>(base + offs[l]);
+        p->count[l] = static_cast<int64_t>(lists[l].size());
+    }
     g_plans.push_front(p);
     while (g_plans.size() > kMaxPlans) {
         free_plan(g_plans.back());
@@ -381,10 +422,11 @@ std::vector<StatePtrs> state_ptrs(int op, int32_t n, const void* states) {
 // ----------------------------------------------------------------------------- pass timing
 
 enum Pass { kPassStats = 0, kPassFinalize, kPassRms, kPassScalars, kPassAfApply, kPassCameMom,
-            kPassCameApply, kPassLambMoments, kPassLambApply, kPassCount };
+            kPassCameApply, kPassLambMoments, kPassLambApply, kPassStatsWide, kPassStatsTiled, kPassCount };
 static_assert(kPassCount == MEO_NUM_PASSES, "pass table");
 const char* const kPassNames[kPassCount] = {"stats", "finalize", "rms", "scalars", "adafactor_apply",
-                                            "came_mom", "came_apply", "lamb_moments", "lamb_apply"};
+                                            "came_mom", "came_apply", "lamb_moments", "lamb_apply",
+                                            "stats_wide", "stats_tiled"};
 
 struct ProfRec { int pass; hipEvent_t a, b; };
 std::mutex g_prof_mu;
@@ -535,27 +577,41 @@ int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
     if (!p) return rc;
     if (p->n == 0) return MEO_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const Table t{p->desc, p->tile_tensor, p->fin_tensor, static_cast<float*>(ws), p->n};
+    float* w = static_cast<float*>(ws);
+    auto tab = [&](int l) { return Table{p->desc, p->items[l], w}; };
 
     const double tt = static_cast<double>(step);
     double rho;
     if (hp->relative_step) rho = std::fmin(hp->warmup_init ? 1e-6 * tt : 1e-2, 1.0 / std::sqrt(tt));
     else rho = hp->lr;
     const double b2 = 1.0 - std::pow(tt, hp->decay_rate);
+    const StatsArgs sa{static_cast<float>(hp->eps1), static_cast<float>(b2), static_cast<float>(1.0 - b2), 1,
+                       b2, 1.0 - b2};
 
     PassTimer pt(s);
-    launch_stats(t, p->tiles, StatsArgs{static_cast<float>(hp->eps1), static_cast<float>(b2),
-                                        static_cast<float>(1.0 - b2), 1}, s);
-    pt.mark(kPassStats);
-    launch_finalize(t, p->fin_items, FinArgs{b2, 0}, s);
+    if (p->count[kListRc0]) {
+        launch_rowstats(0, tab(kListRc0), p->count[kListRc0], sa, s);
+        pt.mark(kPassStats);
+    }
+    if (p->count[kListRc1]) {
+        launch_rowstats(1, tab(kListRc1), p->count[kListRc1], sa, s);
+        pt.mark(kPassStatsWide);
+    }
+    if (p->count[kListTiled]) {
+        launch_stats(tab(kListTiled), p->count[kListTiled], sa, s);
+        pt.mark(kPassStatsTiled);
+    }
+    launch_finalize(tab(kListFin1), p->count[kListFin1], FinArgs{b2, 0, 0}, s);
     pt.mark(kPassFinalize);
-    launch_rms(t, p->tiles, 1, s);
-    pt.mark(kPassRms);
-    launch_scalars(t, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, rho, hp->eps2, hp->clip_threshold,
-                                     hp->weight_decay, 0.0}, s);
+    if (p->count[kListTiled]) {
+        launch_rms(tab(kListTiled), p->count[kListTiled], 1, s);
+        pt.mark(kPassRms);
+    }
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, rho, hp->eps2,
+                                              hp->clip_threshold, hp->weight_decay, 0.0}, s);
     pt.mark(kPassScalars);
-    launch_af_apply(t, p->tiles, AfApplyArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1),
-                                             hp->has_beta1}, s);
+    launch_af_apply(tab(kListAll), p->count[kListAll],
+                    AfApplyArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1), hp->has_beta1}, s);
     pt.mark(kPassAfApply);
     return launch_status("adafactor step launch");
 }
@@ -610,26 +666,43 @@ int meo_came_step(const meo_came_hparams* hp, int64_t step, int32_t n, const meo
     if (!p) return rc;
     if (p->n == 0) return MEO_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const Table t{p->desc, p->tile_tensor, p->fin_tensor, static_cast<float*>(ws), p->n};
+    float* w = static_cast<float*>(ws);
+    auto tab = [&](int l) { return Table{p->desc, p->items[l], w}; };
+    const StatsArgs sa{static_cast<float>(hp->eps1), static_cast<float>(hp->beta2),
+                       static_cast<float>(1.0 - hp->beta2), 0, hp->beta2, 1.0 - hp->beta2};
 
     PassTimer pt(s);
-    launch_stats(t, p->tiles, StatsArgs{static_cast<float>(hp->eps1), static_cast<float>(hp->beta2),
-                                        static_cast<float>(1.0 - hp->beta2), 0}, s);
-    pt.mark(kPassStats);
-    launch_finalize(t, p->fin_items, FinArgs{hp->beta2, 0}, s);
+    if (p->count[kListRc0]) {
+        launch_rowstats(0, tab(kListRc0), p->count[kListRc0], sa, s);
+        pt.mark(kPassStats);
+    }
+    if (p->count[kListRc1]) {
+        launch_rowstats(1, tab(kListRc1), p->count[kListRc1], sa, s);
+        pt.mark(kPassStatsWide);
+    }
+    if (p->count[kListTiled]) {
+        launch_stats(tab(kListTiled), p->count[kListTiled], sa, s);
+        pt.mark(kPassStatsTiled);
+    }
+    launch_finalize(tab(kListFin1), p->count[kListFin1], FinArgs{hp->beta2, 0, 0}, s);
     pt.mark(kPassFinalize);
-    launch_rms(t, p->tiles, 0, s);
-    pt.mark(kPassRms);
-    launch_scalars(t, p->n, ScalArgs{kScalCame1, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay, hp->lr}, s);
+    if (p->count[kListTiled]) {
+        launch_rms(tab(kListTiled), p->count[kListTiled], 0, s);
+        pt.mark(kPassRms);
+    }
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame1, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
+                                              hp->lr}, s);
     pt.mark(kPassScalars);
-    launch_came_mom(t, p->tiles, CameArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1),
-                                          static_cast<float>(hp->eps2), static_cast<float>(hp->lr)}, s);
+    launch_came_mom(tab(kListAll), p->count[kListAll],
+                    CameArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1),
+                             static_cast<float>(hp->eps2), static_cast<float>(hp->lr)}, s);
     pt.mark(kPassCameMom);
-    launch_finalize(t, p->fin_items, FinArgs{hp->beta3, 1}, s);
+    launch_finalize(tab(kListFin2), p->count[kListFin2], FinArgs{hp->beta3, 1, 1}, s);
     pt.mark(kPassFinalize);
-    launch_scalars(t, p->n, ScalArgs{kScalCame2, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay, hp->lr}, s);
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame2, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
+                                              hp->lr}, s);
     pt.mark(kPassScalars);
-    launch_came_apply(t, p->tiles, s);
+    launch_came_apply(tab(kListAll), p->count[kListAll], s);
     pt.mark(kPassCameApply);
     return launch_status("came step launch");
 }
@@ -672,7 +745,9 @@ int meo_lamb_step(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo
     if (!p) return rc;
     if (p->n == 0) return MEO_OK;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const Table t{p->desc, p->tile_tensor, p->fin_tensor, static_cast<float*>(ws), p->n};
+    float* w = static_cast<float*>(ws);
+    const Table t{p->desc, p->items[kListAll], w};
+    const int64_t tiles = p->count[kListAll];
 
     const double tt = static_cast<double>(step);
     const double bc1 = hp->bias_correction ? 1.0 - std::pow(hp->beta1, tt) : 1.0;
@@ -682,11 +757,11 @@ int meo_lamb_step(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo
                       static_cast<float>(1.0 / bc1), static_cast<float>(1.0 / bc2),
                       static_cast<float>(hp->eps), static_cast<float>(hp->weight_decay)};
     PassTimer pt(s);
-    launch_lamb_moments(t, p->tiles, la, s);
+    launch_lamb_moments(t, tiles, la, s);
     pt.mark(kPassLambMoments);
-    launch_scalars(t, p->n, ScalArgs{kScalLamb, 0, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalLamb, 0, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
     pt.mark(kPassScalars);
-    launch_lamb_apply(t, p->tiles, la, s);
+    launch_lamb_apply(t, tiles, la, s);
     pt.mark(kPassLambApply);
     return launch_status("lamb step launch");
 }

@@ -12,16 +12,15 @@
 namespace meo {
 
 __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
-    const int64_t tile = blockIdx.x;
-    const int k = tensor_of(t.tile_tensor, tile);
-    const TDesc d = t.desc[k];
-    const int64_t lt = tile - d.tile0;
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    const int lt = it.y;
     const float* ws = t.ws;
     const float decay = ldf(ws + d.scal + kSlotDecay);
     const bool vec = d.vec, bf = d.gbf16, mom = a.has_beta1;
     const float b1 = a.beta1, omb1 = a.omb1;
 
-    if (d.factored) {
+    if (d.mode != kFlat) {
         const TileRC p = tile_rc(d, lt);
         const float coef = ldf(ws + d.bscal + p.b);
         const int64_t mat = static_cast<int64_t>(p.b) * d.H * d.W;
@@ -63,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
         }
     } else {
         const float coef = ldf(ws + d.bscal);
-        const int64_t base = lt * kFlatTile;
+        const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
         for (int it = 0; it < kFlatIters; ++it) {
             const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
             const int valid = clamp_valid(d.numel - i);
@@ -89,8 +88,8 @@ __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
     }
 }
 
-void launch_af_apply(const Table& t, int64_t tiles, const AfApplyArgs& a, hipStream_t s) {
-    if (tiles > 0) hipLaunchKernelGGL(k_af_apply, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t, a);
+void launch_af_apply(const Table& t, int64_t n, const AfApplyArgs& a, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_af_apply, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
 }
 
 }  // namespace meo

@@ -19,15 +19,14 @@ namespace meo {
 
 __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
     __shared__ __align__(16) float lds[kWaves * kTileCols];
-    const int64_t tile = blockIdx.x;
-    const int k = tensor_of(t.tile_tensor, tile);
-    const TDesc d = t.desc[k];
-    const int64_t lt = tile - d.tile0;
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    const int lt = it.y;
     float* ws = t.ws;
     const bool vec = d.vec, bf = d.gbf16;
     const float b1 = a.beta1, omb1 = a.omb1;
 
-    if (d.factored) {
+    if (d.mode != kFlat) {
         const TileRC p = tile_rc(d, lt);
         const int lane = threadIdx.x & 63;
         const float coef = ldf(ws + d.bscal + p.b);
@@ -77,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
         const float coef = ldf(ws + d.bscal);
         const float decay = ldf(ws + d.scal + kSlotDecay);
         const float lr = a.lr;
-        const int64_t base = lt * kFlatTile;
+        const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
         for (int it = 0; it < kFlatIters; ++it) {
             const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
             const int valid = clamp_valid(d.numel - i);
@@ -99,16 +98,15 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
     }
 }
 
-void launch_came_mom(const Table& t, int64_t tiles, const CameArgs& a, hipStream_t s) {
-    if (tiles > 0) hipLaunchKernelGGL(k_came_mom, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t, a);
+void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_came_mom, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
 }
 
 __global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
-    const int64_t tile = blockIdx.x;
-    const int k = tensor_of(t.tile_tensor, tile);
-    const TDesc d = t.desc[k];
-    if (!d.factored) return;  // 1-D tensors were finished by k_came_mom
-    const int64_t lt = tile - d.tile0;
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    if (d.mode == kFlat) return;  // 1-D tensors were finished by k_came_mom
+    const int lt = it.y;
     const float* ws = t.ws;
     const bool vec = d.vec;
     const TileRC p = tile_rc(d, lt);
@@ -144,8 +142,8 @@ __global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
     }
 }
 
-void launch_came_apply(const Table& t, int64_t tiles, hipStream_t s) {
-    if (tiles > 0) hipLaunchKernelGGL(k_came_apply, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t);
+void launch_came_apply(const Table& t, int64_t n, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_came_apply, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t);
 }
 
 }  // namespace meo

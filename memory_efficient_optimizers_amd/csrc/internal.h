@@ -1,15 +1,21 @@
 // Internal structures and device helpers of the optimizer-step library.
 //
-// Work decomposition shared by every pass:
-//   * A factored tensor, viewed as [B, H, W], is cut into tiles of kTileRows rows
-//     x kTileCols columns inside one matrix. A block of 256 threads (4 wave64s)
-//     owns one tile: each lane owns 8 adjacent columns (one 16-byte bf16 or two
-//     16-byte fp32 loads per row), each wave owns kRowsPerWave rows.
+// Work decomposition:
+//   * Apply-style passes cut a factored tensor, viewed as [B, H, W], into tiles of
+//     kTileRows rows x kTileCols columns inside one matrix. A block of 256 threads
+//     (4 wave64s) owns one tile: each lane owns 8 adjacent columns (one 16-byte
+//     bf16 or two 16-byte fp32 accesses per row), each wave kRowsPerWave rows.
+//   * The first (statistics) pass of a factored tensor whose rows fit a block
+//     ("row-complete" tensors: 16-byte aligned, W % 8 == 0, W <= 12288) uses
+//     strips of kStripRows full rows: the block sees whole rows, so it finishes
+//     the row statistic itself and can weight the column sums by it. Other
+//     factored tensors use the 2-D tiles for their statistics too (and then need a
+//     second read of G for the RMS of the update).
 //   * A flat tensor (1-D Adafactor/CAME tensors, every LAMB tensor) is cut into
 //     tiles of kFlatTile consecutive elements; each thread owns 8 adjacent
 //     elements per iteration.
-//   * The tiles of every tensor in a call form one grid; a block finds its tensor
-//     by binary search over the prefix sums of tile counts (launch table).
+//   * Every launch reads a table of (tensor, tile-within-tensor) pairs, one per
+//     block, built on the host for the whole tensor list.
 // Every cross-block reduction is two-stage with a fixed order, so results are
 // bitwise reproducible and independent of what else is in the list.
 #pragma once
@@ -22,18 +28,26 @@ namespace meo {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kLanes = 64;
-constexpr int kVec = 8;                       // elements per lane per row/iteration
-constexpr int kTileCols = kLanes * kVec;      // 512
+constexpr int kVec = 8;                          // elements per lane per row/iteration
+constexpr int kTileCols = kLanes * kVec;         // 512
 constexpr int kRowsPerWave = 16;
-constexpr int kTileRows = kWaves * kRowsPerWave;  // 64
+constexpr int kTileRows = kWaves * kRowsPerWave; // 64
 constexpr int kFlatIters = 16;
 constexpr int kFlatTile = kThreads * kVec * kFlatIters;  // 32768
-constexpr int kFinChunk = 256;                // rows or columns per finalize block
-constexpr int kScalSlots = 8;                 // floats of per-tensor scalars
+constexpr int kFinChunk = 256;                   // rows or columns per finalize block
+constexpr int kScalSlots = 8;                    // floats of per-tensor scalars
+constexpr int kStripRows = 64;                   // rows per strip of the row-complete pass
+// Widest row of each row-complete class (class 0: 256 threads x 2 groups of 8
+// columns; class 1: 512 threads x 3 groups).
+constexpr int kRcMaxCols0 = 256 * 8 * 2;  // 4096
+constexpr int kRcMaxCols1 = 512 * 8 * 3;  // 12288
 
 // Per-tensor scalar slots in the workspace.
 enum ScalSlot { kSlotAlpha = 0, kSlotCoef = 1, kSlotDecay = 2, kSlotRmsU = 3, kSlotRmsX = 4,
                 kSlotNormD = 5 };
+
+// How a tensor's statistics are gathered.
+enum Mode { kFlat = 0, kRowComplete = 1, kTiled = 2 };
 
 // Device-side descriptor of one tensor of the call (built on the host, cached).
 struct TDesc {
@@ -46,42 +60,37 @@ struct TDesc {
     float* rr;        // CAME confidence row statistic [B*H]
     float* rc;        // CAME confidence column statistic [B*W]
     int64_t numel;
-    int64_t tile0;    // first global tile of this tensor
-    int64_t fin0;     // first finalize item of this tensor
     // workspace offsets, in floats
-    int64_t rowpart;  // [B][tc][H]   row sums per column tile
-    int64_t colpart;  // [B][tr][W]   column sums per row tile
-    int64_t sumr;     // [B][nrc]     sums of the new row statistic per finalize chunk
-    int64_t tilepart; // [ntiles][2]  per-tile partial sums for the per-tensor scalars
-    int64_t bscal;    // [2][B]       per-matrix coefficients
+    int64_t rowpart;  // tiled: [B][tc][H] row sums per column tile
+    int64_t colpart;  // tiled: [B][tr][W] column sums per row tile;
+                      // row-complete: [B][strips][2][W] sums of Q and of G^2/R per strip
+    int64_t sumr;     // tiled: [B][nrc] sums of the new row statistic per finalize chunk;
+                      // row-complete: [B][ncc] sums of S_j / C_j per finalize chunk
+    int64_t tilepart; // [tiles][2] per-tile partial sums for the per-tensor scalars
+    int64_t xpart;    // row-complete: [xchunks] sums of X^2 per chunk of kFlatTile elements
+    int64_t bscal;    // [2][B] per-matrix coefficients
     int64_t scal;     // [kScalSlots] per-tensor scalars
     int32_t B, H, W;
-    int32_t factored; // 1: [B,H,W] factored statistics; 0: flat
+    int32_t mode;     // Mode
     int32_t gbf16;    // gradient dtype is bf16
     int32_t vec;      // 16-byte vector accesses are valid
-    int32_t tr, tc;   // tiles per matrix along rows / columns (flat: tr = 1, tc = ntiles)
-    int32_t ntiles;
+    int32_t tr, tc;   // 2-D tiles per matrix along rows / columns (flat: tr = 1, tc = tiles)
+    int32_t strips;   // row-complete strips per matrix
     int32_t nrc, ncc; // finalize chunks per matrix along rows / columns
-    int32_t pad;
+    int32_t xchunks;  // row-complete: chunks of the parameter for sum(X^2)
 };
 
-// Launch table of one call, device-resident.
+// One launch: its (tensor, local tile) items and the shared descriptors.
 struct Table {
     const TDesc* desc;
-    const int32_t* tile_tensor;  // [tiles] tensor index of every tile
-    const int32_t* fin_tensor;   // [finalize items] tensor index of every finalize item
-    float* ws;                   // workspace base
-    int32_t n;
+    const int2* items;  // [grid] x = tensor index, y = tile (or finalize item) within the tensor;
+                        // in the row-complete first pass y < 0 marks chunk -1 - y of sum(X^2)
+    float* ws;          // workspace base
 };
 
 // ----------------------------------------------------------------------------- helpers
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// Tensor index of a block's tile: one scalar load from the launch table.
-__device__ __forceinline__ int tensor_of(const int32_t* __restrict__ table, int64_t item) {
-    return table[item];
-}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -95,17 +104,21 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-// Sum of two per-thread values over the block, in a fixed order; result valid in
-// thread 0. `lds` must hold 2 * kWaves floats.
+// Sum over the block (NW waves) of two per-thread values, in a fixed order;
+// result valid in thread 0. `lds` holds 2 * NW floats.
+template <int NW = kWaves>
 __device__ __forceinline__ void block_sum2(float& a, float& b, float* lds) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     a = wave_sum(a);
     b = wave_sum(b);
-    if (lane == 0) { lds[w] = a; lds[kWaves + w] = b; }
+    if (lane == 0) { lds[w] = a; lds[NW + w] = b; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        a = (lds[0] + lds[1]) + (lds[2] + lds[3]);
-        b = (lds[4] + lds[5]) + (lds[6] + lds[7]);
+        float sa = lds[0], sb = lds[NW];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) { sa += lds[i]; sb += lds[NW + i]; }
+        a = sa;
+        b = sb;
     }
 }
 
@@ -148,6 +161,11 @@ __device__ __forceinline__ f32x4 ld_f4(const void* p) {
     return *gld<f32x4>(p);
 }
 
+__device__ __forceinline__ void bf16x8(const u32x4 u, float* f) {
+    f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+    f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+}
+
 // 8 gradient values starting at element `i` of `g`; `valid` (0..8) of them are in
 // range, the rest read as 0. Vector loads only when all 8 are valid and `vec`.
 template <bool NT = false>
@@ -156,9 +174,7 @@ __device__ __forceinline__ void load_g8(const void* __restrict__ g, int64_t i, i
     if (bf16) {
         const uint16_t* p = static_cast<const uint16_t*>(g) + i;
         if (vec && valid == kVec) {
-            const u32x4 u = ld_u4<NT>(p);
-            f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
-            f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+            bf16x8(ld_u4<NT>(p), f);
         } else {
             const MEO_GLOBAL uint16_t* q = gld<uint16_t>(p);
 #pragma unroll
@@ -206,7 +222,7 @@ __device__ __forceinline__ void store_f8(float* __restrict__ p, int valid, bool 
     }
 }
 
-// Scalar helpers for state vectors read through generic pointers.
+// Scalar accesses of state vectors and workspace through generic pointers.
 __device__ __forceinline__ float ldf(const float* p) { return *gld<float>(p); }
 __device__ __forceinline__ void stf(float* p, float v) { *gst<float>(p) = v; }
 
@@ -214,12 +230,16 @@ __device__ __forceinline__ int clamp_valid(int64_t remaining) {
     return remaining >= kVec ? kVec : (remaining > 0 ? static_cast<int>(remaining) : 0);
 }
 
+__device__ __forceinline__ float sum8(const float* a) {
+    return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
 // ----------------------------------------------------------------------------- tile helpers
 
-// Mean over the rows of matrix b of the (already updated) row statistic, from the
-// per-chunk sums written by the finalize pass. Every lane of the calling wave gets
-// the same value, and every caller the same bits (fixed order).
-__device__ __forceinline__ double row_mean(const TDesc& d, const float* __restrict__ ws, int b) {
+// Mean over the rows of matrix b of the (already updated) row statistic of a
+// tiled tensor, from the per-chunk sums written by the finalize pass. Every lane of
+// the calling wave gets the same value, and every caller the same bits.
+__device__ __forceinline__ double row_mean_tiled(const TDesc& d, const float* __restrict__ ws, int b) {
     const int lane = threadIdx.x & 63;
     const float* sr = ws + d.sumr + static_cast<int64_t>(b) * d.nrc;
     double s = 0.0;
@@ -227,15 +247,24 @@ __device__ __forceinline__ double row_mean(const TDesc& d, const float* __restri
     return wave_sum(s) / static_cast<double>(d.H);
 }
 
-struct TileRC {   // this thread's position inside a factored tile
+// The same for a row-complete tensor, whose strips summed their new row statistic.
+__device__ __forceinline__ double row_mean_rc(const TDesc& d, const float* __restrict__ ws, int b) {
+    const int lane = threadIdx.x & 63;
+    const float* tp = ws + d.tilepart + 2 * static_cast<int64_t>(b) * d.strips;
+    double s = 0.0;
+    for (int j = lane; j < d.strips; j += kLanes) s += static_cast<double>(ldf(tp + 2 * j));
+    return wave_sum(s) / static_cast<double>(d.H);
+}
+
+struct TileRC {   // this thread's position inside a 2-D tile
     int b, rt, ct, col, valid, row0, nrows;
 };
 
-__device__ __forceinline__ TileRC tile_rc(const TDesc& d, int64_t lt) {
+__device__ __forceinline__ TileRC tile_rc(const TDesc& d, int lt) {
     TileRC p;
     const int per = d.tr * d.tc;
-    p.b = static_cast<int>(lt / per);
-    const int rem = static_cast<int>(lt - static_cast<int64_t>(p.b) * per);
+    p.b = lt / per;
+    const int rem = lt - p.b * per;
     p.rt = rem / d.tc;
     p.ct = rem - p.rt * d.tc;
     const int w = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -246,8 +275,8 @@ __device__ __forceinline__ TileRC tile_rc(const TDesc& d, int64_t lt) {
     return p;
 }
 
-// Column partial sums of one tile: the 4 waves' per-lane sums are combined in a
-// fixed order through LDS (kWaves * kTileCols floats) and written to
+// Column partial sums of one 2-D tile: the 4 waves' per-lane sums are combined in
+// a fixed order through LDS (kWaves * kTileCols floats) and written to
 // colpart[b][rt][col].
 __device__ __forceinline__ void write_colpart(const TDesc& d, float* __restrict__ ws, const TileRC& p,
                                               const float* cs, float* lds) {
@@ -264,22 +293,21 @@ __device__ __forceinline__ void write_colpart(const TDesc& d, float* __restrict_
     }
 }
 
-__device__ __forceinline__ float sum8(const float* a) {
-    return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-}
-
 // ----------------------------------------------------------------------------- launchers
 
 // Arguments of the shared passes.
-struct StatsArgs {      // factored statistics of Q = G^2 + eps1; 1-D full statistic
+struct StatsArgs {      // statistics of Q = G^2 + eps1
     float eps1;
-    float beta;         // EMA weight of the old 1-D statistic (beta2t or beta2); 0: not read
+    float beta;         // EMA weight of the old statistic (beta2t or beta2); 0: not read
     float omb;          // 1 - beta, rounded from fp64
-    int32_t need_x;     // 1-D tiles also accumulate sum(x^2)
+    int32_t need_x;     // also accumulate sum(x^2)
+    double dbeta;       // the same weights in fp64 (row statistic of row-complete strips)
+    double domb;
 };
 struct FinArgs {        // row/column finalize: s <- beta*s + (1-beta)*mean(partials)
     double beta;        // 0: the old statistic is not read
     int32_t which;      // 0: squared-gradient statistic (r, c); 1: CAME confidence (rr, rc)
+    int32_t tiled_all;  // 1: every factored tensor has tiled partials (CAME's second statistic)
 };
 enum ScalMode { kScalAdafactor = 0, kScalCame1 = 1, kScalCame2 = 2, kScalLamb = 3 };
 struct ScalArgs {
@@ -306,14 +334,17 @@ struct LambArgs {
     float eps, wd;
 };
 
-void launch_stats(const Table& t, int64_t tiles, const StatsArgs& a, hipStream_t s);
-void launch_finalize(const Table& t, int64_t items, const FinArgs& a, hipStream_t s);
-void launch_rms(const Table& t, int64_t tiles, int32_t need_x, hipStream_t s);
-void launch_scalars(const Table& t, int32_t n, const ScalArgs& a, hipStream_t s);
-void launch_af_apply(const Table& t, int64_t tiles, const AfApplyArgs& a, hipStream_t s);
-void launch_came_mom(const Table& t, int64_t tiles, const CameArgs& a, hipStream_t s);
-void launch_came_apply(const Table& t, int64_t tiles, hipStream_t s);
-void launch_lamb_moments(const Table& t, int64_t tiles, const LambArgs& a, hipStream_t s);
-void launch_lamb_apply(const Table& t, int64_t tiles, const LambArgs& a, hipStream_t s);
+// Row-complete first pass, class 0 (W <= 4096, also the flat tensors' first pass)
+// and class 1 (W <= 12288).
+void launch_rowstats(int cls, const Table& t, int64_t n, const StatsArgs& a, hipStream_t s);
+void launch_stats(const Table& t, int64_t n, const StatsArgs& a, hipStream_t s);
+void launch_finalize(const Table& t, int64_t n, const FinArgs& a, hipStream_t s);
+void launch_rms(const Table& t, int64_t n, int32_t need_x, hipStream_t s);
+void launch_scalars(const TDesc* desc, float* ws, int32_t n, const ScalArgs& a, hipStream_t s);
+void launch_af_apply(const Table& t, int64_t n, const AfApplyArgs& a, hipStream_t s);
+void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, hipStream_t s);
+void launch_came_apply(const Table& t, int64_t n, hipStream_t s);
+void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, hipStream_t s);
+void launch_lamb_apply(const Table& t, int64_t n, const LambArgs& a, hipStream_t s);
 
 }  // namespace meo

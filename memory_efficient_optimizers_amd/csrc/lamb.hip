@@ -20,12 +20,11 @@ __device__ __forceinline__ float lamb_dir(float m, float v, float x, const LambA
 
 __global__ __launch_bounds__(kThreads) void k_lamb_moments(Table t, LambArgs a) {
     __shared__ float lds[2 * kWaves];
-    const int64_t tile = blockIdx.x;
-    const int k = tensor_of(t.tile_tensor, tile);
-    const TDesc d = t.desc[k];
-    const int64_t lt = tile - d.tile0;
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    const int lt = it.y;
     const bool vec = d.vec, bf = d.gbf16;
-    const int64_t base = lt * kFlatTile;
+    const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
     float sx[kVec], sd[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) { sx[e] = 0.0f; sd[e] = 0.0f; }
@@ -52,24 +51,23 @@ __global__ __launch_bounds__(kThreads) void k_lamb_moments(Table t, LambArgs a) 
     float tx = sum8(sx), td = sum8(sd);
     block_sum2(tx, td, lds);
     if (threadIdx.x == 0) {
-        float* tp = t.ws + d.tilepart + 2 * lt;
+        float* tp = t.ws + d.tilepart + 2 * static_cast<int64_t>(lt);
         stf(tp, tx);
         stf(tp + 1, td);
     }
 }
 
-void launch_lamb_moments(const Table& t, int64_t tiles, const LambArgs& a, hipStream_t s) {
-    if (tiles > 0) hipLaunchKernelGGL(k_lamb_moments, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t, a);
+void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_lamb_moments, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
 }
 
 __global__ __launch_bounds__(kThreads) void k_lamb_apply(Table t, LambArgs a) {
-    const int64_t tile = blockIdx.x;
-    const int k = tensor_of(t.tile_tensor, tile);
-    const TDesc d = t.desc[k];
-    const int64_t lt = tile - d.tile0;
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    const int lt = it.y;
     const bool vec = d.vec;
     const float coef = ldf(t.ws + d.bscal);
-    const int64_t base = lt * kFlatTile;
+    const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
     for (int it = 0; it < kFlatIters; ++it) {
         const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
         const int valid = clamp_valid(d.numel - i);
@@ -84,8 +82,8 @@ __global__ __launch_bounds__(kThreads) void k_lamb_apply(Table t, LambArgs a) {
     }
 }
 
-void launch_lamb_apply(const Table& t, int64_t tiles, const LambArgs& a, hipStream_t s) {
-    if (tiles > 0) hipLaunchKernelGGL(k_lamb_apply, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t, a);
+void launch_lamb_apply(const Table& t, int64_t n, const LambArgs& a, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_lamb_apply, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
 }
 
 }  // namespace meo

@@ -1,31 +1,265 @@
 // Passes shared by Adafactor and CAME (and the scalar pass shared with LAMB).
 //
-//   k_stats     read G once: per-tile row sums and column sums of Q = G^2 + eps1
-//               (factored tensors), or the full 1-D statistic V <- beta V +
-//               (1-beta) Q with per-tile sums of U^2 = G^2 / V (and x^2).
-//   k_finalize  fold the tile partials into the row and column statistics:
-//               s <- beta s + (1 - beta) mean, in fp64, fixed order; per-chunk sums
-//               of the new row statistic for its mean.
-//   k_rms       read G (and X) again: per-tile sums of U^2 with
-//               U = G rsqrt(R_i / mean(R)) rsqrt(C_j) rebuilt on the fly (the
-//               [H, W] estimate is never stored), and of x^2.
-//   k_scalars   one block per tensor: RMS(U), RMS(X), the clip divisor and the
-//               per-matrix coefficients used by the apply passes.
-//
 // The factored statistics follow the "four optimizers" table of the Colossal-AI
 // distributed-optimizers page (second moment approximated by row * col) and its
 // section "Step 3" (row statistic [H], column statistic [W], full statistic for
 // 1-D tensors); RMS clipping and the step-size rules follow the note after its
-// "Step 5".
+// "Step 5". With Q = G^2 + eps1, R_i = mean_j Q_ij, C_j = mean_i Q_ij (EMA'd) and
+// V_ij = R_i C_j / mean(R), the update U = G / sqrt(V) has
+//     sum U^2 = mean(R) * sum_j S_j / C_j,   S_j = sum_i G_ij^2 / R_i,
+// which is what lets a single read of G give both statistics and RMS(U) once a
+// block holds whole rows.
+//
+//   k_rowstats0/1  row-complete tensors: one read of G per strip of full rows:
+//                  new R_i (stored), per-strip column sums of Q and of G^2 / R_i
+//                  and the strip's sum of R_i; interleaved chunk blocks stream X
+//                  for sum(X^2). Flat tensors (with class 0): V <- beta V +
+//                  (1-beta) Q, sums of G^2 / V and X^2.
+//   k_stats        tiled tensors: per-tile row sums and column sums of Q.
+//   k_finalize     column (and, tiled, row) statistics from the partials in fp64,
+//                  fixed order; row-complete: per-chunk sums of S_j / C_j;
+//                  tiled: per-chunk sums of the new row statistic.
+//   k_rms          tiled tensors only: second read of G (and X) for sum U^2, X^2.
+//   k_scalars      one block per tensor: RMS(U), RMS(X), the clip divisor, alpha
+//                  and the per-matrix coefficients of the apply passes.
 #include "internal.h"
 
 namespace meo {
 
-// ----------------------------------------------------------------------------- k_stats
+// ----------------------------------------------------------------------------- flat first pass
 
-__device__ void stats_factored(const TDesc& d, int64_t lt, float* __restrict__ ws, const StatsArgs& a,
-                               float* lds) {
-    const TileRC p = tile_rc(d, lt);
+__device__ void stats_flat(const TDesc& d, int lt, float* __restrict__ ws, const StatsArgs& a, float* lds) {
+    const bool vec = d.vec, bf = d.gbf16;
+    const float beta = a.beta, omb = a.omb;
+    const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
+    float su[kVec], sx[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) { su[e] = 0.0f; sx[e] = 0.0f; }
+    for (int it = 0; it < kFlatIters; ++it) {
+        const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
+        const int valid = clamp_valid(d.numel - i);
+        if (valid == 0) break;
+        float g[kVec], v[kVec] = {};
+        load_g8<true>(d.g, i, valid, vec, bf, g);
+        if (beta != 0.0f) load_f8(d.v + i, valid, vec, v);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const float q = fmaf(g[e], g[e], a.eps1);
+            v[e] = beta != 0.0f ? fmaf(beta, v[e], omb * q) : q;
+            const float u = e < valid ? g[e] * rsqrtf(v[e]) : 0.0f;
+            su[e] = fmaf(u, u, su[e]);
+        }
+        store_f8(d.v + i, valid, vec, v);
+        if (a.need_x) {
+            float x[kVec];
+            load_f8<true>(d.x + i, valid, vec, x);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) sx[e] = fmaf(x[e], x[e], sx[e]);
+        }
+    }
+    float tu = sum8(su), tx = sum8(sx);
+    block_sum2<kWaves>(tu, tx, lds);
+    if (threadIdx.x == 0) {
+        float* tp = ws + d.tilepart + 2 * static_cast<int64_t>(lt);
+        stf(tp, tu);
+        stf(tp + 1, tx);
+    }
+}
+
+// ----------------------------------------------------------------------------- sum of X^2 chunks
+
+// Sum of X^2 over chunk `c` (kFlatTile elements) of a row-complete tensor's
+// parameter; these blocks stream with no barrier inside the strip pass's grid.
+template <int NTHR>
+__device__ void xnorm_chunk(const TDesc& d, int c, float* __restrict__ ws, float* bsum) {
+    constexpr int NW = NTHR / kLanes;
+    constexpr int ITERS = kFlatTile / (NTHR * kVec);
+    const int64_t base = static_cast<int64_t>(c) * kFlatTile;
+    float sx[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) sx[e] = 0.0f;
+#pragma unroll 4
+    for (int it = 0; it < ITERS; ++it) {
+        const int64_t i = base + (static_cast<int64_t>(it) * NTHR + threadIdx.x) * kVec;
+        const int valid = clamp_valid(d.numel - i);
+        if (valid == 0) break;
+        float x[kVec];
+        load_f8<true>(d.x + i, valid, true, x);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) sx[e] = fmaf(x[e], x[e], sx[e]);
+    }
+    float tx = sum8(sx), unused = 0.0f;
+    block_sum2<NW>(tx, unused, bsum);
+    if (threadIdx.x == 0) stf(ws + d.xpart + c, tx);
+}
+
+// ----------------------------------------------------------------------------- row-complete first pass
+
+// One strip of up to kStripRows full rows of matrix b (the sum of X^2 is taken by
+// separate chunk blocks of the same grid). Thread t owns the 8-column
+// groups t, t + NTHR, ..., t + (KMAX-1) NTHR; rows go in batches of RB: the block
+// first sums each row (fixed order: lane partials, wave tree, waves in order),
+// finishes R_i = beta R_i + (1-beta) sum/W, then accumulates the column sums with
+// 1/R_i known.
+template <int NTHR, int KMAX, int RB, bool BF16>
+__device__ void rowstats_strip(const TDesc& d, int lt, float* __restrict__ ws, const StatsArgs& a,
+                               float* red, float* rinv, float* bsum) {
+    constexpr int NW = NTHR / kLanes;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int b = lt / d.strips;
+    const int st = lt - b * d.strips;
+    const int row_begin = st * kStripRows;
+    const int row_end = min(row_begin + kStripRows, d.H);
+    const int W = d.W, ngroups = W / kVec;
+    const int64_t mat = static_cast<int64_t>(b) * d.H * W;
+    float* rstat = d.r + static_cast<int64_t>(b) * d.H;
+
+    float cs[KMAX][kVec], ss[KMAX][kVec];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) { cs[k][e] = 0.0f; ss[k][e] = 0.0f; }
+    float rsum = 0.0f;  // threads < RB: sum of the new R over their rows
+
+    for (int r0 = row_begin; r0 < row_end; r0 += RB) {
+        const int nr = min(RB, row_end - r0);
+        // Raw gradient of the batch: bf16 -> 4 dwords per group, fp32 -> 8.
+        u32x4 gb[RB][KMAX];
+        f32x4 gf[RB][KMAX][2];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                const int grp = tid + k * NTHR;
+                if (r < nr && grp < ngroups) {
+                    const int64_t off = mat + static_cast<int64_t>(r0 + r) * W + grp * kVec;
+                    if (BF16) {
+                        gb[r][k] = ld_u4<true>(static_cast<const uint16_t*>(d.g) + off);
+                    } else {
+                        gf[r][k][0] = ld_f4<true>(static_cast<const float*>(d.g) + off);
+                        gf[r][k][1] = ld_f4<true>(static_cast<const float*>(d.g) + off + 4);
+                    }
+                }
+            }
+        // Row sums of Q.
+        float rs[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            float acc[kVec];
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                const int grp = tid + k * NTHR;
+                if (r < nr && grp < ngroups) {
+                    float g[kVec];
+                    if (BF16) bf16x8(gb[r][k], g);
+                    else {
+                        g[0] = gf[r][k][0].x; g[1] = gf[r][k][0].y; g[2] = gf[r][k][0].z; g[3] = gf[r][k][0].w;
+                        g[4] = gf[r][k][1].x; g[5] = gf[r][k][1].y; g[6] = gf[r][k][1].z; g[7] = gf[r][k][1].w;
+                    }
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) acc[e] += fmaf(g[e], g[e], a.eps1);
+                }
+            }
+            rs[r] = wave_sum(sum8(acc));
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < RB; ++r) red[w * RB + r] = rs[r];
+        }
+        __syncthreads();
+        if (tid < nr) {
+            float tot = red[tid];
+#pragma unroll
+            for (int i = 1; i < NW; ++i) tot += red[i * RB + tid];
+            const int row = r0 + tid;
+            const double mean = static_cast<double>(tot) / static_cast<double>(W);
+            const double rnew = a.beta != 0.0f ? a.dbeta * static_cast<double>(ldf(rstat + row)) + a.domb * mean
+                                               : mean;
+            const float r32 = static_cast<float>(rnew);
+            stf(rstat + row, r32);
+            rinv[tid] = 1.0f / r32;
+            rsum += r32;
+        }
+        __syncthreads();
+        // Column sums of Q and of G^2 / R_i.
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (r < nr) {
+                const float ri = rinv[r];
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k) {
+                    const int grp = tid + k * NTHR;
+                    if (grp < ngroups) {
+                        float g[kVec];
+                        if (BF16) bf16x8(gb[r][k], g);
+                        else {
+                            g[0] = gf[r][k][0].x; g[1] = gf[r][k][0].y; g[2] = gf[r][k][0].z; g[3] = gf[r][k][0].w;
+                            g[4] = gf[r][k][1].x; g[5] = gf[r][k][1].y; g[6] = gf[r][k][1].z; g[7] = gf[r][k][1].w;
+                        }
+#pragma unroll
+                        for (int e = 0; e < kVec; ++e) {
+                            cs[k][e] += fmaf(g[e], g[e], a.eps1);
+                            ss[k][e] = fmaf(g[e] * g[e], ri, ss[k][e]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    // Per-strip column partials: colpart[b][st][0][:] = sum Q, [1][:] = sum G^2 / R.
+    float* cp = ws + d.colpart + (static_cast<int64_t>(b) * d.strips + st) * 2 * W;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int grp = tid + k * NTHR;
+        if (grp < ngroups) {
+            store_f8(cp + grp * kVec, kVec, true, cs[k]);
+            store_f8(cp + W + grp * kVec, kVec, true, ss[k]);
+        }
+    }
+    float tr_ = rsum, unused = 0.0f;
+    block_sum2<NW>(tr_, unused, bsum);
+    if (tid == 0) stf(ws + d.tilepart + 2 * static_cast<int64_t>(lt), tr_);
+}
+
+// Rows per batch of the two classes (bf16 gradients; fp32 ones take half as many,
+// so that both keep the same number of gradient registers).
+constexpr int kRb0 = 4, kRb1 = 2;
+
+__global__ __launch_bounds__(256) void k_rowstats0(Table t, StatsArgs a) {
+    __shared__ float red[kWaves * kRb0], rinv[kRb0], bsum[2 * kWaves];
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    if (d.mode == kFlat) stats_flat(d, it.y, t.ws, a, bsum);
+    else if (it.y < 0) xnorm_chunk<256>(d, -1 - it.y, t.ws, bsum);
+    else if (d.gbf16) rowstats_strip<256, 2, kRb0, true>(d, it.y, t.ws, a, red, rinv, bsum);
+    else rowstats_strip<256, 2, kRb0 / 2, false>(d, it.y, t.ws, a, red, rinv, bsum);
+}
+
+__global__ __launch_bounds__(512) void k_rowstats1(Table t, StatsArgs a) {
+    __shared__ float red[8 * kRb1], rinv[kRb1], bsum[2 * 8];
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    if (it.y < 0) xnorm_chunk<512>(d, -1 - it.y, t.ws, bsum);
+    else if (d.gbf16) rowstats_strip<512, 3, kRb1, true>(d, it.y, t.ws, a, red, rinv, bsum);
+    else rowstats_strip<512, 3, kRb1 / 2, false>(d, it.y, t.ws, a, red, rinv, bsum);
+}
+
+void launch_rowstats(int cls, const Table& t, int64_t n, const StatsArgs& a, hipStream_t s) {
+    if (n <= 0) return;
+    if (cls == 0) hipLaunchKernelGGL(k_rowstats0, dim3(static_cast<uint32_t>(n)), dim3(256), 0, s, t, a);
+    else hipLaunchKernelGGL(k_rowstats1, dim3(static_cast<uint32_t>(n)), dim3(512), 0, s, t, a);
+}
+
+// ----------------------------------------------------------------------------- tiled first pass
+
+__global__ __launch_bounds__(kThreads) void k_stats(Table t, StatsArgs a) {
+    __shared__ __align__(16) float lds[kWaves * kTileCols];
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    float* ws = t.ws;
+    const TileRC p = tile_rc(d, it.y);
     const int lane = threadIdx.x & 63;
     const bool vec = d.vec, bf = d.gbf16;
     const int64_t mat = static_cast<int64_t>(p.b) * d.H * d.W;
@@ -33,7 +267,6 @@ __device__ void stats_factored(const TDesc& d, int64_t lt, float* __restrict__ w
     float cs[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) cs[e] = 0.0f;
-
     for (int i0 = 0; i0 < p.nrows; i0 += 8) {
         float g[8][kVec];
 #pragma unroll
@@ -58,76 +291,46 @@ __device__ void stats_factored(const TDesc& d, int64_t lt, float* __restrict__ w
     write_colpart(d, ws, p, cs, lds);
 }
 
-__device__ void stats_flat(const TDesc& d, int64_t lt, float* __restrict__ ws, const StatsArgs& a,
-                           float* lds) {
-    const bool vec = d.vec, bf = d.gbf16;
-    const float beta = a.beta, omb = a.omb;
-    const int64_t base = lt * kFlatTile;
-    float su[kVec], sx[kVec];
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) { su[e] = 0.0f; sx[e] = 0.0f; }
-    for (int it = 0; it < kFlatIters; ++it) {
-        const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
-        const int valid = clamp_valid(d.numel - i);
-        if (valid == 0) break;
-        float g[kVec], v[kVec] = {};
-        load_g8(d.g, i, valid, vec, bf, g);
-        if (beta != 0.0f) load_f8(d.v + i, valid, vec, v);
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-            const float q = fmaf(g[e], g[e], a.eps1);
-            v[e] = beta != 0.0f ? fmaf(beta, v[e], omb * q) : q;
-            const float u = e < valid ? g[e] * rsqrtf(v[e]) : 0.0f;
-            su[e] = fmaf(u, u, su[e]);
-        }
-        store_f8(d.v + i, valid, vec, v);
-        if (a.need_x) {
-            float x[kVec];
-            load_f8(d.x + i, valid, vec, x);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) sx[e] = fmaf(x[e], x[e], sx[e]);
-        }
-    }
-    float tu = sum8(su), tx = sum8(sx);
-    block_sum2(tu, tx, lds);
-    if (threadIdx.x == 0) {
-        float* tp = ws + d.tilepart + 2 * lt;
-        stf(tp, tu);
-        stf(tp + 1, tx);
-    }
-}
-
-__global__ __launch_bounds__(kThreads) void k_stats(Table t, StatsArgs a) {
-    __shared__ __align__(16) float lds[kWaves * kTileCols];
-    const int64_t tile = blockIdx.x;
-    const int k = tensor_of(t.tile_tensor, tile);
-    const TDesc d = t.desc[k];
-    const int64_t lt = tile - d.tile0;
-    if (d.factored) stats_factored(d, lt, t.ws, a, lds);
-    else stats_flat(d, lt, t.ws, a, lds);
-}
-
-void launch_stats(const Table& t, int64_t tiles, const StatsArgs& a, hipStream_t s) {
-    if (tiles > 0) hipLaunchKernelGGL(k_stats, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t, a);
+void launch_stats(const Table& t, int64_t n, const StatsArgs& a, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_stats, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
 }
 
 // ----------------------------------------------------------------------------- k_finalize
 
-// Items of a factored tensor, per matrix b: nrc row chunks then ncc column chunks.
+// Items per matrix b: row-complete (first statistic): ncc column chunks; tiled (or
+// `tiled_all`): nrc row chunks then ncc column chunks.
 __global__ __launch_bounds__(kThreads) void k_finalize(Table t, FinArgs a) {
     __shared__ double lds[kWaves];
-    const int64_t item = blockIdx.x;
-    const int k = tensor_of(t.fin_tensor, item);
-    const TDesc d = t.desc[k];
-    const int64_t li = item - d.fin0;
-    const int per = d.nrc + d.ncc;
-    const int b = static_cast<int>(li / per);
-    const int j = static_cast<int>(li - static_cast<int64_t>(b) * per);
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
     float* ws = t.ws;
     float* rs = a.which ? d.rr : d.r;
     float* cs = a.which ? d.rc : d.c;
     const double beta = a.beta, omb = 1.0 - a.beta;
-    if (j < d.nrc) {
+    const bool rc = d.mode == kRowComplete && !a.tiled_all;
+    const int per = rc ? d.ncc : d.nrc + d.ncc;
+    const int b = it.y / per;
+    const int j = it.y - b * per;
+    if (rc) {
+        const int col = j * kFinChunk + threadIdx.x;
+        double u = 0.0;
+        if (col < d.W) {
+            const float* cp = ws + d.colpart + static_cast<int64_t>(b) * d.strips * 2 * d.W + col;
+            double sq = 0.0, sg = 0.0;
+            for (int st = 0; st < d.strips; ++st) {
+                sq += static_cast<double>(ldf(cp + static_cast<int64_t>(st) * 2 * d.W));
+                sg += static_cast<double>(ldf(cp + static_cast<int64_t>(st) * 2 * d.W + d.W));
+            }
+            float* dst = cs + static_cast<int64_t>(b) * d.W + col;
+            const double mean = sq / static_cast<double>(d.H);
+            const double cnew = beta != 0.0 ? beta * static_cast<double>(ldf(dst)) + omb * mean : mean;
+            const float c32 = static_cast<float>(cnew);
+            stf(dst, c32);
+            u = sg / static_cast<double>(c32);
+        }
+        const double tot = block_sum_d(u, lds);
+        if (threadIdx.x == 0) stf(ws + d.sumr + static_cast<int64_t>(b) * d.ncc + j, static_cast<float>(tot));
+    } else if (j < d.nrc) {
         const int row = j * kFinChunk + threadIdx.x;
         double rnew = 0.0;
         if (row < d.H) {
@@ -157,23 +360,20 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Table t, FinArgs a) {
     }
 }
 
-void launch_finalize(const Table& t, int64_t items, const FinArgs& a, hipStream_t s) {
-    if (items > 0) hipLaunchKernelGGL(k_finalize, dim3(static_cast<uint32_t>(items)), dim3(kThreads), 0, s, t, a);
+void launch_finalize(const Table& t, int64_t n, const FinArgs& a, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_finalize, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
 }
 
-// ----------------------------------------------------------------------------- k_rms
+// ----------------------------------------------------------------------------- k_rms (tiled)
 
 __global__ __launch_bounds__(kThreads) void k_rms(Table t, int32_t need_x) {
     __shared__ float lds[2 * kWaves];
-    const int64_t tile = blockIdx.x;
-    const int k = tensor_of(t.tile_tensor, tile);
-    const TDesc d = t.desc[k];
-    if (!d.factored) return;  // flat tensors finished their sums in k_stats
-    const int64_t lt = tile - d.tile0;
-    const TileRC p = tile_rc(d, lt);
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    const TileRC p = tile_rc(d, it.y);
     const bool vec = d.vec, bf = d.gbf16;
     const float* ws = t.ws;
-    const float sm = static_cast<float>(sqrt(row_mean(d, ws, p.b)));
+    const float sm = static_cast<float>(sqrt(row_mean_tiled(d, ws, p.b)));
     const int64_t mat = static_cast<int64_t>(p.b) * d.H * d.W;
     float cf[kVec];
 #pragma unroll
@@ -213,67 +413,86 @@ __global__ __launch_bounds__(kThreads) void k_rms(Table t, int32_t need_x) {
         }
     }
     float tu = sum8(su), tx = sum8(sx);
-    block_sum2(tu, tx, lds);
+    block_sum2<kWaves>(tu, tx, lds);
     if (threadIdx.x == 0) {
-        float* tp = t.ws + d.tilepart + 2 * lt;
+        float* tp = t.ws + d.tilepart + 2 * static_cast<int64_t>(it.y);
         stf(tp, tu);
         stf(tp + 1, tx);
     }
 }
 
-void launch_rms(const Table& t, int64_t tiles, int32_t need_x, hipStream_t s) {
-    if (tiles > 0) hipLaunchKernelGGL(k_rms, dim3(static_cast<uint32_t>(tiles)), dim3(kThreads), 0, s, t, need_x);
+void launch_rms(const Table& t, int64_t n, int32_t need_x, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_rms, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, need_x);
 }
 
 // ----------------------------------------------------------------------------- k_scalars
 
-// Sum over the tensor's tiles of tilepart[.][0] and [.][1], fp64, fixed order.
-__device__ __forceinline__ void tile_sums(const TDesc& d, const float* __restrict__ ws, double& su,
-                                          double& sx, double* lds) {
-    double a = 0.0, b = 0.0;
-    const float* tp = ws + d.tilepart;
-    for (int j = threadIdx.x; j < d.ntiles; j += kThreads) {
-        a += static_cast<double>(ldf(tp + 2 * j));
-        b += static_cast<double>(ldf(tp + 2 * j + 1));
-    }
-    su = block_sum_d(a, lds);
+// Sum over `count` tile partials (stride 2, component `comp`), fp64, fixed order;
+// every thread gets the result. `lds` holds kWaves doubles.
+__device__ __forceinline__ double tile_sum(const float* __restrict__ tp, int count, int comp, double* lds) {
+    double a = 0.0;
+    for (int j = threadIdx.x; j < count; j += kThreads) a += static_cast<double>(ldf(tp + 2 * j + comp));
+    const double r = block_sum_d(a, lds);
     __syncthreads();
-    sx = block_sum_d(b, lds + kWaves);
+    return r;
 }
 
-__global__ __launch_bounds__(kThreads) void k_scalars(Table t, ScalArgs a) {
-    __shared__ double lds[2 * kWaves];
+__global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ desc, float* ws, ScalArgs a) {
+    __shared__ double lds[kWaves];
+    __shared__ double wsum[kWaves];
     const int k = blockIdx.x;
-    const TDesc d = t.desc[k];
-    if (d.numel == 0) return;
-    float* ws = t.ws;
+    const TDesc d = desc[k];
     float* scal = ws + d.scal;
     float* bs = ws + d.bscal;
-    const int w = threadIdx.x >> 6;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const double n = static_cast<double>(d.numel);
+    const float* tp = ws + d.tilepart;
 
     if (a.mode == kScalCame2) {
-        // Confidence statistic: per-matrix lr * sqrt(mean of its row statistic).
-        if (!d.factored) return;
+        // Confidence statistic (tiled layout for every factored tensor): per-matrix
+        // lr * sqrt(mean of its row statistic).
+        if (d.mode == kFlat) return;
         for (int b = w; b < d.B; b += kWaves) {
-            const double mr = row_mean(d, ws, b);
-            if ((threadIdx.x & 63) == 0) stf(bs + d.B + b, static_cast<float>(a.lr * sqrt(mr)));
+            const double mr = row_mean_tiled(d, ws, b);
+            if (lane == 0) stf(bs + d.B + b, static_cast<float>(a.lr * sqrt(mr)));
+        }
+        return;
+    }
+    if (a.mode == kScalLamb) {
+        // components: sum of x^2, sum of d^2 (see the LAMB moment pass).
+        const double xn = sqrt(tile_sum(tp, d.tc, 0, lds));
+        const double dn = sqrt(tile_sum(tp, d.tc, 1, lds));
+        const double trust = (xn > 0.0 && dn > 0.0) ? xn / dn : 1.0;
+        if (threadIdx.x == 0) {
+            stf(bs, static_cast<float>(a.lr * trust));
+            stf(scal + kSlotRmsX, static_cast<float>(xn));
+            stf(scal + kSlotNormD, static_cast<float>(dn));
         }
         return;
     }
 
     double su, sx;
-    tile_sums(d, ws, su, sx, lds);
-    if (a.mode == kScalLamb) {
-        // su: sum of x^2, sx: sum of d^2 (see the LAMB moment pass).
-        const double xn = sqrt(su), dn = sqrt(sx);
-        const double trust = (xn > 0.0 && dn > 0.0) ? xn / dn : 1.0;
-        if (threadIdx.x == 0) {
-            stf(bs + 0, static_cast<float>(a.lr * trust));
-            stf(scal + kSlotRmsX, static_cast<float>(xn));
-            stf(scal + kSlotNormD, static_cast<float>(dn));
+    if (d.mode == kRowComplete) {
+        // sum U^2 = sum_b mean(R_b) * sum_j S_j / C_j (finalize chunk sums).
+        double part = 0.0;
+        for (int b = w; b < d.B; b += kWaves) {
+            const double mr = row_mean_rc(d, ws, b);
+            double u = 0.0;
+            const float* sr = ws + d.sumr + static_cast<int64_t>(b) * d.ncc;
+            for (int j = lane; j < d.ncc; j += kLanes) u += static_cast<double>(ldf(sr + j));
+            part += mr * wave_sum(u);
         }
-        return;
+        if (lane == 0) wsum[w] = part;
+        __syncthreads();
+        su = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+        double a_ = 0.0;
+        for (int j = threadIdx.x; j < d.xchunks; j += kThreads) a_ += static_cast<double>(ldf(ws + d.xpart + j));
+        sx = block_sum_d(a_, lds);
+        __syncthreads();
+    } else {
+        const int tiles = d.mode == kFlat ? d.tc : d.B * d.tr * d.tc;
+        su = tile_sum(tp, tiles, 0, lds);
+        sx = tile_sum(tp, tiles, 1, lds);
     }
     const double rms_u = sqrt(su / n);
     const double kappa = fmax(1.0, rms_u / a.clip);
@@ -291,18 +510,18 @@ __global__ __launch_bounds__(kThreads) void k_scalars(Table t, ScalArgs a) {
         // Decoupled weight decay: Adafactor scales it by alpha, CAME by lr.
         stf(scal + kSlotDecay, static_cast<float>(a.mode == kScalAdafactor ? a.wd * alpha : a.wd * a.lr));
     }
-    if (d.factored) {
-        for (int b = w; b < d.B; b += kWaves) {
-            const double mr = row_mean(d, ws, b);
-            if ((threadIdx.x & 63) == 0) stf(bs + b, static_cast<float>(coef * sqrt(mr)));
-        }
-    } else if (threadIdx.x == 0) {
-        stf(bs + 0, static_cast<float>(coef));
+    if (d.mode == kFlat) {
+        if (threadIdx.x == 0) stf(bs, static_cast<float>(coef));
+        return;
+    }
+    for (int b = w; b < d.B; b += kWaves) {
+        const double mr = d.mode == kRowComplete ? row_mean_rc(d, ws, b) : row_mean_tiled(d, ws, b);
+        if (lane == 0) stf(bs + b, static_cast<float>(coef * sqrt(mr)));
     }
 }
 
-void launch_scalars(const Table& t, int32_t n, const ScalArgs& a, hipStream_t s) {
-    if (n > 0) hipLaunchKernelGGL(k_scalars, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
+void launch_scalars(const TDesc* desc, float* ws, int32_t n, const ScalArgs& a, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_scalars, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, desc, ws, a);
 }
 
 }  // namespace meo

@@ -55,8 +55,12 @@ def test_scaled_down_workloads_chained(name):
     _chain(wl, wl.steps, check_every=3)
 
 
+# Row-complete first pass (W % 8 == 0, W <= 4096 or <= 12288): (129, 1024), (1, 8),
+# (700, 8), (2, 3, 72, 136), (70, 5000); tiled first pass: odd widths (1000, 1),
+# (1, 1000)... and the over-wide (3, 16384); flat: 1-D and 0-d.
 EDGE_SHAPES = [(1, 1000), (1000, 1), (37, 1001), (3,), (), (2, 3, 70, 130), (0, 5), (65, 513),
-               (129, 1024), (1, 8), (700, 8), (5000,), (40000,)]
+               (129, 1024), (1, 8), (700, 8), (5000,), (40000,), (2, 3, 72, 136), (70, 5000),
+               (3, 16384)]
 
 
 @pytest.mark.parametrize("gdt", [torch.float32, torch.bfloat16])
