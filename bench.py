@@ -65,52 +65,67 @@ def algorithmic_bytes(wl) -> dict:
     return tot
 
 
-def cpu_baseline(wl, budget_s: float = 20.0) -> dict:
-    """One oracle step over a bounded sample of the workload's tensors, on the host."""
-    import numpy as np
+def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
+    """The fp64 oracle stepping the workload's tensors on the host, one tensor at a
+    time in list order (inputs drawn on the CPU, outside the timing), until about
+    `budget_s` seconds of oracle time: parameters stepped per second."""
     import torch
     import oracle
     import workloads
 
-    # Sample: the workload's tensors in list order, stopping near ~120M parameters
-    # (about 10-30 s of single-threaded fp64 NumPy), at least one tensor.
-    idx, tot = [], 0
-    for k, s in enumerate(wl.specs):
-        if idx and tot + s.numel > 120_000_000:
-            break
-        idx.append(k)
-        tot += s.numel
-    xs = [p.double().numpy() for p in workloads.init_params(wl, "cpu", idx)]
-    sc = workloads.grad_scales(wl, "cpu", idx)
-    gs = [g.to(torch.float64).numpy() for g in workloads.grads(wl, 0, sc, "cpu", idx)]
     hp = dict(wl.hparams)
-    st = [oracle.INIT_STATE[wl.optimizer](x.shape, hp) for x in xs]
-    t0 = time.perf_counter()
-    done = 0
-    for k in range(len(xs)):
-        oracle.STEP_TENSOR[wl.optimizer](xs[k], gs[k], st[k], hp, 1)
-        done += xs[k].size
-        if time.perf_counter() - t0 > budget_s:
+    done, spent, names = 0, 0.0, []
+    for k, spec in enumerate(wl.specs):
+        x = workloads.init_params(wl, "cpu", [k])[0].double().numpy()
+        sc = workloads.grad_scales(wl, "cpu", [k])
+        g = workloads.grads(wl, 0, sc, "cpu", [k])[0].to(torch.float64).numpy()
+        st = oracle.INIT_STATE[wl.optimizer](x.shape, hp)
+        t0 = time.perf_counter()
+        oracle.STEP_TENSOR[wl.optimizer](x, g, st, hp, 1)
+        spent += time.perf_counter() - t0
+        done += x.size
+        names.append(spec.name)
+        del x, g, st
+        if spent > budget_s:
             break
-    dt = time.perf_counter() - t0
-    names = [wl.specs[idx[k]].name for k in range(len(xs))]
-    return {"value": done / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"one fp64 step over {done} parameters of the same workload "
-                      f"({len(names)} tensors from '{names[0]}' on, freshly allocated), "
-                      f"{dt:.1f} s, single-threaded NumPy"}
+    return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"one fp64 step of the first {len(names)} tensors of the same workload "
+                      f"({done} parameters, '{names[0]}' .. '{names[-1]}'), {spent:.1f} s of oracle time, "
+                      f"single-threaded NumPy"}
+
+
+def profile_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter record,
+    or None if there is none or the kernel's sources changed since it was taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"{kernel}_{workload.split('_', 1)[1]}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel") != kernel or rec.get("workload") != workload:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(here, src), "rb") as f:
+            h.update(f.read())
+    return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def copy_calibration(torch, args) -> int:
-    n = 1 << 30  # fp32 elements: 4 GiB read + 4 GiB written per copy
+    n = 1 << 29  # fp32 elements: 2 GiB read + 2 GiB written, one dispatch per copy
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    # torch.mul(..., out=) is one elementwise kernel that reads and writes n floats
+    # (a same-dtype copy_ may go to a DMA engine that kernel counters do not see).
     for _ in range(max(args.warmup, 1)):
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -128,11 +143,8 @@ def main() -> int:
     ap.add_argument("--workload", default="adafactor_llama7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="instead of the step: time a plain device copy of 4 GiB (torch's copy kernel), "
+                    help="instead of the step: time a plain device copy of 4 GiB (one elementwise kernel), "
                          "the reference for achievable bandwidth and for scaling rocprofv3 byte counters")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with the dominant pass's rocprofv3 FETCH_SIZE/WRITE_SIZE (KiB per "
-                         "dispatch) and the copy-kernel scale factor")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -199,12 +211,7 @@ def main() -> int:
     dominant = max((k for k in passes if k in ab), key=lambda k: passes[k]["ms"])  # the apply pass
     avg_ms = passes[dominant]["ms"] / passes[dominant]["launches"]
     achieved = ab[dominant] / (avg_ms / 1e3) / 1e9
-    traffic = None
-    if args.traffic:
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        if tr.get("kernel") == dominant:
-            traffic = tr.get("bytes_per_launch")
+    traffic = profile_traffic(dominant, wl.name)
 
     out = {
         "metric": "optimizer-step params/s + achieved HBM GB/s (% peak), 7B-shaped Adafactor",
