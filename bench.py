@@ -113,6 +113,19 @@ def profile_traffic(kernel: str, workload: str):
     return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
+def flat_views(torch, shapes, dtype, device):
+    """Views of the given shapes into one buffer, each starting 256-byte aligned."""
+    es = torch.empty((), dtype=dtype).element_size()
+    align = 256 // es
+    sizes = [math.prod(s) for s in shapes]
+    offs, o = [], 0
+    for n in sizes:
+        offs.append(o)
+        o += (n + align - 1) // align * align
+    buf = torch.empty(max(o, 1), dtype=dtype, device=device)
+    return [buf[a:a + n].view(s) for a, n, s in zip(offs, sizes, shapes)]
+
+
 def copy_calibration(torch, args) -> int:
     n = 1 << 29  # fp32 elements: 2 GiB read + 2 GiB written, one dispatch per copy
     src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -142,6 +155,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="adafactor_llama7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=["flat", "separate"], default="flat",
+                    help="flat: one buffer per kind of tensor (default); separate: one allocation per tensor")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the step: time a plain device copy of 4 GiB (one elementwise kernel), "
                          "the reference for achievable bandwidth and for scaling rocprofv3 byte counters")
@@ -167,13 +182,28 @@ def main() -> int:
     dev = "cuda"
     torch.cuda.set_device(0)
 
-    params = workloads.init_params(wl, dev)
-    scales = workloads.grad_scales(wl, dev)
-    grads = workloads.grads(wl, 0, scales, dev)
-    del scales
     hp = dict(wl.hparams)
     beta1 = hp.get("beta1") is not None
-    states = [_lib.init_state(wl.optimizer, p, beta1=beta1) for p in params]
+    if args.layout == "flat":
+        # One flat buffer per kind (parameters, gradients, each state), tensors as
+        # 256-byte aligned views, as flat-parameter training frameworks keep them.
+        shapes = [s.shape for s in wl.specs]
+        params = flat_views(torch, shapes, torch.float32, dev)
+        workloads.init_params(wl, dev, out=params)
+        grads = flat_views(torch, shapes, wl.grad_dtype, dev)
+        workloads.grads(wl, 0, workloads.grad_scales(wl, dev), dev, out=grads)
+        proto = [_lib.state_shapes(wl.optimizer, s, beta1=beta1) for s in shapes]
+        states = [dict() for _ in shapes]
+        for key in sorted({k for st in proto for k in st}):
+            idx = [i for i, st in enumerate(proto) if key in st]
+            views = flat_views(torch, [proto[i][key] for i in idx], torch.float32, dev)
+            for i, v in zip(idx, views):
+                v.zero_()
+                states[i][key] = v
+    else:
+        params = workloads.init_params(wl, dev)
+        grads = workloads.grads(wl, 0, workloads.grad_scales(wl, dev), dev)
+        states = [_lib.init_state(wl.optimizer, p, beta1=beta1) for p in params]
     hps = {"adafactor": _lib.adafactor_hparams, "came": _lib.came_hparams,
            "lamb": _lib.lamb_hparams}[wl.optimizer](**hp)
     wsize = getattr(_lib, f"meo_{wl.optimizer}_workspace_size")(params, grads)
@@ -227,7 +257,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "optimizer": wl.optimizer, "tensors": len(wl.specs),
+        "config": {"workload": wl.name, "optimizer": wl.optimizer, "tensors": len(wl.specs), "layout": args.layout,
                    "params": numel, "grad_dtype": str(wl.grad_dtype).replace("torch.", ""),
                    "param_state_dtype": "float32",
                    "hparams": {k: (list(v) if isinstance(v, tuple) else v) for k, v in hp.items()}},

@@ -342,24 +342,29 @@ class PreparedStep:
 
 # ----------------------------------------------------------------------------- state allocation
 
+def state_shapes(optimizer: str, shape, *, beta1: bool = True) -> Dict[str, tuple]:
+    """Shapes of the fp32 state tensors of one parameter, as meo.h expects them."""
+    shape = tuple(shape)
+    if optimizer == "lamb":
+        return {"exp_avg": shape, "exp_avg_sq": shape}
+    st: Dict[str, tuple] = {}
+    if optimizer == "came" or beta1:
+        st["exp_avg"] = shape
+    if len(shape) >= 2:
+        st["exp_avg_sq_row"] = shape[:-1]
+        st["exp_avg_sq_col"] = shape[:-2] + shape[-1:]
+        if optimizer == "came":
+            st["exp_avg_res_row"] = shape[:-1]
+            st["exp_avg_res_col"] = shape[:-2] + shape[-1:]
+    else:
+        st["exp_avg_sq"] = shape
+    return st
+
+
 def init_state(optimizer: str, param: torch.Tensor, *, beta1: bool = True) -> Dict[str, torch.Tensor]:
     """Zero fp32 state tensors for one parameter, with the shapes of meo.h."""
-    z = lambda shape: torch.zeros(shape, dtype=torch.float32, device=param.device)  # noqa: E731
-    shape = tuple(param.shape)
-    st: Dict[str, torch.Tensor] = {}
-    if optimizer == "lamb":
-        return {"exp_avg": z(shape), "exp_avg_sq": z(shape)}
-    if optimizer == "came" or beta1:
-        st["exp_avg"] = z(shape)
-    if len(shape) >= 2:
-        st["exp_avg_sq_row"] = z(shape[:-1])
-        st["exp_avg_sq_col"] = z(shape[:-2] + shape[-1:])
-        if optimizer == "came":
-            st["exp_avg_res_row"] = z(shape[:-1])
-            st["exp_avg_res_col"] = z(shape[:-2] + shape[-1:])
-    else:
-        st["exp_avg_sq"] = z(shape)
-    return st
+    return {k: torch.zeros(s, dtype=torch.float32, device=param.device)
+            for k, s in state_shapes(optimizer, param.shape, beta1=beta1).items()}
 
 
 def workspace(nbytes: int, device) -> Optional[torch.Tensor]:

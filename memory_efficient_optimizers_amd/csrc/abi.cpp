@@ -91,7 +91,7 @@ int64_t layout(int op, int32_t n, const meo_tensor* ts, std::vector<Geo>* out) {
                 g.strips = static_cast<int32_t>(ceil_div(g.H, kStripRows));
                 g.tiles = static_cast<int64_t>(g.B) * g.tr * g.tc;
                 g.nrc = static_cast<int32_t>(ceil_div(g.H, kFinChunk));
-                g.ncc = static_cast<int32_t>(ceil_div(g.W, kFinChunk));
+                g.ncc = static_cast<int32_t>(ceil_div(g.W, kFinCols));
                 const bool tiled_stats = g.mode == kTiled || op == kOpCame;  // CAME's confidence is tiled
                 const int64_t B = g.B;
                 const int64_t colrows = std::max<int64_t>(tiled_stats ? g.tr : 0,
@@ -156,7 +156,7 @@ int check_tensors(int op, int64_t step, int32_t n, const meo_tensor* ts, const v
             const int64_t tiles = t.batch * ceil_div(t.rows, kTileRows) * ceil_div(t.cols, kTileCols);
             if (tiles > kMaxDim) return fail(MEO_ESHAPE, who + "too many tiles");
             total_tiles += tiles;
-            total_fin += t.batch * (ceil_div(t.rows, kFinChunk) + ceil_div(t.cols, kFinChunk));
+            total_fin += t.batch * (ceil_div(t.rows, kFinChunk) + ceil_div(t.cols, kFinCols));
         } else {
             total_tiles += ceil_div(numel, kFlatTile);
         }
@@ -348,7 +348,8 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
                 // Strips interleaved with the chunks that stream X for sum(X^2), so
                 // that barrier-free streaming runs beside the strips' row reductions.
                 std::vector<int2>& L = lists[g.cls == 0 ? kListRc0 : kListRc1];
-                const int64_t ns = static_cast<int64_t>(g.B) * g.strips, nx = g.xchunks;
+                const int64_t ns = static_cast<int64_t>(g.B) * g.strips;
+                const int64_t nx = op == kOpAdafactor ? g.xchunks : 0;  // only Adafactor uses RMS(X)
                 int64_t is = 0, ix = 0;
                 while (is < ns || ix < nx) {
                     if (is < ns) L.push_back(make_int2(id, static_cast<int>(is++)));
@@ -585,7 +586,9 @@ int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
     if (hp->relative_step) rho = std::fmin(hp->warmup_init ? 1e-6 * tt : 1e-2, 1.0 / std::sqrt(tt));
     else rho = hp->lr;
     const double b2 = 1.0 - std::pow(tt, hp->decay_rate);
-    const StatsArgs sa{static_cast<float>(hp->eps1), static_cast<float>(b2), static_cast<float>(1.0 - b2), 1,
+    // RMS(X) is needed only to scale the step (scale_parameter).
+    const int32_t need_x = hp->scale_parameter ? 1 : 0;
+    const StatsArgs sa{static_cast<float>(hp->eps1), static_cast<float>(b2), static_cast<float>(1.0 - b2), need_x,
                        b2, 1.0 - b2};
 
     PassTimer pt(s);
@@ -604,7 +607,7 @@ int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
     launch_finalize(tab(kListFin1), p->count[kListFin1], FinArgs{b2, 0, 0}, s);
     pt.mark(kPassFinalize);
     if (p->count[kListTiled]) {
-        launch_rms(tab(kListTiled), p->count[kListTiled], 1, s);
+        launch_rms(tab(kListTiled), p->count[kListTiled], need_x, s);
         pt.mark(kPassRms);
     }
     launch_scalars(p->desc, w, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, rho, hp->eps2,

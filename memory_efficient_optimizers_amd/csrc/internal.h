@@ -34,7 +34,8 @@ constexpr int kRowsPerWave = 16;
 constexpr int kTileRows = kWaves * kRowsPerWave; // 64
 constexpr int kFlatIters = 16;
 constexpr int kFlatTile = kThreads * kVec * kFlatIters;  // 32768
-constexpr int kFinChunk = 256;                   // rows or columns per finalize block
+constexpr int kFinChunk = 256;                   // rows per finalize block
+constexpr int kFinCols = 64;                     // columns per finalize block
 constexpr int kScalSlots = 8;                    // floats of per-tensor scalars
 constexpr int kStripRows = 64;                   // rows per strip of the row-complete pass
 // Widest row of each row-complete class (class 0: 256 threads x 2 groups of 8

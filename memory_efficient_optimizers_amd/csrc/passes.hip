@@ -71,7 +71,8 @@ __device__ void stats_flat(const TDesc& d, int lt, float* __restrict__ ws, const
 // Sum of X^2 over chunk `c` (kFlatTile elements) of a row-complete tensor's
 // parameter; these blocks stream with no barrier inside the strip pass's grid.
 template <int NTHR>
-__device__ void xnorm_chunk(const TDesc& d, int c, float* __restrict__ ws, float* bsum) {
+__device__ void xnorm_chunk(const TDesc& d, int c, float* __restrict__ ws, const StatsArgs& a, float* bsum) {
+    if (!a.need_x) return;  // the step does not use RMS(X)
     constexpr int NW = NTHR / kLanes;
     constexpr int ITERS = kFlatTile / (NTHR * kVec);
     const int64_t base = static_cast<int64_t>(c) * kFlatTile;
@@ -95,130 +96,168 @@ __device__ void xnorm_chunk(const TDesc& d, int c, float* __restrict__ ws, float
 
 // ----------------------------------------------------------------------------- row-complete first pass
 
-// One strip of up to kStripRows full rows of matrix b (the sum of X^2 is taken by
-// separate chunk blocks of the same grid). Thread t owns the 8-column
-// groups t, t + NTHR, ..., t + (KMAX-1) NTHR; rows go in batches of RB: the block
-// first sums each row (fixed order: lane partials, wave tree, waves in order),
-// finishes R_i = beta R_i + (1-beta) sum/W, then accumulates the column sums with
-// 1/R_i known.
+// Raw gradient of one batch of rows: per 8-column group one u32x4 (bf16) or two
+// (fp32, reinterpreted).
+template <int RB, int KMAX, bool BF16>
+struct GBatch {
+    u32x4 v[RB][KMAX][BF16 ? 1 : 2];
+};
+
+template <int NTHR, int RB, int KMAX, bool BF16>
+__device__ __forceinline__ void load_batch(GBatch<RB, KMAX, BF16>& gb, const void* g, int64_t mat, int r0,
+                                           int nr, int W, int ngroups) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int grp = threadIdx.x + k * NTHR;
+            if (r < nr && grp < ngroups) {
+                const int64_t off = mat + static_cast<int64_t>(r0 + r) * W + grp * kVec;
+                if (BF16) {
+                    gb.v[r][k][0] = ld_u4<true>(static_cast<const uint16_t*>(g) + off);
+                } else {
+                    gb.v[r][k][0] = ld_u4<true>(static_cast<const float*>(g) + off);
+                    gb.v[r][k][BF16 ? 0 : 1] = ld_u4<true>(static_cast<const float*>(g) + off + 4);
+                }
+            }
+        }
+}
+
+template <int RB, int KMAX, bool BF16>
+__device__ __forceinline__ void unpack(const GBatch<RB, KMAX, BF16>& gb, int r, int k, float* g) {
+    if (BF16) {
+        bf16x8(gb.v[r][k][0], g);
+    } else {
+        const u32x4 a = gb.v[r][k][0], b = gb.v[r][k][BF16 ? 0 : 1];
+        g[0] = __uint_as_float(a.x); g[1] = __uint_as_float(a.y); g[2] = __uint_as_float(a.z); g[3] = __uint_as_float(a.w);
+        g[4] = __uint_as_float(b.x); g[5] = __uint_as_float(b.y); g[6] = __uint_as_float(b.z); g[7] = __uint_as_float(b.w);
+    }
+}
+
+// State of one strip while its batches go by.
+struct StripCtx {
+    int64_t mat;
+    int row_begin, row_end, W, ngroups;
+    float* rstat;
+    float rsum;  // thread r < RB: sum of the new R over the rows it stored
+};
+
+// One batch of RB rows held in `cur`: row sums (lane partials, wave tree, waves in
+// order through LDS slot `par`), the next batch's loads into `nxt`, one barrier,
+// then every thread finishes the batch's row statistics from LDS and accumulates
+// the column sums of Q and of G^2 / R_i.
 template <int NTHR, int KMAX, int RB, bool BF16>
-__device__ void rowstats_strip(const TDesc& d, int lt, float* __restrict__ ws, const StatsArgs& a,
-                               float* red, float* rinv, float* bsum) {
+__device__ __forceinline__ void strip_batch(const TDesc& d, const StatsArgs& a, StripCtx& c, int r0, int par,
+                                            const GBatch<RB, KMAX, BF16>& cur, GBatch<RB, KMAX, BF16>& nxt,
+                                            float (&cs)[KMAX][kVec], float (&ss)[KMAX][kVec], float* red,
+                                            const float* rold) {
     constexpr int NW = NTHR / kLanes;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int nr = min(RB, c.row_end - r0);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        float acc[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (r < nr && tid + k * NTHR < c.ngroups) {
+                float g[kVec];
+                unpack<RB, KMAX, BF16>(cur, r, k, g);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) acc[e] += fmaf(g[e], g[e], a.eps1);
+            }
+        }
+        const float rs = wave_sum(sum8(acc));
+        if (lane == 0) red[(par * NW + w) * RB + r] = rs;
+    }
+    const int rn = r0 + RB;
+    if (rn < c.row_end) load_batch<NTHR, RB, KMAX, BF16>(nxt, d.g, c.mat, rn, min(RB, c.row_end - rn), c.W, c.ngroups);
+    __syncthreads();
+    float ri[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        ri[r] = 0.0f;
+        if (r < nr) {
+            float tot = red[(par * NW) * RB + r];
+#pragma unroll
+            for (int i = 1; i < NW; ++i) tot += red[(par * NW + i) * RB + r];
+            const double mean = static_cast<double>(tot) / static_cast<double>(c.W);
+            const double rnew = a.beta != 0.0f
+                                    ? a.dbeta * static_cast<double>(rold[r0 - c.row_begin + r]) + a.domb * mean
+                                    : mean;
+            const float r32 = static_cast<float>(rnew);
+            ri[r] = 1.0f / r32;
+            if (tid == r) {
+                stf(c.rstat + r0 + r, r32);
+                c.rsum += r32;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        if (r < nr) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (tid + k * NTHR < c.ngroups) {
+                    float g[kVec];
+                    unpack<RB, KMAX, BF16>(cur, r, k, g);
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        cs[k][e] += fmaf(g[e], g[e], a.eps1);
+                        ss[k][e] = fmaf(g[e] * g[e], ri[r], ss[k][e]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// One strip of up to kStripRows full rows of matrix b (the sum of X^2 is taken by
+// separate chunk blocks of the same grid). Thread t owns the 8-column groups t,
+// t + NTHR, ..., t + (KMAX-1) NTHR; rows go in batches of RB, two register buffers
+// alternating so that a batch's loads are in flight during the previous one's
+// reduction. `red` holds 2 * NW * RB floats, `rold` kStripRows.
+template <int NTHR, int KMAX, int RB, bool BF16>
+__device__ void rowstats_strip(const TDesc& d, int lt, float* __restrict__ ws, const StatsArgs& a, float* red,
+                               float* rold, float* bsum) {
+    constexpr int NW = NTHR / kLanes;
+    const int tid = threadIdx.x;
     const int b = lt / d.strips;
     const int st = lt - b * d.strips;
-    const int row_begin = st * kStripRows;
-    const int row_end = min(row_begin + kStripRows, d.H);
-    const int W = d.W, ngroups = W / kVec;
-    const int64_t mat = static_cast<int64_t>(b) * d.H * W;
-    float* rstat = d.r + static_cast<int64_t>(b) * d.H;
+    StripCtx c;
+    c.row_begin = st * kStripRows;
+    c.row_end = min(c.row_begin + kStripRows, d.H);
+    c.W = d.W;
+    c.ngroups = d.W / kVec;
+    c.mat = static_cast<int64_t>(b) * d.H * d.W;
+    c.rstat = d.r + static_cast<int64_t>(b) * d.H;
+    c.rsum = 0.0f;
+    if (a.beta != 0.0f && tid < c.row_end - c.row_begin) rold[tid] = ldf(c.rstat + c.row_begin + tid);
 
     float cs[KMAX][kVec], ss[KMAX][kVec];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
 #pragma unroll
         for (int e = 0; e < kVec; ++e) { cs[k][e] = 0.0f; ss[k][e] = 0.0f; }
-    float rsum = 0.0f;  // threads < RB: sum of the new R over their rows
 
-    for (int r0 = row_begin; r0 < row_end; r0 += RB) {
-        const int nr = min(RB, row_end - r0);
-        // Raw gradient of the batch: bf16 -> 4 dwords per group, fp32 -> 8.
-        u32x4 gb[RB][KMAX];
-        f32x4 gf[RB][KMAX][2];
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                const int grp = tid + k * NTHR;
-                if (r < nr && grp < ngroups) {
-                    const int64_t off = mat + static_cast<int64_t>(r0 + r) * W + grp * kVec;
-                    if (BF16) {
-                        gb[r][k] = ld_u4<true>(static_cast<const uint16_t*>(d.g) + off);
-                    } else {
-                        gf[r][k][0] = ld_f4<true>(static_cast<const float*>(d.g) + off);
-                        gf[r][k][1] = ld_f4<true>(static_cast<const float*>(d.g) + off + 4);
-                    }
-                }
-            }
-        // Row sums of Q.
-        float rs[RB];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            float acc[kVec];
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) acc[e] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                const int grp = tid + k * NTHR;
-                if (r < nr && grp < ngroups) {
-                    float g[kVec];
-                    if (BF16) bf16x8(gb[r][k], g);
-                    else {
-                        g[0] = gf[r][k][0].x; g[1] = gf[r][k][0].y; g[2] = gf[r][k][0].z; g[3] = gf[r][k][0].w;
-                        g[4] = gf[r][k][1].x; g[5] = gf[r][k][1].y; g[6] = gf[r][k][1].z; g[7] = gf[r][k][1].w;
-                    }
-#pragma unroll
-                    for (int e = 0; e < kVec; ++e) acc[e] += fmaf(g[e], g[e], a.eps1);
-                }
-            }
-            rs[r] = wave_sum(sum8(acc));
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int r = 0; r < RB; ++r) red[w * RB + r] = rs[r];
-        }
-        __syncthreads();
-        if (tid < nr) {
-            float tot = red[tid];
-#pragma unroll
-            for (int i = 1; i < NW; ++i) tot += red[i * RB + tid];
-            const int row = r0 + tid;
-            const double mean = static_cast<double>(tot) / static_cast<double>(W);
-            const double rnew = a.beta != 0.0f ? a.dbeta * static_cast<double>(ldf(rstat + row)) + a.domb * mean
-                                               : mean;
-            const float r32 = static_cast<float>(rnew);
-            stf(rstat + row, r32);
-            rinv[tid] = 1.0f / r32;
-            rsum += r32;
-        }
-        __syncthreads();
-        // Column sums of Q and of G^2 / R_i.
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            if (r < nr) {
-                const float ri = rinv[r];
-#pragma unroll
-                for (int k = 0; k < KMAX; ++k) {
-                    const int grp = tid + k * NTHR;
-                    if (grp < ngroups) {
-                        float g[kVec];
-                        if (BF16) bf16x8(gb[r][k], g);
-                        else {
-                            g[0] = gf[r][k][0].x; g[1] = gf[r][k][0].y; g[2] = gf[r][k][0].z; g[3] = gf[r][k][0].w;
-                            g[4] = gf[r][k][1].x; g[5] = gf[r][k][1].y; g[6] = gf[r][k][1].z; g[7] = gf[r][k][1].w;
-                        }
-#pragma unroll
-                        for (int e = 0; e < kVec; ++e) {
-                            cs[k][e] += fmaf(g[e], g[e], a.eps1);
-                            ss[k][e] = fmaf(g[e] * g[e], ri, ss[k][e]);
-                        }
-                    }
-                }
-            }
-        }
+    GBatch<RB, KMAX, BF16> b0, b1;
+    load_batch<NTHR, RB, KMAX, BF16>(b0, d.g, c.mat, c.row_begin, min(RB, c.row_end - c.row_begin), c.W, c.ngroups);
+    for (int r0 = c.row_begin; r0 < c.row_end; r0 += 2 * RB) {
+        strip_batch<NTHR, KMAX, RB, BF16>(d, a, c, r0, 0, b0, b1, cs, ss, red, rold);
+        if (r0 + RB < c.row_end) strip_batch<NTHR, KMAX, RB, BF16>(d, a, c, r0 + RB, 1, b1, b0, cs, ss, red, rold);
     }
     // Per-strip column partials: colpart[b][st][0][:] = sum Q, [1][:] = sum G^2 / R.
-    float* cp = ws + d.colpart + (static_cast<int64_t>(b) * d.strips + st) * 2 * W;
+    float* cp = ws + d.colpart + (static_cast<int64_t>(b) * d.strips + st) * 2 * c.W;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         const int grp = tid + k * NTHR;
-        if (grp < ngroups) {
+        if (grp < c.ngroups) {
             store_f8(cp + grp * kVec, kVec, true, cs[k]);
-            store_f8(cp + W + grp * kVec, kVec, true, ss[k]);
+            store_f8(cp + c.W + grp * kVec, kVec, true, ss[k]);
         }
     }
-    float tr_ = rsum, unused = 0.0f;
+    float tr_ = c.rsum, unused = 0.0f;
     block_sum2<NW>(tr_, unused, bsum);
     if (tid == 0) stf(ws + d.tilepart + 2 * static_cast<int64_t>(lt), tr_);
 }
@@ -228,22 +267,22 @@ __device__ void rowstats_strip(const TDesc& d, int lt, float* __restrict__ ws, c
 constexpr int kRb0 = 4, kRb1 = 2;
 
 __global__ __launch_bounds__(256) void k_rowstats0(Table t, StatsArgs a) {
-    __shared__ float red[kWaves * kRb0], rinv[kRb0], bsum[2 * kWaves];
+    __shared__ float red[2 * kWaves * kRb0], rold[kStripRows], bsum[2 * kWaves];
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     if (d.mode == kFlat) stats_flat(d, it.y, t.ws, a, bsum);
-    else if (it.y < 0) xnorm_chunk<256>(d, -1 - it.y, t.ws, bsum);
-    else if (d.gbf16) rowstats_strip<256, 2, kRb0, true>(d, it.y, t.ws, a, red, rinv, bsum);
-    else rowstats_strip<256, 2, kRb0 / 2, false>(d, it.y, t.ws, a, red, rinv, bsum);
+    else if (it.y < 0) xnorm_chunk<256>(d, -1 - it.y, t.ws, a, bsum);
+    else if (d.gbf16) rowstats_strip<256, 2, kRb0, true>(d, it.y, t.ws, a, red, rold, bsum);
+    else rowstats_strip<256, 2, kRb0 / 2, false>(d, it.y, t.ws, a, red, rold, bsum);
 }
 
 __global__ __launch_bounds__(512) void k_rowstats1(Table t, StatsArgs a) {
-    __shared__ float red[8 * kRb1], rinv[kRb1], bsum[2 * 8];
+    __shared__ float red[2 * 8 * kRb1], rold[kStripRows], bsum[2 * 8];
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
-    if (it.y < 0) xnorm_chunk<512>(d, -1 - it.y, t.ws, bsum);
-    else if (d.gbf16) rowstats_strip<512, 3, kRb1, true>(d, it.y, t.ws, a, red, rinv, bsum);
-    else rowstats_strip<512, 3, kRb1 / 2, false>(d, it.y, t.ws, a, red, rinv, bsum);
+    if (it.y < 0) xnorm_chunk<512>(d, -1 - it.y, t.ws, a, bsum);
+    else if (d.gbf16) rowstats_strip<512, 3, kRb1, true>(d, it.y, t.ws, a, red, rold, bsum);
+    else rowstats_strip<512, 3, kRb1 / 2, false>(d, it.y, t.ws, a, red, rold, bsum);
 }
 
 void launch_rowstats(int cls, const Table& t, int64_t n, const StatsArgs& a, hipStream_t s) {
@@ -298,8 +337,11 @@ void launch_stats(const Table& t, int64_t n, const StatsArgs& a, hipStream_t s) 
 // ----------------------------------------------------------------------------- k_finalize
 
 // Items per matrix b: row-complete (first statistic): ncc column chunks; tiled (or
-// `tiled_all`): nrc row chunks then ncc column chunks.
+// `tiled_all`): nrc row chunks (kFinChunk rows) then ncc column chunks
+// (kFinCols columns). A column chunk is one column per lane, the strips (or row
+// tiles) split across the 4 waves, combined in wave order.
 __global__ __launch_bounds__(kThreads) void k_finalize(Table t, FinArgs a) {
+    __shared__ double part[kWaves][kLanes][2];
     __shared__ double lds[kWaves];
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
@@ -311,26 +353,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Table t, FinArgs a) {
     const int per = rc ? d.ncc : d.nrc + d.ncc;
     const int b = it.y / per;
     const int j = it.y - b * per;
-    if (rc) {
-        const int col = j * kFinChunk + threadIdx.x;
-        double u = 0.0;
-        if (col < d.W) {
-            const float* cp = ws + d.colpart + static_cast<int64_t>(b) * d.strips * 2 * d.W + col;
-            double sq = 0.0, sg = 0.0;
-            for (int st = 0; st < d.strips; ++st) {
-                sq += static_cast<double>(ldf(cp + static_cast<int64_t>(st) * 2 * d.W));
-                sg += static_cast<double>(ldf(cp + static_cast<int64_t>(st) * 2 * d.W + d.W));
-            }
-            float* dst = cs + static_cast<int64_t>(b) * d.W + col;
-            const double mean = sq / static_cast<double>(d.H);
-            const double cnew = beta != 0.0 ? beta * static_cast<double>(ldf(dst)) + omb * mean : mean;
-            const float c32 = static_cast<float>(cnew);
-            stf(dst, c32);
-            u = sg / static_cast<double>(c32);
-        }
-        const double tot = block_sum_d(u, lds);
-        if (threadIdx.x == 0) stf(ws + d.sumr + static_cast<int64_t>(b) * d.ncc + j, static_cast<float>(tot));
-    } else if (j < d.nrc) {
+    if (!rc && j < d.nrc) {
         const int row = j * kFinChunk + threadIdx.x;
         double rnew = 0.0;
         if (row < d.H) {
@@ -346,17 +369,44 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Table t, FinArgs a) {
         }
         const double tot = block_sum_d(rnew, lds);
         if (threadIdx.x == 0) stf(ws + d.sumr + static_cast<int64_t>(b) * d.nrc + j, static_cast<float>(tot));
-    } else {
-        const int col = (j - d.nrc) * kFinChunk + threadIdx.x;
-        if (col < d.W) {
+        return;
+    }
+    const int cj = rc ? j : j - d.nrc;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = cj * kFinCols + lane;
+    double sq = 0.0, sg = 0.0;
+    if (col < d.W) {
+        if (rc) {
+            const float* cp = ws + d.colpart + static_cast<int64_t>(b) * d.strips * 2 * d.W + col;
+#pragma unroll 4
+            for (int st = w; st < d.strips; st += kWaves) {
+                sq += static_cast<double>(ldf(cp + static_cast<int64_t>(st) * 2 * d.W));
+                sg += static_cast<double>(ldf(cp + static_cast<int64_t>(st) * 2 * d.W + d.W));
+            }
+        } else {
             const float* cp = ws + d.colpart + static_cast<int64_t>(b) * d.tr * d.W + col;
-            double s = 0.0;
-            for (int rt = 0; rt < d.tr; ++rt) s += static_cast<double>(ldf(cp + static_cast<int64_t>(rt) * d.W));
-            float* dst = cs + static_cast<int64_t>(b) * d.W + col;
-            const double mean = s / static_cast<double>(d.H);
-            const double cnew = beta != 0.0 ? beta * static_cast<double>(ldf(dst)) + omb * mean : mean;
-            stf(dst, static_cast<float>(cnew));
+#pragma unroll 4
+            for (int rt = w; rt < d.tr; rt += kWaves) sq += static_cast<double>(ldf(cp + static_cast<int64_t>(rt) * d.W));
         }
+    }
+    part[w][lane][0] = sq;
+    part[w][lane][1] = sg;
+    __syncthreads();
+    if (w != 0) return;
+    double u = 0.0;
+    if (col < d.W) {
+        sq = (part[0][lane][0] + part[1][lane][0]) + (part[2][lane][0] + part[3][lane][0]);
+        sg = (part[0][lane][1] + part[1][lane][1]) + (part[2][lane][1] + part[3][lane][1]);
+        float* dst = cs + static_cast<int64_t>(b) * d.W + col;
+        const double mean = sq / static_cast<double>(d.H);
+        const double cnew = beta != 0.0 ? beta * static_cast<double>(ldf(dst)) + omb * mean : mean;
+        const float c32 = static_cast<float>(cnew);
+        stf(dst, c32);
+        u = sg / static_cast<double>(c32);
+    }
+    if (rc) {
+        u = wave_sum(u);
+        if (lane == 0) stf(ws + d.sumr + static_cast<int64_t>(b) * d.ncc + cj, static_cast<float>(u));
     }
 }
 
@@ -485,10 +535,13 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
         if (lane == 0) wsum[w] = part;
         __syncthreads();
         su = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-        double a_ = 0.0;
-        for (int j = threadIdx.x; j < d.xchunks; j += kThreads) a_ += static_cast<double>(ldf(ws + d.xpart + j));
-        sx = block_sum_d(a_, lds);
-        __syncthreads();
+        sx = 0.0;
+        if (a.mode == kScalAdafactor && a.scale_parameter) {  // the chunks ran only then
+            double a_ = 0.0;
+            for (int j = threadIdx.x; j < d.xchunks; j += kThreads) a_ += static_cast<double>(ldf(ws + d.xpart + j));
+            sx = block_sum_d(a_, lds);
+            __syncthreads();
+        }
     } else {
         const int tiles = d.mode == kFlat ? d.tc : d.B * d.tr * d.tc;
         su = tile_sum(tp, tiles, 0, lds);

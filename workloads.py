@@ -184,20 +184,21 @@ def _pick(wl: Workload, indices):
     return [(k, wl.specs[k]) for k in ks]
 
 
-def init_params(wl: Workload, device="cpu", indices=None) -> List[torch.Tensor]:
+def init_params(wl: Workload, device="cpu", indices=None, out=None) -> List[torch.Tensor]:
     """fp32 parameters: 2-D+ weights N(0, 0.02) (std 0.02), norm weights 1, biases 0.
-    ``indices`` selects tensors (same draws as in the full list)."""
-    out = []
-    for k, s in _pick(wl, indices):
+    ``indices`` selects tensors (same draws as in the full list); ``out`` gives the
+    fp32 tensors to fill in place (e.g. views into one flat buffer)."""
+    res = []
+    for j, (k, s) in enumerate(_pick(wl, indices)):
+        t = out[j] if out is not None else torch.empty(s.shape, dtype=torch.float32, device=device)
         if s.kind == "weight":
-            t = torch.empty(s.shape, dtype=torch.float32, device=device)
-            t.normal_(0.0, 0.02, generator=_gen(wl, k, 0, device))
+            t.normal_(0.0, 0.02, generator=_gen(wl, k, 0, t.device))
         elif s.kind == "norm":
-            t = torch.ones(s.shape, dtype=torch.float32, device=device)
+            t.fill_(1.0)
         else:
-            t = torch.zeros(s.shape, dtype=torch.float32, device=device)
-        out.append(t)
-    return out
+            t.zero_()
+        res.append(t)
+    return res
 
 
 def _log_uniform(n: int, gen: torch.Generator, device) -> torch.Tensor:
@@ -224,11 +225,12 @@ def grad_scales(wl: Workload, device="cpu", indices=None
     return out
 
 
-def grads(wl: Workload, step_index: int, scales, device="cpu", indices=None) -> List[torch.Tensor]:
+def grads(wl: Workload, step_index: int, scales, device="cpu", indices=None, out=None) -> List[torch.Tensor]:
     """Gradients of 0-based step ``step_index``: std * z * row_scale * col_scale,
     z ~ N(0, 1) redrawn each step, computed in fp32 then cast to the grad dtype.
-    ``scales`` must come from grad_scales with the same ``indices``."""
-    out = []
+    ``scales`` must come from grad_scales with the same ``indices``; ``out`` gives
+    tensors of the grad dtype to fill in place."""
+    res = []
     for j, (k, s) in enumerate(_pick(wl, indices)):
         z = torch.empty(s.shape, dtype=torch.float32, device=device)
         z.normal_(0.0, 1.0, generator=_gen(wl, k, 2 + step_index, device))
@@ -241,5 +243,9 @@ def grads(wl: Workload, step_index: int, scales, device="cpu", indices=None) -> 
                 g = g * a.unsqueeze(-1)
                 if b is not None:
                     g = g * b
-        out.append(g.to(wl.grad_dtype).contiguous())
-    return out
+        if out is not None:
+            out[j].copy_(g)
+            res.append(out[j])
+        else:
+            res.append(g.to(wl.grad_dtype).contiguous())
+    return res
