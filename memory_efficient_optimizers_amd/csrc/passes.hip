@@ -28,15 +28,19 @@ namespace meo {
 
 // ----------------------------------------------------------------------------- flat first pass
 
+// Block of NTHR threads over one flat tile of kFlatTile elements; `lds` holds
+// 2 * NTHR / 64 floats.
+template <int NTHR>
 __device__ void stats_flat(const TDesc& d, int lt, float* __restrict__ ws, const StatsArgs& a, float* lds) {
+    constexpr int ITERS = kFlatTile / (NTHR * kVec);
     const bool vec = d.vec, bf = d.gbf16;
     const float beta = a.beta, omb = a.omb;
     const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
     float su[kVec], sx[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) { su[e] = 0.0f; sx[e] = 0.0f; }
-    for (int it = 0; it < kFlatIters; ++it) {
-        const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
+    for (int it = 0; it < ITERS; ++it) {
+        const int64_t i = base + (static_cast<int64_t>(it) * NTHR + threadIdx.x) * kVec;
         const int valid = clamp_valid(d.numel - i);
         if (valid == 0) break;
         float g[kVec], v[kVec] = {};
@@ -58,7 +62,7 @@ __device__ void stats_flat(const TDesc& d, int lt, float* __restrict__ ws, const
         }
     }
     float tu = sum8(su), tx = sum8(sx);
-    block_sum2<kWaves>(tu, tx, lds);
+    block_sum2<NTHR / kLanes>(tu, tx, lds);
     if (threadIdx.x == 0) {
         float* tp = ws + d.tilepart + 2 * static_cast<int64_t>(lt);
         stf(tp, tu);
@@ -79,7 +83,7 @@ __device__ void xnorm_chunk(const TDesc& d, int c, float* __restrict__ ws, const
     float sx[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) sx[e] = 0.0f;
-#pragma unroll 4
+#pragma unroll 8
     for (int it = 0; it < ITERS; ++it) {
         const int64_t i = base + (static_cast<int64_t>(it) * NTHR + threadIdx.x) * kVec;
         const int valid = clamp_valid(d.numel - i);
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(256) void k_rowstats0(Table t, StatsArgs a) {
     __shared__ float red[2 * kWaves * kRb0], rold[kStripRows], bsum[2 * kWaves];
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
-    if (d.mode == kFlat) stats_flat(d, it.y, t.ws, a, bsum);
+    if (d.mode == kFlat) stats_flat<256>(d, it.y, t.ws, a, bsum);
     else if (it.y < 0) xnorm_chunk<256>(d, -1 - it.y, t.ws, a, bsum);
     else if (d.gbf16) rowstats_strip<256, 2, kRb0, true>(d, it.y, t.ws, a, red, rold, bsum);
     else rowstats_strip<256, 2, kRb0 / 2, false>(d, it.y, t.ws, a, red, rold, bsum);

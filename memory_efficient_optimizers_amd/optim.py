@@ -78,6 +78,8 @@ class Adafactor(_MeoOptimizer):
     scale_parameter=True, relative_step=True, warmup_init=False."""
 
     _kind = "adafactor"
+    _HP = ("lr", "eps", "clip_threshold", "decay_rate", "beta1", "weight_decay", "scale_parameter",
+           "relative_step", "warmup_init")
 
     def __init__(self, params, lr=None, eps=(1e-30, 1e-3), clip_threshold=1.0, decay_rate=-0.8,
                  beta1=None, weight_decay=0.0, scale_parameter=True, relative_step=True,
@@ -98,7 +100,7 @@ class Adafactor(_MeoOptimizer):
         return _lib.meo_adafactor_workspace_size(params, grads)
 
     def _call(self, group, step, params, grads, states, ws):
-        hp = _lib.adafactor_hparams(**{k: group[k] for k in self.defaults})
+        hp = _lib.adafactor_hparams(**{k: group[k] for k in self._HP})
         _lib.meo_adafactor_step(hp, step, params, grads, states, ws)
 
 
@@ -108,6 +110,7 @@ class CAME(_MeoOptimizer):
     weight_decay=0.0; lr must be given."""
 
     _kind = "came"
+    _HP = ("lr", "eps", "clip_threshold", "betas", "weight_decay")
 
     def __init__(self, params, lr=None, eps=(1e-30, 1e-16), clip_threshold=1.0,
                  betas=(0.9, 0.999, 0.9999), weight_decay=0.0):
@@ -124,7 +127,7 @@ class CAME(_MeoOptimizer):
         return _lib.meo_came_workspace_size(params, grads)
 
     def _call(self, group, step, params, grads, states, ws):
-        hp = _lib.came_hparams(**{k: group[k] for k in self.defaults})
+        hp = _lib.came_hparams(**{k: group[k] for k in self._HP})
         _lib.meo_came_step(hp, step, params, grads, states, ws)
 
 
@@ -133,6 +136,7 @@ class Lamb(_MeoOptimizer):
     betas=(0.9, 0.999), eps=1e-6, weight_decay=0, bias_correction=True."""
 
     _kind = "lamb"
+    _HP = ("lr", "betas", "eps", "weight_decay", "bias_correction")
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-6, weight_decay=0.0,
                  bias_correction=True):
@@ -154,5 +158,5 @@ class Lamb(_MeoOptimizer):
         return _lib.meo_lamb_workspace_size(params, grads)
 
     def _call(self, group, step, params, grads, states, ws):
-        hp = _lib.lamb_hparams(**{k: group[k] for k in self.defaults})
+        hp = _lib.lamb_hparams(**{k: group[k] for k in self._HP})
         _lib.meo_lamb_step(hp, step, params, grads, states, ws)

@@ -1,0 +1,160 @@
+"""Behaviour of the library and its torch.optim front ends beyond single-call
+parity: resume from a state_dict, NaN confinement, mixed gradient dtypes, several
+parameter groups, non-default streams, all-or-nothing validation, and the launch
+table cache."""
+import math
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from memory_efficient_optimizers_amd import CAME, Adafactor, Lamb, _lib
+from tests.harness import TOL_F32, Run, lib_hp, lib_states, lib_step, lib_workspace, output_err, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.load()
+
+
+SHAPES = [(96, 520), (520,), (3, 17, 40), (64, 1024)]
+
+
+def _params(seed=0):
+    wl = workloads.custom("robust", "adafactor", SHAPES, seed=seed)
+    return wl, [torch.nn.Parameter(p) for p in workloads.init_params(wl, "cuda")]
+
+
+@pytest.mark.parametrize("cls,hp", [(Adafactor, {"beta1": 0.9}), (CAME, {"lr": 2e-4}),
+                                    (Lamb, {"weight_decay": 0.01})])
+def test_state_dict_resume_is_bitwise(cls, hp):
+    """5 steps == 3 steps, state_dict(), a fresh optimizer loading it, 2 more steps."""
+    wl, ps_a = _params()
+    _, ps_b = _params()
+    scales = workloads.grad_scales(wl, "cuda")
+    opt_a = cls(ps_a, **hp)
+    opt_b = cls(ps_b, **hp)
+    for t in range(5):
+        gs = workloads.grads(wl, t, scales, "cuda")
+        for p, g in zip(ps_a, gs):
+            p.grad = g.clone()
+        opt_a.step()
+        if t < 3:
+            for p, g in zip(ps_b, gs):
+                p.grad = g.clone()
+            opt_b.step()
+        if t == 2:
+            sd = opt_b.state_dict()
+            opt_b = cls(ps_b, **hp)
+            opt_b.load_state_dict(sd)
+        if t >= 3:
+            for p, g in zip(ps_b, gs):
+                p.grad = g.clone()
+            opt_b.step()
+    torch.cuda.synchronize()
+    for a, b in zip(ps_a, ps_b):
+        assert torch.equal(a.detach(), b.detach())
+    for a, b in zip(ps_a, ps_b):
+        for k, v in opt_a.state[a].items():
+            if torch.is_tensor(v):
+                assert torch.equal(v, opt_b.state[b][k]), k
+            else:
+                assert v == opt_b.state[b][k]
+
+
+@pytest.mark.parametrize("opt,hp", [("adafactor", {"beta1": 0.9}), ("came", {"lr": 2e-4}), ("lamb", {})])
+def test_nan_gradient_stays_in_its_tensor(opt, hp):
+    """A NaN in one tensor's gradient propagates to that tensor's update only; the
+    other tensors of the call match the oracle."""
+    wl = workloads.custom("nan", opt, SHAPES, hparams=hp)
+    run = Run(wl)
+    gs = run.grads(0)
+    gs[0][5, 7] = float("nan")
+    run.t += 1
+    ws = lib_workspace(opt, run.params, gs)
+    lib_step(opt, run.hps, run.t, run.params, gs, run.states, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(run.params[0]).any()
+    for k in range(1, len(SHAPES)):
+        xk, _ = oracle.STEP_TENSOR[opt](run.ox[k], to64(gs[k]), run.ost[k], run.hp, 1)
+        assert torch.isfinite(run.params[k]).all()
+        assert output_err("param", to64(run.params[k]), xk) <= TOL_F32
+
+
+def test_mixed_gradient_dtypes_in_one_call():
+    wl32 = workloads.custom("m32", "adafactor", SHAPES, hparams={"beta1": 0.9}, grad_dtype=torch.float32)
+    run = Run(wl32)
+    gs = run.grads(0)
+    gs = [g.to(torch.bfloat16) if k % 2 == 0 else g for k, g in enumerate(gs)]
+    run.step(gs)
+    err, name = run.worst()
+    assert err <= TOL_F32, (name, err)
+
+
+def test_param_groups_and_side_stream():
+    """Two groups with different hyperparameters, stepped on a non-default stream,
+    equal two separate library calls."""
+    wl, ps = _params()
+    scales = workloads.grad_scales(wl, "cuda")
+    gs = workloads.grads(wl, 0, scales, "cuda")
+    ref = [p.detach().clone() for p in ps]
+    opt = Adafactor([{"params": ps[:2]}, {"params": ps[2:], "beta1": 0.5, "weight_decay": 0.1}])
+    for p, g in zip(ps, gs):
+        p.grad = g
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        opt.step()
+    torch.cuda.current_stream().wait_stream(side)
+    st1 = lib_states("adafactor", ref[:2], {})
+    st2 = lib_states("adafactor", ref[2:], {"beta1": 0.5})
+    lib_step("adafactor", _lib.adafactor_hparams(), 1, ref[:2], gs[:2], st1, lib_workspace("adafactor", ref[:2], gs[:2]))
+    lib_step("adafactor", _lib.adafactor_hparams(beta1=0.5, weight_decay=0.1), 1, ref[2:], gs[2:], st2,
+             lib_workspace("adafactor", ref[2:], gs[2:]))
+    torch.cuda.synchronize()
+    for p, q in zip(ps, ref):
+        assert torch.equal(p.detach(), q)
+
+
+def test_rejected_call_changes_nothing():
+    """Validation is all-or-nothing: a bad last tensor leaves the whole list as it was."""
+    wl = workloads.custom("rej", "adafactor", SHAPES, hparams={"beta1": 0.9})
+    run = Run(wl)
+    gs = run.grads(0)
+    before = [p.clone() for p in run.params] + [v.clone() for st in run.states for v in st.values()]
+    bad = [dict(s) for s in run.states]
+    del bad[-1]["exp_avg"]
+    ws = lib_workspace("adafactor", run.params, gs)
+    with pytest.raises(_lib.MeoError) as e:
+        lib_step("adafactor", run.hps, 1, run.params, gs, bad, ws)
+    assert e.value.code == _lib.MEO_ENULL
+    with pytest.raises(_lib.MeoError):
+        lib_step("adafactor", _lib.adafactor_hparams(lr=1e-3), 1, run.params, gs, run.states, ws)
+    torch.cuda.synchronize()
+    after = [p for p in run.params] + [v for st in run.states for v in st.values()]
+    for a, b in zip(before, after):
+        assert torch.equal(a, b)
+
+
+def test_launch_table_cache_eviction():
+    """More distinct tensor lists than the cache holds, revisited: results stay exact."""
+    outs = {}
+    for rep in range(2):
+        for i in range(20):
+            shape = (8 + i, 64 + 8 * i)
+            wl = workloads.custom(f"ev{i}", "adafactor", [shape], hparams={"beta1": 0.9}, seed=i)
+            run = Run(wl)
+            run.step()
+            torch.cuda.synchronize()
+            if rep == 0:
+                outs[i] = run.params[0].clone()
+                err, name = run.worst()
+                assert err <= TOL_F32
+            else:
+                assert torch.equal(outs[i], run.params[0])
+    _lib.meo_release_plans()
