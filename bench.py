@@ -34,8 +34,11 @@ HBM_PEAK_GBPS = 8000.0
 
 
 def _bytes_per_param(wl, spec, numel) -> dict:
-    """Algorithmic bytes of one tensor: whole step, and per pass."""
+    """Algorithmic bytes of one tensor: whole step, and per pass. gb, xb, mb: bytes
+    per element of the gradient, the parameter and the first moment."""
     gb = 2 if str(wl.grad_dtype).endswith("bfloat16") else 4
+    xb = 2 if str(wl.param_dtype).endswith("bfloat16") else 4
+    mb = 2 if str(wl.state_dtype).endswith("bfloat16") else 4
     fac = len(spec.shape) >= 2 and wl.optimizer != "lamb"
     n = numel
     if fac:
@@ -45,16 +48,16 @@ def _bytes_per_param(wl, spec, numel) -> dict:
         rc = 0
     if wl.optimizer == "adafactor":
         mom = wl.hparams.get("beta1") is not None
-        step = n * (gb + 8 + (8 if mom else 0) + (0 if fac else 8)) + 8 * rc
-        apply = n * (gb + 8 + (8 if mom else 0) + (0 if fac else 4)) + 4 * rc
+        step = n * (gb + 2 * xb + (2 * mb if mom else 0) + (0 if fac else 8)) + 8 * rc
+        apply = n * (gb + 2 * xb + (2 * mb if mom else 0) + (0 if fac else 4)) + 4 * rc
         return {"step": step, "adafactor_apply": apply}
     if wl.optimizer == "came":
-        step = n * (gb + 8 + 8 + (0 if fac else 8)) + 16 * rc
-        mom = n * (gb + 8 + (0 if fac else 12)) + 4 * rc   # G, M rw (1-D: also V read, X rw)
-        app = (n * 12 + 4 * rc) if fac else 0               # M read, X rw
+        step = n * (gb + 2 * xb + 2 * mb + (0 if fac else 8)) + 16 * rc
+        mom = n * (gb + 2 * mb + (0 if fac else 4 + 2 * xb)) + 4 * rc   # G, M rw (1-D: also V read, X rw)
+        app = (n * (mb + 2 * xb) + 4 * rc) if fac else 0                 # M read, X rw
         return {"step": step, "came_mom": mom, "came_apply": app}
-    step = n * (gb + 8 + 8 + 8)
-    return {"step": step, "lamb_moments": n * (gb + 4 + 16), "lamb_apply": n * 16}
+    step = n * (gb + 2 * xb + 2 * mb + 8)
+    return {"step": step, "lamb_moments": n * (gb + xb + 2 * mb + 8), "lamb_apply": n * (2 * xb + mb + 4)}
 
 
 def algorithmic_bytes(wl) -> dict:
@@ -74,14 +77,15 @@ def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
     import workloads
 
     hp = dict(wl.hparams)
+    storage = dict(param_bf16=wl.param_dtype == torch.bfloat16, exp_avg_bf16=wl.state_dtype == torch.bfloat16)
     done, spent, names = 0, 0.0, []
     for k, spec in enumerate(wl.specs):
-        x = workloads.init_params(wl, "cpu", [k])[0].double().numpy()
+        x = workloads.init_params(wl, "cpu", [k])[0].to(torch.float64).numpy()
         sc = workloads.grad_scales(wl, "cpu", [k])
         g = workloads.grads(wl, 0, sc, "cpu", [k])[0].to(torch.float64).numpy()
         st = oracle.INIT_STATE[wl.optimizer](x.shape, hp)
         t0 = time.perf_counter()
-        oracle.STEP_TENSOR[wl.optimizer](x, g, st, hp, 1)
+        oracle.STEP_TENSOR[wl.optimizer](x, g, st, hp, 1, **storage)
         spent += time.perf_counter() - t0
         done += x.size
         names.append(spec.name)
@@ -188,7 +192,7 @@ def main() -> int:
         # One flat buffer per kind (parameters, gradients, each state), tensors as
         # 256-byte aligned views, as flat-parameter training frameworks keep them.
         shapes = [s.shape for s in wl.specs]
-        params = flat_views(torch, shapes, torch.float32, dev)
+        params = flat_views(torch, shapes, wl.param_dtype, dev)
         workloads.init_params(wl, dev, out=params)
         grads = flat_views(torch, shapes, wl.grad_dtype, dev)
         workloads.grads(wl, 0, workloads.grad_scales(wl, dev), dev, out=grads)
@@ -196,14 +200,15 @@ def main() -> int:
         states = [dict() for _ in shapes]
         for key in sorted({k for st in proto for k in st}):
             idx = [i for i, st in enumerate(proto) if key in st]
-            views = flat_views(torch, [proto[i][key] for i in idx], torch.float32, dev)
+            dt = wl.state_dtype if key == "exp_avg" else torch.float32
+            views = flat_views(torch, [proto[i][key] for i in idx], dt, dev)
             for i, v in zip(idx, views):
                 v.zero_()
                 states[i][key] = v
     else:
         params = workloads.init_params(wl, dev)
         grads = workloads.grads(wl, 0, workloads.grad_scales(wl, dev), dev)
-        states = [_lib.init_state(wl.optimizer, p, beta1=beta1) for p in params]
+        states = [_lib.init_state(wl.optimizer, p, beta1=beta1, state_dtype=wl.state_dtype) for p in params]
     hps = {"adafactor": _lib.adafactor_hparams, "came": _lib.came_hparams,
            "lamb": _lib.lamb_hparams}[wl.optimizer](**hp)
     wsize = getattr(_lib, f"meo_{wl.optimizer}_workspace_size")(params, grads)
@@ -259,7 +264,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "optimizer": wl.optimizer, "tensors": len(wl.specs), "layout": args.layout,
                    "params": numel, "grad_dtype": str(wl.grad_dtype).replace("torch.", ""),
-                   "param_state_dtype": "float32",
+                   "param_dtype": str(wl.param_dtype).replace("torch.", ""),
+                   "exp_avg_dtype": str(wl.state_dtype).replace("torch.", ""),
                    "hparams": {k: (list(v) if isinstance(v, tuple) else v) for k, v in hp.items()}},
         "hbm": {"step_bytes": ab["step"], "achieved": step_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": step_gbps / HBM_PEAK_GBPS},

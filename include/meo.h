@@ -23,8 +23,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor, state and workspace pointers are DEVICE pointers owned by the
- *   caller. Parameters and states are float32 and updated in place; gradients
- *   are read only. Every buffer is contiguous and row-major (last dim
+ *   caller, in memory of the current device allocated through HIP (hipMalloc,
+ *   hipMallocManaged, or an allocator built on them such as PyTorch's).
+ *   Parameters and states (float32, or bf16 where noted) are updated in place;
+ *   gradients are read only. Every buffer is contiguous and row-major (last dim
  *   innermost). Buffers must not alias one another. fp32 buffers need 4-byte
  *   alignment and bf16 ones 2-byte alignment; 16-byte alignment (and, for
  *   factored tensors, cols % 8 == 0) selects the vectorised path.
@@ -35,7 +37,11 @@
  * - `step` is the 1-based index of the step being taken (the caller increments
  *   its counter before the call); all tensors of one call share it.
  * - Every argument is validated on the host before anything is enqueued: a
- *   failing call leaves every tensor untouched. Return value: MEO_OK, or a
+ *   failing call leaves every tensor untouched. Besides values, shapes, dtypes
+ *   and alignment, a step checks with the HIP runtime that the workspace
+ *   (every call) and every tensor and state (when a launch table is built)
+ *   lies inside one device allocation of the current device (MEO_EWORKSPACE,
+ *   MEO_EMEMORY); meo_*_validate does not touch the device and skips this. Return value: MEO_OK, or a
  *   negative MEO_E* code with a message available from meo_last_error().
  * - Tensors with zero elements are skipped.
  * - `workspace` is device scratch of at least meo_*_workspace_size() bytes,
@@ -56,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MEO_VERSION 1
+#define MEO_VERSION 2
 
 /* Return codes. */
 #define MEO_OK          0
@@ -67,6 +73,9 @@ extern "C" {
 #define MEO_EWORKSPACE (-5) /* workspace NULL, misaligned or too small        */
 #define MEO_EALIGN     (-6) /* tensor pointer misaligned for its dtype        */
 #define MEO_EHIP       (-7) /* HIP runtime error while enqueueing             */
+#define MEO_EMEMORY    (-8) /* a tensor or state pointer is not device memory
+                               of the current device, or the range it
+                               describes passes the end of its allocation   */
 
 /* Element types. */
 #define MEO_F32  0
@@ -81,16 +90,28 @@ extern "C" {
  * LAMB ignores the view and treats the tensor as one flat layer.
  */
 typedef struct meo_tensor {
-    void*       param;       /* float32 [batch*rows*cols], updated in place   */
+    void*       param;       /* param_dtype [batch*rows*cols], updated in place */
     const void* grad;        /* grad_dtype [batch*rows*cols], read only        */
     int64_t     batch;
     int64_t     rows;
     int64_t     cols;
     int32_t     ndim;        /* the tensor's number of dims (0, 1, 2, ...)     */
-    int32_t     param_dtype; /* MEO_F32                                        */
+    int32_t     param_dtype; /* MEO_F32 or MEO_BF16                            */
     int32_t     grad_dtype;  /* MEO_F32 or MEO_BF16                            */
-    int32_t     reserved;    /* set to 0                                       */
+    int32_t     state_dtype; /* element type of this tensor's exp_avg (first
+                                moment): MEO_F32 or MEO_BF16; every other state
+                                array is float32                               */
 } meo_tensor;
+
+/*
+ * 16-bit storage (the memory-saving 16-bit path that the page's DistributedCAME
+ * paragraph says CAME supports). A bf16 parameter or first moment is widened to
+ * float32 on load, every step computes in float32, and each new value is rounded
+ * to the nearest bf16 (ties to even) when it is formed: later uses within the same
+ * step (the update, CAME's instability, LAMB's direction) see the rounded first
+ * moment, exactly what the next step will read back. Statistics, second moments
+ * and the workspace stay float32. A bf16 pointer must be 2-byte aligned.
+ */
 
 /* ------------------------------------------------------------------ Adafactor */
 
@@ -121,10 +142,11 @@ typedef struct meo_adafactor_hparams {
     int32_t reserved;
 } meo_adafactor_hparams;
 
-/* Per-tensor state, float32, caller-allocated, zero before the first step.
+/* Per-tensor state, caller-allocated, zero before the first step; float32 except
+ * exp_avg, whose type is the tensor's state_dtype.
  * Names follow the page ("Step 3"). */
 typedef struct meo_adafactor_state {
-    float* exp_avg;        /* [numel]; required iff has_beta1, else ignored     */
+    void*  exp_avg;        /* state_dtype [numel]; required iff has_beta1       */
     float* exp_avg_sq_row; /* [batch*rows]; factored tensors only               */
     float* exp_avg_sq_col; /* [batch*cols]; factored tensors only               */
     float* exp_avg_sq;     /* [numel]; 1-D tensors only                          */
@@ -160,10 +182,11 @@ typedef struct meo_came_hparams {
     int32_t reserved;
 } meo_came_hparams;
 
-/* Per-tensor state, float32, zero before the first step. The confidence
- * statistic is factored like the squared-gradient one. */
+/* Per-tensor state, zero before the first step; float32 except exp_avg
+ * (state_dtype). The confidence statistic is factored like the squared-gradient
+ * one. */
 typedef struct meo_came_state {
-    float* exp_avg;         /* [numel], always required                          */
+    void*  exp_avg;         /* state_dtype [numel], always required              */
     float* exp_avg_sq_row;  /* [batch*rows]; factored only                       */
     float* exp_avg_sq_col;  /* [batch*cols]; factored only                       */
     float* exp_avg_res_row; /* [batch*rows]; factored only                       */
@@ -198,8 +221,10 @@ typedef struct meo_lamb_hparams {
     int32_t reserved;
 } meo_lamb_hparams;
 
+/* Per-tensor state, zero before the first step; exp_avg is state_dtype,
+ * exp_avg_sq float32. */
 typedef struct meo_lamb_state {
-    float* exp_avg;    /* [numel] */
+    void*  exp_avg;    /* state_dtype [numel] */
     float* exp_avg_sq; /* [numel] */
 } meo_lamb_state;
 

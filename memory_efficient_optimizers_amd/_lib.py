@@ -22,12 +22,12 @@ c_int32, c_int64, c_double, c_void_p, c_size_t = (ctypes.c_int32, ctypes.c_int64
                                                   ctypes.c_void_p, ctypes.c_size_t)
 c_float_p = ctypes.POINTER(ctypes.c_float)
 
-MEO_OK, MEO_EINVAL, MEO_ESHAPE, MEO_EDTYPE, MEO_ENULL, MEO_EWORKSPACE, MEO_EALIGN, MEO_EHIP = (
-    0, -1, -2, -3, -4, -5, -6, -7)
+MEO_OK, MEO_EINVAL, MEO_ESHAPE, MEO_EDTYPE, MEO_ENULL, MEO_EWORKSPACE, MEO_EALIGN, MEO_EHIP, MEO_EMEMORY = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8)
 MEO_F32, MEO_BF16 = 0, 1
 ERROR_NAMES = {MEO_EINVAL: "MEO_EINVAL", MEO_ESHAPE: "MEO_ESHAPE", MEO_EDTYPE: "MEO_EDTYPE",
                MEO_ENULL: "MEO_ENULL", MEO_EWORKSPACE: "MEO_EWORKSPACE", MEO_EALIGN: "MEO_EALIGN",
-               MEO_EHIP: "MEO_EHIP"}
+               MEO_EHIP: "MEO_EHIP", MEO_EMEMORY: "MEO_EMEMORY"}
 EXPORTS = [
     "meo_adafactor_defaults", "meo_adafactor_workspace_size", "meo_adafactor_validate",
     "meo_adafactor_step", "meo_came_defaults", "meo_came_workspace_size", "meo_came_validate",
@@ -48,7 +48,7 @@ class MeoError(RuntimeError):
 class meo_tensor(ctypes.Structure):
     _fields_ = [("param", c_void_p), ("grad", c_void_p), ("batch", c_int64), ("rows", c_int64),
                 ("cols", c_int64), ("ndim", c_int32), ("param_dtype", c_int32),
-                ("grad_dtype", c_int32), ("reserved", c_int32)]
+                ("grad_dtype", c_int32), ("state_dtype", c_int32)]
 
 
 class meo_adafactor_hparams(ctypes.Structure):
@@ -140,12 +140,19 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def tensor_struct(param: torch.Tensor, grad: torch.Tensor) -> meo_tensor:
-    """[batch, rows, cols] view of a parameter and its gradient (see meo.h)."""
-    if param.dtype != torch.float32:
-        raise TypeError("parameters must be float32")
-    if grad.dtype not in (torch.float32, torch.bfloat16):
+_DTYPE = {torch.float32: MEO_F32, torch.bfloat16: MEO_BF16}
+
+
+def tensor_struct(param: torch.Tensor, grad: torch.Tensor,
+                  state_dtype: torch.dtype = torch.float32) -> meo_tensor:
+    """[batch, rows, cols] view of a parameter and its gradient (see meo.h);
+    ``state_dtype`` is the element type of the parameter's first moment."""
+    if param.dtype not in _DTYPE:
+        raise TypeError("parameters must be float32 or bfloat16")
+    if grad.dtype not in _DTYPE:
         raise TypeError("gradients must be float32 or bfloat16")
+    if state_dtype not in _DTYPE:
+        raise TypeError("the first moment must be float32 or bfloat16")
     if not (param.is_contiguous() and grad.is_contiguous()):
         raise ValueError("parameter and gradient must be contiguous")
     if grad.shape != param.shape:
@@ -158,16 +165,19 @@ def tensor_struct(param: torch.Tensor, grad: torch.Tensor) -> meo_tensor:
         rows, cols = shape[-2], shape[-1]
     else:
         batch, rows, cols = 1, 1, param.numel()
-    return meo_tensor(param.data_ptr(), grad.data_ptr(), batch, rows, cols, len(shape), MEO_F32,
-                      MEO_BF16 if grad.dtype == torch.bfloat16 else MEO_F32, 0)
+    return meo_tensor(param.data_ptr(), grad.data_ptr(), batch, rows, cols, len(shape),
+                      _DTYPE[param.dtype], _DTYPE[grad.dtype], _DTYPE[state_dtype])
 
 
-def _tensors(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor]):
+def _tensors(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor], states=None):
     if len(params) != len(grads):
         raise ValueError("params and grads differ in length")
+    if states is not None and len(states) != len(params):
+        raise ValueError("params and states differ in length")
     arr = (meo_tensor * max(len(params), 1))()
     for i, (p, g) in enumerate(zip(params, grads)):
-        arr[i] = tensor_struct(p, g)
+        m = None if states is None else states[i].get("exp_avg")
+        arr[i] = tensor_struct(p, g, torch.float32 if m is None else m.dtype)
     return arr
 
 
@@ -188,6 +198,10 @@ def _ws(workspace: Optional[torch.Tensor]):
 def _states(cls, keys, states: Sequence[Dict[str, torch.Tensor]]):
     arr = (cls * max(len(states), 1))()
     for i, st in enumerate(states):
+        for k in keys:
+            t = st.get(k)
+            if t is not None and t.dtype != torch.float32 and not (k == "exp_avg" and t.dtype == torch.bfloat16):
+                raise TypeError(f"state {k} must be float32" + (" or bfloat16" if k == "exp_avg" else ""))
         arr[i] = cls(*[_ptr(st.get(k)) for k in keys])
     return arr
 
@@ -256,36 +270,36 @@ def meo_lamb_workspace_size(params, grads) -> int:
 
 
 def meo_adafactor_validate(hp, step, params, grads, states) -> None:
-    _check(load().meo_adafactor_validate(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+    _check(load().meo_adafactor_validate(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
                                          _states(meo_adafactor_state, ADAFACTOR_KEYS, states)))
 
 
 def meo_came_validate(hp, step, params, grads, states) -> None:
-    _check(load().meo_came_validate(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+    _check(load().meo_came_validate(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
                                     _states(meo_came_state, CAME_KEYS, states)))
 
 
 def meo_lamb_validate(hp, step, params, grads, states) -> None:
-    _check(load().meo_lamb_validate(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+    _check(load().meo_lamb_validate(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
                                     _states(meo_lamb_state, LAMB_KEYS, states)))
 
 
 def meo_adafactor_step(hp, step, params, grads, states, workspace=None, stream=None) -> None:
     ws, nb = _ws(workspace)
-    _check(load().meo_adafactor_step(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+    _check(load().meo_adafactor_step(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
                                      _states(meo_adafactor_state, ADAFACTOR_KEYS, states), ws, nb,
                                      _stream(stream)))
 
 
 def meo_came_step(hp, step, params, grads, states, workspace=None, stream=None) -> None:
     ws, nb = _ws(workspace)
-    _check(load().meo_came_step(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+    _check(load().meo_came_step(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
                                 _states(meo_came_state, CAME_KEYS, states), ws, nb, _stream(stream)))
 
 
 def meo_lamb_step(hp, step, params, grads, states, workspace=None, stream=None) -> None:
     ws, nb = _ws(workspace)
-    _check(load().meo_lamb_step(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+    _check(load().meo_lamb_step(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
                                 _states(meo_lamb_state, LAMB_KEYS, states), ws, nb, _stream(stream)))
 
 
@@ -330,7 +344,7 @@ class PreparedStep:
         self.fn = getattr(load(), f"meo_{optimizer}_step")
         self.hp = hp
         self.n = len(params)
-        self.tensors = _tensors(params, grads)
+        self.tensors = _tensors(params, grads, states)
         self.states = _states(cls, keys, states)
         self.ws, self.ws_bytes = _ws(workspace)
         self._keep = (list(params), list(grads), list(states), workspace)
@@ -343,7 +357,7 @@ class PreparedStep:
 # ----------------------------------------------------------------------------- state allocation
 
 def state_shapes(optimizer: str, shape, *, beta1: bool = True) -> Dict[str, tuple]:
-    """Shapes of the fp32 state tensors of one parameter, as meo.h expects them."""
+    """Shapes of the state tensors of one parameter, as meo.h expects them."""
     shape = tuple(shape)
     if optimizer == "lamb":
         return {"exp_avg": shape, "exp_avg_sq": shape}
@@ -361,9 +375,11 @@ def state_shapes(optimizer: str, shape, *, beta1: bool = True) -> Dict[str, tupl
     return st
 
 
-def init_state(optimizer: str, param: torch.Tensor, *, beta1: bool = True) -> Dict[str, torch.Tensor]:
-    """Zero fp32 state tensors for one parameter, with the shapes of meo.h."""
-    return {k: torch.zeros(s, dtype=torch.float32, device=param.device)
+def init_state(optimizer: str, param: torch.Tensor, *, beta1: bool = True,
+               state_dtype: torch.dtype = torch.float32) -> Dict[str, torch.Tensor]:
+    """Zero state tensors for one parameter, with the shapes of meo.h: float32,
+    except the first moment ``exp_avg``, which is ``state_dtype``."""
+    return {k: torch.zeros(s, dtype=state_dtype if k == "exp_avg" else torch.float32, device=param.device)
             for k, s in state_shapes(optimizer, param.shape, beta1=beta1).items()}
 
 

@@ -35,7 +35,7 @@ enum Op { kOpAdafactor = 0, kOpCame = 1, kOpLamb = 2 };
 
 // Uniform view of the per-tensor state pointers of the three optimizers.
 struct StatePtrs {
-    float* m = nullptr;
+    void* m = nullptr;   // float32 or bf16 (the tensor's state_dtype)
     float* v = nullptr;
     float* r = nullptr;
     float* c = nullptr;
@@ -140,13 +140,17 @@ int check_tensors(int op, int64_t step, int32_t n, const meo_tensor* ts, const v
         if (overflow_numel(t, &numel)) return fail(MEO_ESHAPE, who + "too many elements");
         if (t.ndim <= 1 && numel > 0 && (t.batch != 1 || t.rows != 1))
             return fail(MEO_ESHAPE, who + "a tensor with ndim <= 1 must have batch == rows == 1");
-        if (t.param_dtype != MEO_F32) return fail(MEO_EDTYPE, who + "param_dtype must be MEO_F32");
+        if (t.param_dtype != MEO_F32 && t.param_dtype != MEO_BF16)
+            return fail(MEO_EDTYPE, who + "param_dtype must be MEO_F32 or MEO_BF16");
         if (t.grad_dtype != MEO_F32 && t.grad_dtype != MEO_BF16)
             return fail(MEO_EDTYPE, who + "grad_dtype must be MEO_F32 or MEO_BF16");
+        if (t.state_dtype != MEO_F32 && t.state_dtype != MEO_BF16)
+            return fail(MEO_EDTYPE, who + "state_dtype must be MEO_F32 or MEO_BF16");
         if (numel == 0) continue;
         if (!t.param) return fail(MEO_ENULL, who + "param is NULL");
         if (!t.grad) return fail(MEO_ENULL, who + "grad is NULL");
-        if (reinterpret_cast<uintptr_t>(t.param) % 4) return fail(MEO_EALIGN, who + "param not 4-byte aligned");
+        if (reinterpret_cast<uintptr_t>(t.param) % (t.param_dtype == MEO_BF16 ? 2 : 4))
+            return fail(MEO_EALIGN, who + "param misaligned for its dtype");
         if (reinterpret_cast<uintptr_t>(t.grad) % (t.grad_dtype == MEO_BF16 ? 2 : 4))
             return fail(MEO_EALIGN, who + "grad misaligned for its dtype");
         const bool fac = is_factored(op, t);
@@ -173,10 +177,12 @@ int check_tensors(int op, int64_t step, int32_t n, const meo_tensor* ts, const v
             const auto& s = static_cast<const meo_lamb_state*>(states)[k];
             sp.m = s.exp_avg; sp.v = s.exp_avg_sq;
         }
-        const float* need[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+        const void* need[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
         const char* names[6] = {"", "", "", "", "", ""};
+        uintptr_t align[6] = {4, 4, 4, 4, 4, 4};
         int nn = 0;
         if (op == kOpLamb) {
+            align[nn] = t.state_dtype == MEO_BF16 ? 2 : 4;
             need[nn] = sp.m; names[nn++] = "exp_avg";
             need[nn] = sp.v; names[nn++] = "exp_avg_sq";
         } else {
@@ -193,7 +199,8 @@ int check_tensors(int op, int64_t step, int32_t n, const meo_tensor* ts, const v
         }
         for (int i = 0; i < nn; ++i) {
             if (!need[i]) return fail(MEO_ENULL, who + names[i] + " is NULL");
-            if (reinterpret_cast<uintptr_t>(need[i]) % 4) return fail(MEO_EALIGN, who + names[i] + " misaligned");
+            if (reinterpret_cast<uintptr_t>(need[i]) % align[i])
+                return fail(MEO_EALIGN, who + names[i] + " misaligned");
         }
     }
     if (total_tiles > 0xffffffffLL || total_fin > 0xffffffffLL)
@@ -245,6 +252,33 @@ int check_lamb_hp(const meo_lamb_hparams* hp) {
     return MEO_OK;
 }
 
+// Whether [p, p + bytes) lies in one allocation of device memory of device `dev`
+// that the HIP runtime knows (hipMalloc, hipMallocManaged, allocators built on
+// them). Catches host, truncated or stale pointers and ranges described past the
+// end of their memory before any kernel touches them. Returns `code` on failure.
+int check_device_range(const void* p, size_t bytes, int dev, const std::string& what, int code) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(code, what + " is not device memory known to HIP");
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return fail(code, what + " is not device memory");
+    if (attr.type == hipMemoryTypeDevice && attr.device != dev)
+        return fail(code, what + " is on device " + std::to_string(attr.device) + ", the current device is " +
+                              std::to_string(dev));
+    void* base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(code, what + ": the extent of its allocation is unknown to HIP");
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+    if (q < b || bytes > size - (q - b))
+        return fail(code, what + " (" + std::to_string(bytes) + " bytes) extends past the end of its allocation");
+    return MEO_OK;
+}
+
 int check_workspace(int op, int32_t n, const meo_tensor* ts, void* ws, size_t bytes) {
     const int64_t need = layout(op, n, ts, nullptr) * static_cast<int64_t>(sizeof(float));
     if (need == 0) return MEO_OK;
@@ -252,6 +286,44 @@ int check_workspace(int op, int32_t n, const meo_tensor* ts, void* ws, size_t by
     if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MEO_EWORKSPACE, "workspace not 256-byte aligned");
     if (bytes < static_cast<size_t>(need))
         return fail(MEO_EWORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MEO_EHIP, "hipGetDevice failed");
+    }
+    return check_device_range(ws, bytes, dev, "workspace", MEO_EWORKSPACE);
+}
+
+// Every pointer of the list against its allocation (at launch-table creation; a
+// cached table stands for pointers that were checked).
+int check_tensor_memory(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int has_m, int dev) {
+    for (int32_t k = 0; k < n; ++k) {
+        const meo_tensor& t = ts[k];
+        int64_t numel = 0;
+        overflow_numel(t, &numel);
+        if (numel == 0) continue;
+        const std::string who = "tensor " + std::to_string(k) + ": ";
+        const size_t ne = static_cast<size_t>(numel);
+        const size_t rows = static_cast<size_t>(t.batch * t.rows), cols = static_cast<size_t>(t.batch * t.cols);
+        struct Range { const void* p; size_t bytes; const char* name; };
+        std::vector<Range> rs = {{t.param, ne * (t.param_dtype == MEO_BF16 ? 2 : 4), "param"},
+                                 {t.grad, ne * (t.grad_dtype == MEO_BF16 ? 2 : 4), "grad"}};
+        if (has_m) rs.push_back({sp[k].m, ne * (t.state_dtype == MEO_BF16 ? 2 : 4), "exp_avg"});
+        if (is_factored(op, t)) {
+            rs.push_back({sp[k].r, rows * 4, "exp_avg_sq_row"});
+            rs.push_back({sp[k].c, cols * 4, "exp_avg_sq_col"});
+            if (op == kOpCame) {
+                rs.push_back({sp[k].rr, rows * 4, "exp_avg_res_row"});
+                rs.push_back({sp[k].rc, cols * 4, "exp_avg_res_col"});
+            }
+        } else {
+            rs.push_back({sp[k].v, ne * 4, "exp_avg_sq"});
+        }
+        for (const Range& r : rs) {
+            const int rc = check_device_range(r.p, r.bytes, dev, who + r.name, MEO_EMEMORY);
+            if (rc) return rc;
+        }
+    }
     return MEO_OK;
 }
 
@@ -265,6 +337,7 @@ struct Plan {
     int device = 0;
     void* mem = nullptr;  // [n TDesc][item tables]
     int32_t n = 0;
+    int32_t storage = kStoreF32;  // Storage class of the list's parameters and first moments
     const TDesc* desc = nullptr;
     const int2* items[kListCount] = {};
     int64_t count[kListCount] = {};
@@ -281,6 +354,18 @@ void free_plan(Plan* p) {
     (void)hipFree(p->mem);  // waits for work still using it
     if (cur != p->device) (void)hipSetDevice(cur);
     delete p;
+}
+
+// All fp32, all bf16 (a first moment, where there is one, of the parameter's
+// type), or a mix.
+int32_t storage_class(const std::vector<TDesc>& desc) {
+    bool all_f32 = true, all_bf16 = true;
+    for (const TDesc& d : desc) {
+        const bool xb = d.xbf16 != 0, mb = d.m ? d.mbf16 != 0 : xb;
+        all_f32 = all_f32 && !xb && !mb;
+        all_bf16 = all_bf16 && xb && mb;
+    }
+    return all_f32 ? kStoreF32 : (all_bf16 ? kStoreBf16 : kStoreMixed);
 }
 
 // Builds (or finds) the launch table for this list. Returns nullptr with g_err set
@@ -308,6 +393,8 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
             return p;
         }
     }
+    *rc = check_tensor_memory(op, n, ts, sp, has_m, dev);
+    if (*rc) return nullptr;
     std::vector<Geo> geo;
     layout(op, n, ts, &geo);
     std::vector<TDesc> desc;
@@ -318,7 +405,7 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
         const int32_t id = static_cast<int32_t>(desc.size());
         TDesc d;
         std::memset(&d, 0, sizeof d);
-        d.x = static_cast<float*>(ts[k].param);
+        d.x = ts[k].param;
         d.g = ts[k].grad;
         d.m = has_m ? sp[k].m : nullptr;
         d.v = sp[k].v; d.r = sp[k].r; d.c = sp[k].c; d.rr = sp[k].rr; d.rc = sp[k].rc;
@@ -329,6 +416,8 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
         d.B = g.B; d.H = g.H; d.W = g.W;
         d.mode = g.mode;
         d.gbf16 = ts[k].grad_dtype == MEO_BF16;
+        d.xbf16 = ts[k].param_dtype == MEO_BF16;
+        d.mbf16 = ts[k].state_dtype == MEO_BF16;
         bool vec = aligned16(d.x) && aligned16(d.g) && (!d.m || aligned16(d.m));
         if (g.mode != kFlat) vec = vec && (g.W % kVec == 0);
         else vec = vec && (!d.v || aligned16(d.v));
@@ -380,6 +469,7 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
     p->key = std::move(key);
     p->device = dev;
     p->n = m;
+    p->storage = storage_class(desc);
     if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
         hipMemcpy(p->mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
         if (p->mem) (void)hipFree(p->mem);
@@ -560,7 +650,7 @@ int meo_adafactor_validate(const meo_adafactor_hparams* hp, int64_t step, int32_
             overflow_numel(ts[k], &numel);
             if (numel > 0 && !st[k].exp_avg)
                 return fail(MEO_ENULL, "tensor " + std::to_string(k) + ": exp_avg is NULL but beta1 is set");
-            if (numel > 0 && reinterpret_cast<uintptr_t>(st[k].exp_avg) % 4)
+            if (numel > 0 && reinterpret_cast<uintptr_t>(st[k].exp_avg) % (ts[k].state_dtype == MEO_BF16 ? 2 : 4))
                 return fail(MEO_EALIGN, "tensor " + std::to_string(k) + ": exp_avg misaligned");
         }
     return MEO_OK;
@@ -614,7 +704,8 @@ int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
                                               hp->clip_threshold, hp->weight_decay, 0.0}, s);
     pt.mark(kPassScalars);
     launch_af_apply(tab(kListAll), p->count[kListAll],
-                    AfApplyArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1), hp->has_beta1}, s);
+                    AfApplyArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1), hp->has_beta1},
+                    p->storage, s);
     pt.mark(kPassAfApply);
     return launch_status("adafactor step launch");
 }
@@ -651,7 +742,7 @@ int meo_came_validate(const meo_came_hparams* hp, int64_t step, int32_t n, const
         int64_t numel;
         overflow_numel(ts[k], &numel);
         if (numel > 0 && !st[k].exp_avg) return fail(MEO_ENULL, "tensor " + std::to_string(k) + ": exp_avg is NULL");
-        if (numel > 0 && reinterpret_cast<uintptr_t>(st[k].exp_avg) % 4)
+        if (numel > 0 && reinterpret_cast<uintptr_t>(st[k].exp_avg) % (ts[k].state_dtype == MEO_BF16 ? 2 : 4))
             return fail(MEO_EALIGN, "tensor " + std::to_string(k) + ": exp_avg misaligned");
     }
     return MEO_OK;
@@ -698,14 +789,15 @@ int meo_came_step(const meo_came_hparams* hp, int64_t step, int32_t n, const meo
     pt.mark(kPassScalars);
     launch_came_mom(tab(kListAll), p->count[kListAll],
                     CameArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1),
-                             static_cast<float>(hp->eps2), static_cast<float>(hp->lr)}, s);
+                             static_cast<float>(hp->eps2), static_cast<float>(hp->lr)},
+                    p->storage, s);
     pt.mark(kPassCameMom);
     launch_finalize(tab(kListFin2), p->count[kListFin2], FinArgs{hp->beta3, 1, 1}, s);
     pt.mark(kPassFinalize);
     launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame2, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
                                               hp->lr}, s);
     pt.mark(kPassScalars);
-    launch_came_apply(tab(kListAll), p->count[kListAll], s);
+    launch_came_apply(tab(kListAll), p->count[kListAll], p->storage, s);
     pt.mark(kPassCameApply);
     return launch_status("came step launch");
 }
@@ -760,11 +852,11 @@ int meo_lamb_step(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo
                       static_cast<float>(1.0 / bc1), static_cast<float>(1.0 / bc2),
                       static_cast<float>(hp->eps), static_cast<float>(hp->weight_decay)};
     PassTimer pt(s);
-    launch_lamb_moments(t, tiles, la, s);
+    launch_lamb_moments(t, tiles, la, p->storage, s);
     pt.mark(kPassLambMoments);
     launch_scalars(p->desc, w, p->n, ScalArgs{kScalLamb, 0, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
     pt.mark(kPassScalars);
-    launch_lamb_apply(t, tiles, la, s);
+    launch_lamb_apply(t, tiles, la, p->storage, s);
     pt.mark(kPassLambApply);
     return launch_status("lamb step launch");
 }

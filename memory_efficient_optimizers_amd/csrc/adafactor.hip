@@ -6,42 +6,158 @@
 // Colossal-AI distributed-optimizers page. With beta1 (page "Step 3": beta1 set ->
 // exp_avg kept) M <- beta1 M + (1 - beta1) u and the step is M; otherwise the step
 // is u. The parameter takes decoupled weight decay on its pre-update value:
-// X <- X - (weight_decay * alpha) X - step.
+// X <- X - (weight_decay * alpha) X - step. With 16-bit storage the parameter and
+// first moment are widened to fp32 on load and rounded to the nearest bf16 when
+// stored; the new first moment is rounded as soon as it is formed, so the step
+// is the stored value.
 #include "internal.h"
 
 namespace meo {
 
+// 8 fp32 values from two 16-byte words.
+__device__ __forceinline__ void f32x8(const u32x4 a, const u32x4 b, float* f) {
+    f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+    f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
+}
+
+__device__ __forceinline__ u32x4 u4_of(float a, float b, float c, float e) {
+    return u32x4{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(e)};
+}
+
+// The rows of one wave in a 2-D tile with 16-byte aligned rows (W % 8 == 0, so a
+// lane has all 8 of its columns or none). The wave's 16 rows are addressed through
+// buffer resources: a scalar base per tensor, the row offset in a scalar register
+// and one 32-bit lane offset, instead of a 64-bit address per lane and load.
+// G16 / S16: gradient / parameter and first moment stored in bf16. RB rows are
+// loaded per batch and stay packed until their row is computed; 16-bit storage
+// moves half the bytes per row, so it takes twice the rows. W < 2^26 keeps the
+// wave's byte range within 32 bits.
+template <bool G16, bool S16>
+__device__ __forceinline__ void af_rows(const TDesc& d, int lt, float coef, float decay,
+                                        const AfApplyArgs& a) {
+    constexpr int RB = S16 ? 8 : 4;
+    constexpr int GW = G16 ? 1 : 2, SW = S16 ? 1 : 2;       // 16-byte words per lane and row
+    constexpr uint32_t GE = G16 ? 2 : 4, SE = S16 ? 2 : 4;  // bytes per element
+    const TileRC p = tile_rc(d, lt);
+    if (p.valid != kVec || p.nrows <= 0) return;
+    const bool mom = a.has_beta1;
+    float cf[kVec];
+    const float* ccol = d.c + static_cast<int64_t>(p.b) * d.W + p.col;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) cf[e] = rsqrtf(ldf(ccol + e));
+    const float* rrow = d.r + static_cast<int64_t>(p.b) * d.H + p.row0;
+    const int64_t first = (static_cast<int64_t>(p.b) * d.H + p.row0) * d.W;
+    const uint32_t n = static_cast<uint32_t>(p.nrows) * static_cast<uint32_t>(d.W);
+    const Rsrc rg = make_rsrc(static_cast<const char*>(d.g) + first * GE, n * GE);
+    const Rsrc rx = make_rsrc(static_cast<const char*>(d.x) + first * SE, n * SE);
+    const Rsrc rm = make_rsrc(mom ? static_cast<const char*>(d.m) + first * SE : nullptr, mom ? n * SE : 0u);
+    const uint32_t w = static_cast<uint32_t>(d.W), col = static_cast<uint32_t>(p.col);
+    const uint32_t lg = col * GE, ls = col * SE;
+    for (int i0 = 0; i0 < p.nrows; i0 += RB) {
+        u32x4 gr[RB][GW], xr[RB][SW], mr[RB][SW];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            if (i0 + i < p.nrows) {
+                const uint32_t r = static_cast<uint32_t>(i0 + i) * w;
+#pragma unroll
+                for (int k = 0; k < GW; ++k) gr[i][k] = buf_ld(rg, lg + 16u * k, r * GE);
+#pragma unroll
+                for (int k = 0; k < SW; ++k) xr[i][k] = buf_ld(rx, ls + 16u * k, r * SE);
+                if (mom) {
+#pragma unroll
+                    for (int k = 0; k < SW; ++k) mr[i][k] = buf_ld(rm, ls + 16u * k, r * SE);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            if (i0 + i < p.nrows) {
+                const uint32_t r = static_cast<uint32_t>(i0 + i) * w;
+                const float rf = rsqrtf(ldf(rrow + i0 + i)) * coef;
+                float gf[kVec], xf[kVec], mf[kVec];
+                if (G16) bf16x8(gr[i][0], gf); else f32x8(gr[i][0], gr[i][GW - 1], gf);
+                if (S16) bf16x8(xr[i][0], xf); else f32x8(xr[i][0], xr[i][SW - 1], xf);
+                if (mom) {
+                    if (S16) bf16x8(mr[i][0], mf); else f32x8(mr[i][0], mr[i][SW - 1], mf);
+                }
+                u32x4 mp;
+#pragma unroll
+                for (int e = 0; e < kVec; e += 2) {
+                    float u0 = (gf[e] * cf[e]) * rf, u1 = (gf[e + 1] * cf[e + 1]) * rf;
+                    if (mom) {
+                        mf[e] = fmaf(a.beta1, mf[e], a.omb1 * u0);
+                        mf[e + 1] = fmaf(a.beta1, mf[e + 1], a.omb1 * u1);
+                        if (S16) {
+                            // rounded once to bf16; the step is the stored value
+                            const uint32_t wd = bf16_bits(mf[e]) | (bf16_bits(mf[e + 1]) << 16);
+                            mp[e / 2] = wd;
+                            mf[e] = bf16_lo(wd);
+                            mf[e + 1] = bf16_hi(wd);
+                        }
+                        u0 = mf[e];
+                        u1 = mf[e + 1];
+                    }
+                    xf[e] = fmaf(-decay, xf[e], xf[e]) - u0;
+                    xf[e + 1] = fmaf(-decay, xf[e + 1], xf[e + 1]) - u1;
+                }
+                if (S16) {
+                    if (mom) buf_st(mp, rm, ls, r * SE);
+                    buf_st(pack_bf16x8(xf), rx, ls, r * SE);
+                } else {
+                    if (mom) {
+                        buf_st(u4_of(mf[0], mf[1], mf[2], mf[3]), rm, ls, r * SE);
+                        buf_st(u4_of(mf[4], mf[5], mf[6], mf[7]), rm, ls + 16u, r * SE);
+                    }
+                    buf_st(u4_of(xf[0], xf[1], xf[2], xf[3]), rx, ls, r * SE);
+                    buf_st(u4_of(xf[4], xf[5], xf[6], xf[7]), rx, ls + 16u, r * SE);
+                }
+            }
+        }
+    }
+}
+
+template <int ST>
 __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
     const float* ws = t.ws;
     const float decay = ldf(ws + d.scal + kSlotDecay);
-    const bool vec = d.vec, bf = d.gbf16, mom = a.has_beta1;
+    const bool vec = d.vec, bf = d.gbf16, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d), mom = a.has_beta1;
     const float b1 = a.beta1, omb1 = a.omb1;
 
     if (d.mode != kFlat) {
         const TileRC p = tile_rc(d, lt);
         const float coef = ldf(ws + d.bscal + p.b);
+        if constexpr (ST == kStoreBf16) {
+            if (vec && d.W < (1 << 26)) {
+                if (bf) af_rows<true, true>(d, lt, coef, decay, a);
+                else af_rows<false, true>(d, lt, coef, decay, a);
+                return;
+            }
+        }
         const int64_t mat = static_cast<int64_t>(p.b) * d.H * d.W;
         float cf[kVec];
 #pragma unroll
         for (int e = 0; e < kVec; ++e)
             cf[e] = e < p.valid ? rsqrtf(ldf(d.c + static_cast<int64_t>(p.b) * d.W + p.col + e)) : 0.0f;
         const float* rrow = d.r + static_cast<int64_t>(p.b) * d.H;
-        for (int i0 = 0; i0 < p.nrows; i0 += 4) {
-            float g[4][kVec], x[4][kVec], m[4][kVec];
+        // fp32 storage: 4 rows per batch; unaligned 16-bit rows or mixed storage
+        // (rare): 2, which keeps this loop from setting the kernel's registers.
+        constexpr int RB = ST == kStoreF32 ? 4 : 2;
+        for (int i0 = 0; i0 < p.nrows; i0 += RB) {
+            float g[RB][kVec], x[RB][kVec], m[RB][kVec];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < RB; ++i) {
                 if (i0 + i < p.nrows) {
                     const int64_t off = mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col;
-                    load_g8(d.g, off, p.valid, vec, bf, g[i]);
-                    load_f8(d.x + off, p.valid, vec, x[i]);
-                    if (mom) load_f8(d.m + off, p.valid, vec, m[i]);
+                    load_v8(d.g, off, p.valid, vec, bf, g[i]);
+                    load_v8(d.x, off, p.valid, vec, xb, x[i]);
+                    if (mom) load_v8(d.m, off, p.valid, vec, mb, m[i]);
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < RB; ++i) {
                 if (i0 + i < p.nrows) {
                     const int64_t off = mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col;
                     const float rf = rsqrtf(ldf(rrow + p.row0 + i0 + i)) * coef;
@@ -50,13 +166,13 @@ __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
                         const float u = (g[i][e] * cf[e]) * rf;
                         float step = u;
                         if (mom) {
-                            m[i][e] = fmaf(b1, m[i][e], omb1 * u);
+                            m[i][e] = as_stored(fmaf(b1, m[i][e], omb1 * u), mb);
                             step = m[i][e];
                         }
                         x[i][e] = fmaf(-decay, x[i][e], x[i][e]) - step;
                     }
-                    if (mom) store_f8(d.m + off, p.valid, vec, m[i]);
-                    store_f8(d.x + off, p.valid, vec, x[i]);
+                    if (mom) store_v8(d.m, off, p.valid, vec, mb, m[i]);
+                    store_v8(d.x, off, p.valid, vec, xb, x[i]);
                 }
             }
         }
@@ -68,28 +184,32 @@ __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
             const int valid = clamp_valid(d.numel - i);
             if (valid == 0) break;
             float g[kVec], v[kVec], x[kVec], m[kVec] = {};
-            load_g8(d.g, i, valid, vec, bf, g);
+            load_v8(d.g, i, valid, vec, bf, g);
             load_f8(d.v + i, valid, vec, v);
-            load_f8(d.x + i, valid, vec, x);
-            if (mom) load_f8(d.m + i, valid, vec, m);
+            load_v8(d.x, i, valid, vec, xb, x);
+            if (mom) load_v8(d.m, i, valid, vec, mb, m);
 #pragma unroll
             for (int e = 0; e < kVec; ++e) {
                 const float u = e < valid ? (g[e] * rsqrtf(v[e])) * coef : 0.0f;
                 float step = u;
                 if (mom) {
-                    m[e] = fmaf(b1, m[e], omb1 * u);
+                    m[e] = as_stored(fmaf(b1, m[e], omb1 * u), mb);
                     step = m[e];
                 }
                 x[e] = fmaf(-decay, x[e], x[e]) - step;
             }
-            if (mom) store_f8(d.m + i, valid, vec, m);
-            store_f8(d.x + i, valid, vec, x);
+            if (mom) store_v8(d.m, i, valid, vec, mb, m);
+            store_v8(d.x, i, valid, vec, xb, x);
         }
     }
 }
 
-void launch_af_apply(const Table& t, int64_t n, const AfApplyArgs& a, hipStream_t s) {
-    if (n > 0) hipLaunchKernelGGL(k_af_apply, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
+void launch_af_apply(const Table& t, int64_t n, const AfApplyArgs& a, int storage, hipStream_t s) {
+    if (n <= 0) return;
+    const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
+    if (storage == kStoreF32) hipLaunchKernelGGL(k_af_apply<kStoreF32>, grid, block, 0, s, t, a);
+    else if (storage == kStoreBf16) hipLaunchKernelGGL(k_af_apply<kStoreBf16>, grid, block, 0, s, t, a);
+    else hipLaunchKernelGGL(k_af_apply<kStoreMixed>, grid, block, 0, s, t, a);
 }
 
 }  // namespace meo

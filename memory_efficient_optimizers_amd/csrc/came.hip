@@ -17,13 +17,14 @@
 
 namespace meo {
 
+template <int ST>
 __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
     __shared__ __align__(16) float lds[kWaves * kTileCols];
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
     float* ws = t.ws;
-    const bool vec = d.vec, bf = d.gbf16;
+    const bool vec = d.vec, bf = d.gbf16, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d);
     const float b1 = a.beta1, omb1 = a.omb1;
 
     if (d.mode != kFlat) {
@@ -45,8 +46,8 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
             for (int i = 0; i < 4; ++i) {
                 if (i0 + i < p.nrows) {
                     const int64_t off = mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col;
-                    load_g8(d.g, off, p.valid, vec, bf, g[i]);
-                    load_f8(d.m + off, p.valid, vec, m[i]);
+                    load_v8(d.g, off, p.valid, vec, bf, g[i]);
+                    load_v8(d.m, off, p.valid, vec, mb, m[i]);
                 }
             }
 #pragma unroll
@@ -59,13 +60,13 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
 #pragma unroll
                     for (int e = 0; e < kVec; ++e) {
                         const float u = (g[i][e] * cf[e]) * rf;
-                        m[i][e] = fmaf(b1, m[i][e], omb1 * u);
+                        m[i][e] = as_stored(fmaf(b1, m[i][e], omb1 * u), mb);
                         const float du = u - m[i][e];
                         const float q = e < p.valid ? fmaf(du, du, a.eps2) : 0.0f;
                         cs[e] += q;
                         rs += q;
                     }
-                    store_f8(d.m + off, p.valid, vec, m[i]);
+                    store_v8(d.m, off, p.valid, vec, mb, m[i]);
                     rs = wave_sum(rs);
                     if (lane == 0) stf(rowpart + row, rs);
                 }
@@ -82,33 +83,38 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
             const int valid = clamp_valid(d.numel - i);
             if (valid == 0) break;
             float g[kVec], v[kVec], x[kVec], m[kVec];
-            load_g8(d.g, i, valid, vec, bf, g);
+            load_v8(d.g, i, valid, vec, bf, g);
             load_f8(d.v + i, valid, vec, v);
-            load_f8(d.x + i, valid, vec, x);
-            load_f8(d.m + i, valid, vec, m);
+            load_v8(d.x, i, valid, vec, xb, x);
+            load_v8(d.m, i, valid, vec, mb, m);
 #pragma unroll
             for (int e = 0; e < kVec; ++e) {
                 const float u = e < valid ? (g[e] * rsqrtf(v[e])) * coef : 0.0f;
-                m[e] = fmaf(b1, m[e], omb1 * u);
+                m[e] = as_stored(fmaf(b1, m[e], omb1 * u), mb);
                 x[e] = fmaf(-decay, x[e], x[e]) - lr * m[e];
             }
-            store_f8(d.m + i, valid, vec, m);
-            store_f8(d.x + i, valid, vec, x);
+            store_v8(d.m, i, valid, vec, mb, m);
+            store_v8(d.x, i, valid, vec, xb, x);
         }
     }
 }
 
-void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, hipStream_t s) {
-    if (n > 0) hipLaunchKernelGGL(k_came_mom, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
+void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, int storage, hipStream_t s) {
+    if (n <= 0) return;
+    const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
+    if (storage == kStoreF32) hipLaunchKernelGGL(k_came_mom<kStoreF32>, grid, block, 0, s, t, a);
+    else if (storage == kStoreBf16) hipLaunchKernelGGL(k_came_mom<kStoreBf16>, grid, block, 0, s, t, a);
+    else hipLaunchKernelGGL(k_came_mom<kStoreMixed>, grid, block, 0, s, t, a);
 }
 
+template <int ST>
 __global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     if (d.mode == kFlat) return;  // 1-D tensors were finished by k_came_mom
     const int lt = it.y;
     const float* ws = t.ws;
-    const bool vec = d.vec;
+    const bool vec = d.vec, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d);
     const TileRC p = tile_rc(d, lt);
     const float coef = ldf(ws + d.bscal + d.B + p.b);
     const float decay = ldf(ws + d.scal + kSlotDecay);
@@ -124,8 +130,8 @@ __global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
         for (int i = 0; i < 4; ++i) {
             if (i0 + i < p.nrows) {
                 const int64_t off = mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col;
-                load_f8(d.x + off, p.valid, vec, x[i]);
-                load_f8(d.m + off, p.valid, vec, m[i]);
+                load_v8(d.x, off, p.valid, vec, xb, x[i]);
+                load_v8(d.m, off, p.valid, vec, mb, m[i]);
             }
         }
 #pragma unroll
@@ -136,14 +142,18 @@ __global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
                 const float sr = rsqrtf(ldf(rrow + row)) * coef;
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) x[i][e] = fmaf(-decay, x[i][e], x[i][e]) - (m[i][e] * sc[e]) * sr;
-                store_f8(d.x + off, p.valid, vec, x[i]);
+                store_v8(d.x, off, p.valid, vec, xb, x[i]);
             }
         }
     }
 }
 
-void launch_came_apply(const Table& t, int64_t n, hipStream_t s) {
-    if (n > 0) hipLaunchKernelGGL(k_came_apply, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t);
+void launch_came_apply(const Table& t, int64_t n, int storage, hipStream_t s) {
+    if (n <= 0) return;
+    const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
+    if (storage == kStoreF32) hipLaunchKernelGGL(k_came_apply<kStoreF32>, grid, block, 0, s, t);
+    else if (storage == kStoreBf16) hipLaunchKernelGGL(k_came_apply<kStoreBf16>, grid, block, 0, s, t);
+    else hipLaunchKernelGGL(k_came_apply<kStoreMixed>, grid, block, 0, s, t);
 }
 
 }  // namespace meo

@@ -47,14 +47,19 @@ constexpr int kRcMaxCols1 = 512 * 8 * 3;  // 12288
 enum ScalSlot { kSlotAlpha = 0, kSlotCoef = 1, kSlotDecay = 2, kSlotRmsU = 3, kSlotRmsX = 4,
                 kSlotNormD = 5 };
 
+// Storage class of a launch's parameters and first moments: all fp32, all bf16,
+// or a mix (then read per tensor from its descriptor). The streaming kernels are
+// compiled once per class, so the uniform cases carry no dtype branches.
+enum Storage { kStoreF32 = 0, kStoreBf16 = 1, kStoreMixed = 2 };
+
 // How a tensor's statistics are gathered.
 enum Mode { kFlat = 0, kRowComplete = 1, kTiled = 2 };
 
 // Device-side descriptor of one tensor of the call (built on the host, cached).
 struct TDesc {
-    float* x;         // parameter
+    void* x;          // parameter (fp32 or bf16)
     const void* g;    // gradient (fp32 or bf16)
-    float* m;         // first moment (nullable)
+    void* m;          // first moment (fp32 or bf16; nullable)
     float* v;         // full second moment (1-D Adafactor/CAME; LAMB)
     float* r;         // factored row statistic [B*H]
     float* c;         // factored column statistic [B*W]
@@ -74,6 +79,8 @@ struct TDesc {
     int32_t B, H, W;
     int32_t mode;     // Mode
     int32_t gbf16;    // gradient dtype is bf16
+    int32_t xbf16;    // parameter dtype is bf16
+    int32_t mbf16;    // first-moment dtype is bf16
     int32_t vec;      // 16-byte vector accesses are valid
     int32_t tr, tc;   // 2-D tiles per matrix along rows / columns (flat: tr = 1, tc = tiles)
     int32_t strips;   // row-complete strips per matrix
@@ -92,6 +99,16 @@ struct Table {
 // ----------------------------------------------------------------------------- helpers
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Element types of a tensor's parameter and first moment under storage class ST.
+template <int ST>
+__device__ __forceinline__ bool x_is_bf16(const TDesc& d) {
+    return ST == kStoreMixed ? d.xbf16 != 0 : ST == kStoreBf16;
+}
+template <int ST>
+__device__ __forceinline__ bool m_is_bf16(const TDesc& d) {
+    return ST == kStoreMixed ? d.mbf16 != 0 : ST == kStoreBf16;
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -167,10 +184,11 @@ __device__ __forceinline__ void bf16x8(const u32x4 u, float* f) {
     f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
 }
 
-// 8 gradient values starting at element `i` of `g`; `valid` (0..8) of them are in
-// range, the rest read as 0. Vector loads only when all 8 are valid and `vec`.
+// 8 values starting at element `i` of the fp32 or bf16 tensor `g` (gradient,
+// parameter or first moment), widened to fp32; `valid` (0..8) of them are in range,
+// the rest read as 0. Vector loads only when all 8 are valid and `vec`.
 template <bool NT = false>
-__device__ __forceinline__ void load_g8(const void* __restrict__ g, int64_t i, int valid,
+__device__ __forceinline__ void load_v8(const void* __restrict__ g, int64_t i, int valid,
                                         bool vec, bool bf16, float* f) {
     if (bf16) {
         const uint16_t* p = static_cast<const uint16_t*>(g) + i;
@@ -221,6 +239,60 @@ __device__ __forceinline__ void store_f8(float* __restrict__ p, int valid, bool 
         for (int e = 0; e < kVec; ++e)
             if (e < valid) q[e] = f[e];
     }
+}
+
+// Nearest bf16 value of f (ties to even; NaN stays NaN), as fp32.
+__device__ __forceinline__ float round_bf16(float f) {
+    return static_cast<float>(static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// A freshly formed first-moment value as it will be stored: rounded to bf16
+// when the first moment is held in bf16, so that every later use in the step
+// sees the stored value.
+__device__ __forceinline__ float as_stored(float v, bool bf16) { return bf16 ? round_bf16(v) : v; }
+
+// 8 fp32 values rounded to bf16 (nearest, ties to even), packed in element order.
+__device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
+    return u32x4{bf16_bits(f[0]) | (bf16_bits(f[1]) << 16), bf16_bits(f[2]) | (bf16_bits(f[3]) << 16),
+                 bf16_bits(f[4]) | (bf16_bits(f[5]) << 16), bf16_bits(f[6]) | (bf16_bits(f[7]) << 16)};
+}
+
+// Stores 8 fp32 values at element `i` of the fp32 or bf16 tensor `p`, bf16 rounded
+// to nearest (ties to even); only the first `valid` are written.
+__device__ __forceinline__ void store_v8(void* __restrict__ p, int64_t i, int valid, bool vec, bool bf16,
+                                         const float* f) {
+    if (bf16) {
+        uint16_t* q = static_cast<uint16_t*>(p) + i;
+        if (vec && valid == kVec) {
+            *gst<u32x4>(q) = pack_bf16x8(f);
+        } else {
+            MEO_GLOBAL uint16_t* s = gst<uint16_t>(q);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e)
+                if (e < valid) s[e] = static_cast<uint16_t>(bf16_bits(f[e]));
+        }
+    } else {
+        store_f8(static_cast<float*>(p) + i, valid, vec, f);
+    }
+}
+
+// Buffer resources: a base address and a byte range held in scalar registers, so a
+// wave addresses rows of a tile with one 32-bit lane offset plus a scalar row
+// offset instead of a 64-bit address per lane and row. Accesses beyond
+// `bytes` read 0 and write nothing.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld(Rsrc r, uint32_t lane_off, uint32_t row_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, row_off, 0);
+}
+__device__ __forceinline__ void buf_st(u32x4 v, Rsrc r, uint32_t lane_off, uint32_t row_off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, lane_off, row_off, 0);
 }
 
 // Scalar accesses of state vectors and workspace through generic pointers.
@@ -342,10 +414,10 @@ void launch_stats(const Table& t, int64_t n, const StatsArgs& a, hipStream_t s);
 void launch_finalize(const Table& t, int64_t n, const FinArgs& a, hipStream_t s);
 void launch_rms(const Table& t, int64_t n, int32_t need_x, hipStream_t s);
 void launch_scalars(const TDesc* desc, float* ws, int32_t n, const ScalArgs& a, hipStream_t s);
-void launch_af_apply(const Table& t, int64_t n, const AfApplyArgs& a, hipStream_t s);
-void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, hipStream_t s);
-void launch_came_apply(const Table& t, int64_t n, hipStream_t s);
-void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, hipStream_t s);
-void launch_lamb_apply(const Table& t, int64_t n, const LambArgs& a, hipStream_t s);
+void launch_af_apply(const Table& t, int64_t n, const AfApplyArgs& a, int storage, hipStream_t s);
+void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, int storage, hipStream_t s);
+void launch_came_apply(const Table& t, int64_t n, int storage, hipStream_t s);
+void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, int storage, hipStream_t s);
+void launch_lamb_apply(const Table& t, int64_t n, const LambArgs& a, int storage, hipStream_t s);
 
 }  // namespace meo

@@ -18,12 +18,13 @@ __device__ __forceinline__ float lamb_dir(float m, float v, float x, const LambA
     return (m * a.inv_bc1) / (sqrtf(v * a.inv_bc2) + a.eps) + a.wd * x;
 }
 
+template <int ST>
 __global__ __launch_bounds__(kThreads) void k_lamb_moments(Table t, LambArgs a) {
     __shared__ float lds[2 * kWaves];
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
-    const bool vec = d.vec, bf = d.gbf16;
+    const bool vec = d.vec, bf = d.gbf16, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d);
     const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
     float sx[kVec], sd[kVec];
 #pragma unroll
@@ -33,19 +34,19 @@ __global__ __launch_bounds__(kThreads) void k_lamb_moments(Table t, LambArgs a) 
         const int valid = clamp_valid(d.numel - i);
         if (valid == 0) break;
         float g[kVec], x[kVec], m[kVec], v[kVec];
-        load_g8(d.g, i, valid, vec, bf, g);
-        load_f8(d.x + i, valid, vec, x);
-        load_f8(d.m + i, valid, vec, m);
+        load_v8(d.g, i, valid, vec, bf, g);
+        load_v8(d.x, i, valid, vec, xb, x);
+        load_v8(d.m, i, valid, vec, mb, m);
         load_f8(d.v + i, valid, vec, v);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
-            m[e] = fmaf(a.beta1, m[e], a.omb1 * g[e]);
+            m[e] = as_stored(fmaf(a.beta1, m[e], a.omb1 * g[e]), mb);
             v[e] = fmaf(a.beta2, v[e], a.omb2 * (g[e] * g[e]));
             const float dd = e < valid ? lamb_dir(m[e], v[e], x[e], a) : 0.0f;
             sx[e] = fmaf(x[e], x[e], sx[e]);
             sd[e] = fmaf(dd, dd, sd[e]);
         }
-        store_f8(d.m + i, valid, vec, m);
+        store_v8(d.m, i, valid, vec, mb, m);
         store_f8(d.v + i, valid, vec, v);
     }
     float tx = sum8(sx), td = sum8(sd);
@@ -57,15 +58,20 @@ __global__ __launch_bounds__(kThreads) void k_lamb_moments(Table t, LambArgs a) 
     }
 }
 
-void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, hipStream_t s) {
-    if (n > 0) hipLaunchKernelGGL(k_lamb_moments, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
+void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, int storage, hipStream_t s) {
+    if (n <= 0) return;
+    const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
+    if (storage == kStoreF32) hipLaunchKernelGGL(k_lamb_moments<kStoreF32>, grid, block, 0, s, t, a);
+    else if (storage == kStoreBf16) hipLaunchKernelGGL(k_lamb_moments<kStoreBf16>, grid, block, 0, s, t, a);
+    else hipLaunchKernelGGL(k_lamb_moments<kStoreMixed>, grid, block, 0, s, t, a);
 }
 
+template <int ST>
 __global__ __launch_bounds__(kThreads) void k_lamb_apply(Table t, LambArgs a) {
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
-    const bool vec = d.vec;
+    const bool vec = d.vec, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d);
     const float coef = ldf(t.ws + d.bscal);
     const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
     for (int it = 0; it < kFlatIters; ++it) {
@@ -73,17 +79,21 @@ __global__ __launch_bounds__(kThreads) void k_lamb_apply(Table t, LambArgs a) {
         const int valid = clamp_valid(d.numel - i);
         if (valid == 0) break;
         float x[kVec], m[kVec], v[kVec];
-        load_f8(d.x + i, valid, vec, x);
-        load_f8(d.m + i, valid, vec, m);
+        load_v8(d.x, i, valid, vec, xb, x);
+        load_v8(d.m, i, valid, vec, mb, m);
         load_f8(d.v + i, valid, vec, v);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) x[e] = x[e] - coef * lamb_dir(m[e], v[e], x[e], a);
-        store_f8(d.x + i, valid, vec, x);
+        store_v8(d.x, i, valid, vec, xb, x);
     }
 }
 
-void launch_lamb_apply(const Table& t, int64_t n, const LambArgs& a, hipStream_t s) {
-    if (n > 0) hipLaunchKernelGGL(k_lamb_apply, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, a);
+void launch_lamb_apply(const Table& t, int64_t n, const LambArgs& a, int storage, hipStream_t s) {
+    if (n <= 0) return;
+    const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
+    if (storage == kStoreF32) hipLaunchKernelGGL(k_lamb_apply<kStoreF32>, grid, block, 0, s, t, a);
+    else if (storage == kStoreBf16) hipLaunchKernelGGL(k_lamb_apply<kStoreBf16>, grid, block, 0, s, t, a);
+    else hipLaunchKernelGGL(k_lamb_apply<kStoreMixed>, grid, block, 0, s, t, a);
 }
 
 }  // namespace meo

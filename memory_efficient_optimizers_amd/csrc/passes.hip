@@ -44,7 +44,7 @@ __device__ void stats_flat(const TDesc& d, int lt, float* __restrict__ ws, const
         const int valid = clamp_valid(d.numel - i);
         if (valid == 0) break;
         float g[kVec], v[kVec] = {};
-        load_g8<true>(d.g, i, valid, vec, bf, g);
+        load_v8<true>(d.g, i, valid, vec, bf, g);
         if (beta != 0.0f) load_f8(d.v + i, valid, vec, v);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
@@ -56,7 +56,7 @@ __device__ void stats_flat(const TDesc& d, int lt, float* __restrict__ ws, const
         store_f8(d.v + i, valid, vec, v);
         if (a.need_x) {
             float x[kVec];
-            load_f8<true>(d.x + i, valid, vec, x);
+            load_v8<true>(d.x, i, valid, vec, d.xbf16, x);
 #pragma unroll
             for (int e = 0; e < kVec; ++e) sx[e] = fmaf(x[e], x[e], sx[e]);
         }
@@ -83,15 +83,31 @@ __device__ void xnorm_chunk(const TDesc& d, int c, float* __restrict__ ws, const
     float sx[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) sx[e] = 0.0f;
-#pragma unroll 8
-    for (int it = 0; it < ITERS; ++it) {
-        const int64_t i = base + (static_cast<int64_t>(it) * NTHR + threadIdx.x) * kVec;
-        const int valid = clamp_valid(d.numel - i);
-        if (valid == 0) break;
-        float x[kVec];
-        load_f8<true>(d.x + i, valid, true, x);
+    if (d.xbf16 && base + kFlatTile <= d.numel) {
+        // A whole bf16 chunk: half the bytes of fp32 per element, so all of the
+        // thread's 16-byte loads are issued before the first is used.
+        const uint16_t* xp = static_cast<const uint16_t*>(d.x) + base + threadIdx.x * kVec;
+        u32x4 raw[ITERS];
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) sx[e] = fmaf(x[e], x[e], sx[e]);
+        for (int it = 0; it < ITERS; ++it) raw[it] = ld_u4<true>(xp + static_cast<int64_t>(it) * NTHR * kVec);
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            float x[kVec];
+            bf16x8(raw[it], x);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) sx[e] = fmaf(x[e], x[e], sx[e]);
+        }
+    } else {
+#pragma unroll 8
+        for (int it = 0; it < ITERS; ++it) {
+            const int64_t i = base + (static_cast<int64_t>(it) * NTHR + threadIdx.x) * kVec;
+            const int valid = clamp_valid(d.numel - i);
+            if (valid == 0) break;
+            float x[kVec];
+            load_v8<true>(d.x, i, valid, true, d.xbf16, x);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) sx[e] = fmaf(x[e], x[e], sx[e]);
+        }
     }
     float tx = sum8(sx), unused = 0.0f;
     block_sum2<NW>(tx, unused, bsum);
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(Table t, StatsArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (i0 + i < p.nrows)
-                load_g8<true>(d.g, mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, bf, g[i]);
+                load_v8<true>(d.g, mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, bf, g[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (i0 + i < p.nrows) {
@@ -442,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void k_rms(Table t, int32_t need_x) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (i0 + i < p.nrows)
-                load_g8<true>(d.g, mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, bf, g[i]);
+                load_v8<true>(d.g, mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, bf, g[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (i0 + i < p.nrows) {
@@ -459,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void k_rms(Table t, int32_t need_x) {
             for (int i = 0; i < 8; ++i) {
                 if (i0 + i < p.nrows) {
                     float x[kVec];
-                    load_f8<true>(d.x + mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, x);
+                    load_v8<true>(d.x, mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col, p.valid, vec, d.xbf16, x);
 #pragma unroll
                     for (int e = 0; e < kVec; ++e) sx[e] = fmaf(x[e], x[e], sx[e]);
                 }

@@ -1,13 +1,20 @@
 """torch.optim front ends over the C ABI: Adafactor, CAME and Lamb.
 
-Each class owns its state tensors (fp32, on the parameter's device, named as on
-the Colossal-AI distributed-optimizers page: ``step``, ``exp_avg``,
+Each class owns its state tensors (on the parameter's device, named as on the
+Colossal-AI distributed-optimizers page: ``step``, ``exp_avg``,
 ``exp_avg_sq_row``, ``exp_avg_sq_col``, ``exp_avg_sq``; CAME adds
 ``exp_avg_res_row`` / ``exp_avg_res_col``) and a device workspace, and hands
 every parameter with a gradient to one library call per parameter group (and per
 step count, should parameters have taken different numbers of steps). The update
 itself runs in the HIP kernels; ``state_dict()`` / ``load_state_dict()`` work as
 for any torch optimizer.
+
+Parameters may be float32 or bfloat16 (the page's DistributedCAME paragraph
+mentions a memory-saving 16-bit path). Statistics are always float32; the first
+moment ``exp_avg`` is kept in ``state_dtype``, which by default follows the
+parameter (bfloat16 parameters get a bfloat16 first moment, float32 ones a
+float32 one). The arithmetic is float32 throughout, and bfloat16 values are
+rounded to nearest even when stored.
 """
 from __future__ import annotations
 
@@ -22,9 +29,17 @@ from . import _lib
 class _MeoOptimizer(torch.optim.Optimizer):
     _kind = ""
 
-    def __init__(self, params, defaults):
+    def __init__(self, params, defaults, state_dtype: Optional[torch.dtype] = None):
+        if state_dtype not in (None, torch.float32, torch.bfloat16):
+            raise TypeError("state_dtype must be None, torch.float32 or torch.bfloat16")
         super().__init__(params, defaults)
+        self._state_dtype = state_dtype
         self._workspace: Dict[torch.device, torch.Tensor] = {}
+
+    def _moment_dtype(self, p: torch.Tensor) -> torch.dtype:
+        if self._state_dtype is not None:
+            return self._state_dtype
+        return torch.bfloat16 if p.dtype == torch.bfloat16 else torch.float32
 
     def _ws(self, nbytes: int, device) -> Optional[torch.Tensor]:
         if nbytes <= 0:
@@ -34,6 +49,19 @@ class _MeoOptimizer(torch.optim.Optimizer):
             ws = _lib.workspace(nbytes, device)
             self._workspace[device] = ws
         return ws
+
+    def load_state_dict(self, state_dict) -> None:
+        """As torch's, except that state tensors keep the dtypes they were saved
+        with: torch would cast them to the parameter's dtype, rounding the float32
+        statistics of a bfloat16 parameter to bfloat16."""
+        saved = state_dict["state"]
+        super().load_state_dict(state_dict)
+        ids = [i for g in state_dict["param_groups"] for i in g["params"]]
+        params = [p for g in self.param_groups for p in g["params"]]
+        for i, p in zip(ids, params):
+            for key, v in saved.get(i, {}).items():
+                if torch.is_tensor(v) and key != "step":
+                    self.state[p][key] = v.to(device=p.device, copy=True).contiguous()
 
     def _state_for(self, p: torch.Tensor, group) -> Dict[str, torch.Tensor]:
         raise NotImplementedError
@@ -75,7 +103,8 @@ class _MeoOptimizer(torch.optim.Optimizer):
 class Adafactor(_MeoOptimizer):
     """Adafactor with the page's defaults ("Step 3"): lr=None, eps=(1e-30, 1e-3),
     clip_threshold=1.0, decay_rate=-0.8, beta1=None, weight_decay=0.0,
-    scale_parameter=True, relative_step=True, warmup_init=False."""
+    scale_parameter=True, relative_step=True, warmup_init=False. ``state_dtype``:
+    element type of ``exp_avg`` (None: that of the parameter)."""
 
     _kind = "adafactor"
     _HP = ("lr", "eps", "clip_threshold", "decay_rate", "beta1", "weight_decay", "scale_parameter",
@@ -83,7 +112,7 @@ class Adafactor(_MeoOptimizer):
 
     def __init__(self, params, lr=None, eps=(1e-30, 1e-3), clip_threshold=1.0, decay_rate=-0.8,
                  beta1=None, weight_decay=0.0, scale_parameter=True, relative_step=True,
-                 warmup_init=False):
+                 warmup_init=False, state_dtype=None):
         if lr is not None and relative_step:
             raise ValueError("Cannot combine manual lr and relative_step=True options")
         if warmup_init and not relative_step:
@@ -91,10 +120,11 @@ class Adafactor(_MeoOptimizer):
         defaults = dict(lr=lr, eps=eps, clip_threshold=clip_threshold, decay_rate=decay_rate,
                         beta1=beta1, weight_decay=weight_decay, scale_parameter=scale_parameter,
                         relative_step=relative_step, warmup_init=warmup_init)
-        super().__init__(params, defaults)
+        super().__init__(params, defaults, state_dtype)
 
     def _state_for(self, p, group):
-        return _lib.init_state("adafactor", p, beta1=group["beta1"] is not None)
+        return _lib.init_state("adafactor", p, beta1=group["beta1"] is not None,
+                               state_dtype=self._moment_dtype(p))
 
     def _wsize(self, params, grads):
         return _lib.meo_adafactor_workspace_size(params, grads)
@@ -107,21 +137,22 @@ class Adafactor(_MeoOptimizer):
 class CAME(_MeoOptimizer):
     """CAME with the page's defaults (DistributedCAME paragraph):
     eps=(1e-30, 1e-16), clip_threshold=1.0, betas=(0.9, 0.999, 0.9999),
-    weight_decay=0.0; lr must be given."""
+    weight_decay=0.0; lr must be given. ``state_dtype``: element type of
+    ``exp_avg`` (None: that of the parameter)."""
 
     _kind = "came"
     _HP = ("lr", "eps", "clip_threshold", "betas", "weight_decay")
 
     def __init__(self, params, lr=None, eps=(1e-30, 1e-16), clip_threshold=1.0,
-                 betas=(0.9, 0.999, 0.9999), weight_decay=0.0):
+                 betas=(0.9, 0.999, 0.9999), weight_decay=0.0, state_dtype=None):
         if lr is None:
             raise ValueError("CAME requires an explicit lr")
         defaults = dict(lr=lr, eps=eps, clip_threshold=clip_threshold, betas=betas,
                         weight_decay=weight_decay)
-        super().__init__(params, defaults)
+        super().__init__(params, defaults, state_dtype)
 
     def _state_for(self, p, group):
-        return _lib.init_state("came", p)
+        return _lib.init_state("came", p, state_dtype=self._moment_dtype(p))
 
     def _wsize(self, params, grads):
         return _lib.meo_came_workspace_size(params, grads)
@@ -133,13 +164,15 @@ class CAME(_MeoOptimizer):
 
 class Lamb(_MeoOptimizer):
     """LAMB with the page's defaults (DistributedLAMB paragraph): lr=1e-3,
-    betas=(0.9, 0.999), eps=1e-6, weight_decay=0, bias_correction=True."""
+    betas=(0.9, 0.999), eps=1e-6, weight_decay=0, bias_correction=True.
+    ``state_dtype``: element type of ``exp_avg`` (None: that of the parameter);
+    ``exp_avg_sq`` is float32."""
 
     _kind = "lamb"
     _HP = ("lr", "betas", "eps", "weight_decay", "bias_correction")
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-6, weight_decay=0.0,
-                 bias_correction=True):
+                 bias_correction=True, state_dtype=None):
         if not lr >= 0.0:
             raise ValueError(f"Invalid learning rate: {lr}")
         if not eps >= 0.0:
@@ -149,10 +182,10 @@ class Lamb(_MeoOptimizer):
                 raise ValueError(f"Invalid beta parameter at index {i}: {b}")
         defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay,
                         bias_correction=bias_correction)
-        super().__init__(params, defaults)
+        super().__init__(params, defaults, state_dtype)
 
     def _state_for(self, p, group):
-        return _lib.init_state("lamb", p)
+        return _lib.init_state("lamb", p, state_dtype=self._moment_dtype(p))
 
     def _wsize(self, params, grads):
         return _lib.meo_lamb_workspace_size(params, grads)

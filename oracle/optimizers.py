@@ -32,6 +32,13 @@ Sources (the pages), by function:
   "DistributedLAMB" paragraph (defaults, validation). The step follows the LAMB
   paper the page cites (arXiv:1904.00962).
 
+* 16-bit storage: the DistributedCAME paragraph says the optimizer supports a
+  memory-saving 16-bit path under mixed precision. With ``param_bf16`` /
+  ``exp_avg_bf16`` the parameter / first moment is held in bfloat16: the inputs
+  are bf16 values (exact in float64), the arithmetic is unchanged, and each new
+  value is rounded to bf16 as it is formed (``round_bf16``), so the rest of the
+  step uses the stored first moment.
+
 Readings where the pages are silent are listed, with reasons, in the design notes
 of this repository; each is marked "reading" at the line that applies it.
 """
@@ -79,6 +86,30 @@ def rms(a: Array) -> float:
     if a.size == 0:
         return 0.0
     return math.sqrt(float(np.mean(a * a)))
+
+
+def round_bf16(a) -> Array:
+    """Nearest bfloat16 value of each element, as float64.
+
+    bfloat16 is the upper half of an IEEE float32 (sign, the 8 exponent bits, the
+    first 7 of the 23 fraction bits). reading: the value is first rounded to
+    float32, the type in which the GPU forms it, then to the nearest bf16 with ties
+    to the even last kept bit; values beyond the largest bf16 go to +-inf, NaN
+    stays NaN."""
+    f = np.atleast_1d(np.asarray(a, dtype=np.float64)).astype(np.float32)
+    bits = f.view(np.uint32).astype(np.uint64)
+    keep_lsb = (bits >> np.uint64(16)) & np.uint64(1)
+    # Adding 0x7fff plus the last kept bit carries into the kept half exactly when
+    # the dropped half is above the midpoint, or at it with an odd kept half.
+    rounded = ((bits + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)) << np.uint64(16)
+    out = (rounded & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.float32).astype(np.float64)
+    out[np.isnan(f)] = np.nan
+    return out.reshape(np.shape(a))
+
+
+def _stored(a: Array, bf16: bool) -> Array:
+    """A new value of a tensor as its storage holds it (reading: 16-bit storage)."""
+    return round_bf16(a) if bf16 else a
 
 
 def is_factored(shape: Tuple[int, ...]) -> bool:
@@ -139,7 +170,8 @@ def adafactor_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None) -> S
     return st
 
 
-def adafactor_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int
+def adafactor_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int, *,
+                          param_bf16: bool = False, exp_avg_bf16: bool = False
                           ) -> Tuple[Array, State]:
     """One Adafactor step of one tensor; returns (new parameter, new state)."""
     h = adafactor_hparams(hp)
@@ -177,22 +209,22 @@ def adafactor_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], 
     u = alpha * u
     if h["beta1"] is not None:
         # reading: the first moment averages the clipped, lr-scaled update.
-        m = h["beta1"] * state["exp_avg"] + (1.0 - h["beta1"]) * u
+        m = _stored(h["beta1"] * state["exp_avg"] + (1.0 - h["beta1"]) * u, exp_avg_bf16)
         new["exp_avg"] = m
         delta = m
     else:
         delta = u
     # reading: decoupled weight decay on the pre-update parameter, scaled by alpha.
-    x_new = x - h["weight_decay"] * alpha * x - delta
+    x_new = _stored(x - h["weight_decay"] * alpha * x - delta, param_bf16)
     return x_new, new
 
 
 def adafactor_step(xs: Sequence[Array], gs: Sequence[Array], states: Sequence[State],
-                   hp: Optional[dict], t: int) -> Tuple[List[Array], List[State]]:
+                   hp: Optional[dict], t: int, **storage) -> Tuple[List[Array], List[State]]:
     """A step over a list: every statistic is per tensor, so each is independent."""
     out_x, out_s = [], []
     for x, g, st in zip(xs, gs, states):
-        a, b = adafactor_step_tensor(x, g, st, hp, t)
+        a, b = adafactor_step_tensor(x, g, st, hp, t, **storage)
         out_x.append(a)
         out_s.append(b)
     return out_x, out_s
@@ -233,7 +265,8 @@ def _factored_estimate(row: Array, col: Array) -> Array:
     return row[..., :, None] * col[..., None, :] / row.mean(axis=-1)[..., None, None]
 
 
-def came_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int
+def came_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int, *,
+                     param_bf16: bool = False, exp_avg_bf16: bool = False
                      ) -> Tuple[Array, State]:
     """One CAME step of one tensor; returns (new parameter, new state)."""
     h = came_hparams(hp)
@@ -264,7 +297,7 @@ def came_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
     u = g / np.sqrt(v_hat)
     u = u / max(1.0, rms(u) / h["clip_threshold"])
 
-    m = beta1 * state["exp_avg"] + (1.0 - beta1) * u
+    m = _stored(beta1 * state["exp_avg"] + (1.0 - beta1) * u, exp_avg_bf16)
     new["exp_avg"] = m
 
     if fac:
@@ -279,14 +312,14 @@ def came_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
     else:
         # reading: a full 1-D statistic carries no factorisation error to correct.
         delta = m
-    x_new = x - lr * h["weight_decay"] * x - lr * delta
+    x_new = _stored(x - lr * h["weight_decay"] * x - lr * delta, param_bf16)
     return x_new, new
 
 
-def came_step(xs, gs, states, hp, t):
+def came_step(xs, gs, states, hp, t, **storage):
     out_x, out_s = [], []
     for x, g, st in zip(xs, gs, states):
-        a, b = came_step_tensor(x, g, st, hp, t)
+        a, b = came_step_tensor(x, g, st, hp, t, **storage)
         out_x.append(a)
         out_s.append(b)
     return out_x, out_s
@@ -313,7 +346,8 @@ def lamb_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None) -> State:
     return {"exp_avg": np.zeros(shape), "exp_avg_sq": np.zeros(shape)}
 
 
-def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int
+def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int, *,
+                     param_bf16: bool = False, exp_avg_bf16: bool = False
                      ) -> Tuple[Array, State]:
     """One LAMB step of one tensor (the whole tensor is one layer for the trust ratio)."""
     h = lamb_hparams(hp)
@@ -324,7 +358,7 @@ def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
     if x.size == 0:
         return _untouched(x, state)
     beta1, beta2 = h["betas"]
-    m = beta1 * state["exp_avg"] + (1.0 - beta1) * g
+    m = _stored(beta1 * state["exp_avg"] + (1.0 - beta1) * g, exp_avg_bf16)
     v = beta2 * state["exp_avg_sq"] + (1.0 - beta2) * g * g
     if h["bias_correction"]:
         m_hat = m / (1.0 - beta1 ** t)
@@ -337,14 +371,14 @@ def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
     d_norm = float(np.sqrt(np.sum(d * d)))
     # reading: identity scaling of the parameter norm; ratio 1 when either norm is 0.
     trust = x_norm / d_norm if (x_norm > 0.0 and d_norm > 0.0) else 1.0
-    x_new = x - h["lr"] * trust * d
+    x_new = _stored(x - h["lr"] * trust * d, param_bf16)
     return x_new, {"exp_avg": m, "exp_avg_sq": v}
 
 
-def lamb_step(xs, gs, states, hp, t):
+def lamb_step(xs, gs, states, hp, t, **storage):
     out_x, out_s = [], []
     for x, g, st in zip(xs, gs, states):
-        a, b = lamb_step_tensor(x, g, st, hp, t)
+        a, b = lamb_step_tensor(x, g, st, hp, t, **storage)
         out_x.append(a)
         out_s.append(b)
     return out_x, out_s

@@ -35,7 +35,8 @@ def test_header_declares_the_binding_exports():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared():
         assert hasattr(lib, name), name
-    assert _lib.meo_version() == 1
+    declared = int(re.search(r"#define MEO_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert _lib.meo_version() == declared
 
 
 def test_defaults_are_the_pages(lib):
@@ -115,8 +116,24 @@ def test_tensor_checks(lib):
     t[0].grad_dtype = 7
     assert val(t) == _lib.MEO_EDTYPE
     t[0].grad_dtype = _lib.MEO_F32
-    t[0].param_dtype = _lib.MEO_BF16
+    t[0].param_dtype = 7
     assert val(t) == _lib.MEO_EDTYPE
+    assert "param_dtype" in _lib.meo_last_error()
+    t[0].param_dtype = _lib.MEO_F32
+    t[0].state_dtype = 2
+    assert val(t) == _lib.MEO_EDTYPE
+    assert "state_dtype" in _lib.meo_last_error()
+    t[0].state_dtype = _lib.MEO_BF16
+    assert val(t) == _lib.MEO_OK
+    t[0].state_dtype = _lib.MEO_F32
+    # a bf16 parameter needs 2-byte alignment only, an fp32 one 4
+    t[0].param = t[0].param + 2
+    assert val(t) == _lib.MEO_EALIGN
+    t[0].param_dtype = _lib.MEO_BF16
+    assert val(t) == _lib.MEO_OK
+    t[0].param = t[0].param + 1
+    assert val(t) == _lib.MEO_EALIGN
+    t[0].param = t[0].param - 3
     t[0].param_dtype = _lib.MEO_F32
     t[0].rows = -1
     assert val(t) == _lib.MEO_ESHAPE
@@ -135,6 +152,46 @@ def test_tensor_checks(lib):
     assert val(t) == _lib.MEO_OK
 
 
+def test_first_moment_alignment_follows_its_dtype(lib):
+    """exp_avg must be 4-byte aligned as fp32 and 2-byte aligned as bf16, for every
+    optimizer that keeps it."""
+    ps, gs = _mk([(4, 8)])
+    for opt, keys, cls, hp in (("adafactor", _lib.ADAFACTOR_KEYS, _lib.meo_adafactor_state,
+                                _lib.adafactor_hparams(beta1=0.9)),
+                               ("came", _lib.CAME_KEYS, _lib.meo_came_state, _lib.came_hparams(lr=1e-3)),
+                               ("lamb", _lib.LAMB_KEYS, _lib.meo_lamb_state, _lib.lamb_hparams())):
+        st = [_lib.init_state(opt, ps[0], beta1=True)]
+        t = _lib._tensors(ps, gs)
+        sts = _lib._states(cls, keys, st)
+        fn = getattr(lib, f"meo_{opt}_validate")
+
+        def val():
+            return fn(_lib.ctypes.byref(hp), 1, 1, t, sts)
+
+        assert val() == _lib.MEO_OK
+        sts[0].exp_avg += 2
+        assert val() == _lib.MEO_EALIGN, opt
+        t[0].state_dtype = _lib.MEO_BF16
+        assert val() == _lib.MEO_OK, opt
+        sts[0].exp_avg += 1
+        assert val() == _lib.MEO_EALIGN, opt
+
+
+def test_binding_rejects_mismatched_state_dtypes(lib):
+    """The binding declares exp_avg's dtype from the tensor itself and refuses
+    non-fp32 statistics (the library could not tell)."""
+    ps, gs = _mk([(4, 8)])
+    st = _lib.init_state("adafactor", ps[0], beta1=True, state_dtype=torch.bfloat16)
+    assert st["exp_avg"].dtype == torch.bfloat16 and st["exp_avg_sq_row"].dtype == torch.float32
+    assert _lib._tensors(ps, gs, [st])[0].state_dtype == _lib.MEO_BF16
+    bad = dict(st)
+    bad["exp_avg_sq_row"] = bad["exp_avg_sq_row"].to(torch.bfloat16)
+    with pytest.raises(TypeError):
+        _lib.meo_adafactor_validate(_lib.adafactor_hparams(beta1=0.9), 1, ps, gs, [bad])
+    with pytest.raises(TypeError):
+        _lib.tensor_struct(ps[0].to(torch.float16), gs[0])
+
+
 def test_workspace_checks(lib):
     ps, gs = _mk([(100, 600), (33,)])
     need = _lib.meo_adafactor_workspace_size(ps, gs)
@@ -149,6 +206,12 @@ def test_workspace_checks(lib):
     assert _code(_lib.meo_adafactor_step, hp, 1, ps, gs, st, None, 0)[0] == _lib.MEO_EWORKSPACE
     assert _lib.meo_lamb_workspace_size(ps, gs) > 0
     assert _lib.meo_came_workspace_size(ps, gs) > 0
+    # host memory of the right size and alignment is not device memory: refused
+    # before anything is enqueued (here, with no device at all, and on a GPU machine)
+    host = torch.empty(need + 256, dtype=torch.uint8)
+    off = (-host.data_ptr()) % 256
+    code, msg = _code(_lib.meo_adafactor_step, hp, 1, ps, gs, st, host[off:off + need], 0)
+    assert code in (_lib.MEO_EWORKSPACE, _lib.MEO_EHIP), (code, msg)
 
 
 def test_came_validation(lib):

@@ -1,0 +1,57 @@
+"""CPU checks of the parity bars used by the GPU tests (tests/harness.py): the
+16-bit rules accept the one-step rounding disagreements that near-tie values may
+take, and reject systematic faults planted on the CPU (truncation instead of
+rounding to nearest, a skipped rounding, a wrong value in a tail)."""
+import numpy as np
+
+import oracle
+from tests.harness import TOL_F32, bar_kind, judge
+
+
+def _bits_down(a):
+    """bf16 by truncation (the planted fault): drop the low 16 bits of the float32."""
+    f = np.asarray(a, dtype=np.float32)
+    return (f.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+
+
+def _one_step_up(a):
+    """The next bf16 value away from zero (a one-step rounding disagreement)."""
+    f = np.asarray(a, dtype=np.float32)
+    return (f.view(np.uint32) + np.uint32(0x10000)).view(np.float32).astype(np.float64)
+
+
+def test_bar_kinds():
+    st = dict(param_bf16=False, exp_avg_bf16=True)
+    assert bar_kind("adafactor", {}, st, "param") == "f32"                 # no first moment
+    assert bar_kind("adafactor", {"beta1": 0.9}, st, "param") == "bf16"    # stepped by a bf16 moment
+    assert bar_kind("came", {}, st, "exp_avg_res_row") == "bf16"
+    assert bar_kind("came", {}, st, "exp_avg_sq_col") == "f32"             # depends on G only
+    assert bar_kind("lamb", {}, st, "exp_avg_sq") == "f32"
+    assert bar_kind("lamb", {}, dict(param_bf16=True), "param") == "bf16"
+    assert bar_kind("lamb", {}, dict(param_bf16=True), "exp_avg") == "f32"
+
+
+def test_sixteen_bit_rules():
+    rng = np.random.default_rng(5)
+    exact = rng.normal(0, 1e-3, 20000)
+    ref = oracle.round_bf16(exact)
+    # one-step disagreements on a few near-tie elements pass
+    lib = ref.copy()
+    idx = rng.choice(lib.size, 60, replace=False)
+    lib[idx] = _one_step_up(lib[idx])
+    ok, err, over, n = judge("bf16", "exp_avg", lib, ref)
+    assert ok and over == 60 and err <= 2.0 ** -7
+    # the same disagreements fail the fp32 bar
+    assert not judge("f32", "exp_avg", lib, ref)[0]
+    # truncation instead of round-to-nearest moves about half the elements
+    ok, err, over, n = judge("bf16", "exp_avg", _bits_down(exact), ref)
+    assert not ok and over > 0.3 * n
+    # a skipped rounding (fp32 values stored) moves nearly all of them
+    assert not judge("bf16", "exp_avg", exact.astype(np.float32).astype(np.float64), ref)[0]
+    # garbage in a ragged tail of 7 elements breaks the elementwise bound
+    lib = ref.copy()
+    lib[-7:] = 0.0
+    assert not judge("bf16", "exp_avg", lib, ref)[0]
+    # an exact match passes both bars
+    assert judge("f32", "param", ref, ref)[:2] == (True, 0.0)
+    assert TOL_F32 == 1e-5

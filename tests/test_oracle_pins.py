@@ -436,3 +436,110 @@ def test_adafactor_matches_hugging_face(variant):
         xs, st = oracle.adafactor_step(xs, gs, st, variant, t)
         for p, x in zip(ps, xs):
             assert _rel(p.detach().numpy(), x) < 1e-12, (variant, t)
+
+
+# ----------------------------------------------------------------------------- 16-bit storage
+
+def _bf16_from_bits(hi):
+    """The bf16 value whose 16 bits are ``hi`` (as the upper half of a float32)."""
+    return np.array([hi << 16], dtype=np.uint32).view(np.float32).astype(np.float64)[0]
+
+
+def test_round_bf16_ties_and_limits():
+    """Closed forms of round-to-nearest-even at bf16's 7 fraction bits: 1 + 2^-8
+    is the midpoint of 1 and 1 + 2^-7 and goes to the even 1; 1 + 3 * 2^-8 goes up
+    to 1 + 2^-6; just above a midpoint goes up; the midpoint above the largest
+    finite bf16 (0x7f7f, odd) goes to +inf; signs are symmetric."""
+    r = oracle.round_bf16
+    assert r(1.0 + 2.0 ** -8) == 1.0
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+    assert r(-(1.0 + 2.0 ** -8)) == -1.0
+    assert r(1.0 + 2.0 ** -9) == 1.0
+    big = _bf16_from_bits(0x7F7F)
+    assert r(big) == big
+    mid = np.array([0x7F7F8000], dtype=np.uint32).view(np.float32).astype(np.float64)[0]
+    assert r(mid) == math.inf and r(-mid) == -math.inf
+    assert math.isnan(r(math.nan))
+    assert r(0.0) == 0.0 and math.copysign(1.0, r(-0.0)) == -1.0
+    # the smallest bf16 subnormal, and half of it (a tie with zero -> 0)
+    tiny = _bf16_from_bits(0x0001)
+    assert r(tiny) == tiny and r(tiny / 2) == 0.0
+
+
+def test_round_bf16_matches_torch():
+    """Against PyTorch's CPU float32 -> bfloat16 conversion (round to nearest even)
+    on random bit patterns, exact ties, subnormals and out-of-range values."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    bits = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2 ** 16, 20000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    f = np.concatenate([bits.view(np.float32), ties.view(np.float32),
+                        np.array([3.4e38, -3.4e38, 1e-40, -1e-45, np.inf, -np.inf], np.float32)])
+    f = f[~np.isnan(f)]
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_bf16(f.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("kind", ["adafactor", "came", "lamb"])
+def test_bf16_storage_outputs_are_bf16_values(kind):
+    """With 16-bit storage the new parameter and first moment are bf16 values, the
+    fp32-kept statistics equal those of fp32 storage (they depend on g only, except
+    CAME's confidence, which depends on the first moment), and the result stays
+    within bf16 rounding of the fp32-storage result on the first step."""
+    rng = np.random.default_rng(22)
+    shape = (6, 10)
+    x = oracle.round_bf16(rng.normal(0, 0.02, shape))
+    g = rng.normal(size=shape)
+    hp = {"adafactor": {"beta1": 0.9}, "came": {"lr": 1e-3}, "lamb": {}}[kind]
+    st = oracle.INIT_STATE[kind](shape, hp)
+    x16, s16 = oracle.STEP_TENSOR[kind](x, g, st, hp, 1, param_bf16=True, exp_avg_bf16=True)
+    x32, s32 = oracle.STEP_TENSOR[kind](x, g, st, hp, 1)
+    assert np.array_equal(oracle.round_bf16(x16), x16)
+    assert np.array_equal(oracle.round_bf16(s16["exp_avg"]), s16["exp_avg"])
+    for key in s32:
+        if key not in ("exp_avg", "exp_avg_res_row", "exp_avg_res_col"):
+            assert np.array_equal(s16[key], s32[key]), key
+    assert np.max(np.abs(s16["exp_avg"] - s32["exp_avg"]) / np.abs(s32["exp_avg"])) <= 2.0 ** -8
+    assert not np.array_equal(x16, x32)
+
+
+@pytest.mark.parametrize("kind", ["adafactor", "came"])
+def test_bf16_first_moment_is_the_step(kind):
+    """Adafactor with beta1 and 1-D CAME take the first moment itself as the step:
+    with 16-bit first-moment storage the step must be the *stored* (rounded) value,
+    not the unrounded one (fp32 parameter, no weight decay)."""
+    rng = np.random.default_rng(23)
+    shape = (6, 10) if kind == "adafactor" else (37,)
+    hp = {"adafactor": {"beta1": 0.9, "scale_parameter": False}, "came": {"lr": 1e-3}}[kind]
+    scale = 1e-2 if kind == "adafactor" else 1e-3   # the lr that multiplies the moment
+    x = rng.normal(0, 0.02, shape)
+    st = oracle.INIT_STATE[kind](shape, hp)
+    st["exp_avg"] = oracle.round_bf16(rng.normal(0, 1e-3, shape))
+    for t in (1, 2):
+        g = rng.normal(size=shape)
+        xn, st = oracle.STEP_TENSOR[kind](x, g, st, hp, t, exp_avg_bf16=True)
+        m = st["exp_avg"]
+        assert np.array_equal(oracle.round_bf16(m), m)
+        step = (x - xn) if kind == "adafactor" else (x - xn) / scale
+        assert np.allclose(step, m, rtol=1e-12, atol=1e-20)
+        x = xn
+
+
+def test_bf16_lamb_direction_uses_stored_moment():
+    """LAMB at step 1 with bias correction and no weight decay: the update is
+    lr * ||x|| times the unit direction of m_hat / (sqrt(v_hat) + eps), with
+    v_hat = g^2; with a bf16 first moment m_hat is the stored round(0.1 g) / 0.1,
+    which differs from g, so the direction must follow it."""
+    rng = np.random.default_rng(24)
+    shape = (7, 9)
+    x = rng.normal(0, 0.02, shape)
+    g = rng.normal(0, 1e-2, shape)
+    xn, st = oracle.lamb_step_tensor(x, g, oracle.lamb_init_state(shape), {}, 1, exp_avg_bf16=True)
+    m_hat = st["exp_avg"] / 0.1
+    d = m_hat / (np.abs(g) + 1e-6)
+    upd = (x - xn) / (1e-3 * np.linalg.norm(x))
+    assert np.allclose(upd, d / np.linalg.norm(d), rtol=1e-12, atol=0)
+    d32 = g / (np.abs(g) + 1e-6)
+    assert not np.allclose(upd, d32 / np.linalg.norm(d32), rtol=1e-6, atol=0)

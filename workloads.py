@@ -48,6 +48,8 @@ class Workload:
     grad_scaling: str  # "row": per-row scale; "rowcol": row x col scales; "none"
     steps: int
     seed: int = 0
+    param_dtype: torch.dtype = torch.float32   # storage of the parameter
+    state_dtype: torch.dtype = torch.float32   # storage of the first moment (exp_avg)
 
     @property
     def numel(self) -> int:
@@ -146,6 +148,13 @@ _register(_wl("came_llama_layer", "came", _CAME, llama_layer_specs(),
 _register(_wl("lamb_bert_large", "lamb", _LAMB, bert_specs(),
               torch.float32, 1e-2, "none", 20))
 
+# 16-bit storage: the 7B and one-layer Adafactor configurations with bf16
+# parameters and bf16 first moments.
+_register(dataclasses.replace(WORKLOADS["adafactor_llama7b"], name="adafactor_llama7b_bf16",
+                              param_dtype=torch.bfloat16, state_dtype=torch.bfloat16))
+_register(dataclasses.replace(WORKLOADS["adafactor_llama_layer"], name="adafactor_llama_layer_bf16",
+                              param_dtype=torch.bfloat16, state_dtype=torch.bfloat16))
+
 # Scaled-down versions of the same structure (ragged widths included) that the
 # oracle runs element by element in seconds.
 _register(_wl("adafactor_llama_mini", "adafactor", _AF_BETA1,
@@ -158,17 +167,24 @@ _register(_wl("lamb_bert_mini", "lamb", _LAMB,
               bert_specs(layers=2, hidden=128, ffn=512, vocab=3001, max_pos=64),
               torch.float32, 1e-2, "none", 10))
 
+# Scaled-down 16-bit-storage versions.
+for _n in ("adafactor_llama_mini", "came_llama_mini", "lamb_bert_mini"):
+    _register(dataclasses.replace(WORKLOADS[_n], name=_n + "_bf16", param_dtype=torch.bfloat16,
+                                  state_dtype=torch.bfloat16))
+del _n
+
 
 def custom(name: str, optimizer: str, shapes: Sequence[Tuple[int, ...]], *, hparams=None,
            grad_dtype=torch.float32, grad_std=1.0, grad_scaling="row", steps=3,
-           kinds: Optional[Sequence[str]] = None, seed: int = 0) -> Workload:
+           kinds: Optional[Sequence[str]] = None, seed: int = 0,
+           param_dtype=torch.float32, state_dtype=torch.float32) -> Workload:
     """An ad-hoc workload over the given shapes (edge cases in tests)."""
     specs = []
     for i, shp in enumerate(shapes):
         kind = kinds[i] if kinds else ("weight" if len(shp) >= 2 else "norm")
         specs.append(TensorSpec(f"t{i}", tuple(int(s) for s in shp), kind))
     return Workload(name, optimizer, dict(hparams or {}), tuple(specs), grad_dtype, grad_std,
-                    grad_scaling, steps, seed)
+                    grad_scaling, steps, seed, param_dtype, state_dtype)
 
 
 # ----------------------------------------------------------------------------- draws
@@ -185,14 +201,19 @@ def _pick(wl: Workload, indices):
 
 
 def init_params(wl: Workload, device="cpu", indices=None, out=None) -> List[torch.Tensor]:
-    """fp32 parameters: 2-D+ weights N(0, 0.02) (std 0.02), norm weights 1, biases 0.
-    ``indices`` selects tensors (same draws as in the full list); ``out`` gives the
-    fp32 tensors to fill in place (e.g. views into one flat buffer)."""
+    """Parameters of the workload's param dtype: 2-D+ weights N(0, 0.02) drawn in
+    fp32 (then rounded to a 16-bit dtype), norm weights 1, biases 0. ``indices``
+    selects tensors (same draws as in the full list); ``out`` gives tensors of the
+    param dtype to fill in place (e.g. views into one flat buffer)."""
     res = []
     for j, (k, s) in enumerate(_pick(wl, indices)):
-        t = out[j] if out is not None else torch.empty(s.shape, dtype=torch.float32, device=device)
+        t = out[j] if out is not None else torch.empty(s.shape, dtype=wl.param_dtype, device=device)
         if s.kind == "weight":
-            t.normal_(0.0, 0.02, generator=_gen(wl, k, 0, t.device))
+            if t.dtype == torch.float32:
+                t.normal_(0.0, 0.02, generator=_gen(wl, k, 0, t.device))
+            else:
+                w = torch.empty(s.shape, dtype=torch.float32, device=t.device)
+                t.copy_(w.normal_(0.0, 0.02, generator=_gen(wl, k, 0, t.device)))
         elif s.kind == "norm":
             t.fill_(1.0)
         else:
