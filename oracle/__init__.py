@@ -10,5 +10,5 @@ from .optimizers import (  # noqa: F401
     adafactor_beta2t, adafactor_hparams, adafactor_init_state, adafactor_step,
     adafactor_step_size, adafactor_step_tensor, came_hparams, came_init_state, came_step,
     came_step_tensor, is_factored, lamb_hparams, lamb_init_state, lamb_step, lamb_step_tensor,
-    rms, round_bf16,
+    rms, round_bf16, quantize_i8, dequantize_i8, I8_GROUP,
 )

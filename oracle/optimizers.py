@@ -38,6 +38,12 @@ Sources (the pages), by function:
   are bf16 values (exact in float64), the arithmetic is unchanged, and each new
   value is rounded to bf16 as it is formed (``round_bf16``), so the rest of the
   step uses the stored first moment.
+* 8-bit first moment: the GaLore section's 8-bit optimizer base (nbits=8,
+  block_wise=True) and the ms-swift page's Q-GaLore ``quantize_tensor`` (groups of
+  128 values, one absmax scale per group, int8 codes). With ``exp_avg_i8`` the
+  state holds ``exp_avg`` as int8 codes and ``exp_avg_scale`` as one float32 scale
+  per group; each step dequantizes, updates and re-quantizes the first moment, and
+  the rest of the step uses the dequantized new value (``quantize_i8``).
 
 Readings where the pages are silent are listed, with reasons, in the design notes
 of this repository; each is marked "reading" at the line that applies it.
@@ -112,6 +118,60 @@ def _stored(a: Array, bf16: bool) -> Array:
     return round_bf16(a) if bf16 else a
 
 
+I8_GROUP = 128  # the group_size of the ms-swift page's quantize_tensor
+
+
+def quantize_i8(a) -> Tuple[Array, Array]:
+    """(codes, scales) of the ms-swift page's group-wise int8 quantization (section
+    on Q-GaLore): the values, flattened, are cut into groups of 128 consecutive
+    ones; each group's scale is its largest magnitude / 127 and each code is
+    value / scale rounded to the nearest integer and clamped to [-128, 127].
+
+    reading: the arithmetic is that of the page's float32 tensors: values are first
+    rounded to float32, the scale is the float32 quotient and each code the float32
+    quotient rounded half to even (torch.round).
+    reading: a group of zeros gets scale 0 and codes 0 (the page would divide by 0).
+    reading: when the element count is not a multiple of 128 the last, shorter
+    group is a group of its own (the page's reshape needs a multiple)."""
+    x = np.asarray(a, dtype=np.float64).reshape(-1).astype(np.float32)
+    n = x.size
+    ng = -(-n // I8_GROUP)
+    padded = np.zeros(ng * I8_GROUP, dtype=np.float32)
+    padded[:n] = x
+    groups = padded.reshape(ng, I8_GROUP)
+    scale = (np.max(np.abs(groups), axis=1) / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint(groups / safe[:, None]).astype(np.float32)
+    q = np.where(scale[:, None] > 0, q, np.float32(0.0))
+    codes = np.clip(q, -128, 127).astype(np.int8).reshape(-1)[:n]
+    return codes.reshape(np.shape(a)), scale
+
+
+def dequantize_i8(codes, scales) -> Array:
+    """code * scale of its group, in float32 as on the page, returned as float64."""
+    q = np.asarray(codes).reshape(-1).astype(np.float32)
+    s = np.repeat(np.asarray(scales, dtype=np.float32), I8_GROUP)[:q.size]
+    return (q * s).astype(np.float64).reshape(np.shape(codes))
+
+
+def _moment_in(state: State, i8: bool) -> Array:
+    """The stored first moment as a value (dequantized when it is kept in 8 bits)."""
+    if i8:
+        return dequantize_i8(state["exp_avg"], state["exp_avg_scale"])
+    return state["exp_avg"]
+
+
+def _moment_out(m: Array, new: State, bf16: bool, i8: bool) -> Array:
+    """Stores a new first moment in `new` as its storage keeps it and returns the
+    value the rest of the step uses (reading: the stored one)."""
+    if i8:
+        codes, scales = quantize_i8(m)
+        new["exp_avg"], new["exp_avg_scale"] = codes, scales
+        return dequantize_i8(codes, scales)
+    new["exp_avg"] = _stored(m, bf16)
+    return new["exp_avg"]
+
+
 def is_factored(shape: Tuple[int, ...]) -> bool:
     """Page "Step 3": factored = len(param_shape) >= 2."""
     return len(shape) >= 2
@@ -153,15 +213,27 @@ def adafactor_beta2t(h: dict, t: int) -> float:
     return 1.0 - math.pow(t, h["decay_rate"])
 
 
-def adafactor_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None) -> State:
+def _i8_state(st: State, shape) -> State:
+    """Zero 8-bit first moment: int8 codes and one float32 scale per 128 values."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    st["exp_avg"] = np.zeros(shape, dtype=np.int8)
+    st["exp_avg_scale"] = np.zeros(-(-n // I8_GROUP), dtype=np.float32)
+    return st
+
+
+def adafactor_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None, *, exp_avg_i8: bool = False
+                         ) -> State:
     """Zero state with the shapes of page "Step 3": row statistic over shape[:-1],
     column statistic over shape[:-2] + shape[-1:], full statistic for 1-D, and
-    ``exp_avg`` only when beta1 is set."""
+    ``exp_avg`` only when beta1 is set (as codes and scales with ``exp_avg_i8``)."""
     h = adafactor_hparams(hp)
     shape = tuple(shape)
     st: State = {}
     if h["beta1"] is not None:
-        st["exp_avg"] = np.zeros(shape)
+        if exp_avg_i8:
+            _i8_state(st, shape)
+        else:
+            st["exp_avg"] = np.zeros(shape)
     if is_factored(shape):
         st["exp_avg_sq_row"] = np.zeros(shape[:-1])
         st["exp_avg_sq_col"] = np.zeros(shape[:-2] + shape[-1:])
@@ -171,7 +243,7 @@ def adafactor_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None) -> S
 
 
 def adafactor_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int, *,
-                          param_bf16: bool = False, exp_avg_bf16: bool = False
+                          param_bf16: bool = False, exp_avg_bf16: bool = False, exp_avg_i8: bool = False
                           ) -> Tuple[Array, State]:
     """One Adafactor step of one tensor; returns (new parameter, new state)."""
     h = adafactor_hparams(hp)
@@ -209,9 +281,8 @@ def adafactor_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], 
     u = alpha * u
     if h["beta1"] is not None:
         # reading: the first moment averages the clipped, lr-scaled update.
-        m = _stored(h["beta1"] * state["exp_avg"] + (1.0 - h["beta1"]) * u, exp_avg_bf16)
-        new["exp_avg"] = m
-        delta = m
+        m = h["beta1"] * _moment_in(state, exp_avg_i8) + (1.0 - h["beta1"]) * u
+        delta = _moment_out(m, new, exp_avg_bf16, exp_avg_i8)
     else:
         delta = u
     # reading: decoupled weight decay on the pre-update parameter, scaled by alpha.
@@ -245,11 +316,12 @@ def came_hparams(hp: Optional[dict] = None) -> dict:
     return h
 
 
-def came_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None) -> State:
+def came_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None, *, exp_avg_i8: bool = False
+                    ) -> State:
     """Zero state: first moment, factored (or full) squared-gradient statistic and,
     for factored tensors, the factored confidence statistic."""
     shape = tuple(shape)
-    st: State = {"exp_avg": np.zeros(shape)}
+    st: State = _i8_state({}, shape) if exp_avg_i8 else {"exp_avg": np.zeros(shape)}
     if is_factored(shape):
         st["exp_avg_sq_row"] = np.zeros(shape[:-1])
         st["exp_avg_sq_col"] = np.zeros(shape[:-2] + shape[-1:])
@@ -266,7 +338,7 @@ def _factored_estimate(row: Array, col: Array) -> Array:
 
 
 def came_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int, *,
-                     param_bf16: bool = False, exp_avg_bf16: bool = False
+                     param_bf16: bool = False, exp_avg_bf16: bool = False, exp_avg_i8: bool = False
                      ) -> Tuple[Array, State]:
     """One CAME step of one tensor; returns (new parameter, new state)."""
     h = came_hparams(hp)
@@ -297,8 +369,7 @@ def came_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
     u = g / np.sqrt(v_hat)
     u = u / max(1.0, rms(u) / h["clip_threshold"])
 
-    m = _stored(beta1 * state["exp_avg"] + (1.0 - beta1) * u, exp_avg_bf16)
-    new["exp_avg"] = m
+    m = _moment_out(beta1 * _moment_in(state, exp_avg_i8) + (1.0 - beta1) * u, new, exp_avg_bf16, exp_avg_i8)
 
     if fac:
         # Instability of the update against its running mean, factored the same
@@ -341,13 +412,16 @@ def lamb_hparams(hp: Optional[dict] = None) -> dict:
     return h
 
 
-def lamb_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None) -> State:
+def lamb_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None, *, exp_avg_i8: bool = False
+                    ) -> State:
     shape = tuple(shape)
-    return {"exp_avg": np.zeros(shape), "exp_avg_sq": np.zeros(shape)}
+    st: State = _i8_state({}, shape) if exp_avg_i8 else {"exp_avg": np.zeros(shape)}
+    st["exp_avg_sq"] = np.zeros(shape)
+    return st
 
 
 def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int, *,
-                     param_bf16: bool = False, exp_avg_bf16: bool = False
+                     param_bf16: bool = False, exp_avg_bf16: bool = False, exp_avg_i8: bool = False
                      ) -> Tuple[Array, State]:
     """One LAMB step of one tensor (the whole tensor is one layer for the trust ratio)."""
     h = lamb_hparams(hp)
@@ -358,7 +432,8 @@ def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
     if x.size == 0:
         return _untouched(x, state)
     beta1, beta2 = h["betas"]
-    m = _stored(beta1 * state["exp_avg"] + (1.0 - beta1) * g, exp_avg_bf16)
+    new: State = {}
+    m = _moment_out(beta1 * _moment_in(state, exp_avg_i8) + (1.0 - beta1) * g, new, exp_avg_bf16, exp_avg_i8)
     v = beta2 * state["exp_avg_sq"] + (1.0 - beta2) * g * g
     if h["bias_correction"]:
         m_hat = m / (1.0 - beta1 ** t)
@@ -372,7 +447,8 @@ def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
     # reading: identity scaling of the parameter norm; ratio 1 when either norm is 0.
     trust = x_norm / d_norm if (x_norm > 0.0 and d_norm > 0.0) else 1.0
     x_new = _stored(x - h["lr"] * trust * d, param_bf16)
-    return x_new, {"exp_avg": m, "exp_avg_sq": v}
+    new["exp_avg_sq"] = v
+    return x_new, new
 
 
 def lamb_step(xs, gs, states, hp, t, **storage):

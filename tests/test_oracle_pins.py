@@ -543,3 +543,105 @@ def test_bf16_lamb_direction_uses_stored_moment():
     assert np.allclose(upd, d / np.linalg.norm(d), rtol=1e-12, atol=0)
     d32 = g / (np.abs(g) + 1e-6)
     assert not np.allclose(upd, d32 / np.linalg.norm(d32), rtol=1e-6, atol=0)
+
+
+# ----------------------------------------------------------------------------- 8-bit first moment
+
+def test_quantize_i8_closed_forms():
+    """The ms-swift page's group quantizer on values whose results are fixed by its
+    definition: scale = 127 / 127 = 1, codes are the values rounded half to even
+    (torch.round), a zero group has scale 0 and codes 0, the last short group of a
+    300-element tensor is a group of its own, and the most negative value maps to
+    -127 (the absmax scale never needs -128)."""
+    q, s = oracle.quantize_i8(np.array([127.0, -127, 63.5, 62.5, 0.5, -0.5, 1.49, -2.5]))
+    assert s.tolist() == [1.0]
+    assert q.tolist() == [127, -127, 64, 62, 0, 0, 1, -2]
+    q, s = oracle.quantize_i8(np.zeros(130))
+    assert s.tolist() == [0.0, 0.0] and not q.any()
+    x = np.concatenate([np.full(128, 2.0), np.full(128, -0.5), np.linspace(-254.0, 0.0, 44)])
+    q, s = oracle.quantize_i8(x)
+    f32 = np.float32
+    assert s.tolist() == [f32(2.0) / f32(127), f32(0.5) / f32(127), 2.0]
+    assert (q[:128] == 127).all() and (q[128:256] == -127).all()
+    assert q[256] == -127 and q[-1] == 0
+    assert np.array_equal(oracle.dequantize_i8(q, s)[256:], np.rint(x[256:] / 2.0) * 2.0)
+
+
+def test_quantize_i8_invariants():
+    """On magnitudes spanning 8 decades: every nonzero group reaches |code| = 127,
+    dequantized values lie within half a step of the (float32) inputs, the map is
+    odd, and scaling by a power of two scales the scales and keeps the codes."""
+    rng = np.random.default_rng(31)
+    x = rng.normal(size=128 * 40 + 17) * 10.0 ** rng.uniform(-4, 4, 128 * 40 + 17)
+    q, s = oracle.quantize_i8(x)
+    groups = np.concatenate([q, np.zeros(-q.size % 128, np.int8)]).reshape(-1, 128)
+    assert (np.abs(groups.astype(int)).max(axis=1) == 127).all()
+    x32 = x.astype(np.float32).astype(np.float64)
+    step = np.repeat(s.astype(np.float64), 128)[:x.size]
+    assert (np.abs(oracle.dequantize_i8(q, s) - x32) <= 0.5 * step * (1 + 1e-6) + 1e-45).all()
+    deq = oracle.dequantize_i8(q, s)   # code x scale is a float32 product, as on the page
+    assert np.array_equal(deq.astype(np.float32).astype(np.float64), deq)
+    qn, sn = oracle.quantize_i8(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    q8, s8 = oracle.quantize_i8(x * 8.0)
+    assert np.array_equal(q8, q) and np.array_equal(s8, s * np.float32(8.0))
+
+
+@pytest.mark.parametrize("kind", ["adafactor", "came", "lamb"])
+def test_i8_first_moment_state(kind):
+    """With an 8-bit first moment the state holds int8 codes and one float32 scale
+    per 128 values; every nonzero group reaches |code| 127; the fp32-kept
+    statistics that depend on G only equal those of fp32 storage."""
+    rng = np.random.default_rng(32)
+    shape = (6, 256) if kind != "lamb" else (700,)
+    hp = {"adafactor": {"beta1": 0.9}, "came": {"lr": 1e-3}, "lamb": {}}[kind]
+    x = rng.normal(0, 0.02, shape)
+    g = rng.normal(size=shape)
+    s8 = oracle.INIT_STATE[kind](shape, hp, exp_avg_i8=True)
+    s32 = oracle.INIT_STATE[kind](shape, hp)
+    for t in (1, 2):
+        x8, s8 = oracle.STEP_TENSOR[kind](x, g, s8, hp, t, exp_avg_i8=True)
+        x32, s32 = oracle.STEP_TENSOR[kind](x, g, s32, hp, t)
+    assert s8["exp_avg"].dtype == np.int8 and s8["exp_avg_scale"].dtype == np.float32
+    assert s8["exp_avg_scale"].size == -(-int(np.prod(shape)) // 128)
+    codes = np.concatenate([s8["exp_avg"].reshape(-1), np.zeros(-s8["exp_avg"].size % 128, np.int8)])
+    assert (np.abs(codes.reshape(-1, 128).astype(int)).max(axis=1) == 127).all()
+    for key in s32:
+        if key not in ("exp_avg", "exp_avg_res_row", "exp_avg_res_col"):
+            assert np.array_equal(s8[key], s32[key]), key
+    m8 = oracle.dequantize_i8(s8["exp_avg"], s8["exp_avg_scale"])
+    assert np.max(np.abs(m8 - s32["exp_avg"])) <= 2.5 * np.max(s8["exp_avg_scale"])
+
+
+@pytest.mark.parametrize("kind", ["adafactor", "came"])
+def test_i8_step_is_the_dequantized_moment(kind):
+    """Adafactor with beta1 and 1-D CAME step by the first moment itself: with 8-bit
+    storage that is the dequantized stored value (codes x scale), not the
+    pre-quantization one."""
+    rng = np.random.default_rng(33)
+    shape = (4, 384) if kind == "adafactor" else (300,)
+    hp = {"adafactor": {"beta1": 0.9, "scale_parameter": False}, "came": {"lr": 1e-3}}[kind]
+    scale = 1.0 if kind == "adafactor" else 1e-3
+    x = rng.normal(0, 0.02, shape)
+    st = oracle.INIT_STATE[kind](shape, hp, exp_avg_i8=True)
+    for t in (1, 2, 3):
+        g = rng.normal(size=shape)
+        xn, st = oracle.STEP_TENSOR[kind](x, g, st, hp, t, exp_avg_i8=True)
+        m = oracle.dequantize_i8(st["exp_avg"], st["exp_avg_scale"])
+        # x - x_new cancels: the error is relative to x, so the bound is set by max |m|
+        assert np.allclose((x - xn) / scale, m, rtol=1e-12, atol=1e-12 * np.max(np.abs(m)))
+        x = xn
+
+
+def test_i8_lamb_direction_uses_dequantized_moment():
+    """LAMB step 1, bias correction, no decay: the update direction is that of
+    m_hat / (|g| + eps) with m_hat = dequantized stored m / 0.1."""
+    rng = np.random.default_rng(34)
+    x = rng.normal(0, 0.02, 512)
+    g = rng.normal(0, 1e-2, 512) * 10.0 ** rng.uniform(-2, 2, 512)
+    xn, st = oracle.lamb_step_tensor(x, g, oracle.lamb_init_state((512,), exp_avg_i8=True), {}, 1,
+                                     exp_avg_i8=True)
+    m_hat = oracle.dequantize_i8(st["exp_avg"], st["exp_avg_scale"]) / 0.1
+    d = m_hat / (np.abs(g) + 1e-6)
+    upd = (x - xn) / (1e-3 * np.linalg.norm(x))
+    assert np.allclose(upd, d / np.linalg.norm(d), rtol=1e-12, atol=1e-15)
