@@ -131,6 +131,9 @@ def quantize_i8(a) -> Tuple[Array, Array]:
     rounded to float32, the scale is the float32 quotient and each code the float32
     quotient rounded half to even (torch.round).
     reading: a group of zeros gets scale 0 and codes 0 (the page would divide by 0).
+    reading: a group holding a NaN or an infinity has no finite scale; it keeps
+    scale NaN and codes 0, so the whole group reads back NaN (a non-finite moment
+    stays visible, as it does in float32 storage).
     reading: when the element count is not a multiple of 128 the last, shorter
     group is a group of its own (the page's reshape needs a multiple)."""
     x = np.asarray(a, dtype=np.float64).reshape(-1).astype(np.float32)
@@ -139,10 +142,13 @@ def quantize_i8(a) -> Tuple[Array, Array]:
     padded = np.zeros(ng * I8_GROUP, dtype=np.float32)
     padded[:n] = x
     groups = padded.reshape(ng, I8_GROUP)
-    scale = (np.max(np.abs(groups), axis=1) / np.float32(127.0)).astype(np.float32)
-    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    q = np.rint(groups / safe[:, None]).astype(np.float32)
-    q = np.where(scale[:, None] > 0, q, np.float32(0.0))
+    with np.errstate(invalid="ignore", over="ignore"):
+        scale = (np.max(np.abs(groups), axis=1) / np.float32(127.0)).astype(np.float32)
+        scale[~np.isfinite(scale)] = np.float32(np.nan)
+        usable = np.isfinite(scale) & (scale > 0)
+        safe = np.where(usable, scale, np.float32(1.0)).astype(np.float32)
+        q = np.rint(groups / safe[:, None]).astype(np.float32)
+        q = np.where(usable[:, None], q, np.float32(0.0))
     codes = np.clip(q, -128, 127).astype(np.int8).reshape(-1)[:n]
     return codes.reshape(np.shape(a)), scale
 

@@ -565,6 +565,12 @@ def test_quantize_i8_closed_forms():
     assert (q[:128] == 127).all() and (q[128:256] == -127).all()
     assert q[256] == -127 and q[-1] == 0
     assert np.array_equal(oracle.dequantize_i8(q, s)[256:], np.rint(x[256:] / 2.0) * 2.0)
+    # a non-finite value makes its group read back NaN; other groups are unaffected
+    x = np.concatenate([np.ones(128), [np.nan] + [1.0] * 127, [np.inf] + [1.0] * 127])
+    q, s = oracle.quantize_i8(x)
+    d = oracle.dequantize_i8(q, s)
+    assert np.isnan(s[1:]).all() and not q[128:].any() and np.isnan(d[128:]).all()
+    assert np.array_equal(d[:128], np.ones(128))
 
 
 def test_quantize_i8_invariants():
