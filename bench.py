@@ -33,12 +33,21 @@ import time
 HBM_PEAK_GBPS = 8000.0
 
 
+def _moment_bytes(wl, spec) -> float:
+    """Bytes per element of the tensor's first moment: 4, 2, or 1 + 4 / 128 for
+    int8 codes with one float32 scale per 128 values (where the 8-bit rule applies)."""
+    import torch
+    from memory_efficient_optimizers_amd.optim import moment_dtype
+    dt = moment_dtype(wl.optimizer, spec.shape, wl.state_dtype, wl.param_dtype)
+    return {torch.float32: 4.0, torch.bfloat16: 2.0, torch.int8: 1.0 + 4.0 / 128}[dt]
+
+
 def _bytes_per_param(wl, spec, numel) -> dict:
     """Algorithmic bytes of one tensor: whole step, and per pass. gb, xb, mb: bytes
     per element of the gradient, the parameter and the first moment."""
     gb = 2 if str(wl.grad_dtype).endswith("bfloat16") else 4
     xb = 2 if str(wl.param_dtype).endswith("bfloat16") else 4
-    mb = 2 if str(wl.state_dtype).endswith("bfloat16") else 4
+    mb = _moment_bytes(wl, spec)
     fac = len(spec.shape) >= 2 and wl.optimizer != "lamb"
     n = numel
     if fac:
@@ -76,14 +85,17 @@ def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
     import oracle
     import workloads
 
+    from memory_efficient_optimizers_amd.optim import moment_dtype
     hp = dict(wl.hparams)
-    storage = dict(param_bf16=wl.param_dtype == torch.bfloat16, exp_avg_bf16=wl.state_dtype == torch.bfloat16)
     done, spent, names = 0, 0.0, []
     for k, spec in enumerate(wl.specs):
         x = workloads.init_params(wl, "cpu", [k])[0].to(torch.float64).numpy()
         sc = workloads.grad_scales(wl, "cpu", [k])
         g = workloads.grads(wl, 0, sc, "cpu", [k])[0].to(torch.float64).numpy()
-        st = oracle.INIT_STATE[wl.optimizer](x.shape, hp)
+        mdt = moment_dtype(wl.optimizer, spec.shape, wl.state_dtype, wl.param_dtype)
+        storage = dict(param_bf16=wl.param_dtype == torch.bfloat16, exp_avg_bf16=mdt == torch.bfloat16,
+                       exp_avg_i8=mdt == torch.int8)
+        st = oracle.INIT_STATE[wl.optimizer](x.shape, hp, exp_avg_i8=storage["exp_avg_i8"])
         t0 = time.perf_counter()
         oracle.STEP_TENSOR[wl.optimizer](x, g, st, hp, 1, **storage)
         spent += time.perf_counter() - t0
@@ -175,6 +187,7 @@ def main() -> int:
     import torch
     import workloads
     from memory_efficient_optimizers_amd import _lib
+    from memory_efficient_optimizers_amd.optim import moment_dtype
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -188,6 +201,7 @@ def main() -> int:
 
     hp = dict(wl.hparams)
     beta1 = hp.get("beta1") is not None
+    mdts = [moment_dtype(wl.optimizer, s.shape, wl.state_dtype, wl.param_dtype) for s in wl.specs]
     if args.layout == "flat":
         # One flat buffer per kind (parameters, gradients, each state), tensors as
         # 256-byte aligned views, as flat-parameter training frameworks keep them.
@@ -196,11 +210,11 @@ def main() -> int:
         workloads.init_params(wl, dev, out=params)
         grads = flat_views(torch, shapes, wl.grad_dtype, dev)
         workloads.grads(wl, 0, workloads.grad_scales(wl, dev), dev, out=grads)
-        proto = [_lib.state_shapes(wl.optimizer, s, beta1=beta1) for s in shapes]
+        proto = [_lib.state_shapes(wl.optimizer, s, beta1=beta1, i8=m == torch.int8) for s, m in zip(shapes, mdts)]
         states = [dict() for _ in shapes]
-        for key in sorted({k for st in proto for k in st}):
-            idx = [i for i, st in enumerate(proto) if key in st]
-            dt = wl.state_dtype if key == "exp_avg" else torch.float32
+        for key, dt in sorted({(k, mdts[i] if k == "exp_avg" else torch.float32)
+                               for i, st in enumerate(proto) for k in st}, key=str):
+            idx = [i for i, st in enumerate(proto) if key in st and (key != "exp_avg" or mdts[i] == dt)]
             views = flat_views(torch, [proto[i][key] for i in idx], dt, dev)
             for i, v in zip(idx, views):
                 v.zero_()
@@ -208,7 +222,7 @@ def main() -> int:
     else:
         params = workloads.init_params(wl, dev)
         grads = workloads.grads(wl, 0, workloads.grad_scales(wl, dev), dev)
-        states = [_lib.init_state(wl.optimizer, p, beta1=beta1, state_dtype=wl.state_dtype) for p in params]
+        states = [_lib.init_state(wl.optimizer, p, beta1=beta1, state_dtype=m) for p, m in zip(params, mdts)]
     hps = {"adafactor": _lib.adafactor_hparams, "came": _lib.came_hparams,
            "lamb": _lib.lamb_hparams}[wl.optimizer](**hp)
     wsize = getattr(_lib, f"meo_{wl.optimizer}_workspace_size")(params, grads)

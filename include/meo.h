@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MEO_VERSION 2
+#define MEO_VERSION 3
 
 /* Return codes. */
 #define MEO_OK          0
@@ -80,6 +80,7 @@ extern "C" {
 /* Element types. */
 #define MEO_F32  0
 #define MEO_BF16 1
+#define MEO_I8   2   /* state_dtype only: 8-bit group-quantized first moment */
 
 /*
  * One parameter tensor and its gradient, viewed as [batch, rows, cols]:
@@ -99,8 +100,8 @@ typedef struct meo_tensor {
     int32_t     param_dtype; /* MEO_F32 or MEO_BF16                            */
     int32_t     grad_dtype;  /* MEO_F32 or MEO_BF16                            */
     int32_t     state_dtype; /* element type of this tensor's exp_avg (first
-                                moment): MEO_F32 or MEO_BF16; every other state
-                                array is float32                               */
+                                moment): MEO_F32, MEO_BF16 or MEO_I8; every
+                                other state array is float32                   */
 } meo_tensor;
 
 /*
@@ -111,6 +112,18 @@ typedef struct meo_tensor {
  * step (the update, CAME's instability, LAMB's direction) see the rounded first
  * moment, exactly what the next step will read back. Statistics, second moments
  * and the workspace stay float32. A bf16 pointer must be 2-byte aligned.
+ *
+ * 8-bit first moment (state_dtype MEO_I8): the GaLore section's 8-bit optimizer
+ * base keeps its states block-wise quantized, and the ms-swift page's Q-GaLore
+ * code quantizes in groups of 128 values with one absmax scale each. exp_avg
+ * then holds int8 codes [numel] and exp_avg_scale one float32 scale per group of
+ * 128 consecutive values (row-major order) [ceil(numel / 128)]; a last short
+ * group stands alone. Each step dequantizes (code * scale), updates in float32,
+ * and re-quantizes: scale = max|m| / 127 over the group, code = m / scale rounded
+ * half to even (0 for a zero group). The rest of the step uses the dequantized
+ * new value. A group holding a NaN or an infinity stores scale NaN and codes 0.
+ * Factored tensors (Adafactor and CAME, ndim >= 2) need cols % 128 == 0, so that
+ * no group crosses a row (MEO_ESHAPE otherwise). Both states start at zero.
  */
 
 /* ------------------------------------------------------------------ Adafactor */
@@ -150,6 +163,7 @@ typedef struct meo_adafactor_state {
     float* exp_avg_sq_row; /* [batch*rows]; factored tensors only               */
     float* exp_avg_sq_col; /* [batch*cols]; factored tensors only               */
     float* exp_avg_sq;     /* [numel]; 1-D tensors only                          */
+    float* exp_avg_scale;  /* [ceil(numel / 128)]; iff exp_avg is MEO_I8          */
 } meo_adafactor_state;
 
 void   meo_adafactor_defaults(meo_adafactor_hparams* hp);
@@ -192,6 +206,7 @@ typedef struct meo_came_state {
     float* exp_avg_res_row; /* [batch*rows]; factored only                       */
     float* exp_avg_res_col; /* [batch*cols]; factored only                       */
     float* exp_avg_sq;      /* [numel]; 1-D only                                  */
+    float* exp_avg_scale;   /* [ceil(numel / 128)]; iff exp_avg is MEO_I8         */
 } meo_came_state;
 
 void   meo_came_defaults(meo_came_hparams* hp);
@@ -224,8 +239,9 @@ typedef struct meo_lamb_hparams {
 /* Per-tensor state, zero before the first step; exp_avg is state_dtype,
  * exp_avg_sq float32. */
 typedef struct meo_lamb_state {
-    void*  exp_avg;    /* state_dtype [numel] */
-    float* exp_avg_sq; /* [numel] */
+    void*  exp_avg;       /* state_dtype [numel] */
+    float* exp_avg_sq;    /* [numel] */
+    float* exp_avg_scale; /* [ceil(numel / 128)]; iff exp_avg is MEO_I8 */
 } meo_lamb_state;
 
 void   meo_lamb_defaults(meo_lamb_hparams* hp);

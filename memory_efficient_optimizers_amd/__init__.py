@@ -7,6 +7,6 @@ torch.optim front ends that own the state tensors.
 """
 from . import _lib  # noqa: F401
 from ._lib import MeoError  # noqa: F401
-from .optim import CAME, Adafactor, Lamb  # noqa: F401
+from .optim import CAME, Adafactor, Lamb, moment_dtype  # noqa: F401
 
-__all__ = ["Adafactor", "CAME", "Lamb", "MeoError"]
+__all__ = ["Adafactor", "CAME", "Lamb", "MeoError", "moment_dtype"]

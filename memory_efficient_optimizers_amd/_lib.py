@@ -24,7 +24,8 @@ c_float_p = ctypes.POINTER(ctypes.c_float)
 
 MEO_OK, MEO_EINVAL, MEO_ESHAPE, MEO_EDTYPE, MEO_ENULL, MEO_EWORKSPACE, MEO_EALIGN, MEO_EHIP, MEO_EMEMORY = (
     0, -1, -2, -3, -4, -5, -6, -7, -8)
-MEO_F32, MEO_BF16 = 0, 1
+MEO_F32, MEO_BF16, MEO_I8 = 0, 1, 2
+I8_GROUP = 128  # values per scale of an 8-bit first moment
 ERROR_NAMES = {MEO_EINVAL: "MEO_EINVAL", MEO_ESHAPE: "MEO_ESHAPE", MEO_EDTYPE: "MEO_EDTYPE",
                MEO_ENULL: "MEO_ENULL", MEO_EWORKSPACE: "MEO_EWORKSPACE", MEO_EALIGN: "MEO_EALIGN",
                MEO_EHIP: "MEO_EHIP", MEO_EMEMORY: "MEO_EMEMORY"}
@@ -61,7 +62,7 @@ class meo_adafactor_hparams(ctypes.Structure):
 
 class meo_adafactor_state(ctypes.Structure):
     _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq_row", c_void_p), ("exp_avg_sq_col", c_void_p),
-                ("exp_avg_sq", c_void_p)]
+                ("exp_avg_sq", c_void_p), ("exp_avg_scale", c_void_p)]
 
 
 class meo_came_hparams(ctypes.Structure):
@@ -74,7 +75,7 @@ class meo_came_hparams(ctypes.Structure):
 class meo_came_state(ctypes.Structure):
     _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq_row", c_void_p), ("exp_avg_sq_col", c_void_p),
                 ("exp_avg_res_row", c_void_p), ("exp_avg_res_col", c_void_p),
-                ("exp_avg_sq", c_void_p)]
+                ("exp_avg_sq", c_void_p), ("exp_avg_scale", c_void_p)]
 
 
 class meo_lamb_hparams(ctypes.Structure):
@@ -83,7 +84,7 @@ class meo_lamb_hparams(ctypes.Structure):
 
 
 class meo_lamb_state(ctypes.Structure):
-    _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq", c_void_p)]
+    _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq", c_void_p), ("exp_avg_scale", c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -141,6 +142,7 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 _DTYPE = {torch.float32: MEO_F32, torch.bfloat16: MEO_BF16}
+_STATE_DTYPE = {torch.float32: MEO_F32, torch.bfloat16: MEO_BF16, torch.int8: MEO_I8}
 
 
 def tensor_struct(param: torch.Tensor, grad: torch.Tensor,
@@ -151,8 +153,8 @@ def tensor_struct(param: torch.Tensor, grad: torch.Tensor,
         raise TypeError("parameters must be float32 or bfloat16")
     if grad.dtype not in _DTYPE:
         raise TypeError("gradients must be float32 or bfloat16")
-    if state_dtype not in _DTYPE:
-        raise TypeError("the first moment must be float32 or bfloat16")
+    if state_dtype not in _STATE_DTYPE:
+        raise TypeError("the first moment must be float32, bfloat16 or int8")
     if not (param.is_contiguous() and grad.is_contiguous()):
         raise ValueError("parameter and gradient must be contiguous")
     if grad.shape != param.shape:
@@ -166,7 +168,7 @@ def tensor_struct(param: torch.Tensor, grad: torch.Tensor,
     else:
         batch, rows, cols = 1, 1, param.numel()
     return meo_tensor(param.data_ptr(), grad.data_ptr(), batch, rows, cols, len(shape),
-                      _DTYPE[param.dtype], _DTYPE[grad.dtype], _DTYPE[state_dtype])
+                      _DTYPE[param.dtype], _DTYPE[grad.dtype], _STATE_DTYPE[state_dtype])
 
 
 def _tensors(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor], states=None):
@@ -200,16 +202,16 @@ def _states(cls, keys, states: Sequence[Dict[str, torch.Tensor]]):
     for i, st in enumerate(states):
         for k in keys:
             t = st.get(k)
-            if t is not None and t.dtype != torch.float32 and not (k == "exp_avg" and t.dtype == torch.bfloat16):
-                raise TypeError(f"state {k} must be float32" + (" or bfloat16" if k == "exp_avg" else ""))
+            if t is not None and t.dtype != torch.float32 and not (k == "exp_avg" and t.dtype in _STATE_DTYPE):
+                raise TypeError(f"state {k} must be float32" + (", bfloat16 or int8" if k == "exp_avg" else ""))
         arr[i] = cls(*[_ptr(st.get(k)) for k in keys])
     return arr
 
 
-ADAFACTOR_KEYS = ["exp_avg", "exp_avg_sq_row", "exp_avg_sq_col", "exp_avg_sq"]
+ADAFACTOR_KEYS = ["exp_avg", "exp_avg_sq_row", "exp_avg_sq_col", "exp_avg_sq", "exp_avg_scale"]
 CAME_KEYS = ["exp_avg", "exp_avg_sq_row", "exp_avg_sq_col", "exp_avg_res_row", "exp_avg_res_col",
-             "exp_avg_sq"]
-LAMB_KEYS = ["exp_avg", "exp_avg_sq"]
+             "exp_avg_sq", "exp_avg_scale"]
+LAMB_KEYS = ["exp_avg", "exp_avg_sq", "exp_avg_scale"]
 
 
 # ----------------------------------------------------------------------------- hparams
@@ -356,14 +358,24 @@ class PreparedStep:
 
 # ----------------------------------------------------------------------------- state allocation
 
-def state_shapes(optimizer: str, shape, *, beta1: bool = True) -> Dict[str, tuple]:
-    """Shapes of the state tensors of one parameter, as meo.h expects them."""
+def state_shapes(optimizer: str, shape, *, beta1: bool = True, i8: bool = False) -> Dict[str, tuple]:
+    """Shapes of the state tensors of one parameter, as meo.h expects them; with
+    ``i8`` the first moment also has one scale per 128 values."""
     shape = tuple(shape)
+    n = 1
+    for d in shape:
+        n *= d
+    groups = ((n + I8_GROUP - 1) // I8_GROUP,)
     if optimizer == "lamb":
-        return {"exp_avg": shape, "exp_avg_sq": shape}
+        st = {"exp_avg": shape, "exp_avg_sq": shape}
+        if i8:
+            st["exp_avg_scale"] = groups
+        return st
     st: Dict[str, tuple] = {}
     if optimizer == "came" or beta1:
         st["exp_avg"] = shape
+        if i8:
+            st["exp_avg_scale"] = groups
     if len(shape) >= 2:
         st["exp_avg_sq_row"] = shape[:-1]
         st["exp_avg_sq_col"] = shape[:-2] + shape[-1:]
@@ -378,9 +390,11 @@ def state_shapes(optimizer: str, shape, *, beta1: bool = True) -> Dict[str, tupl
 def init_state(optimizer: str, param: torch.Tensor, *, beta1: bool = True,
                state_dtype: torch.dtype = torch.float32) -> Dict[str, torch.Tensor]:
     """Zero state tensors for one parameter, with the shapes of meo.h: float32,
-    except the first moment ``exp_avg``, which is ``state_dtype``."""
+    except the first moment ``exp_avg``, which is ``state_dtype`` (float32, bfloat16,
+    or int8 codes with float32 ``exp_avg_scale``)."""
+    shapes = state_shapes(optimizer, param.shape, beta1=beta1, i8=state_dtype == torch.int8)
     return {k: torch.zeros(s, dtype=state_dtype if k == "exp_avg" else torch.float32, device=param.device)
-            for k, s in state_shapes(optimizer, param.shape, beta1=beta1).items()}
+            for k, s in shapes.items()}
 
 
 def workspace(nbytes: int, device) -> Optional[torch.Tensor]:

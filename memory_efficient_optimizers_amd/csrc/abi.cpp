@@ -33,9 +33,12 @@ int fail(int code, const std::string& msg) {
 
 enum Op { kOpAdafactor = 0, kOpCame = 1, kOpLamb = 2 };
 
+uintptr_t elem_bytes(int32_t dtype) { return dtype == MEO_F32 ? 4 : (dtype == MEO_BF16 ? 2 : 1); }
+
 // Uniform view of the per-tensor state pointers of the three optimizers.
 struct StatePtrs {
-    void* m = nullptr;   // float32 or bf16 (the tensor's state_dtype)
+    void* m = nullptr;   // float32, bf16 or int8 codes (the tensor's state_dtype)
+    float* ms = nullptr; // scales of an 8-bit first moment
     float* v = nullptr;
     float* r = nullptr;
     float* c = nullptr;
@@ -124,6 +127,25 @@ int64_t layout(int op, int32_t n, const meo_tensor* ts, std::vector<Geo>* out) {
 
 bool finite(double v) { return std::isfinite(v); }
 
+// The first moment of tensor k, when the step uses it: present and aligned for
+// its dtype; an 8-bit one also needs its scales and, for a factored tensor,
+// cols % 128 == 0 (no quantization group crosses a row).
+int check_moment(int op, int32_t k, const meo_tensor& t, const void* m, const float* scale, const char* why) {
+    int64_t numel = 0;
+    overflow_numel(t, &numel);
+    if (numel == 0) return MEO_OK;
+    const std::string who = "tensor " + std::to_string(k) + ": ";
+    if (!m) return fail(MEO_ENULL, who + "exp_avg is NULL" + why);
+    if (reinterpret_cast<uintptr_t>(m) % elem_bytes(t.state_dtype)) return fail(MEO_EALIGN, who + "exp_avg misaligned");
+    if (t.state_dtype == MEO_I8) {
+        if (!scale) return fail(MEO_ENULL, who + "exp_avg_scale is NULL (8-bit first moment)");
+        if (reinterpret_cast<uintptr_t>(scale) % 4) return fail(MEO_EALIGN, who + "exp_avg_scale misaligned");
+        if (is_factored(op, t) && t.cols % kI8Group != 0)
+            return fail(MEO_ESHAPE, who + "an 8-bit first moment of a factored tensor needs cols % 128 == 0");
+    }
+    return MEO_OK;
+}
+
 int check_tensors(int op, int64_t step, int32_t n, const meo_tensor* ts, const void* states) {
     if (step < 1) return fail(MEO_EINVAL, "step must be >= 1 (1-based index of the step being taken)");
     if (n < 0) return fail(MEO_EINVAL, "negative tensor count");
@@ -144,8 +166,8 @@ int check_tensors(int op, int64_t step, int32_t n, const meo_tensor* ts, const v
             return fail(MEO_EDTYPE, who + "param_dtype must be MEO_F32 or MEO_BF16");
         if (t.grad_dtype != MEO_F32 && t.grad_dtype != MEO_BF16)
             return fail(MEO_EDTYPE, who + "grad_dtype must be MEO_F32 or MEO_BF16");
-        if (t.state_dtype != MEO_F32 && t.state_dtype != MEO_BF16)
-            return fail(MEO_EDTYPE, who + "state_dtype must be MEO_F32 or MEO_BF16");
+        if (t.state_dtype != MEO_F32 && t.state_dtype != MEO_BF16 && t.state_dtype != MEO_I8)
+            return fail(MEO_EDTYPE, who + "state_dtype must be MEO_F32, MEO_BF16 or MEO_I8");
         if (numel == 0) continue;
         if (!t.param) return fail(MEO_ENULL, who + "param is NULL");
         if (!t.grad) return fail(MEO_ENULL, who + "grad is NULL");
@@ -169,20 +191,21 @@ int check_tensors(int op, int64_t step, int32_t n, const meo_tensor* ts, const v
         if (op == kOpAdafactor) {
             const auto& s = static_cast<const meo_adafactor_state*>(states)[k];
             sp.m = s.exp_avg; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col; sp.v = s.exp_avg_sq;
+            sp.ms = s.exp_avg_scale;
         } else if (op == kOpCame) {
             const auto& s = static_cast<const meo_came_state*>(states)[k];
-            sp.m = s.exp_avg; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col;
+            sp.m = s.exp_avg; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col; sp.ms = s.exp_avg_scale;
             sp.rr = s.exp_avg_res_row; sp.rc = s.exp_avg_res_col; sp.v = s.exp_avg_sq;
         } else {
             const auto& s = static_cast<const meo_lamb_state*>(states)[k];
-            sp.m = s.exp_avg; sp.v = s.exp_avg_sq;
+            sp.m = s.exp_avg; sp.v = s.exp_avg_sq; sp.ms = s.exp_avg_scale;
         }
         const void* need[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
         const char* names[6] = {"", "", "", "", "", ""};
         uintptr_t align[6] = {4, 4, 4, 4, 4, 4};
         int nn = 0;
         if (op == kOpLamb) {
-            align[nn] = t.state_dtype == MEO_BF16 ? 2 : 4;
+            align[nn] = elem_bytes(t.state_dtype);
             need[nn] = sp.m; names[nn++] = "exp_avg";
             need[nn] = sp.v; names[nn++] = "exp_avg_sq";
         } else {
@@ -308,7 +331,9 @@ int check_tensor_memory(int op, int32_t n, const meo_tensor* ts, const StatePtrs
         struct Range { const void* p; size_t bytes; const char* name; };
         std::vector<Range> rs = {{t.param, ne * (t.param_dtype == MEO_BF16 ? 2 : 4), "param"},
                                  {t.grad, ne * (t.grad_dtype == MEO_BF16 ? 2 : 4), "grad"}};
-        if (has_m) rs.push_back({sp[k].m, ne * (t.state_dtype == MEO_BF16 ? 2 : 4), "exp_avg"});
+        if (has_m) rs.push_back({sp[k].m, ne * elem_bytes(t.state_dtype), "exp_avg"});
+        if (has_m && t.state_dtype == MEO_I8)
+            rs.push_back({sp[k].ms, static_cast<size_t>((numel + kI8Group - 1) / kI8Group) * 4, "exp_avg_scale"});
         if (is_factored(op, t)) {
             rs.push_back({sp[k].r, rows * 4, "exp_avg_sq_row"});
             rs.push_back({sp[k].c, cols * 4, "exp_avg_sq_col"});
@@ -356,16 +381,24 @@ void free_plan(Plan* p) {
     delete p;
 }
 
-// All fp32, all bf16 (a first moment, where there is one, of the parameter's
-// type), or a mix.
+// One parameter type for the whole list, and one first-moment type among the
+// tensors that keep a moment: fp32/fp32, bf16/bf16, fp32/int8 or bf16/int8;
+// anything else is mixed (types read per tensor).
 int32_t storage_class(const std::vector<TDesc>& desc) {
-    bool all_f32 = true, all_bf16 = true;
+    if (desc.empty()) return kStoreF32;
+    const bool xb = desc[0].xbf16 != 0;
+    int mkind = -1;  // 0 fp32, 1 bf16, 2 int8; -1 no moment seen
     for (const TDesc& d : desc) {
-        const bool xb = d.xbf16 != 0, mb = d.m ? d.mbf16 != 0 : xb;
-        all_f32 = all_f32 && !xb && !mb;
-        all_bf16 = all_bf16 && xb && mb;
+        if ((d.xbf16 != 0) != xb) return kStoreMixed;
+        if (!d.m) continue;
+        const int k = d.mi8 ? 2 : (d.mbf16 ? 1 : 0);
+        if (mkind >= 0 && k != mkind) return kStoreMixed;
+        mkind = k;
     }
-    return all_f32 ? kStoreF32 : (all_bf16 ? kStoreBf16 : kStoreMixed);
+    if (mkind == 2) return xb ? kStoreBf16I8 : kStoreF32I8;
+    if (mkind == -1) return xb ? kStoreBf16 : kStoreF32;
+    if (mkind == (xb ? 1 : 0)) return xb ? kStoreBf16 : kStoreF32;
+    return kStoreMixed;
 }
 
 // Builds (or finds) the launch table for this list. Returns nullptr with g_err set
@@ -418,6 +451,8 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
         d.gbf16 = ts[k].grad_dtype == MEO_BF16;
         d.xbf16 = ts[k].param_dtype == MEO_BF16;
         d.mbf16 = ts[k].state_dtype == MEO_BF16;
+        d.mi8 = has_m && ts[k].state_dtype == MEO_I8;
+        d.ms = d.mi8 ? sp[k].ms : nullptr;
         bool vec = aligned16(d.x) && aligned16(d.g) && (!d.m || aligned16(d.m));
         if (g.mode != kFlat) vec = vec && (g.W % kVec == 0);
         else vec = vec && (!d.v || aligned16(d.v));
@@ -498,13 +533,15 @@ std::vector<StatePtrs> state_ptrs(int op, int32_t n, const void* states) {
         if (op == kOpAdafactor) {
             const auto& s = static_cast<const meo_adafactor_state*>(states)[k];
             sp.m = s.exp_avg; sp.v = s.exp_avg_sq; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col;
+            sp.ms = s.exp_avg_scale;
         } else if (op == kOpCame) {
             const auto& s = static_cast<const meo_came_state*>(states)[k];
             sp.m = s.exp_avg; sp.v = s.exp_avg_sq; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col;
+            sp.ms = s.exp_avg_scale;
             sp.rr = s.exp_avg_res_row; sp.rc = s.exp_avg_res_col;
         } else {
             const auto& s = static_cast<const meo_lamb_state*>(states)[k];
-            sp.m = s.exp_avg; sp.v = s.exp_avg_sq;
+            sp.m = s.exp_avg; sp.v = s.exp_avg_sq; sp.ms = s.exp_avg_scale;
         }
     }
     return out;
@@ -646,12 +683,8 @@ int meo_adafactor_validate(const meo_adafactor_hparams* hp, int64_t step, int32_
     if (rc) return rc;
     if (hp->has_beta1)
         for (int32_t k = 0; k < n; ++k) {
-            int64_t numel;
-            overflow_numel(ts[k], &numel);
-            if (numel > 0 && !st[k].exp_avg)
-                return fail(MEO_ENULL, "tensor " + std::to_string(k) + ": exp_avg is NULL but beta1 is set");
-            if (numel > 0 && reinterpret_cast<uintptr_t>(st[k].exp_avg) % (ts[k].state_dtype == MEO_BF16 ? 2 : 4))
-                return fail(MEO_EALIGN, "tensor " + std::to_string(k) + ": exp_avg misaligned");
+            rc = check_moment(kOpAdafactor, k, ts[k], st[k].exp_avg, st[k].exp_avg_scale, " but beta1 is set");
+            if (rc) return rc;
         }
     return MEO_OK;
 }
@@ -739,11 +772,8 @@ int meo_came_validate(const meo_came_hparams* hp, int64_t step, int32_t n, const
     rc = check_tensors(kOpCame, step, n, ts, st);
     if (rc) return rc;
     for (int32_t k = 0; k < n; ++k) {
-        int64_t numel;
-        overflow_numel(ts[k], &numel);
-        if (numel > 0 && !st[k].exp_avg) return fail(MEO_ENULL, "tensor " + std::to_string(k) + ": exp_avg is NULL");
-        if (numel > 0 && reinterpret_cast<uintptr_t>(st[k].exp_avg) % (ts[k].state_dtype == MEO_BF16 ? 2 : 4))
-            return fail(MEO_EALIGN, "tensor " + std::to_string(k) + ": exp_avg misaligned");
+        rc = check_moment(kOpCame, k, ts[k], st[k].exp_avg, st[k].exp_avg_scale, "");
+        if (rc) return rc;
     }
     return MEO_OK;
 }
@@ -825,7 +855,13 @@ int meo_lamb_validate(const meo_lamb_hparams* hp, int64_t step, int32_t n, const
     g_err.clear();
     int rc = check_lamb_hp(hp);
     if (rc) return rc;
-    return check_tensors(kOpLamb, step, n, ts, st);
+    rc = check_tensors(kOpLamb, step, n, ts, st);
+    if (rc) return rc;
+    for (int32_t k = 0; k < n; ++k) {
+        rc = check_moment(kOpLamb, k, ts[k], st[k].exp_avg, st[k].exp_avg_scale, "");
+        if (rc) return rc;
+    }
+    return MEO_OK;
 }
 
 int meo_lamb_step(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
     float* ws = t.ws;
-    const bool vec = d.vec, bf = d.gbf16, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d);
+    const bool vec = d.vec, bf = d.gbf16, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d), mi = m_is_i8<ST>(d);
     const float b1 = a.beta1, omb1 = a.omb1;
 
     if (d.mode != kFlat) {
@@ -40,33 +40,42 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
         }
         const float* rrow = d.r + static_cast<int64_t>(p.b) * d.H;
         float* rowpart = ws + d.rowpart + (static_cast<int64_t>(p.b) * d.tc + p.ct) * d.H;
-        for (int i0 = 0; i0 < p.nrows; i0 += 4) {
-            float g[4][kVec], m[4][kVec];
+        // 2 rows per batch with an 8-bit first moment (registers of its
+        // re-quantization), 4 otherwise.
+        constexpr int RB = (ST == kStoreF32I8 || ST == kStoreBf16I8) ? 2 : 4;
+        for (int i0 = 0; i0 < p.nrows; i0 += RB) {
+            float g[RB][kVec], m[RB][kVec];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < RB; ++i) {
                 if (i0 + i < p.nrows) {
                     const int64_t off = mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col;
                     load_v8(d.g, off, p.valid, vec, bf, g[i]);
-                    load_v8(d.m, off, p.valid, vec, mb, m[i]);
+                    load_m8(d, off, p.valid, vec, mb, mi, m[i]);
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < RB; ++i) {
                 if (i0 + i < p.nrows) {
                     const int row = p.row0 + i0 + i;
                     const int64_t off = mat + static_cast<int64_t>(row) * d.W + p.col;
                     const float rf = rsqrtf(ldf(rrow + row)) * coef;
+                    float u[kVec];
+#pragma unroll
+                    for (int e = 0; e < kVec; ++e) {
+                        u[e] = (g[i][e] * cf[e]) * rf;
+                        m[i][e] = fmaf(b1, m[i][e], omb1 * u[e]);
+                    }
+                    Q8 qm;
+                    settle_m8(m[i], mb, mi, qm);  // the instability uses the stored moment
                     float rs = 0.0f;
 #pragma unroll
                     for (int e = 0; e < kVec; ++e) {
-                        const float u = (g[i][e] * cf[e]) * rf;
-                        m[i][e] = as_stored(fmaf(b1, m[i][e], omb1 * u), mb);
-                        const float du = u - m[i][e];
+                        const float du = u[e] - m[i][e];
                         const float q = e < p.valid ? fmaf(du, du, a.eps2) : 0.0f;
                         cs[e] += q;
                         rs += q;
                     }
-                    store_v8(d.m, off, p.valid, vec, mb, m[i]);
+                    store_m8(d, off, p.valid, vec, mb, mi, m[i], qm);
                     rs = wave_sum(rs);
                     if (lane == 0) stf(rowpart + row, rs);
                 }
@@ -79,21 +88,25 @@ __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
         const float lr = a.lr;
         const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
         for (int it = 0; it < kFlatIters; ++it) {
+            // Block-uniform exit (cross-lane work of an 8-bit first moment).
+            if (base + static_cast<int64_t>(it) * kThreads * kVec >= d.numel) break;
             const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
             const int valid = clamp_valid(d.numel - i);
-            if (valid == 0) break;
             float g[kVec], v[kVec], x[kVec], m[kVec];
             load_v8(d.g, i, valid, vec, bf, g);
             load_f8(d.v + i, valid, vec, v);
             load_v8(d.x, i, valid, vec, xb, x);
-            load_v8(d.m, i, valid, vec, mb, m);
+            load_m8(d, i, valid, vec, mb, mi, m);
 #pragma unroll
             for (int e = 0; e < kVec; ++e) {
                 const float u = e < valid ? (g[e] * rsqrtf(v[e])) * coef : 0.0f;
-                m[e] = as_stored(fmaf(b1, m[e], omb1 * u), mb);
-                x[e] = fmaf(-decay, x[e], x[e]) - lr * m[e];
+                m[e] = fmaf(b1, m[e], omb1 * u);
             }
-            store_v8(d.m, i, valid, vec, mb, m);
+            Q8 qm;
+            settle_m8(m, mb, mi, qm);  // the step is the stored moment
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) x[e] = fmaf(-decay, x[e], x[e]) - lr * m[e];
+            store_m8(d, i, valid, vec, mb, mi, m, qm);
             store_v8(d.x, i, valid, vec, xb, x);
         }
     }
@@ -104,6 +117,8 @@ void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, int storage, 
     const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
     if (storage == kStoreF32) hipLaunchKernelGGL(k_came_mom<kStoreF32>, grid, block, 0, s, t, a);
     else if (storage == kStoreBf16) hipLaunchKernelGGL(k_came_mom<kStoreBf16>, grid, block, 0, s, t, a);
+    else if (storage == kStoreF32I8) hipLaunchKernelGGL(k_came_mom<kStoreF32I8>, grid, block, 0, s, t, a);
+    else if (storage == kStoreBf16I8) hipLaunchKernelGGL(k_came_mom<kStoreBf16I8>, grid, block, 0, s, t, a);
     else hipLaunchKernelGGL(k_came_mom<kStoreMixed>, grid, block, 0, s, t, a);
 }
 
@@ -114,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
     if (d.mode == kFlat) return;  // 1-D tensors were finished by k_came_mom
     const int lt = it.y;
     const float* ws = t.ws;
-    const bool vec = d.vec, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d);
+    const bool vec = d.vec, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d), mi = m_is_i8<ST>(d);
     const TileRC p = tile_rc(d, lt);
     const float coef = ldf(ws + d.bscal + d.B + p.b);
     const float decay = ldf(ws + d.scal + kSlotDecay);
@@ -131,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
             if (i0 + i < p.nrows) {
                 const int64_t off = mat + static_cast<int64_t>(p.row0 + i0 + i) * d.W + p.col;
                 load_v8(d.x, off, p.valid, vec, xb, x[i]);
-                load_v8(d.m, off, p.valid, vec, mb, m[i]);
+                load_m8(d, off, p.valid, vec, mb, mi, m[i]);
             }
         }
 #pragma unroll
@@ -153,6 +168,8 @@ void launch_came_apply(const Table& t, int64_t n, int storage, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
     if (storage == kStoreF32) hipLaunchKernelGGL(k_came_apply<kStoreF32>, grid, block, 0, s, t);
     else if (storage == kStoreBf16) hipLaunchKernelGGL(k_came_apply<kStoreBf16>, grid, block, 0, s, t);
+    else if (storage == kStoreF32I8) hipLaunchKernelGGL(k_came_apply<kStoreF32I8>, grid, block, 0, s, t);
+    else if (storage == kStoreBf16I8) hipLaunchKernelGGL(k_came_apply<kStoreBf16I8>, grid, block, 0, s, t);
     else hipLaunchKernelGGL(k_came_apply<kStoreMixed>, grid, block, 0, s, t);
 }
 

@@ -48,9 +48,14 @@ enum ScalSlot { kSlotAlpha = 0, kSlotCoef = 1, kSlotDecay = 2, kSlotRmsU = 3, kS
                 kSlotNormD = 5 };
 
 // Storage class of a launch's parameters and first moments: all fp32, all bf16,
-// or a mix (then read per tensor from its descriptor). The streaming kernels are
-// compiled once per class, so the uniform cases carry no dtype branches.
-enum Storage { kStoreF32 = 0, kStoreBf16 = 1, kStoreMixed = 2 };
+// fp32 or bf16 parameters with 8-bit first moments, or a mix (then read per tensor
+// from its descriptor). The streaming kernels are compiled once per class, so the
+// uniform cases carry no dtype branches.
+enum Storage { kStoreF32 = 0, kStoreBf16 = 1, kStoreMixed = 2, kStoreF32I8 = 3, kStoreBf16I8 = 4 };
+
+// 8-bit first moment: one float32 scale per group of 128 consecutive values,
+// i.e. 16 lanes of 8 values.
+constexpr int kI8Group = 128;
 
 // How a tensor's statistics are gathered.
 enum Mode { kFlat = 0, kRowComplete = 1, kTiled = 2 };
@@ -59,7 +64,8 @@ enum Mode { kFlat = 0, kRowComplete = 1, kTiled = 2 };
 struct TDesc {
     void* x;          // parameter (fp32 or bf16)
     const void* g;    // gradient (fp32 or bf16)
-    void* m;          // first moment (fp32 or bf16; nullable)
+    void* m;          // first moment (fp32, bf16 or int8 codes; nullable)
+    float* ms;        // scales of an 8-bit first moment [ceil(numel / 128)]
     float* v;         // full second moment (1-D Adafactor/CAME; LAMB)
     float* r;         // factored row statistic [B*H]
     float* c;         // factored column statistic [B*W]
@@ -81,6 +87,7 @@ struct TDesc {
     int32_t gbf16;    // gradient dtype is bf16
     int32_t xbf16;    // parameter dtype is bf16
     int32_t mbf16;    // first-moment dtype is bf16
+    int32_t mi8;      // first moment is 8-bit group-quantized
     int32_t vec;      // 16-byte vector accesses are valid
     int32_t tr, tc;   // 2-D tiles per matrix along rows / columns (flat: tr = 1, tc = tiles)
     int32_t strips;   // row-complete strips per matrix
@@ -103,11 +110,15 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // Element types of a tensor's parameter and first moment under storage class ST.
 template <int ST>
 __device__ __forceinline__ bool x_is_bf16(const TDesc& d) {
-    return ST == kStoreMixed ? d.xbf16 != 0 : ST == kStoreBf16;
+    return ST == kStoreMixed ? d.xbf16 != 0 : (ST == kStoreBf16 || ST == kStoreBf16I8);
 }
 template <int ST>
 __device__ __forceinline__ bool m_is_bf16(const TDesc& d) {
     return ST == kStoreMixed ? d.mbf16 != 0 : ST == kStoreBf16;
+}
+template <int ST>
+__device__ __forceinline__ bool m_is_i8(const TDesc& d) {
+    return ST == kStoreMixed ? d.mi8 != 0 : (ST == kStoreF32I8 || ST == kStoreBf16I8);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -250,10 +261,6 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// A freshly formed first-moment value as it will be stored: rounded to bf16
-// when the first moment is held in bf16, so that every later use in the step
-// sees the stored value.
-__device__ __forceinline__ float as_stored(float v, bool bf16) { return bf16 ? round_bf16(v) : v; }
 
 // 8 fp32 values rounded to bf16 (nearest, ties to even), packed in element order.
 __device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
@@ -293,6 +300,117 @@ __device__ __forceinline__ u32x4 buf_ld(Rsrc r, uint32_t lane_off, uint32_t row_
 }
 __device__ __forceinline__ void buf_st(u32x4 v, Rsrc r, uint32_t lane_off, uint32_t row_off) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, lane_off, row_off, 0);
+}
+
+// ----------------------------------------------------------------------------- 8-bit first moment
+
+// 8 values of an 8-bit first moment at element i (a multiple of 8): codes times
+// their group's scale, in fp32; the `valid` first are in range, the rest read 0.
+__device__ __forceinline__ void load_i8x8(const void* __restrict__ codes, const float* __restrict__ scales,
+                                          int64_t i, int valid, bool vec, float* f) {
+    if (valid <= 0) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) f[e] = 0.0f;
+        return;
+    }
+    const float s = *gld<float>(scales + (i >> 7));
+    const int8_t* p = static_cast<const int8_t*>(codes) + i;
+    if (vec && valid == kVec) {
+        typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+        const u32x2v w = *gld<u32x2v>(p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = static_cast<float>(static_cast<int8_t>(w.x >> (8 * e))) * s;
+            f[4 + e] = static_cast<float>(static_cast<int8_t>(w.y >> (8 * e))) * s;
+        }
+    } else {
+        const MEO_GLOBAL int8_t* q = gld<int8_t>(p);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) f[e] = e < valid ? static_cast<float>(q[e]) * s : 0.0f;
+    }
+}
+
+// Re-quantizes this lane's 8 new values together with the 15 other lanes of its
+// group of 128 (lanes 16k..16k+15 hold consecutive values): scale = max|m| / 127,
+// code = m / scale rounded half to even and clamped to [-128, 127] (0 when the
+// scale is 0; a NaN or infinite maximum gives scale NaN and codes 0). `m` is
+// replaced by the dequantized values. Values outside the tensor must be 0. Every
+// lane of the wave calls it (cross-lane maximum).
+// Larger of two magnitudes, a NaN winning.
+__device__ __forceinline__ float max_nan(float a, float b) { return (b > a || b != b) ? b : a; }
+
+// DPP move within a row of 16 lanes (all lanes active).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ void quant_i8x8(float* m, uint32_t& lo, uint32_t& hi, float& scale) {
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) a = max_nan(a, fabsf(m[e]));
+    // Maximum over the 16 lanes of the group, which is one DPP row: swap neighbours,
+    // swap pairs, mirror halves, mirror the row.
+    a = max_nan(a, dpp<0xb1>(a));   // quad_perm [1, 0, 3, 2]
+    a = max_nan(a, dpp<0x4e>(a));   // quad_perm [2, 3, 0, 1]
+    a = max_nan(a, dpp<0x141>(a));  // row_half_mirror
+    a = max_nan(a, dpp<0x140>(a));  // row_mirror
+    scale = a / 127.0f;
+    const bool ok = scale > 0.0f && scale <= 3.402823466e38f;  // finite and nonzero
+    if (!(scale <= 3.402823466e38f)) scale = __builtin_nanf("");
+    lo = 0u;
+    hi = 0u;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+        float q = ok ? rintf(m[e] / scale) : 0.0f;  // the fp32 quotient, rounded half to even
+        q = fminf(fmaxf(q, -128.0f), 127.0f);
+        const uint32_t byte = static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xffu;
+        if (e < 4) lo |= byte << (8 * e); else hi |= byte << (8 * (e - 4));
+        m[e] = q * scale;  // a zero scale reads back 0, a NaN one NaN
+    }
+}
+
+// Stores the codes of quant_i8x8 at element i (the `valid` first of 8) and, from
+// the first lane of each group that holds data, the group's scale.
+__device__ __forceinline__ void store_i8x8(void* __restrict__ codes, float* __restrict__ scales, int64_t i,
+                                           int valid, bool vec, uint32_t lo, uint32_t hi, float scale) {
+    if (valid <= 0) return;
+    int8_t* p = static_cast<int8_t*>(codes) + i;
+    if (vec && valid == kVec) {
+        typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+        *gst<u32x2v>(p) = u32x2v{lo, hi};
+    } else {
+        MEO_GLOBAL int8_t* q = gst<int8_t>(p);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e)
+            if (e < valid) q[e] = static_cast<int8_t>(((e < 4 ? lo >> (8 * e) : hi >> (8 * (e - 4)))) & 0xffu);
+    }
+    if ((i & (kI8Group - 1)) == 0) *gst<float>(scales + (i >> 7)) = scale;
+}
+
+// Storage of a new first moment: bf16 rounding or 8-bit re-quantization (with
+// its codes and scale kept for the store). After settle_m8, `m` holds the values
+// the rest of the step uses; every lane of the wave calls it.
+struct Q8 {
+    uint32_t lo = 0u, hi = 0u;
+    float s = 0.0f;
+};
+__device__ __forceinline__ void load_m8(const TDesc& d, int64_t i, int valid, bool vec, bool mb, bool mi, float* f) {
+    if (mi) load_i8x8(d.m, d.ms, i, valid, vec, f);
+    else load_v8(d.m, i, valid, vec, mb, f);
+}
+__device__ __forceinline__ void settle_m8(float* m, bool mb, bool mi, Q8& q) {
+    if (mi) {
+        quant_i8x8(m, q.lo, q.hi, q.s);
+    } else if (mb) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) m[e] = round_bf16(m[e]);
+    }
+}
+__device__ __forceinline__ void store_m8(const TDesc& d, int64_t i, int valid, bool vec, bool mb, bool mi,
+                                         const float* m, const Q8& q) {
+    if (mi) store_i8x8(d.m, d.ms, i, valid, vec, q.lo, q.hi, q.s);
+    else store_v8(d.m, i, valid, vec, mb, m);
 }
 
 // Scalar accesses of state vectors and workspace through generic pointers.

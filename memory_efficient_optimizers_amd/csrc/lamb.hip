@@ -24,29 +24,35 @@ __global__ __launch_bounds__(kThreads) void k_lamb_moments(Table t, LambArgs a) 
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
-    const bool vec = d.vec, bf = d.gbf16, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d);
+    const bool vec = d.vec, bf = d.gbf16, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d), mi = m_is_i8<ST>(d);
     const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
     float sx[kVec], sd[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) { sx[e] = 0.0f; sd[e] = 0.0f; }
     for (int it = 0; it < kFlatIters; ++it) {
+        // Block-uniform exit (cross-lane work of an 8-bit first moment).
+        if (base + static_cast<int64_t>(it) * kThreads * kVec >= d.numel) break;
         const int64_t i = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * kVec;
         const int valid = clamp_valid(d.numel - i);
-        if (valid == 0) break;
         float g[kVec], x[kVec], m[kVec], v[kVec];
         load_v8(d.g, i, valid, vec, bf, g);
         load_v8(d.x, i, valid, vec, xb, x);
-        load_v8(d.m, i, valid, vec, mb, m);
+        load_m8(d, i, valid, vec, mb, mi, m);
         load_f8(d.v + i, valid, vec, v);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
-            m[e] = as_stored(fmaf(a.beta1, m[e], a.omb1 * g[e]), mb);
+            m[e] = fmaf(a.beta1, m[e], a.omb1 * g[e]);
             v[e] = fmaf(a.beta2, v[e], a.omb2 * (g[e] * g[e]));
+        }
+        Q8 qm;
+        settle_m8(m, mb, mi, qm);  // the direction uses the stored moment
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
             const float dd = e < valid ? lamb_dir(m[e], v[e], x[e], a) : 0.0f;
             sx[e] = fmaf(x[e], x[e], sx[e]);
             sd[e] = fmaf(dd, dd, sd[e]);
         }
-        store_v8(d.m, i, valid, vec, mb, m);
+        store_m8(d, i, valid, vec, mb, mi, m, qm);
         store_f8(d.v + i, valid, vec, v);
     }
     float tx = sum8(sx), td = sum8(sd);
@@ -63,6 +69,8 @@ void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, int stora
     const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
     if (storage == kStoreF32) hipLaunchKernelGGL(k_lamb_moments<kStoreF32>, grid, block, 0, s, t, a);
     else if (storage == kStoreBf16) hipLaunchKernelGGL(k_lamb_moments<kStoreBf16>, grid, block, 0, s, t, a);
+    else if (storage == kStoreF32I8) hipLaunchKernelGGL(k_lamb_moments<kStoreF32I8>, grid, block, 0, s, t, a);
+    else if (storage == kStoreBf16I8) hipLaunchKernelGGL(k_lamb_moments<kStoreBf16I8>, grid, block, 0, s, t, a);
     else hipLaunchKernelGGL(k_lamb_moments<kStoreMixed>, grid, block, 0, s, t, a);
 }
 
@@ -71,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void k_lamb_apply(Table t, LambArgs a) {
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
-    const bool vec = d.vec, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d);
+    const bool vec = d.vec, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d), mi = m_is_i8<ST>(d);
     const float coef = ldf(t.ws + d.bscal);
     const int64_t base = static_cast<int64_t>(lt) * kFlatTile;
     for (int it = 0; it < kFlatIters; ++it) {
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void k_lamb_apply(Table t, LambArgs a) {
         if (valid == 0) break;
         float x[kVec], m[kVec], v[kVec];
         load_v8(d.x, i, valid, vec, xb, x);
-        load_v8(d.m, i, valid, vec, mb, m);
+        load_m8(d, i, valid, vec, mb, mi, m);
         load_f8(d.v + i, valid, vec, v);
 #pragma unroll
         for (int e = 0; e < kVec; ++e) x[e] = x[e] - coef * lamb_dir(m[e], v[e], x[e], a);
@@ -93,6 +101,8 @@ void launch_lamb_apply(const Table& t, int64_t n, const LambArgs& a, int storage
     const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
     if (storage == kStoreF32) hipLaunchKernelGGL(k_lamb_apply<kStoreF32>, grid, block, 0, s, t, a);
     else if (storage == kStoreBf16) hipLaunchKernelGGL(k_lamb_apply<kStoreBf16>, grid, block, 0, s, t, a);
+    else if (storage == kStoreF32I8) hipLaunchKernelGGL(k_lamb_apply<kStoreF32I8>, grid, block, 0, s, t, a);
+    else if (storage == kStoreBf16I8) hipLaunchKernelGGL(k_lamb_apply<kStoreBf16I8>, grid, block, 0, s, t, a);
     else hipLaunchKernelGGL(k_lamb_apply<kStoreMixed>, grid, block, 0, s, t, a);
 }
 

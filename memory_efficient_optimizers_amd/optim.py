@@ -14,7 +14,10 @@ mentions a memory-saving 16-bit path). Statistics are always float32; the first
 moment ``exp_avg`` is kept in ``state_dtype``, which by default follows the
 parameter (bfloat16 parameters get a bfloat16 first moment, float32 ones a
 float32 one). The arithmetic is float32 throughout, and bfloat16 values are
-rounded to nearest even when stored.
+rounded to nearest even when stored. ``state_dtype=torch.int8`` keeps the first
+moment 8-bit group-quantized (128 values per float32 scale, the GaLore section's
+8-bit base and the ms-swift page's quantizer) for every tensor that
+``moment_dtype`` allows; the others keep it in float32.
 """
 from __future__ import annotations
 
@@ -26,20 +29,40 @@ import torch
 from . import _lib
 
 
+def moment_dtype(optimizer: str, shape, requested: Optional[torch.dtype], param_dtype: torch.dtype,
+                 min_8bit_size: int = 4096) -> torch.dtype:
+    """The first moment's dtype for one parameter. None follows the parameter
+    (bfloat16 -> bfloat16, else float32). int8 applies to tensors of at least
+    ``min_8bit_size`` elements (the GaLore section's 8-bit optimizer default: smaller
+    ones stay 32-bit) whose rows hold whole groups of 128 when the statistics are
+    factored (Adafactor and CAME with ndim >= 2); other tensors get float32."""
+    if requested is None:
+        return torch.bfloat16 if param_dtype == torch.bfloat16 else torch.float32
+    if requested != torch.int8:
+        return requested
+    shape = tuple(shape)
+    n = 1
+    for d in shape:
+        n *= d
+    factored = optimizer != "lamb" and len(shape) >= 2
+    if n < min_8bit_size or (factored and shape[-1] % _lib.I8_GROUP != 0):
+        return torch.float32
+    return torch.int8
+
+
 class _MeoOptimizer(torch.optim.Optimizer):
     _kind = ""
 
-    def __init__(self, params, defaults, state_dtype: Optional[torch.dtype] = None):
-        if state_dtype not in (None, torch.float32, torch.bfloat16):
-            raise TypeError("state_dtype must be None, torch.float32 or torch.bfloat16")
+    def __init__(self, params, defaults, state_dtype: Optional[torch.dtype] = None, min_8bit_size: int = 4096):
+        if state_dtype not in (None, torch.float32, torch.bfloat16, torch.int8):
+            raise TypeError("state_dtype must be None, torch.float32, torch.bfloat16 or torch.int8")
         super().__init__(params, defaults)
         self._state_dtype = state_dtype
+        self._min_8bit_size = min_8bit_size
         self._workspace: Dict[torch.device, torch.Tensor] = {}
 
     def _moment_dtype(self, p: torch.Tensor) -> torch.dtype:
-        if self._state_dtype is not None:
-            return self._state_dtype
-        return torch.bfloat16 if p.dtype == torch.bfloat16 else torch.float32
+        return moment_dtype(self._kind, p.shape, self._state_dtype, p.dtype, self._min_8bit_size)
 
     def _ws(self, nbytes: int, device) -> Optional[torch.Tensor]:
         if nbytes <= 0:
@@ -104,7 +127,8 @@ class Adafactor(_MeoOptimizer):
     """Adafactor with the page's defaults ("Step 3"): lr=None, eps=(1e-30, 1e-3),
     clip_threshold=1.0, decay_rate=-0.8, beta1=None, weight_decay=0.0,
     scale_parameter=True, relative_step=True, warmup_init=False. ``state_dtype``:
-    element type of ``exp_avg`` (None: that of the parameter)."""
+    element type of ``exp_avg`` (None: that of the parameter; torch.int8: 8-bit where
+    ``moment_dtype`` allows, with ``min_8bit_size``)."""
 
     _kind = "adafactor"
     _HP = ("lr", "eps", "clip_threshold", "decay_rate", "beta1", "weight_decay", "scale_parameter",
@@ -112,7 +136,8 @@ class Adafactor(_MeoOptimizer):
 
     def __init__(self, params, lr=None, eps=(1e-30, 1e-3), clip_threshold=1.0, decay_rate=-0.8,
                  beta1=None, weight_decay=0.0, scale_parameter=True, relative_step=True,
-                 warmup_init=False, state_dtype=None):
+                 warmup_init=False, state_dtype=None,
+                 min_8bit_size=4096):
         if lr is not None and relative_step:
             raise ValueError("Cannot combine manual lr and relative_step=True options")
         if warmup_init and not relative_step:
@@ -120,7 +145,7 @@ class Adafactor(_MeoOptimizer):
         defaults = dict(lr=lr, eps=eps, clip_threshold=clip_threshold, decay_rate=decay_rate,
                         beta1=beta1, weight_decay=weight_decay, scale_parameter=scale_parameter,
                         relative_step=relative_step, warmup_init=warmup_init)
-        super().__init__(params, defaults, state_dtype)
+        super().__init__(params, defaults, state_dtype, min_8bit_size)
 
     def _state_for(self, p, group):
         return _lib.init_state("adafactor", p, beta1=group["beta1"] is not None,
@@ -144,12 +169,13 @@ class CAME(_MeoOptimizer):
     _HP = ("lr", "eps", "clip_threshold", "betas", "weight_decay")
 
     def __init__(self, params, lr=None, eps=(1e-30, 1e-16), clip_threshold=1.0,
-                 betas=(0.9, 0.999, 0.9999), weight_decay=0.0, state_dtype=None):
+                 betas=(0.9, 0.999, 0.9999), weight_decay=0.0, state_dtype=None,
+                 min_8bit_size=4096):
         if lr is None:
             raise ValueError("CAME requires an explicit lr")
         defaults = dict(lr=lr, eps=eps, clip_threshold=clip_threshold, betas=betas,
                         weight_decay=weight_decay)
-        super().__init__(params, defaults, state_dtype)
+        super().__init__(params, defaults, state_dtype, min_8bit_size)
 
     def _state_for(self, p, group):
         return _lib.init_state("came", p, state_dtype=self._moment_dtype(p))
@@ -172,7 +198,8 @@ class Lamb(_MeoOptimizer):
     _HP = ("lr", "betas", "eps", "weight_decay", "bias_correction")
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-6, weight_decay=0.0,
-                 bias_correction=True, state_dtype=None):
+                 bias_correction=True, state_dtype=None,
+                 min_8bit_size=4096):
         if not lr >= 0.0:
             raise ValueError(f"Invalid learning rate: {lr}")
         if not eps >= 0.0:
@@ -182,7 +209,7 @@ class Lamb(_MeoOptimizer):
                 raise ValueError(f"Invalid beta parameter at index {i}: {b}")
         defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay,
                         bias_correction=bias_correction)
-        super().__init__(params, defaults, state_dtype)
+        super().__init__(params, defaults, state_dtype, min_8bit_size)
 
     def _state_for(self, p, group):
         return _lib.init_state("lamb", p, state_dtype=self._moment_dtype(p))

@@ -31,6 +31,17 @@ statistics; a fp32 parameter stepped by a bf16 first moment), are judged by:
 
 A systematic fault (truncation instead of rounding to nearest, a wrong dtype, a
 mis-rounded tail) moves most elements and fails the second rule.
+
+8-bit first moment. The same near-tie disagreement can move an int8 code by one
+step (code = m / scale rounded, decided on each side's own m). Such a step is
+1/127 of its group's largest magnitude; it then decays with beta1 in later
+steps, but the group's scale may shrink meanwhile, so in codes it can span more
+than one step. The first moment is therefore judged on its dequantized values
+(code x scale), relative to its group's largest magnitude (127 x scale):
+* every value within 2e-2 of it (one code step is 0.79%); and
+* at most 1% (+4) of the codes differ.
+The scales (max |m| / 127 per group), the parameter and CAME's confidence
+statistics follow the 16-bit rules above.
 """
 from __future__ import annotations
 
@@ -42,7 +53,7 @@ import torch
 
 import oracle
 import workloads
-from memory_efficient_optimizers_amd import _lib
+from memory_efficient_optimizers_amd import _lib, moment_dtype
 
 TOL_F32 = 1e-5
 TOL_BF16 = 2e-2
@@ -80,24 +91,46 @@ def output_err(key: str, a, b) -> float:
     return floored_rel_err(a, b, 0.0 if key in POSITIVE_KEYS else 1.0)
 
 
-def storage_of(wl) -> dict:
-    return dict(param_bf16=wl.param_dtype == torch.bfloat16, exp_avg_bf16=wl.state_dtype == torch.bfloat16)
+def storage_of_tensor(param: torch.Tensor, state: Dict[str, torch.Tensor]) -> dict:
+    """The oracle's storage flags for one tensor, read from the library's buffers."""
+    m = state.get("exp_avg")
+    return dict(param_bf16=param.dtype == torch.bfloat16,
+                exp_avg_bf16=m is not None and m.dtype == torch.bfloat16,
+                exp_avg_i8=m is not None and m.dtype == torch.int8)
 
 
 def bar_kind(opt: str, hp: dict, storage: dict, key: str) -> str:
-    """"f32": held to 1e-5; "bf16": decided by a bf16 rounding (stored in bf16, or
-    computed from a bf16-stored first moment), held to the 16-bit rules above."""
-    pb, mb = storage.get("param_bf16", False), storage.get("exp_avg_bf16", False)
+    """"f32": held to 1e-5; "rounded": decided by a storage rounding (stored in
+    bf16, or computed from a bf16 or 8-bit first moment), held to the 16-bit rules
+    above; "codes": int8 codes of an 8-bit first moment."""
+    pb, mb, mi = (storage.get(k, False) for k in ("param_bf16", "exp_avg_bf16", "exp_avg_i8"))
     has_m = opt != "adafactor" or hp.get("beta1") is not None
     if key == "param":
-        return "bf16" if pb or (mb and has_m) else "f32"
-    if key in ("exp_avg", "exp_avg_res_row", "exp_avg_res_col"):
-        return "bf16" if mb else "f32"
+        return "rounded" if pb or ((mb or mi) and has_m) else "f32"
+    if key == "exp_avg":
+        return "codes" if mi else ("rounded" if mb else "f32")
+    if key == "exp_avg_scale":
+        return "rounded"
+    if key in ("exp_avg_res_row", "exp_avg_res_col"):
+        return "rounded" if mb or mi else "f32"
     return "f32"
 
 
 def judge(kind: str, key: str, a, b):
-    """(ok, max error, elements above 1e-5, elements) of one output under its bar."""
+    """(ok, max error, elements off the fp32 bar (or codes that differ), elements)
+    of one output under its bar. For "codes", a and b are (codes, scales) pairs."""
+    if kind == "codes":
+        (ca, sa), (cb, sb) = a, b
+        ca, cb = np.asarray(ca).reshape(-1), np.asarray(cb).reshape(-1)
+        da = oracle.dequantize_i8(ca, np.asarray(sa, dtype=np.float32))
+        db = oracle.dequantize_i8(cb, np.asarray(sb, dtype=np.float32))
+        amax = 127.0 * np.repeat(np.asarray(sb, dtype=np.float64), oracle.I8_GROUP)[:cb.size]
+        den = np.maximum(np.abs(db), amax)
+        den = np.where(den > 0, den, 1.0)
+        e = np.abs(da - db) / den
+        err = float(np.max(e)) if e.size else 0.0
+        over = int(np.count_nonzero(ca.astype(np.int64) != cb.astype(np.int64)))
+        return err <= TOL_BF16 and over <= MAX_SHARE * e.size + MAX_EXTRA, err, over, e.size
     e = output_errs(key, a, b)
     err = float(np.max(e)) if e.size else 0.0
     over = int(np.count_nonzero(e > TOL_F32))
@@ -119,9 +152,27 @@ def lib_hp(opt: str, hp: dict):
             "lamb": _lib.lamb_hparams}[opt](**hp)
 
 
-def lib_states(opt: str, params, hp: dict, state_dtype=torch.float32) -> List[Dict[str, torch.Tensor]]:
+def outputs(param: torch.Tensor, state: Dict[str, torch.Tensor], ox, ost) -> list:
+    """(key, library value, oracle value) of every output of one tensor; an 8-bit
+    first moment is one output made of its codes and scales."""
+    out = [("param", to64(param), ox)]
+    i8 = "exp_avg_scale" in ost
+    for key, ref in ost.items():
+        if key == "exp_avg" and i8:
+            out.append((key, (state[key].cpu().numpy(), state["exp_avg_scale"].cpu().numpy()),
+                        (ref, ost["exp_avg_scale"])))
+        else:
+            out.append((key, to64(state[key]), ref))
+    return out
+
+
+def lib_states(opt: str, params, hp: dict, state_dtype=torch.float32, min_8bit_size: int = 4096
+               ) -> List[Dict[str, torch.Tensor]]:
+    """Zero library states; an int8 request applies where moment_dtype allows it."""
     beta1 = hp.get("beta1") is not None
-    return [_lib.init_state(opt, p, beta1=beta1, state_dtype=state_dtype) for p in params]
+    return [_lib.init_state(opt, p, beta1=beta1,
+                            state_dtype=moment_dtype(opt, p.shape, state_dtype, p.dtype, min_8bit_size))
+            for p in params]
 
 
 def lib_step(opt, hp_struct, t, params, grads, states, ws, stream=None):
@@ -139,18 +190,19 @@ def lib_workspace(opt, params, grads):
 class Run:
     """The library and the oracle side by side over a workload."""
 
-    def __init__(self, wl: workloads.Workload, device="cuda", hp: dict = None):
+    def __init__(self, wl: workloads.Workload, device="cuda", hp: dict = None, min_8bit_size: int = 4096):
         self.wl = wl
         self.opt = wl.optimizer
         self.hp = dict(wl.hparams if hp is None else hp)
         self.device = device
         self.params = workloads.init_params(wl, device)
         self.scales = workloads.grad_scales(wl, device)
-        self.states = lib_states(self.opt, self.params, self.hp, wl.state_dtype)
-        self.storage = storage_of(wl)
+        self.states = lib_states(self.opt, self.params, self.hp, wl.state_dtype, min_8bit_size)
+        self.storage = [storage_of_tensor(p, st) for p, st in zip(self.params, self.states)]
         self.hps = lib_hp(self.opt, self.hp)
         self.ox = [to64(p) for p in self.params]
-        self.ost = [oracle.INIT_STATE[self.opt](tuple(p.shape), self.hp) for p in self.params]
+        self.ost = [oracle.INIT_STATE[self.opt](tuple(p.shape), self.hp, exp_avg_i8=s["exp_avg_i8"])
+                    for p, s in zip(self.params, self.storage)]
         self.ws = None
         self.t = 0
 
@@ -166,7 +218,9 @@ class Run:
         lib_step(self.opt, self.hps, self.t, self.params, grads, self.states, self.ws)
         if oracle_too:
             gs = [to64(g) for g in grads]
-            self.ox, self.ost = oracle.STEP[self.opt](self.ox, gs, self.ost, self.hp, self.t, **self.storage)
+            for k in range(len(gs)):
+                self.ox[k], self.ost[k] = oracle.STEP_TENSOR[self.opt](self.ox[k], gs[k], self.ost[k], self.hp,
+                                                                       self.t, **self.storage[k])
         return grads
 
     def verdicts(self) -> Dict[str, tuple]:
@@ -174,11 +228,9 @@ class Run:
         torch.cuda.synchronize()
         out = {}
         for k, spec in enumerate(self.wl.specs):
-            pairs = [("param", self.params[k], self.ox[k])]
-            pairs += [(key, self.states[k][key], arr) for key, arr in self.ost[k].items()]
-            for key, lib, ref in pairs:
-                kind = bar_kind(self.opt, self.hp, self.storage, key)
-                out[f"{spec.name}:{key}"] = judge(kind, key, to64(lib), ref) + (kind,)
+            for key, lib, ref in outputs(self.params[k], self.states[k], self.ox[k], self.ost[k]):
+                kind = bar_kind(self.opt, self.hp, self.storage[k], key)
+                out[f"{spec.name}:{key}"] = judge(kind, key, lib, ref) + (kind,)
         return out
 
     def errors(self) -> Dict[str, float]:
@@ -189,7 +241,7 @@ class Run:
         v = self.verdicts()
         bad = {k: x for k, x in v.items() if not x[0]}
         f32 = {k: x[1] for k, x in v.items() if x[4] == "f32"}
-        b16 = {k: x for k, x in v.items() if x[4] == "bf16"}
+        b16 = {k: x for k, x in v.items() if x[4] != "f32"}
         msg = f"  {self.wl.name} {label}"
         if f32:
             w = max(f32, key=f32.get)
@@ -197,7 +249,7 @@ class Run:
         if b16:
             w = max(b16, key=lambda k: b16[k][1])
             share = max(x[2] / max(x[3], 1) for x in b16.values())
-            msg += f"; bf16-decided worst {b16[w][1]:.3e} at {w}, max share above 1e-5 {share:.2e}"
+            msg += f"; storage-decided worst {b16[w][1]:.3e} at {w}, max share off {share:.2e}"
         print(msg, flush=True)
         assert not bad, f"{label}: " + ", ".join(
             f"{k} ({x[4]} bar): err {x[1]:.3e}, {x[2]}/{x[3]} above 1e-5" for k, x in bad.items())

@@ -120,7 +120,7 @@ def test_tensor_checks(lib):
     assert val(t) == _lib.MEO_EDTYPE
     assert "param_dtype" in _lib.meo_last_error()
     t[0].param_dtype = _lib.MEO_F32
-    t[0].state_dtype = 2
+    t[0].state_dtype = 7
     assert val(t) == _lib.MEO_EDTYPE
     assert "state_dtype" in _lib.meo_last_error()
     t[0].state_dtype = _lib.MEO_BF16
@@ -175,6 +175,40 @@ def test_first_moment_alignment_follows_its_dtype(lib):
         assert val() == _lib.MEO_OK, opt
         sts[0].exp_avg += 1
         assert val() == _lib.MEO_EALIGN, opt
+
+
+def test_eight_bit_first_moment_rules(lib):
+    """An 8-bit first moment needs its scales, and a factored tensor needs
+    cols % 128 == 0 (no quantization group crosses a row); 1-D and LAMB tensors
+    take any length. int8 codes need no alignment."""
+    for opt, keys, cls, hp in (("adafactor", _lib.ADAFACTOR_KEYS, _lib.meo_adafactor_state,
+                                _lib.adafactor_hparams(beta1=0.9)),
+                               ("came", _lib.CAME_KEYS, _lib.meo_came_state, _lib.came_hparams(lr=1e-3)),
+                               ("lamb", _lib.LAMB_KEYS, _lib.meo_lamb_state, _lib.lamb_hparams())):
+        fn = getattr(lib, f"meo_{opt}_validate")
+        for shape, ok in (((4, 256), True), ((4, 200), opt == "lamb"), ((300,), True), ((2, 3, 128), True)):
+            ps, gs = _mk([shape])
+            st = [_lib.init_state(opt, ps[0], beta1=True, state_dtype=torch.int8)]
+            assert st[0]["exp_avg"].dtype == torch.int8
+            assert st[0]["exp_avg_scale"].numel() == -(-ps[0].numel() // 128)
+            t = _lib._tensors(ps, gs, st)
+            assert t[0].state_dtype == _lib.MEO_I8
+            sts = _lib._states(cls, keys, st)
+            code = fn(_lib.ctypes.byref(hp), 1, 1, t, sts)
+            assert code == (_lib.MEO_OK if ok else _lib.MEO_ESHAPE), (opt, shape, code)
+            if ok:
+                sts[0].exp_avg += 1  # codes are bytes
+                assert fn(_lib.ctypes.byref(hp), 1, 1, t, sts) == _lib.MEO_OK
+                sts[0].exp_avg_scale = None
+                assert fn(_lib.ctypes.byref(hp), 1, 1, t, sts) == _lib.MEO_ENULL
+                assert "exp_avg_scale" in _lib.meo_last_error()
+    # no first moment (Adafactor without beta1): the dtype is not used
+    ps, gs = _mk([(4, 200)])
+    st = [_lib.init_state("adafactor", ps[0], beta1=False)]
+    t = _lib._tensors(ps, gs, st)
+    t[0].state_dtype = _lib.MEO_I8
+    sts = _lib._states(_lib.meo_adafactor_state, _lib.ADAFACTOR_KEYS, st)
+    assert lib.meo_adafactor_validate(_lib.ctypes.byref(_lib.adafactor_hparams()), 1, 1, t, sts) == _lib.MEO_OK
 
 
 def test_binding_rejects_mismatched_state_dtypes(lib):

@@ -15,8 +15,8 @@ import torch
 
 import oracle
 import workloads
-from tests.harness import (Run, bar_kind, judge, lib_hp, lib_states, lib_step, lib_workspace, storage_of,
-                           to64)
+from tests.harness import (Run, bar_kind, judge, lib_hp, lib_states, lib_step, lib_workspace, outputs,
+                           storage_of_tensor, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,8 @@ def test_adafactor_small_all_steps():
 
 
 @pytest.mark.parametrize("name", ["adafactor_llama_mini", "came_llama_mini", "lamb_bert_mini",
-                                  "adafactor_llama_mini_bf16", "came_llama_mini_bf16", "lamb_bert_mini_bf16"])
+                                  "adafactor_llama_mini_bf16", "came_llama_mini_bf16", "lamb_bert_mini_bf16",
+                                  "adafactor_llama_mini_i8", "came_llama_mini_i8", "lamb_bert_mini_i8"])
 def test_scaled_down_workloads_chained(name):
     wl = workloads.WORKLOADS[name]
     _chain(wl, wl.steps, check_every=3)
@@ -118,7 +119,7 @@ def test_resume_at_step_40000():
 # ----------------------------------------------------------------------------- invariants of the library
 
 @pytest.mark.parametrize("name", ["adafactor_llama_mini", "came_llama_mini", "lamb_bert_mini",
-                                  "came_llama_mini_bf16"])
+                                  "came_llama_mini_bf16", "came_llama_mini_i8"])
 def test_bitwise_deterministic_and_list_independent(name):
     """Two runs give identical bits, and a step over the list gives the same bits
     as a step over each tensor alone."""
@@ -168,7 +169,8 @@ def test_optimizer_classes_match_binding():
 
 # ----------------------------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("name", ["adafactor_llama_layer", "came_llama_layer", "adafactor_llama_layer_bf16"])
+@pytest.mark.parametrize("name", ["adafactor_llama_layer", "came_llama_layer", "adafactor_llama_layer_bf16",
+                                  "adafactor_llama_layer_i8"])
 def test_full_llama_layer(name):
     """One Llama-7B decoder layer (202M parameters, bf16 grads), 2 chained steps,
     every element of every tensor against the oracle."""
@@ -185,9 +187,10 @@ def _sampled_full(wl, sample_idx, steps):
     sts = lib_states(opt, ps, hp, wl.state_dtype)
     hps = lib_hp(opt, hp)
     scales = workloads.grad_scales(wl, dev)
-    storage = storage_of(wl)
+    storage = {k: storage_of_tensor(ps[k], sts[k]) for k in sample_idx}
     ox = {k: to64(ps[k]) for k in sample_idx}
-    ost = {k: oracle.INIT_STATE[opt](tuple(ps[k].shape), hp) for k in sample_idx}
+    ost = {k: oracle.INIT_STATE[opt](tuple(ps[k].shape), hp, exp_avg_i8=storage[k]["exp_avg_i8"])
+           for k in sample_idx}
     ws = None
     for t in range(1, steps + 1):
         gs = workloads.grads(wl, t - 1, scales, dev)
@@ -196,9 +199,9 @@ def _sampled_full(wl, sample_idx, steps):
         lib_step(opt, hps, t, ps, gs, sts, ws)
         torch.cuda.synchronize()
         for k in sample_idx:
-            ox[k], ost[k] = oracle.STEP_TENSOR[opt](ox[k], to64(gs[k]), ost[k], hp, t, **storage)
-            outs = [("param", ps[k], ox[k])] + [(key, sts[k][key], arr) for key, arr in ost[k].items()]
-            res = {key: judge(bar_kind(opt, hp, storage, key), key, to64(lib), ref) for key, lib, ref in outs}
+            ox[k], ost[k] = oracle.STEP_TENSOR[opt](ox[k], to64(gs[k]), ost[k], hp, t, **storage[k])
+            res = {key: judge(bar_kind(opt, hp, storage[k], key), key, lib, ref)
+                   for key, lib, ref in outputs(ps[k], sts[k], ox[k], ost[k])}
             worst = max(res, key=lambda key: res[key][1])
             print(f"  {wl.name} step {t} {wl.specs[k].name}: worst {res[worst][1]:.3e} ({worst})", flush=True)
             bad = {key: r for key, r in res.items() if not r[0]}
@@ -206,7 +209,7 @@ def _sampled_full(wl, sample_idx, steps):
         del gs
 
 
-@pytest.mark.parametrize("name", ["adafactor_llama7b", "adafactor_llama7b_bf16"])
+@pytest.mark.parametrize("name", ["adafactor_llama7b", "adafactor_llama7b_bf16", "adafactor_llama7b_i8"])
 def test_full_llama7b_sampled(name):
     """The 7B list (291 tensors, 6.74e9 parameters) in one call per step, with fp32
     and with bf16 parameter and first-moment storage. Step 1: the embedding, the
@@ -251,17 +254,21 @@ def test_edge_shapes_bf16_storage(opt, hp):
                                     ("lamb", {"weight_decay": 0.01})])
 def test_mixed_storage_list(opt, hp):
     """One call over a list mixing every storage combination (fp32/bf16 parameter x
-    fp32/bf16 first moment): each tensor matches the oracle under its own storage."""
-    shapes = [(64, 520), (130, 256), (300,), (3, 40, 96)]
+    fp32/bf16/8-bit first moment): each tensor matches the oracle under its own
+    storage."""
+    shapes = [(64, 520), (130, 256), (300,), (3, 40, 96), (64, 512), (700,)]
     combos = [(torch.float32, torch.float32), (torch.bfloat16, torch.bfloat16),
-              (torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16)]
+              (torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16),
+              (torch.float32, torch.int8), (torch.bfloat16, torch.int8)]
     wl = workloads.custom(f"mixed_{opt}", opt, shapes, hparams=hp, grad_dtype=torch.bfloat16)
     scales = workloads.grad_scales(wl, "cuda")
     ps = [p.to(pd) for p, (pd, _) in zip(workloads.init_params(wl, "cuda"), combos)]
-    sts = [lib_states(opt, [p], hp, sd)[0] for p, (_, sd) in zip(ps, combos)]
+    sts = [lib_states(opt, [p], hp, sd, min_8bit_size=0)[0] for p, (_, sd) in zip(ps, combos)]
+    storage = [storage_of_tensor(p, st) for p, st in zip(ps, sts)]
+    assert storage[4]["exp_avg_i8"] and storage[5]["exp_avg_i8"]
     hps = lib_hp(opt, hp)
     ox = [to64(p) for p in ps]
-    ost = [oracle.INIT_STATE[opt](tuple(p.shape), hp) for p in ps]
+    ost = [oracle.INIT_STATE[opt](tuple(p.shape), hp, exp_avg_i8=st["exp_avg_i8"]) for p, st in zip(ps, storage)]
     ws = None
     for t in range(1, 4):
         gs = workloads.grads(wl, t - 1, scales, "cuda")
@@ -269,10 +276,35 @@ def test_mixed_storage_list(opt, hp):
             ws = lib_workspace(opt, ps, gs)
         lib_step(opt, hps, t, ps, gs, sts, ws)
         torch.cuda.synchronize()
-        for k, (pd, sd) in enumerate(combos):
-            storage = dict(param_bf16=pd == torch.bfloat16, exp_avg_bf16=sd == torch.bfloat16)
-            ox[k], ost[k] = oracle.STEP_TENSOR[opt](ox[k], to64(gs[k]), ost[k], hp, t, **storage)
-            outs = [("param", ps[k], ox[k])] + [(key, sts[k][key], arr) for key, arr in ost[k].items()]
-            for key, lib, ref in outs:
-                ok, err, over, n = judge(bar_kind(opt, hp, storage, key), key, to64(lib), ref)
+        for k in range(len(ps)):
+            ox[k], ost[k] = oracle.STEP_TENSOR[opt](ox[k], to64(gs[k]), ost[k], hp, t, **storage[k])
+            for key, lib, ref in outputs(ps[k], sts[k], ox[k], ost[k]):
+                ok, err, over, n = judge(bar_kind(opt, hp, storage[k], key), key, lib, ref)
                 assert ok, (t, k, key, err, over, n)
+
+
+# ----------------------------------------------------------------------------- 8-bit first moment
+
+# Shapes for the 8-bit first moment: factored ones need cols % 128 == 0 (row-complete
+# 1024 and 512 wide, batched, a ragged column tile of 640 = 512 + 128, the tiled
+# 16384-wide path); 1-D ones of any length (ragged last group).
+I8_SHAPES = [(129, 1024), (4, 384), (2, 3, 64, 256), (65, 640), (3, 16384), (5000,), (40000,), (3,), (300,)]
+
+
+@pytest.mark.parametrize("opt,hp", [
+    ("adafactor", {"beta1": 0.9, "weight_decay": 0.1}),
+    ("adafactor", {"beta1": 0.5, "scale_parameter": False, "clip_threshold": 0.3}),
+    ("came", {"lr": 1e-3, "weight_decay": 0.05}),
+    ("lamb", {"lr": 1e-3, "weight_decay": 0.01}),
+])
+@pytest.mark.parametrize("pdt", [torch.float32, torch.bfloat16])
+def test_i8_moment_shapes(opt, hp, pdt):
+    """The 8-bit first moment on every tile path (row-complete, tiled, flat with a
+    ragged last group), with fp32 and bf16 parameters, 3 chained steps."""
+    wl = workloads.custom(f"i8_{opt}", opt, I8_SHAPES, hparams=hp, grad_dtype=torch.bfloat16, steps=3,
+                          param_dtype=pdt, state_dtype=torch.int8)
+    run = Run(wl, min_8bit_size=0)
+    assert all(s["exp_avg_i8"] for s in run.storage)
+    for s in range(3):
+        run.step()
+        run.check(f"step {s + 1}")

@@ -23,12 +23,18 @@ def _one_step_up(a):
 def test_bar_kinds():
     st = dict(param_bf16=False, exp_avg_bf16=True)
     assert bar_kind("adafactor", {}, st, "param") == "f32"                 # no first moment
-    assert bar_kind("adafactor", {"beta1": 0.9}, st, "param") == "bf16"    # stepped by a bf16 moment
-    assert bar_kind("came", {}, st, "exp_avg_res_row") == "bf16"
+    assert bar_kind("adafactor", {"beta1": 0.9}, st, "param") == "rounded"    # stepped by a bf16 moment
+    assert bar_kind("came", {}, st, "exp_avg_res_row") == "rounded"
     assert bar_kind("came", {}, st, "exp_avg_sq_col") == "f32"             # depends on G only
     assert bar_kind("lamb", {}, st, "exp_avg_sq") == "f32"
-    assert bar_kind("lamb", {}, dict(param_bf16=True), "param") == "bf16"
+    assert bar_kind("lamb", {}, dict(param_bf16=True), "param") == "rounded"
     assert bar_kind("lamb", {}, dict(param_bf16=True), "exp_avg") == "f32"
+    i8 = dict(exp_avg_i8=True)
+    assert bar_kind("lamb", {}, i8, "exp_avg") == "codes"
+    assert bar_kind("lamb", {}, i8, "exp_avg_scale") == "rounded"
+    assert bar_kind("adafactor", {"beta1": 0.9}, i8, "param") == "rounded"
+    assert bar_kind("came", {}, i8, "exp_avg_res_col") == "rounded"
+    assert bar_kind("came", {}, i8, "exp_avg_sq_row") == "f32"
 
 
 def test_sixteen_bit_rules():
@@ -39,19 +45,40 @@ def test_sixteen_bit_rules():
     lib = ref.copy()
     idx = rng.choice(lib.size, 60, replace=False)
     lib[idx] = _one_step_up(lib[idx])
-    ok, err, over, n = judge("bf16", "exp_avg", lib, ref)
+    ok, err, over, n = judge("rounded", "exp_avg", lib, ref)
     assert ok and over == 60 and err <= 2.0 ** -7
     # the same disagreements fail the fp32 bar
     assert not judge("f32", "exp_avg", lib, ref)[0]
     # truncation instead of round-to-nearest moves about half the elements
-    ok, err, over, n = judge("bf16", "exp_avg", _bits_down(exact), ref)
+    ok, err, over, n = judge("rounded", "exp_avg", _bits_down(exact), ref)
     assert not ok and over > 0.3 * n
     # a skipped rounding (fp32 values stored) moves nearly all of them
-    assert not judge("bf16", "exp_avg", exact.astype(np.float32).astype(np.float64), ref)[0]
+    assert not judge("rounded", "exp_avg", exact.astype(np.float32).astype(np.float64), ref)[0]
     # garbage in a ragged tail of 7 elements breaks the elementwise bound
     lib = ref.copy()
     lib[-7:] = 0.0
-    assert not judge("bf16", "exp_avg", lib, ref)[0]
+    assert not judge("rounded", "exp_avg", lib, ref)[0]
     # an exact match passes both bars
     assert judge("f32", "param", ref, ref)[:2] == (True, 0.0)
     assert TOL_F32 == 1e-5
+
+
+def test_code_rules():
+    """8-bit first moment, judged on code x scale against its group's largest
+    magnitude: scattered one- and two-step disagreements pass; a value off by 3
+    steps, a systematic shift of many codes, or a wrong scale fails."""
+    rng = np.random.default_rng(6)
+    m = rng.normal(size=128 * 400) * 10.0 ** np.repeat(rng.uniform(-3, 1, 400), 128)
+    codes, scales = oracle.quantize_i8(m)
+    ref = (codes, scales)
+    lib = codes.astype(np.int16)
+    idx = rng.choice(lib.size, 100, replace=False)
+    lib[idx] = np.clip(lib[idx] + 1, -127, 127)
+    lib[idx[:3]] = np.clip(lib[idx[:3]] + 1, -127, 127)   # three values two steps off
+    ok, err, over, n = judge("codes", "exp_avg", (lib.astype(np.int8), scales), ref)
+    assert ok and err <= 2.5 / 127 and over <= 100
+    lib[idx[0]] = np.clip(codes[idx[0]] + 3, -127, 127)
+    assert not judge("codes", "exp_avg", (lib.astype(np.int8), scales), ref)[0]
+    shifted = np.clip(codes.astype(np.int16) + (rng.random(codes.size) < 0.2), -127, 127).astype(np.int8)
+    assert not judge("codes", "exp_avg", (shifted, scales), ref)[0]
+    assert not judge("codes", "exp_avg", (codes, scales * np.float32(1.03)), ref)[0]

@@ -49,7 +49,8 @@ class Workload:
     steps: int
     seed: int = 0
     param_dtype: torch.dtype = torch.float32   # storage of the parameter
-    state_dtype: torch.dtype = torch.float32   # storage of the first moment (exp_avg)
+    state_dtype: torch.dtype = torch.float32   # storage of the first moment (exp_avg); int8 applies
+                                               # where the optimizer's 8-bit rule allows it
 
     @property
     def numel(self) -> int:
@@ -154,6 +155,12 @@ _register(dataclasses.replace(WORKLOADS["adafactor_llama7b"], name="adafactor_ll
                               param_dtype=torch.bfloat16, state_dtype=torch.bfloat16))
 _register(dataclasses.replace(WORKLOADS["adafactor_llama_layer"], name="adafactor_llama_layer_bf16",
                               param_dtype=torch.bfloat16, state_dtype=torch.bfloat16))
+# 8-bit first moment (fp32 parameters and statistics).
+_register(dataclasses.replace(WORKLOADS["adafactor_llama7b"], name="adafactor_llama7b_i8", state_dtype=torch.int8))
+_register(dataclasses.replace(WORKLOADS["adafactor_llama_layer"], name="adafactor_llama_layer_i8",
+                              state_dtype=torch.int8))
+_register(dataclasses.replace(WORKLOADS["came_llama_layer"], name="came_llama_layer_i8", state_dtype=torch.int8))
+_register(dataclasses.replace(WORKLOADS["lamb_bert_large"], name="lamb_bert_large_i8", state_dtype=torch.int8))
 
 # Scaled-down versions of the same structure (ragged widths included) that the
 # oracle runs element by element in seconds.
@@ -167,10 +174,11 @@ _register(_wl("lamb_bert_mini", "lamb", _LAMB,
               bert_specs(layers=2, hidden=128, ffn=512, vocab=3001, max_pos=64),
               torch.float32, 1e-2, "none", 10))
 
-# Scaled-down 16-bit-storage versions.
+# Scaled-down 16-bit-storage and 8-bit-moment versions.
 for _n in ("adafactor_llama_mini", "came_llama_mini", "lamb_bert_mini"):
     _register(dataclasses.replace(WORKLOADS[_n], name=_n + "_bf16", param_dtype=torch.bfloat16,
                                   state_dtype=torch.bfloat16))
+    _register(dataclasses.replace(WORKLOADS[_n], name=_n + "_i8", state_dtype=torch.int8))
 del _n
 
 
