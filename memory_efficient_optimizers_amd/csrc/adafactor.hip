@@ -119,6 +119,7 @@ __device__ __forceinline__ void af_rows(const TDesc& d, int lt, float coef, floa
 template <int ST>
 __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
     const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;  // an empty item of an XCD-aligned list
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
     const float* ws = t.ws;

@@ -21,6 +21,7 @@ template <int ST>
 __global__ __launch_bounds__(kThreads) void k_came_mom(Table t, CameArgs a) {
     __shared__ __align__(16) float lds[kWaves * kTileCols];
     const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;  // an empty item of an XCD-aligned list
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
     float* ws = t.ws;
@@ -125,6 +126,7 @@ void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, int storage, 
 template <int ST>
 __global__ __launch_bounds__(kThreads) void k_came_apply(Table t) {
     const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;  // an empty item of an XCD-aligned list
     const TDesc d = t.desc[it.x];
     if (d.mode == kFlat) return;  // 1-D tensors were finished by k_came_mom
     const int lt = it.y;

@@ -99,7 +99,8 @@ struct TDesc {
 struct Table {
     const TDesc* desc;
     const int2* items;  // [grid] x = tensor index, y = tile (or finalize item) within the tensor;
-                        // in the row-complete first pass y < 0 marks chunk -1 - y of sum(X^2)
+                        // in the row-complete first pass y < 0 marks chunk -1 - y of sum(X^2);
+                        // x < 0: an empty item (padding of an XCD-aligned streaming list)
     float* ws;          // workspace base
 };
 

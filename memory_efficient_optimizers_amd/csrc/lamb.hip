@@ -22,6 +22,7 @@ template <int ST>
 __global__ __launch_bounds__(kThreads) void k_lamb_moments(Table t, LambArgs a) {
     __shared__ float lds[2 * kWaves];
     const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;  // an empty item of an XCD-aligned list
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
     const bool vec = d.vec, bf = d.gbf16, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d), mi = m_is_i8<ST>(d);
@@ -77,6 +78,7 @@ void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, int stora
 template <int ST>
 __global__ __launch_bounds__(kThreads) void k_lamb_apply(Table t, LambArgs a) {
     const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;  // an empty item of an XCD-aligned list
     const TDesc d = t.desc[it.x];
     const int lt = it.y;
     const bool vec = d.vec, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d), mi = m_is_i8<ST>(d);
