@@ -252,6 +252,72 @@ int    meo_lamb_step(const meo_lamb_hparams* hp, int64_t step, int32_t n,
                      const meo_tensor* tensors, const meo_lamb_state* states,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------- row-sharded steps */
+
+/*
+ * One rank's share of a step whose tensors are split by rows across ranks, the
+ * layout of the page's tensor-parallel and ZeRO versions ([CAI] "Step 4":
+ * setup_distributed; row statistics reduced within the group, column statistics
+ * gathered). Each rank holds whole rows of every factored tensor (rows
+ * [r0, r0 + rows) of dim -2, all columns) and a contiguous element range of every
+ * 1-D tensor (LAMB: of every tensor). A factored tensor stays factored whatever its
+ * share: a shard of one row is still one row of a factored matrix (the page makes
+ * CAME's H = 1 shards factored for the same reason).
+ *
+ * A step is three stages:
+ *   1. meo_*_shard_stats: the shard's own statistics (Adafactor: its row statistic
+ *      and, for 1-D tensors, its full second moment; LAMB: its moments) plus a
+ *      record of partial sums in `partials`;
+ *   2. the caller sums `partials` over all ranks (an all-reduce with SUM of one flat
+ *      float32 buffer, e.g. RCCL over xGMI); the library does no communication;
+ *   3. meo_*_shard_apply with the reduced `partials`: the replicated statistics
+ *      (Adafactor's column statistic, kept whole on every rank and updated
+ *      identically), the per-tensor scalars and the update of the shard.
+ * The same hparams, step, tensors, shards and states go to both calls.
+ *
+ * `partials` (float32, meo_*_partials_size() floats, contiguous; every entry is a
+ * sum, so summing the ranks' buffers gives the whole tensor's values), per tensor
+ * in list order:
+ *   Adafactor, factored: [B][W] sum of G^2 + eps1 over the shard's rows, [B][W] sum
+ *     of G^2 / R_i (R_i the new row statistic), [B] sum of the new R_i, [1] sum of
+ *     X^2 of the shard;
+ *   Adafactor, 1-D: [1] sum of U^2 = G^2 / V, [1] sum of X^2;
+ *   LAMB: [1] sum of X^2, [1] sum of d^2 (the update direction).
+ * Every tensor has its record, also where the rank holds none of it (rows = 0 or
+ * an empty range): the stats call writes zeros there, so all ranks' buffers line
+ * up; such a rank neither uses nor updates that tensor's column statistic.
+ * Factored Adafactor shards need row-complete rows (cols % 8 == 0, cols <= 12288,
+ * param and grad 16-byte aligned; MEO_ESHAPE otherwise). The workspace is scratch
+ * for each call; nothing in it is carried from the stats call to the apply call.
+ * Errors as for the whole-tensor step, plus MEO_ENULL for NULL shards or partials,
+ * MEO_ESHAPE for rows_total below the shard's size, and MEO_EMEMORY when partials
+ * is not device memory of the record's size.
+ */
+typedef struct meo_shard {
+    int64_t rows_total;  /* rows of the whole matrix (dim -2) for a factored tensor;
+                            elements of the whole tensor for a 1-D one (LAMB: for
+                            every tensor); >= the shard's own                       */
+} meo_shard;
+
+size_t meo_adafactor_partials_size(int32_t n, const meo_tensor* tensors);
+int    meo_adafactor_shard_stats(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
+                                 const meo_tensor* tensors, const meo_shard* shards,
+                                 const meo_adafactor_state* states, float* partials,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+int    meo_adafactor_shard_apply(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
+                                 const meo_tensor* tensors, const meo_shard* shards,
+                                 const meo_adafactor_state* states, const float* partials,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+size_t meo_lamb_partials_size(int32_t n, const meo_tensor* tensors);
+int    meo_lamb_shard_stats(const meo_lamb_hparams* hp, int64_t step, int32_t n,
+                            const meo_tensor* tensors, const meo_shard* shards,
+                            const meo_lamb_state* states, float* partials,
+                            void* workspace, size_t workspace_bytes, void* stream);
+int    meo_lamb_shard_apply(const meo_lamb_hparams* hp, int64_t step, int32_t n,
+                            const meo_tensor* tensors, const meo_shard* shards,
+                            const meo_lamb_state* states, const float* partials,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ----------------------------------------------------------------- utilities */
 
 /* Message of the last failing call on this thread ("" if none). The pointer

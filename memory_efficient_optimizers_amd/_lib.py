@@ -35,6 +35,8 @@ EXPORTS = [
     "meo_came_step", "meo_lamb_defaults", "meo_lamb_workspace_size", "meo_lamb_validate",
     "meo_lamb_step", "meo_last_error", "meo_release_plans", "meo_version", "meo_profile_enable",
     "meo_pass_name", "meo_profile_collect",
+    "meo_adafactor_partials_size", "meo_adafactor_shard_stats", "meo_adafactor_shard_apply",
+    "meo_lamb_partials_size", "meo_lamb_shard_stats", "meo_lamb_shard_apply",
 ]
 MEO_NUM_PASSES = 11
 
@@ -50,6 +52,10 @@ class meo_tensor(ctypes.Structure):
     _fields_ = [("param", c_void_p), ("grad", c_void_p), ("batch", c_int64), ("rows", c_int64),
                 ("cols", c_int64), ("ndim", c_int32), ("param_dtype", c_int32),
                 ("grad_dtype", c_int32), ("state_dtype", c_int32)]
+
+
+class meo_shard(ctypes.Structure):
+    _fields_ = [("rows_total", c_int64)]
 
 
 class meo_adafactor_hparams(ctypes.Structure):
@@ -113,6 +119,16 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         getattr(lib, f"meo_{opt}_step").argtypes = [ctypes.POINTER(hp), c_int64, c_int32, T,
                                                     ctypes.POINTER(st), c_void_p, c_size_t, c_void_p]
         getattr(lib, f"meo_{opt}_step").restype = ctypes.c_int
+    S = ctypes.POINTER(meo_shard)
+    for opt, hp, st in (("adafactor", meo_adafactor_hparams, meo_adafactor_state),
+                        ("lamb", meo_lamb_hparams, meo_lamb_state)):
+        getattr(lib, f"meo_{opt}_partials_size").argtypes = [c_int32, T]
+        getattr(lib, f"meo_{opt}_partials_size").restype = c_size_t
+        for stage in ("stats", "apply"):
+            fn = getattr(lib, f"meo_{opt}_shard_{stage}")
+            fn.argtypes = [ctypes.POINTER(hp), c_int64, c_int32, T, S, ctypes.POINTER(st), c_void_p, c_void_p,
+                           c_size_t, c_void_p]
+            fn.restype = ctypes.c_int
     lib.meo_last_error.argtypes = []
     lib.meo_last_error.restype = ctypes.c_char_p
     lib.meo_release_plans.argtypes = []
@@ -303,6 +319,51 @@ def meo_lamb_step(hp, step, params, grads, states, workspace=None, stream=None) 
     ws, nb = _ws(workspace)
     _check(load().meo_lamb_step(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
                                 _states(meo_lamb_state, LAMB_KEYS, states), ws, nb, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- row-sharded steps
+
+def _shards(totals: Sequence[int]):
+    arr = (meo_shard * max(len(totals), 1))()
+    for i, t in enumerate(totals):
+        arr[i] = meo_shard(int(t))
+    return arr
+
+
+def meo_adafactor_partials_size(params, grads) -> int:
+    """Floats of the partial-sum record of a row-sharded Adafactor step."""
+    return int(load().meo_adafactor_partials_size(len(params), _tensors(params, grads)))
+
+
+def meo_lamb_partials_size(params, grads) -> int:
+    return int(load().meo_lamb_partials_size(len(params), _tensors(params, grads)))
+
+
+def _shard_call(opt, stage, hp, step, params, grads, totals, states, partials, workspace, stream):
+    cls, keys = {"adafactor": (meo_adafactor_state, ADAFACTOR_KEYS), "lamb": (meo_lamb_state, LAMB_KEYS)}[opt]
+    ws, nb = _ws(workspace)
+    _check(getattr(load(), f"meo_{opt}_shard_{stage}")(
+        ctypes.byref(hp), step, len(params), _tensors(params, grads, states), _shards(totals),
+        _states(cls, keys, states), _ptr(partials), ws, nb, _stream(stream)))
+
+
+def meo_adafactor_shard_stats(hp, step, params, grads, totals, states, partials, workspace=None, stream=None):
+    """Stage 1 of a row-sharded step: the shard's statistics and its partial sums
+    (``totals[k]``: rows of the whole matrix, or elements of a whole 1-D tensor)."""
+    _shard_call("adafactor", "stats", hp, step, params, grads, totals, states, partials, workspace, stream)
+
+
+def meo_adafactor_shard_apply(hp, step, params, grads, totals, states, partials, workspace=None, stream=None):
+    """Stage 3: the update of the shard from the partial sums reduced over all ranks."""
+    _shard_call("adafactor", "apply", hp, step, params, grads, totals, states, partials, workspace, stream)
+
+
+def meo_lamb_shard_stats(hp, step, params, grads, totals, states, partials, workspace=None, stream=None):
+    _shard_call("lamb", "stats", hp, step, params, grads, totals, states, partials, workspace, stream)
+
+
+def meo_lamb_shard_apply(hp, step, params, grads, totals, states, partials, workspace=None, stream=None):
+    _shard_call("lamb", "apply", hp, step, params, grads, totals, states, partials, workspace, stream)
 
 
 def meo_last_error() -> str:

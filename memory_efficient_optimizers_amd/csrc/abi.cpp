@@ -275,6 +275,23 @@ int check_lamb_hp(const meo_lamb_hparams* hp) {
     return MEO_OK;
 }
 
+// Offsets (floats) of each tensor's record of partial sums in a row-sharded step,
+// and the total; the layout is the one meo.h documents.
+int64_t partials_layout(int op, int32_t n, const meo_tensor* ts, std::vector<int64_t>* offs) {
+    int64_t off = 0;
+    if (offs) offs->assign(n, 0);
+    for (int32_t k = 0; k < n; ++k) {
+        int64_t numel = 0;
+        overflow_numel(ts[k], &numel);
+        if (offs) (*offs)[k] = off;
+        // Every tensor has its record, also where this rank holds none of it, so that
+        // the ranks' buffers line up for the all-reduce.
+        if (is_factored(op, ts[k])) off += ts[k].batch * (2 * ts[k].cols + 1) + 1;
+        else off += 2;
+    }
+    return off;
+}
+
 // Whether [p, p + bytes) lies in one allocation of device memory of device `dev`
 // that the HIP runtime knows (hipMalloc, hipMallocManaged, allocators built on
 // them). Catches host, truncated or stale pointers and ranges described past the
@@ -355,7 +372,8 @@ int check_tensor_memory(int op, int32_t n, const meo_tensor* ts, const StatePtrs
 // ----------------------------------------------------------------------------- plan cache
 
 // Item tables of the launches of one call.
-enum List { kListRc0 = 0, kListRc1, kListTiled, kListAll, kListFin1, kListFin2, kListCount };
+enum List { kListRc0 = 0, kListRc1, kListTiled, kListAll, kListFin1, kListFin2, kListShard, kListFold, kListEmpty,
+            kListCount };
 
 struct Plan {
     std::vector<uint8_t> key;
@@ -431,19 +449,23 @@ void xcd_order(std::vector<int2>& items, const std::vector<TDesc>& desc) {
 
 // Builds (or finds) the launch table for this list. Returns nullptr with g_err set
 // on a HIP failure.
-Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int has_m, int* rc) {
+// `shards` (row-sharded steps; else null): the whole tensors' sizes, part of the key.
+Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int has_m, int* rc,
+               const meo_shard* shards = nullptr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
         *rc = fail(MEO_EHIP, "hipGetDevice failed");
         return nullptr;
     }
-    std::vector<uint8_t> key(sizeof(int) * 4 + n * (sizeof(meo_tensor) + sizeof(StatePtrs)));
+    const size_t nsh = shards ? n * sizeof(meo_shard) : 0;
+    std::vector<uint8_t> key(sizeof(int) * 5 + n * (sizeof(meo_tensor) + sizeof(StatePtrs)) + nsh);
     {
         uint8_t* w = key.data();
-        const int hdr[4] = {op, n, dev, has_m};
+        const int hdr[5] = {op, n, dev, has_m, shards ? 1 : 0};
         std::memcpy(w, hdr, sizeof hdr); w += sizeof hdr;
         std::memcpy(w, ts, n * sizeof(meo_tensor)); w += n * sizeof(meo_tensor);
-        std::memcpy(w, sp, n * sizeof(StatePtrs));
+        std::memcpy(w, sp, n * sizeof(StatePtrs)); w += n * sizeof(StatePtrs);
+        if (nsh) std::memcpy(w, shards, nsh);
     }
     std::lock_guard<std::mutex> lock(g_mu);
     for (auto it = g_plans.begin(); it != g_plans.end(); ++it) {
@@ -458,11 +480,19 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
     if (*rc) return nullptr;
     std::vector<Geo> geo;
     layout(op, n, ts, &geo);
+    std::vector<int64_t> poff;
+    if (shards) partials_layout(op, n, ts, &poff);
     std::vector<TDesc> desc;
     std::vector<int2> lists[kListCount];
     for (int32_t k = 0; k < n; ++k) {
         const Geo& g = geo[k];
-        if (g.numel == 0) continue;
+        if (g.numel == 0) {
+            if (shards) {  // a rank with none of the tensor contributes zeros
+                const int64_t len = (k + 1 < n ? poff[k + 1] : partials_layout(op, n, ts, nullptr)) - poff[k];
+                lists[kListEmpty].push_back(make_int2(static_cast<int>(poff[k]), static_cast<int>(len)));
+            }
+            continue;
+        }
         const int32_t id = static_cast<int32_t>(desc.size());
         TDesc d;
         std::memset(&d, 0, sizeof d);
@@ -487,10 +517,19 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
         d.vec = vec;
         d.tr = g.tr; d.tc = g.tc; d.strips = g.strips;
         d.nrc = g.nrc; d.ncc = g.ncc;
+        if (shards) {
+            d.part = poff[k];
+            d.total = shards[k].rows_total;
+        }
         desc.push_back(d);
         auto add = [&](int list, int64_t count) {
             for (int64_t i = 0; i < count; ++i) lists[list].push_back(make_int2(id, static_cast<int>(i)));
         };
+        if (shards) {  // the record of partial sums, and (factored) its fold
+            const int64_t per = g.mode == kFlat ? 1 : static_cast<int64_t>(g.B) * ceil_div(g.W, kThreads);
+            add(kListShard, per);
+            if (g.mode != kFlat) add(kListFold, per);
+        }
         if (g.mode == kFlat) {
             add(kListAll, g.tiles);
             if (op != kOpLamb) add(kListRc0, g.tiles);
@@ -766,7 +805,7 @@ int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
         launch_rms(tab(kListTiled), p->count[kListTiled], need_x, s);
         pt.mark(kPassRms);
     }
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, rho, hp->eps2,
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, nullptr, rho, hp->eps2,
                                               hp->clip_threshold, hp->weight_decay, 0.0}, s);
     pt.mark(kPassScalars);
     launch_af_apply(tab(kListAll), p->count[kListAll],
@@ -847,7 +886,7 @@ int meo_came_step(const meo_came_hparams* hp, int64_t step, int32_t n, const meo
         launch_rms(tab(kListTiled), p->count[kListTiled], 0, s);
         pt.mark(kPassRms);
     }
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame1, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame1, 0, nullptr, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
                                               hp->lr}, s);
     pt.mark(kPassScalars);
     launch_came_mom(tab(kListAll), p->count[kListAll],
@@ -857,7 +896,7 @@ int meo_came_step(const meo_came_hparams* hp, int64_t step, int32_t n, const meo
     pt.mark(kPassCameMom);
     launch_finalize(tab(kListFin2), p->count[kListFin2], FinArgs{hp->beta3, 1, 1}, s);
     pt.mark(kPassFinalize);
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame2, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame2, 0, nullptr, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
                                               hp->lr}, s);
     pt.mark(kPassScalars);
     launch_came_apply(tab(kListAll), p->count[kListAll], p->storage, s);
@@ -923,11 +962,197 @@ int meo_lamb_step(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo
     PassTimer pt(s);
     launch_lamb_moments(t, tiles, la, p->storage, s);
     pt.mark(kPassLambMoments);
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalLamb, 0, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalLamb, 0, nullptr, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
     pt.mark(kPassScalars);
     launch_lamb_apply(t, tiles, la, p->storage, s);
     pt.mark(kPassLambApply);
     return launch_status("lamb step launch");
+}
+
+
+// ----------------------------------------------------------------------------- row-sharded steps
+
+namespace {
+
+// The shard sizes and the partial-sum buffer: factored shards need row-complete
+// rows (the single exchange rests on whole rows), the whole tensor is at least the
+// shard, and the buffer is device memory of the record's size.
+int check_shards(int op, int32_t n, const meo_tensor* ts, const meo_shard* sh, const void* partials) {
+    if (n == 0) return MEO_OK;
+    if (!sh) return fail(MEO_ENULL, "shards is NULL");
+    if (!partials) return fail(MEO_ENULL, "partials is NULL");
+    if (reinterpret_cast<uintptr_t>(partials) % 4) return fail(MEO_EALIGN, "partials not 4-byte aligned");
+    for (int32_t k = 0; k < n; ++k) {
+        const meo_tensor& t = ts[k];
+        int64_t numel = 0;
+        overflow_numel(t, &numel);
+        if (numel == 0) continue;
+        const std::string who = "tensor " + std::to_string(k) + ": ";
+        if (is_factored(op, t)) {
+            if (sh[k].rows_total < t.rows || sh[k].rows_total > kMaxDim)
+                return fail(MEO_ESHAPE, who + "rows_total must be >= the shard's rows and < 2^31");
+            if (t.cols % kVec != 0 || t.cols > kRcMaxCols1 || !aligned16(t.param) || !aligned16(t.grad))
+                return fail(MEO_ESHAPE, who + "a row-sharded factored tensor needs cols % 8 == 0, cols <= " +
+                                            std::to_string(kRcMaxCols1) + " and 16-byte aligned param and grad");
+        } else if (sh[k].rows_total < numel) {
+            return fail(MEO_ESHAPE, who + "rows_total (elements of the whole tensor) must be >= the shard's");
+        }
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MEO_EHIP, "hipGetDevice failed");
+    }
+    const int64_t floats = partials_layout(op, n, ts, nullptr);
+    if (floats > kMaxDim) return fail(MEO_ESHAPE, "the partial-sum record exceeds 2^31 - 1 floats");
+    return check_device_range(partials, static_cast<size_t>(floats) * 4, dev, "partials", MEO_EMEMORY);
+}
+
+struct AfShard {
+    Plan* p = nullptr;
+    double rho = 0.0, b2 = 0.0;
+};
+
+int af_shard_prepare(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                     const meo_shard* sh, const meo_adafactor_state* st, const void* partials, void* ws,
+                     size_t ws_bytes, AfShard* out) {
+    int rc = meo_adafactor_validate(hp, step, n, ts, st);
+    if (rc) return rc;
+    if (n == 0) return MEO_OK;
+    rc = check_shards(kOpAdafactor, n, ts, sh, partials);
+    if (rc) return rc;
+    rc = check_workspace(kOpAdafactor, n, ts, ws, ws_bytes);
+    if (rc) return rc;
+    const std::vector<StatePtrs> sp = state_ptrs(kOpAdafactor, n, st);
+    out->p = get_plan(kOpAdafactor, n, ts, sp.data(), hp->has_beta1, &rc, sh);
+    if (!out->p) return rc;
+    const double tt = static_cast<double>(step);
+    out->rho = hp->relative_step ? std::fmin(hp->warmup_init ? 1e-6 * tt : 1e-2, 1.0 / std::sqrt(tt)) : hp->lr;
+    out->b2 = 1.0 - std::pow(tt, hp->decay_rate);
+    return MEO_OK;
+}
+
+LambArgs lamb_args(const meo_lamb_hparams* hp, int64_t step) {
+    const double tt = static_cast<double>(step);
+    const double bc1 = hp->bias_correction ? 1.0 - std::pow(hp->beta1, tt) : 1.0;
+    const double bc2 = hp->bias_correction ? 1.0 - std::pow(hp->beta2, tt) : 1.0;
+    return LambArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1),
+                    static_cast<float>(hp->beta2), static_cast<float>(1.0 - hp->beta2),
+                    static_cast<float>(1.0 / bc1), static_cast<float>(1.0 / bc2),
+                    static_cast<float>(hp->eps), static_cast<float>(hp->weight_decay)};
+}
+
+int lamb_shard_prepare(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                       const meo_shard* sh, const meo_lamb_state* st, const void* partials, void* ws,
+                       size_t ws_bytes, Plan** out) {
+    int rc = meo_lamb_validate(hp, step, n, ts, st);
+    if (rc) return rc;
+    if (n == 0) return MEO_OK;
+    rc = check_shards(kOpLamb, n, ts, sh, partials);
+    if (rc) return rc;
+    rc = check_workspace(kOpLamb, n, ts, ws, ws_bytes);
+    if (rc) return rc;
+    const std::vector<StatePtrs> sp = state_ptrs(kOpLamb, n, st);
+    *out = get_plan(kOpLamb, n, ts, sp.data(), 1, &rc, sh);
+    return *out ? MEO_OK : rc;
+}
+
+}  // namespace
+
+size_t meo_adafactor_partials_size(int32_t n, const meo_tensor* ts) {
+    if (n <= 0 || !ts) return 0;
+    return static_cast<size_t>(partials_layout(kOpAdafactor, n, ts, nullptr));
+}
+
+size_t meo_lamb_partials_size(int32_t n, const meo_tensor* ts) {
+    if (n <= 0 || !ts) return 0;
+    return static_cast<size_t>(partials_layout(kOpLamb, n, ts, nullptr));
+}
+
+int meo_adafactor_shard_stats(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                              const meo_shard* sh, const meo_adafactor_state* st, float* partials, void* ws,
+                              size_t ws_bytes, void* stream) {
+    AfShard a;
+    int rc = af_shard_prepare(hp, step, n, ts, sh, st, partials, ws, ws_bytes, &a);
+    if (rc || n == 0) return rc;
+    Plan* p = a.p;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    launch_zero_records(p->items[kListEmpty], p->count[kListEmpty], partials, s);
+    if (p->n == 0) return launch_status("adafactor shard statistics launch");
+    float* w = static_cast<float*>(ws);
+    auto tab = [&](int l) { return Table{p->desc, p->items[l], w}; };
+    const int32_t need_x = hp->scale_parameter ? 1 : 0;
+    const StatsArgs sa{static_cast<float>(hp->eps1), static_cast<float>(a.b2), static_cast<float>(1.0 - a.b2), need_x,
+                       a.b2, 1.0 - a.b2};
+    PassTimer pt(s);
+    if (p->count[kListRc0]) {
+        launch_rowstats(0, tab(kListRc0), p->count[kListRc0], sa, s);
+        pt.mark(kPassStats);
+    }
+    if (p->count[kListRc1]) {
+        launch_rowstats(1, tab(kListRc1), p->count[kListRc1], sa, s);
+        pt.mark(kPassStatsWide);
+    }
+    launch_shard_partials(tab(kListShard), p->count[kListShard], partials, need_x, s);
+    pt.mark(kPassFinalize);
+    return launch_status("adafactor shard statistics launch");
+}
+
+int meo_adafactor_shard_apply(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                              const meo_shard* sh, const meo_adafactor_state* st, const float* partials, void* ws,
+                              size_t ws_bytes, void* stream) {
+    AfShard a;
+    int rc = af_shard_prepare(hp, step, n, ts, sh, st, partials, ws, ws_bytes, &a);
+    if (rc || n == 0 || a.p->n == 0) return rc;
+    Plan* p = a.p;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    float* w = static_cast<float*>(ws);
+    auto tab = [&](int l) { return Table{p->desc, p->items[l], w}; };
+    PassTimer pt(s);
+    launch_shard_fold(tab(kListFold), p->count[kListFold], partials, a.b2, s);
+    pt.mark(kPassFinalize);
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, partials, a.rho, hp->eps2,
+                                              hp->clip_threshold, hp->weight_decay, 0.0}, s);
+    pt.mark(kPassScalars);
+    launch_af_apply(tab(kListAll), p->count[kListAll],
+                    AfApplyArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1), hp->has_beta1},
+                    p->storage, s);
+    pt.mark(kPassAfApply);
+    return launch_status("adafactor shard apply launch");
+}
+
+int meo_lamb_shard_stats(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                         const meo_shard* sh, const meo_lamb_state* st, float* partials, void* ws, size_t ws_bytes,
+                         void* stream) {
+    Plan* p = nullptr;
+    int rc = lamb_shard_prepare(hp, step, n, ts, sh, st, partials, ws, ws_bytes, &p);
+    if (rc || n == 0) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    launch_zero_records(p->items[kListEmpty], p->count[kListEmpty], partials, s);
+    if (p->n == 0) return launch_status("lamb shard statistics launch");
+    float* w = static_cast<float*>(ws);
+    PassTimer pt(s);
+    launch_lamb_moments(Table{p->desc, p->items[kListAll], w}, p->count[kListAll], lamb_args(hp, step), p->storage, s);
+    pt.mark(kPassLambMoments);
+    launch_shard_partials(Table{p->desc, p->items[kListShard], w}, p->count[kListShard], partials, 0, s);
+    pt.mark(kPassFinalize);
+    return launch_status("lamb shard statistics launch");
+}
+
+int meo_lamb_shard_apply(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                         const meo_shard* sh, const meo_lamb_state* st, const float* partials, void* ws,
+                         size_t ws_bytes, void* stream) {
+    Plan* p = nullptr;
+    int rc = lamb_shard_prepare(hp, step, n, ts, sh, st, partials, ws, ws_bytes, &p);
+    if (rc || n == 0 || p->n == 0) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    float* w = static_cast<float*>(ws);
+    PassTimer pt(s);
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalLamb, 0, partials, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
+    pt.mark(kPassScalars);
+    launch_lamb_apply(Table{p->desc, p->items[kListAll], w}, p->count[kListAll], lamb_args(hp, step), p->storage, s);
+    pt.mark(kPassLambApply);
+    return launch_status("lamb shard apply launch");
 }
 
 }  // extern "C"

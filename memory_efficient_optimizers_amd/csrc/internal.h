@@ -93,6 +93,11 @@ struct TDesc {
     int32_t strips;   // row-complete strips per matrix
     int32_t nrc, ncc; // finalize chunks per matrix along rows / columns
     int32_t xchunks;  // row-complete: chunks of the parameter for sum(X^2)
+    // Row-sharded steps: where the tensor's record starts in the partial-sum buffer
+    // (floats) and the size of the whole tensor (rows of each matrix when factored,
+    // elements when flat).
+    int64_t part;
+    int64_t total;
 };
 
 // One launch: its (tensor, local tile) items and the shared descriptors.
@@ -505,6 +510,7 @@ enum ScalMode { kScalAdafactor = 0, kScalCame1 = 1, kScalCame2 = 2, kScalLamb = 
 struct ScalArgs {
     int32_t mode;
     int32_t scale_parameter;
+    const float* partials;  // row-sharded steps: the all-reduced partial sums; else null
     double rho;         // Adafactor base step size
     double eps2;        // Adafactor floor of RMS(param)
     double clip;        // clip threshold
@@ -538,5 +544,11 @@ void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, int storage, 
 void launch_came_apply(const Table& t, int64_t n, int storage, hipStream_t s);
 void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, int storage, hipStream_t s);
 void launch_lamb_apply(const Table& t, int64_t n, const LambArgs& a, int storage, hipStream_t s);
+// Row-sharded steps: the shard's partial sums, and their fold (after the caller's
+// all-reduce) into the replicated column statistic.
+void launch_shard_partials(const Table& t, int64_t n, float* partials, int32_t need_x, hipStream_t s);
+void launch_shard_fold(const Table& t, int64_t n, const float* partials, double beta, hipStream_t s);
+// Zero-fills records (x = first float, y = length) of tensors a rank holds none of.
+void launch_zero_records(const int2* items, int64_t n, float* partials, hipStream_t s);
 
 }  // namespace meo

@@ -528,10 +528,12 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
         }
         return;
     }
+    // Row-sharded steps: the tensor's record of all-reduced partial sums.
+    const float* P = a.partials ? a.partials + d.part : nullptr;
     if (a.mode == kScalLamb) {
         // components: sum of x^2, sum of d^2 (see the LAMB moment pass).
-        const double xn = sqrt(tile_sum(tp, d.tc, 0, lds));
-        const double dn = sqrt(tile_sum(tp, d.tc, 1, lds));
+        const double xn = sqrt(P ? static_cast<double>(ldf(P)) : tile_sum(tp, d.tc, 0, lds));
+        const double dn = sqrt(P ? static_cast<double>(ldf(P + 1)) : tile_sum(tp, d.tc, 1, lds));
         const double trust = (xn > 0.0 && dn > 0.0) ? xn / dn : 1.0;
         if (threadIdx.x == 0) {
             stf(bs, static_cast<float>(a.lr * trust));
@@ -542,11 +544,22 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
     }
 
     double su, sx;
-    if (d.mode == kRowComplete) {
+    double numel = n;
+    const int64_t BW = static_cast<int64_t>(d.B) * d.W;
+    // mean of the new row statistic of matrix b
+    auto row_mean = [&](int b) -> double {
+        if (P) return static_cast<double>(ldf(P + 2 * BW + b)) / static_cast<double>(d.total);
+        return d.mode == kRowComplete ? row_mean_rc(d, ws, b) : row_mean_tiled(d, ws, b);
+    };
+    if (P && d.mode == kFlat) {
+        su = static_cast<double>(ldf(P));
+        sx = static_cast<double>(ldf(P + 1));
+        numel = static_cast<double>(d.total);
+    } else if (d.mode == kRowComplete) {
         // sum U^2 = sum_b mean(R_b) * sum_j S_j / C_j (finalize chunk sums).
         double part = 0.0;
         for (int b = w; b < d.B; b += kWaves) {
-            const double mr = row_mean_rc(d, ws, b);
+            const double mr = row_mean(b);
             double u = 0.0;
             const float* sr = ws + d.sumr + static_cast<int64_t>(b) * d.ncc;
             for (int j = lane; j < d.ncc; j += kLanes) u += static_cast<double>(ldf(sr + j));
@@ -556,7 +569,10 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
         __syncthreads();
         su = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
         sx = 0.0;
-        if (a.mode == kScalAdafactor && a.scale_parameter) {  // the chunks ran only then
+        if (P) {
+            sx = static_cast<double>(ldf(P + 2 * BW + d.B));
+            numel = static_cast<double>(d.B) * static_cast<double>(d.total) * static_cast<double>(d.W);
+        } else if (a.mode == kScalAdafactor && a.scale_parameter) {  // the chunks ran only then
             double a_ = 0.0;
             for (int j = threadIdx.x; j < d.xchunks; j += kThreads) a_ += static_cast<double>(ldf(ws + d.xpart + j));
             sx = block_sum_d(a_, lds);
@@ -567,11 +583,11 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
         su = tile_sum(tp, tiles, 0, lds);
         sx = tile_sum(tp, tiles, 1, lds);
     }
-    const double rms_u = sqrt(su / n);
+    const double rms_u = sqrt(su / numel);
     const double kappa = fmax(1.0, rms_u / a.clip);
     double alpha = 1.0;
     if (a.mode == kScalAdafactor) {
-        const double rms_x = sqrt(sx / n);
+        const double rms_x = sqrt(sx / numel);
         alpha = a.rho * (a.scale_parameter ? fmax(a.eps2, rms_x) : 1.0);
         if (threadIdx.x == 0) stf(scal + kSlotRmsX, static_cast<float>(rms_x));
     }
@@ -588,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
         return;
     }
     for (int b = w; b < d.B; b += kWaves) {
-        const double mr = d.mode == kRowComplete ? row_mean_rc(d, ws, b) : row_mean_tiled(d, ws, b);
+        const double mr = row_mean(b);
         if (lane == 0) stf(bs + b, static_cast<float>(coef * sqrt(mr)));
     }
 }

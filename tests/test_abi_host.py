@@ -274,3 +274,34 @@ def test_lamb_validation(lib):
 def test_empty_list_is_a_noop(lib):
     assert lib.meo_adafactor_step(_lib.ctypes.byref(_lib.adafactor_hparams()), 1, 0, None, None, None, 0,
                                   None) == _lib.MEO_OK
+
+
+def test_shard_checks(lib):
+    """Row-sharded entry points validate shards and the partial-sum buffer on the
+    host before anything is enqueued."""
+    ps, gs = _mk([(4, 8), (8, 20), (30,)])
+    st = [_lib.init_state("adafactor", p, beta1=True) for p in ps]
+    hp = _lib.adafactor_hparams(beta1=0.9)
+    size = _lib.meo_adafactor_partials_size(ps, gs)
+    assert size == (2 * 8 + 1) + 1 + (2 * 20 + 1) + 1 + 2
+    part = torch.zeros(size)
+    # a factored shard needs row-complete rows: cols % 8 == 0
+    code, msg = _code(_lib.meo_adafactor_shard_stats, hp, 1, ps, gs, [8, 16, 30], st, part, None, 0)
+    assert code == _lib.MEO_ESHAPE and "cols % 8" in msg
+    ps, gs = _mk([(4, 8), (8, 24), (30,)])
+    st = [_lib.init_state("adafactor", p, beta1=True) for p in ps]
+    part = torch.zeros(_lib.meo_adafactor_partials_size(ps, gs))
+    code, msg = _code(_lib.meo_adafactor_shard_stats, hp, 1, ps, gs, [8, 4, 30], st, part, None, 0)
+    assert code == _lib.MEO_ESHAPE and "rows_total" in msg
+    code, msg = _code(_lib.meo_adafactor_shard_stats, hp, 1, ps, gs, [8, 16, 20], st, part, None, 0)
+    assert code == _lib.MEO_ESHAPE
+    code, msg = _code(_lib.meo_adafactor_shard_apply, hp, 1, ps, gs, [8, 16, 30], st, None, None, 0)
+    assert code == _lib.MEO_ENULL and "partials" in msg
+    # host memory as partials: refused (no device at all here, or not device memory)
+    code, msg = _code(_lib.meo_adafactor_shard_apply, hp, 1, ps, gs, [8, 16, 30], st, part, None, 0)
+    assert code in (_lib.MEO_EMEMORY, _lib.MEO_EHIP)
+    lst = [_lib.init_state("lamb", p) for p in ps]
+    assert _lib.meo_lamb_partials_size(ps, gs) == 6
+    code, msg = _code(_lib.meo_lamb_shard_stats, _lib.lamb_hparams(), 1, ps, gs, [31, 191, 30], lst,
+                      torch.zeros(6), None, 0)
+    assert code == _lib.MEO_ESHAPE   # 4 x 8 = 32 elements > 31

@@ -1,0 +1,152 @@
+"""Row-sharded steps on one GPU: N ranks' shares of every tensor, each stepped by
+the library's two shard calls, with the ranks' partial-sum records summed in
+between (what an all-reduce over the ranks would give; here a sum of the N
+buffers on the GPU). After every step the shards, put back together, must match
+the oracle's whole-tensor step: the parameter, first moment and row statistic row
+by row, and every rank's copy of the column statistic. Bars as in the parity tests
+(tests/harness.py): the ranks sum partials in another order than one pass over the
+whole tensor, which moves results by fp32 rounding only.
+
+Shapes cover one row per rank (a factored shard of height 1 stays factored, which
+the page's DistributedCAME note requires), ranks holding no rows of a small
+tensor (their records must read zero), batched matrices, 11008-wide rows (the wide
+first-pass class) and 1-D tensors split by elements; LAMB splits every tensor by
+elements."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from memory_efficient_optimizers_amd import _lib
+from tests.harness import TOL_F32, output_err, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _lib.load()
+
+
+SHAPES = [(129, 1024), (8, 4096), (4, 8), (2, 3, 72, 136), (40, 11008), (5000,), (300,), (3,)]
+
+
+def _split(n, parts):
+    return [(n * r // parts, n * (r + 1) // parts) for r in range(parts)]
+
+
+def _shard_of(t, opt, r0, r1):
+    """Rows r0:r1 of dim -2 (factored), else elements r0:r1 of the flattened tensor."""
+    if opt != "lamb" and t.dim() >= 2:
+        return t[..., r0:r1, :].contiguous()
+    return t.reshape(-1)[r0:r1].contiguous()
+
+
+def _ranges(opt, shape, nranks):
+    if opt != "lamb" and len(shape) >= 2:
+        return _split(shape[-2], nranks), shape[-2]
+    n = math.prod(shape)
+    return _split(n, nranks), n
+
+
+@pytest.mark.parametrize("nranks", [1, 3, 8])
+@pytest.mark.parametrize("opt,hp", [
+    ("adafactor", {"beta1": 0.9, "weight_decay": 0.1}),
+    ("adafactor", {}),
+    ("adafactor", {"scale_parameter": False, "beta1": 0.5, "clip_threshold": 0.3}),
+    ("lamb", {"weight_decay": 0.01}),
+])
+def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
+    wl = workloads.custom(f"shard_{opt}", opt, SHAPES, hparams=hp, grad_dtype=torch.bfloat16,
+                          grad_scaling="rowcol" if opt != "lamb" else "row")
+    full = workloads.init_params(wl, "cuda")
+    scales = workloads.grad_scales(wl, "cuda")
+    hps = (_lib.adafactor_hparams if opt == "adafactor" else _lib.lamb_hparams)(**hp)
+    beta1 = hp.get("beta1") is not None or opt == "lamb"
+    ranges = [_ranges(opt, tuple(p.shape), nranks) for p in full]
+    totals = [tot for _, tot in ranges]
+    ranks = []
+    for r in range(nranks):
+        ps = [_shard_of(p, opt, *ranges[k][0][r]) for k, p in enumerate(full)]
+        sts = []
+        for k, p in enumerate(ps):
+            st = _lib.init_state(opt, p, beta1=beta1)
+            if "exp_avg_sq_col" in st:  # the column statistic is kept whole on every rank
+                st["exp_avg_sq_col"] = torch.zeros(full[k].shape[:-2] + full[k].shape[-1:], device="cuda")
+            sts.append(st)
+        ranks.append({"params": ps, "states": sts})
+    size = getattr(_lib, f"meo_{opt}_partials_size")(ranks[0]["params"], ranks[0]["params"])
+    stats = getattr(_lib, f"meo_{opt}_shard_stats")
+    apply = getattr(_lib, f"meo_{opt}_shard_apply")
+    ox = [to64(p) for p in full]
+    ost = [oracle.INIT_STATE[opt](tuple(p.shape), hp) for p in full]
+    for t in range(1, 4):
+        gfull = workloads.grads(wl, t - 1, scales, "cuda")
+        parts = []
+        for r, rk in enumerate(ranks):
+            gs = [_shard_of(g, opt, *ranges[k][0][r]) for k, g in enumerate(gfull)]
+            rk["grads"] = gs
+            ws = _lib.workspace(getattr(_lib, f"meo_{opt}_workspace_size")(rk["params"], gs), "cuda")
+            rk["ws"] = ws
+            part = torch.full((size,), float("nan"), device="cuda")  # every entry must be written
+            stats(hps, t, rk["params"], gs, totals, rk["states"], part, ws)
+            parts.append(part)
+        reduced = torch.stack(parts).sum(0)  # the all-reduce
+        assert torch.isfinite(reduced).all()
+        for rk in ranks:
+            apply(hps, t, rk["params"], rk["grads"], totals, rk["states"], reduced, rk["ws"])
+        torch.cuda.synchronize()
+        ox, ost = oracle.STEP[opt](ox, [to64(g) for g in gfull], ost, hp, t)
+        for k, spec in enumerate(wl.specs):
+            fac = opt != "lamb" and len(spec.shape) >= 2
+            dim = -2 if fac else 0
+
+            def whole(key):
+                pieces = [rk["states"][k][key] if key != "param" else rk["params"][k] for rk in ranks]
+                if fac:
+                    if key == "exp_avg_sq_row":
+                        return torch.cat(pieces, dim=-1)
+                    return torch.cat(pieces, dim=-2)
+                return torch.cat([p.reshape(-1) for p in pieces]).reshape(spec.shape)
+
+            errs = {"param": output_err("param", to64(whole("param")), ox[k])}
+            for key in ost[k]:
+                if key == "exp_avg_sq_col":
+                    cols = [rk["states"][k][key] for rk, (r0, r1) in zip(ranks, ranges[k][0]) if r1 > r0]
+                    for c in cols[1:]:
+                        assert torch.equal(c, cols[0]), "ranks disagree on the column statistic"
+                    errs[key] = output_err(key, to64(cols[0]), ost[k][key])
+                else:
+                    errs[key] = output_err(key, to64(whole(key)), ost[k][key])
+            worst = max(errs, key=errs.get)
+            print(f"  {opt} N={nranks} step {t} {spec.name} {tuple(spec.shape)}: worst {errs[worst]:.3e} ({worst})",
+                  flush=True)
+            assert errs[worst] <= TOL_F32, (t, spec.shape, worst, errs[worst])
+
+
+def test_shard_of_the_whole_is_the_whole_step():
+    """One rank holding everything: the sharded calls give the whole-tensor step's
+    parameters (the same kernels; sums in a different order, so within fp32 bars)."""
+    wl = workloads.custom("shard1", "adafactor", [(129, 1024), (300,)], hparams={"beta1": 0.9},
+                          grad_dtype=torch.bfloat16)
+    a = workloads.init_params(wl, "cuda")
+    b = [p.clone() for p in a]
+    scales = workloads.grad_scales(wl, "cuda")
+    hps = _lib.adafactor_hparams(beta1=0.9)
+    sa = [_lib.init_state("adafactor", p, beta1=True) for p in a]
+    sb = [_lib.init_state("adafactor", p, beta1=True) for p in b]
+    part = torch.zeros(_lib.meo_adafactor_partials_size(a, a), device="cuda")
+    for t in range(1, 4):
+        gs = workloads.grads(wl, t - 1, scales, "cuda")
+        ws = _lib.workspace(_lib.meo_adafactor_workspace_size(a, gs), "cuda")
+        _lib.meo_adafactor_step(hps, t, a, gs, sa, ws)
+        _lib.meo_adafactor_shard_stats(hps, t, b, gs, [129, 300], sb, part, ws)
+        _lib.meo_adafactor_shard_apply(hps, t, b, gs, [129, 300], sb, part, ws)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert output_err("param", to64(y), to64(x)) <= TOL_F32
