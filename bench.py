@@ -164,6 +164,73 @@ def copy_calibration(torch, args) -> int:
     return 0
 
 
+def shard_bench(torch, _lib, workloads, wl, args) -> int:
+    """One rank's share of a row-sharded step over N ranks, at the workload's real
+    shapes: rank 0's rows of every factored tensor (all columns; the column
+    statistic whole) and its element range of every 1-D tensor (LAMB: of every
+    tensor); stats call, then apply call, per step. The partial sums go from one
+    call to the next unreduced: the all-reduce over ranks that sits between them is
+    not part of the measured work, so the values reached are not a real step's."""
+    from memory_efficient_optimizers_amd.optim import moment_dtype
+    if wl.optimizer not in ("adafactor", "lamb"):
+        print("row-sharded steps exist for Adafactor and LAMB", file=sys.stderr)
+        return 2
+    n, dev, opt = args.shard_ranks, "cuda", wl.optimizer
+    hp = dict(wl.hparams)
+    beta1 = hp.get("beta1") is not None or opt == "lamb"
+    local, totals = [], []
+    for s in wl.specs:
+        if opt != "lamb" and len(s.shape) >= 2:
+            local.append(tuple(s.shape[:-2]) + (s.shape[-2] // n,) + tuple(s.shape[-1:]))
+            totals.append(s.shape[-2])
+        else:
+            local.append((math.prod(s.shape) // n,))
+            totals.append(math.prod(s.shape))
+    params = flat_views(torch, local, wl.param_dtype, dev)
+    for p in params:
+        p.normal_(0.0, 0.02)
+    grads = flat_views(torch, local, wl.grad_dtype, dev)
+    for g in grads:
+        g.normal_(0.0, 1e-3)
+    states = []
+    for s, p in zip(wl.specs, params):
+        st = _lib.init_state(opt, p, beta1=beta1, state_dtype=moment_dtype(opt, s.shape, wl.state_dtype, wl.param_dtype))
+        if "exp_avg_sq_col" in st:
+            st["exp_avg_sq_col"] = torch.zeros(tuple(s.shape[:-2]) + tuple(s.shape[-1:]), device=dev)
+        states.append(st)
+    hps = {"adafactor": _lib.adafactor_hparams, "lamb": _lib.lamb_hparams}[opt](**hp)
+    ws = _lib.workspace(getattr(_lib, f"meo_{opt}_workspace_size")(params, grads), dev)
+    part = torch.zeros(getattr(_lib, f"meo_{opt}_partials_size")(params, grads), device=dev)
+    call = _lib.PreparedShardStep(opt, hps, params, grads, totals, states, part, ws)
+    stream = torch.cuda.current_stream()
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        call.stats(t, stream)
+        call.apply(t, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        t += 1
+        call.stats(t, stream)
+        call.apply(t, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    numel = sum(math.prod(s) for s in local)
+    whole = algorithmic_bytes(wl)["step"]
+    step_bytes = whole * numel / wl.numel  # the same bytes per parameter on the rank's share
+    out = {"metric": f"one rank's share of a row-sharded optimizer step over {n} ranks (all-reduce excluded)",
+           "value": numel / (ms / 1e3), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "data": "synthetic",
+           "config": {"workload": wl.name, "ranks": n, "rank_params": numel, "partials_floats": part.numel()},
+           "hbm": {"step_bytes": step_bytes, "achieved": step_bytes / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBPS,
+                   "unit": "GB/s", "frac": step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +240,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", choices=["flat", "separate"], default="flat",
                     help="flat: one buffer per kind of tensor (default); separate: one allocation per tensor")
+    ap.add_argument("--shard-ranks", type=int, default=0,
+                    help="instead of the whole step: time one rank's share of a row-sharded step over N ranks "
+                         "(Adafactor or LAMB; the all-reduce of the partial sums between the two calls is "
+                         "not part of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the step: time a plain device copy of 4 GiB (one elementwise kernel), "
                          "the reference for achievable bandwidth and for scaling rocprofv3 byte counters")
@@ -198,6 +269,8 @@ def main() -> int:
     wl = workloads.WORKLOADS[args.workload]
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.shard_ranks > 1:
+        return shard_bench(torch, _lib, workloads, wl, args)
 
     hp = dict(wl.hparams)
     beta1 = hp.get("beta1") is not None

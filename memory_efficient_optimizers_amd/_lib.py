@@ -366,6 +366,37 @@ def meo_lamb_shard_apply(hp, step, params, grads, totals, states, partials, work
     _shard_call("lamb", "apply", hp, step, params, grads, totals, states, partials, workspace, stream)
 
 
+class PreparedShardStep:
+    """Both calls of a row-sharded step over a fixed list, marshalled once (see
+    PreparedStep): ``stats(step)`` fills ``partials`` and, after the caller has
+    summed them over the ranks, ``apply(step)`` updates the shard."""
+
+    _KIND = {"adafactor": (meo_adafactor_state, ADAFACTOR_KEYS), "lamb": (meo_lamb_state, LAMB_KEYS)}
+
+    def __init__(self, optimizer: str, hp, params, grads, totals, states, partials, workspace=None):
+        cls, keys = self._KIND[optimizer]
+        lib = load()
+        self._fns = (getattr(lib, f"meo_{optimizer}_shard_stats"), getattr(lib, f"meo_{optimizer}_shard_apply"))
+        self.hp = hp
+        self.n = len(params)
+        self.tensors = _tensors(params, grads, states)
+        self.shards = _shards(totals)
+        self.states = _states(cls, keys, states)
+        self.partials = _ptr(partials)
+        self.ws, self.ws_bytes = _ws(workspace)
+        self._keep = (list(params), list(grads), list(states), partials, workspace)
+
+    def _call(self, fn, step, stream):
+        _check(fn(ctypes.byref(self.hp), step, self.n, self.tensors, self.shards, self.states, self.partials,
+                  self.ws, self.ws_bytes, _stream(stream)))
+
+    def stats(self, step: int, stream=None) -> None:
+        self._call(self._fns[0], step, stream)
+
+    def apply(self, step: int, stream=None) -> None:
+        self._call(self._fns[1], step, stream)
+
+
 def meo_last_error() -> str:
     return load().meo_last_error().decode("utf-8", "replace")
 
