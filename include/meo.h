@@ -308,6 +308,26 @@ int    meo_adafactor_shard_apply(const meo_adafactor_hparams* hp, int64_t step, 
                                  const meo_tensor* tensors, const meo_shard* shards,
                                  const meo_adafactor_state* states, const float* partials,
                                  void* workspace, size_t workspace_bytes, void* stream);
+/* CAME takes two exchanges. meo_came_shard_stats writes `partials` (the Adafactor
+ * record above; its sum of X^2 is 0); after the all-reduce, meo_came_shard_moment
+ * folds it (column statistic, clip divisor), updates the first moment of the shard
+ * (1-D tensors finish their step here), finishes the confidence row statistic
+ * (whole rows) and writes `confidence`: per factored tensor [B][W] sums of the
+ * instability E = (U - M)^2 + eps2 over the shard's rows and [B] sums of the new
+ * confidence row statistic; 1-D tensors have no entry. After its all-reduce,
+ * meo_came_shard_apply folds it into the replicated confidence column statistic
+ * and applies the step to the shard. */
+size_t meo_came_partials_size(int32_t n, const meo_tensor* tensors);
+size_t meo_came_confidence_size(int32_t n, const meo_tensor* tensors);
+int    meo_came_shard_stats(const meo_came_hparams* hp, int64_t step, int32_t n, const meo_tensor* tensors,
+                            const meo_shard* shards, const meo_came_state* states, float* partials,
+                            void* workspace, size_t workspace_bytes, void* stream);
+int    meo_came_shard_moment(const meo_came_hparams* hp, int64_t step, int32_t n, const meo_tensor* tensors,
+                             const meo_shard* shards, const meo_came_state* states, const float* partials,
+                             float* confidence, void* workspace, size_t workspace_bytes, void* stream);
+int    meo_came_shard_apply(const meo_came_hparams* hp, int64_t step, int32_t n, const meo_tensor* tensors,
+                            const meo_shard* shards, const meo_came_state* states, const float* confidence,
+                            void* workspace, size_t workspace_bytes, void* stream);
 size_t meo_lamb_partials_size(int32_t n, const meo_tensor* tensors);
 int    meo_lamb_shard_stats(const meo_lamb_hparams* hp, int64_t step, int32_t n,
                             const meo_tensor* tensors, const meo_shard* shards,

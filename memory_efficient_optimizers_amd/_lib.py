@@ -37,6 +37,8 @@ EXPORTS = [
     "meo_pass_name", "meo_profile_collect",
     "meo_adafactor_partials_size", "meo_adafactor_shard_stats", "meo_adafactor_shard_apply",
     "meo_lamb_partials_size", "meo_lamb_shard_stats", "meo_lamb_shard_apply",
+    "meo_came_partials_size", "meo_came_confidence_size", "meo_came_shard_stats", "meo_came_shard_moment",
+    "meo_came_shard_apply",
 ]
 MEO_NUM_PASSES = 11
 
@@ -129,6 +131,16 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             fn.argtypes = [ctypes.POINTER(hp), c_int64, c_int32, T, S, ctypes.POINTER(st), c_void_p, c_void_p,
                            c_size_t, c_void_p]
             fn.restype = ctypes.c_int
+    CH, CS = ctypes.POINTER(meo_came_hparams), ctypes.POINTER(meo_came_state)
+    for name in ("meo_came_partials_size", "meo_came_confidence_size"):
+        getattr(lib, name).argtypes = [c_int32, T]
+        getattr(lib, name).restype = c_size_t
+    for name in ("meo_came_shard_stats", "meo_came_shard_apply"):
+        getattr(lib, name).argtypes = [CH, c_int64, c_int32, T, S, CS, c_void_p, c_void_p, c_size_t, c_void_p]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.meo_came_shard_moment.argtypes = [CH, c_int64, c_int32, T, S, CS, c_void_p, c_void_p, c_void_p, c_size_t,
+                                          c_void_p]
+    lib.meo_came_shard_moment.restype = ctypes.c_int
     lib.meo_last_error.argtypes = []
     lib.meo_last_error.restype = ctypes.c_char_p
     lib.meo_release_plans.argtypes = []
@@ -364,6 +376,41 @@ def meo_lamb_shard_stats(hp, step, params, grads, totals, states, partials, work
 
 def meo_lamb_shard_apply(hp, step, params, grads, totals, states, partials, workspace=None, stream=None):
     _shard_call("lamb", "apply", hp, step, params, grads, totals, states, partials, workspace, stream)
+
+
+def meo_came_partials_size(params, grads) -> int:
+    return int(load().meo_came_partials_size(len(params), _tensors(params, grads)))
+
+
+def meo_came_confidence_size(params, grads) -> int:
+    """Floats of CAME's second record (confidence sums) in a row-sharded step."""
+    return int(load().meo_came_confidence_size(len(params), _tensors(params, grads)))
+
+
+def _came_args(hp, step, params, grads, totals, states):
+    return (ctypes.byref(hp), step, len(params), _tensors(params, grads, states), _shards(totals),
+            _states(meo_came_state, CAME_KEYS, states))
+
+
+def meo_came_shard_stats(hp, step, params, grads, totals, states, partials, workspace=None, stream=None):
+    ws, nb = _ws(workspace)
+    _check(load().meo_came_shard_stats(*_came_args(hp, step, params, grads, totals, states), _ptr(partials), ws, nb,
+                                       _stream(stream)))
+
+
+def meo_came_shard_moment(hp, step, params, grads, totals, states, partials, confidence, workspace=None,
+                          stream=None):
+    """CAME's second stage: from the reduced ``partials``, the moment update of the
+    shard and its confidence sums (``confidence``, to be reduced over the ranks)."""
+    ws, nb = _ws(workspace)
+    _check(load().meo_came_shard_moment(*_came_args(hp, step, params, grads, totals, states), _ptr(partials),
+                                        _ptr(confidence), ws, nb, _stream(stream)))
+
+
+def meo_came_shard_apply(hp, step, params, grads, totals, states, confidence, workspace=None, stream=None):
+    ws, nb = _ws(workspace)
+    _check(load().meo_came_shard_apply(*_came_args(hp, step, params, grads, totals, states), _ptr(confidence), ws,
+                                       nb, _stream(stream)))
 
 
 class PreparedShardStep:

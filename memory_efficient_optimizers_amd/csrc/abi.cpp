@@ -292,6 +292,18 @@ int64_t partials_layout(int op, int32_t n, const meo_tensor* ts, std::vector<int
     return off;
 }
 
+// CAME's second record (confidence sums): [B][W] + [B] per factored tensor, none for
+// 1-D tensors (their step ends in the moment pass).
+int64_t confidence_layout(int32_t n, const meo_tensor* ts, std::vector<int64_t>* offs) {
+    int64_t off = 0;
+    if (offs) offs->assign(n, 0);
+    for (int32_t k = 0; k < n; ++k) {
+        if (offs) (*offs)[k] = off;
+        if (is_factored(kOpCame, ts[k])) off += ts[k].batch * (ts[k].cols + 1);
+    }
+    return off;
+}
+
 // Whether [p, p + bytes) lies in one allocation of device memory of device `dev`
 // that the HIP runtime knows (hipMalloc, hipMallocManaged, allocators built on
 // them). Catches host, truncated or stale pointers and ranges described past the
@@ -373,7 +385,7 @@ int check_tensor_memory(int op, int32_t n, const meo_tensor* ts, const StatePtrs
 
 // Item tables of the launches of one call.
 enum List { kListRc0 = 0, kListRc1, kListTiled, kListAll, kListFin1, kListFin2, kListShard, kListFold, kListEmpty,
-            kListCount };
+            kListConfRows, kListConf, kListEmpty2, kListCount };
 
 struct Plan {
     std::vector<uint8_t> key;
@@ -480,8 +492,9 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
     if (*rc) return nullptr;
     std::vector<Geo> geo;
     layout(op, n, ts, &geo);
-    std::vector<int64_t> poff;
+    std::vector<int64_t> poff, poff2;
     if (shards) partials_layout(op, n, ts, &poff);
+    if (shards && op == kOpCame) confidence_layout(n, ts, &poff2);
     std::vector<TDesc> desc;
     std::vector<int2> lists[kListCount];
     for (int32_t k = 0; k < n; ++k) {
@@ -490,6 +503,11 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
             if (shards) {  // a rank with none of the tensor contributes zeros
                 const int64_t len = (k + 1 < n ? poff[k + 1] : partials_layout(op, n, ts, nullptr)) - poff[k];
                 lists[kListEmpty].push_back(make_int2(static_cast<int>(poff[k]), static_cast<int>(len)));
+                if (op == kOpCame) {
+                    const int64_t len2 = (k + 1 < n ? poff2[k + 1] : confidence_layout(n, ts, nullptr)) - poff2[k];
+                    if (len2 > 0)
+                        lists[kListEmpty2].push_back(make_int2(static_cast<int>(poff2[k]), static_cast<int>(len2)));
+                }
             }
             continue;
         }
@@ -520,6 +538,7 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
         if (shards) {
             d.part = poff[k];
             d.total = shards[k].rows_total;
+            if (op == kOpCame) d.part2 = poff2[k];
         }
         desc.push_back(d);
         auto add = [&](int list, int64_t count) {
@@ -529,6 +548,14 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
             const int64_t per = g.mode == kFlat ? 1 : static_cast<int64_t>(g.B) * ceil_div(g.W, kThreads);
             add(kListShard, per);
             if (g.mode != kFlat) add(kListFold, per);
+            if (op == kOpCame && g.mode != kFlat) {
+                add(kListConf, per);
+                // the row items of the confidence finalize (its tiled layout: nrc row
+                // chunks then ncc column chunks per matrix)
+                for (int32_t b = 0; b < g.B; ++b)
+                    for (int32_t j = 0; j < g.nrc; ++j)
+                        lists[kListConfRows].push_back(make_int2(id, b * (g.nrc + g.ncc) + j));
+            }
         }
         if (g.mode == kFlat) {
             add(kListAll, g.tiles);
@@ -977,11 +1004,25 @@ namespace {
 // The shard sizes and the partial-sum buffer: factored shards need row-complete
 // rows (the single exchange rests on whole rows), the whole tensor is at least the
 // shard, and the buffer is device memory of the record's size.
-int check_shards(int op, int32_t n, const meo_tensor* ts, const meo_shard* sh, const void* partials) {
+// A record buffer: device memory of `floats` floats, 4-byte aligned.
+int check_record(const void* p, int64_t floats, const char* name) {
+    if (floats == 0) return MEO_OK;
+    if (!p) return fail(MEO_ENULL, std::string(name) + " is NULL");
+    if (reinterpret_cast<uintptr_t>(p) % 4) return fail(MEO_EALIGN, std::string(name) + " not 4-byte aligned");
+    if (floats > kMaxDim) return fail(MEO_ESHAPE, std::string("the record ") + name + " exceeds 2^31 - 1 floats");
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MEO_EHIP, "hipGetDevice failed");
+    }
+    return check_device_range(p, static_cast<size_t>(floats) * 4, dev, name, MEO_EMEMORY);
+}
+
+int check_shards(int op, int32_t n, const meo_tensor* ts, const meo_shard* sh, const void* partials,
+                 bool with_partials = true) {
     if (n == 0) return MEO_OK;
     if (!sh) return fail(MEO_ENULL, "shards is NULL");
-    if (!partials) return fail(MEO_ENULL, "partials is NULL");
-    if (reinterpret_cast<uintptr_t>(partials) % 4) return fail(MEO_EALIGN, "partials not 4-byte aligned");
+    if (with_partials && !partials) return fail(MEO_ENULL, "partials is NULL");
     for (int32_t k = 0; k < n; ++k) {
         const meo_tensor& t = ts[k];
         int64_t numel = 0;
@@ -998,14 +1039,8 @@ int check_shards(int op, int32_t n, const meo_tensor* ts, const meo_shard* sh, c
             return fail(MEO_ESHAPE, who + "rows_total (elements of the whole tensor) must be >= the shard's");
         }
     }
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(MEO_EHIP, "hipGetDevice failed");
-    }
-    const int64_t floats = partials_layout(op, n, ts, nullptr);
-    if (floats > kMaxDim) return fail(MEO_ESHAPE, "the partial-sum record exceeds 2^31 - 1 floats");
-    return check_device_range(partials, static_cast<size_t>(floats) * 4, dev, "partials", MEO_EMEMORY);
+    if (!with_partials) return MEO_OK;
+    return check_record(partials, partials_layout(op, n, ts, nullptr), "partials");
 }
 
 struct AfShard {
@@ -1153,6 +1188,117 @@ int meo_lamb_shard_apply(const meo_lamb_hparams* hp, int64_t step, int32_t n, co
     launch_lamb_apply(Table{p->desc, p->items[kListAll], w}, p->count[kListAll], lamb_args(hp, step), p->storage, s);
     pt.mark(kPassLambApply);
     return launch_status("lamb shard apply launch");
+}
+
+// ----------------------------------------------------------------------------- CAME, row-sharded
+
+namespace {
+
+int came_shard_prepare(const meo_came_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                       const meo_shard* sh, const meo_came_state* st, const void* partials, bool with_partials,
+                       const void* conf, bool with_conf, void* ws, size_t ws_bytes, Plan** out) {
+    int rc = meo_came_validate(hp, step, n, ts, st);
+    if (rc) return rc;
+    if (n == 0) return MEO_OK;
+    rc = check_shards(kOpCame, n, ts, sh, partials, with_partials);
+    if (rc) return rc;
+    if (with_conf) {
+        rc = check_record(conf, confidence_layout(n, ts, nullptr), "confidence");
+        if (rc) return rc;
+    }
+    rc = check_workspace(kOpCame, n, ts, ws, ws_bytes);
+    if (rc) return rc;
+    const std::vector<StatePtrs> sp = state_ptrs(kOpCame, n, st);
+    *out = get_plan(kOpCame, n, ts, sp.data(), 1, &rc, sh);
+    return *out ? MEO_OK : rc;
+}
+
+}  // namespace
+
+size_t meo_came_partials_size(int32_t n, const meo_tensor* ts) {
+    if (n <= 0 || !ts) return 0;
+    return static_cast<size_t>(partials_layout(kOpCame, n, ts, nullptr));
+}
+
+size_t meo_came_confidence_size(int32_t n, const meo_tensor* ts) {
+    if (n <= 0 || !ts) return 0;
+    return static_cast<size_t>(confidence_layout(n, ts, nullptr));
+}
+
+int meo_came_shard_stats(const meo_came_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                         const meo_shard* sh, const meo_came_state* st, float* partials, void* ws, size_t ws_bytes,
+                         void* stream) {
+    Plan* p = nullptr;
+    int rc = came_shard_prepare(hp, step, n, ts, sh, st, partials, true, nullptr, false, ws, ws_bytes, &p);
+    if (rc || n == 0) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    launch_zero_records(p->items[kListEmpty], p->count[kListEmpty], partials, s);
+    if (p->n == 0) return launch_status("came shard statistics launch");
+    float* w = static_cast<float*>(ws);
+    auto tab = [&](int l) { return Table{p->desc, p->items[l], w}; };
+    const StatsArgs sa{static_cast<float>(hp->eps1), static_cast<float>(hp->beta2),
+                       static_cast<float>(1.0 - hp->beta2), 0, hp->beta2, 1.0 - hp->beta2};
+    PassTimer pt(s);
+    if (p->count[kListRc0]) {
+        launch_rowstats(0, tab(kListRc0), p->count[kListRc0], sa, s);
+        pt.mark(kPassStats);
+    }
+    if (p->count[kListRc1]) {
+        launch_rowstats(1, tab(kListRc1), p->count[kListRc1], sa, s);
+        pt.mark(kPassStatsWide);
+    }
+    launch_shard_partials(tab(kListShard), p->count[kListShard], partials, 0, s);
+    pt.mark(kPassFinalize);
+    return launch_status("came shard statistics launch");
+}
+
+int meo_came_shard_moment(const meo_came_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                          const meo_shard* sh, const meo_came_state* st, const float* partials, float* conf,
+                          void* ws, size_t ws_bytes, void* stream) {
+    Plan* p = nullptr;
+    int rc = came_shard_prepare(hp, step, n, ts, sh, st, partials, true, conf, true, ws, ws_bytes, &p);
+    if (rc || n == 0) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    launch_zero_records(p->items[kListEmpty2], p->count[kListEmpty2], conf, s);
+    if (p->n == 0) return launch_status("came shard moment launch");
+    float* w = static_cast<float*>(ws);
+    auto tab = [&](int l) { return Table{p->desc, p->items[l], w}; };
+    PassTimer pt(s);
+    launch_shard_fold(tab(kListFold), p->count[kListFold], partials, hp->beta2, s);
+    pt.mark(kPassFinalize);
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame1, 0, partials, 0.0, 0.0, hp->clip_threshold,
+                                              hp->weight_decay, hp->lr}, s);
+    pt.mark(kPassScalars);
+    launch_came_mom(tab(kListAll), p->count[kListAll],
+                    CameArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1),
+                             static_cast<float>(hp->eps2), static_cast<float>(hp->lr)},
+                    p->storage, s);
+    pt.mark(kPassCameMom);
+    // the confidence row statistic is local (whole rows); its column sums are not
+    launch_finalize(tab(kListConfRows), p->count[kListConfRows], FinArgs{hp->beta3, 1, 1}, s);
+    launch_conf_partials(tab(kListConf), p->count[kListConf], conf, s);
+    pt.mark(kPassFinalize);
+    return launch_status("came shard moment launch");
+}
+
+int meo_came_shard_apply(const meo_came_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                         const meo_shard* sh, const meo_came_state* st, const float* conf, void* ws,
+                         size_t ws_bytes, void* stream) {
+    Plan* p = nullptr;
+    int rc = came_shard_prepare(hp, step, n, ts, sh, st, nullptr, false, conf, true, ws, ws_bytes, &p);
+    if (rc || n == 0 || p->n == 0) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    float* w = static_cast<float*>(ws);
+    auto tab = [&](int l) { return Table{p->desc, p->items[l], w}; };
+    PassTimer pt(s);
+    launch_conf_fold(tab(kListConf), p->count[kListConf], conf, hp->beta3, s);
+    pt.mark(kPassFinalize);
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame2, 0, conf, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
+                                              hp->lr}, s);
+    pt.mark(kPassScalars);
+    launch_came_apply(tab(kListAll), p->count[kListAll], p->storage, s);
+    pt.mark(kPassCameApply);
+    return launch_status("came shard apply launch");
 }
 
 }  // extern "C"

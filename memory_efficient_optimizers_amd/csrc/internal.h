@@ -98,6 +98,7 @@ struct TDesc {
     // elements when flat).
     int64_t part;
     int64_t total;
+    int64_t part2;    // CAME: the tensor's record of confidence sums (second exchange)
 };
 
 // One launch: its (tensor, local tile) items and the shared descriptors.
@@ -550,5 +551,10 @@ void launch_shard_partials(const Table& t, int64_t n, float* partials, int32_t n
 void launch_shard_fold(const Table& t, int64_t n, const float* partials, double beta, hipStream_t s);
 // Zero-fills records (x = first float, y = length) of tensors a rank holds none of.
 void launch_zero_records(const int2* items, int64_t n, float* partials, hipStream_t s);
+// CAME's second exchange: the shard's column sums of the instability and the sum
+// of its new confidence row statistic; then their fold into the replicated
+// confidence column statistic.
+void launch_conf_partials(const Table& t, int64_t n, float* conf, hipStream_t s);
+void launch_conf_fold(const Table& t, int64_t n, const float* conf, double beta, hipStream_t s);
 
 }  // namespace meo

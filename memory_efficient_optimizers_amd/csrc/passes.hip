@@ -520,10 +520,16 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
 
     if (a.mode == kScalCame2) {
         // Confidence statistic (tiled layout for every factored tensor): per-matrix
-        // lr * sqrt(mean of its row statistic).
+        // lr * sqrt(mean of its row statistic); in a row-sharded step the mean comes
+        // from the reduced confidence record (a.partials). The decay is written again
+        // so that the apply pass needs nothing from an earlier call.
         if (d.mode == kFlat) return;
+        if (threadIdx.x == 0) stf(scal + kSlotDecay, static_cast<float>(a.wd * a.lr));
+        const float* P2 = a.partials ? a.partials + d.part2 : nullptr;
         for (int b = w; b < d.B; b += kWaves) {
-            const double mr = row_mean_tiled(d, ws, b);
+            const double mr = P2 ? static_cast<double>(ldf(P2 + static_cast<int64_t>(d.B) * d.W + b)) /
+                                       static_cast<double>(d.total)
+                                 : row_mean_tiled(d, ws, b);
             if (lane == 0) stf(bs + d.B + b, static_cast<float>(a.lr * sqrt(mr)));
         }
         return;

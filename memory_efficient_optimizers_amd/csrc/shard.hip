@@ -108,6 +108,58 @@ void launch_shard_fold(const Table& t, int64_t n, const float* partials, double 
                                   beta);
 }
 
+// CAME, after the moment pass on the shard's rows: items (tensor, matrix b and
+// 256-column chunk). Column sums of E = (U - M)^2 + eps2 over the shard's row tiles,
+// and (chunk 0) the sum of the new confidence row statistic, which the finalize
+// pass left per 256-row chunk in sumr. Record: [B][W] sums of E, [B] sums of Rr.
+__global__ __launch_bounds__(kThreads) void k_conf_partials(Table t, float* conf) {
+    __shared__ double lds[kWaves];
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    const float* ws = t.ws;
+    float* out = conf + d.part2;
+    const int chunks = (d.W + kThreads - 1) / kThreads;
+    const int b = it.y / chunks, ch = it.y - b * chunks;
+    const int col = ch * kThreads + threadIdx.x;
+    if (col < d.W) {
+        const float* cp = ws + d.colpart + static_cast<int64_t>(b) * d.tr * d.W + col;
+        double e = 0.0;
+        for (int rt = 0; rt < d.tr; ++rt) e += static_cast<double>(ldf(cp + static_cast<int64_t>(rt) * d.W));
+        stf(out + static_cast<int64_t>(b) * d.W + col, static_cast<float>(e));
+    }
+    if (ch == 0) {  // block-uniform
+        const float* sr = ws + d.sumr + static_cast<int64_t>(b) * d.nrc;
+        double r = 0.0;
+        for (int j = threadIdx.x; j < d.nrc; j += kThreads) r += static_cast<double>(ldf(sr + j));
+        r = block_sum_d(r, lds);
+        if (threadIdx.x == 0) stf(out + static_cast<int64_t>(d.B) * d.W + b, static_cast<float>(r));
+    }
+}
+
+void launch_conf_partials(const Table& t, int64_t n, float* conf, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_conf_partials, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, conf);
+}
+
+// CAME, from the confidence totals: Rc_j <- beta3 Rc_j + (1 - beta3) (sum of E_j
+// over all rows) / H.
+__global__ __launch_bounds__(kThreads) void k_conf_fold(Table t, const float* conf, double beta) {
+    const int2 it = t.items[blockIdx.x];
+    const TDesc d = t.desc[it.x];
+    const int chunks = (d.W + kThreads - 1) / kThreads;
+    const int b = it.y / chunks, ch = it.y - b * chunks;
+    const int col = ch * kThreads + threadIdx.x;
+    if (col >= d.W) return;
+    float* dst = d.rc + static_cast<int64_t>(b) * d.W + col;
+    const double mean = static_cast<double>(ldf(conf + d.part2 + static_cast<int64_t>(b) * d.W + col)) /
+                        static_cast<double>(d.total);
+    const double cnew = beta != 0.0 ? beta * static_cast<double>(ldf(dst)) + (1.0 - beta) * mean : mean;
+    stf(dst, static_cast<float>(cnew));
+}
+
+void launch_conf_fold(const Table& t, int64_t n, const float* conf, double beta, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_conf_fold, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, conf, beta);
+}
+
 __global__ __launch_bounds__(kThreads) void k_zero_records(const int2* items, float* partials) {
     const int2 r = items[blockIdx.x];
     for (int i = threadIdx.x; i < r.y; i += kThreads) stf(partials + r.x + i, 0.0f);

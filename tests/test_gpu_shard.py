@@ -60,13 +60,14 @@ def _ranges(opt, shape, nranks):
     ("adafactor", {}),
     ("adafactor", {"scale_parameter": False, "beta1": 0.5, "clip_threshold": 0.3}),
     ("lamb", {"weight_decay": 0.01}),
+    ("came", {"lr": 2e-4, "weight_decay": 0.05}),
 ])
 def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
     wl = workloads.custom(f"shard_{opt}", opt, SHAPES, hparams=hp, grad_dtype=torch.bfloat16,
                           grad_scaling="rowcol" if opt != "lamb" else "row")
     full = workloads.init_params(wl, "cuda")
     scales = workloads.grad_scales(wl, "cuda")
-    hps = (_lib.adafactor_hparams if opt == "adafactor" else _lib.lamb_hparams)(**hp)
+    hps = {"adafactor": _lib.adafactor_hparams, "lamb": _lib.lamb_hparams, "came": _lib.came_hparams}[opt](**hp)
     beta1 = hp.get("beta1") is not None or opt == "lamb"
     ranges = [_ranges(opt, tuple(p.shape), nranks) for p in full]
     totals = [tot for _, tot in ranges]
@@ -76,11 +77,13 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
         sts = []
         for k, p in enumerate(ps):
             st = _lib.init_state(opt, p, beta1=beta1)
-            if "exp_avg_sq_col" in st:  # the column statistic is kept whole on every rank
-                st["exp_avg_sq_col"] = torch.zeros(full[k].shape[:-2] + full[k].shape[-1:], device="cuda")
+            for key in ("exp_avg_sq_col", "exp_avg_res_col"):  # column statistics are kept whole on every rank
+                if key in st:
+                    st[key] = torch.zeros(full[k].shape[:-2] + full[k].shape[-1:], device="cuda")
             sts.append(st)
         ranks.append({"params": ps, "states": sts})
     size = getattr(_lib, f"meo_{opt}_partials_size")(ranks[0]["params"], ranks[0]["params"])
+    csize = _lib.meo_came_confidence_size(ranks[0]["params"], ranks[0]["params"]) if opt == "came" else 0
     stats = getattr(_lib, f"meo_{opt}_shard_stats")
     apply = getattr(_lib, f"meo_{opt}_shard_apply")
     ox = [to64(p) for p in full]
@@ -98,6 +101,15 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
             parts.append(part)
         reduced = torch.stack(parts).sum(0)  # the all-reduce
         assert torch.isfinite(reduced).all()
+        if opt == "came":  # the second exchange: the confidence sums
+            confs = []
+            for rk in ranks:
+                conf = torch.full((max(csize, 1),), float("nan"), device="cuda")
+                _lib.meo_came_shard_moment(hps, t, rk["params"], rk["grads"], totals, rk["states"], reduced, conf,
+                                           rk["ws"])
+                confs.append(conf)
+            reduced = torch.stack(confs).sum(0)
+            assert torch.isfinite(reduced[:csize]).all()
         for rk in ranks:
             apply(hps, t, rk["params"], rk["grads"], totals, rk["states"], reduced, rk["ws"])
         torch.cuda.synchronize()
@@ -109,14 +121,14 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
             def whole(key):
                 pieces = [rk["states"][k][key] if key != "param" else rk["params"][k] for rk in ranks]
                 if fac:
-                    if key == "exp_avg_sq_row":
+                    if key in ("exp_avg_sq_row", "exp_avg_res_row"):
                         return torch.cat(pieces, dim=-1)
                     return torch.cat(pieces, dim=-2)
                 return torch.cat([p.reshape(-1) for p in pieces]).reshape(spec.shape)
 
             errs = {"param": output_err("param", to64(whole("param")), ox[k])}
             for key in ost[k]:
-                if key == "exp_avg_sq_col":
+                if key in ("exp_avg_sq_col", "exp_avg_res_col"):
                     cols = [rk["states"][k][key] for rk, (r0, r1) in zip(ranks, ranges[k][0]) if r1 > r0]
                     for c in cols[1:]:
                         assert torch.equal(c, cols[0]), "ranks disagree on the column statistic"
@@ -127,6 +139,12 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
             print(f"  {opt} N={nranks} step {t} {spec.name} {tuple(spec.shape)}: worst {errs[worst]:.3e} ({worst})",
                   flush=True)
             assert errs[worst] <= TOL_F32, (t, spec.shape, worst, errs[worst])
+
+
+def test_came_confidence_record_layout():
+    """CAME's second record: B x (W + 1) floats per factored tensor, none for 1-D."""
+    ps = [torch.zeros(s, device="cuda") for s in ((129, 1024), (300,), (2, 3, 72, 136))]
+    assert _lib.meo_came_confidence_size(ps, ps) == 1 * 1025 + 0 + 6 * 137
 
 
 def test_shard_of_the_whole_is_the_whole_step():
