@@ -1,5 +1,8 @@
 """fp64 oracle of the optimizer step (test infrastructure only).
 
+``oracle.optimizers``: Adafactor, CAME, LAMB. ``oracle.galore``: the GaLore step
+(low-rank projected AdamW with a periodic SVD refresh of the projector).
+
 Only the test suite, the package smoke check and the bench's CPU-baseline leg may
 import this package. It is independent of the HIP library: no shared code,
 headers, helpers or constants.
