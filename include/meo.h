@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MEO_VERSION 3
+#define MEO_VERSION 4
 
 /* Return codes. */
 #define MEO_OK          0
@@ -338,6 +338,74 @@ int    meo_lamb_shard_apply(const meo_lamb_hparams* hp, int64_t step, int32_t n,
                             const meo_lamb_state* states, const float* partials,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* -------------------------------------------------------------------- GaLore */
+
+/* GaLore: AdamW on a low-rank projection of each 2-D gradient (Colossal-AI
+ * distributed-optimizers page, section on GaLore's special configuration, with
+ * its table of group fields; ms-swift page, section on low-rank projection).
+ *
+ * A tensor with ndim == 2 (batch 1) is projected. With m = rows, n = cols,
+ * d = min(m, n), D = max(m, n) and r = min(rank, d) (the effective rank):
+ *   - every update_proj_gap steps, at steps t with (t - 1) % update_proj_gap == 0,
+ *     the projector U (d x r, orthonormal columns) is recomputed from the current
+ *     gradient: the leading r right singular vectors of G when m >= n, the leading
+ *     left singular vectors when m < n (proj_type "std": the shorter side), each
+ *     signed so that its entry of largest magnitude is positive;
+ *   - project(): R = G U (m >= n) or R = G^T U (m < n), D x r;
+ *   - AdamW on R: exp_avg <- b1 exp_avg + (1 - b1) R, exp_avg_sq <- b2 exp_avg_sq
+ *     + (1 - b2) R^2, N = (exp_avg / (1 - b1^t)) / (sqrt(exp_avg_sq / (1 - b2^t)) + eps);
+ *   - project_back() and update: X <- X (1 - lr wd) - lr scale (N U^T) for m >= n,
+ *     X <- X (1 - lr wd) - lr scale (U N^T) for m < n.
+ * Every other tensor takes the same AdamW update on its elements, without scale.
+ * The moments persist across projector refreshes.
+ *
+ * Storage of a projected tensor: grad bf16 (MEO_EDTYPE otherwise; the products
+ * run on bf16 matrix cores with fp32 accumulation), param fp32 or bf16,
+ * state_dtype MEO_F32; exp_avg and exp_avg_sq float32 [D][r]; the projector in
+ * bf16 (rounded to nearest even) twice, as `projector` [d][r] and as its
+ * transpose `projector_t` [r][d], both written by the refresh and read by every
+ * step. N is split into two bf16 planes (its nearest bf16 and the bf16 of the
+ * remainder) for the back-projection. r must not exceed 256 (MEO_EINVAL).
+ * Non-projected tensors: param and grad fp32 or bf16, exp_avg and exp_avg_sq
+ * float32 [numel], projector pointers NULL. All states start at zero.
+ *
+ * Defaults (meo_galore_defaults): rank 256, update_proj_gap 200, scale 0.25
+ * (the page's table); lr 1e-3, betas (0.9, 0.999), eps 1e-8, weight_decay 0 (the
+ * pages name these fields without values). Errors (MEO_EINVAL): lr < 0, a beta
+ * outside [0, 1), eps < 0, rank < 1, update_proj_gap < 1, non-finite values.
+ */
+typedef struct meo_galore_hparams {
+    double  lr;
+    double  beta1, beta2;
+    double  eps;
+    double  weight_decay;
+    int32_t rank;
+    int32_t update_proj_gap;
+    double  scale;
+} meo_galore_hparams;
+
+typedef struct meo_galore_state {
+    float* exp_avg;      /* [D][r] projected, [numel] otherwise                */
+    float* exp_avg_sq;   /* [D][r] projected, [numel] otherwise                */
+    void*  projector;    /* bf16 [d][r]; NULL for tensors that are not 2-D      */
+    void*  projector_t;  /* bf16 [r][d]; NULL for tensors that are not 2-D      */
+} meo_galore_state;
+
+void    meo_galore_defaults(meo_galore_hparams* hp);
+/* Effective rank r of a tensor (0 when it is not projected). */
+int32_t meo_galore_rank(const meo_galore_hparams* hp, const meo_tensor* tensor);
+size_t  meo_galore_workspace_size(const meo_galore_hparams* hp, int32_t n, const meo_tensor* tensors);
+int     meo_galore_validate(const meo_galore_hparams* hp, int64_t step, int32_t n, const meo_tensor* tensors,
+                            const meo_galore_state* states);
+/* One step of the list; refreshes the projectors first when the step is due. */
+int     meo_galore_step(const meo_galore_hparams* hp, int64_t step, int32_t n, const meo_tensor* tensors,
+                        const meo_galore_state* states, void* workspace, size_t workspace_bytes, void* stream);
+/* Recomputes the projectors of the list's 2-D tensors from their gradients, as a
+ * due step does before projecting, and changes nothing else. */
+int     meo_galore_refresh(const meo_galore_hparams* hp, int32_t n, const meo_tensor* tensors,
+                           const meo_galore_state* states, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* ----------------------------------------------------------------- utilities */
 
 /* Message of the last failing call on this thread ("" if none). The pointer
@@ -361,7 +429,7 @@ int meo_version(void);
  * launches[id] (both arrays of MEO_NUM_PASSES entries, caller-owned host
  * memory, zeroed by the caller), and forgets the events. Returns MEO_OK or
  * MEO_EHIP. Not for use under graph capture. */
-#define MEO_NUM_PASSES 11
+#define MEO_NUM_PASSES 14
 int         meo_profile_enable(int on);
 const char* meo_pass_name(int id);
 int         meo_profile_collect(double* total_ms, int64_t* launches);

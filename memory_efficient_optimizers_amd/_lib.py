@@ -39,8 +39,10 @@ EXPORTS = [
     "meo_lamb_partials_size", "meo_lamb_shard_stats", "meo_lamb_shard_apply",
     "meo_came_partials_size", "meo_came_confidence_size", "meo_came_shard_stats", "meo_came_shard_moment",
     "meo_came_shard_apply",
+    "meo_galore_defaults", "meo_galore_rank", "meo_galore_workspace_size", "meo_galore_validate",
+    "meo_galore_step", "meo_galore_refresh",
 ]
-MEO_NUM_PASSES = 11
+MEO_NUM_PASSES = 14
 
 
 class MeoError(RuntimeError):
@@ -93,6 +95,17 @@ class meo_lamb_hparams(ctypes.Structure):
 
 class meo_lamb_state(ctypes.Structure):
     _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq", c_void_p), ("exp_avg_scale", c_void_p)]
+
+
+class meo_galore_hparams(ctypes.Structure):
+    _fields_ = [("lr", c_double), ("beta1", c_double), ("beta2", c_double), ("eps", c_double),
+                ("weight_decay", c_double), ("rank", c_int32), ("update_proj_gap", c_int32),
+                ("scale", c_double)]
+
+
+class meo_galore_state(ctypes.Structure):
+    _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq", c_void_p), ("projector", c_void_p),
+                ("projector_t", c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -153,6 +166,19 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.meo_pass_name.restype = ctypes.c_char_p
     lib.meo_profile_collect.argtypes = [ctypes.POINTER(c_double), ctypes.POINTER(c_int64)]
     lib.meo_profile_collect.restype = ctypes.c_int
+    GH, GS = ctypes.POINTER(meo_galore_hparams), ctypes.POINTER(meo_galore_state)
+    lib.meo_galore_defaults.argtypes = [GH]
+    lib.meo_galore_defaults.restype = None
+    lib.meo_galore_rank.argtypes = [GH, T]
+    lib.meo_galore_rank.restype = c_int32
+    lib.meo_galore_workspace_size.argtypes = [GH, c_int32, T]
+    lib.meo_galore_workspace_size.restype = c_size_t
+    lib.meo_galore_validate.argtypes = [GH, c_int64, c_int32, T, GS]
+    lib.meo_galore_validate.restype = ctypes.c_int
+    lib.meo_galore_step.argtypes = [GH, c_int64, c_int32, T, GS, c_void_p, c_size_t, c_void_p]
+    lib.meo_galore_step.restype = ctypes.c_int
+    lib.meo_galore_refresh.argtypes = [GH, c_int32, T, GS, c_void_p, c_size_t, c_void_p]
+    lib.meo_galore_refresh.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -232,6 +258,8 @@ def _states(cls, keys, states: Sequence[Dict[str, torch.Tensor]]):
             t = st.get(k)
             if t is not None and t.dtype != torch.float32 and not (k == "exp_avg" and t.dtype in _STATE_DTYPE):
                 raise TypeError(f"state {k} must be float32" + (", bfloat16 or int8" if k == "exp_avg" else ""))
+            if t is not None and not t.is_contiguous():
+                raise ValueError(f"state {k} must be contiguous (row-major)")
         arr[i] = cls(*[_ptr(st.get(k)) for k in keys])
     return arr
 
@@ -265,6 +293,14 @@ def lamb_hparams(lr=1e-3, betas=(0.9, 0.999), eps=1e-6, weight_decay=0.0,
                  bias_correction=True) -> meo_lamb_hparams:
     return meo_lamb_hparams(float(lr), float(betas[0]), float(betas[1]), float(eps),
                             float(weight_decay), int(bool(bias_correction)), 0)
+
+
+def galore_hparams(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, rank=256, update_proj_gap=200,
+                   scale=0.25, proj_type="std") -> meo_galore_hparams:
+    if proj_type != "std":
+        raise ValueError("only proj_type='std' is supported")
+    return meo_galore_hparams(float(lr), float(betas[0]), float(betas[1]), float(eps), float(weight_decay),
+                              int(rank), int(update_proj_gap), float(scale))
 
 
 def meo_adafactor_defaults() -> meo_adafactor_hparams:
@@ -493,6 +529,76 @@ class PreparedStep:
     def __call__(self, step: int, stream=None) -> None:
         _check(self.fn(ctypes.byref(self.hp), step, self.n, self.tensors, self.states, self.ws,
                        self.ws_bytes, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- GaLore
+
+GALORE_KEYS = ["exp_avg", "exp_avg_sq", "projector", "projector_t"]
+
+
+def meo_galore_defaults() -> meo_galore_hparams:
+    hp = meo_galore_hparams()
+    load().meo_galore_defaults(ctypes.byref(hp))
+    return hp
+
+
+def _galore_states(states):
+    arr = (meo_galore_state * max(len(states), 1))()
+    for i, st in enumerate(states):
+        for k in ("exp_avg", "exp_avg_sq"):
+            if st[k].dtype != torch.float32:
+                raise TypeError(f"GaLore state {k} must be float32")
+        for k in ("projector", "projector_t"):
+            if st.get(k) is not None and st[k].dtype != torch.bfloat16:
+                raise TypeError(f"GaLore state {k} must be bfloat16")
+        for k, t in st.items():
+            if not t.is_contiguous():
+                raise ValueError(f"GaLore state {k} must be contiguous (row-major)")
+        arr[i] = meo_galore_state(*[_ptr(st.get(k)) for k in GALORE_KEYS])
+    return arr
+
+
+def meo_galore_rank(hp, param) -> int:
+    return int(load().meo_galore_rank(ctypes.byref(hp), ctypes.byref(tensor_struct(param, param))))
+
+
+def meo_galore_workspace_size(hp, params, grads) -> int:
+    return int(load().meo_galore_workspace_size(ctypes.byref(hp), len(params), _tensors(params, grads)))
+
+
+def meo_galore_validate(hp, step, params, grads, states) -> None:
+    _check(load().meo_galore_validate(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+                                      _galore_states(states)))
+
+
+def meo_galore_step(hp, step, params, grads, states, workspace=None, stream=None) -> None:
+    ws, nb = _ws(workspace)
+    _check(load().meo_galore_step(ctypes.byref(hp), step, len(params), _tensors(params, grads),
+                                  _galore_states(states), ws, nb, _stream(stream)))
+
+
+def meo_galore_refresh(hp, params, grads, states, workspace=None, stream=None) -> None:
+    ws, nb = _ws(workspace)
+    _check(load().meo_galore_refresh(ctypes.byref(hp), len(params), _tensors(params, grads),
+                                     _galore_states(states), ws, nb, _stream(stream)))
+
+
+def galore_state_shapes(shape, rank: int) -> Dict[str, tuple]:
+    """Shapes of one parameter's GaLore states (meo.h): 2-D parameters keep
+    [max(m, n)][r] moments and the projector [min(m, n)][r] with its transpose."""
+    shape = tuple(shape)
+    if len(shape) == 2 and shape[0] > 0 and shape[1] > 0:
+        r = min(rank, min(shape))
+        return {"exp_avg": (max(shape), r), "exp_avg_sq": (max(shape), r),
+                "projector": (min(shape), r), "projector_t": (r, min(shape))}
+    return {"exp_avg": shape, "exp_avg_sq": shape}
+
+
+def galore_init_state(param: torch.Tensor, rank: int) -> Dict[str, torch.Tensor]:
+    """Zero GaLore states for one parameter (projectors in bfloat16)."""
+    return {k: torch.zeros(s, dtype=torch.bfloat16 if k.startswith("projector") else torch.float32,
+                           device=param.device)
+            for k, s in galore_state_shapes(param.shape, rank).items()}
 
 
 # ----------------------------------------------------------------------------- state allocation

@@ -19,6 +19,7 @@
 
 #include "meo.h"
 #include "internal.h"
+#include "galore.h"
 
 using namespace meo;
 
@@ -32,6 +33,8 @@ int fail(int code, const std::string& msg) {
 }
 
 enum Op { kOpAdafactor = 0, kOpCame = 1, kOpLamb = 2 };
+
+void release_galore_plans();  // GaLore launch tables (defined with the GaLore entry points)
 
 uintptr_t elem_bytes(int32_t dtype) { return dtype == MEO_F32 ? 4 : (dtype == MEO_BF16 ? 2 : 1); }
 
@@ -649,11 +652,13 @@ std::vector<StatePtrs> state_ptrs(int op, int32_t n, const void* states) {
 // ----------------------------------------------------------------------------- pass timing
 
 enum Pass { kPassStats = 0, kPassFinalize, kPassRms, kPassScalars, kPassAfApply, kPassCameMom,
-            kPassCameApply, kPassLambMoments, kPassLambApply, kPassStatsWide, kPassStatsTiled, kPassCount };
+            kPassCameApply, kPassLambMoments, kPassLambApply, kPassStatsWide, kPassStatsTiled,
+            kPassGaProject, kPassGaBack, kPassGaAdamw, kPassCount };
 static_assert(kPassCount == MEO_NUM_PASSES, "pass table");
 const char* const kPassNames[kPassCount] = {"stats", "finalize", "rms", "scalars", "adafactor_apply",
                                             "came_mom", "came_apply", "lamb_moments", "lamb_apply",
-                                            "stats_wide", "stats_tiled"};
+                                            "stats_wide", "stats_tiled", "galore_project", "galore_back",
+                                            "galore_adamw"};
 
 struct ProfRec { int pass; hipEvent_t a, b; };
 std::mutex g_prof_mu;
@@ -747,6 +752,7 @@ void meo_release_plans(void) {
     std::lock_guard<std::mutex> lock(g_mu);
     for (Plan* p : g_plans) free_plan(p);
     g_plans.clear();
+    release_galore_plans();
 }
 
 // ----------------------------------------------------------------------------- Adafactor
@@ -1299,6 +1305,379 @@ int meo_came_shard_apply(const meo_came_hparams* hp, int64_t step, int32_t n, co
     launch_came_apply(tab(kListAll), p->count[kListAll], p->storage, s);
     pt.mark(kPassCameApply);
     return launch_status("came shard apply launch");
+}
+
+// ----------------------------------------------------------------------------- GaLore
+
+namespace {
+
+enum GaList { kGaProjR = 0, kGaProjL, kGaBackR, kGaBackL, kGaFlat, kGaListCount };
+
+struct GaPlan {
+    std::vector<uint8_t> key;
+    int device = 0;
+    void* mem = nullptr;  // [GDesc right..., left...][TDesc flat...][item tables]
+    const GDesc* gdesc = nullptr;
+    const TDesc* fdesc = nullptr;
+    const int2* items[kGaListCount] = {};
+    int64_t count[kGaListCount] = {};
+};
+std::list<GaPlan*> g_ga_plans;  // most recently used first, under g_mu
+
+void release_galore_plans() {  // caller holds g_mu
+    for (GaPlan* p : g_ga_plans) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        if (cur != p->device) (void)hipSetDevice(p->device);
+        (void)hipFree(p->mem);
+        if (cur != p->device) (void)hipSetDevice(cur);
+        delete p;
+    }
+    g_ga_plans.clear();
+}
+
+bool ga_projected(const meo_tensor& t) { return t.ndim == 2 && t.rows > 0 && t.cols > 0; }
+
+int32_t ga_rank(const meo_galore_hparams* hp, const meo_tensor& t) {
+    if (!ga_projected(t)) return 0;
+    return static_cast<int32_t>(std::min<int64_t>(hp->rank, std::min(t.rows, t.cols)));
+}
+
+// Workspace: per projected tensor the two bf16 planes of N, [D][r] each, every
+// plane at a 256-byte boundary. Offsets in bytes.
+int64_t ga_layout(const meo_galore_hparams* hp, int32_t n, const meo_tensor* ts, std::vector<int64_t>* offs) {
+    int64_t off = 0;
+    if (offs) offs->assign(n, -1);
+    for (int32_t k = 0; k < n; ++k) {
+        const int32_t r = ga_rank(hp, ts[k]);
+        if (!r) continue;
+        if (offs) (*offs)[k] = off;
+        const int64_t plane = (std::max(ts[k].rows, ts[k].cols) * r * 2 + 255) / 256 * 256;
+        off += 2 * plane;
+    }
+    return off;
+}
+
+int check_galore_hp(const meo_galore_hparams* hp) {
+    if (!hp) return fail(MEO_ENULL, "hparams is NULL");
+    if (!finite(hp->lr) || !finite(hp->beta1) || !finite(hp->beta2) || !finite(hp->eps) ||
+        !finite(hp->weight_decay) || !finite(hp->scale))
+        return fail(MEO_EINVAL, "non-finite hyperparameter");
+    if (hp->lr < 0.0) return fail(MEO_EINVAL, "Invalid learning rate: " + std::to_string(hp->lr));
+    if (hp->beta1 < 0.0 || hp->beta1 >= 1.0 || hp->beta2 < 0.0 || hp->beta2 >= 1.0)
+        return fail(MEO_EINVAL, "betas must lie in [0, 1)");
+    if (hp->eps < 0.0) return fail(MEO_EINVAL, "Invalid epsilon value: " + std::to_string(hp->eps));
+    if (hp->rank < 1) return fail(MEO_EINVAL, "rank must be >= 1");
+    if (hp->update_proj_gap < 1) return fail(MEO_EINVAL, "update_proj_gap must be >= 1");
+    return MEO_OK;
+}
+
+int check_galore_tensors(const meo_galore_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                         const meo_galore_state* st) {
+    if (step < 1) return fail(MEO_EINVAL, "step must be >= 1 (1-based index of the step being taken)");
+    if (n < 0) return fail(MEO_EINVAL, "negative tensor count");
+    if (n == 0) return MEO_OK;
+    if (!ts) return fail(MEO_ENULL, "tensors is NULL");
+    if (!st) return fail(MEO_ENULL, "states is NULL");
+    int64_t blocks[kGaListCount] = {};
+    for (int32_t k = 0; k < n; ++k) {
+        const meo_tensor& t = ts[k];
+        const std::string who = "tensor " + std::to_string(k) + ": ";
+        if (t.batch < 0 || t.rows < 0 || t.cols < 0 || t.ndim < 0)
+            return fail(MEO_ESHAPE, who + "negative batch, rows, cols or ndim");
+        int64_t numel;
+        if (overflow_numel(t, &numel)) return fail(MEO_ESHAPE, who + "too many elements");
+        if (t.ndim <= 1 && numel > 0 && (t.batch != 1 || t.rows != 1))
+            return fail(MEO_ESHAPE, who + "a tensor with ndim <= 1 must have batch == rows == 1");
+        if (t.ndim == 2 && numel > 0 && t.batch != 1) return fail(MEO_ESHAPE, who + "a 2-D tensor has batch 1");
+        if (t.param_dtype != MEO_F32 && t.param_dtype != MEO_BF16)
+            return fail(MEO_EDTYPE, who + "param_dtype must be MEO_F32 or MEO_BF16");
+        if (t.grad_dtype != MEO_F32 && t.grad_dtype != MEO_BF16)
+            return fail(MEO_EDTYPE, who + "grad_dtype must be MEO_F32 or MEO_BF16");
+        if (t.state_dtype != MEO_F32) return fail(MEO_EDTYPE, who + "GaLore states are float32 (state_dtype MEO_F32)");
+        if (numel == 0) continue;
+        if (!t.param) return fail(MEO_ENULL, who + "param is NULL");
+        if (!t.grad) return fail(MEO_ENULL, who + "grad is NULL");
+        if (reinterpret_cast<uintptr_t>(t.param) % (t.param_dtype == MEO_BF16 ? 2 : 4))
+            return fail(MEO_EALIGN, who + "param misaligned for its dtype");
+        if (reinterpret_cast<uintptr_t>(t.grad) % (t.grad_dtype == MEO_BF16 ? 2 : 4))
+            return fail(MEO_EALIGN, who + "grad misaligned for its dtype");
+        const meo_galore_state& s = st[k];
+        if (!s.exp_avg) return fail(MEO_ENULL, who + "exp_avg is NULL");
+        if (!s.exp_avg_sq) return fail(MEO_ENULL, who + "exp_avg_sq is NULL");
+        if (reinterpret_cast<uintptr_t>(s.exp_avg) % 4 || reinterpret_cast<uintptr_t>(s.exp_avg_sq) % 4)
+            return fail(MEO_EALIGN, who + "exp_avg or exp_avg_sq misaligned");
+        if (ga_projected(t)) {
+            if (t.grad_dtype != MEO_BF16)
+                return fail(MEO_EDTYPE, who + "a projected (2-D) tensor needs a bf16 gradient");
+            if (t.rows > kMaxDim || t.cols > kMaxDim) return fail(MEO_ESHAPE, who + "rows or cols exceed 2^31 - 1");
+            const int32_t r = ga_rank(hp, t);
+            if (r > kGaWide) return fail(MEO_EINVAL, who + "effective rank " + std::to_string(r) + " exceeds 256");
+            if (!s.projector || !s.projector_t) return fail(MEO_ENULL, who + "projector or projector_t is NULL");
+            if (reinterpret_cast<uintptr_t>(s.projector) % 2 || reinterpret_cast<uintptr_t>(s.projector_t) % 2)
+                return fail(MEO_EALIGN, who + "projector misaligned");
+            const int64_t D = std::max(t.rows, t.cols);
+            blocks[kGaProjR] += ceil_div(D, kGaTile);
+            blocks[kGaBackR] += ceil_div(t.rows, kGaTile) * ceil_div(t.cols, kGaTile);
+        } else {
+            blocks[kGaFlat] += ceil_div(numel, kFlatTile);
+        }
+    }
+    for (int64_t b : blocks)
+        if (b > 0x7fffffffLL) return fail(MEO_ESHAPE, "the tensor list needs more than 2^31 blocks in one pass");
+    return MEO_OK;
+}
+
+int check_galore_memory(const meo_galore_hparams* hp, int32_t n, const meo_tensor* ts, const meo_galore_state* st,
+                        int dev) {
+    for (int32_t k = 0; k < n; ++k) {
+        const meo_tensor& t = ts[k];
+        int64_t numel = 0;
+        overflow_numel(t, &numel);
+        if (numel == 0) continue;
+        const std::string who = "tensor " + std::to_string(k) + ": ";
+        const size_t ne = static_cast<size_t>(numel);
+        const int32_t r = ga_rank(hp, t);
+        const size_t mom = r ? static_cast<size_t>(std::max(t.rows, t.cols)) * r : ne;
+        struct Range { const void* p; size_t bytes; const char* name; };
+        std::vector<Range> rs = {{t.param, ne * (t.param_dtype == MEO_BF16 ? 2 : 4), "param"},
+                                 {t.grad, ne * (t.grad_dtype == MEO_BF16 ? 2 : 4), "grad"},
+                                 {st[k].exp_avg, mom * 4, "exp_avg"}, {st[k].exp_avg_sq, mom * 4, "exp_avg_sq"}};
+        if (r) {
+            const size_t pu = static_cast<size_t>(std::min(t.rows, t.cols)) * r * 2;
+            rs.push_back({st[k].projector, pu, "projector"});
+            rs.push_back({st[k].projector_t, pu, "projector_t"});
+        }
+        for (const Range& rg : rs) {
+            const int rc = check_device_range(rg.p, rg.bytes, dev, who + rg.name, MEO_EMEMORY);
+            if (rc) return rc;
+        }
+    }
+    return MEO_OK;
+}
+
+int check_galore_workspace(const meo_galore_hparams* hp, int32_t n, const meo_tensor* ts, void* ws, size_t bytes) {
+    const int64_t need = ga_layout(hp, n, ts, nullptr);
+    if (need == 0) return MEO_OK;
+    if (!ws) return fail(MEO_EWORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MEO_EWORKSPACE, "workspace not 256-byte aligned");
+    if (bytes < static_cast<size_t>(need))
+        return fail(MEO_EWORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MEO_EHIP, "hipGetDevice failed");
+    }
+    return check_device_range(ws, bytes, dev, "workspace", MEO_EWORKSPACE);
+}
+
+GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tensor* ts, const meo_galore_state* st,
+                        void* ws, int* rc) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        *rc = fail(MEO_EHIP, "hipGetDevice failed");
+        return nullptr;
+    }
+    std::vector<uint8_t> key(sizeof(int) * 3 + sizeof(void*) + n * (sizeof(meo_tensor) + sizeof(meo_galore_state)));
+    {
+        uint8_t* w = key.data();
+        const int hdr[3] = {n, dev, hp->rank};
+        std::memcpy(w, hdr, sizeof hdr); w += sizeof hdr;
+        std::memcpy(w, &ws, sizeof ws); w += sizeof ws;
+        std::memcpy(w, ts, n * sizeof(meo_tensor)); w += n * sizeof(meo_tensor);
+        std::memcpy(w, st, n * sizeof(meo_galore_state));
+    }
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (auto it = g_ga_plans.begin(); it != g_ga_plans.end(); ++it) {
+        if ((*it)->key == key) {
+            GaPlan* p = *it;
+            g_ga_plans.erase(it);
+            g_ga_plans.push_front(p);
+            return p;
+        }
+    }
+    *rc = check_galore_memory(hp, n, ts, st, dev);
+    if (*rc) return nullptr;
+    std::vector<int64_t> woff;
+    ga_layout(hp, n, ts, &woff);
+    std::vector<GDesc> right, left;
+    std::vector<TDesc> flat;
+    std::vector<int2> lists[kGaListCount];
+    std::vector<int32_t> kr, kl;  // tensor indices of the right and left descriptors
+    for (int32_t k = 0; k < n; ++k) {
+        const meo_tensor& t = ts[k];
+        int64_t numel = 0;
+        overflow_numel(t, &numel);
+        if (numel == 0) continue;
+        const meo_galore_state& s = st[k];
+        if (ga_projected(t)) {
+            GDesc d;
+            std::memset(&d, 0, sizeof d);
+            d.m = static_cast<int32_t>(t.rows);
+            d.n = static_cast<int32_t>(t.cols);
+            d.D = std::max(d.m, d.n);
+            d.d = std::min(d.m, d.n);
+            d.r = ga_rank(hp, t);
+            d.g = static_cast<const uint16_t*>(t.grad);
+            d.x = t.param;
+            d.xbf16 = t.param_dtype == MEO_BF16;
+            d.em = s.exp_avg;
+            d.ev = s.exp_avg_sq;
+            d.u = static_cast<uint16_t*>(s.projector);
+            d.ut = static_cast<uint16_t*>(s.projector_t);
+            uint8_t* wb = static_cast<uint8_t*>(ws) + woff[k];
+            d.nh = reinterpret_cast<uint16_t*>(wb);
+            d.nl = reinterpret_cast<uint16_t*>(wb + (static_cast<int64_t>(d.D) * d.r * 2 + 255) / 256 * 256);
+            d.vec = aligned16(d.g) && aligned16(d.u) && aligned16(d.ut) && d.n % 8 == 0 && d.d % 8 == 0 &&
+                    d.r % 8 == 0;
+            const bool is_left = d.m < d.n;
+            d.btj = static_cast<int32_t>(is_left ? ceil_div(d.n, kGaTile) : ceil_div(d.n, kGaWide));
+            (is_left ? left : right).push_back(d);
+            (is_left ? kl : kr).push_back(k);
+        } else {
+            TDesc d;
+            std::memset(&d, 0, sizeof d);
+            d.x = t.param;
+            d.g = t.grad;
+            d.m = s.exp_avg;
+            d.v = s.exp_avg_sq;
+            d.numel = numel;
+            d.gbf16 = t.grad_dtype == MEO_BF16;
+            d.xbf16 = t.param_dtype == MEO_BF16;
+            d.vec = aligned16(d.x) && aligned16(d.g) && aligned16(d.m) && aligned16(d.v);
+            const int32_t id = static_cast<int32_t>(flat.size());
+            flat.push_back(d);
+            for (int64_t i = 0; i < ceil_div(numel, kFlatTile); ++i) lists[kGaFlat].push_back(make_int2(id, static_cast<int>(i)));
+        }
+    }
+    // Right descriptors first, then left; the item tables index that array.
+    std::vector<GDesc> gd(right);
+    gd.insert(gd.end(), left.begin(), left.end());
+    for (size_t i = 0; i < gd.size(); ++i) {
+        const GDesc& d = gd[i];
+        const bool is_left = i >= right.size();
+        const int id = static_cast<int>(i);
+        const int64_t pt = ceil_div(d.D, kGaTile);
+        const int64_t bt = is_left ? ceil_div(d.m, kGaWide) * d.btj : ceil_div(d.m, kGaTile) * d.btj;
+        for (int64_t y = 0; y < pt; ++y) lists[is_left ? kGaProjL : kGaProjR].push_back(make_int2(id, static_cast<int>(y)));
+        for (int64_t y = 0; y < bt; ++y) lists[is_left ? kGaBackL : kGaBackR].push_back(make_int2(id, static_cast<int>(y)));
+    }
+    size_t offs[kGaListCount];
+    size_t total = (gd.size() * sizeof(GDesc) + 255) / 256 * 256;
+    const size_t foff = total;
+    total += (flat.size() * sizeof(TDesc) + 255) / 256 * 256;
+    for (int l = 0; l < kGaListCount; ++l) {
+        offs[l] = total;
+        total += (lists[l].size() * sizeof(int2) + 255) / 256 * 256;
+    }
+    total = std::max<size_t>(total, 256);
+    std::vector<uint8_t> host(total, 0);
+    if (!gd.empty()) std::memcpy(host.data(), gd.data(), gd.size() * sizeof(GDesc));
+    if (!flat.empty()) std::memcpy(host.data() + foff, flat.data(), flat.size() * sizeof(TDesc));
+    for (int l = 0; l < kGaListCount; ++l)
+        if (!lists[l].empty()) std::memcpy(host.data() + offs[l], lists[l].data(), lists[l].size() * sizeof(int2));
+    GaPlan* p = new GaPlan;
+    p->key = std::move(key);
+    p->device = dev;
+    if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
+        hipMemcpy(p->mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+        if (p->mem) (void)hipFree(p->mem);
+        delete p;
+        *rc = fail(MEO_EHIP, "could not allocate or upload the launch table");
+        return nullptr;
+    }
+    uint8_t* base = static_cast<uint8_t*>(p->mem);
+    p->gdesc = reinterpret_cast<const GDesc*>(base);
+    p->fdesc = reinterpret_cast<const TDesc*>(base + foff);
+    for (int l = 0; l < kGaListCount; ++l) {
+        p->items[l] = reinterpret_cast<const int2*>(base + offs[l]);
+        p->count[l] = static_cast<int64_t>(lists[l].size());
+    }
+    g_ga_plans.push_front(p);
+    while (g_ga_plans.size() > kMaxPlans) {
+        GaPlan* q = g_ga_plans.back();
+        g_ga_plans.pop_back();
+        (void)hipFree(q->mem);
+        delete q;
+    }
+    return p;
+}
+
+}  // namespace
+
+void meo_galore_defaults(meo_galore_hparams* hp) {
+    if (!hp) return;
+    std::memset(hp, 0, sizeof *hp);
+    hp->lr = 1e-3;
+    hp->beta1 = 0.9;
+    hp->beta2 = 0.999;
+    hp->eps = 1e-8;
+    hp->weight_decay = 0.0;
+    hp->rank = 256;
+    hp->update_proj_gap = 200;
+    hp->scale = 0.25;
+}
+
+int32_t meo_galore_rank(const meo_galore_hparams* hp, const meo_tensor* t) {
+    if (!hp || !t || hp->rank < 1) return 0;
+    return ga_rank(hp, *t);
+}
+
+size_t meo_galore_workspace_size(const meo_galore_hparams* hp, int32_t n, const meo_tensor* ts) {
+    if (!hp || n <= 0 || !ts || hp->rank < 1) return 0;
+    return static_cast<size_t>(ga_layout(hp, n, ts, nullptr));
+}
+
+int meo_galore_validate(const meo_galore_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                        const meo_galore_state* st) {
+    g_err.clear();
+    const int rc = check_galore_hp(hp);
+    if (rc) return rc;
+    return check_galore_tensors(hp, step, n, ts, st);
+}
+
+int meo_galore_refresh(const meo_galore_hparams* hp, int32_t n, const meo_tensor* ts, const meo_galore_state* st,
+                       void* ws, size_t ws_bytes, void* stream) {
+    int rc = meo_galore_validate(hp, 1, n, ts, st);
+    if (rc) return rc;
+    (void)ws; (void)ws_bytes; (void)stream;
+    bool any = false;
+    for (int32_t k = 0; k < n; ++k) any = any || ga_rank(hp, ts[k]) > 0;
+    if (!any) return MEO_OK;
+    return fail(MEO_EINVAL, "projector refresh is not available in this build");
+}
+
+int meo_galore_step(const meo_galore_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                    const meo_galore_state* st, void* ws, size_t ws_bytes, void* stream) {
+    int rc = meo_galore_validate(hp, step, n, ts, st);
+    if (rc) return rc;
+    if (n == 0) return MEO_OK;
+    rc = check_galore_workspace(hp, n, ts, ws, ws_bytes);
+    if (rc) return rc;
+    if ((step - 1) % hp->update_proj_gap == 0) {
+        rc = meo_galore_refresh(hp, n, ts, st, ws, ws_bytes, stream);
+        if (rc) return rc;
+    }
+    GaPlan* p = get_galore_plan(hp, n, ts, st, ws, &rc);
+    if (!p) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const double tt = static_cast<double>(step);
+    const double bc1 = 1.0 - std::pow(hp->beta1, tt), bc2 = 1.0 - std::pow(hp->beta2, tt);
+    GaArgs a{static_cast<float>(hp->beta1), static_cast<float>(hp->beta2), static_cast<float>(1.0 - hp->beta1),
+             static_cast<float>(1.0 - hp->beta2), static_cast<float>(1.0 / bc1), static_cast<float>(1.0 / bc2),
+             static_cast<float>(hp->eps), static_cast<float>(1.0 - hp->lr * hp->weight_decay),
+             static_cast<float>(hp->lr * hp->scale)};
+    PassTimer pt(s);
+    launch_galore_project(GTable{p->gdesc, p->items[kGaProjR]}, p->count[kGaProjR], a, false, s);
+    launch_galore_project(GTable{p->gdesc, p->items[kGaProjL]}, p->count[kGaProjL], a, true, s);
+    pt.mark(kPassGaProject);
+    launch_galore_back(GTable{p->gdesc, p->items[kGaBackR]}, p->count[kGaBackR], a, false, s);
+    launch_galore_back(GTable{p->gdesc, p->items[kGaBackL]}, p->count[kGaBackL], a, true, s);
+    pt.mark(kPassGaBack);
+    a.coef = static_cast<float>(hp->lr);
+    launch_galore_adamw(Table{p->fdesc, p->items[kGaFlat], nullptr}, p->count[kGaFlat], a, s);
+    pt.mark(kPassGaAdamw);
+    return launch_status("galore step launch");
 }
 
 }  // extern "C"

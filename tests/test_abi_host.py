@@ -305,3 +305,67 @@ def test_shard_checks(lib):
     code, msg = _code(_lib.meo_lamb_shard_stats, _lib.lamb_hparams(), 1, ps, gs, [31, 191, 30], lst,
                       torch.zeros(6), None, 0)
     assert code == _lib.MEO_ESHAPE   # 4 x 8 = 32 elements > 31
+
+
+def test_galore_defaults_are_the_pages(lib):
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "page_defaults.json")))["galore"]
+    h = _lib.meo_galore_defaults()
+    assert (h.rank, h.update_proj_gap, h.scale) == (g["rank"], g["update_proj_gap"], g["scale"])
+    # fields the pages name without values: the readings stated in meo.h
+    assert (h.lr, h.beta1, h.beta2, h.eps, h.weight_decay) == (1e-3, 0.9, 0.999, 1e-8, 0.0)
+
+
+def _ga(shapes, rank=8, gdt=torch.bfloat16):
+    ps = [torch.zeros(s, dtype=torch.float32) for s in shapes]
+    gs = [torch.zeros(s, dtype=gdt) for s in shapes]
+    return ps, gs, [_lib.galore_init_state(p, rank) for p in ps]
+
+
+def test_galore_validation(lib):
+    ps, gs, st = _ga([(16, 40), (40, 16), (9,), (2, 3, 4)])
+    h = _lib.galore_hparams(rank=8)
+    _lib.meo_galore_validate(h, 1, ps, gs, st)
+    assert [_lib.meo_galore_rank(h, p) for p in ps] == [8, 8, 0, 0]
+    assert _lib.meo_galore_rank(_lib.galore_hparams(rank=300), torch.zeros(20, 30)) == 20
+    # workspace: two bf16 planes of [max(m, n)][r] per projected tensor, each 256-byte aligned
+    plane = (40 * 8 * 2 + 255) // 256 * 256
+    assert _lib.meo_galore_workspace_size(h, ps, gs) == 2 * 2 * plane
+    for bad, code in ((dict(lr=-1.0), _lib.MEO_EINVAL), (dict(betas=(1.0, 0.9)), _lib.MEO_EINVAL),
+                      (dict(eps=-1e-8), _lib.MEO_EINVAL), (dict(rank=0), _lib.MEO_EINVAL),
+                      (dict(update_proj_gap=0), _lib.MEO_EINVAL), (dict(scale=float("nan")), _lib.MEO_EINVAL)):
+        assert _code(_lib.meo_galore_validate, _lib.galore_hparams(**dict(dict(rank=8), **bad)), 1, ps, gs, st)[0] == code
+    assert _code(_lib.meo_galore_validate, h, 0, ps, gs, st)[0] == _lib.MEO_EINVAL
+    # a projected tensor needs a bf16 gradient; the flat ones take fp32 too
+    ps2, gs2, st2 = _ga([(16, 40)], gdt=torch.float32)
+    code, msg = _code(_lib.meo_galore_validate, h, 1, ps2, gs2, st2)
+    assert code == _lib.MEO_EDTYPE and "bf16 gradient" in msg
+    ps3, gs3, st3 = _ga([(33,), (2, 3, 4)], gdt=torch.float32)
+    _lib.meo_galore_validate(h, 1, ps3, gs3, st3)
+    # effective rank above 256
+    ps4, gs4, st4 = _ga([(300, 400)], rank=257)
+    assert _code(_lib.meo_galore_validate, _lib.galore_hparams(rank=257), 1, ps4, gs4, st4)[0] == _lib.MEO_EINVAL
+    # missing projector, float32 state dtype only
+    bad = [dict(s) for s in st]
+    del bad[0]["projector_t"]
+    assert _code(_lib.meo_galore_validate, h, 1, ps, gs, bad)[0] == _lib.MEO_ENULL
+    t = _lib._tensors(ps, gs)
+    t[0].state_dtype = _lib.MEO_BF16
+    assert lib.meo_galore_validate(_lib.ctypes.byref(h), 1, len(ps), t, _lib._galore_states(st)) == _lib.MEO_EDTYPE
+    with pytest.raises(TypeError):
+        _lib._galore_states([dict(st[0], projector=st[0]["projector"].float())])
+    # an empty list is a no-op
+    _lib.meo_galore_step(h, 1, [], [], [], stream=0)
+
+
+def test_binding_rejects_strided_states(lib):
+    """The library reads every state row-major: a transposed view would be read as
+    its transpose, so the binding refuses it."""
+    ps, gs, st = _ga([(16, 40)])
+    bad = [dict(st[0], projector=st[0]["projector_t"].T)]
+    with pytest.raises(ValueError):
+        _lib._galore_states(bad)
+    p = torch.zeros(6, 4)
+    s = _lib.init_state("lamb", p)
+    s["exp_avg_sq"] = torch.zeros(4, 6).T
+    with pytest.raises(ValueError):
+        _lib._states(_lib.meo_lamb_state, _lib.LAMB_KEYS, [s])

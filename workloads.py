@@ -278,3 +278,59 @@ def grads(wl: Workload, step_index: int, scales, device="cpu", indices=None, out
         else:
             res.append(g.to(wl.grad_dtype).contiguous())
     return res
+
+
+# ----------------------------------------------------------------------------- GaLore
+
+def galore_inputs(shapes: Sequence[Tuple[int, ...]], rank: int, seed: int = 0, *,
+                  param_dtype=torch.float32, device="cpu", gstd: float = 1e-3,
+                  state: str = "seeded", spectrum: Optional[Tuple[float, float]] = None):
+    """Parameters, bf16 gradients and GaLore states (meo.h layout) for `shapes`.
+
+    Drawn on the CPU from torch.Generator(seed) (the same bits on every device),
+    then moved to `device`. Parameters N(0, 0.02); gradients N(0, gstd^2), or, with
+    ``spectrum = (decay, noise)``, a low-rank-plus-noise matrix U diag(s) V^T +
+    noise with s_i = gstd * sqrt(max(m, n)) * decay^i (random orthonormal U, V) and
+    N(0, (noise * gstd)^2) noise, the structure the projection relies on. With
+    ``state = "seeded"`` the moments of a mid-run step are drawn (exp_avg
+    N(0, gstd^2 / 4), exp_avg_sq gstd^2 * U(0.5, 1.5)) and each 2-D tensor gets a
+    random orthonormal projector (QR of a Gaussian) rounded to bf16, stored with
+    its transpose; with ``state = "zero"`` everything starts at zero.
+    """
+    gen = torch.Generator().manual_seed(seed)
+    params, grads, states = [], [], []
+    for shape in shapes:
+        shape = tuple(shape)
+        x = (0.02 * torch.randn(shape, generator=gen, dtype=torch.float64)).to(param_dtype)
+        if spectrum is not None and len(shape) == 2:
+            m, n = shape
+            k = min(m, n)
+            qa, _ = torch.linalg.qr(torch.randn(m, k, generator=gen, dtype=torch.float64))
+            qb, _ = torch.linalg.qr(torch.randn(n, k, generator=gen, dtype=torch.float64))
+            s = gstd * math.sqrt(max(m, n)) * spectrum[0] ** torch.arange(k, dtype=torch.float64)
+            g = (qa * s) @ qb.T + spectrum[1] * gstd * torch.randn(m, n, generator=gen, dtype=torch.float64)
+        else:
+            g = gstd * torch.randn(shape, generator=gen, dtype=torch.float64)
+        g = g.to(torch.bfloat16)
+        projected = len(shape) == 2 and shape[0] > 0 and shape[1] > 0
+        if projected:
+            r = min(rank, min(shape))
+            mshape, d = (max(shape), r), min(shape)
+        else:
+            mshape = shape
+        if state == "seeded":
+            st = {"exp_avg": (0.5 * gstd * torch.randn(mshape, generator=gen, dtype=torch.float64)).float(),
+                  "exp_avg_sq": (gstd * gstd * (0.5 + torch.rand(mshape, generator=gen, dtype=torch.float64))).float()}
+            if projected:
+                q, _ = torch.linalg.qr(torch.randn(d, r, generator=gen, dtype=torch.float64))
+                st["projector"] = q.to(torch.bfloat16).contiguous()  # QR returns column-major Q
+        else:
+            st = {"exp_avg": torch.zeros(mshape), "exp_avg_sq": torch.zeros(mshape)}
+            if projected:
+                st["projector"] = torch.zeros((d, r), dtype=torch.bfloat16)
+        if projected:
+            st["projector_t"] = st["projector"].T.contiguous()
+        params.append(x.to(device))
+        grads.append(g.to(device))
+        states.append({k: v.to(device) for k, v in st.items()})
+    return params, grads, states
