@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmeo.so")
-SOURCES = ["abi.cpp", "passes.hip", "adafactor.hip", "came.hip", "lamb.hip", "shard.hip", "galore.hip"]
+SOURCES = ["abi.cpp", "passes.hip", "adafactor.hip", "came.hip", "lamb.hip", "shard.hip", "galore.hip", "galore_refresh.hip"]
 ARCH = os.environ.get("MEO_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -653,12 +653,12 @@ std::vector<StatePtrs> state_ptrs(int op, int32_t n, const void* states) {
 
 enum Pass { kPassStats = 0, kPassFinalize, kPassRms, kPassScalars, kPassAfApply, kPassCameMom,
             kPassCameApply, kPassLambMoments, kPassLambApply, kPassStatsWide, kPassStatsTiled,
-            kPassGaProject, kPassGaBack, kPassGaAdamw, kPassCount };
+            kPassGaProject, kPassGaBack, kPassGaAdamw, kPassGaRefresh, kPassCount };
 static_assert(kPassCount == MEO_NUM_PASSES, "pass table");
 const char* const kPassNames[kPassCount] = {"stats", "finalize", "rms", "scalars", "adafactor_apply",
                                             "came_mom", "came_apply", "lamb_moments", "lamb_apply",
                                             "stats_wide", "stats_tiled", "galore_project", "galore_back",
-                                            "galore_adamw"};
+                                            "galore_adamw", "galore_refresh"};
 
 struct ProfRec { int pass; hipEvent_t a, b; };
 std::mutex g_prof_mu;
@@ -1311,14 +1311,17 @@ int meo_came_shard_apply(const meo_came_hparams* hp, int64_t step, int32_t n, co
 
 namespace {
 
-enum GaList { kGaProjR = 0, kGaProjL, kGaBackR, kGaBackL, kGaFlat, kGaListCount };
+enum GaList { kGaProjR = 0, kGaProjL, kGaBackR, kGaBackL, kGaFlat,
+              // projector refresh
+              kRfInit, kRfG0N, kRfG0T, kRfG1N, kRfG1T, kRfGram, kRfOne, kRfCols, kRfStore, kGaListCount };
 
 struct GaPlan {
     std::vector<uint8_t> key;
     int device = 0;
-    void* mem = nullptr;  // [GDesc right..., left...][TDesc flat...][item tables]
+    void* mem = nullptr;  // [GDesc right..., left...][TDesc flat...][RDesc...][item tables]
     const GDesc* gdesc = nullptr;
     const TDesc* fdesc = nullptr;
+    const RDesc* rdesc = nullptr;
     const int2* items[kGaListCount] = {};
     int64_t count[kGaListCount] = {};
 };
@@ -1343,17 +1346,30 @@ int32_t ga_rank(const meo_galore_hparams* hp, const meo_tensor& t) {
     return static_cast<int32_t>(std::min<int64_t>(hp->rank, std::min(t.rows, t.cols)));
 }
 
-// Workspace: per projected tensor the two bf16 planes of N, [D][r] each, every
-// plane at a 256-byte boundary. Offsets in bytes.
-int64_t ga_layout(const meo_galore_hparams* hp, int32_t n, const meo_tensor* ts, std::vector<int64_t>* offs) {
+int64_t align256(int64_t bytes) { return (bytes + 255) / 256 * 256; }
+
+// Workspace, per projected tensor, every array at a 256-byte boundary (offsets in
+// bytes): the step's two bf16 planes of N, [D][r] each; then, for the projector
+// refresh, two fp32 [r][d] iterates, one fp32 [r][D] product, and four fp64
+// [r][r] matrices.
+int64_t ga_layout(const meo_galore_hparams* hp, int32_t n, const meo_tensor* ts, std::vector<int64_t>* offs,
+                  std::vector<int64_t>* roffs = nullptr) {
     int64_t off = 0;
     if (offs) offs->assign(n, -1);
+    if (roffs) roffs->assign(n, -1);
     for (int32_t k = 0; k < n; ++k) {
         const int32_t r = ga_rank(hp, ts[k]);
         if (!r) continue;
         if (offs) (*offs)[k] = off;
-        const int64_t plane = (std::max(ts[k].rows, ts[k].cols) * r * 2 + 255) / 256 * 256;
-        off += 2 * plane;
+        off += 2 * align256(std::max(ts[k].rows, ts[k].cols) * r * 2);
+    }
+    for (int32_t k = 0; k < n; ++k) {
+        const int32_t r = ga_rank(hp, ts[k]);
+        if (!r) continue;
+        if (roffs) (*roffs)[k] = off;
+        const int64_t d = std::min(ts[k].rows, ts[k].cols), D = std::max(ts[k].rows, ts[k].cols);
+        off += 2 * align256(static_cast<int64_t>(r) * d * 4) + align256(static_cast<int64_t>(r) * D * 4) +
+               4 * align256(static_cast<int64_t>(r) * r * 8);
     }
     return off;
 }
@@ -1498,8 +1514,9 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
     }
     *rc = check_galore_memory(hp, n, ts, st, dev);
     if (*rc) return nullptr;
-    std::vector<int64_t> woff;
-    ga_layout(hp, n, ts, &woff);
+    std::vector<int64_t> woff, roff;
+    ga_layout(hp, n, ts, &woff, &roff);
+    std::vector<RDesc> rd;
     std::vector<GDesc> right, left;
     std::vector<TDesc> flat;
     std::vector<int2> lists[kGaListCount];
@@ -1534,6 +1551,37 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
             d.btj = static_cast<int32_t>(is_left ? ceil_div(d.n, kGaTile) : ceil_div(d.n, kGaWide));
             (is_left ? left : right).push_back(d);
             (is_left ? kl : kr).push_back(k);
+            // refresh descriptor
+            RDesc q;
+            std::memset(&q, 0, sizeof q);
+            q.g = d.g; q.u = d.u; q.ut = d.ut;
+            q.m = d.m; q.n = d.n; q.D = d.D; q.d = d.d; q.r = d.r; q.p = d.r;
+            q.left = is_left;
+            q.gvec = aligned16(d.g) && d.n % 8 == 0;
+            q.seed = k;
+            uint8_t* rb = static_cast<uint8_t*>(ws) + roff[k];
+            const int64_t sq = align256(static_cast<int64_t>(q.r) * q.d * 4);
+            const int64_t sy = align256(static_cast<int64_t>(q.r) * q.D * 4);
+            const int64_t ss = align256(static_cast<int64_t>(q.r) * q.r * 8);
+            q.qa = reinterpret_cast<float*>(rb);
+            q.qb = reinterpret_cast<float*>(rb + sq);
+            q.yt = reinterpret_cast<float*>(rb + 2 * sq);
+            q.s = reinterpret_cast<double*>(rb + 2 * sq + sy);
+            q.w = reinterpret_cast<double*>(rb + 2 * sq + sy + ss);
+            q.s2 = reinterpret_cast<double*>(rb + 2 * sq + sy + 2 * ss);
+            q.w2 = reinterpret_cast<double*>(rb + 2 * sq + sy + 3 * ss);
+            const int id = static_cast<int>(rd.size());
+            rd.push_back(q);
+            auto addr = [&](int list, int64_t count) {
+                for (int64_t i = 0; i < count; ++i) lists[list].push_back(make_int2(id, static_cast<int>(i)));
+            };
+            addr(kRfInit, ceil_div(static_cast<int64_t>(q.p) * q.d, kThreads * kVec));
+            addr(is_left ? kRfG0T : kRfG0N, ceil_div(q.D, kGaTile));
+            addr(is_left ? kRfG1N : kRfG1T, ceil_div(q.d, kGaTile));
+            addr(kRfGram, ceil_div(q.p, 64) * ceil_div(q.p, 64));
+            addr(kRfOne, 1);
+            addr(kRfCols, ceil_div(q.d, 32));
+            addr(kRfStore, q.r);
         } else {
             TDesc d;
             std::memset(&d, 0, sizeof d);
@@ -1566,6 +1614,8 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
     size_t total = (gd.size() * sizeof(GDesc) + 255) / 256 * 256;
     const size_t foff = total;
     total += (flat.size() * sizeof(TDesc) + 255) / 256 * 256;
+    const size_t roffb = total;
+    total += (rd.size() * sizeof(RDesc) + 255) / 256 * 256;
     for (int l = 0; l < kGaListCount; ++l) {
         offs[l] = total;
         total += (lists[l].size() * sizeof(int2) + 255) / 256 * 256;
@@ -1574,6 +1624,7 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
     std::vector<uint8_t> host(total, 0);
     if (!gd.empty()) std::memcpy(host.data(), gd.data(), gd.size() * sizeof(GDesc));
     if (!flat.empty()) std::memcpy(host.data() + foff, flat.data(), flat.size() * sizeof(TDesc));
+    if (!rd.empty()) std::memcpy(host.data() + roffb, rd.data(), rd.size() * sizeof(RDesc));
     for (int l = 0; l < kGaListCount; ++l)
         if (!lists[l].empty()) std::memcpy(host.data() + offs[l], lists[l].data(), lists[l].size() * sizeof(int2));
     GaPlan* p = new GaPlan;
@@ -1589,6 +1640,7 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
     uint8_t* base = static_cast<uint8_t*>(p->mem);
     p->gdesc = reinterpret_cast<const GDesc*>(base);
     p->fdesc = reinterpret_cast<const TDesc*>(base + foff);
+    p->rdesc = reinterpret_cast<const RDesc*>(base + roffb);
     for (int l = 0; l < kGaListCount; ++l) {
         p->items[l] = reinterpret_cast<const int2*>(base + offs[l]);
         p->count[l] = static_cast<int64_t>(lists[l].size());
@@ -1640,11 +1692,46 @@ int meo_galore_refresh(const meo_galore_hparams* hp, int32_t n, const meo_tensor
                        void* ws, size_t ws_bytes, void* stream) {
     int rc = meo_galore_validate(hp, 1, n, ts, st);
     if (rc) return rc;
-    (void)ws; (void)ws_bytes; (void)stream;
-    bool any = false;
-    for (int32_t k = 0; k < n; ++k) any = any || ga_rank(hp, ts[k]) > 0;
-    if (!any) return MEO_OK;
-    return fail(MEO_EINVAL, "projector refresh is not available in this build");
+    if (n == 0) return MEO_OK;
+    rc = check_galore_workspace(hp, n, ts, ws, ws_bytes);
+    if (rc) return rc;
+    GaPlan* p = get_galore_plan(hp, n, ts, st, ws, &rc);
+    if (!p) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    auto tab = [&](int l) { return RTable{p->rdesc, p->items[l]}; };
+    auto cnt = [&](int l) { return p->count[l]; };
+    if (cnt(kRfOne) == 0) return MEO_OK;
+    PassTimer pt(s);
+    // Cholesky-QR applied twice to the p x d block in `buf` (the other iterate
+    // buffer is scratch); the orthonormal rows end in `buf`.
+    auto cholqr2 = [&](int buf) {
+        const int other = buf == kRbQa ? kRbQb : kRbQa;
+        launch_rf_gram(tab(kRfGram), cnt(kRfGram), buf, false, s);
+        launch_rf_chol(tab(kRfOne), cnt(kRfOne), s);
+        launch_rf_trmm(tab(kRfCols), cnt(kRfCols), buf, other, s);
+        launch_rf_gram(tab(kRfGram), cnt(kRfGram), other, false, s);
+        launch_rf_chol(tab(kRfOne), cnt(kRfOne), s);
+        launch_rf_trmm(tab(kRfCols), cnt(kRfCols), other, buf, s);
+    };
+    auto times_xt = [&](int src, int dst) {  // Y^T = Q^T X^T
+        launch_rf_gemm(tab(kRfG0N), cnt(kRfG0N), 0, src, dst, false, s);
+        launch_rf_gemm(tab(kRfG0T), cnt(kRfG0T), 0, src, dst, true, s);
+    };
+    launch_rf_init(tab(kRfInit), cnt(kRfInit), kRbQa, s);
+    cholqr2(kRbQa);
+    for (int i = 0; i < kRfIters; ++i) {
+        times_xt(kRbQa, kRbYt);
+        launch_rf_gemm(tab(kRfG1N), cnt(kRfG1N), 1, kRbYt, kRbQa, false, s);  // Z^T = Y^T X
+        launch_rf_gemm(tab(kRfG1T), cnt(kRfG1T), 1, kRbYt, kRbQa, true, s);
+        cholqr2(kRbQa);
+    }
+    times_xt(kRbQa, kRbYt);
+    launch_rf_gram(tab(kRfGram), cnt(kRfGram), kRbYt, true, s);
+    launch_rf_jacobi(tab(kRfOne), cnt(kRfOne), s);
+    launch_rf_basis(tab(kRfCols), cnt(kRfCols), kRbQa, s);
+    launch_rf_store(tab(kRfStore), cnt(kRfStore), s);
+    pt.mark(kPassGaRefresh);
+    return launch_status("galore refresh launch");
 }
 
 int meo_galore_step(const meo_galore_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,

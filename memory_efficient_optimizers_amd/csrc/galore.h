@@ -44,4 +44,51 @@ void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool lef
 void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, hipStream_t s);
 void launch_galore_adamw(const Table& t, int64_t n, const GaArgs& a, hipStream_t s);
 
+// ------------------------------------------------------------------ projector refresh
+
+constexpr int kRfIters = 4;        // subspace iterations per refresh
+constexpr int kRfKb = 32;          // contraction block of the refresh products
+constexpr int kRfPitch = kRfKb + 8;
+constexpr int kRfMaxP = 256;       // iteration block (the rank) at most 256
+
+// One projected tensor of a refresh. X is the gradient oriented so that the
+// projector spans its rows' space: X = G (m >= n, D x d) or G^T (m < n). The
+// iterate holds p orthonormal rows of length d (the transposed basis).
+struct RDesc {
+    const uint16_t* g;  // bf16 gradient [m][n]
+    uint16_t* u;        // out: projector [d][r], bf16
+    uint16_t* ut;       // out: projector transposed [r][d], bf16
+    float* qa;          // [p][d] iterate / scratch
+    float* qb;          // [p][d] iterate / scratch
+    float* yt;          // [p][D] X Q, transposed; later U^T in fp32 [r][d]
+    double* s;          // [p][p] Gram matrix, Cholesky factor, eigenproblem
+    double* w;          // [p][p] inverse factor, eigenvectors
+    double* s2;         // [p][p] second buffer of the eigenproblem
+    double* w2;         // [p][p] second buffer of the eigenvectors
+    int32_t m, n, D, d, r, p;
+    int32_t left;       // m < n
+    int32_t gvec;       // gradient rows may use 16-byte loads (n % 8 == 0, aligned)
+    int32_t seed;       // index of the tensor in its list (start vectors)
+};
+
+struct RTable {
+    const RDesc* desc;
+    const int2* items;
+};
+
+// Buffers named in launches.
+enum RBuf { kRbQa = 0, kRbQb = 1, kRbYt = 2 };
+
+void launch_rf_init(const RTable& t, int64_t n, int dst, hipStream_t s);
+// out[c][l] = sum_k in[c][k] X?[l][k]: `stage` 0 is Y^T = Q^T X^T (l over D, k over d),
+// stage 1 is Z^T = Y^T X (l over d, k over D).
+// `trans`: the gradient is read transposed (stage 0 with m < n, stage 1 with m >= n).
+void launch_rf_gemm(const RTable& t, int64_t n, int stage, int src, int dst, bool trans, hipStream_t s);
+void launch_rf_gram(const RTable& t, int64_t n, int src, bool over_long, hipStream_t s);
+void launch_rf_chol(const RTable& t, int64_t n, hipStream_t s);
+void launch_rf_trmm(const RTable& t, int64_t n, int src, int dst, hipStream_t s);
+void launch_rf_jacobi(const RTable& t, int64_t n, hipStream_t s);
+void launch_rf_basis(const RTable& t, int64_t n, int src, hipStream_t s);
+void launch_rf_store(const RTable& t, int64_t n, hipStream_t s);
+
 }  // namespace meo

@@ -1,0 +1,546 @@
+// GaLore projector refresh: the leading r singular vectors of the gradient. The
+// Colossal-AI distributed-optimizers page (section on GaLore's special
+// configuration) redoes an SVD every update_proj_gap steps to refresh the
+// orthogonal projection matrix; the ms-swift page (section on low-rank
+// projection) keeps the leading singular directions. Only those r vectors are
+// needed, so the refresh computes them by randomized subspace iteration with a
+// Rayleigh-Ritz step (Halko, Martinsson and Tropp, "Finding structure with
+// randomness", SIAM Review 2011, Algorithm 4.4 followed by the small SVD of
+// Algorithm 5.1), with the gradient oriented as X (D x d) so that the wanted
+// vectors span its rows' space:
+//
+//   Q^T (r x d) <- orthonormal rows of a Gaussian block (counter-based normals)
+//   repeat kRfIters times:
+//     Y^T = Q^T X^T   (r x D)          k_rf_gemm stage 0, bf16 MFMA, Q split in
+//     Z^T = Y^T X     (r x d)          k_rf_gemm stage 1   two bf16 planes
+//     Q^T <- orthonormal rows of Z^T   Cholesky-QR twice: k_rf_gram (fp64 Gram),
+//                                      k_rf_chol (fp64 factor and its inverse),
+//                                      k_rf_trmm (Q^T = L^-1 Z^T)
+//   Y^T = Q^T X^T; S = Y^T Y (r x r, fp64) = W diag(sigma^2) W^T   k_rf_jacobi
+//   U^T = (Q W)^T, columns by decreasing sigma                       k_rf_basis
+//   each vector signed so that its largest-magnitude entry is positive, stored
+//   in bf16 as U [d][r] and U^T [r][d]                               k_rf_store
+//
+// The result is the SVD's leading vectors up to the iteration's convergence,
+// (sigma_{r+1} / sigma_r)^(2 kRfIters) for the subspace, and fp32 rounding.
+#include "galore.h"
+
+namespace meo {
+
+typedef __bf16 bfv8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace {
+
+__device__ __forceinline__ f32x16 mfma32(const bfv8& a, const bfv8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float* rbuf(const RDesc& d, int which) {
+    return which == kRbQa ? d.qa : (which == kRbQb ? d.qb : d.yt);
+}
+
+// splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014): a counter-based 64-bit mix.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+    x += 0x9e3779b97f4a7c15ull;
+    x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
+    x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
+    return x ^ (x >> 31);
+}
+
+// A standard normal value for counter `key` (Box-Muller on two 24-bit uniforms).
+__device__ __forceinline__ float normal_at(uint64_t key) {
+    const uint64_t h = splitmix64(key);
+    const float u1 = static_cast<float>((h >> 40) + 1) * (1.0f / 16777217.0f);  // (0, 1]
+    const float u2 = static_cast<float>((h >> 16) & 0xffffffu) * (1.0f / 16777216.0f);
+    return sqrtf(-2.0f * logf(u1)) * cospif(2.0f * u2);
+}
+
+__device__ __forceinline__ u32x4 ld_row8(const uint16_t* p, int64_t rows, int64_t cols, int64_t row, int64_t col,
+                                         bool vec) {
+    if (row >= rows || col >= cols) return u32x4{0u, 0u, 0u, 0u};
+    const uint16_t* q = p + row * cols + col;
+    if (vec && col + 8 <= cols) return *gld<u32x4>(q);
+    const MEO_GLOBAL uint16_t* s = gld<uint16_t>(q);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = col + 2 * e < cols ? s[2 * e] : 0u;
+        const uint32_t hi = col + 2 * e + 1 < cols ? s[2 * e + 1] : 0u;
+        w[e] = lo | (hi << 16);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+// Block-wide sum / max of doubles (256 threads).
+__device__ double rf_sum_d(double v, double* lds) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (lds[0] + lds[1]) + (lds[2] + lds[3]);
+}
+
+__device__ double rf_max_d(double v, double* lds) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return fmax(fmax(lds[0], lds[1]), fmax(lds[2], lds[3]));
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ start block
+
+// Gaussian p x d block, one normal per element from the counter (tensor, index).
+__global__ __launch_bounds__(kThreads) void k_rf_init(RTable t, int dst) {
+    const int2 it = t.items[blockIdx.x];
+    const RDesc d = t.desc[it.x];
+    float* out = rbuf(d, dst);
+    const int64_t total = static_cast<int64_t>(d.p) * d.d;
+    const int64_t base = static_cast<int64_t>(it.y) * kThreads * kVec;
+    const uint64_t key = static_cast<uint64_t>(d.seed) << 40;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+        const int64_t i = base + static_cast<int64_t>(e) * kThreads + threadIdx.x;
+        if (i < total) out[i] = normal_at(key + static_cast<uint64_t>(i));
+    }
+}
+
+void launch_rf_init(const RTable& t, int64_t n, int dst, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_rf_init, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, dst);
+}
+
+// ------------------------------------------------------------------ products with the gradient
+
+// out[c][l] = sum_k in[c][k] B[l][k], c < p (fp32, split into two bf16 planes),
+// B from the bf16 gradient G [m][n]: Trans = false reads B[l][k] = G[l][k] (G is
+// [L][K]); Trans = true reads B[l][k] = G[k][l] (G is [K][L]), staged through LDS.
+// Stage 0: L = D, K = d; stage 1: L = d, K = D. Tile: all p rows x 64 columns.
+template <bool Trans>
+__global__ __launch_bounds__(kThreads) void k_rf_gemm(RTable t, int stage, int src, int dst) {
+    __shared__ __attribute__((aligned(16))) uint16_t ah[kRfMaxP * kRfPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t al[kRfMaxP * kRfPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t bs[kGaTile * kRfPitch];
+    const int2 it = t.items[blockIdx.x];
+    const RDesc d = t.desc[it.x];
+    const float* A = rbuf(d, src);
+    float* C = rbuf(d, dst);
+    const int64_t K = stage == 0 ? d.d : d.D;
+    const int64_t L = stage == 0 ? d.D : d.d;
+    const int64_t l0 = static_cast<int64_t>(it.y) * kGaTile;
+    const int P = d.p;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool active = wave * 64 < P;
+    const bool avec = (K & 3) == 0;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.0f;
+
+    for (int64_t k0 = 0; k0 < K; k0 += kRfKb) {
+        // A: rows 0..255 x 32 columns, fp32 -> high and low bf16 planes.
+        for (int c = threadIdx.x; c < kRfMaxP * (kRfKb / 8); c += kThreads) {
+            const int row = c >> 2, kc = (c & 3) * 8;
+            float v[8];
+            const int64_t col = k0 + kc;
+            if (row < P && avec && col + 8 <= K) {
+                const f32x4 x0 = *gld<f32x4>(A + row * K + col);
+                const f32x4 x1 = *gld<f32x4>(A + row * K + col + 4);
+                v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+                v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (row < P && col + e < K) ? A[row * K + col + e] : 0.0f;
+            }
+            float hi[8], lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                hi[e] = round_bf16(v[e]);
+                lo[e] = v[e] - hi[e];
+            }
+            *reinterpret_cast<u32x4*>(ah + row * kRfPitch + kc) = pack_bf16x8(hi);
+            *reinterpret_cast<u32x4*>(al + row * kRfPitch + kc) = pack_bf16x8(lo);
+        }
+        if (!Trans) {  // B rows l0.. of G [L][K]
+            for (int c = threadIdx.x; c < kGaTile * (kRfKb / 8); c += kThreads) {
+                const int l = c >> 2, kc = (c & 3) * 8;
+                *reinterpret_cast<u32x4*>(bs + l * kRfPitch + kc) = ld_row8(d.g, L, K, l0 + l, k0 + kc, d.gvec);
+            }
+        } else {       // B[l][k] = G[k0 + k][l0 + l], G [K][L]
+            for (int c = threadIdx.x; c < kRfKb * (kGaTile / 8); c += kThreads) {
+                const int k = c >> 3, lc = (c & 7) * 8;
+                const u32x4 v = ld_row8(d.g, K, L, k0 + k, l0 + lc, d.gvec);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bs[(lc + 2 * e) * kRfPitch + k] = static_cast<uint16_t>(w[e] & 0xffffu);
+                    bs[(lc + 2 * e + 1) * kRfPitch + k] = static_cast<uint16_t>(w[e] >> 16);
+                }
+            }
+        }
+        __syncthreads();
+        if (active) {
+#pragma unroll
+            for (int ks = 0; ks < kRfKb; ks += 16) {
+                const int kk = ks + 8 * (lane >> 5);
+                bfv8 fh[2], fl[2], fb[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int r = wave * 64 + b * 32 + (lane & 31);
+                    fh[b] = *reinterpret_cast<const bfv8*>(ah + r * kRfPitch + kk);
+                    fl[b] = *reinterpret_cast<const bfv8*>(al + r * kRfPitch + kk);
+                    fb[b] = *reinterpret_cast<const bfv8*>(bs + (b * 32 + (lane & 31)) * kRfPitch + kk);
+                }
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                    for (int jb = 0; jb < 2; ++jb) {
+                        acc[ib][jb] = mfma32(fh[ib], fb[jb], acc[ib][jb]);
+                        acc[ib][jb] = mfma32(fl[ib], fb[jb], acc[ib][jb]);
+                    }
+            }
+        }
+        __syncthreads();
+    }
+    if (!active) return;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int64_t l = l0 + jb * 32 + (lane & 31);
+            if (l >= L) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = wave * 64 + ib * 32 + acc_row(v, lane);
+                if (row < P) C[row * L + l] = acc[ib][jb][v];
+            }
+        }
+}
+
+void launch_rf_gemm(const RTable& t, int64_t n, int stage, int src, int dst, bool trans, hipStream_t s) {
+    if (n <= 0) return;
+    const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
+    if (trans) hipLaunchKernelGGL(k_rf_gemm<true>, grid, block, 0, s, t, stage, src, dst);
+    else hipLaunchKernelGGL(k_rf_gemm<false>, grid, block, 0, s, t, stage, src, dst);
+}
+
+// ------------------------------------------------------------------ Gram matrix (fp64)
+
+// S[a][b] = sum_k A[a][k] A[b][k] over the p rows of `src` (length d, or D when
+// over_long): products of fp32 values are exact in fp64 and summed in fp64.
+__global__ __launch_bounds__(kThreads) void k_rf_gram(RTable t, int src, int over_long) {
+    __shared__ float sa[64][33];
+    __shared__ float sb[64][33];
+    const int2 it = t.items[blockIdx.x];
+    const RDesc d = t.desc[it.x];
+    const float* A = rbuf(d, src);
+    const int64_t K = over_long ? d.D : d.d;
+    const int P = d.p;
+    const int tp = (P + 63) / 64;
+    const int a0 = (it.y / tp) * 64, b0 = (it.y % tp) * 64;
+    const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+    double acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int64_t k0 = 0; k0 < K; k0 += 32) {
+        for (int c = threadIdx.x; c < 64 * 32; c += kThreads) {
+            const int r = c >> 5, k = c & 31;
+            const bool kin = k0 + k < K;
+            sa[r][k] = (a0 + r < P && kin) ? A[(a0 + r) * K + k0 + k] : 0.0f;
+            sb[r][k] = (b0 + r < P && kin) ? A[(b0 + r) * K + k0 + k] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = 0; k < 32; ++k) {
+            double av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[i] = static_cast<double>(sa[ty * 4 + i][k]);
+                bv[i] = static_cast<double>(sb[tx * 4 + i][k]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fma(av[i], bv[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int a = a0 + ty * 4 + i, b = b0 + tx * 4 + j;
+            if (a < P && b < P) d.s[a * P + b] = acc[i][j];
+        }
+}
+
+void launch_rf_gram(const RTable& t, int64_t n, int src, bool over_long, hipStream_t s) {
+    if (n > 0)
+        hipLaunchKernelGGL(k_rf_gram, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, src,
+                           over_long ? 1 : 0);
+}
+
+// ------------------------------------------------------------------ Cholesky factor and its inverse
+
+// One block per tensor: S <- L (lower, in place) with S + 1e-13 max(diag S) I =
+// L L^T, then W <- L^-1 (lower). The shift keeps a numerically rank-deficient
+// block finite; a pivot that is not positive is replaced by 1.
+__global__ __launch_bounds__(kThreads) void k_rf_chol(RTable t) {
+    __shared__ double red[kWaves];
+    __shared__ double inv;
+    const RDesc d = t.desc[t.items[blockIdx.x].x];
+    double* S = d.s;
+    double* W = d.w;
+    const int P = d.p;
+    double mx = 0.0;
+    for (int i = threadIdx.x; i < P; i += kThreads) mx = fmax(mx, S[i * P + i]);
+    mx = rf_max_d(mx, red);
+    const double shift = 1e-13 * mx;
+    for (int i = threadIdx.x; i < P; i += kThreads) S[i * P + i] += shift;
+    __syncthreads();
+    for (int k = 0; k < P; ++k) {
+        if (threadIdx.x == 0) {
+            const double piv = S[k * P + k];
+            const double lkk = (piv > 0.0 && piv < INFINITY) ? sqrt(piv) : 1.0;
+            S[k * P + k] = lkk;
+            inv = 1.0 / lkk;
+        }
+        __syncthreads();
+        for (int i = k + 1 + threadIdx.x; i < P; i += kThreads) S[i * P + k] *= inv;
+        __syncthreads();
+        const int nr = P - k - 1;
+        for (int idx = threadIdx.x; idx < nr * nr; idx += kThreads) {
+            const int i = k + 1 + idx / nr, j = k + 1 + idx % nr;
+            if (j <= i) S[i * P + j] = fma(-S[i * P + k], S[j * P + k], S[i * P + j]);
+        }
+        __syncthreads();
+    }
+    for (int j = threadIdx.x; j < P; j += kThreads) {
+        for (int i = 0; i < j; ++i) W[i * P + j] = 0.0;
+        W[j * P + j] = 1.0 / S[j * P + j];
+        for (int i = j + 1; i < P; ++i) {
+            double acc = 0.0;
+            for (int k = j; k < i; ++k) acc = fma(S[i * P + k], W[k * P + j], acc);
+            W[i * P + j] = -acc / S[i * P + i];
+        }
+    }
+}
+
+void launch_rf_chol(const RTable& t, int64_t n, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_rf_chol, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t);
+}
+
+// dst[a][j] = sum_{b <= a} W[a][b] src[b][j]: 32 columns of the p x d block per
+// block, staged in LDS; fp64 sums.
+__global__ __launch_bounds__(kThreads) void k_rf_trmm(RTable t, int src, int dst) {
+    __shared__ float zs[kRfMaxP][33];
+    const int2 it = t.items[blockIdx.x];
+    const RDesc d = t.desc[it.x];
+    const float* Z = rbuf(d, src);
+    float* Q = rbuf(d, dst);
+    const int P = d.p;
+    const int64_t j0 = static_cast<int64_t>(it.y) * 32;
+    for (int c = threadIdx.x; c < P * 32; c += kThreads) {
+        const int b = c >> 5, jj = c & 31;
+        zs[b][jj] = j0 + jj < d.d ? Z[b * static_cast<int64_t>(d.d) + j0 + jj] : 0.0f;
+    }
+    __syncthreads();
+    const int jj = threadIdx.x & 31, ag = threadIdx.x >> 5;
+    if (j0 + jj >= d.d) return;
+    for (int a = ag; a < P; a += kThreads / 32) {
+        double acc = 0.0;
+        for (int b = 0; b <= a; ++b) acc = fma(d.w[a * P + b], static_cast<double>(zs[b][jj]), acc);
+        Q[a * static_cast<int64_t>(d.d) + j0 + jj] = static_cast<float>(acc);
+    }
+}
+
+void launch_rf_trmm(const RTable& t, int64_t n, int src, int dst, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_rf_trmm, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, src, dst);
+}
+
+// ------------------------------------------------------------------ symmetric eigenproblem (fp64)
+
+// One block per tensor: cyclic Jacobi with the round-robin ordering, so each round
+// applies p/2 disjoint rotations at once: S <- J^T S J, W <- W J, with J's column
+// a holding c_a at a and t_a at its partner (t = -s for the first of a pair, +s
+// for the second). Rotation angles as in the classical method (Rutishauser's
+// formulation: tan of the angle from theta = (S_jj - S_ii) / (2 S_ij)). Stops when
+// the off-diagonal norm is below 1e-13 of the whole, or after 16 sweeps. On exit
+// S holds the eigenvalues on its diagonal and W the eigenvectors as columns.
+__global__ __launch_bounds__(kThreads) void k_rf_jacobi(RTable t) {
+    __shared__ double cc[kRfMaxP + 1], tt[kRfMaxP + 1];
+    __shared__ int qq[kRfMaxP + 1];
+    __shared__ double red[kWaves];
+    const RDesc d = t.desc[t.items[blockIdx.x].x];
+    const int P = d.p;
+    const int Pe = P + (P & 1);  // an odd size gets a dummy index P
+    double* S = d.s;
+    double* W = d.w;
+    double* S2 = d.s2;
+    double* W2 = d.w2;
+    for (int i = threadIdx.x; i < P * P; i += kThreads) W[i] = (i / P == i % P) ? 1.0 : 0.0;
+    __syncthreads();
+    for (int sweep = 0; sweep < 16; ++sweep) {
+        double off = 0.0, tot = 0.0;
+        for (int i = threadIdx.x; i < P * P; i += kThreads) {
+            const double v = S[i] * S[i];
+            tot += v;
+            if (i / P != i % P) off += v;
+        }
+        off = rf_sum_d(off, red);
+        tot = rf_sum_d(tot, red);
+        if (!(off > 1e-26 * tot)) break;  // uniform: every thread holds the same sums
+        for (int round = 0; round < Pe - 1; ++round) {
+            // pairs of the circle method: 0 with 1 + round, and the rest mirrored
+            for (int k = threadIdx.x; k < Pe / 2; k += kThreads) {
+                int i, j;
+                if (k == 0) {
+                    i = 0;
+                    j = 1 + round;
+                } else {
+                    i = 1 + (round + k) % (Pe - 1);
+                    j = 1 + (round + Pe - 1 - k) % (Pe - 1);
+                }
+                if (i > j) { const int x = i; i = j; j = x; }
+                double c = 1.0, s = 0.0;
+                if (j < P) {
+                    const double sij = S[i * P + j];
+                    if (sij != 0.0) {
+                        const double theta = (S[j * P + j] - S[i * P + i]) / (2.0 * sij);
+                        const double tn = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(fma(theta, theta, 1.0)));
+                        c = 1.0 / sqrt(fma(tn, tn, 1.0));
+                        s = tn * c;
+                    }
+                }
+                cc[i] = c; tt[i] = -s; qq[i] = j;
+                cc[j] = c; tt[j] = s; qq[j] = i;
+            }
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < P * P; idx += kThreads) {
+                const int a = idx / P, b = idx % P;
+                const int qa = qq[a], qb = qq[b];
+                const double ca = cc[a], ta = tt[a], cb = cc[b], tb = tt[b];
+                double v = ca * cb * S[a * P + b];
+                if (qb < P) v = fma(ca * tb, S[a * P + qb], v);
+                if (qa < P) v = fma(ta * cb, S[qa * P + b], v);
+                if (qa < P && qb < P) v = fma(ta * tb, S[qa * P + qb], v);
+                S2[idx] = v;
+                double w = cb * W[idx];
+                if (qb < P) w = fma(tb, W[a * P + qb], w);
+                W2[idx] = w;
+            }
+            __syncthreads();
+            double* x = S; S = S2; S2 = x;
+            x = W; W = W2; W2 = x;
+        }
+    }
+    if (S != d.s) {  // leave the result in s and w
+        for (int i = threadIdx.x; i < P * P; i += kThreads) {
+            d.s[i] = S[i];
+            d.w[i] = W[i];
+        }
+    }
+}
+
+void launch_rf_jacobi(const RTable& t, int64_t n, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_rf_jacobi, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t);
+}
+
+// ------------------------------------------------------------------ basis and storage
+
+// U^T[c][j] = sum_b W[b][o_c] Q^T[b][j] for c < r, where o sorts the eigenvalues
+// (diagonal of S) in decreasing order (ties by index); written as fp32 [r][d]
+// into the yt buffer.
+__global__ __launch_bounds__(kThreads) void k_rf_basis(RTable t, int src) {
+    __shared__ float zs[kRfMaxP][33];
+    __shared__ int ord[kRfMaxP];
+    const int2 it = t.items[blockIdx.x];
+    const RDesc d = t.desc[it.x];
+    const float* Q = rbuf(d, src);
+    const int P = d.p;
+    for (int i = threadIdx.x; i < P; i += kThreads) {
+        const double li = d.s[i * P + i];
+        int rank = 0;
+        for (int k = 0; k < P; ++k) {
+            const double lk = d.s[k * P + k];
+            rank += (lk > li || (lk == li && k < i)) ? 1 : 0;
+        }
+        ord[rank] = i;
+    }
+    const int64_t j0 = static_cast<int64_t>(it.y) * 32;
+    for (int c = threadIdx.x; c < P * 32; c += kThreads) {
+        const int b = c >> 5, jj = c & 31;
+        zs[b][jj] = j0 + jj < d.d ? Q[b * static_cast<int64_t>(d.d) + j0 + jj] : 0.0f;
+    }
+    __syncthreads();
+    const int jj = threadIdx.x & 31, cg = threadIdx.x >> 5;
+    if (j0 + jj >= d.d) return;
+    for (int c = cg; c < d.r; c += kThreads / 32) {
+        const int oc = ord[c];
+        double acc = 0.0;
+        for (int b = 0; b < P; ++b) acc = fma(d.w[b * P + oc], static_cast<double>(zs[b][jj]), acc);
+        d.yt[c * static_cast<int64_t>(d.d) + j0 + jj] = static_cast<float>(acc);
+    }
+}
+
+void launch_rf_basis(const RTable& t, int64_t n, int src, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_rf_basis, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, src);
+}
+
+// One block per (tensor, vector c): the sign that makes the largest-magnitude entry
+// (first on a tie) positive, then U^T[c][:] and U[:][c] in bf16.
+__global__ __launch_bounds__(kThreads) void k_rf_store(RTable t) {
+    __shared__ float bv[kWaves];
+    __shared__ int bi[kWaves];
+    __shared__ float sign;
+    const int2 it = t.items[blockIdx.x];
+    const RDesc d = t.desc[it.x];
+    const int c = it.y;
+    const float* row = d.yt + c * static_cast<int64_t>(d.d);
+    float best = -1.0f;
+    int bidx = 0x7fffffff;
+    for (int j = threadIdx.x; j < d.d; j += kThreads) {
+        const float a = fabsf(row[j]);
+        if (a > best) { best = a; bidx = j; }  // j increases: first index on a tie
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ob = __shfl_xor(best, o);
+        const int oi = __shfl_xor(bidx, o);
+        if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
+    }
+    if ((threadIdx.x & 63) == 0) { bv[threadIdx.x >> 6] = best; bi[threadIdx.x >> 6] = bidx; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = bv[0];
+        int i = bi[0];
+        for (int w = 1; w < kWaves; ++w)
+            if (bv[w] > b || (bv[w] == b && bi[w] < i)) { b = bv[w]; i = bi[w]; }
+        sign = (i < d.d && row[i] < 0.0f) ? -1.0f : 1.0f;
+    }
+    __syncthreads();
+    const float sg = sign;
+    for (int j = threadIdx.x; j < d.d; j += kThreads) {
+        const uint16_t v = static_cast<uint16_t>(bf16_bits(sg * row[j]));
+        d.ut[c * static_cast<int64_t>(d.d) + j] = v;
+        d.u[static_cast<int64_t>(j) * d.r + c] = v;
+    }
+}
+
+void launch_rf_store(const RTable& t, int64_t n, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_rf_store, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t);
+}
+
+}  // namespace meo

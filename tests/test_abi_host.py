@@ -327,9 +327,12 @@ def test_galore_validation(lib):
     _lib.meo_galore_validate(h, 1, ps, gs, st)
     assert [_lib.meo_galore_rank(h, p) for p in ps] == [8, 8, 0, 0]
     assert _lib.meo_galore_rank(_lib.galore_hparams(rank=300), torch.zeros(20, 30)) == 20
-    # workspace: two bf16 planes of [max(m, n)][r] per projected tensor, each 256-byte aligned
-    plane = (40 * 8 * 2 + 255) // 256 * 256
-    assert _lib.meo_galore_workspace_size(h, ps, gs) == 2 * 2 * plane
+    # workspace per projected tensor, each array 256-byte aligned: two bf16 planes of
+    # [max(m, n)][r] (the step); two fp32 [r][min], one fp32 [r][max] and four fp64
+    # [r][r] arrays (the refresh)
+    a = lambda b: (b + 255) // 256 * 256
+    per = 2 * a(40 * 8 * 2) + 2 * a(8 * 16 * 4) + a(8 * 40 * 4) + 4 * a(8 * 8 * 8)
+    assert _lib.meo_galore_workspace_size(h, ps, gs) == 2 * per
     for bad, code in ((dict(lr=-1.0), _lib.MEO_EINVAL), (dict(betas=(1.0, 0.9)), _lib.MEO_EINVAL),
                       (dict(eps=-1e-8), _lib.MEO_EINVAL), (dict(rank=0), _lib.MEO_EINVAL),
                       (dict(update_proj_gap=0), _lib.MEO_EINVAL), (dict(scale=float("nan")), _lib.MEO_EINVAL)):

@@ -289,9 +289,10 @@ def galore_inputs(shapes: Sequence[Tuple[int, ...]], rank: int, seed: int = 0, *
 
     Drawn on the CPU from torch.Generator(seed) (the same bits on every device),
     then moved to `device`. Parameters N(0, 0.02); gradients N(0, gstd^2), or, with
-    ``spectrum = (decay, noise)``, a low-rank-plus-noise matrix U diag(s) V^T +
-    noise with s_i = gstd * sqrt(max(m, n)) * decay^i (random orthonormal U, V) and
-    N(0, (noise * gstd)^2) noise, the structure the projection relies on. With
+    ``spectrum = (decay, noise, k)``, a rank-k signal plus noise, U diag(s) V^T +
+    E with s_i = gstd * sqrt(max(m, n)) * decay^i for i < k (random orthonormal U,
+    V) and E ~ N(0, (noise * gstd)^2): the low-rank structure the projection relies
+    on, with a spectral gap after the k-th singular value. With
     ``state = "seeded"`` the moments of a mid-run step are drawn (exp_avg
     N(0, gstd^2 / 4), exp_avg_sq gstd^2 * U(0.5, 1.5)) and each 2-D tensor gets a
     random orthonormal projector (QR of a Gaussian) rounded to bf16, stored with
@@ -304,7 +305,7 @@ def galore_inputs(shapes: Sequence[Tuple[int, ...]], rank: int, seed: int = 0, *
         x = (0.02 * torch.randn(shape, generator=gen, dtype=torch.float64)).to(param_dtype)
         if spectrum is not None and len(shape) == 2:
             m, n = shape
-            k = min(m, n)
+            k = min(m, n, spectrum[2])
             qa, _ = torch.linalg.qr(torch.randn(m, k, generator=gen, dtype=torch.float64))
             qb, _ = torch.linalg.qr(torch.randn(n, k, generator=gen, dtype=torch.float64))
             s = gstd * math.sqrt(max(m, n)) * spectrum[0] ** torch.arange(k, dtype=torch.float64)
