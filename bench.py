@@ -231,12 +231,180 @@ def shard_bench(torch, _lib, workloads, wl, args) -> int:
     return 0
 
 
+GALORE_WORKLOADS = {
+    # name: (parameter dtype, rank, scale, update_proj_gap)
+    "galore_llama7b": ("float32", 256, 0.25, 200),
+    "galore_llama7b_bf16": ("bfloat16", 256, 0.25, 200),
+}
+
+
+def galore_bytes_flops(shapes, rank: int, xb: int) -> dict:
+    """Algorithmic HBM bytes and matrix flops of one GaLore step (not a refresh
+    step) per pass. Projected (2-D) tensor, d = min(m, n), D = max(m, n), r =
+    min(rank, d): the projection reads G (bf16) and U^T once, reads and writes both
+    moments ([D][r] fp32) and writes N's two bf16 planes; the back-projection reads
+    N's planes and U once and reads and writes the parameter; 2 m n r flops for the
+    projection, twice that for the back-projection (two planes). Other tensors:
+    AdamW reads G and both moments and writes both moments, reads and writes X."""
+    out = {"galore_project": 0, "galore_back": 0, "galore_adamw": 0,
+           "flops_project": 0, "flops_back": 0}
+    for shape in shapes:
+        n_el = math.prod(shape)
+        if len(shape) == 2 and n_el:
+            m, n = shape
+            d, D = min(m, n), max(m, n)
+            r = min(rank, d)
+            out["galore_project"] += m * n * 2 + D * r * (16 + 4) + d * r * 2
+            out["galore_back"] += m * n * 2 * xb + D * r * 4 + d * r * 2
+            out["flops_project"] += 2 * m * n * r
+            out["flops_back"] += 4 * m * n * r
+        else:
+            out["galore_adamw"] += n_el * (2 + 2 * xb + 16)
+    out["step"] = out["galore_project"] + out["galore_back"] + out["galore_adamw"]
+    return out
+
+
+def galore_cpu_baseline(shapes, rank: int, scale: float, param_bf16: bool, budget_s: float = 15.0) -> dict:
+    """The fp64 oracle's GaLore step (a step that is not a refresh step, seeded
+    projectors) on the workload's tensors in list order until about `budget_s`
+    seconds, on one BLAS thread: parameters stepped per second."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import galore as ga
+    rng = np.random.default_rng(0)
+    hp = dict(rank=rank, scale=scale)
+    done, spent, count = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for shape in shapes:
+            x = 0.02 * rng.standard_normal(shape)
+            g = 1e-3 * rng.standard_normal(shape)
+            st = ga.galore_init_state(shape, hp)
+            if "projector" in st:
+                st["projector"] = np.linalg.qr(rng.standard_normal(st["projector"].shape))[0]
+            t0 = time.perf_counter()
+            ga.galore_step_tensor(x, g, st, hp, 2, param_bf16=param_bf16)
+            spent += time.perf_counter() - t0
+            done += x.size
+            count += 1
+            if spent > budget_s:
+                break
+    return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"one fp64 GaLore step (not a refresh step) of the first {count} tensors of the same "
+                      f"list ({done} parameters), {spent:.1f} s of oracle time, NumPy on one BLAS thread"}
+
+
+def galore_bench(torch, _lib, workloads, args) -> int:
+    """The GaLore step over the Llama-7B-shaped list: every 2-D tensor projected at
+    rank 256 (scale 0.25), norms by flat AdamW. The first warmup step is a refresh
+    step (t = 1), which computes every projector; the timed steps are not (t - 1 is
+    not a multiple of update_proj_gap). The refresh is timed on its own afterwards."""
+    pdt, rank, scale, gap = GALORE_WORKLOADS[args.workload]
+    pdt = getattr(torch, pdt)
+    specs = workloads.llama_specs()
+    shapes = [s.shape for s in specs]
+    dev = "cuda"
+    gen = torch.Generator(device=dev).manual_seed(0)
+    params = flat_views(torch, shapes, pdt, dev)
+    grads = flat_views(torch, shapes, torch.bfloat16, dev)
+    for p, g in zip(params, grads):
+        p.copy_(0.02 * torch.randn(p.shape, generator=gen, device=dev))
+        g.copy_(1e-3 * torch.randn(g.shape, generator=gen, device=dev))
+    states = []
+    for p in params:
+        st = {}
+        for k, shp in _lib.galore_state_shapes(p.shape, rank).items():
+            st[k] = torch.zeros(shp, dtype=torch.bfloat16 if k.startswith("projector") else torch.float32,
+                                device=dev)
+        states.append(st)
+    hp = _lib.galore_hparams(lr=1e-3, rank=rank, scale=scale, update_proj_gap=gap, weight_decay=0.0)
+    ws = _lib.workspace(_lib.meo_galore_workspace_size(hp, params, grads), dev)
+    stream = torch.cuda.current_stream()
+    numel = sum(p.numel() for p in params)
+
+    t = 0
+    for _ in range(max(args.warmup, 1)):
+        t += 1
+        _lib.meo_galore_step(hp, t, params, grads, states, ws, stream)
+    torch.cuda.synchronize()
+    _lib.meo_profile_enable(True)
+    _lib.meo_profile_collect()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        t += 1
+        assert (t - 1) % gap != 0
+        _lib.meo_galore_step(hp, t, params, grads, states, ws, stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    passes = _lib.meo_profile_collect()
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    # the refresh alone
+    nref = 2
+    _lib.meo_profile_collect()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(nref):
+        _lib.meo_galore_refresh(hp, params, grads, states, ws, stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    _lib.meo_profile_enable(False)
+    _lib.meo_profile_collect()
+    refresh_ms = r0.elapsed_time(r1) / nref
+
+    xb = 2 if pdt == torch.bfloat16 else 4
+    ab = galore_bytes_flops(shapes, rank, xb)
+    dominant = max((k for k in passes if k in ab), key=lambda k: passes[k]["ms"])
+    avg_ms = passes[dominant]["ms"] / passes[dominant]["launches"]
+    per_pass = {}
+    for k in ("galore_project", "galore_back"):
+        if k in passes:
+            ms = passes[k]["ms"] / passes[k]["launches"]
+            fl = ab["flops_project" if k == "galore_project" else "flops_back"]
+            per_pass[k] = {"ms": ms, "GB/s": ab[k] / (ms / 1e3) / 1e9, "TFLOP/s": fl / (ms / 1e3) / 1e12}
+    achieved = ab[dominant] / (avg_ms / 1e3) / 1e9
+    value = numel / (ms_step / 1e3)
+    out = {
+        "metric": "optimizer-step params/s, 7B-shaped GaLore (rank 256) step",
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "step_ms": {"min": min(step_ms), "median": sorted(step_ms)[len(step_ms) // 2], "max": max(step_ms)},
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 mfma, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "optimizer": "galore", "tensors": len(shapes), "params": numel,
+                   "grad_dtype": "bfloat16", "param_dtype": str(pdt).replace("torch.", ""), "rank": rank,
+                   "scale": scale, "update_proj_gap": gap},
+        "refresh_ms": refresh_ms,
+        "amortized_ms_per_step": ms_step + refresh_ms / gap,
+        "hbm": {"step_bytes": ab["step"], "achieved": ab["step"] / (ms_step / 1e3) / 1e9, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": ab["step"] / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": profile_traffic(dominant, args.workload),
+                     "bytes_per_launch": ab[dominant], "avg_ms": avg_ms},
+        "mfma": {k: {"achieved": v["TFLOP/s"], "peak": 2500.0, "unit": "TFLOP/s", "frac": v["TFLOP/s"] / 2500.0}
+                 for k, v in per_pass.items()},
+        "passes_ms_per_step": {k: v["ms"] / args.steps for k, v in passes.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = galore_cpu_baseline(shapes, rank, scale, pdt == torch.bfloat16)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="adafactor_llama7b")
+    ap.add_argument("--workload", default="adafactor_llama7b",
+                    help="a workload of workloads.py, or galore_llama7b / galore_llama7b_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", choices=["flat", "separate"], default="flat",
                     help="flat: one buffer per kind of tensor (default); separate: one allocation per tensor")
@@ -266,6 +434,9 @@ def main() -> int:
     if args.copy_calibration:
         return copy_calibration(torch, args)
     _lib.load()
+    if args.workload in GALORE_WORKLOADS:
+        torch.cuda.set_device(0)
+        return galore_bench(torch, _lib, workloads, args)
     wl = workloads.WORKLOADS[args.workload]
     dev = "cuda"
     torch.cuda.set_device(0)
