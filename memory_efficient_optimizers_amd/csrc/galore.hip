@@ -28,6 +28,8 @@
 // LDS. Non-projected tensors take a flat AdamW kernel (k_galore_adamw).
 #include "galore.h"
 
+#include <type_traits>
+
 namespace meo {
 
 typedef __bf16 bfv8 __attribute__((ext_vector_type(8)));
@@ -63,36 +65,57 @@ __device__ __forceinline__ bfv8 ld_frag(const uint16_t* p) {
     return *reinterpret_cast<const bfv8*>(p);
 }
 
-// Stage rows [r0, r0 + nrows) x contraction columns [k0, k0 + kGaKb) of a row-major
-// [rows][cols] bf16 array into LDS (row pitch kGaPitch), zero outside the array.
+// Rows [r0, r0 + NROWS) x contraction columns [k0, k0 + kGaKb) of a row-major
+// [rows][cols] bf16 array, zero outside it: loaded into registers first (all of a
+// thread's chunks in flight at once, and the next block's while the current one
+// is multiplied), then written to LDS (row pitch kGaPitch).
 template <int NROWS>
-__device__ __forceinline__ void stage_rows(uint16_t* lds, const uint16_t* p, int64_t rows, int64_t cols,
-                                           int64_t r0, int64_t k0, bool vec) {
-    constexpr int kChunks = NROWS * (kGaKb / 8);
+struct RowStage {
+    static constexpr int kPer = NROWS * (kGaKb / 8) / kThreads;
+    u32x4 v[kPer];
+    __device__ __forceinline__ void load(const uint16_t* p, int64_t rows, int64_t cols, int64_t r0, int64_t k0,
+                                         bool vec) {
 #pragma unroll
-    for (int c = threadIdx.x; c < kChunks; c += kThreads) {
-        const int row = c >> 3, kc = (c & 7) * 8;
-        st_lds8(lds + row * kGaPitch + kc, ld_row8(p, rows, cols, r0 + row, k0 + kc, vec));
-    }
-}
-
-// Stage the transposed tile A[i][k] = G[k0 + k][i0 + i] (i < kGaTile, k < kGaKb) of
-// the row-major gradient G [K][D]: coalesced along G's rows, scattered into LDS.
-__device__ __forceinline__ void stage_transposed(uint16_t* lds, const uint16_t* g, int64_t K, int64_t D,
-                                                 int64_t i0, int64_t k0, bool vec) {
-    constexpr int kChunks = kGaKb * (kGaTile / 8);
-#pragma unroll
-    for (int c = threadIdx.x; c < kChunks; c += kThreads) {
-        const int k = c >> 3, ic = (c & 7) * 8;
-        const u32x4 v = ld_row8(g, K, D, k0 + k, i0 + ic, vec);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            lds[(ic + 2 * e) * kGaPitch + k] = static_cast<uint16_t>(w[e] & 0xffffu);
-            lds[(ic + 2 * e + 1) * kGaPitch + k] = static_cast<uint16_t>(w[e] >> 16);
+        for (int i = 0; i < kPer; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            v[i] = ld_row8(p, rows, cols, r0 + (c >> 3), k0 + (c & 7) * 8, vec);
         }
     }
-}
+    __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            st_lds8(lds + (c >> 3) * kGaPitch + (c & 7) * 8, v[i]);
+        }
+    }
+};
+
+// The transposed tile A[i][k] = G[k0 + k][i0 + i] (i < kGaTile, k < kGaKb) of the
+// row-major gradient G [K][D]: loaded along G's rows, scattered into LDS.
+struct TransStage {
+    static constexpr int kPer = kGaKb * (kGaTile / 8) / kThreads;
+    u32x4 v[kPer];
+    __device__ __forceinline__ void load(const uint16_t* g, int64_t K, int64_t D, int64_t i0, int64_t k0, bool vec) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            v[i] = ld_row8(g, K, D, k0 + (c >> 3), i0 + (c & 7) * 8, vec);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            const int k = c >> 3, ic = (c & 7) * 8;
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lds[(ic + 2 * e) * kGaPitch + k] = static_cast<uint16_t>(w[e] & 0xffffu);
+                lds[(ic + 2 * e + 1) * kGaPitch + k] = static_cast<uint16_t>(w[e] >> 16);
+            }
+        }
+    }
+};
 
 // Accumulator element v of a 32x32 block held by `lane`: row and column in the block.
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
@@ -117,11 +140,19 @@ __global__ __launch_bounds__(kThreads) void k_galore_project(GTable t, GaArgs a)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.0f;
 
+    typename std::conditional<Left, TransStage, RowStage<kGaTile>>::type pa;
+    RowStage<kGaWide> pb;
+    auto fetch = [&](int64_t k0) {
+        if constexpr (Left) pa.load(d.g, d.d, d.D, i0, k0, vec);
+        else pa.load(d.g, d.D, d.d, i0, k0, vec);
+        pb.load(d.ut, d.r, d.d, 0, k0, vec);
+    };
+    fetch(0);
     for (int64_t k0 = 0; k0 < d.d; k0 += kGaKb) {
-        if (Left) stage_transposed(sa, d.g, d.d, d.D, i0, k0, vec);
-        else stage_rows<kGaTile>(sa, d.g, d.D, d.d, i0, k0, vec);
-        stage_rows<kGaWide>(sb, d.ut, d.r, d.d, 0, k0, vec);
+        pa.store(sa);
+        pb.store(sb);
         __syncthreads();
+        if (k0 + kGaKb < d.d) fetch(k0 + kGaKb);
         if (active) {
 #pragma unroll
             for (int ks = 0; ks < kGaKb; ks += 16) {
@@ -142,21 +173,31 @@ __global__ __launch_bounds__(kThreads) void k_galore_project(GTable t, GaArgs a)
     }
     if (!active) return;
     // AdamW on the tile of R: lanes 0..31 of an accumulator register hold 32
-    // consecutive columns of one row.
+    // consecutive columns of one row. The moments of a 32x32 block are loaded
+    // together, then updated and stored.
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
             const int col = wave * 64 + jb * 32 + acc_col(lane);
-            if (col >= d.r) continue;
+            const bool cok = col < d.r;
+            float m0[16], v0[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t row = i0 + ib * 32 + acc_row(v, lane);
-                if (row >= d.D) continue;
+                const bool ok = cok && row < d.D;
+                const int64_t idx = row * d.r + col;
+                m0[v] = ok ? *gld<float>(d.em + idx) : 0.0f;
+                v0[v] = ok ? *gld<float>(d.ev + idx) : 0.0f;
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = i0 + ib * 32 + acc_row(v, lane);
+                if (!cok || row >= d.D) continue;
                 const int64_t idx = row * d.r + col;
                 const float rv = acc[ib][jb][v];
-                const float m = fmaf(a.beta1, *gld<float>(d.em + idx), a.omb1 * rv);
-                const float vv = fmaf(a.beta2, *gld<float>(d.ev + idx), a.omb2 * (rv * rv));
+                const float m = fmaf(a.beta1, m0[v], a.omb1 * rv);
+                const float vv = fmaf(a.beta2, v0[v], a.omb2 * (rv * rv));
                 *gst<float>(d.em + idx) = m;
                 *gst<float>(d.ev + idx) = vv;
                 const float n = (m * a.inv_bc1) / (sqrtf(vv * a.inv_bc2) + a.eps);
@@ -202,11 +243,20 @@ __global__ __launch_bounds__(kThreads) void k_galore_back(GTable t, GaArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.0f;
 
+    RowStage<kGaTile> ph, pl;
+    RowStage<kGaWide> pu;
+    auto fetch = [&](int k0) {
+        ph.load(d.nh, d.D, d.r, n0, k0, vec);
+        pl.load(d.nl, d.D, d.r, n0, k0, vec);
+        pu.load(d.u, d.d, d.r, u0, k0, vec);
+    };
+    fetch(0);
     for (int k0 = 0; k0 < d.r; k0 += kGaKb) {
-        stage_rows<kGaTile>(sh, d.nh, d.D, d.r, n0, k0, vec);
-        stage_rows<kGaTile>(sl, d.nl, d.D, d.r, n0, k0, vec);
-        stage_rows<kGaWide>(su, d.u, d.d, d.r, u0, k0, vec);
+        ph.store(sh);
+        pl.store(sl);
+        pu.store(su);
         __syncthreads();
+        if (k0 + kGaKb < d.r) fetch(k0 + kGaKb);
 #pragma unroll
         for (int ks = 0; ks < kGaKb; ks += 16) {
             const int kk = ks + 8 * (lane >> 5);
@@ -232,7 +282,8 @@ __global__ __launch_bounds__(kThreads) void k_galore_back(GTable t, GaArgs a) {
         }
         __syncthreads();
     }
-    // W <- decay W - coef C; lanes 0..31 of a register hold 32 consecutive columns.
+    // W <- decay W - coef C; lanes 0..31 of a register hold 32 consecutive
+    // columns. The parameters of a 32x32 block are loaded together, then stored.
     const int64_t wr0 = Left ? r0 + wave * 64 : r0;
     const int64_t wc0 = Left ? c0 : c0 + wave * 64;
 #pragma unroll
@@ -240,20 +291,31 @@ __global__ __launch_bounds__(kThreads) void k_galore_back(GTable t, GaArgs a) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
             const int64_t col = wc0 + jb * 32 + acc_col(lane);
-            if (col >= d.n) continue;
+            const bool cok = col < d.n;
+            float w[16];
+            if (d.xbf16) {
+                const uint16_t* xp = static_cast<const uint16_t*>(d.x);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t row = wr0 + ib * 32 + acc_row(v, lane);
+                    w[v] = (cok && row < d.m) ? __uint_as_float(static_cast<uint32_t>(*gld<uint16_t>(xp + row * d.n + col)) << 16)
+                                              : 0.0f;
+                }
+            } else {
+                const float* xp = static_cast<const float*>(d.x);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t row = wr0 + ib * 32 + acc_row(v, lane);
+                    w[v] = (cok && row < d.m) ? *gld<float>(xp + row * d.n + col) : 0.0f;
+                }
+            }
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t row = wr0 + ib * 32 + acc_row(v, lane);
-                if (row >= d.m) continue;
-                const int64_t idx = row * d.n + col;
-                if (d.xbf16) {
-                    MEO_GLOBAL uint16_t* p = gst<uint16_t>(static_cast<uint16_t*>(d.x) + idx);
-                    const float w = __uint_as_float(static_cast<uint32_t>(*p) << 16);
-                    *p = static_cast<uint16_t>(bf16_bits(a.decay * w - a.coef * acc[ib][jb][v]));
-                } else {
-                    MEO_GLOBAL float* p = gst<float>(static_cast<float*>(d.x) + idx);
-                    *p = a.decay * *p - a.coef * acc[ib][jb][v];
-                }
+                if (!cok || row >= d.m) continue;
+                const float nw = a.decay * w[v] - a.coef * acc[ib][jb][v];
+                if (d.xbf16) *gst<uint16_t>(static_cast<uint16_t*>(d.x) + row * d.n + col) = static_cast<uint16_t>(bf16_bits(nw));
+                else *gst<float>(static_cast<float*>(d.x) + row * d.n + col) = nw;
             }
         }
 }
