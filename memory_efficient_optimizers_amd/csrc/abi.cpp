@@ -1702,16 +1702,19 @@ int meo_galore_refresh(const meo_galore_hparams* hp, int32_t n, const meo_tensor
     auto cnt = [&](int l) { return p->count[l]; };
     if (cnt(kRfOne) == 0) return MEO_OK;
     PassTimer pt(s);
-    // Cholesky-QR applied twice to the p x d block in `buf` (the other iterate
-    // buffer is scratch); the orthonormal rows end in `buf`.
+    // Cholesky-QR of the p x d block in `src`, into `dst`.
+    auto cholqr = [&](int src, int dst) {
+        launch_rf_gram(tab(kRfGram), cnt(kRfGram), src, false, s);
+        launch_rf_chol(tab(kRfOne), cnt(kRfOne), s);
+        launch_rf_trmm(tab(kRfCols), cnt(kRfCols), src, dst, s);
+    };
+    // Twice, for rows orthonormal to fp32 rounding (the start block and the block
+    // of the Rayleigh-Ritz step); once between products, where a well-conditioned
+    // basis is enough. The result ends in `buf`.
     auto cholqr2 = [&](int buf) {
         const int other = buf == kRbQa ? kRbQb : kRbQa;
-        launch_rf_gram(tab(kRfGram), cnt(kRfGram), buf, false, s);
-        launch_rf_chol(tab(kRfOne), cnt(kRfOne), s);
-        launch_rf_trmm(tab(kRfCols), cnt(kRfCols), buf, other, s);
-        launch_rf_gram(tab(kRfGram), cnt(kRfGram), other, false, s);
-        launch_rf_chol(tab(kRfOne), cnt(kRfOne), s);
-        launch_rf_trmm(tab(kRfCols), cnt(kRfCols), other, buf, s);
+        cholqr(buf, other);
+        cholqr(other, buf);
     };
     auto times_xt = [&](int src, int dst) {  // Y^T = Q^T X^T
         launch_rf_gemm(tab(kRfG0N), cnt(kRfG0N), 0, src, dst, false, s);
@@ -1721,9 +1724,14 @@ int meo_galore_refresh(const meo_galore_hparams* hp, int32_t n, const meo_tensor
     cholqr2(kRbQa);
     for (int i = 0; i < kRfIters; ++i) {
         times_xt(kRbQa, kRbYt);
-        launch_rf_gemm(tab(kRfG1N), cnt(kRfG1N), 1, kRbYt, kRbQa, false, s);  // Z^T = Y^T X
-        launch_rf_gemm(tab(kRfG1T), cnt(kRfG1T), 1, kRbYt, kRbQa, true, s);
-        cholqr2(kRbQa);
+        launch_rf_gemm(tab(kRfG1N), cnt(kRfG1N), 1, kRbYt, kRbQb, false, s);  // Z^T = Y^T X
+        launch_rf_gemm(tab(kRfG1T), cnt(kRfG1T), 1, kRbYt, kRbQb, true, s);
+        if (i + 1 < kRfIters) {
+            cholqr(kRbQb, kRbQa);
+        } else {
+            cholqr(kRbQb, kRbQa);
+            cholqr2(kRbQa);
+        }
     }
     times_xt(kRbQa, kRbYt);
     launch_rf_gram(tab(kRfGram), cnt(kRfGram), kRbYt, true, s);

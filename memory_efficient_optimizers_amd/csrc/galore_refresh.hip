@@ -36,8 +36,8 @@ __device__ __forceinline__ f32x16 mfma32(const bfv8& a, const bfv8& b, const f32
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float* rbuf(const RDesc& d, int which) {
-    return which == kRbQa ? d.qa : (which == kRbQb ? d.qb : d.yt);
+__device__ __forceinline__ float* rbuf(float* qa, float* qb, float* yt, int which) {
+    return which == kRbQa ? qa : (which == kRbQb ? qb : yt);
 }
 
 // splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
@@ -75,14 +75,18 @@ __device__ __forceinline__ u32x4 ld_row8(const uint16_t* p, int64_t rows, int64_
 
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
-// Block-wide sum / max of doubles (256 threads).
+constexpr int kRfBig = 1024;  // threads of the one-block-per-tensor kernels
+
+// Block-wide sum / max of doubles over kRfBig threads (every thread gets the result).
 __device__ double rf_sum_d(double v, double* lds) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
     __syncthreads();
-    return (lds[0] + lds[1]) + (lds[2] + lds[3]);
+    double s = 0.0;
+    for (int w = 0; w < kRfBig / 64; ++w) s += lds[w];
+    return s;
 }
 
 __device__ double rf_max_d(double v, double* lds) {
@@ -91,25 +95,35 @@ __device__ double rf_max_d(double v, double* lds) {
     __syncthreads();
     if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
     __syncthreads();
-    return fmax(fmax(lds[0], lds[1]), fmax(lds[2], lds[3]));
+    double s = lds[0];
+    for (int w = 1; w < kRfBig / 64; ++w) s = fmax(s, lds[w]);
+    return s;
 }
 
 }  // namespace
 
 // ------------------------------------------------------------------ start block
 
-// Gaussian p x d block, one normal per element from the counter (tensor, index).
+// Start block: the stored projector's rows (U^T, zero before the first refresh)
+// plus a Gaussian block scaled by 1e-3 / sqrt(d), one normal per element from
+// the counter (tensor, index). The Gaussian keeps the block of full rank when
+// there is no stored basis (or it has lost rank); a stored basis that is close
+// to the new one starts the iteration near its end.
 __global__ __launch_bounds__(kThreads) void k_rf_init(RTable t, int dst) {
     const int2 it = t.items[blockIdx.x];
     const RDesc d = t.desc[it.x];
-    float* out = rbuf(d, dst);
+    float* out = rbuf(d.qa, d.qb, d.yt, dst);
     const int64_t total = static_cast<int64_t>(d.p) * d.d;
     const int64_t base = static_cast<int64_t>(it.y) * kThreads * kVec;
     const uint64_t key = static_cast<uint64_t>(d.seed) << 40;
+    const float eps = 1e-3f / sqrtf(static_cast<float>(d.d));
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
         const int64_t i = base + static_cast<int64_t>(e) * kThreads + threadIdx.x;
-        if (i < total) out[i] = normal_at(key + static_cast<uint64_t>(i));
+        if (i < total) {
+            const float u = __uint_as_float(static_cast<uint32_t>(d.ut[i]) << 16);
+            out[i] = fmaf(eps, normal_at(key + static_cast<uint64_t>(i)), u);
+        }
     }
 }
 
@@ -130,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void k_rf_gemm(RTable t, int stage, int s
     __shared__ __attribute__((aligned(16))) uint16_t bs[kGaTile * kRfPitch];
     const int2 it = t.items[blockIdx.x];
     const RDesc d = t.desc[it.x];
-    const float* A = rbuf(d, src);
-    float* C = rbuf(d, dst);
+    const float* A = rbuf(d.qa, d.qb, d.yt, src);
+    float* C = rbuf(d.qa, d.qb, d.yt, dst);
     const int64_t K = stage == 0 ? d.d : d.D;
     const int64_t L = stage == 0 ? d.D : d.d;
     const int64_t l0 = static_cast<int64_t>(it.y) * kGaTile;
@@ -147,21 +161,43 @@ __global__ __launch_bounds__(kThreads) void k_rf_gemm(RTable t, int stage, int s
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.0f;
 
-    for (int64_t k0 = 0; k0 < K; k0 += kRfKb) {
-        // A: rows 0..255 x 32 columns, fp32 -> high and low bf16 planes.
-        for (int c = threadIdx.x; c < kRfMaxP * (kRfKb / 8); c += kThreads) {
-            const int row = c >> 2, kc = (c & 3) * 8;
-            float v[8];
-            const int64_t col = k0 + kc;
+    // Staging: a thread's chunks of the next block are loaded into registers while
+    // the current block is multiplied, then written to LDS.
+    constexpr int kAPer = kRfMaxP * (kRfKb / 8) / kThreads;   // 8-float chunks of A
+    constexpr int kBPer = kGaTile * (kRfKb / 8) / kThreads;   // 8-bf16 chunks of B
+    f32x4 ra[kAPer][2];
+    u32x4 rb[kBPer];
+    auto fetch = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < kAPer; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            const int row = c >> 2;
+            const int64_t col = k0 + (c & 3) * 8;
             if (row < P && avec && col + 8 <= K) {
-                const f32x4 x0 = *gld<f32x4>(A + row * K + col);
-                const f32x4 x1 = *gld<f32x4>(A + row * K + col + 4);
-                v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
-                v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+                ra[i][0] = *gld<f32x4>(A + row * K + col);
+                ra[i][1] = *gld<f32x4>(A + row * K + col + 4);
             } else {
+                float v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = (row < P && col + e < K) ? A[row * K + col + e] : 0.0f;
+                ra[i][0] = f32x4{v[0], v[1], v[2], v[3]};
+                ra[i][1] = f32x4{v[4], v[5], v[6], v[7]};
             }
+        }
+#pragma unroll
+        for (int i = 0; i < kBPer; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            if (!Trans) rb[i] = ld_row8(d.g, L, K, l0 + (c >> 2), k0 + (c & 3) * 8, d.gvec);
+            else rb[i] = ld_row8(d.g, K, L, k0 + (c >> 3), l0 + (c & 7) * 8, d.gvec);
+        }
+    };
+    auto put = [&]() {
+#pragma unroll
+        for (int i = 0; i < kAPer; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            const int row = c >> 2, kc = (c & 3) * 8;
+            const float v[8] = {ra[i][0].x, ra[i][0].y, ra[i][0].z, ra[i][0].w,
+                                ra[i][1].x, ra[i][1].y, ra[i][1].z, ra[i][1].w};
             float hi[8], lo[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -171,16 +207,14 @@ __global__ __launch_bounds__(kThreads) void k_rf_gemm(RTable t, int stage, int s
             *reinterpret_cast<u32x4*>(ah + row * kRfPitch + kc) = pack_bf16x8(hi);
             *reinterpret_cast<u32x4*>(al + row * kRfPitch + kc) = pack_bf16x8(lo);
         }
-        if (!Trans) {  // B rows l0.. of G [L][K]
-            for (int c = threadIdx.x; c < kGaTile * (kRfKb / 8); c += kThreads) {
-                const int l = c >> 2, kc = (c & 3) * 8;
-                *reinterpret_cast<u32x4*>(bs + l * kRfPitch + kc) = ld_row8(d.g, L, K, l0 + l, k0 + kc, d.gvec);
-            }
-        } else {       // B[l][k] = G[k0 + k][l0 + l], G [K][L]
-            for (int c = threadIdx.x; c < kRfKb * (kGaTile / 8); c += kThreads) {
+#pragma unroll
+        for (int i = 0; i < kBPer; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            if (!Trans) {
+                *reinterpret_cast<u32x4*>(bs + (c >> 2) * kRfPitch + (c & 3) * 8) = rb[i];
+            } else {
                 const int k = c >> 3, lc = (c & 7) * 8;
-                const u32x4 v = ld_row8(d.g, K, L, k0 + k, l0 + lc, d.gvec);
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     bs[(lc + 2 * e) * kRfPitch + k] = static_cast<uint16_t>(w[e] & 0xffffu);
@@ -188,7 +222,12 @@ __global__ __launch_bounds__(kThreads) void k_rf_gemm(RTable t, int stage, int s
                 }
             }
         }
+    };
+    fetch(0);
+    for (int64_t k0 = 0; k0 < K; k0 += kRfKb) {
+        put();
         __syncthreads();
+        if (k0 + kRfKb < K) fetch(k0 + kRfKb);
         if (active) {
 #pragma unroll
             for (int ks = 0; ks < kRfKb; ks += 16) {
@@ -243,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_rf_gram(RTable t, int src, int ove
     __shared__ float sb[64][33];
     const int2 it = t.items[blockIdx.x];
     const RDesc d = t.desc[it.x];
-    const float* A = rbuf(d, src);
+    const float* A = rbuf(d.qa, d.qb, d.yt, src);
     const int64_t K = over_long ? d.D : d.d;
     const int P = d.p;
     const int tp = (P + 63) / 64;
@@ -296,50 +335,62 @@ void launch_rf_gram(const RTable& t, int64_t n, int src, bool over_long, hipStre
 
 // One block per tensor: S <- L (lower, in place) with S + 1e-13 max(diag S) I =
 // L L^T, then W <- L^-1 (lower). The shift keeps a numerically rank-deficient
-// block finite; a pivot that is not positive is replaced by 1.
-__global__ __launch_bounds__(kThreads) void k_rf_chol(RTable t) {
-    __shared__ double red[kWaves];
+// block finite; a pivot that is not positive is replaced by 1. The inverse is
+// taken 16 columns at a time, one wave per column, the column kept in LDS and
+// each row's sum split over the wave's lanes.
+__global__ __launch_bounds__(kRfBig) void k_rf_chol(RTable t) {
+    __shared__ double red[kRfBig / 64];
     __shared__ double inv;
+    __shared__ double col[kRfBig / 64][kRfMaxP];
     const RDesc d = t.desc[t.items[blockIdx.x].x];
     double* S = d.s;
     double* W = d.w;
     const int P = d.p;
+    const int tid = threadIdx.x;
     double mx = 0.0;
-    for (int i = threadIdx.x; i < P; i += kThreads) mx = fmax(mx, S[i * P + i]);
+    for (int i = tid; i < P; i += kRfBig) mx = fmax(mx, S[i * P + i]);
     mx = rf_max_d(mx, red);
     const double shift = 1e-13 * mx;
-    for (int i = threadIdx.x; i < P; i += kThreads) S[i * P + i] += shift;
+    for (int i = tid; i < P; i += kRfBig) S[i * P + i] += shift;
     __syncthreads();
     for (int k = 0; k < P; ++k) {
-        if (threadIdx.x == 0) {
+        if (tid == 0) {
             const double piv = S[k * P + k];
             const double lkk = (piv > 0.0 && piv < INFINITY) ? sqrt(piv) : 1.0;
             S[k * P + k] = lkk;
             inv = 1.0 / lkk;
         }
         __syncthreads();
-        for (int i = k + 1 + threadIdx.x; i < P; i += kThreads) S[i * P + k] *= inv;
+        for (int i = k + 1 + tid; i < P; i += kRfBig) S[i * P + k] *= inv;
         __syncthreads();
-        const int nr = P - k - 1;
-        for (int idx = threadIdx.x; idx < nr * nr; idx += kThreads) {
-            const int i = k + 1 + idx / nr, j = k + 1 + idx % nr;
-            if (j <= i) S[i * P + j] = fma(-S[i * P + k], S[j * P + k], S[i * P + j]);
+        const int j = k + 1 + (tid & (kRfMaxP - 1));
+        if (j < P) {
+            const double sjk = S[j * P + k];
+            for (int i = k + 1 + (tid >> 8); i < P; i += kRfBig / kRfMaxP)
+                if (j <= i) S[i * P + j] = fma(-S[i * P + k], sjk, S[i * P + j]);
         }
         __syncthreads();
     }
-    for (int j = threadIdx.x; j < P; j += kThreads) {
-        for (int i = 0; i < j; ++i) W[i * P + j] = 0.0;
-        W[j * P + j] = 1.0 / S[j * P + j];
+    // W = L^-1: column j solves L w = e_j; w_i = -(sum_{j<=k<i} L_ik w_k) / L_ii.
+    const int lane = tid & 63, wv = tid >> 6;
+    double* cw = col[wv];
+    for (int j = wv; j < P; j += kRfBig / 64) {
+        for (int i = lane; i < P; i += 64) cw[i] = 0.0;
+        if (lane == 0) cw[j] = 1.0 / S[j * P + j];
         for (int i = j + 1; i < P; ++i) {
             double acc = 0.0;
-            for (int k = j; k < i; ++k) acc = fma(S[i * P + k], W[k * P + j], acc);
-            W[i * P + j] = -acc / S[i * P + i];
+            for (int k = j + lane; k < i; k += 64) acc = fma(S[i * P + k], cw[k], acc);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+            if (lane == 0) cw[i] = -acc / S[i * P + i];
+            __builtin_amdgcn_wave_barrier();  // lane 0's write precedes the next row's reads
         }
+        for (int i = lane; i < P; i += 64) W[i * P + j] = cw[i];
     }
 }
 
 void launch_rf_chol(const RTable& t, int64_t n, hipStream_t s) {
-    if (n > 0) hipLaunchKernelGGL(k_rf_chol, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t);
+    if (n > 0) hipLaunchKernelGGL(k_rf_chol, dim3(static_cast<uint32_t>(n)), dim3(kRfBig), 0, s, t);
 }
 
 // dst[a][j] = sum_{b <= a} W[a][b] src[b][j]: 32 columns of the p x d block per
@@ -348,8 +399,8 @@ __global__ __launch_bounds__(kThreads) void k_rf_trmm(RTable t, int src, int dst
     __shared__ float zs[kRfMaxP][33];
     const int2 it = t.items[blockIdx.x];
     const RDesc d = t.desc[it.x];
-    const float* Z = rbuf(d, src);
-    float* Q = rbuf(d, dst);
+    const float* Z = rbuf(d.qa, d.qb, d.yt, src);
+    float* Q = rbuf(d.qa, d.qb, d.yt, dst);
     const int P = d.p;
     const int64_t j0 = static_cast<int64_t>(it.y) * 32;
     for (int c = threadIdx.x; c < P * 32; c += kThreads) {
@@ -360,9 +411,17 @@ __global__ __launch_bounds__(kThreads) void k_rf_trmm(RTable t, int src, int dst
     const int jj = threadIdx.x & 31, ag = threadIdx.x >> 5;
     if (j0 + jj >= d.d) return;
     for (int a = ag; a < P; a += kThreads / 32) {
-        double acc = 0.0;
-        for (int b = 0; b <= a; ++b) acc = fma(d.w[a * P + b], static_cast<double>(zs[b][jj]), acc);
-        Q[a * static_cast<int64_t>(d.d) + j0 + jj] = static_cast<float>(acc);
+        const double* wa = d.w + a * P;
+        double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+        int b = 0;
+        for (; b + 4 <= a + 1; b += 4) {
+            s0 = fma(wa[b], static_cast<double>(zs[b][jj]), s0);
+            s1 = fma(wa[b + 1], static_cast<double>(zs[b + 1][jj]), s1);
+            s2 = fma(wa[b + 2], static_cast<double>(zs[b + 2][jj]), s2);
+            s3 = fma(wa[b + 3], static_cast<double>(zs[b + 3][jj]), s3);
+        }
+        for (; b <= a; ++b) s0 = fma(wa[b], static_cast<double>(zs[b][jj]), s0);
+        Q[a * static_cast<int64_t>(d.d) + j0 + jj] = static_cast<float>((s0 + s1) + (s2 + s3));
     }
 }
 
@@ -379,32 +438,38 @@ void launch_rf_trmm(const RTable& t, int64_t n, int src, int dst, hipStream_t s)
 // formulation: tan of the angle from theta = (S_jj - S_ii) / (2 S_ij)). Stops when
 // the off-diagonal norm is below 1e-13 of the whole, or after 16 sweeps. On exit
 // S holds the eigenvalues on its diagonal and W the eigenvectors as columns.
-__global__ __launch_bounds__(kThreads) void k_rf_jacobi(RTable t) {
+__global__ __launch_bounds__(kRfBig) void k_rf_jacobi(RTable t) {
     __shared__ double cc[kRfMaxP + 1], tt[kRfMaxP + 1];
     __shared__ int qq[kRfMaxP + 1];
-    __shared__ double red[kWaves];
+    __shared__ double red[kRfBig / 64];
     const RDesc d = t.desc[t.items[blockIdx.x].x];
     const int P = d.p;
     const int Pe = P + (P & 1);  // an odd size gets a dummy index P
+    const int tid = threadIdx.x;
+    const int b = tid & (kRfMaxP - 1), a0 = tid >> 8;  // column, first row of this thread
+    constexpr int kRowStep = kRfBig / kRfMaxP;
     double* S = d.s;
     double* W = d.w;
     double* S2 = d.s2;
     double* W2 = d.w2;
-    for (int i = threadIdx.x; i < P * P; i += kThreads) W[i] = (i / P == i % P) ? 1.0 : 0.0;
+    if (b < P)
+        for (int a = a0; a < P; a += kRowStep) W[a * P + b] = a == b ? 1.0 : 0.0;
     __syncthreads();
     for (int sweep = 0; sweep < 16; ++sweep) {
         double off = 0.0, tot = 0.0;
-        for (int i = threadIdx.x; i < P * P; i += kThreads) {
-            const double v = S[i] * S[i];
-            tot += v;
-            if (i / P != i % P) off += v;
-        }
+        if (b < P)
+            for (int a = a0; a < P; a += kRowStep) {
+                const double v = S[a * P + b] * S[a * P + b];
+                tot += v;
+                if (a != b) off += v;
+            }
         off = rf_sum_d(off, red);
         tot = rf_sum_d(tot, red);
         if (!(off > 1e-26 * tot)) break;  // uniform: every thread holds the same sums
         for (int round = 0; round < Pe - 1; ++round) {
             // pairs of the circle method: 0 with 1 + round, and the rest mirrored
-            for (int k = threadIdx.x; k < Pe / 2; k += kThreads) {
+            if (tid < Pe / 2) {
+                const int k = tid;
                 int i, j;
                 if (k == 0) {
                     i = 0;
@@ -428,34 +493,37 @@ __global__ __launch_bounds__(kThreads) void k_rf_jacobi(RTable t) {
                 cc[j] = c; tt[j] = s; qq[j] = i;
             }
             __syncthreads();
-            for (int idx = threadIdx.x; idx < P * P; idx += kThreads) {
-                const int a = idx / P, b = idx % P;
-                const int qa = qq[a], qb = qq[b];
-                const double ca = cc[a], ta = tt[a], cb = cc[b], tb = tt[b];
-                double v = ca * cb * S[a * P + b];
-                if (qb < P) v = fma(ca * tb, S[a * P + qb], v);
-                if (qa < P) v = fma(ta * cb, S[qa * P + b], v);
-                if (qa < P && qb < P) v = fma(ta * tb, S[qa * P + qb], v);
-                S2[idx] = v;
-                double w = cb * W[idx];
-                if (qb < P) w = fma(tb, W[a * P + qb], w);
-                W2[idx] = w;
+            if (b < P) {
+                const int qb = qq[b];
+                const double cb = cc[b], tb = tt[b];
+                for (int a = a0; a < P; a += kRowStep) {
+                    const int qa = qq[a];
+                    const double ca = cc[a], ta = tt[a];
+                    double v = ca * cb * S[a * P + b];
+                    if (qb < P) v = fma(ca * tb, S[a * P + qb], v);
+                    if (qa < P) v = fma(ta * cb, S[qa * P + b], v);
+                    if (qa < P && qb < P) v = fma(ta * tb, S[qa * P + qb], v);
+                    S2[a * P + b] = v;
+                    double w = cb * W[a * P + b];
+                    if (qb < P) w = fma(tb, W[a * P + qb], w);
+                    W2[a * P + b] = w;
+                }
             }
             __syncthreads();
             double* x = S; S = S2; S2 = x;
             x = W; W = W2; W2 = x;
         }
     }
-    if (S != d.s) {  // leave the result in s and w
-        for (int i = threadIdx.x; i < P * P; i += kThreads) {
-            d.s[i] = S[i];
-            d.w[i] = W[i];
+    if (S != d.s && b < P) {  // leave the result in s and w
+        for (int a = a0; a < P; a += kRowStep) {
+            d.s[a * P + b] = S[a * P + b];
+            d.w[a * P + b] = W[a * P + b];
         }
     }
 }
 
 void launch_rf_jacobi(const RTable& t, int64_t n, hipStream_t s) {
-    if (n > 0) hipLaunchKernelGGL(k_rf_jacobi, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t);
+    if (n > 0) hipLaunchKernelGGL(k_rf_jacobi, dim3(static_cast<uint32_t>(n)), dim3(kRfBig), 0, s, t);
 }
 
 // ------------------------------------------------------------------ basis and storage
@@ -468,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void k_rf_basis(RTable t, int src) {
     __shared__ int ord[kRfMaxP];
     const int2 it = t.items[blockIdx.x];
     const RDesc d = t.desc[it.x];
-    const float* Q = rbuf(d, src);
+    const float* Q = rbuf(d.qa, d.qb, d.yt, src);
     const int P = d.p;
     for (int i = threadIdx.x; i < P; i += kThreads) {
         const double li = d.s[i * P + i];
@@ -489,9 +557,14 @@ __global__ __launch_bounds__(kThreads) void k_rf_basis(RTable t, int src) {
     if (j0 + jj >= d.d) return;
     for (int c = cg; c < d.r; c += kThreads / 32) {
         const int oc = ord[c];
-        double acc = 0.0;
-        for (int b = 0; b < P; ++b) acc = fma(d.w[b * P + oc], static_cast<double>(zs[b][jj]), acc);
-        d.yt[c * static_cast<int64_t>(d.d) + j0 + jj] = static_cast<float>(acc);
+        double s0 = 0.0, s1 = 0.0;
+        int b = 0;
+        for (; b + 2 <= P; b += 2) {
+            s0 = fma(d.w[b * P + oc], static_cast<double>(zs[b][jj]), s0);
+            s1 = fma(d.w[(b + 1) * P + oc], static_cast<double>(zs[b + 1][jj]), s1);
+        }
+        if (b < P) s0 = fma(d.w[b * P + oc], static_cast<double>(zs[b][jj]), s0);
+        d.yt[c * static_cast<int64_t>(d.d) + j0 + jj] = static_cast<float>(s0 + s1);
     }
 }
 
