@@ -295,7 +295,9 @@ def galore_cpu_baseline(shapes, rank: int, scale: float, param_bf16: bool, budge
 
 def galore_bench(torch, _lib, workloads, args) -> int:
     """The GaLore step over the Llama-7B-shaped list: every 2-D tensor projected at
-    rank 256 (scale 0.25), norms by flat AdamW. The first warmup step is a refresh
+    rank 256 (scale 0.25), norms by flat AdamW. Gradients of 2-D tensors are a
+    rank-256 signal plus noise; the step's time does not depend on the values,
+    the refresh's convergence does. The first warmup step is a refresh
     step (t = 1), which computes every projector; the timed steps are not (t - 1 is
     not a multiple of update_proj_gap). The refresh is timed on its own afterwards,
     started from the stored bases as every refresh after the first is
@@ -311,7 +313,21 @@ def galore_bench(torch, _lib, workloads, args) -> int:
     grads = flat_views(torch, shapes, torch.bfloat16, dev)
     for p, g in zip(params, grads):
         p.copy_(0.02 * torch.randn(p.shape, generator=gen, device=dev))
-        g.copy_(1e-3 * torch.randn(g.shape, generator=gen, device=dev))
+        if p.dim() == 2:
+            # rank-`rank` signal plus noise (entries ~1e-3): singular values decaying
+            # by 0.99 per index, then a gap to a noise floor about a tenth of the
+            # last one, the low-rank structure the projection relies on
+            m, n = p.shape
+            k = min(rank, m, n)
+            a = torch.randn(m, k, generator=gen, device=dev)
+            b = torch.randn(n, k, generator=gen, device=dev)
+            sv = 0.99 ** torch.arange(k, device=dev, dtype=torch.float32)
+            sig = (a * sv) @ b.T
+            sig *= 1e-3 / sig.std()
+            g.copy_(sig + 3e-5 * torch.randn(m, n, generator=gen, device=dev))
+            del a, b, sig
+        else:
+            g.copy_(1e-3 * torch.randn(g.shape, generator=gen, device=dev))
     states = []
     for p in params:
         st = {}
