@@ -1547,6 +1547,8 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
             d.nl = reinterpret_cast<uint16_t*>(wb + (static_cast<int64_t>(d.D) * d.r * 2 + 255) / 256 * 256);
             d.vec = aligned16(d.g) && aligned16(d.u) && aligned16(d.ut) && d.n % 8 == 0 && d.d % 8 == 0 &&
                     d.r % 8 == 0;
+            d.rvec = aligned16(d.em) && aligned16(d.ev) && d.r % 8 == 0;
+            d.wvec = aligned16(d.x) && d.n % 8 == 0;
             const bool is_left = d.m < d.n;
             d.btj = static_cast<int32_t>(is_left ? ceil_div(d.n, kGaTile) : ceil_div(d.n, kGaWide));
             (is_left ? left : right).push_back(d);

@@ -24,6 +24,8 @@ struct GDesc {
     int32_t m, n, D, d, r;
     int32_t xbf16;      // parameter is bf16
     int32_t vec;        // rows of g, u, ut, nh and the moments may use 16-byte accesses
+    int32_t rvec;       // moment rows ([D][r] fp32) may use 16-byte accesses
+    int32_t wvec;       // parameter rows may use 16-byte accesses
     int32_t btj;        // back-projection tiles along the tile's second dimension
 };
 

@@ -121,6 +121,32 @@ struct TransStage {
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 
+// Epilogue exchange: a wave's 32 x 64 half tile (accumulator blocks (ib, 0) and
+// (ib, 1)) goes through LDS so that each lane then holds 8 consecutive columns
+// of a row, for 16-byte loads and stores of the row-major outputs. Lane l gets
+// rows (l >> 3) + 8 q (q < 4) and columns 8 (l & 7) .. 8 (l & 7) + 7. Only the
+// wave itself touches its LDS region, and its LDS accesses run in program order.
+constexpr int kEpPitch = 68;  // floats per LDS row of the exchange
+constexpr int kEpWave = 32 * kEpPitch;
+
+__device__ __forceinline__ void ep_spill(const f32x16& a0, const f32x16& a1, float* lw, int lane) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        lw[acc_row(v, lane) * kEpPitch + (lane & 31)] = a0[v];
+        lw[acc_row(v, lane) * kEpPitch + 32 + (lane & 31)] = a1[v];
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ void ep_gather(const float* lw, int lane, int q, float* c) {
+    const float* p = lw + ((lane >> 3) + 8 * q) * kEpPitch + (lane & 7) * 8;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
+    c[0] = x0.x; c[1] = x0.y; c[2] = x0.z; c[3] = x0.w;
+    c[4] = x1.x; c[5] = x1.y; c[6] = x1.z; c[7] = x1.w;
+    __builtin_amdgcn_wave_barrier();
+}
+
 // ------------------------------------------------------------------ projection + AdamW
 
 template <bool Left>
@@ -172,41 +198,67 @@ __global__ __launch_bounds__(kThreads) void k_galore_project(GTable t, GaArgs a)
         __syncthreads();
     }
     if (!active) return;
-    // AdamW on the tile of R: lanes 0..31 of an accumulator register hold 32
-    // consecutive columns of one row. The moments of a 32x32 block are loaded
-    // together, then updated and stored.
+    // AdamW on the tile of R, rows of 8 columns per lane (see ep_spill): moments
+    // read and written, N's planes written, 16 bytes at a time where rows allow.
+    float* lw = reinterpret_cast<float*>(sb) + wave * kEpWave;
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
+    for (int ib = 0; ib < 2; ++ib) {
+        ep_spill(acc[ib][0], acc[ib][1], lw, lane);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const int col = wave * 64 + jb * 32 + acc_col(lane);
-            const bool cok = col < d.r;
-            float m0[16], v0[16];
+        for (int q = 0; q < 4; ++q) {
+            const int64_t row = i0 + ib * 32 + (lane >> 3) + 8 * q;
+            const int col = wave * 64 + (lane & 7) * 8;
+            if (row >= d.D || col >= d.r) continue;
+            float rv[8], m[8], v[8], nh[8], nl[8];
+            ep_gather(lw, lane, q, rv);
+            const int64_t idx = row * d.r + col;
+            const bool full = d.rvec && col + 8 <= d.r;
+            if (full) {
+                const f32x4 m0 = *gld<f32x4>(d.em + idx), m1 = *gld<f32x4>(d.em + idx + 4);
+                const f32x4 v0 = *gld<f32x4>(d.ev + idx), v1 = *gld<f32x4>(d.ev + idx + 4);
+                m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w; m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
+                v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+            } else {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = i0 + ib * 32 + acc_row(v, lane);
-                const bool ok = cok && row < d.D;
-                const int64_t idx = row * d.r + col;
-                m0[v] = ok ? *gld<float>(d.em + idx) : 0.0f;
-                v0[v] = ok ? *gld<float>(d.ev + idx) : 0.0f;
+                for (int e = 0; e < 8; ++e) {
+                    m[e] = col + e < d.r ? *gld<float>(d.em + idx + e) : 0.0f;
+                    v[e] = col + e < d.r ? *gld<float>(d.ev + idx + e) : 0.0f;
+                }
             }
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = i0 + ib * 32 + acc_row(v, lane);
-                if (!cok || row >= d.D) continue;
-                const int64_t idx = row * d.r + col;
-                const float rv = acc[ib][jb][v];
-                const float m = fmaf(a.beta1, m0[v], a.omb1 * rv);
-                const float vv = fmaf(a.beta2, v0[v], a.omb2 * (rv * rv));
-                *gst<float>(d.em + idx) = m;
-                *gst<float>(d.ev + idx) = vv;
-                const float n = (m * a.inv_bc1) / (sqrtf(vv * a.inv_bc2) + a.eps);
-                const __bf16 hi = static_cast<__bf16>(n);
-                const __bf16 lo = static_cast<__bf16>(n - static_cast<float>(hi));
-                *gst<uint16_t>(d.nh + idx) = __builtin_bit_cast(uint16_t, hi);
-                *gst<uint16_t>(d.nl + idx) = __builtin_bit_cast(uint16_t, lo);
+            for (int e = 0; e < 8; ++e) {
+                m[e] = fmaf(a.beta1, m[e], a.omb1 * rv[e]);
+                v[e] = fmaf(a.beta2, v[e], a.omb2 * (rv[e] * rv[e]));
+                const float n = (m[e] * a.inv_bc1) / (sqrtf(v[e] * a.inv_bc2) + a.eps);
+                nh[e] = round_bf16(n);
+                nl[e] = n - nh[e];
+            }
+            if (full) {
+                *gst<f32x4>(d.em + idx) = f32x4{m[0], m[1], m[2], m[3]};
+                *gst<f32x4>(d.em + idx + 4) = f32x4{m[4], m[5], m[6], m[7]};
+                *gst<f32x4>(d.ev + idx) = f32x4{v[0], v[1], v[2], v[3]};
+                *gst<f32x4>(d.ev + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < d.r) {
+                        *gst<float>(d.em + idx + e) = m[e];
+                        *gst<float>(d.ev + idx + e) = v[e];
+                    }
+            }
+            if (d.vec && col + 8 <= d.r) {  // the planes are 256-byte aligned; rows of r % 8 == 0
+                *gst<u32x4>(d.nh + idx) = pack_bf16x8(nh);
+                *gst<u32x4>(d.nl + idx) = pack_bf16x8(nl);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < d.r) {
+                        *gst<uint16_t>(d.nh + idx + e) = static_cast<uint16_t>(bf16_bits(nh[e]));
+                        *gst<uint16_t>(d.nl + idx + e) = static_cast<uint16_t>(bf16_bits(nl[e]));
+                    }
             }
         }
+    }
 }
 
 void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool left, hipStream_t s) {
@@ -282,42 +334,63 @@ __global__ __launch_bounds__(kThreads) void k_galore_back(GTable t, GaArgs a) {
         }
         __syncthreads();
     }
-    // W <- decay W - coef C; lanes 0..31 of a register hold 32 consecutive
-    // columns. The parameters of a 32x32 block are loaded together, then stored.
+    // W <- decay W - coef C, rows of 8 columns per lane (see ep_spill), 16 bytes at
+    // a time where rows allow.
     const int64_t wr0 = Left ? r0 + wave * 64 : r0;
     const int64_t wc0 = Left ? c0 : c0 + wave * 64;
+    float* lw = reinterpret_cast<float*>(su) + wave * kEpWave;
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
+    for (int ib = 0; ib < 2; ++ib) {
+        ep_spill(acc[ib][0], acc[ib][1], lw, lane);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const int64_t col = wc0 + jb * 32 + acc_col(lane);
-            const bool cok = col < d.n;
-            float w[16];
+        for (int q = 0; q < 4; ++q) {
+            const int64_t row = wr0 + ib * 32 + (lane >> 3) + 8 * q;
+            const int64_t col = wc0 + (lane & 7) * 8;
+            if (row >= d.m || col >= d.n) continue;
+            float c[8], w[8];
+            ep_gather(lw, lane, q, c);
+            const int64_t idx = row * d.n + col;
+            const bool full = d.wvec && col + 8 <= d.n;
             if (d.xbf16) {
-                const uint16_t* xp = static_cast<const uint16_t*>(d.x);
+                uint16_t* xp = static_cast<uint16_t*>(d.x) + idx;
+                if (full) {
+                    bf16x8(*gld<u32x4>(xp), w);
+                } else {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int64_t row = wr0 + ib * 32 + acc_row(v, lane);
-                    w[v] = (cok && row < d.m) ? __uint_as_float(static_cast<uint32_t>(*gld<uint16_t>(xp + row * d.n + col)) << 16)
-                                              : 0.0f;
+                    for (int e = 0; e < 8; ++e)
+                        w[e] = col + e < d.n ? __uint_as_float(static_cast<uint32_t>(*gld<uint16_t>(xp + e)) << 16) : 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = a.decay * w[e] - a.coef * c[e];
+                if (full) {
+                    *gst<u32x4>(xp) = pack_bf16x8(w);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (col + e < d.n) *gst<uint16_t>(xp + e) = static_cast<uint16_t>(bf16_bits(w[e]));
                 }
             } else {
-                const float* xp = static_cast<const float*>(d.x);
+                float* xp = static_cast<float*>(d.x) + idx;
+                if (full) {
+                    const f32x4 x0 = *gld<f32x4>(xp), x1 = *gld<f32x4>(xp + 4);
+                    w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w; w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+                } else {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int64_t row = wr0 + ib * 32 + acc_row(v, lane);
-                    w[v] = (cok && row < d.m) ? *gld<float>(xp + row * d.n + col) : 0.0f;
+                    for (int e = 0; e < 8; ++e) w[e] = col + e < d.n ? *gld<float>(xp + e) : 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = a.decay * w[e] - a.coef * c[e];
+                if (full) {
+                    *gst<f32x4>(xp) = f32x4{w[0], w[1], w[2], w[3]};
+                    *gst<f32x4>(xp + 4) = f32x4{w[4], w[5], w[6], w[7]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (col + e < d.n) *gst<float>(xp + e) = w[e];
                 }
             }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = wr0 + ib * 32 + acc_row(v, lane);
-                if (!cok || row >= d.m) continue;
-                const float nw = a.decay * w[v] - a.coef * acc[ib][jb][v];
-                if (d.xbf16) *gst<uint16_t>(static_cast<uint16_t*>(d.x) + row * d.n + col) = static_cast<uint16_t>(bf16_bits(nw));
-                else *gst<float>(static_cast<float*>(d.x) + row * d.n + col) = nw;
-            }
         }
+    }
 }
 
 void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, hipStream_t s) {
