@@ -1608,9 +1608,27 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
         const bool is_left = i >= right.size();
         const int id = static_cast<int>(i);
         const int64_t pt = ceil_div(d.D, kGaTile);
-        const int64_t bt = is_left ? ceil_div(d.m, kGaWide) * d.btj : ceil_div(d.m, kGaTile) * d.btj;
         for (int64_t y = 0; y < pt; ++y) lists[is_left ? kGaProjL : kGaProjR].push_back(make_int2(id, static_cast<int>(y)));
-        for (int64_t y = 0; y < bt; ++y) lists[is_left ? kGaBackL : kGaBackR].push_back(make_int2(id, static_cast<int>(y)));
+        // Back-projection tiles, XCD-aligned: blocks go to the 8 XCDs in turn, so
+        // the blocks that read one tile of N (a row tile for m >= n, a column tile
+        // for m < n) are placed 8 apart and share one L2. The tensor starts at a
+        // multiple of 8; empty items (x = -1) fill the gaps.
+        std::vector<int2>& L = lists[is_left ? kGaBackL : kGaBackR];
+        const int64_t ti_n = is_left ? ceil_div(d.m, kGaWide) : ceil_div(d.m, kGaTile);
+        const int64_t na = is_left ? d.btj : ti_n;   // tiles of N
+        const int64_t nb = is_left ? ti_n : d.btj;   // tiles of U
+        while (L.size() % 8) L.push_back(make_int2(-1, 0));
+        for (int64_t g = 0; g < ceil_div(na, 8); ++g)
+            for (int64_t b = 0; b < nb; ++b)
+                for (int64_t x = 0; x < 8; ++x) {
+                    const int64_t a = 8 * g + x;
+                    if (a >= na) {
+                        L.push_back(make_int2(-1, 0));
+                        continue;
+                    }
+                    const int64_t ti = is_left ? b : a, tj = is_left ? a : b;
+                    L.push_back(make_int2(id, static_cast<int>(ti * d.btj + tj)));
+                }
     }
     size_t offs[kGaListCount];
     size_t total = (gd.size() * sizeof(GDesc) + 255) / 256 * 256;

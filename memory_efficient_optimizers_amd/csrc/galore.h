@@ -31,7 +31,8 @@ struct GDesc {
 
 struct GTable {
     const GDesc* desc;
-    const int2* items;  // [grid] x = tensor, y = tile within the tensor
+    const int2* items;  // [grid] x = tensor, y = tile within the tensor; x < 0: an empty
+                        // item (padding of the XCD-aligned back-projection list)
 };
 
 struct GaArgs {

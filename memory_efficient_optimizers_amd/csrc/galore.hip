@@ -150,7 +150,9 @@ __device__ __forceinline__ void ep_gather(const float* lw, int lane, int q, floa
 // ------------------------------------------------------------------ projection + AdamW
 
 template <bool Left>
-__global__ __launch_bounds__(kThreads) void k_galore_project(GTable t, GaArgs a) {
+// 3 waves per SIMD: 13% faster on the 7B list than the 2 that the registers would
+// otherwise allow, with no spills. (The back-projection spills under the same bound.)
+__global__ __launch_bounds__(kThreads, 3) void k_galore_project(GTable t, GaArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sa[kGaTile * kGaPitch];
     __shared__ __attribute__((aligned(16))) uint16_t sb[kGaWide * kGaPitch];
     const int2 it = t.items[blockIdx.x];
@@ -278,6 +280,7 @@ __global__ __launch_bounds__(kThreads) void k_galore_back(GTable t, GaArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sl[kGaTile * kGaPitch];   // N, low plane
     __shared__ __attribute__((aligned(16))) uint16_t su[kGaWide * kGaPitch];   // U rows
     const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;  // an empty item of the XCD-aligned list
     const GDesc d = t.desc[it.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ti = it.y / d.btj, tj = it.y % d.btj;
