@@ -551,8 +551,9 @@ def _galore_states(states):
         for k in ("projector", "projector_t"):
             if st.get(k) is not None and st[k].dtype != torch.bfloat16:
                 raise TypeError(f"GaLore state {k} must be bfloat16")
-        for k, t in st.items():
-            if not t.is_contiguous():
+        for k in GALORE_KEYS:
+            t = st.get(k)
+            if t is not None and not t.is_contiguous():
                 raise ValueError(f"GaLore state {k} must be contiguous (row-major)")
         arr[i] = meo_galore_state(*[_ptr(st.get(k)) for k in GALORE_KEYS])
     return arr

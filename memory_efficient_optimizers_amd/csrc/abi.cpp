@@ -1550,7 +1550,7 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
             d.rvec = aligned16(d.em) && aligned16(d.ev) && d.r % 8 == 0;
             d.wvec = aligned16(d.x) && d.n % 8 == 0;
             const bool is_left = d.m < d.n;
-            d.btj = static_cast<int32_t>(is_left ? ceil_div(d.n, kGaTile) : ceil_div(d.n, kGaWide));
+            d.btj = static_cast<int32_t>(is_left ? ceil_div(d.n, kGaTile * kGaBackRW) : ceil_div(d.n, kGaWide));
             (is_left ? left : right).push_back(d);
             (is_left ? kl : kr).push_back(k);
             // refresh descriptor
@@ -1614,7 +1614,7 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
         // for m < n) are placed 8 apart and share one L2. The tensor starts at a
         // multiple of 8; empty items (x = -1) fill the gaps.
         std::vector<int2>& L = lists[is_left ? kGaBackL : kGaBackR];
-        const int64_t ti_n = is_left ? ceil_div(d.m, kGaWide) : ceil_div(d.m, kGaTile);
+        const int64_t ti_n = is_left ? ceil_div(d.m, kGaWide) : ceil_div(d.m, kGaTile * kGaBackRW);
         const int64_t na = is_left ? d.btj : ti_n;   // tiles of N
         const int64_t nb = is_left ? ti_n : d.btj;   // tiles of U
         while (L.size() % 8) L.push_back(make_int2(-1, 0));

@@ -69,22 +69,22 @@ __device__ __forceinline__ bfv8 ld_frag(const uint16_t* p) {
 // [rows][cols] bf16 array, zero outside it: loaded into registers first (all of a
 // thread's chunks in flight at once, and the next block's while the current one
 // is multiplied), then written to LDS (row pitch kGaPitch).
-template <int NROWS>
+template <int NROWS, int THREADS = kThreads>
 struct RowStage {
-    static constexpr int kPer = NROWS * (kGaKb / 8) / kThreads;
+    static constexpr int kPer = NROWS * (kGaKb / 8) / THREADS;
     u32x4 v[kPer];
     __device__ __forceinline__ void load(const uint16_t* p, int64_t rows, int64_t cols, int64_t r0, int64_t k0,
                                          bool vec) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int c = threadIdx.x + i * kThreads;
+            const int c = threadIdx.x + i * THREADS;
             v[i] = ld_row8(p, rows, cols, r0 + (c >> 3), k0 + (c & 7) * 8, vec);
         }
     }
     __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int c = threadIdx.x + i * kThreads;
+            const int c = threadIdx.x + i * THREADS;
             st_lds8(lds + (c >> 3) * kGaPitch + (c & 7) * 8, v[i]);
         }
     }
@@ -272,21 +272,32 @@ void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool lef
 
 // ------------------------------------------------------------------ back-projection + update
 
-// m >= n: tile 64 rows x 256 columns of W; C = Nh U^T + Nl U^T, waves along columns.
-// m <  n: tile 256 rows x 64 columns; C = U Nh^T + U Nl^T, waves along rows.
+// Tiles of W: 64 kGaBackRW rows x 256 columns for m >= n (C = Nh U^T + Nl U^T),
+// 256 rows x 64 kGaBackRW columns for m < n (C = U Nh^T + U Nl^T); 4 kGaBackRW
+// waves of 64 x 64, wave w at U group w % 4 and N group w / 4. A larger tile
+// shares each staged U block among more rows of N: per output element the staging
+// reads 4r / 256 + 2r / (64 kGaBackRW) bytes from L2.
+constexpr int kBackThreads = kThreads * kGaBackRW;
+constexpr int kBackN = kGaTile * kGaBackRW;  // rows of N per tile
+
 template <bool Left>
-__global__ __launch_bounds__(kThreads) void k_galore_back(GTable t, GaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sh[kGaTile * kGaPitch];   // N, high plane
-    __shared__ __attribute__((aligned(16))) uint16_t sl[kGaTile * kGaPitch];   // N, low plane
-    __shared__ __attribute__((aligned(16))) uint16_t su[kGaWide * kGaPitch];   // U rows
+__global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a) {
+    // one arena: N's planes [kBackN][pitch] twice, then U [256][pitch]; reused by
+    // the epilogue exchange (4 kGaBackRW x 8.5 KB)
+    __shared__ __attribute__((aligned(16))) uint16_t arena[(2 * kBackN + kGaWide) * kGaPitch];
+    static_assert((2 * kBackN + kGaWide) * kGaPitch * 2 >= kBackThreads / 64 * kEpWave * 4, "exchange space");
+    uint16_t* sh = arena;                           // N, high plane
+    uint16_t* sl = arena + kBackN * kGaPitch;       // N, low plane
+    uint16_t* su = arena + 2 * kBackN * kGaPitch;   // U rows
     const int2 it = t.items[blockIdx.x];
     if (it.x < 0) return;  // an empty item of the XCD-aligned list
     const GDesc d = t.desc[it.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ug = wave & 3, ng = wave >> 2;  // the wave's 64-row groups of U and of N
     const int ti = it.y / d.btj, tj = it.y % d.btj;
-    // Tile origin in W; the 64-wide side indexes N's rows, the 256-wide side U's rows.
-    const int64_t r0 = Left ? static_cast<int64_t>(ti) * kGaWide : static_cast<int64_t>(ti) * kGaTile;
-    const int64_t c0 = Left ? static_cast<int64_t>(tj) * kGaTile : static_cast<int64_t>(tj) * kGaWide;
+    // Tile origin in W; the N side indexes N's rows, the 256-wide side U's rows.
+    const int64_t r0 = Left ? static_cast<int64_t>(ti) * kGaWide : static_cast<int64_t>(ti) * kBackN;
+    const int64_t c0 = Left ? static_cast<int64_t>(tj) * kBackN : static_cast<int64_t>(tj) * kGaWide;
     const int64_t n0 = Left ? c0 : r0;  // first row of N in the tile
     const int64_t u0 = Left ? r0 : c0;  // first row of U in the tile
     const bool vec = d.vec;
@@ -298,8 +309,8 @@ __global__ __launch_bounds__(kThreads) void k_galore_back(GTable t, GaArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.0f;
 
-    RowStage<kGaTile> ph, pl;
-    RowStage<kGaWide> pu;
+    RowStage<kBackN, kBackThreads> ph, pl;
+    RowStage<kGaWide, kBackThreads> pu;
     auto fetch = [&](int k0) {
         ph.load(d.nh, d.D, d.r, n0, k0, vec);
         pl.load(d.nl, d.D, d.r, n0, k0, vec);
@@ -318,9 +329,9 @@ __global__ __launch_bounds__(kThreads) void k_galore_back(GTable t, GaArgs a) {
             bfv8 fu[2], fh[2], fl[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-                fu[b] = ld_frag(su + (wave * 64 + b * 32 + (lane & 31)) * kGaPitch + kk);
-                fh[b] = ld_frag(sh + (b * 32 + (lane & 31)) * kGaPitch + kk);
-                fl[b] = ld_frag(sl + (b * 32 + (lane & 31)) * kGaPitch + kk);
+                fu[b] = ld_frag(su + (ug * 64 + b * 32 + (lane & 31)) * kGaPitch + kk);
+                fh[b] = ld_frag(sh + (ng * 64 + b * 32 + (lane & 31)) * kGaPitch + kk);
+                fl[b] = ld_frag(sl + (ng * 64 + b * 32 + (lane & 31)) * kGaPitch + kk);
             }
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib)
@@ -339,9 +350,9 @@ __global__ __launch_bounds__(kThreads) void k_galore_back(GTable t, GaArgs a) {
     }
     // W <- decay W - coef C, rows of 8 columns per lane (see ep_spill), 16 bytes at
     // a time where rows allow.
-    const int64_t wr0 = Left ? r0 + wave * 64 : r0;
-    const int64_t wc0 = Left ? c0 : c0 + wave * 64;
-    float* lw = reinterpret_cast<float*>(su) + wave * kEpWave;
+    const int64_t wr0 = Left ? r0 + ug * 64 : r0 + ng * 64;
+    const int64_t wc0 = Left ? c0 + ng * 64 : c0 + ug * 64;
+    float* lw = reinterpret_cast<float*>(arena) + wave * kEpWave;
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
         ep_spill(acc[ib][0], acc[ib][1], lw, lane);
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void k_galore_back(GTable t, GaArgs a) {
 
 void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, hipStream_t s) {
     if (n <= 0) return;
-    const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
+    const dim3 grid(static_cast<uint32_t>(n)), block(kBackThreads);
     if (left) hipLaunchKernelGGL(k_galore_back<true>, grid, block, 0, s, t, a);
     else hipLaunchKernelGGL(k_galore_back<false>, grid, block, 0, s, t, a);
 }

@@ -1,4 +1,4 @@
-"""torch.optim front ends over the C ABI: Adafactor, CAME and Lamb.
+"""torch.optim front ends over the C ABI: Adafactor, CAME, Lamb and GaLoreAdamW.
 
 Each class owns its state tensors (on the parameter's device, named as on the
 Colossal-AI distributed-optimizers page: ``step``, ``exp_avg``,
@@ -220,3 +220,108 @@ class Lamb(_MeoOptimizer):
     def _call(self, group, step, params, grads, states, ws):
         hp = _lib.lamb_hparams(**{k: group[k] for k in self._HP})
         _lib.meo_lamb_step(hp, step, params, grads, states, ws)
+
+
+_NO_DECAY = ("bias", "LayerNorm.weight")
+
+
+def get_galore_param_groups(model: torch.nn.Module, weight_decay: float, rank: int = 256,
+                            update_proj_gap: int = 200, scale: float = 0.25, proj_type: str = "std"):
+    """Parameter groups for ``GaLoreAdamW``, following the grouping rule of the
+    Colossal-AI page's GaLore section: 2-D parameters get the projection fields
+    (rank, update_proj_gap, scale, proj_type) and ``weight_decay``; the other
+    parameters take plain AdamW with ``weight_decay``; parameters whose name holds
+    ``bias`` or ``LayerNorm.weight`` take no weight decay (the no-decay rule is
+    applied first). Empty groups are left out."""
+    galore, other, no_decay = [], [], []
+    for name, p in model.named_parameters():
+        if not p.requires_grad:
+            continue
+        if any(nd in name for nd in _NO_DECAY):
+            no_decay.append(p)
+        elif p.dim() == 2:
+            galore.append(p)
+        else:
+            other.append(p)
+    groups = [dict(params=galore, weight_decay=weight_decay, rank=rank, update_proj_gap=update_proj_gap,
+                   scale=scale, proj_type=proj_type),
+              dict(params=other, weight_decay=weight_decay),
+              dict(params=no_decay, weight_decay=0.0)]
+    return [g for g in groups if g["params"]]
+
+
+class GaLoreAdamW(_MeoOptimizer):
+    """AdamW under GaLore's low-rank gradient projection (the Colossal-AI page's
+    GaLore section, with its group fields; the ms-swift page's low-rank projection).
+
+    A parameter group with a ``rank`` field projects its 2-D parameters: every
+    ``update_proj_gap`` steps (default 200) the projector is refreshed from the
+    gradient's leading ``rank`` singular vectors (default 256) on the shorter side,
+    AdamW runs on the projected gradient, and the update is projected back and
+    multiplied by ``scale`` (default 0.25). ``proj_type`` must be "std". Groups
+    without ``rank``, and the other parameters of a group with one, take plain
+    AdamW. Weight decay is decoupled (applied to the parameter before the update).
+
+    The projection runs on bf16 matrix cores: a projected parameter's gradient is
+    read in bfloat16 (converted if it is float32), and its projector is kept in
+    bfloat16. States: ``exp_avg`` and ``exp_avg_sq`` float32 ([max(m, n)][r] when
+    projected), ``projector`` [min(m, n)][r] and ``projector_t`` [r][min(m, n)]."""
+
+    _kind = "galore"
+
+    def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0):
+        if not lr >= 0.0:
+            raise ValueError(f"Invalid learning rate: {lr}")
+        if not eps >= 0.0:
+            raise ValueError(f"Invalid epsilon value: {eps}")
+        for i, b in enumerate(betas):
+            if not 0.0 <= b < 1.0:
+                raise ValueError(f"Invalid beta parameter at index {i}: {b}")
+        defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
+        super().__init__(params, defaults, None)
+        for g in self.param_groups:
+            if "rank" in g:
+                g.setdefault("update_proj_gap", 200)
+                g.setdefault("scale", 0.25)
+                g.setdefault("proj_type", "std")
+                if g["proj_type"] != "std":
+                    raise ValueError("only proj_type='std' is supported")
+
+    @staticmethod
+    def _projected(p: torch.Tensor, group) -> bool:
+        return "rank" in group and p.dim() == 2 and p.numel() > 0
+
+    def _state_for(self, p, group):
+        if self._projected(p, group):
+            return _lib.galore_init_state(p, group["rank"])
+        return {k: torch.zeros(p.shape, dtype=torch.float32, device=p.device) for k in ("exp_avg", "exp_avg_sq")}
+
+    def _lists(self, group, params, grads, states):
+        # Tensors that are not projected go to the library as flat views, which it
+        # steps with AdamW whatever their shape.
+        ps, gs, ss = [], [], []
+        for p, g, st in zip(params, grads, states):
+            if self._projected(p, group):
+                ps.append(p)
+                gs.append(g if g.dtype == torch.bfloat16 else g.to(torch.bfloat16))
+                ss.append(st)
+            else:
+                ps.append(p.view(-1))
+                gs.append(g.reshape(-1))
+                ss.append({k: st[k].view(-1) for k in ("exp_avg", "exp_avg_sq")})
+        return ps, gs, ss
+
+    def _hp(self, group):
+        return _lib.galore_hparams(lr=group["lr"], betas=group["betas"], eps=group["eps"],
+                                   weight_decay=group["weight_decay"], rank=group.get("rank", 256),
+                                   update_proj_gap=group.get("update_proj_gap", 200),
+                                   scale=group.get("scale", 0.25))
+
+    def _wsize(self, params, grads):
+        return 0  # computed in _call, where the group is known
+
+    def _call(self, group, step, params, grads, states, ws):
+        ps, gs, ss = self._lists(group, params, grads, states)
+        hp = self._hp(group)
+        ws = self._ws(_lib.meo_galore_workspace_size(hp, ps, gs), ps[0].device)
+        _lib.meo_galore_step(hp, step, ps, gs, ss, ws)

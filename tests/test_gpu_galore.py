@@ -22,7 +22,7 @@ import torch
 
 import workloads
 from oracle import galore as ga
-from memory_efficient_optimizers_amd import _lib
+from memory_efficient_optimizers_amd import GaLoreAdamW, _lib
 from tests.harness import floored_rel_err, judge, to64
 
 pytestmark = pytest.mark.gpu
@@ -247,3 +247,51 @@ def test_refresh_schedule():
     torch.cuda.synchronize()
     assert not torch.equal(states[0]["projector"], u0)
     check_projector(states[0]["projector"], to64(grads[0]), 8)
+
+
+def test_torch_front_end():
+    """GaLoreAdamW over a model's groups equals the binding called directly (bit for
+    bit) on the projected weights, and torch.optim.AdamW on the others."""
+    dev = "cuda"
+    torch.manual_seed(0)
+    model = torch.nn.Sequential(torch.nn.Linear(96, 64), torch.nn.LayerNorm(64), torch.nn.Linear(64, 160)).to(dev)
+    names = [n for n, _ in model.named_parameters()]  # 0.weight 0.bias 1.weight 1.bias 2.weight 2.bias
+    twin = [p.detach().clone() for p in model.parameters()]
+    opt = GaLoreAdamW(get_galore_param_groups_named(model), lr=0.02, weight_decay=0.01)
+    ref = [p.detach().clone().requires_grad_(True) for p in model.parameters()]
+    # torch reference for the groups without a rank: 1.weight decays, the biases do not
+    torch_opt = torch.optim.AdamW([dict(params=[ref[2]], weight_decay=0.01),
+                                   dict(params=[ref[1], ref[3], ref[5]], weight_decay=0.0)], lr=0.02)
+    grads = []
+    for t in range(1, 4):
+        gs = []
+        for k, p in enumerate(model.parameters()):
+            g = workloads.galore_inputs([tuple(p.shape)], 8, 100 * t + k, device=dev, state="zero",
+                                        spectrum=(0.9, 0.005, 8) if p.dim() == 2 else None)[1][0].float()
+            p.grad = g
+            gs.append(g)
+        grads.append(gs)
+        opt.step()
+        for r, g in zip(ref, gs):
+            r.grad = g.clone()
+        torch_opt.step()
+    # the binding directly, on copies of the two projected weights
+    hp2 = _lib.galore_hparams(lr=0.02, weight_decay=0.01, rank=8)
+    w2 = [twin[0], twin[4]]
+    st2 = [_lib.galore_init_state(w, 8) for w in w2]
+    for t in range(1, 4):
+        g2 = [grads[t - 1][0].to(torch.bfloat16), grads[t - 1][4].to(torch.bfloat16)]
+        ws = _lib.workspace(_lib.meo_galore_workspace_size(hp2, w2, g2), dev)
+        _lib.meo_galore_step(hp2, t, w2, g2, st2, ws)
+    torch.cuda.synchronize()
+    ps = list(model.parameters())
+    assert torch.equal(ps[0].detach(), w2[0]) and torch.equal(ps[4].detach(), w2[1])
+    assert torch.equal(opt.state[ps[0]]["projector"], st2[0]["projector"])
+    for k in (1, 2, 3, 5):
+        e = floored_rel_err(to64(ps[k].detach()), to64(ref[k].detach()))
+        assert e < 1e-5, (names[k], e)
+
+
+def get_galore_param_groups_named(model):
+    from memory_efficient_optimizers_amd import get_galore_param_groups
+    return get_galore_param_groups(model, weight_decay=0.01, rank=8)
