@@ -1607,7 +1607,7 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
         const GDesc& d = gd[i];
         const bool is_left = i >= right.size();
         const int id = static_cast<int>(i);
-        const int64_t pt = ceil_div(d.D, kGaTile);
+        const int64_t pt = ceil_div(d.D, kGaProjRows);
         for (int64_t y = 0; y < pt; ++y) lists[is_left ? kGaProjL : kGaProjR].push_back(make_int2(id, static_cast<int>(y)));
         // Back-projection tiles, XCD-aligned: blocks go to the 8 XCDs in turn, so
         // the blocks that read one tile of N (a row tile for m >= n, a column tile

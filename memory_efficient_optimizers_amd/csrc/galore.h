@@ -8,6 +8,8 @@ constexpr int kGaTile = 64;       // rows of the long side per projection tile; 
 constexpr int kGaWide = 256;      // long tile side of the back-projection; maximum rank
 constexpr int kGaKb = 64;         // contraction block staged in LDS
 constexpr int kGaPitch = kGaKb + 8;  // bf16 per LDS row (padding against bank conflicts)
+constexpr int kGaProjRB = 1;       // projection tile: 64 kGaProjRB rows of R per block
+constexpr int kGaProjRows = kGaTile * kGaProjRB;
 constexpr int kGaBackRW = 1;      // back-projection tile: 64 kGaBackRW rows of N per block
 
 // One projected (2-D, bf16-gradient) tensor. With m >= n (right side) the low-rank

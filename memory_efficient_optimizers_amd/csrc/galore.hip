@@ -92,21 +92,23 @@ struct RowStage {
 
 // The transposed tile A[i][k] = G[k0 + k][i0 + i] (i < kGaTile, k < kGaKb) of the
 // row-major gradient G [K][D]: loaded along G's rows, scattered into LDS.
+template <int IROWS>
 struct TransStage {
-    static constexpr int kPer = kGaKb * (kGaTile / 8) / kThreads;
+    static constexpr int kRowChunks = IROWS / 8;  // 16-byte chunks per row of G
+    static constexpr int kPer = kGaKb * kRowChunks / kThreads;
     u32x4 v[kPer];
     __device__ __forceinline__ void load(const uint16_t* g, int64_t K, int64_t D, int64_t i0, int64_t k0, bool vec) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int c = threadIdx.x + i * kThreads;
-            v[i] = ld_row8(g, K, D, k0 + (c >> 3), i0 + (c & 7) * 8, vec);
+            v[i] = ld_row8(g, K, D, k0 + c / kRowChunks, i0 + (c % kRowChunks) * 8, vec);
         }
     }
     __device__ __forceinline__ void store(uint16_t* lds) const {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int c = threadIdx.x + i * kThreads;
-            const int k = c >> 3, ic = (c & 7) * 8;
+            const int k = c / kRowChunks, ic = (c % kRowChunks) * 8;
             const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -150,25 +152,28 @@ __device__ __forceinline__ void ep_gather(const float* lw, int lane, int q, floa
 // ------------------------------------------------------------------ projection + AdamW
 
 template <bool Left>
-// 3 waves per SIMD: 13% faster on the 7B list than the 2 that the registers would
-// otherwise allow, with no spills. (The back-projection spills under the same bound.)
-__global__ __launch_bounds__(kThreads, 3) void k_galore_project(GTable t, GaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sa[kGaTile * kGaPitch];
+// Tile: kGaProjRows rows of R x all r columns; wave w holds columns 64w .. 64w + 63.
+// With 64-row tiles, 3 waves per SIMD: 13% faster on the 7B list than the 2 that
+// the registers would otherwise allow, with no spills. (The back-projection spills
+// under the same bound.)
+__global__ __launch_bounds__(kThreads, kGaProjRB == 1 ? 3 : 2) void k_galore_project(GTable t, GaArgs a) {
+    constexpr int kRB = 2 * kGaProjRB;  // 32-row blocks of a wave's tile
+    __shared__ __attribute__((aligned(16))) uint16_t sa[kGaProjRows * kGaPitch];
     __shared__ __attribute__((aligned(16))) uint16_t sb[kGaWide * kGaPitch];
     const int2 it = t.items[blockIdx.x];
     const GDesc d = t.desc[it.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t i0 = static_cast<int64_t>(it.y) * kGaTile;
+    const int64_t i0 = static_cast<int64_t>(it.y) * kGaProjRows;
     const bool vec = d.vec, active = wave * 64 < d.r;
-    f32x16 acc[2][2];
+    f32x16 acc[kRB][2];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
+    for (int ib = 0; ib < kRB; ++ib)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.0f;
 
-    typename std::conditional<Left, TransStage, RowStage<kGaTile>>::type pa;
+    typename std::conditional<Left, TransStage<kGaProjRows>, RowStage<kGaProjRows>>::type pa;
     RowStage<kGaWide> pb;
     auto fetch = [&](int64_t k0) {
         if constexpr (Left) pa.load(d.g, d.d, d.D, i0, k0, vec);
@@ -185,14 +190,14 @@ __global__ __launch_bounds__(kThreads, 3) void k_galore_project(GTable t, GaArgs
 #pragma unroll
             for (int ks = 0; ks < kGaKb; ks += 16) {
                 const int kk = ks + 8 * (lane >> 5);
-                bfv8 fa[2], fb[2];
+                bfv8 fa[kRB], fb[2];
 #pragma unroll
-                for (int ib = 0; ib < 2; ++ib) fa[ib] = ld_frag(sa + (ib * 32 + (lane & 31)) * kGaPitch + kk);
+                for (int ib = 0; ib < kRB; ++ib) fa[ib] = ld_frag(sa + (ib * 32 + (lane & 31)) * kGaPitch + kk);
 #pragma unroll
                 for (int jb = 0; jb < 2; ++jb)
                     fb[jb] = ld_frag(sb + (wave * 64 + jb * 32 + (lane & 31)) * kGaPitch + kk);
 #pragma unroll
-                for (int ib = 0; ib < 2; ++ib)
+                for (int ib = 0; ib < kRB; ++ib)
 #pragma unroll
                     for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma32(fa[ib], fb[jb], acc[ib][jb]);
             }
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_galore_project(GTable t, GaArgs
     // read and written, N's planes written, 16 bytes at a time where rows allow.
     float* lw = reinterpret_cast<float*>(sb) + wave * kEpWave;
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
+    for (int ib = 0; ib < kRB; ++ib) {
         ep_spill(acc[ib][0], acc[ib][1], lw, lane);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
