@@ -1582,7 +1582,7 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
             addr(is_left ? kRfG1N : kRfG1T, ceil_div(q.d, kGaTile));
             addr(kRfGram, ceil_div(q.p, 64) * ceil_div(q.p, 64));
             addr(kRfOne, 1);
-            addr(kRfCols, ceil_div(q.d, 32));
+            addr(kRfCols, ceil_div(q.p, 64) * ceil_div(q.d, 64));
             addr(kRfStore, q.r);
         } else {
             TDesc d;
