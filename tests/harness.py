@@ -116,7 +116,7 @@ def bar_kind(opt: str, hp: dict, storage: dict, key: str) -> str:
     return "f32"
 
 
-def judge(kind: str, key: str, a, b):
+def check_bar(kind: str, key: str, a, b):
     """(ok, max error, elements off the fp32 bar (or codes that differ), elements)
     of one output under its bar. For "codes", a and b are (codes, scales) pairs."""
     if kind == "codes":
@@ -230,7 +230,7 @@ class Run:
         for k, spec in enumerate(self.wl.specs):
             for key, lib, ref in outputs(self.params[k], self.states[k], self.ox[k], self.ost[k]):
                 kind = bar_kind(self.opt, self.hp, self.storage[k], key)
-                out[f"{spec.name}:{key}"] = judge(kind, key, lib, ref) + (kind,)
+                out[f"{spec.name}:{key}"] = check_bar(kind, key, lib, ref) + (kind,)
         return out
 
     def errors(self) -> Dict[str, float]:

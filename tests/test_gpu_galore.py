@@ -23,7 +23,7 @@ import torch
 import workloads
 from oracle import galore as ga
 from memory_efficient_optimizers_amd import GaLoreAdamW, _lib
-from tests.harness import floored_rel_err, judge, to64
+from tests.harness import floored_rel_err, check_bar, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +56,7 @@ def run_case(shapes, rank, t=5, hp=None, param_dtype=torch.float32, seed=0, chec
                   ("f32", "exp_avg", to64(states[k]["exp_avg"]), want_s["exp_avg"]),
                   ("f32", "exp_avg_sq", to64(states[k]["exp_avg_sq"]), want_s["exp_avg_sq"])]
         for kd, key, a, b in checks:
-            ok, err, over, n = judge(kd, key, a, b)
+            ok, err, over, n = check_bar(kd, key, a, b)
             if not ok:
                 bad.append(f"tensor {k} {shape} {key}: err {err:.3g} ({over}/{n} above 1e-5)")
         if param_dtype == torch.float32 and check_update:

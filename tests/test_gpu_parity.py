@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from tests.harness import (Run, bar_kind, judge, lib_hp, lib_states, lib_step, lib_workspace, outputs,
+from tests.harness import (Run, bar_kind, check_bar, lib_hp, lib_states, lib_step, lib_workspace, outputs,
                            storage_of_tensor, to64)
 
 pytestmark = pytest.mark.gpu
@@ -200,7 +200,7 @@ def _sampled_full(wl, sample_idx, steps):
         torch.cuda.synchronize()
         for k in sample_idx:
             ox[k], ost[k] = oracle.STEP_TENSOR[opt](ox[k], to64(gs[k]), ost[k], hp, t, **storage[k])
-            res = {key: judge(bar_kind(opt, hp, storage[k], key), key, lib, ref)
+            res = {key: check_bar(bar_kind(opt, hp, storage[k], key), key, lib, ref)
                    for key, lib, ref in outputs(ps[k], sts[k], ox[k], ost[k])}
             worst = max(res, key=lambda key: res[key][1])
             print(f"  {wl.name} step {t} {wl.specs[k].name}: worst {res[worst][1]:.3e} ({worst})", flush=True)
@@ -279,7 +279,7 @@ def test_mixed_storage_list(opt, hp):
         for k in range(len(ps)):
             ox[k], ost[k] = oracle.STEP_TENSOR[opt](ox[k], to64(gs[k]), ost[k], hp, t, **storage[k])
             for key, lib, ref in outputs(ps[k], sts[k], ox[k], ost[k]):
-                ok, err, over, n = judge(bar_kind(opt, hp, storage[k], key), key, lib, ref)
+                ok, err, over, n = check_bar(bar_kind(opt, hp, storage[k], key), key, lib, ref)
                 assert ok, (t, k, key, err, over, n)
 
 

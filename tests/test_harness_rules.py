@@ -5,7 +5,7 @@ rounding to nearest, a skipped rounding, a wrong value in a tail)."""
 import numpy as np
 
 import oracle
-from tests.harness import TOL_F32, bar_kind, judge
+from tests.harness import TOL_F32, bar_kind, check_bar
 
 
 def _bits_down(a):
@@ -45,21 +45,21 @@ def test_sixteen_bit_rules():
     lib = ref.copy()
     idx = rng.choice(lib.size, 60, replace=False)
     lib[idx] = _one_step_up(lib[idx])
-    ok, err, over, n = judge("rounded", "exp_avg", lib, ref)
+    ok, err, over, n = check_bar("rounded", "exp_avg", lib, ref)
     assert ok and over == 60 and err <= 2.0 ** -7
     # the same disagreements fail the fp32 bar
-    assert not judge("f32", "exp_avg", lib, ref)[0]
+    assert not check_bar("f32", "exp_avg", lib, ref)[0]
     # truncation instead of round-to-nearest moves about half the elements
-    ok, err, over, n = judge("rounded", "exp_avg", _bits_down(exact), ref)
+    ok, err, over, n = check_bar("rounded", "exp_avg", _bits_down(exact), ref)
     assert not ok and over > 0.3 * n
     # a skipped rounding (fp32 values stored) moves nearly all of them
-    assert not judge("rounded", "exp_avg", exact.astype(np.float32).astype(np.float64), ref)[0]
+    assert not check_bar("rounded", "exp_avg", exact.astype(np.float32).astype(np.float64), ref)[0]
     # garbage in a ragged tail of 7 elements breaks the elementwise bound
     lib = ref.copy()
     lib[-7:] = 0.0
-    assert not judge("rounded", "exp_avg", lib, ref)[0]
+    assert not check_bar("rounded", "exp_avg", lib, ref)[0]
     # an exact match passes both bars
-    assert judge("f32", "param", ref, ref)[:2] == (True, 0.0)
+    assert check_bar("f32", "param", ref, ref)[:2] == (True, 0.0)
     assert TOL_F32 == 1e-5
 
 
@@ -75,10 +75,10 @@ def test_code_rules():
     idx = rng.choice(lib.size, 100, replace=False)
     lib[idx] = np.clip(lib[idx] + 1, -127, 127)
     lib[idx[:3]] = np.clip(lib[idx[:3]] + 1, -127, 127)   # three values two steps off
-    ok, err, over, n = judge("codes", "exp_avg", (lib.astype(np.int8), scales), ref)
+    ok, err, over, n = check_bar("codes", "exp_avg", (lib.astype(np.int8), scales), ref)
     assert ok and err <= 2.5 / 127 and over <= 100
     lib[idx[0]] = np.clip(codes[idx[0]] + 3, -127, 127)
-    assert not judge("codes", "exp_avg", (lib.astype(np.int8), scales), ref)[0]
+    assert not check_bar("codes", "exp_avg", (lib.astype(np.int8), scales), ref)[0]
     shifted = np.clip(codes.astype(np.int16) + (rng.random(codes.size) < 0.2), -127, 127).astype(np.int8)
-    assert not judge("codes", "exp_avg", (shifted, scales), ref)[0]
-    assert not judge("codes", "exp_avg", (codes, scales * np.float32(1.03)), ref)[0]
+    assert not check_bar("codes", "exp_avg", (shifted, scales), ref)[0]
+    assert not check_bar("codes", "exp_avg", (codes, scales * np.float32(1.03)), ref)[0]
