@@ -295,3 +295,66 @@ def test_torch_front_end():
 def get_galore_param_groups_named(model):
     from memory_efficient_optimizers_amd import get_galore_param_groups
     return get_galore_param_groups(model, weight_decay=0.01, rank=8)
+
+
+def test_refresh_full_rank():
+    """rank >= min(m, n): the basis is the whole space, every vector still the SVD's."""
+    dev = "cuda"
+    params, grads, states = workloads.galore_inputs([(160, 48), (40, 120)], 256, 21, device=dev, state="zero",
+                                                    spectrum=(0.93, 0.0, 256))
+    h = _lib.galore_hparams(rank=256)
+    ws = _lib.workspace(_lib.meo_galore_workspace_size(h, params, grads), dev)
+    print("galore refresh: full rank", flush=True)
+    _lib.meo_galore_refresh(h, params, grads, states, ws)
+    torch.cuda.synchronize()
+    for k in range(2):
+        check_projector(states[k]["projector"], to64(grads[k]), 256)
+
+
+def test_refresh_rank_deficient_gradient():
+    """A gradient of rank 3 with r = 8: the leading 3 vectors are the SVD's; the rest
+    (which the SVD leaves free) are finite and complete an orthonormal basis."""
+    dev = "cuda"
+    params, grads, states = workloads.galore_inputs([(200, 96)], 8, 22, device=dev, state="zero",
+                                                    spectrum=(0.8, 0.0, 3))
+    h = _lib.galore_hparams(rank=8)
+    ws = _lib.workspace(_lib.meo_galore_workspace_size(h, params, grads), dev)
+    print("galore refresh: rank-deficient gradient", flush=True)
+    _lib.meo_galore_refresh(h, params, grads, states, ws)
+    torch.cuda.synchronize()
+    u = to64(states[0]["projector"])
+    assert np.all(np.isfinite(u))
+    e = ga.galore_projector(to64(grads[0]), 8, projector_bf16=False)
+    bound = 2.0 ** -8 * np.abs(e[:, :3]) + TOL_BASIS * np.max(np.abs(e[:, :3]), axis=0, keepdims=True)
+    assert np.all(np.abs(u[:, :3] - e[:, :3]) <= bound)
+    np.testing.assert_allclose(u.T @ u, np.eye(8), atol=2e-2)  # bf16-rounded orthonormal columns
+
+
+@pytest.mark.parametrize("param_dtype", [torch.float32, torch.bfloat16])
+def test_refresh_every_step(param_dtype):
+    """update_proj_gap = 1 over 3 steps (a refresh before each), against the oracle's
+    SVD-based steps; the bar of the due step above (the projectors may differ in a
+    last bf16 bit)."""
+    dev = "cuda"
+    rank = 16
+    hpo = dict(lr=0.01, rank=rank, update_proj_gap=1, weight_decay=0.01)
+    shapes = [(192, 96), (96, 256)]
+    params, grads, states = workloads.galore_inputs(shapes, rank, 23, device=dev, state="zero",
+                                                    param_dtype=param_dtype, spectrum=(0.9, 0.005, rank))
+    ox = [to64(p) for p in params]
+    ost = [{k: to64(v) for k, v in s.items() if k != "projector_t"} for s in states]
+    h = _lib.galore_hparams(**hpo)
+    ws = _lib.workspace(_lib.meo_galore_workspace_size(h, params, grads), dev)
+    print(f"galore refresh every step: {param_dtype}", flush=True)
+    for t in range(1, 4):
+        g = workloads.galore_inputs(shapes, rank, 30 + t, device=dev, state="zero", spectrum=(0.9, 0.005, rank))[1]
+        _lib.meo_galore_step(h, t, params, g, states, ws)
+        for k in range(2):
+            ox[k], ost[k] = ga.galore_step_tensor(ox[k], to64(g[k]), ost[k], hpo, t,
+                                                  param_bf16=param_dtype == torch.bfloat16)
+    torch.cuda.synchronize()
+    for k in range(2):
+        check_projector(states[k]["projector"], to64(g[k]), rank)
+        for key, a, b in (("param", to64(params[k]), ox[k]), ("exp_avg", to64(states[k]["exp_avg"]), ost[k]["exp_avg"])):
+            e = floored_rel_err(a, b)
+            assert e <= 2e-2, f"tensor {k} {key}: {e:.3g}"
