@@ -105,10 +105,13 @@ __device__ double rf_max_d(double v, double* lds) {
 // ------------------------------------------------------------------ start block
 
 // Start block: the stored projector's rows (U^T, zero before the first refresh)
-// plus a Gaussian block scaled by 1e-3 / sqrt(d), one normal per element from
-// the counter (tensor, index). The Gaussian keeps the block of full rank when
-// there is no stored basis (or it has lost rank); a stored basis that is close
-// to the new one starts the iteration near its end.
+// plus a Gaussian block scaled by 1e-6 / sqrt(d) (1e-6 of a unit vector's
+// entries), one normal per element from the counter (tensor, index). The Gaussian
+// keeps the block of full rank when there is no stored basis (the Cholesky-QR is
+// scale-free) or it has lost rank; a stored basis close to the new one starts the
+// iteration near its end, and the Rayleigh-Ritz matrix near diagonal: the
+// perturbation's rotation inside the subspace, which the iteration does not
+// remove, stays at 1e-6.
 __global__ __launch_bounds__(kThreads) void k_rf_init(RTable t, int dst) {
     const int2 it = t.items[blockIdx.x];
     const RDesc d = t.desc[it.x];
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void k_rf_init(RTable t, int dst) {
     const int64_t total = static_cast<int64_t>(d.p) * d.d;
     const int64_t base = static_cast<int64_t>(it.y) * kThreads * kVec;
     const uint64_t key = static_cast<uint64_t>(d.seed) << 40;
-    const float eps = 1e-3f / sqrtf(static_cast<float>(d.d));
+    const float eps = 1e-6f / sqrtf(static_cast<float>(d.d));
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
         const int64_t i = base + static_cast<int64_t>(e) * kThreads + threadIdx.x;
@@ -487,9 +490,9 @@ void launch_rf_trmm(const RTable& t, int64_t n, int src, int dst, hipStream_t s)
 // a holding c_a at a and t_a at its partner (t = -s for the first of a pair, +s
 // for the second). Rotation angles as in the classical method (Rutishauser's
 // formulation: tan of the angle from theta = (S_jj - S_ii) / (2 S_ij)). Stops when
-// the off-diagonal norm is below 1e-11 of the whole (an eigenvector then moves by
-// about 1e-11 / relative gap, far below the bf16 rounding of the stored basis), or
-// after 16 sweeps. On exit
+// the off-diagonal norm is below 1e-9 of the whole (an eigenvector then moves by
+// about 1e-9 over its gap relative to the largest eigenvalue, 1e-5 for gaps of
+// 1e-4; the stored basis is rounded to bf16, 4e-3), or after 16 sweeps. On exit
 // S holds the eigenvalues on its diagonal and W the eigenvectors as columns.
 __global__ __launch_bounds__(kRfBig) void k_rf_jacobi(RTable t) {
     __shared__ double cc[kRfMaxP + 1], tt[kRfMaxP + 1];
@@ -518,7 +521,7 @@ __global__ __launch_bounds__(kRfBig) void k_rf_jacobi(RTable t) {
             }
         off = rf_sum_d(off, red);
         tot = rf_sum_d(tot, red);
-        if (!(off > 1e-22 * tot)) break;  // uniform: every thread holds the same sums
+        if (!(off > 1e-18 * tot)) break;  // uniform: every thread holds the same sums
         for (int round = 0; round < Pe - 1; ++round) {
             // pairs of the circle method: 0 with 1 + round, and the rest mirrored
             if (tid < Pe / 2) {
