@@ -28,8 +28,9 @@ Readings where the pages are silent (each is marked "reading" where applied):
   low-rank gradient is G Q with Q (n x r) the leading right singular vectors;
   for m < n it is P^T G with P (m x r) the leading left singular vectors. This
   is the only choice that gives the rank / min(m, n) state compression the page
-  states. The low-rank tensors are kept as max(m, n) x r arrays (for m < n the
-  transpose of P^T G).
+  states. "reverse_std", which the page names beside it, is the other side: P^T G
+  for m >= n, G Q for m < n. The low-rank tensors are kept as [rows][r] arrays:
+  G Q is m x r; P^T G is stored transposed, n x r.
 * The effective rank is min(rank, min(m, n)).
 * The projector is (re)computed from the current gradient at steps t with
   (t - 1) % update_proj_gap == 0, before projecting; the Adam moments are kept
@@ -75,8 +76,8 @@ def galore_hparams(hp: Optional[dict] = None) -> dict:
         if unknown:
             raise TypeError(f"unknown GaLore hyperparameters: {sorted(unknown)}")
         out.update(hp)
-    if out["proj_type"] != "std":
-        raise ValueError("only proj_type='std' is defined")
+    if out["proj_type"] not in ("std", "reverse_std"):
+        raise ValueError("proj_type must be 'std' or 'reverse_std'")
     if not (isinstance(out["rank"], int) and out["rank"] >= 1):
         raise ValueError("rank must be a positive integer")
     if not (isinstance(out["update_proj_gap"], int) and out["update_proj_gap"] >= 1):
@@ -89,10 +90,12 @@ def is_projected(shape: Tuple[int, ...]) -> bool:
     return len(shape) == 2
 
 
-def galore_side(shape: Tuple[int, int]) -> str:
-    """"right" (m >= n: R = G Q) or "left" (m < n: R = P^T G); reading of "std"."""
+def galore_side(shape: Tuple[int, int], proj_type: str = "std") -> str:
+    """"right" (R = G Q, Q from the right singular vectors) or "left" (R = P^T G, P
+    from the left ones): std takes the shorter side, reverse_std the longer (reading)."""
     m, n = shape
-    return "right" if m >= n else "left"
+    short_is_cols = m >= n
+    return "right" if short_is_cols == (proj_type == "std") else "left"
 
 
 def galore_rank(shape: Tuple[int, int], rank: int) -> int:
@@ -109,29 +112,31 @@ def canonical_signs(u: Array) -> Array:
     return u
 
 
-def galore_projector(g: Array, rank: int, *, projector_bf16: bool = True) -> Array:
-    """The orthonormal basis U (min(m,n) x r) of the leading singular directions.
+def galore_projector(g: Array, rank: int, *, projector_bf16: bool = True, proj_type: str = "std") -> Array:
+    """The orthonormal basis of the leading singular directions on the projected side.
 
-    right (m >= n): the leading right singular vectors of G (columns of V);
-    left (m < n): the leading left singular vectors (columns of U of the SVD).
+    right: the leading right singular vectors of G (columns of V), n x r;
+    left: the leading left singular vectors (columns of U of the SVD), m x r.
     """
     g = np.asarray(g, dtype=np.float64)
     r = galore_rank(g.shape, rank)
     left, _, vt = np.linalg.svd(g, full_matrices=False)  # library SVD as one step
-    basis = vt[:r].T if galore_side(g.shape) == "right" else left[:, :r]
+    basis = vt[:r].T if galore_side(g.shape, proj_type) == "right" else left[:, :r]
     basis = canonical_signs(basis)
     return round_bf16(basis) if projector_bf16 else basis
 
 
-def galore_project(g: Array, u: Array) -> Array:
-    """project(): the low-rank gradient, max(m,n) x r (left side: (P^T G)^T)."""
+def galore_project(g: Array, u: Array, proj_type: str = "std") -> Array:
+    """project(): the low-rank gradient, m x r for the right side, (P^T G)^T (n x r)
+    for the left."""
     g = np.asarray(g, dtype=np.float64)
-    return g @ u if galore_side(g.shape) == "right" else g.T @ u
+    return g @ u if galore_side(g.shape, proj_type) == "right" else g.T @ u
 
 
-def galore_project_back(n_low: Array, u: Array, shape: Tuple[int, int], scale: float) -> Array:
+def galore_project_back(n_low: Array, u: Array, shape: Tuple[int, int], scale: float,
+                        proj_type: str = "std") -> Array:
     """project_back(): the full-shape update, scale times the back-projection."""
-    full = n_low @ u.T if galore_side(shape) == "right" else u @ n_low.T
+    full = n_low @ u.T if galore_side(shape, proj_type) == "right" else u @ n_low.T
     return scale * full
 
 
@@ -139,9 +144,10 @@ def galore_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None) -> Stat
     h = galore_hparams(hp)
     if is_projected(shape):
         r = galore_rank(shape, h["rank"])
-        long_side, short_side = max(shape), min(shape)
-        return dict(exp_avg=np.zeros((long_side, r)), exp_avg_sq=np.zeros((long_side, r)),
-                    projector=np.zeros((short_side, r)))
+        m, n = shape
+        rows, basis = (m, n) if galore_side(shape, h["proj_type"]) == "right" else (n, m)
+        return dict(exp_avg=np.zeros((rows, r)), exp_avg_sq=np.zeros((rows, r)),
+                    projector=np.zeros((basis, r)))
     return dict(exp_avg=np.zeros(shape), exp_avg_sq=np.zeros(shape))
 
 
@@ -167,9 +173,9 @@ def galore_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: 
     if is_projected(x.shape):
         u = np.asarray(state["projector"], dtype=np.float64)
         if galore_refresh_due(h, t):
-            u = galore_projector(g, h["rank"], projector_bf16=projector_bf16)
+            u = galore_projector(g, h["rank"], projector_bf16=projector_bf16, proj_type=h["proj_type"])
         new["projector"] = u
-        low = galore_project(g, u)
+        low = galore_project(g, u, h["proj_type"])
     else:
         low = g
     m = b1 * state["exp_avg"] + (1.0 - b1) * low
@@ -177,7 +183,7 @@ def galore_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: 
     new["exp_avg"], new["exp_avg_sq"] = m, v
     direction = _adam_direction(m, v, h, t)
     if is_projected(x.shape):
-        update = galore_project_back(direction, new["projector"], x.shape, h["scale"])
+        update = galore_project_back(direction, new["projector"], x.shape, h["scale"], h["proj_type"])
     else:
         update = direction
     x_new = x * (1.0 - h["lr"] * h["weight_decay"]) - h["lr"] * update

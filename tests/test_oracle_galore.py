@@ -32,8 +32,9 @@ def _orthonormal(rng, n, k):
 def test_worked_examples(case):
     x, g = np.array(case["x"], float), np.array(case["g"], float)
     st = ga.galore_init_state(x.shape, case["hp"])
-    x_new, new = ga.galore_step_tensor(x, g, st, case["hp"], case["t"])
-    np.testing.assert_allclose(new["projector"], np.array(case["projector"]), atol=0, rtol=0)
+    x_new, new = ga.galore_step_tensor(x, g, st, case["hp"], case["t"],
+                                       projector_bf16=case.get("projector_bf16", True))
+    np.testing.assert_allclose(new["projector"], np.array(case["projector"]), atol=1e-15, rtol=0)
     np.testing.assert_allclose(x_new, np.array(case["x_new"]), rtol=1e-15, atol=1e-15)
 
 
@@ -182,7 +183,8 @@ def test_update_odd_in_gradient():
 
 def test_hparam_validation():
     with pytest.raises(ValueError):
-        ga.galore_hparams(dict(proj_type="reverse_std"))
+        ga.galore_hparams(dict(proj_type="right"))
+    assert ga.galore_hparams(dict(proj_type="reverse_std"))["proj_type"] == "reverse_std"
     with pytest.raises(ValueError):
         ga.galore_hparams(dict(rank=0))
     with pytest.raises(ValueError):
@@ -190,3 +192,20 @@ def test_hparam_validation():
     assert ga.GALORE_DEFAULTS["rank"] == 256
     assert ga.GALORE_DEFAULTS["update_proj_gap"] == 200
     assert ga.GALORE_DEFAULTS["scale"] == 0.25
+
+
+@pytest.mark.parametrize("shape,rank", [((64, 16), 4), ((16, 64), 4)])
+def test_reverse_std_shapes_and_basis(shape, rank):
+    """reverse_std keeps the projector on the longer side: [max][r] basis, [min][r]
+    moments; the basis is the leading singular vectors of that side."""
+    rng = np.random.default_rng(7)
+    m, n = shape
+    k = min(m, n)
+    a, b = _orthonormal(rng, m, k), _orthonormal(rng, n, k)
+    g = a @ np.diag(np.linspace(5.0, 1.0, k)) @ b.T
+    hp = dict(rank=rank, proj_type="reverse_std")
+    st = ga.galore_init_state(shape, hp)
+    assert st["exp_avg"].shape == (min(shape), rank) and st["projector"].shape == (max(shape), rank)
+    u = ga.galore_projector(g, rank, projector_bf16=False, proj_type="reverse_std")
+    want = (a if m >= n else b)[:, :rank]
+    np.testing.assert_allclose(np.abs(np.sum(u * want, axis=0)), np.ones(rank), atol=1e-10)
