@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MEO_VERSION 4
+#define MEO_VERSION 5
 
 /* Return codes. */
 #define MEO_OK          0
@@ -344,18 +344,22 @@ int    meo_lamb_shard_apply(const meo_lamb_hparams* hp, int64_t step, int32_t n,
  * distributed-optimizers page, section on GaLore's special configuration, with
  * its table of group fields; ms-swift page, section on low-rank projection).
  *
- * A tensor with ndim == 2 (batch 1) is projected. With m = rows, n = cols,
- * d = min(m, n), D = max(m, n) and r = min(rank, d) (the effective rank):
+ * A tensor with ndim == 2 (batch 1) is projected. With m = rows, n = cols and
+ * r = min(rank, min(m, n)) (the effective rank), the projection takes one side of
+ * the matrix: proj_type MEO_GALORE_STD takes the shorter one (m >= n: the right
+ * side, else the left), MEO_GALORE_REVERSE_STD the longer one (the page's table
+ * names "std" and "reverse_std"). On the right side d = n and D = m, on the left
+ * d = m and D = n:
  *   - every update_proj_gap steps, at steps t with (t - 1) % update_proj_gap == 0,
  *     the projector U (d x r, orthonormal columns) is recomputed from the current
- *     gradient: the leading r right singular vectors of G when m >= n, the leading
- *     left singular vectors when m < n (proj_type "std": the shorter side), each
- *     signed so that its entry of largest magnitude is positive;
- *   - project(): R = G U (m >= n) or R = G^T U (m < n), D x r;
+ *     gradient: the leading r right singular vectors of G (right side) or left
+ *     singular vectors (left side), each signed so that its entry of largest
+ *     magnitude is positive;
+ *   - project(): R = G U (right) or R = G^T U (left), D x r;
  *   - AdamW on R: exp_avg <- b1 exp_avg + (1 - b1) R, exp_avg_sq <- b2 exp_avg_sq
  *     + (1 - b2) R^2, N = (exp_avg / (1 - b1^t)) / (sqrt(exp_avg_sq / (1 - b2^t)) + eps);
- *   - project_back() and update: X <- X (1 - lr wd) - lr scale (N U^T) for m >= n,
- *     X <- X (1 - lr wd) - lr scale (U N^T) for m < n.
+ *   - project_back() and update: X <- X (1 - lr wd) - lr scale (N U^T) (right),
+ *     X <- X (1 - lr wd) - lr scale (U N^T) (left).
  * Every other tensor takes the same AdamW update on its elements, without scale.
  * The moments persist across projector refreshes.
  *
@@ -369,11 +373,14 @@ int    meo_lamb_shard_apply(const meo_lamb_hparams* hp, int64_t step, int32_t n,
  * Non-projected tensors: param and grad fp32 or bf16, exp_avg and exp_avg_sq
  * float32 [numel], projector pointers NULL. All states start at zero.
  *
- * Defaults (meo_galore_defaults): rank 256, update_proj_gap 200, scale 0.25
- * (the page's table); lr 1e-3, betas (0.9, 0.999), eps 1e-8, weight_decay 0 (the
- * pages name these fields without values). Errors (MEO_EINVAL): lr < 0, a beta
- * outside [0, 1), eps < 0, rank < 1, update_proj_gap < 1, non-finite values.
+ * Defaults (meo_galore_defaults): rank 256, update_proj_gap 200, scale 0.25,
+ * proj_type std (the page's table); lr 1e-3, betas (0.9, 0.999), eps 1e-8,
+ * weight_decay 0 (the pages name these fields without values). Errors
+ * (MEO_EINVAL): lr < 0, a beta outside [0, 1), eps < 0, rank < 1,
+ * update_proj_gap < 1, an unknown proj_type, non-finite values.
  */
+#define MEO_GALORE_STD          0
+#define MEO_GALORE_REVERSE_STD  1
 typedef struct meo_galore_hparams {
     double  lr;
     double  beta1, beta2;
@@ -382,6 +389,8 @@ typedef struct meo_galore_hparams {
     int32_t rank;
     int32_t update_proj_gap;
     double  scale;
+    int32_t proj_type;   /* MEO_GALORE_STD or MEO_GALORE_REVERSE_STD */
+    int32_t reserved;    /* 0 */
 } meo_galore_hparams;
 
 typedef struct meo_galore_state {

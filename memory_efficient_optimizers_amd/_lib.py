@@ -97,10 +97,14 @@ class meo_lamb_state(ctypes.Structure):
     _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq", c_void_p), ("exp_avg_scale", c_void_p)]
 
 
+MEO_GALORE_STD, MEO_GALORE_REVERSE_STD = 0, 1
+_PROJ_TYPE = {"std": MEO_GALORE_STD, "reverse_std": MEO_GALORE_REVERSE_STD}
+
+
 class meo_galore_hparams(ctypes.Structure):
     _fields_ = [("lr", c_double), ("beta1", c_double), ("beta2", c_double), ("eps", c_double),
                 ("weight_decay", c_double), ("rank", c_int32), ("update_proj_gap", c_int32),
-                ("scale", c_double)]
+                ("scale", c_double), ("proj_type", c_int32), ("reserved", c_int32)]
 
 
 class meo_galore_state(ctypes.Structure):
@@ -297,10 +301,10 @@ def lamb_hparams(lr=1e-3, betas=(0.9, 0.999), eps=1e-6, weight_decay=0.0,
 
 def galore_hparams(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, rank=256, update_proj_gap=200,
                    scale=0.25, proj_type="std") -> meo_galore_hparams:
-    if proj_type != "std":
-        raise ValueError("only proj_type='std' is supported")
+    if proj_type not in _PROJ_TYPE:
+        raise ValueError("proj_type must be 'std' or 'reverse_std'")
     return meo_galore_hparams(float(lr), float(betas[0]), float(betas[1]), float(eps), float(weight_decay),
-                              int(rank), int(update_proj_gap), float(scale))
+                              int(rank), int(update_proj_gap), float(scale), _PROJ_TYPE[proj_type], 0)
 
 
 def meo_adafactor_defaults() -> meo_adafactor_hparams:
@@ -584,22 +588,24 @@ def meo_galore_refresh(hp, params, grads, states, workspace=None, stream=None) -
                                      _galore_states(states), ws, nb, _stream(stream)))
 
 
-def galore_state_shapes(shape, rank: int) -> Dict[str, tuple]:
-    """Shapes of one parameter's GaLore states (meo.h): 2-D parameters keep
-    [max(m, n)][r] moments and the projector [min(m, n)][r] with its transpose."""
+def galore_state_shapes(shape, rank: int, proj_type: str = "std") -> Dict[str, tuple]:
+    """Shapes of one parameter's GaLore states (meo.h): a 2-D parameter keeps
+    [D][r] moments and the projector [d][r] with its transpose, where d is the
+    projected side (std: the shorter, reverse_std: the longer) and D the other."""
     shape = tuple(shape)
     if len(shape) == 2 and shape[0] > 0 and shape[1] > 0:
         r = min(rank, min(shape))
-        return {"exp_avg": (max(shape), r), "exp_avg_sq": (max(shape), r),
-                "projector": (min(shape), r), "projector_t": (r, min(shape))}
+        d = min(shape) if proj_type == "std" else max(shape)
+        D = shape[0] * shape[1] // d
+        return {"exp_avg": (D, r), "exp_avg_sq": (D, r), "projector": (d, r), "projector_t": (r, d)}
     return {"exp_avg": shape, "exp_avg_sq": shape}
 
 
-def galore_init_state(param: torch.Tensor, rank: int) -> Dict[str, torch.Tensor]:
+def galore_init_state(param: torch.Tensor, rank: int, proj_type: str = "std") -> Dict[str, torch.Tensor]:
     """Zero GaLore states for one parameter (projectors in bfloat16)."""
     return {k: torch.zeros(s, dtype=torch.bfloat16 if k.startswith("projector") else torch.float32,
                            device=param.device)
-            for k, s in galore_state_shapes(param.shape, rank).items()}
+            for k, s in galore_state_shapes(param.shape, rank, proj_type).items()}
 
 
 # ----------------------------------------------------------------------------- state allocation

@@ -1346,6 +1346,14 @@ int32_t ga_rank(const meo_galore_hparams* hp, const meo_tensor& t) {
     return static_cast<int32_t>(std::min<int64_t>(hp->rank, std::min(t.rows, t.cols)));
 }
 
+// The projected side: left (R = P^T G, P from the left singular vectors) or right.
+// std takes the shorter side, reverse_std the longer one.
+bool ga_left(const meo_galore_hparams* hp, const meo_tensor& t) {
+    return (t.rows < t.cols) == (hp->proj_type == MEO_GALORE_STD);
+}
+int64_t ga_rows(const meo_galore_hparams* hp, const meo_tensor& t) { return ga_left(hp, t) ? t.cols : t.rows; }   // D
+int64_t ga_basis(const meo_galore_hparams* hp, const meo_tensor& t) { return ga_left(hp, t) ? t.rows : t.cols; }  // d
+
 int64_t align256(int64_t bytes) { return (bytes + 255) / 256 * 256; }
 
 // Workspace, per projected tensor, every array at a 256-byte boundary (offsets in
@@ -1361,14 +1369,15 @@ int64_t ga_layout(const meo_galore_hparams* hp, int32_t n, const meo_tensor* ts,
         const int32_t r = ga_rank(hp, ts[k]);
         if (!r) continue;
         if (offs) (*offs)[k] = off;
-        off += 2 * align256(std::max(ts[k].rows, ts[k].cols) * r * 2);
+        off += 2 * align256(ga_rows(hp, ts[k]) * r * 2);
     }
     for (int32_t k = 0; k < n; ++k) {
         const int32_t r = ga_rank(hp, ts[k]);
         if (!r) continue;
         if (roffs) (*roffs)[k] = off;
-        const int64_t d = std::min(ts[k].rows, ts[k].cols), D = std::max(ts[k].rows, ts[k].cols);
-        off += 2 * align256(static_cast<int64_t>(r) * d * 4) + align256(static_cast<int64_t>(r) * D * 4) +
+        const int64_t d = ga_basis(hp, ts[k]), D = ga_rows(hp, ts[k]);
+        // the product buffer [r][D] later holds the basis [r][d] too
+        off += 2 * align256(static_cast<int64_t>(r) * d * 4) + align256(static_cast<int64_t>(r) * std::max(D, d) * 4) +
                4 * align256(static_cast<int64_t>(r) * r * 8);
     }
     return off;
@@ -1385,6 +1394,8 @@ int check_galore_hp(const meo_galore_hparams* hp) {
     if (hp->eps < 0.0) return fail(MEO_EINVAL, "Invalid epsilon value: " + std::to_string(hp->eps));
     if (hp->rank < 1) return fail(MEO_EINVAL, "rank must be >= 1");
     if (hp->update_proj_gap < 1) return fail(MEO_EINVAL, "update_proj_gap must be >= 1");
+    if (hp->proj_type != MEO_GALORE_STD && hp->proj_type != MEO_GALORE_REVERSE_STD)
+        return fail(MEO_EINVAL, "proj_type must be MEO_GALORE_STD or MEO_GALORE_REVERSE_STD");
     return MEO_OK;
 }
 
@@ -1432,7 +1443,7 @@ int check_galore_tensors(const meo_galore_hparams* hp, int64_t step, int32_t n, 
             if (!s.projector || !s.projector_t) return fail(MEO_ENULL, who + "projector or projector_t is NULL");
             if (reinterpret_cast<uintptr_t>(s.projector) % 2 || reinterpret_cast<uintptr_t>(s.projector_t) % 2)
                 return fail(MEO_EALIGN, who + "projector misaligned");
-            const int64_t D = std::max(t.rows, t.cols);
+            const int64_t D = ga_rows(hp, t);
             blocks[kGaProjR] += ceil_div(D, kGaTile);
             blocks[kGaBackR] += ceil_div(t.rows, kGaTile) * ceil_div(t.cols, kGaTile);
         } else {
@@ -1454,13 +1465,13 @@ int check_galore_memory(const meo_galore_hparams* hp, int32_t n, const meo_tenso
         const std::string who = "tensor " + std::to_string(k) + ": ";
         const size_t ne = static_cast<size_t>(numel);
         const int32_t r = ga_rank(hp, t);
-        const size_t mom = r ? static_cast<size_t>(std::max(t.rows, t.cols)) * r : ne;
+        const size_t mom = r ? static_cast<size_t>(ga_rows(hp, t)) * r : ne;
         struct Range { const void* p; size_t bytes; const char* name; };
         std::vector<Range> rs = {{t.param, ne * (t.param_dtype == MEO_BF16 ? 2 : 4), "param"},
                                  {t.grad, ne * (t.grad_dtype == MEO_BF16 ? 2 : 4), "grad"},
                                  {st[k].exp_avg, mom * 4, "exp_avg"}, {st[k].exp_avg_sq, mom * 4, "exp_avg_sq"}};
         if (r) {
-            const size_t pu = static_cast<size_t>(std::min(t.rows, t.cols)) * r * 2;
+            const size_t pu = static_cast<size_t>(ga_basis(hp, t)) * r * 2;
             rs.push_back({st[k].projector, pu, "projector"});
             rs.push_back({st[k].projector_t, pu, "projector_t"});
         }
@@ -1497,7 +1508,7 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
     std::vector<uint8_t> key(sizeof(int) * 3 + sizeof(void*) + n * (sizeof(meo_tensor) + sizeof(meo_galore_state)));
     {
         uint8_t* w = key.data();
-        const int hdr[3] = {n, dev, hp->rank};
+        const int hdr[3] = {n, dev, hp->rank * 2 + (hp->proj_type == MEO_GALORE_REVERSE_STD ? 1 : 0)};
         std::memcpy(w, hdr, sizeof hdr); w += sizeof hdr;
         std::memcpy(w, &ws, sizeof ws); w += sizeof ws;
         std::memcpy(w, ts, n * sizeof(meo_tensor)); w += n * sizeof(meo_tensor);
@@ -1532,8 +1543,9 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
             std::memset(&d, 0, sizeof d);
             d.m = static_cast<int32_t>(t.rows);
             d.n = static_cast<int32_t>(t.cols);
-            d.D = std::max(d.m, d.n);
-            d.d = std::min(d.m, d.n);
+            const bool is_left = ga_left(hp, t);
+            d.D = static_cast<int32_t>(ga_rows(hp, t));
+            d.d = static_cast<int32_t>(ga_basis(hp, t));
             d.r = ga_rank(hp, t);
             d.g = static_cast<const uint16_t*>(t.grad);
             d.x = t.param;
@@ -1549,7 +1561,6 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
                     d.r % 8 == 0;
             d.rvec = aligned16(d.em) && aligned16(d.ev) && d.r % 8 == 0;
             d.wvec = aligned16(d.x) && d.n % 8 == 0;
-            const bool is_left = d.m < d.n;
             d.btj = static_cast<int32_t>(is_left ? ceil_div(d.n, kGaTile * kGaBackRW) : ceil_div(d.n, kGaWide));
             (is_left ? left : right).push_back(d);
             (is_left ? kl : kr).push_back(k);
@@ -1563,7 +1574,7 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
             q.seed = k;
             uint8_t* rb = static_cast<uint8_t*>(ws) + roff[k];
             const int64_t sq = align256(static_cast<int64_t>(q.r) * q.d * 4);
-            const int64_t sy = align256(static_cast<int64_t>(q.r) * q.D * 4);
+            const int64_t sy = align256(static_cast<int64_t>(q.r) * std::max(q.D, q.d) * 4);
             const int64_t ss = align256(static_cast<int64_t>(q.r) * q.r * 8);
             q.qa = reinterpret_cast<float*>(rb);
             q.qb = reinterpret_cast<float*>(rb + sq);
@@ -1688,6 +1699,7 @@ void meo_galore_defaults(meo_galore_hparams* hp) {
     hp->rank = 256;
     hp->update_proj_gap = 200;
     hp->scale = 0.25;
+    hp->proj_type = MEO_GALORE_STD;
 }
 
 int32_t meo_galore_rank(const meo_galore_hparams* hp, const meo_tensor* t) {

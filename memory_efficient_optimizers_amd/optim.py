@@ -258,7 +258,8 @@ class GaLoreAdamW(_MeoOptimizer):
     ``update_proj_gap`` steps (default 200) the projector is refreshed from the
     gradient's leading ``rank`` singular vectors (default 256) on the shorter side,
     AdamW runs on the projected gradient, and the update is projected back and
-    multiplied by ``scale`` (default 0.25). ``proj_type`` must be "std". Groups
+    multiplied by ``scale`` (default 0.25). ``proj_type`` "std" (default) projects
+    along the shorter side of each matrix, "reverse_std" along the longer. Groups
     without ``rank``, and the other parameters of a group with one, take plain
     AdamW. Weight decay is decoupled (applied to the parameter before the update).
 
@@ -284,8 +285,8 @@ class GaLoreAdamW(_MeoOptimizer):
                 g.setdefault("update_proj_gap", 200)
                 g.setdefault("scale", 0.25)
                 g.setdefault("proj_type", "std")
-                if g["proj_type"] != "std":
-                    raise ValueError("only proj_type='std' is supported")
+                if g["proj_type"] not in ("std", "reverse_std"):
+                    raise ValueError("proj_type must be 'std' or 'reverse_std'")
 
     @staticmethod
     def _projected(p: torch.Tensor, group) -> bool:
@@ -293,7 +294,7 @@ class GaLoreAdamW(_MeoOptimizer):
 
     def _state_for(self, p, group):
         if self._projected(p, group):
-            return _lib.galore_init_state(p, group["rank"])
+            return _lib.galore_init_state(p, group["rank"], group["proj_type"])
         return {k: torch.zeros(p.shape, dtype=torch.float32, device=p.device) for k in ("exp_avg", "exp_avg_sq")}
 
     def _lists(self, group, params, grads, states):
@@ -315,7 +316,7 @@ class GaLoreAdamW(_MeoOptimizer):
         return _lib.galore_hparams(lr=group["lr"], betas=group["betas"], eps=group["eps"],
                                    weight_decay=group["weight_decay"], rank=group.get("rank", 256),
                                    update_proj_gap=group.get("update_proj_gap", 200),
-                                   scale=group.get("scale", 0.25))
+                                   scale=group.get("scale", 0.25), proj_type=group.get("proj_type", "std"))
 
     def _wsize(self, params, grads):
         return 0  # computed in _call, where the group is known

@@ -311,6 +311,7 @@ def test_galore_defaults_are_the_pages(lib):
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "page_defaults.json")))["galore"]
     h = _lib.meo_galore_defaults()
     assert (h.rank, h.update_proj_gap, h.scale) == (g["rank"], g["update_proj_gap"], g["scale"])
+    assert h.proj_type == {"std": _lib.MEO_GALORE_STD}[g["proj_type"]]
     # fields the pages name without values: the readings stated in meo.h
     assert (h.lr, h.beta1, h.beta2, h.eps, h.weight_decay) == (1e-3, 0.9, 0.999, 1e-8, 0.0)
 
@@ -356,6 +357,17 @@ def test_galore_validation(lib):
     assert lib.meo_galore_validate(_lib.ctypes.byref(h), 1, len(ps), t, _lib._galore_states(st)) == _lib.MEO_EDTYPE
     with pytest.raises(TypeError):
         _lib._galore_states([dict(st[0], projector=st[0]["projector"].float())])
+    # reverse_std: the projector on the longer side, moments on the shorter
+    hr = _lib.galore_hparams(rank=8, proj_type="reverse_std")
+    psr, gsr = ps[:2], gs[:2]
+    str_ = [_lib.galore_init_state(p, 8, "reverse_std") for p in psr]
+    assert str_[0]["projector"].shape == (40, 8) and str_[0]["exp_avg"].shape == (16, 8)
+    _lib.meo_galore_validate(hr, 1, psr, gsr, str_)
+    per_r = 2 * a(16 * 8 * 2) + 2 * a(8 * 40 * 4) + a(8 * 40 * 4) + 4 * a(8 * 8 * 8)
+    assert _lib.meo_galore_workspace_size(hr, psr, gsr) == 2 * per_r
+    bad_hp = _lib.galore_hparams(rank=8)
+    bad_hp.proj_type = 2
+    assert _code(_lib.meo_galore_validate, bad_hp, 1, ps, gs, st)[0] == _lib.MEO_EINVAL
     # an empty list is a no-op
     _lib.meo_galore_step(h, 1, [], [], [], stream=0)
 

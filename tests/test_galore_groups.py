@@ -37,6 +37,7 @@ def test_defaults_and_validation():
     opt = GaLoreAdamW(groups)
     assert opt.defaults["lr"] == 1e-3 and opt.defaults["betas"] == (0.9, 0.999) and opt.defaults["eps"] == 1e-8
     with pytest.raises(ValueError):
-        GaLoreAdamW([dict(params=[torch.nn.Parameter(torch.zeros(3, 3))], rank=2, proj_type="reverse_std")])
+        GaLoreAdamW([dict(params=[torch.nn.Parameter(torch.zeros(3, 3))], rank=2, proj_type="reverse")])
+    GaLoreAdamW([dict(params=[torch.nn.Parameter(torch.zeros(3, 3))], rank=2, proj_type="reverse_std")])
     with pytest.raises(ValueError):
         GaLoreAdamW(groups, lr=-1.0)

@@ -34,7 +34,8 @@ def run_case(shapes, rank, t=5, hp=None, param_dtype=torch.float32, seed=0, chec
     dev = "cuda"
     hp = dict(dict(lr=0.05, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, scale=0.25), **(hp or {}))
     hpo = dict(hp, rank=rank)
-    params, grads, states = workloads.galore_inputs(shapes, rank, seed, param_dtype=param_dtype, device=dev)
+    params, grads, states = workloads.galore_inputs(shapes, rank, seed, param_dtype=param_dtype, device=dev,
+                                                    proj_type=hp.get("proj_type", "std"))
     x0 = [to64(p) for p in params]
     g0 = [to64(g) for g in grads]
     s0 = [{k: to64(v) for k, v in s.items() if k != "projector_t"} for s in states]
@@ -360,3 +361,28 @@ def test_refresh_every_step(param_dtype):
         for key, a, b in (("param", to64(params[k]), ox[k]), ("exp_avg", to64(states[k]["exp_avg"]), ost[k]["exp_avg"])):
             e = floored_rel_err(a, b)
             assert e <= 2e-2, f"tensor {k} {key}: {e:.3g}"
+
+
+@pytest.mark.parametrize("shape,rank", [((256, 128), 32), ((128, 320), 64), ((300, 136), 40), ((72, 333), 24),
+                                        ((512, 384), 256)])
+def test_step_reverse_std(shape, rank):
+    """proj_type reverse_std: the projector on the longer side."""
+    run_case([shape], rank, hp=dict(proj_type="reverse_std"))
+
+
+@pytest.mark.parametrize("shape", [(384, 160), (160, 384)])
+def test_refresh_reverse_std(shape):
+    dev = "cuda"
+    rank = 24
+    params, grads, states = workloads.galore_inputs([shape], rank, 41, device=dev, state="zero",
+                                                    spectrum=(0.93, 0.005, rank), proj_type="reverse_std")
+    h = _lib.galore_hparams(rank=rank, proj_type="reverse_std")
+    ws = _lib.workspace(_lib.meo_galore_workspace_size(h, params, grads), dev)
+    print(f"galore refresh reverse_std: {shape}", flush=True)
+    _lib.meo_galore_refresh(h, params, grads, states, ws)
+    torch.cuda.synchronize()
+    e = ga.galore_projector(to64(grads[0]), rank, projector_bf16=False, proj_type="reverse_std")
+    u = to64(states[0]["projector"])
+    assert u.shape == (max(shape), rank)
+    bound = 2.0 ** -8 * np.abs(e) + TOL_BASIS * np.max(np.abs(e), axis=0, keepdims=True)
+    assert np.all(np.abs(u - e) <= bound)

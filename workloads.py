@@ -284,7 +284,8 @@ def grads(wl: Workload, step_index: int, scales, device="cpu", indices=None, out
 
 def galore_inputs(shapes: Sequence[Tuple[int, ...]], rank: int, seed: int = 0, *,
                   param_dtype=torch.float32, device="cpu", gstd: float = 1e-3,
-                  state: str = "seeded", spectrum: Optional[Tuple[float, float]] = None):
+                  state: str = "seeded", spectrum: Optional[Tuple[float, float, int]] = None,
+                  proj_type: str = "std"):
     """Parameters, bf16 gradients and GaLore states (meo.h layout) for `shapes`.
 
     Drawn on the CPU from torch.Generator(seed) (the same bits on every device),
@@ -296,7 +297,9 @@ def galore_inputs(shapes: Sequence[Tuple[int, ...]], rank: int, seed: int = 0, *
     ``state = "seeded"`` the moments of a mid-run step are drawn (exp_avg
     N(0, gstd^2 / 4), exp_avg_sq gstd^2 * U(0.5, 1.5)) and each 2-D tensor gets a
     random orthonormal projector (QR of a Gaussian) rounded to bf16, stored with
-    its transpose; with ``state = "zero"`` everything starts at zero.
+    its transpose; with ``state = "zero"`` everything starts at zero. State shapes
+    follow ``proj_type`` (the projector on the shorter side for "std", the longer for
+    "reverse_std").
     """
     gen = torch.Generator().manual_seed(seed)
     params, grads, states = [], [], []
@@ -316,7 +319,8 @@ def galore_inputs(shapes: Sequence[Tuple[int, ...]], rank: int, seed: int = 0, *
         projected = len(shape) == 2 and shape[0] > 0 and shape[1] > 0
         if projected:
             r = min(rank, min(shape))
-            mshape, d = (max(shape), r), min(shape)
+            d = min(shape) if proj_type == "std" else max(shape)
+            mshape = (shape[0] * shape[1] // d, r)
         else:
             mshape = shape
         if state == "seeded":
