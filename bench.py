@@ -168,13 +168,11 @@ def shard_bench(torch, _lib, workloads, wl, args) -> int:
     """One rank's share of a row-sharded step over N ranks, at the workload's real
     shapes: rank 0's rows of every factored tensor (all columns; the column
     statistic whole) and its element range of every 1-D tensor (LAMB: of every
-    tensor); stats call, then apply call, per step. The partial sums go from one
-    call to the next unreduced: the all-reduce over ranks that sits between them is
-    not part of the measured work, so the values reached are not a real step's."""
+    tensor); stats call, then apply call, per step (CAME: stats, moment, apply).
+    The partial sums go from one call to the next unreduced: the all-reduce over
+    ranks that sits between them is not part of the measured work, so the values
+    reached are not a real step's."""
     from memory_efficient_optimizers_amd.optim import moment_dtype
-    if wl.optimizer not in ("adafactor", "lamb"):
-        print("row-sharded steps exist for Adafactor and LAMB", file=sys.stderr)
-        return 2
     n, dev, opt = args.shard_ranks, "cuda", wl.optimizer
     hp = dict(wl.hparams)
     beta1 = hp.get("beta1") is not None or opt == "lamb"
@@ -198,23 +196,29 @@ def shard_bench(torch, _lib, workloads, wl, args) -> int:
         if "exp_avg_sq_col" in st:
             st["exp_avg_sq_col"] = torch.zeros(tuple(s.shape[:-2]) + tuple(s.shape[-1:]), device=dev)
         states.append(st)
-    hps = {"adafactor": _lib.adafactor_hparams, "lamb": _lib.lamb_hparams}[opt](**hp)
+    hps = {"adafactor": _lib.adafactor_hparams, "lamb": _lib.lamb_hparams, "came": _lib.came_hparams}[opt](**hp)
     ws = _lib.workspace(getattr(_lib, f"meo_{opt}_workspace_size")(params, grads), dev)
     part = torch.zeros(getattr(_lib, f"meo_{opt}_partials_size")(params, grads), device=dev)
-    call = _lib.PreparedShardStep(opt, hps, params, grads, totals, states, part, ws)
+    conf = torch.zeros(max(_lib.meo_came_confidence_size(params, grads), 1), device=dev) if opt == "came" else None
+    call = _lib.PreparedShardStep(opt, hps, params, grads, totals, states, part, ws, conf)
+
+    def step(t):
+        call.stats(t, stream)
+        if opt == "came":
+            call.moment(t, stream)
+        call.apply(t, stream)
+
     stream = torch.cuda.current_stream()
     t = 0
     for _ in range(args.warmup):
         t += 1
-        call.stats(t, stream)
-        call.apply(t, stream)
+        step(t)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
         t += 1
-        call.stats(t, stream)
-        call.apply(t, stream)
+        step(t)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -436,8 +440,7 @@ def main() -> int:
                     help="flat: one buffer per kind of tensor (default); separate: one allocation per tensor")
     ap.add_argument("--shard-ranks", type=int, default=0,
                     help="instead of the whole step: time one rank's share of a row-sharded step over N ranks "
-                         "(Adafactor or LAMB; the all-reduce of the partial sums between the two calls is "
-                         "not part of it)")
+                         "(the all-reduces of the partial sums between the calls are not part of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the step: time a plain device copy of 4 GiB (one elementwise kernel), "
                          "the reference for achievable bandwidth and for scaling rocprofv3 byte counters")

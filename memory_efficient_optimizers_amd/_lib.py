@@ -454,34 +454,48 @@ def meo_came_shard_apply(hp, step, params, grads, totals, states, confidence, wo
 
 
 class PreparedShardStep:
-    """Both calls of a row-sharded step over a fixed list, marshalled once (see
+    """The calls of a row-sharded step over a fixed list, marshalled once (see
     PreparedStep): ``stats(step)`` fills ``partials`` and, after the caller has
-    summed them over the ranks, ``apply(step)`` updates the shard."""
+    summed them over the ranks, ``apply(step)`` updates the shard. CAME has a call
+    between the two: ``moment(step)`` takes the summed ``partials`` and fills
+    ``confidence``, which ``apply(step)`` takes summed over the ranks."""
 
-    _KIND = {"adafactor": (meo_adafactor_state, ADAFACTOR_KEYS), "lamb": (meo_lamb_state, LAMB_KEYS)}
+    _KIND = {"adafactor": (meo_adafactor_state, ADAFACTOR_KEYS), "lamb": (meo_lamb_state, LAMB_KEYS),
+             "came": (meo_came_state, CAME_KEYS)}
 
-    def __init__(self, optimizer: str, hp, params, grads, totals, states, partials, workspace=None):
+    def __init__(self, optimizer: str, hp, params, grads, totals, states, partials, workspace=None,
+                 confidence=None):
         cls, keys = self._KIND[optimizer]
         lib = load()
-        self._fns = (getattr(lib, f"meo_{optimizer}_shard_stats"), getattr(lib, f"meo_{optimizer}_shard_apply"))
+        self.came = optimizer == "came"
+        if self.came and confidence is None:
+            raise ValueError("CAME's row-sharded step needs the confidence buffer")
+        self._fns = (getattr(lib, f"meo_{optimizer}_shard_stats"), getattr(lib, f"meo_{optimizer}_shard_apply"),
+                     lib.meo_came_shard_moment if self.came else None)
         self.hp = hp
         self.n = len(params)
         self.tensors = _tensors(params, grads, states)
         self.shards = _shards(totals)
         self.states = _states(cls, keys, states)
         self.partials = _ptr(partials)
+        self.confidence = _ptr(confidence)
         self.ws, self.ws_bytes = _ws(workspace)
-        self._keep = (list(params), list(grads), list(states), partials, workspace)
+        self._keep = (list(params), list(grads), list(states), partials, confidence, workspace)
 
-    def _call(self, fn, step, stream):
-        _check(fn(ctypes.byref(self.hp), step, self.n, self.tensors, self.shards, self.states, self.partials,
+    def _call(self, fn, step, stream, *bufs):
+        _check(fn(ctypes.byref(self.hp), step, self.n, self.tensors, self.shards, self.states, *bufs,
                   self.ws, self.ws_bytes, _stream(stream)))
 
     def stats(self, step: int, stream=None) -> None:
-        self._call(self._fns[0], step, stream)
+        self._call(self._fns[0], step, stream, self.partials)
+
+    def moment(self, step: int, stream=None) -> None:
+        if not self.came:
+            raise ValueError("only CAME's row-sharded step has a moment call")
+        self._call(self._fns[2], step, stream, self.partials, self.confidence)
 
     def apply(self, step: int, stream=None) -> None:
-        self._call(self._fns[1], step, stream)
+        self._call(self._fns[1], step, stream, self.confidence if self.came else self.partials)
 
 
 def meo_last_error() -> str:

@@ -168,3 +168,32 @@ def test_shard_of_the_whole_is_the_whole_step():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert output_err("param", to64(y), to64(x)) <= TOL_F32
+
+
+def test_prepared_came_shard_of_the_whole_is_the_whole_step():
+    """CAME's three prepared calls (stats, moment, apply) on one rank holding
+    everything give the whole-tensor step's parameters within the fp32 bar."""
+    wl = workloads.custom("shard1c", "came", [(129, 1024), (300,)], hparams={"lr": 2e-4},
+                          grad_dtype=torch.bfloat16)
+    a = workloads.init_params(wl, "cuda")
+    b = [p.clone() for p in a]
+    scales = workloads.grad_scales(wl, "cuda")
+    hps = _lib.came_hparams(lr=2e-4)
+    sa = [_lib.init_state("came", p) for p in a]
+    sb = [_lib.init_state("came", p) for p in b]
+    part = torch.zeros(_lib.meo_came_partials_size(a, a), device="cuda")
+    conf = torch.zeros(max(_lib.meo_came_confidence_size(a, a), 1), device="cuda")
+    gs = workloads.grads(wl, 0, scales, "cuda")
+    ws = _lib.workspace(max(_lib.meo_came_workspace_size(a, gs), 256), "cuda")
+    call = _lib.PreparedShardStep("came", hps, b, gs, [129, 300], sb, part, ws, conf)
+    for t in range(1, 4):
+        g_new = workloads.grads(wl, t - 1, scales, "cuda")
+        for g, n in zip(gs, g_new):
+            g.copy_(n)
+        _lib.meo_came_step(hps, t, a, gs, sa, ws)
+        call.stats(t)
+        call.moment(t)
+        call.apply(t)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert output_err("param", to64(y), to64(x)) <= TOL_F32
