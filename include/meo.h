@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MEO_VERSION 5
+#define MEO_VERSION 6
 
 /* Return codes. */
 #define MEO_OK          0
@@ -438,7 +438,7 @@ int meo_version(void);
  * launches[id] (both arrays of MEO_NUM_PASSES entries, caller-owned host
  * memory, zeroed by the caller), and forgets the events. Returns MEO_OK or
  * MEO_EHIP. Not for use under graph capture. */
-#define MEO_NUM_PASSES 15
+#define MEO_NUM_PASSES 16
 int         meo_profile_enable(int on);
 const char* meo_pass_name(int id);
 int         meo_profile_collect(double* total_ms, int64_t* launches);

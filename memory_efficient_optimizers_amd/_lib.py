@@ -42,7 +42,7 @@ EXPORTS = [
     "meo_galore_defaults", "meo_galore_rank", "meo_galore_workspace_size", "meo_galore_validate",
     "meo_galore_step", "meo_galore_refresh",
 ]
-MEO_NUM_PASSES = 15
+MEO_NUM_PASSES = 16
 
 
 class MeoError(RuntimeError):

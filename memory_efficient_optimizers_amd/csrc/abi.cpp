@@ -388,7 +388,7 @@ int check_tensor_memory(int op, int32_t n, const meo_tensor* ts, const StatePtrs
 
 // Item tables of the launches of one call.
 enum List { kListRc0 = 0, kListRc1, kListTiled, kListAll, kListFin1, kListFin2, kListShard, kListFold, kListEmpty,
-            kListConfRows, kListConf, kListEmpty2, kListCount };
+            kListConfRows, kListConf, kListEmpty2, kListXnorm, kListCount };
 
 struct Plan {
     std::vector<uint8_t> key;
@@ -566,17 +566,8 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
         } else {
             add(kListAll, g.tiles);
             if (g.mode == kRowComplete) {
-                // Strips interleaved with the chunks that stream X for sum(X^2), so
-                // that barrier-free streaming runs beside the strips' row reductions.
-                std::vector<int2>& L = lists[g.cls == 0 ? kListRc0 : kListRc1];
-                const int64_t ns = static_cast<int64_t>(g.B) * g.strips;
-                const int64_t nx = op == kOpAdafactor ? g.xchunks : 0;  // only Adafactor uses RMS(X)
-                int64_t is = 0, ix = 0;
-                while (is < ns || ix < nx) {
-                    if (is < ns) L.push_back(make_int2(id, static_cast<int>(is++)));
-                    const int64_t want = (is * nx + ns - 1) / ns;  // x chunks due after `is` strips
-                    while (ix < nx && (ix < want || is == ns)) L.push_back(make_int2(id, static_cast<int>(-1 - ix++)));
-                }
+                add(g.cls == 0 ? kListRc0 : kListRc1, static_cast<int64_t>(g.B) * g.strips);
+                if (op == kOpAdafactor) add(kListXnorm, g.xchunks);  // only Adafactor uses RMS(X)
                 add(kListFin1, static_cast<int64_t>(g.B) * g.ncc);
             } else {
                 add(kListTiled, g.tiles);
@@ -653,12 +644,12 @@ std::vector<StatePtrs> state_ptrs(int op, int32_t n, const void* states) {
 
 enum Pass { kPassStats = 0, kPassFinalize, kPassRms, kPassScalars, kPassAfApply, kPassCameMom,
             kPassCameApply, kPassLambMoments, kPassLambApply, kPassStatsWide, kPassStatsTiled,
-            kPassGaProject, kPassGaBack, kPassGaAdamw, kPassGaRefresh, kPassCount };
+            kPassGaProject, kPassGaBack, kPassGaAdamw, kPassGaRefresh, kPassXnorm, kPassCount };
 static_assert(kPassCount == MEO_NUM_PASSES, "pass table");
 const char* const kPassNames[kPassCount] = {"stats", "finalize", "rms", "scalars", "adafactor_apply",
                                             "came_mom", "came_apply", "lamb_moments", "lamb_apply",
                                             "stats_wide", "stats_tiled", "galore_project", "galore_back",
-                                            "galore_adamw", "galore_refresh"};
+                                            "galore_adamw", "galore_refresh", "xnorm"};
 
 struct ProfRec { int pass; hipEvent_t a, b; };
 std::mutex g_prof_mu;
@@ -820,6 +811,10 @@ int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
                        b2, 1.0 - b2};
 
     PassTimer pt(s);
+    if (need_x && p->count[kListXnorm]) {
+        launch_xnorm(tab(kListXnorm), p->count[kListXnorm], sa, s);
+        pt.mark(kPassXnorm);
+    }
     if (p->count[kListRc0]) {
         launch_rowstats(0, tab(kListRc0), p->count[kListRc0], sa, s);
         pt.mark(kPassStats);
@@ -1126,6 +1121,10 @@ int meo_adafactor_shard_stats(const meo_adafactor_hparams* hp, int64_t step, int
     const StatsArgs sa{static_cast<float>(hp->eps1), static_cast<float>(a.b2), static_cast<float>(1.0 - a.b2), need_x,
                        a.b2, 1.0 - a.b2};
     PassTimer pt(s);
+    if (need_x && p->count[kListXnorm]) {
+        launch_xnorm(tab(kListXnorm), p->count[kListXnorm], sa, s);
+        pt.mark(kPassXnorm);
+    }
     if (p->count[kListRc0]) {
         launch_rowstats(0, tab(kListRc0), p->count[kListRc0], sa, s);
         pt.mark(kPassStats);

@@ -536,6 +536,7 @@ struct LambArgs {
 // Row-complete first pass, class 0 (W <= 4096, also the flat tensors' first pass)
 // and class 1 (W <= 12288).
 void launch_rowstats(int cls, const Table& t, int64_t n, const StatsArgs& a, hipStream_t s);
+void launch_xnorm(const Table& t, int64_t n, const StatsArgs& a, hipStream_t s);
 void launch_stats(const Table& t, int64_t n, const StatsArgs& a, hipStream_t s);
 void launch_finalize(const Table& t, int64_t n, const FinArgs& a, hipStream_t s);
 void launch_rms(const Table& t, int64_t n, int32_t need_x, hipStream_t s);

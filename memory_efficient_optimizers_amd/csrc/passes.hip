@@ -12,9 +12,9 @@
 //
 //   k_rowstats0/1  row-complete tensors: one read of G per strip of full rows:
 //                  new R_i (stored), per-strip column sums of Q and of G^2 / R_i
-//                  and the strip's sum of R_i; interleaved chunk blocks stream X
-//                  for sum(X^2). Flat tensors (with class 0): V <- beta V +
-//                  (1-beta) Q, sums of G^2 / V and X^2.
+//                  and the strip's sum of R_i. Flat tensors (with class 0):
+//                  V <- beta V + (1-beta) Q, sums of G^2 / V and X^2.
+//   k_xnorm        row-complete tensors (Adafactor): sum(X^2) per chunk of X.
 //   k_stats        tiled tensors: per-tile row sums and column sums of Q.
 //   k_finalize     column (and, tiled, row) statistics from the partials in fp64,
 //                  fixed order; row-complete: per-chunk sums of S_j / C_j;
@@ -73,7 +73,10 @@ __device__ void stats_flat(const TDesc& d, int lt, float* __restrict__ ws, const
 // ----------------------------------------------------------------------------- sum of X^2 chunks
 
 // Sum of X^2 over chunk `c` (kFlatTile elements) of a row-complete tensor's
-// parameter; these blocks stream with no barrier inside the strip pass's grid.
+// parameter. These blocks run as a grid of their own: with few registers, 8 waves
+// per SIMD keep the loads in flight. Interleaved with the strips in one grid they
+// ran at the strips' 3 waves per SIMD, and the two streams together took 1.2 ms
+// longer than apart on the 7B list.
 template <int NTHR>
 __device__ void xnorm_chunk(const TDesc& d, int c, float* __restrict__ ws, const StatsArgs& a, float* bsum) {
     if (!a.need_x) return;  // the step does not use RMS(X)
@@ -291,7 +294,6 @@ __global__ __launch_bounds__(256) void k_rowstats0(Table t, StatsArgs a) {
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     if (d.mode == kFlat) stats_flat<256>(d, it.y, t.ws, a, bsum);
-    else if (it.y < 0) xnorm_chunk<256>(d, -1 - it.y, t.ws, a, bsum);
     else if (d.gbf16) rowstats_strip<256, 2, kRb0, true>(d, it.y, t.ws, a, red, rold, bsum);
     else rowstats_strip<256, 2, kRb0 / 2, false>(d, it.y, t.ws, a, red, rold, bsum);
 }
@@ -300,9 +302,19 @@ __global__ __launch_bounds__(512) void k_rowstats1(Table t, StatsArgs a) {
     __shared__ float red[2 * 8 * kRb1], rold[kStripRows], bsum[2 * 8];
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
-    if (it.y < 0) xnorm_chunk<512>(d, -1 - it.y, t.ws, a, bsum);
-    else if (d.gbf16) rowstats_strip<512, 3, kRb1, true>(d, it.y, t.ws, a, red, rold, bsum);
+    if (d.gbf16) rowstats_strip<512, 3, kRb1, true>(d, it.y, t.ws, a, red, rold, bsum);
     else rowstats_strip<512, 3, kRb1 / 2, false>(d, it.y, t.ws, a, red, rold, bsum);
+}
+
+__global__ __launch_bounds__(256) void k_xnorm(Table t, StatsArgs a) {
+    __shared__ float bsum[2 * kWaves];
+    const int2 it = t.items[blockIdx.x];
+    xnorm_chunk<256>(t.desc[it.x], it.y, t.ws, a, bsum);
+}
+
+void launch_xnorm(const Table& t, int64_t n, const StatsArgs& a, hipStream_t s) {
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_xnorm, dim3(static_cast<uint32_t>(n)), dim3(256), 0, s, t, a);
 }
 
 void launch_rowstats(int cls, const Table& t, int64_t n, const StatsArgs& a, hipStream_t s) {
