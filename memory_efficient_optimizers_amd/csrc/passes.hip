@@ -237,7 +237,7 @@ __device__ __forceinline__ void strip_batch(const TDesc& d, const StatsArgs& a, 
 }
 
 // One strip of up to kStripRows full rows of matrix b (the sum of X^2 is taken by
-// separate chunk blocks of the same grid). Thread t owns the 8-column groups t,
+// k_xnorm). Thread t owns the 8-column groups t,
 // t + NTHR, ..., t + (KMAX-1) NTHR; rows go in batches of RB, two register buffers
 // alternating so that a batch's loads are in flight during the previous one's
 // reduction. `red` holds 2 * NW * RB floats, `rold` kStripRows.
