@@ -18,6 +18,15 @@ hipEvents on the stream (synchronised on both sides). One JSON line on stdout:
 * ``cpu_baseline``: the fp64 oracle (single-threaded NumPy) on a bounded sample of
   the same workload, one step, in parameters per second.
 
+Adafactor with scale_parameter steps through meo_adafactor_step_carry by default
+(``--param-sumsq carry``): each step's apply pass sums the squares of the
+parameter it stores, and the next step takes RMS(X) from that sum instead of
+reading the parameter again. Nothing else writes the parameters between the
+steps here, which is what the carry requires. The same number of steps of the
+plain call (RMS(X) read from the parameter every step) is timed afterwards on the
+same buffers and reported under ``read_param_sumsq``; ``--param-sumsq read``
+times only the plain call.
+
 With more than one GPU requested it exits: the step has no cross-GPU work to
 measure here (see the design notes on sharding).
 """
@@ -441,6 +450,9 @@ def main() -> int:
     ap.add_argument("--shard-ranks", type=int, default=0,
                     help="instead of the whole step: time one rank's share of a row-sharded step over N ranks "
                          "(the all-reduces of the partial sums between the calls are not part of it)")
+    ap.add_argument("--param-sumsq", choices=["carry", "read"], default="carry",
+                    help="Adafactor with scale_parameter: carry sum(X^2) from the previous step's apply pass "
+                         "(default; the plain call is timed beside it), or read X for it every step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the step: time a plain device copy of 4 GiB (one elementwise kernel), "
                          "the reference for achievable bandwidth and for scaling rocprofv3 byte counters")
@@ -500,33 +512,44 @@ def main() -> int:
            "lamb": _lib.lamb_hparams}[wl.optimizer](**hp)
     wsize = getattr(_lib, f"meo_{wl.optimizer}_workspace_size")(params, grads)
     ws = _lib.workspace(wsize, dev)
-    call = _lib.PreparedStep(wl.optimizer, hps, params, grads, states, ws)
+    carry = (wl.optimizer == "adafactor" and hp.get("scale_parameter", True) and args.param_sumsq == "carry")
+    if carry:
+        sums = torch.zeros(len(states), dtype=torch.float32, device=dev)
+        for i, st in enumerate(states):
+            st["param_sumsq"] = sums[i:i + 1]
+    call = _lib.PreparedStep(wl.optimizer, hps, params, grads, states, ws, carry=carry)
     stream = torch.cuda.current_stream()
     numel = wl.numel
 
-    t = 0
-    for _ in range(args.warmup):
-        t += 1
-        call(t, stream)
-    torch.cuda.synchronize()
+    def timed(call, t):
+        """W untimed steps, then K timed ones; (step index, per-step ms, total ms, passes)."""
+        for _ in range(args.warmup):
+            t += 1
+            call(t, stream)
+        torch.cuda.synchronize()
+        _lib.meo_profile_enable(True)
+        _lib.meo_profile_collect()  # drop anything recorded before
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            t += 1
+            call(t, stream)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+        _lib.meo_profile_enable(False)
+        return t, step_ms, evs[0].elapsed_time(evs[-1]), _lib.meo_profile_collect()
 
-    _lib.meo_profile_enable(True)
-    _lib.meo_profile_collect()  # drop anything recorded before
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        t += 1
-        call(t, stream)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    ev0, ev1 = evs[0], evs[-1]
-    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
-    _lib.meo_profile_enable(False)
-    passes = _lib.meo_profile_collect()
-    total_ms = ev0.elapsed_time(ev1)
+    t, step_ms, total_ms, passes = timed(call, 0)
     ms_step = total_ms / args.steps
     value = numel / (ms_step / 1e3)
+    read = None
+    if carry:  # the plain call on the same buffers, for comparison
+        t, r_ms, r_total, r_passes = timed(_lib.PreparedStep(wl.optimizer, hps, params, grads, states, ws), t)
+        read = {"ms_per_step": r_total / args.steps, "value": numel / (r_total / args.steps / 1e3),
+                "step_ms": {"min": min(r_ms), "median": sorted(r_ms)[len(r_ms) // 2], "max": max(r_ms)},
+                "passes_ms_per_step": {k: v["ms"] / args.steps for k, v in r_passes.items()}}
 
     ab = algorithmic_bytes(wl)
     step_gbps = ab["step"] / (ms_step / 1e3) / 1e9
@@ -553,6 +576,7 @@ def main() -> int:
                    "params": numel, "grad_dtype": str(wl.grad_dtype).replace("torch.", ""),
                    "param_dtype": str(wl.param_dtype).replace("torch.", ""),
                    "exp_avg_dtype": str(wl.state_dtype).replace("torch.", ""),
+                   "param_sumsq": "carry" if carry else "read",
                    "hparams": {k: (list(v) if isinstance(v, tuple) else v) for k, v in hp.items()}},
         "hbm": {"step_bytes": ab["step"], "achieved": step_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": step_gbps / HBM_PEAK_GBPS},
@@ -561,6 +585,8 @@ def main() -> int:
                      "bytes_per_launch": ab[dominant], "avg_ms": avg_ms},
         "passes_ms_per_step": {k: v["ms"] / args.steps for k, v in passes.items()},
     }
+    if read is not None:
+        out["read_param_sumsq"] = read
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MEO_VERSION 6
+#define MEO_VERSION 7
 
 /* Return codes. */
 #define MEO_OK          0
@@ -164,6 +164,7 @@ typedef struct meo_adafactor_state {
     float* exp_avg_sq_col; /* [batch*cols]; factored tensors only               */
     float* exp_avg_sq;     /* [numel]; 1-D tensors only                          */
     float* exp_avg_scale;  /* [ceil(numel / 128)]; iff exp_avg is MEO_I8          */
+    float* param_sumsq;    /* [1]; meo_adafactor_step_carry only (else ignored)  */
 } meo_adafactor_state;
 
 void   meo_adafactor_defaults(meo_adafactor_hparams* hp);
@@ -173,6 +174,41 @@ int    meo_adafactor_validate(const meo_adafactor_hparams* hp, int64_t step, int
 int    meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
                           const meo_tensor* tensors, const meo_adafactor_state* states,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same step, carrying sum(X^2) from one step to the next.
+ *
+ * scale_parameter multiplies the step size by RMS(X) of the parameter before
+ * the update (the note after "Step 5": the step size scales with the
+ * parameter's RMS). That parameter is exactly what the previous step stored, so
+ * this call sums the squares of the parameter it stores, in the same pass that
+ * stores it, and leaves the sum in each tensor's param_sumsq[0] (float32, the
+ * sum over the whole tensor of the stored values: bf16 parameters as rounded).
+ * The next call can then take RMS(X) from it instead of reading the parameter
+ * a second time, which saves 4 (fp32) or 2 (bf16) bytes per parameter of HBM
+ * traffic per step.
+ *
+ * param_sumsq_valid (host flag, for the whole list):
+ *   1  every tensor's param_sumsq holds the sum that the previous carry call
+ *      left for it, and nothing has written the parameter since. RMS(X) comes
+ *      from it; the parameter is read only by the apply pass.
+ *   0  RMS(X) is taken from the parameter, as meo_adafactor_step does (the
+ *      first step, or after anything else wrote a parameter, e.g. a checkpoint
+ *      load). Use 0 whenever in doubt: a stale sum silently scales the step by
+ *      the wrong RMS.
+ * In both cases param_sumsq is rewritten with the new parameter's sum. Results
+ * equal meo_adafactor_step's up to the order of the sum of squares (relative
+ * difference of RMS(X) around 1e-7).
+ *
+ * Every tensor with elements needs param_sumsq (4-byte aligned device memory,
+ * MEO_ENULL / MEO_EALIGN / MEO_EMEMORY otherwise); entries of tensors with zero
+ * elements are not touched. With scale_parameter = 0 the step uses no RMS(X):
+ * param_sumsq is neither read nor written and the call equals
+ * meo_adafactor_step. Everything else (validation, workspace, stream, errors)
+ * is as for meo_adafactor_step. */
+int    meo_adafactor_step_carry(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
+                                const meo_tensor* tensors, const meo_adafactor_state* states,
+                                int32_t param_sumsq_valid, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* ----------------------------------------------------------------------- CAME */
 
@@ -438,7 +474,7 @@ int meo_version(void);
  * launches[id] (both arrays of MEO_NUM_PASSES entries, caller-owned host
  * memory, zeroed by the caller), and forgets the events. Returns MEO_OK or
  * MEO_EHIP. Not for use under graph capture. */
-#define MEO_NUM_PASSES 16
+#define MEO_NUM_PASSES 17
 int         meo_profile_enable(int on);
 const char* meo_pass_name(int id);
 int         meo_profile_collect(double* total_ms, int64_t* launches);

@@ -31,7 +31,7 @@ ERROR_NAMES = {MEO_EINVAL: "MEO_EINVAL", MEO_ESHAPE: "MEO_ESHAPE", MEO_EDTYPE: "
                MEO_EHIP: "MEO_EHIP", MEO_EMEMORY: "MEO_EMEMORY"}
 EXPORTS = [
     "meo_adafactor_defaults", "meo_adafactor_workspace_size", "meo_adafactor_validate",
-    "meo_adafactor_step", "meo_came_defaults", "meo_came_workspace_size", "meo_came_validate",
+    "meo_adafactor_step", "meo_adafactor_step_carry", "meo_came_defaults", "meo_came_workspace_size", "meo_came_validate",
     "meo_came_step", "meo_lamb_defaults", "meo_lamb_workspace_size", "meo_lamb_validate",
     "meo_lamb_step", "meo_last_error", "meo_release_plans", "meo_version", "meo_profile_enable",
     "meo_pass_name", "meo_profile_collect",
@@ -42,7 +42,7 @@ EXPORTS = [
     "meo_galore_defaults", "meo_galore_rank", "meo_galore_workspace_size", "meo_galore_validate",
     "meo_galore_step", "meo_galore_refresh",
 ]
-MEO_NUM_PASSES = 16
+MEO_NUM_PASSES = 17
 
 
 class MeoError(RuntimeError):
@@ -72,7 +72,7 @@ class meo_adafactor_hparams(ctypes.Structure):
 
 class meo_adafactor_state(ctypes.Structure):
     _fields_ = [("exp_avg", c_void_p), ("exp_avg_sq_row", c_void_p), ("exp_avg_sq_col", c_void_p),
-                ("exp_avg_sq", c_void_p), ("exp_avg_scale", c_void_p)]
+                ("exp_avg_sq", c_void_p), ("exp_avg_scale", c_void_p), ("param_sumsq", c_void_p)]
 
 
 class meo_came_hparams(ctypes.Structure):
@@ -138,6 +138,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         getattr(lib, f"meo_{opt}_step").argtypes = [ctypes.POINTER(hp), c_int64, c_int32, T,
                                                     ctypes.POINTER(st), c_void_p, c_size_t, c_void_p]
         getattr(lib, f"meo_{opt}_step").restype = ctypes.c_int
+    lib.meo_adafactor_step_carry.argtypes = [ctypes.POINTER(meo_adafactor_hparams), c_int64, c_int32, T,
+                                             ctypes.POINTER(meo_adafactor_state), c_int32, c_void_p, c_size_t,
+                                             c_void_p]
+    lib.meo_adafactor_step_carry.restype = ctypes.c_int
     S = ctypes.POINTER(meo_shard)
     for opt, hp, st in (("adafactor", meo_adafactor_hparams, meo_adafactor_state),
                         ("lamb", meo_lamb_hparams, meo_lamb_state)):
@@ -268,7 +272,7 @@ def _states(cls, keys, states: Sequence[Dict[str, torch.Tensor]]):
     return arr
 
 
-ADAFACTOR_KEYS = ["exp_avg", "exp_avg_sq_row", "exp_avg_sq_col", "exp_avg_sq", "exp_avg_scale"]
+ADAFACTOR_KEYS = ["exp_avg", "exp_avg_sq_row", "exp_avg_sq_col", "exp_avg_sq", "exp_avg_scale", "param_sumsq"]
 CAME_KEYS = ["exp_avg", "exp_avg_sq_row", "exp_avg_sq_col", "exp_avg_res_row", "exp_avg_res_col",
              "exp_avg_sq", "exp_avg_scale"]
 LAMB_KEYS = ["exp_avg", "exp_avg_sq", "exp_avg_scale"]
@@ -359,6 +363,17 @@ def meo_adafactor_step(hp, step, params, grads, states, workspace=None, stream=N
     _check(load().meo_adafactor_step(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
                                      _states(meo_adafactor_state, ADAFACTOR_KEYS, states), ws, nb,
                                      _stream(stream)))
+
+
+def meo_adafactor_step_carry(hp, step, params, grads, states, param_sumsq_valid: bool, workspace=None,
+                             stream=None) -> None:
+    """meo_adafactor_step that leaves each tensor's sum of squares of its updated
+    parameter in ``states[k]["param_sumsq"]`` (float32 [1]) and, with
+    ``param_sumsq_valid``, takes RMS(X) from the sums the previous call left."""
+    ws, nb = _ws(workspace)
+    _check(load().meo_adafactor_step_carry(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
+                                           _states(meo_adafactor_state, ADAFACTOR_KEYS, states),
+                                           1 if param_sumsq_valid else 0, ws, nb, _stream(stream)))
 
 
 def meo_came_step(hp, step, params, grads, states, workspace=None, stream=None) -> None:
@@ -534,9 +549,16 @@ class PreparedStep:
     _KIND = {"adafactor": (meo_adafactor_state, ADAFACTOR_KEYS),
              "came": (meo_came_state, CAME_KEYS), "lamb": (meo_lamb_state, LAMB_KEYS)}
 
-    def __init__(self, optimizer: str, hp, params, grads, states, workspace=None):
+    def __init__(self, optimizer: str, hp, params, grads, states, workspace=None, carry: bool = False):
+        """carry (Adafactor): call meo_adafactor_step_carry; the first call reads
+        RMS(X) from the parameters, later ones take it from the carried sums until
+        ``invalidate()`` (for callers that write the parameters between steps)."""
         cls, keys = self._KIND[optimizer]
-        self.fn = getattr(load(), f"meo_{optimizer}_step")
+        if carry and optimizer != "adafactor":
+            raise ValueError("only Adafactor carries sum(X^2)")
+        self.fn = getattr(load(), f"meo_{optimizer}_step_carry" if carry else f"meo_{optimizer}_step")
+        self.carry = carry
+        self.valid = False
         self.hp = hp
         self.n = len(params)
         self.tensors = _tensors(params, grads, states)
@@ -544,7 +566,15 @@ class PreparedStep:
         self.ws, self.ws_bytes = _ws(workspace)
         self._keep = (list(params), list(grads), list(states), workspace)
 
+    def invalidate(self) -> None:
+        self.valid = False
+
     def __call__(self, step: int, stream=None) -> None:
+        if self.carry:
+            _check(self.fn(ctypes.byref(self.hp), step, self.n, self.tensors, self.states, 1 if self.valid else 0,
+                           self.ws, self.ws_bytes, _stream(stream)))
+            self.valid = True
+            return
         _check(self.fn(ctypes.byref(self.hp), step, self.n, self.tensors, self.states, self.ws,
                        self.ws_bytes, _stream(stream)))
 

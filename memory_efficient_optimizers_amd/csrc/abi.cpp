@@ -47,6 +47,7 @@ struct StatePtrs {
     float* c = nullptr;
     float* rr = nullptr;
     float* rc = nullptr;
+    float* xsq = nullptr; // Adafactor: carried sum(X^2) [1]
 };
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
@@ -70,7 +71,7 @@ struct Geo {
     int32_t mode = kFlat, cls = 0, B = 1, H = 1, W = 1, tr = 1, tc = 0, strips = 0, nrc = 0, ncc = 0;
     int64_t tiles = 0;  // 2-D tiles (factored) or flat tiles
     int32_t xchunks = 0;
-    int64_t rowpart = 0, colpart = 0, sumr = 0, tilepart = 0, xpart = 0, bscal = 0, scal = 0;
+    int64_t rowpart = 0, colpart = 0, sumr = 0, tilepart = 0, xpart = 0, apart = 0, bscal = 0, scal = 0;
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -117,6 +118,9 @@ int64_t layout(int op, int32_t n, const meo_tensor* ts, std::vector<Geo>* out) {
                 g.tiles = ceil_div(g.numel, kFlatTile);
                 g.tc = static_cast<int32_t>(g.tiles);
                 g.tilepart = off; off = align64(off + 2 * g.tiles);
+            }
+            if (op == kOpAdafactor) {  // the apply pass's sums of the updated X^2
+                g.apart = off; off = align64(off + g.tiles);
             }
             g.bscal = off; off = align64(off + 2 * static_cast<int64_t>(g.B));
             g.scal = off;  off = align64(off + kScalSlots);
@@ -376,6 +380,7 @@ int check_tensor_memory(int op, int32_t n, const meo_tensor* ts, const StatePtrs
         } else {
             rs.push_back({sp[k].v, ne * 4, "exp_avg_sq"});
         }
+        if (sp[k].xsq) rs.push_back({sp[k].xsq, 4, "param_sumsq"});
         for (const Range& r : rs) {
             const int rc = check_device_range(r.p, r.bytes, dev, who + r.name, MEO_EMEMORY);
             if (rc) return rc;
@@ -523,7 +528,8 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
         d.v = sp[k].v; d.r = sp[k].r; d.c = sp[k].c; d.rr = sp[k].rr; d.rc = sp[k].rc;
         d.numel = g.numel;
         d.rowpart = g.rowpart; d.colpart = g.colpart; d.sumr = g.sumr;
-        d.tilepart = g.tilepart; d.xpart = g.xpart; d.bscal = g.bscal; d.scal = g.scal;
+        d.tilepart = g.tilepart; d.xpart = g.xpart; d.apart = g.apart; d.bscal = g.bscal; d.scal = g.scal;
+        d.xsq = sp[k].xsq;
         d.xchunks = g.xchunks;
         d.B = g.B; d.H = g.H; d.W = g.W;
         d.mode = g.mode;
@@ -627,6 +633,7 @@ std::vector<StatePtrs> state_ptrs(int op, int32_t n, const void* states) {
             const auto& s = static_cast<const meo_adafactor_state*>(states)[k];
             sp.m = s.exp_avg; sp.v = s.exp_avg_sq; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col;
             sp.ms = s.exp_avg_scale;
+            sp.xsq = s.param_sumsq;
         } else if (op == kOpCame) {
             const auto& s = static_cast<const meo_came_state*>(states)[k];
             sp.m = s.exp_avg; sp.v = s.exp_avg_sq; sp.r = s.exp_avg_sq_row; sp.c = s.exp_avg_sq_col;
@@ -644,12 +651,12 @@ std::vector<StatePtrs> state_ptrs(int op, int32_t n, const void* states) {
 
 enum Pass { kPassStats = 0, kPassFinalize, kPassRms, kPassScalars, kPassAfApply, kPassCameMom,
             kPassCameApply, kPassLambMoments, kPassLambApply, kPassStatsWide, kPassStatsTiled,
-            kPassGaProject, kPassGaBack, kPassGaAdamw, kPassGaRefresh, kPassXnorm, kPassCount };
+            kPassGaProject, kPassGaBack, kPassGaAdamw, kPassGaRefresh, kPassXnorm, kPassSumsqFold, kPassCount };
 static_assert(kPassCount == MEO_NUM_PASSES, "pass table");
 const char* const kPassNames[kPassCount] = {"stats", "finalize", "rms", "scalars", "adafactor_apply",
                                             "came_mom", "came_apply", "lamb_moments", "lamb_apply",
                                             "stats_wide", "stats_tiled", "galore_project", "galore_back",
-                                            "galore_adamw", "galore_refresh", "xnorm"};
+                                            "galore_adamw", "galore_refresh", "xnorm", "sumsq_fold"};
 
 struct ProfRec { int pass; hipEvent_t a, b; };
 std::mutex g_prof_mu;
@@ -785,10 +792,28 @@ int meo_adafactor_validate(const meo_adafactor_hparams* hp, int64_t step, int32_
     return MEO_OK;
 }
 
-int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
-                       const meo_adafactor_state* st, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// carry: -1 plain step; 0 or 1 a step that leaves the updated parameter's sum of
+// squares in each tensor's param_sumsq (1: and takes RMS(X) from it).
+int adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                   const meo_adafactor_state* st, int carry, void* ws, size_t ws_bytes, void* stream) {
     int rc = meo_adafactor_validate(hp, step, n, ts, st);
     if (rc) return rc;
+    // RMS(X) is needed only to scale the step (scale_parameter); without it the
+    // carried sum is neither read nor written.
+    if (!hp->scale_parameter) carry = -1;
+    if (carry >= 0)
+        for (int32_t k = 0; k < n; ++k) {
+            int64_t numel = 0;
+            overflow_numel(ts[k], &numel);
+            if (numel == 0) continue;
+            if (!st[k].param_sumsq) return fail(MEO_ENULL, "tensor " + std::to_string(k) + ": param_sumsq is NULL");
+            if (reinterpret_cast<uintptr_t>(st[k].param_sumsq) % 4)
+                return fail(MEO_EALIGN, "tensor " + std::to_string(k) + ": param_sumsq misaligned");
+        }
     if (n == 0) return MEO_OK;
     rc = check_workspace(kOpAdafactor, n, ts, ws, ws_bytes);
     if (rc) return rc;
@@ -805,8 +830,8 @@ int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
     if (hp->relative_step) rho = std::fmin(hp->warmup_init ? 1e-6 * tt : 1e-2, 1.0 / std::sqrt(tt));
     else rho = hp->lr;
     const double b2 = 1.0 - std::pow(tt, hp->decay_rate);
-    // RMS(X) is needed only to scale the step (scale_parameter).
-    const int32_t need_x = hp->scale_parameter ? 1 : 0;
+    // The first pass reads X for RMS(X) unless the carried sums stand for it.
+    const int32_t need_x = hp->scale_parameter && carry != 1 ? 1 : 0;
     const StatsArgs sa{static_cast<float>(hp->eps1), static_cast<float>(b2), static_cast<float>(1.0 - b2), need_x,
                        b2, 1.0 - b2};
 
@@ -833,14 +858,33 @@ int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
         launch_rms(tab(kListTiled), p->count[kListTiled], need_x, s);
         pt.mark(kPassRms);
     }
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, nullptr, rho, hp->eps2,
-                                              hp->clip_threshold, hp->weight_decay, 0.0}, s);
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, nullptr, carry == 1 ? 1 : 0,
+                                              rho, hp->eps2, hp->clip_threshold, hp->weight_decay, 0.0}, s);
     pt.mark(kPassScalars);
     launch_af_apply(tab(kListAll), p->count[kListAll],
                     AfApplyArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1), hp->has_beta1},
-                    p->storage, s);
+                    p->storage, carry >= 0, s);
     pt.mark(kPassAfApply);
+    if (carry >= 0) {
+        launch_sumsq_fold(p->desc, w, p->n, s);
+        pt.mark(kPassSumsqFold);
+    }
     return launch_status("adafactor step launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int meo_adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                       const meo_adafactor_state* st, void* ws, size_t ws_bytes, void* stream) {
+    return adafactor_step(hp, step, n, ts, st, -1, ws, ws_bytes, stream);
+}
+
+int meo_adafactor_step_carry(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                             const meo_adafactor_state* st, int32_t param_sumsq_valid, void* ws, size_t ws_bytes,
+                             void* stream) {
+    return adafactor_step(hp, step, n, ts, st, param_sumsq_valid ? 1 : 0, ws, ws_bytes, stream);
 }
 
 // ----------------------------------------------------------------------------- CAME
@@ -914,7 +958,7 @@ int meo_came_step(const meo_came_hparams* hp, int64_t step, int32_t n, const meo
         launch_rms(tab(kListTiled), p->count[kListTiled], 0, s);
         pt.mark(kPassRms);
     }
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame1, 0, nullptr, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame1, 0, nullptr, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
                                               hp->lr}, s);
     pt.mark(kPassScalars);
     launch_came_mom(tab(kListAll), p->count[kListAll],
@@ -924,7 +968,7 @@ int meo_came_step(const meo_came_hparams* hp, int64_t step, int32_t n, const meo
     pt.mark(kPassCameMom);
     launch_finalize(tab(kListFin2), p->count[kListFin2], FinArgs{hp->beta3, 1, 1}, s);
     pt.mark(kPassFinalize);
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame2, 0, nullptr, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame2, 0, nullptr, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
                                               hp->lr}, s);
     pt.mark(kPassScalars);
     launch_came_apply(tab(kListAll), p->count[kListAll], p->storage, s);
@@ -990,7 +1034,7 @@ int meo_lamb_step(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo
     PassTimer pt(s);
     launch_lamb_moments(t, tiles, la, p->storage, s);
     pt.mark(kPassLambMoments);
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalLamb, 0, nullptr, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalLamb, 0, nullptr, 0, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
     pt.mark(kPassScalars);
     launch_lamb_apply(t, tiles, la, p->storage, s);
     pt.mark(kPassLambApply);
@@ -1151,12 +1195,12 @@ int meo_adafactor_shard_apply(const meo_adafactor_hparams* hp, int64_t step, int
     PassTimer pt(s);
     launch_shard_fold(tab(kListFold), p->count[kListFold], partials, a.b2, s);
     pt.mark(kPassFinalize);
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, partials, a.rho, hp->eps2,
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalAdafactor, hp->scale_parameter, partials, 0, a.rho, hp->eps2,
                                               hp->clip_threshold, hp->weight_decay, 0.0}, s);
     pt.mark(kPassScalars);
     launch_af_apply(tab(kListAll), p->count[kListAll],
                     AfApplyArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1), hp->has_beta1},
-                    p->storage, s);
+                    p->storage, false, s);
     pt.mark(kPassAfApply);
     return launch_status("adafactor shard apply launch");
 }
@@ -1188,7 +1232,7 @@ int meo_lamb_shard_apply(const meo_lamb_hparams* hp, int64_t step, int32_t n, co
     const hipStream_t s = static_cast<hipStream_t>(stream);
     float* w = static_cast<float*>(ws);
     PassTimer pt(s);
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalLamb, 0, partials, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalLamb, 0, partials, 0, 0.0, 0.0, 1.0, hp->weight_decay, hp->lr}, s);
     pt.mark(kPassScalars);
     launch_lamb_apply(Table{p->desc, p->items[kListAll], w}, p->count[kListAll], lamb_args(hp, step), p->storage, s);
     pt.mark(kPassLambApply);
@@ -1271,7 +1315,7 @@ int meo_came_shard_moment(const meo_came_hparams* hp, int64_t step, int32_t n, c
     PassTimer pt(s);
     launch_shard_fold(tab(kListFold), p->count[kListFold], partials, hp->beta2, s);
     pt.mark(kPassFinalize);
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame1, 0, partials, 0.0, 0.0, hp->clip_threshold,
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame1, 0, partials, 0, 0.0, 0.0, hp->clip_threshold,
                                               hp->weight_decay, hp->lr}, s);
     pt.mark(kPassScalars);
     launch_came_mom(tab(kListAll), p->count[kListAll],
@@ -1298,7 +1342,7 @@ int meo_came_shard_apply(const meo_came_hparams* hp, int64_t step, int32_t n, co
     PassTimer pt(s);
     launch_conf_fold(tab(kListConf), p->count[kListConf], conf, hp->beta3, s);
     pt.mark(kPassFinalize);
-    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame2, 0, conf, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
+    launch_scalars(p->desc, w, p->n, ScalArgs{kScalCame2, 0, conf, 0, 0.0, 0.0, hp->clip_threshold, hp->weight_decay,
                                               hp->lr}, s);
     pt.mark(kPassScalars);
     launch_came_apply(tab(kListAll), p->count[kListAll], p->storage, s);

@@ -10,6 +10,11 @@
 // first moment are widened to fp32 on load and rounded to the nearest bf16 when
 // stored; the new first moment is rounded as soon as it is formed, so the step
 // is the stored value.
+//
+// The SQ variant also sums the squares of the updated parameter, as stored, per
+// tile: the next step's RMS(X) (scale_parameter) is taken on exactly this
+// parameter, so a caller that leaves the parameter alone between steps need not
+// read it again for that statistic.
 #include "internal.h"
 
 namespace meo {
@@ -24,6 +29,20 @@ __device__ __forceinline__ u32x4 u4_of(float a, float b, float c, float e) {
     return u32x4{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(e)};
 }
 
+__device__ __forceinline__ float sumsq8(const float* f) {
+    return ((f[0] * f[0] + f[1] * f[1]) + (f[2] * f[2] + f[3] * f[3])) +
+           ((f[4] * f[4] + f[5] * f[5]) + (f[6] * f[6] + f[7] * f[7]));
+}
+
+// Sum of the squares of the first `valid` of 8 parameter values as they were
+// stored (bf16: rounded to nearest even).
+__device__ __forceinline__ float stored_sumsq8(const float* x, int valid, bool bf16) {
+    float f[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) f[e] = e < valid ? (bf16 ? round_bf16(x[e]) : x[e]) : 0.0f;
+    return sumsq8(f);
+}
+
 // The rows of one wave in a 2-D tile with 16-byte aligned rows (W % 8 == 0, so a
 // lane has all 8 of its columns or none). The wave's 16 rows are addressed through
 // buffer resources: a scalar base per tensor, the row offset in a scalar register
@@ -32,15 +51,16 @@ __device__ __forceinline__ u32x4 u4_of(float a, float b, float c, float e) {
 // loaded per batch and stay packed until their row is computed; 16-bit storage
 // moves half the bytes per row, so it takes twice the rows. W < 2^26 keeps the
 // wave's byte range within 32 bits.
-template <bool G16, bool S16>
-__device__ __forceinline__ void af_rows(const TDesc& d, int lt, float coef, float decay,
-                                        const AfApplyArgs& a) {
+template <bool G16, bool S16, bool SQ>
+__device__ __forceinline__ float af_rows(const TDesc& d, int lt, float coef, float decay,
+                                         const AfApplyArgs& a) {
     constexpr int RB = S16 ? 8 : 4;
     constexpr int GW = G16 ? 1 : 2, SW = S16 ? 1 : 2;       // 16-byte words per lane and row
     constexpr uint32_t GE = G16 ? 2 : 4, SE = S16 ? 2 : 4;  // bytes per element
     const TileRC p = tile_rc(d, lt);
-    if (p.valid != kVec || p.nrows <= 0) return;
+    if (p.valid != kVec || p.nrows <= 0) return 0.0f;
     const bool mom = a.has_beta1;
+    float sq = 0.0f;  // sum of the updated X^2 over this lane's rows
     float cf[kVec];
     const float* ccol = d.c + static_cast<int64_t>(p.b) * d.W + p.col;
 #pragma unroll
@@ -102,7 +122,12 @@ __device__ __forceinline__ void af_rows(const TDesc& d, int lt, float coef, floa
                 }
                 if (S16) {
                     if (mom) buf_st(mp, rm, ls, r * SE);
-                    buf_st(pack_bf16x8(xf), rx, ls, r * SE);
+                    const u32x4 xp = pack_bf16x8(xf);
+                    buf_st(xp, rx, ls, r * SE);
+                    if (SQ) {
+                        bf16x8(xp, xf);  // the stored values
+                        sq += sumsq8(xf);
+                    }
                 } else {
                     if (mom) {
                         buf_st(u4_of(mf[0], mf[1], mf[2], mf[3]), rm, ls, r * SE);
@@ -110,19 +135,20 @@ __device__ __forceinline__ void af_rows(const TDesc& d, int lt, float coef, floa
                     }
                     buf_st(u4_of(xf[0], xf[1], xf[2], xf[3]), rx, ls, r * SE);
                     buf_st(u4_of(xf[4], xf[5], xf[6], xf[7]), rx, ls + 16u, r * SE);
+                    if (SQ) sq += sumsq8(xf);
                 }
             }
         }
     }
+    return sq;
 }
 
-template <int ST>
-__global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
-    const int2 it = t.items[blockIdx.x];
-    if (it.x < 0) return;  // an empty item of an XCD-aligned list
-    const TDesc d = t.desc[it.x];
-    const int lt = it.y;
+// One apply tile; returns this thread's sum of the updated X^2 (SQ; else 0), over
+// the elements it stored.
+template <int ST, bool SQ>
+__device__ __forceinline__ float af_tile(const Table& t, const TDesc& d, int lt, const AfApplyArgs& a) {
     const float* ws = t.ws;
+    float sq = 0.0f;
     const float decay = ldf(ws + d.scal + kSlotDecay);
     const bool vec = d.vec, bf = d.gbf16, xb = x_is_bf16<ST>(d), mb = m_is_bf16<ST>(d), mi = m_is_i8<ST>(d);
     const bool mom = a.has_beta1;
@@ -133,9 +159,8 @@ __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
         const float coef = ldf(ws + d.bscal + p.b);
         if constexpr (ST == kStoreBf16) {
             if (vec && d.W < (1 << 26)) {
-                if (bf) af_rows<true, true>(d, lt, coef, decay, a);
-                else af_rows<false, true>(d, lt, coef, decay, a);
-                return;
+                if (bf) return af_rows<true, true, SQ>(d, lt, coef, decay, a);
+                return af_rows<false, true, SQ>(d, lt, coef, decay, a);
             }
         }
         const int64_t mat = static_cast<int64_t>(p.b) * d.H * d.W;
@@ -180,6 +205,7 @@ __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
                     for (int e = 0; e < kVec; ++e) x[i][e] = fmaf(-decay, x[i][e], x[i][e]) - step[e];
                     if (mom) store_m8(d, off, p.valid, vec, mb, mi, m[i], q);
                     store_v8(d.x, off, p.valid, vec, xb, x[i]);
+                    if (SQ) sq += stored_sumsq8(x[i], p.valid, xb);
                 }
             }
         }
@@ -211,18 +237,42 @@ __global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
             for (int e = 0; e < kVec; ++e) x[e] = fmaf(-decay, x[e], x[e]) - step[e];
             if (mom) store_m8(d, i, valid, vec, mb, mi, m, q);
             store_v8(d.x, i, valid, vec, xb, x);
+            if (SQ) sq += stored_sumsq8(x, valid, xb);
         }
+    }
+    return sq;
+}
+
+template <int ST, bool SQ>
+__global__ __launch_bounds__(kThreads) void k_af_apply(Table t, AfApplyArgs a) {
+    const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;  // an empty item of an XCD-aligned list (the whole block)
+    const TDesc d = t.desc[it.x];
+    float sq = af_tile<ST, SQ>(t, d, it.y, a);
+    if constexpr (SQ) {
+        // every thread of the block gets here: af_tile has no barrier and no exit
+        // that skips this reduction
+        __shared__ float red[2 * kWaves];
+        float unused = 0.0f;
+        block_sum2(sq, unused, red);
+        if (threadIdx.x == 0) stf(t.ws + d.apart + it.y, sq);
     }
 }
 
-void launch_af_apply(const Table& t, int64_t n, const AfApplyArgs& a, int storage, hipStream_t s) {
-    if (n <= 0) return;
+template <bool SQ>
+void launch_af_apply_sq(const Table& t, int64_t n, const AfApplyArgs& a, int storage, hipStream_t s) {
     const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
-    if (storage == kStoreF32) hipLaunchKernelGGL(k_af_apply<kStoreF32>, grid, block, 0, s, t, a);
-    else if (storage == kStoreBf16) hipLaunchKernelGGL(k_af_apply<kStoreBf16>, grid, block, 0, s, t, a);
-    else if (storage == kStoreF32I8) hipLaunchKernelGGL(k_af_apply<kStoreF32I8>, grid, block, 0, s, t, a);
-    else if (storage == kStoreBf16I8) hipLaunchKernelGGL(k_af_apply<kStoreBf16I8>, grid, block, 0, s, t, a);
-    else hipLaunchKernelGGL(k_af_apply<kStoreMixed>, grid, block, 0, s, t, a);
+    if (storage == kStoreF32) hipLaunchKernelGGL((k_af_apply<kStoreF32, SQ>), grid, block, 0, s, t, a);
+    else if (storage == kStoreBf16) hipLaunchKernelGGL((k_af_apply<kStoreBf16, SQ>), grid, block, 0, s, t, a);
+    else if (storage == kStoreF32I8) hipLaunchKernelGGL((k_af_apply<kStoreF32I8, SQ>), grid, block, 0, s, t, a);
+    else if (storage == kStoreBf16I8) hipLaunchKernelGGL((k_af_apply<kStoreBf16I8, SQ>), grid, block, 0, s, t, a);
+    else hipLaunchKernelGGL((k_af_apply<kStoreMixed, SQ>), grid, block, 0, s, t, a);
+}
+
+void launch_af_apply(const Table& t, int64_t n, const AfApplyArgs& a, int storage, bool sumsq, hipStream_t s) {
+    if (n <= 0) return;
+    if (sumsq) launch_af_apply_sq<true>(t, n, a, storage, s);
+    else launch_af_apply_sq<false>(t, n, a, storage, s);
 }
 
 }  // namespace meo

@@ -80,6 +80,8 @@ struct TDesc {
                       // row-complete: [B][ncc] sums of S_j / C_j per finalize chunk
     int64_t tilepart; // [tiles][2] per-tile partial sums for the per-tensor scalars
     int64_t xpart;    // row-complete: [xchunks] sums of X^2 per chunk of kFlatTile elements
+    int64_t apart;    // Adafactor: [tiles] sums of the updated X^2 per apply tile (carried sum(X^2))
+    float* xsq;       // Adafactor: the carried sum(X^2) of the parameter [1] (nullable)
     int64_t bscal;    // [2][B] per-matrix coefficients
     int64_t scal;     // [kScalSlots] per-tensor scalars
     int32_t B, H, W;
@@ -512,6 +514,7 @@ struct ScalArgs {
     int32_t mode;
     int32_t scale_parameter;
     const float* partials;  // row-sharded steps: the all-reduced partial sums; else null
+    int32_t carried_x;      // Adafactor: take sum(X^2) from each tensor's carried value (TDesc::xsq)
     double rho;         // Adafactor base step size
     double eps2;        // Adafactor floor of RMS(param)
     double clip;        // clip threshold
@@ -541,7 +544,10 @@ void launch_stats(const Table& t, int64_t n, const StatsArgs& a, hipStream_t s);
 void launch_finalize(const Table& t, int64_t n, const FinArgs& a, hipStream_t s);
 void launch_rms(const Table& t, int64_t n, int32_t need_x, hipStream_t s);
 void launch_scalars(const TDesc* desc, float* ws, int32_t n, const ScalArgs& a, hipStream_t s);
-void launch_af_apply(const Table& t, int64_t n, const AfApplyArgs& a, int storage, hipStream_t s);
+// sumsq: also sum the squares of the updated parameter per tile (into TDesc::apart).
+void launch_af_apply(const Table& t, int64_t n, const AfApplyArgs& a, int storage, bool sumsq, hipStream_t s);
+// Folds the per-tile sums of the updated X^2 into each tensor's carried value.
+void launch_sumsq_fold(const TDesc* desc, const float* ws, int32_t n, hipStream_t s);
 void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, int storage, hipStream_t s);
 void launch_came_apply(const Table& t, int64_t n, int storage, hipStream_t s);
 void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, int storage, hipStream_t s);

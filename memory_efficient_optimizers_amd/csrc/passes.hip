@@ -590,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
         if (P) {
             sx = static_cast<double>(ldf(P + 2 * BW + d.B));
             numel = static_cast<double>(d.B) * static_cast<double>(d.total) * static_cast<double>(d.W);
-        } else if (a.mode == kScalAdafactor && a.scale_parameter) {  // the chunks ran only then
+        } else if (a.mode == kScalAdafactor && a.scale_parameter && !a.carried_x) {  // the chunks ran only then
             double a_ = 0.0;
             for (int j = threadIdx.x; j < d.xchunks; j += kThreads) a_ += static_cast<double>(ldf(ws + d.xpart + j));
             sx = block_sum_d(a_, lds);
@@ -601,6 +601,9 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
         su = tile_sum(tp, tiles, 0, lds);
         sx = tile_sum(tp, tiles, 1, lds);
     }
+    // The carried sum of X^2: the previous step's apply pass summed the squares of
+    // the parameter it stored, which is this step's pre-update parameter.
+    if (a.carried_x && a.mode == kScalAdafactor && d.xsq) sx = static_cast<double>(ldf(d.xsq));
     const double rms_u = sqrt(su / numel);
     const double kappa = fmax(1.0, rms_u / a.clip);
     double alpha = 1.0;
@@ -629,6 +632,26 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
 
 void launch_scalars(const TDesc* desc, float* ws, int32_t n, const ScalArgs& a, hipStream_t s) {
     if (n > 0) hipLaunchKernelGGL(k_scalars, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, desc, ws, a);
+}
+
+// ----------------------------------------------------------------------------- carried sum(X^2)
+
+// One block per tensor: the apply pass's per-tile sums of the updated X^2, in
+// fp64 and a fixed order, into the tensor's carried value.
+__global__ __launch_bounds__(kThreads) void k_sumsq_fold(const TDesc* __restrict__ desc, const float* ws) {
+    __shared__ double lds[kWaves];
+    const TDesc d = desc[blockIdx.x];
+    if (!d.xsq) return;  // the whole block
+    const int64_t tiles = d.mode == kFlat ? static_cast<int64_t>(d.tc)
+                                          : static_cast<int64_t>(d.B) * d.tr * d.tc;
+    double a = 0.0;
+    for (int64_t j = threadIdx.x; j < tiles; j += kThreads) a += static_cast<double>(ldf(ws + d.apart + j));
+    const double sum = block_sum_d(a, lds);
+    if (threadIdx.x == 0) stf(d.xsq, static_cast<float>(sum));
+}
+
+void launch_sumsq_fold(const TDesc* desc, const float* ws, int32_t n, hipStream_t s) {
+    if (n > 0) hipLaunchKernelGGL(k_sumsq_fold, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, desc, ws);
 }
 
 }  // namespace meo

@@ -128,7 +128,17 @@ class Adafactor(_MeoOptimizer):
     clip_threshold=1.0, decay_rate=-0.8, beta1=None, weight_decay=0.0,
     scale_parameter=True, relative_step=True, warmup_init=False. ``state_dtype``:
     element type of ``exp_avg`` (None: that of the parameter; torch.int8: 8-bit where
-    ``moment_dtype`` allows, with ``min_8bit_size``)."""
+    ``moment_dtype`` allows, with ``min_8bit_size``).
+
+    ``carry_param_sumsq``: with scale_parameter, keep each parameter's sum of
+    squares from the step that stored it (state ``param_sumsq``) and take the next
+    step's RMS(X) from it instead of reading the parameter again (4 or 2 bytes per
+    parameter less HBM traffic per step). It is used only while every parameter of
+    the call is unchanged since the previous step: the optimizer compares the
+    parameter's version counter (bumped by every in-place operation on the
+    parameter or its views), storage and the state tensor. Writes through
+    ``param.data`` bypass the version counter; a caller that writes parameters
+    that way must leave this off or call ``invalidate_param_sumsq()``."""
 
     _kind = "adafactor"
     _HP = ("lr", "eps", "clip_threshold", "decay_rate", "beta1", "weight_decay", "scale_parameter",
@@ -137,7 +147,7 @@ class Adafactor(_MeoOptimizer):
     def __init__(self, params, lr=None, eps=(1e-30, 1e-3), clip_threshold=1.0, decay_rate=-0.8,
                  beta1=None, weight_decay=0.0, scale_parameter=True, relative_step=True,
                  warmup_init=False, state_dtype=None,
-                 min_8bit_size=4096):
+                 min_8bit_size=4096, carry_param_sumsq=False):
         if lr is not None and relative_step:
             raise ValueError("Cannot combine manual lr and relative_step=True options")
         if warmup_init and not relative_step:
@@ -146,17 +156,43 @@ class Adafactor(_MeoOptimizer):
                         beta1=beta1, weight_decay=weight_decay, scale_parameter=scale_parameter,
                         relative_step=relative_step, warmup_init=warmup_init)
         super().__init__(params, defaults, state_dtype, min_8bit_size)
+        self._carry = bool(carry_param_sumsq)
+        # id(param) -> (version, data_ptr, id of its param_sumsq) after the last carry step
+        self._carried: Dict[int, Tuple[int, int, int]] = {}
+
+    def invalidate_param_sumsq(self) -> None:
+        """The next step reads every parameter for RMS(X) again."""
+        self._carried.clear()
+
+    def load_state_dict(self, state_dict) -> None:
+        super().load_state_dict(state_dict)
+        self._carried.clear()
 
     def _state_for(self, p, group):
-        return _lib.init_state("adafactor", p, beta1=group["beta1"] is not None,
-                               state_dtype=self._moment_dtype(p))
+        st = _lib.init_state("adafactor", p, beta1=group["beta1"] is not None,
+                             state_dtype=self._moment_dtype(p))
+        if self._carry:
+            st["param_sumsq"] = torch.zeros(1, dtype=torch.float32, device=p.device)
+        return st
+
+    def _tag(self, p, st):
+        return (p._version, p.data_ptr(), id(st["param_sumsq"]))
 
     def _wsize(self, params, grads):
         return _lib.meo_adafactor_workspace_size(params, grads)
 
     def _call(self, group, step, params, grads, states, ws):
         hp = _lib.adafactor_hparams(**{k: group[k] for k in self._HP})
-        _lib.meo_adafactor_step(hp, step, params, grads, states, ws)
+        if not (self._carry and group["scale_parameter"]):
+            _lib.meo_adafactor_step(hp, step, params, grads, states, ws)
+            return
+        for p, st in zip(params, states):
+            if "param_sumsq" not in st:  # e.g. state loaded from a run without the carry
+                st["param_sumsq"] = torch.zeros(1, dtype=torch.float32, device=p.device)
+        valid = all(self._carried.get(id(p)) == self._tag(p, st) for p, st in zip(params, states))
+        _lib.meo_adafactor_step_carry(hp, step, params, grads, states, valid, ws)
+        for p, st in zip(params, states):
+            self._carried[id(p)] = self._tag(p, st)
 
 
 class CAME(_MeoOptimizer):

@@ -190,7 +190,10 @@ def lib_workspace(opt, params, grads):
 class Run:
     """The library and the oracle side by side over a workload."""
 
-    def __init__(self, wl: workloads.Workload, device="cuda", hp: dict = None, min_8bit_size: int = 4096):
+    def __init__(self, wl: workloads.Workload, device="cuda", hp: dict = None, min_8bit_size: int = 4096,
+                 carry: bool = False):
+        """carry (Adafactor): step through meo_adafactor_step_carry, taking RMS(X)
+        from the carried sums from the second step on (``carry_valid``)."""
         self.wl = wl
         self.opt = wl.optimizer
         self.hp = dict(wl.hparams if hp is None else hp)
@@ -205,6 +208,12 @@ class Run:
                     for p, s in zip(self.params, self.storage)]
         self.ws = None
         self.t = 0
+        self.carry = carry
+        self.carry_valid = False
+        if carry:
+            assert self.opt == "adafactor"
+            for st, p in zip(self.states, self.params):
+                st["param_sumsq"] = torch.zeros(1, dtype=torch.float32, device=p.device)
 
     def grads(self, s: int):
         return workloads.grads(self.wl, s, self.scales, self.device)
@@ -215,7 +224,12 @@ class Run:
             grads = self.grads(self.t - 1)
         if self.ws is None:
             self.ws = lib_workspace(self.opt, self.params, grads)
-        lib_step(self.opt, self.hps, self.t, self.params, grads, self.states, self.ws)
+        if self.carry:
+            _lib.meo_adafactor_step_carry(self.hps, self.t, self.params, grads, self.states, self.carry_valid,
+                                          self.ws)
+            self.carry_valid = True
+        else:
+            lib_step(self.opt, self.hps, self.t, self.params, grads, self.states, self.ws)
         if oracle_too:
             gs = [to64(g) for g in grads]
             for k in range(len(gs)):
@@ -231,6 +245,19 @@ class Run:
             for key, lib, ref in outputs(self.params[k], self.states[k], self.ox[k], self.ost[k]):
                 kind = bar_kind(self.opt, self.hp, self.storage[k], key)
                 out[f"{spec.name}:{key}"] = check_bar(kind, key, lib, ref) + (kind,)
+        return out
+
+    def sumsq_errors(self) -> Dict[str, float]:
+        """Carry runs: relative error of each tensor's carried sum of squares against
+        the sum of squares of the oracle's parameter (by definition, in fp64)."""
+        torch.cuda.synchronize()
+        out = {}
+        for k, spec in enumerate(self.wl.specs):
+            if self.params[k].numel() == 0:
+                continue
+            want = float(np.sum(np.square(self.ox[k])))
+            got = float(self.states[k]["param_sumsq"].item())
+            out[spec.name] = abs(got - want) / want if want > 0 else abs(got)
         return out
 
     def errors(self) -> Dict[str, float]:
