@@ -321,13 +321,35 @@ __global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a
         pl.load(d.nl, d.D, d.r, n0, k0, vec);
         pu.load(d.u, d.d, d.r, u0, k0, vec);
     };
-    fetch(0);
-    for (int k0 = 0; k0 < d.r; k0 += kGaKb) {
-        ph.store(sh);
-        pl.store(sl);
-        pu.store(su);
-        __syncthreads();
-        if (k0 + kGaKb < d.r) fetch(k0 + kGaKb);
+    // The wave's part of the parameter tile, as the epilogue reads it (lane: rows
+    // (lane >> 3) + 8 q of each 32-row half ib, columns 8 (lane & 7) ..): loaded
+    // during the last contraction block, when the staging registers are free, so
+    // that its HBM latency overlaps those MFMAs. Chunks that are not whole 16-byte
+    // rows are read in the epilogue instead.
+    const int64_t wr0 = Left ? r0 + ug * 64 : r0 + ng * 64;
+    const int64_t wc0 = Left ? c0 + ng * 64 : c0 + ug * 64;
+    const int64_t wcol = wc0 + (lane & 7) * 8;
+    u32x4 wpre[2][4][2];
+    auto prefetch_w = [&]() {
+        if (!(d.wvec && wcol + 8 <= d.n)) return;
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t row = wr0 + ib * 32 + (lane >> 3) + 8 * q;
+                if (row >= d.m) continue;
+                const int64_t idx = row * d.n + wcol;
+                if (d.xbf16) {
+                    wpre[ib][q][0] = *gld<u32x4>(static_cast<const uint16_t*>(d.x) + idx);
+                } else {
+                    wpre[ib][q][0] = *gld<u32x4>(static_cast<const float*>(d.x) + idx);
+                    wpre[ib][q][1] = *gld<u32x4>(static_cast<const float*>(d.x) + idx + 4);
+                }
+            }
+    };
+    // One staged contraction block: 4 steps of 16, two MFMAs (high and low plane)
+    // per accumulator block.
+    auto multiply = [&]() {
 #pragma unroll
         for (int ks = 0; ks < kGaKb; ks += 16) {
             const int kk = ks + 8 * (lane >> 5);
@@ -351,12 +373,30 @@ __global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a
                     }
                 }
         }
+    };
+    fetch(0);
+    // All blocks but the last: the next block's loads go out before the multiply.
+    // The last one (peeled, so that the parameter registers are live only there
+    // and in the epilogue) prefetches the parameter tile instead.
+    const int klast = (d.r - 1) / kGaKb * kGaKb;
+    for (int k0 = 0; k0 < klast; k0 += kGaKb) {
+        ph.store(sh);
+        pl.store(sl);
+        pu.store(su);
+        __syncthreads();
+        fetch(k0 + kGaKb);
+        multiply();
         __syncthreads();
     }
+    ph.store(sh);
+    pl.store(sl);
+    pu.store(su);
+    __syncthreads();
+    prefetch_w();
+    multiply();
+    __syncthreads();
     // W <- decay W - coef C, rows of 8 columns per lane (see ep_spill), 16 bytes at
     // a time where rows allow.
-    const int64_t wr0 = Left ? r0 + ug * 64 : r0 + ng * 64;
-    const int64_t wc0 = Left ? c0 + ng * 64 : c0 + ug * 64;
     float* lw = reinterpret_cast<float*>(arena) + wave * kEpWave;
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
@@ -373,7 +413,7 @@ __global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a
             if (d.xbf16) {
                 uint16_t* xp = static_cast<uint16_t*>(d.x) + idx;
                 if (full) {
-                    bf16x8(*gld<u32x4>(xp), w);
+                    bf16x8(wpre[ib][q][0], w);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
@@ -391,8 +431,11 @@ __global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a
             } else {
                 float* xp = static_cast<float*>(d.x) + idx;
                 if (full) {
-                    const f32x4 x0 = *gld<f32x4>(xp), x1 = *gld<f32x4>(xp + 4);
-                    w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w; w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+                    const u32x4 x0 = wpre[ib][q][0], x1 = wpre[ib][q][1];
+                    w[0] = __uint_as_float(x0.x); w[1] = __uint_as_float(x0.y);
+                    w[2] = __uint_as_float(x0.z); w[3] = __uint_as_float(x0.w);
+                    w[4] = __uint_as_float(x1.x); w[5] = __uint_as_float(x1.y);
+                    w[6] = __uint_as_float(x1.z); w[7] = __uint_as_float(x1.w);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) w[e] = col + e < d.n ? *gld<float>(xp + e) : 0.0f;
