@@ -180,7 +180,8 @@ def shard_bench(torch, _lib, workloads, wl, args) -> int:
     tensor); stats call, then apply call, per step (CAME: stats, moment, apply).
     The partial sums go from one call to the next unreduced: the all-reduce over
     ranks that sits between them is not part of the measured work, so the values
-    reached are not a real step's."""
+    reached are not a real step's. Adafactor with scale_parameter carries the
+    shard's sum(X^2) as the whole-list bench does (``--param-sumsq``)."""
     from memory_efficient_optimizers_amd.optim import moment_dtype
     n, dev, opt = args.shard_ranks, "cuda", wl.optimizer
     hp = dict(wl.hparams)
@@ -205,11 +206,16 @@ def shard_bench(torch, _lib, workloads, wl, args) -> int:
         if "exp_avg_sq_col" in st:
             st["exp_avg_sq_col"] = torch.zeros(tuple(s.shape[:-2]) + tuple(s.shape[-1:]), device=dev)
         states.append(st)
+    carry = opt == "adafactor" and hp.get("scale_parameter", True) and args.param_sumsq == "carry"
+    if carry:
+        sums = torch.zeros(len(states), dtype=torch.float32, device=dev)
+        for i, st in enumerate(states):
+            st["param_sumsq"] = sums[i:i + 1]
     hps = {"adafactor": _lib.adafactor_hparams, "lamb": _lib.lamb_hparams, "came": _lib.came_hparams}[opt](**hp)
     ws = _lib.workspace(getattr(_lib, f"meo_{opt}_workspace_size")(params, grads), dev)
     part = torch.zeros(getattr(_lib, f"meo_{opt}_partials_size")(params, grads), device=dev)
     conf = torch.zeros(max(_lib.meo_came_confidence_size(params, grads), 1), device=dev) if opt == "came" else None
-    call = _lib.PreparedShardStep(opt, hps, params, grads, totals, states, part, ws, conf)
+    call = _lib.PreparedShardStep(opt, hps, params, grads, totals, states, part, ws, conf, carry=carry)
 
     def step(t):
         call.stats(t, stream)
@@ -237,7 +243,8 @@ def shard_bench(torch, _lib, workloads, wl, args) -> int:
     out = {"metric": f"one rank's share of a row-sharded optimizer step over {n} ranks (all-reduce excluded)",
            "value": numel / (ms / 1e3), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "data": "synthetic",
-           "config": {"workload": wl.name, "ranks": n, "rank_params": numel, "partials_floats": part.numel()},
+           "config": {"workload": wl.name, "ranks": n, "rank_params": numel, "partials_floats": part.numel(),
+                      "param_sumsq": "carry" if carry else "read"},
            "hbm": {"step_bytes": step_bytes, "achieved": step_bytes / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBPS,
                    "unit": "GB/s", "frac": step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS}}
     print(json.dumps(out), flush=True)

@@ -344,6 +344,25 @@ int    meo_adafactor_shard_apply(const meo_adafactor_hparams* hp, int64_t step, 
                                  const meo_tensor* tensors, const meo_shard* shards,
                                  const meo_adafactor_state* states, const float* partials,
                                  void* workspace, size_t workspace_bytes, void* stream);
+/* The row-sharded Adafactor step with the carried sum(X^2) of
+ * meo_adafactor_step_carry. Each rank's param_sumsq holds the sum of squares of
+ * its own shard: meo_adafactor_shard_apply_carry leaves it (the sum over the rows
+ * the rank stored), and meo_adafactor_shard_stats_carry with
+ * param_sumsq_valid = 1 puts it into the record's sum of X^2 instead of reading the
+ * shard's parameter, so the all-reduce still yields the whole tensor's sum.
+ * param_sumsq_valid = 0 reads the parameter as meo_adafactor_shard_stats does.
+ * The flag must be the same on every rank (it selects what the record holds, not
+ * how it is summed). param_sumsq requirements and the scale_parameter = 0 case are
+ * as for meo_adafactor_step_carry; everything else as for the plain shard calls. */
+int    meo_adafactor_shard_stats_carry(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
+                                       const meo_tensor* tensors, const meo_shard* shards,
+                                       const meo_adafactor_state* states, int32_t param_sumsq_valid,
+                                       float* partials, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+int    meo_adafactor_shard_apply_carry(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
+                                       const meo_tensor* tensors, const meo_shard* shards,
+                                       const meo_adafactor_state* states, const float* partials,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 /* CAME takes two exchanges. meo_came_shard_stats writes `partials` (the Adafactor
  * record above; its sum of X^2 is 0); after the all-reduce, meo_came_shard_moment
  * folds it (column statistic, clip divisor), updates the first moment of the shard

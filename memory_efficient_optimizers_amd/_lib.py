@@ -36,6 +36,7 @@ EXPORTS = [
     "meo_lamb_step", "meo_last_error", "meo_release_plans", "meo_version", "meo_profile_enable",
     "meo_pass_name", "meo_profile_collect",
     "meo_adafactor_partials_size", "meo_adafactor_shard_stats", "meo_adafactor_shard_apply",
+    "meo_adafactor_shard_stats_carry", "meo_adafactor_shard_apply_carry",
     "meo_lamb_partials_size", "meo_lamb_shard_stats", "meo_lamb_shard_apply",
     "meo_came_partials_size", "meo_came_confidence_size", "meo_came_shard_stats", "meo_came_shard_moment",
     "meo_came_shard_apply",
@@ -152,6 +153,13 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
             fn.argtypes = [ctypes.POINTER(hp), c_int64, c_int32, T, S, ctypes.POINTER(st), c_void_p, c_void_p,
                            c_size_t, c_void_p]
             fn.restype = ctypes.c_int
+    AH, AS = ctypes.POINTER(meo_adafactor_hparams), ctypes.POINTER(meo_adafactor_state)
+    lib.meo_adafactor_shard_stats_carry.argtypes = [AH, c_int64, c_int32, T, S, AS, c_int32, c_void_p, c_void_p,
+                                                    c_size_t, c_void_p]
+    lib.meo_adafactor_shard_stats_carry.restype = ctypes.c_int
+    lib.meo_adafactor_shard_apply_carry.argtypes = [AH, c_int64, c_int32, T, S, AS, c_void_p, c_void_p, c_size_t,
+                                                    c_void_p]
+    lib.meo_adafactor_shard_apply_carry.restype = ctypes.c_int
     CH, CS = ctypes.POINTER(meo_came_hparams), ctypes.POINTER(meo_came_state)
     for name in ("meo_came_partials_size", "meo_came_confidence_size"):
         getattr(lib, name).argtypes = [c_int32, T]
@@ -425,6 +433,23 @@ def meo_adafactor_shard_apply(hp, step, params, grads, totals, states, partials,
     _shard_call("adafactor", "apply", hp, step, params, grads, totals, states, partials, workspace, stream)
 
 
+def meo_adafactor_shard_stats_carry(hp, step, params, grads, totals, states, param_sumsq_valid: bool, partials,
+                                    workspace=None, stream=None):
+    """meo_adafactor_shard_stats whose record takes the shard's carried sum of X^2
+    (``states[k]["param_sumsq"]``) when ``param_sumsq_valid``."""
+    ws, nb = _ws(workspace)
+    _check(load().meo_adafactor_shard_stats_carry(
+        ctypes.byref(hp), step, len(params), _tensors(params, grads, states), _shards(totals),
+        _states(meo_adafactor_state, ADAFACTOR_KEYS, states), 1 if param_sumsq_valid else 0, _ptr(partials), ws, nb,
+        _stream(stream)))
+
+
+def meo_adafactor_shard_apply_carry(hp, step, params, grads, totals, states, partials, workspace=None, stream=None):
+    """meo_adafactor_shard_apply that leaves each shard's sum of squares of its
+    updated rows in ``states[k]["param_sumsq"]``."""
+    _shard_call("adafactor", "apply_carry", hp, step, params, grads, totals, states, partials, workspace, stream)
+
+
 def meo_lamb_shard_stats(hp, step, params, grads, totals, states, partials, workspace=None, stream=None):
     _shard_call("lamb", "stats", hp, step, params, grads, totals, states, partials, workspace, stream)
 
@@ -473,19 +498,27 @@ class PreparedShardStep:
     PreparedStep): ``stats(step)`` fills ``partials`` and, after the caller has
     summed them over the ranks, ``apply(step)`` updates the shard. CAME has a call
     between the two: ``moment(step)`` takes the summed ``partials`` and fills
-    ``confidence``, which ``apply(step)`` takes summed over the ranks."""
+    ``confidence``, which ``apply(step)`` takes summed over the ranks.
+    ``carry`` (Adafactor): the carry calls; the first ``stats`` reads the shard's
+    parameter, later ones take its carried sum of X^2 until ``invalidate()``."""
 
     _KIND = {"adafactor": (meo_adafactor_state, ADAFACTOR_KEYS), "lamb": (meo_lamb_state, LAMB_KEYS),
              "came": (meo_came_state, CAME_KEYS)}
 
     def __init__(self, optimizer: str, hp, params, grads, totals, states, partials, workspace=None,
-                 confidence=None):
+                 confidence=None, carry: bool = False):
         cls, keys = self._KIND[optimizer]
         lib = load()
         self.came = optimizer == "came"
         if self.came and confidence is None:
             raise ValueError("CAME's row-sharded step needs the confidence buffer")
-        self._fns = (getattr(lib, f"meo_{optimizer}_shard_stats"), getattr(lib, f"meo_{optimizer}_shard_apply"),
+        if carry and optimizer != "adafactor":
+            raise ValueError("only Adafactor carries sum(X^2)")
+        self.carry = carry
+        self.valid = False
+        sfx = "_carry" if carry else ""
+        self._fns = (getattr(lib, f"meo_{optimizer}_shard_stats{sfx}"),
+                     getattr(lib, f"meo_{optimizer}_shard_apply{sfx}"),
                      lib.meo_came_shard_moment if self.came else None)
         self.hp = hp
         self.n = len(params)
@@ -501,7 +534,13 @@ class PreparedShardStep:
         _check(fn(ctypes.byref(self.hp), step, self.n, self.tensors, self.shards, self.states, *bufs,
                   self.ws, self.ws_bytes, _stream(stream)))
 
+    def invalidate(self) -> None:
+        self.valid = False
+
     def stats(self, step: int, stream=None) -> None:
+        if self.carry:
+            self._call(self._fns[0], step, stream, 1 if self.valid else 0, self.partials)
+            return
         self._call(self._fns[0], step, stream, self.partials)
 
     def moment(self, step: int, stream=None) -> None:
@@ -511,6 +550,7 @@ class PreparedShardStep:
 
     def apply(self, step: int, stream=None) -> None:
         self._call(self._fns[1], step, stream, self.confidence if self.came else self.partials)
+        self.valid = self.carry
 
 
 def meo_last_error() -> str:

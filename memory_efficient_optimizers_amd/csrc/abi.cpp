@@ -796,6 +796,19 @@ int meo_adafactor_validate(const meo_adafactor_hparams* hp, int64_t step, int32_
 
 namespace {
 
+// Every tensor with elements has a 4-byte aligned param_sumsq (the carry calls).
+int check_param_sumsq(int32_t n, const meo_tensor* ts, const meo_adafactor_state* st) {
+    for (int32_t k = 0; k < n; ++k) {
+        int64_t numel = 0;
+        overflow_numel(ts[k], &numel);
+        if (numel == 0) continue;
+        if (!st[k].param_sumsq) return fail(MEO_ENULL, "tensor " + std::to_string(k) + ": param_sumsq is NULL");
+        if (reinterpret_cast<uintptr_t>(st[k].param_sumsq) % 4)
+            return fail(MEO_EALIGN, "tensor " + std::to_string(k) + ": param_sumsq misaligned");
+    }
+    return MEO_OK;
+}
+
 // carry: -1 plain step; 0 or 1 a step that leaves the updated parameter's sum of
 // squares in each tensor's param_sumsq (1: and takes RMS(X) from it).
 int adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
@@ -805,15 +818,10 @@ int adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n, con
     // RMS(X) is needed only to scale the step (scale_parameter); without it the
     // carried sum is neither read nor written.
     if (!hp->scale_parameter) carry = -1;
-    if (carry >= 0)
-        for (int32_t k = 0; k < n; ++k) {
-            int64_t numel = 0;
-            overflow_numel(ts[k], &numel);
-            if (numel == 0) continue;
-            if (!st[k].param_sumsq) return fail(MEO_ENULL, "tensor " + std::to_string(k) + ": param_sumsq is NULL");
-            if (reinterpret_cast<uintptr_t>(st[k].param_sumsq) % 4)
-                return fail(MEO_EALIGN, "tensor " + std::to_string(k) + ": param_sumsq misaligned");
-        }
+    if (carry >= 0) {
+        rc = check_param_sumsq(n, ts, st);
+        if (rc) return rc;
+    }
     if (n == 0) return MEO_OK;
     rc = check_workspace(kOpAdafactor, n, ts, ws, ws_bytes);
     if (rc) return rc;
@@ -1095,9 +1103,13 @@ struct AfShard {
 
 int af_shard_prepare(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
                      const meo_shard* sh, const meo_adafactor_state* st, const void* partials, void* ws,
-                     size_t ws_bytes, AfShard* out) {
+                     size_t ws_bytes, AfShard* out, bool carry = false) {
     int rc = meo_adafactor_validate(hp, step, n, ts, st);
     if (rc) return rc;
+    if (carry && hp->scale_parameter) {
+        rc = check_param_sumsq(n, ts, st);
+        if (rc) return rc;
+    }
     if (n == 0) return MEO_OK;
     rc = check_shards(kOpAdafactor, n, ts, sh, partials);
     if (rc) return rc;
@@ -1149,11 +1161,13 @@ size_t meo_lamb_partials_size(int32_t n, const meo_tensor* ts) {
     return static_cast<size_t>(partials_layout(kOpLamb, n, ts, nullptr));
 }
 
-int meo_adafactor_shard_stats(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
-                              const meo_shard* sh, const meo_adafactor_state* st, float* partials, void* ws,
-                              size_t ws_bytes, void* stream) {
+// carry: -1 plain; 0 or 1 as for the whole-tensor carry call (1: the record's sum
+// of X^2 is the shard's carried value and X is not read).
+static int af_shard_stats(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                   const meo_shard* sh, const meo_adafactor_state* st, float* partials, int carry, void* ws,
+                   size_t ws_bytes, void* stream) {
     AfShard a;
-    int rc = af_shard_prepare(hp, step, n, ts, sh, st, partials, ws, ws_bytes, &a);
+    int rc = af_shard_prepare(hp, step, n, ts, sh, st, partials, ws, ws_bytes, &a, carry >= 0);
     if (rc || n == 0) return rc;
     Plan* p = a.p;
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1161,7 +1175,8 @@ int meo_adafactor_shard_stats(const meo_adafactor_hparams* hp, int64_t step, int
     if (p->n == 0) return launch_status("adafactor shard statistics launch");
     float* w = static_cast<float*>(ws);
     auto tab = [&](int l) { return Table{p->desc, p->items[l], w}; };
-    const int32_t need_x = hp->scale_parameter ? 1 : 0;
+    const int32_t carried = hp->scale_parameter && carry == 1 ? 1 : 0;
+    const int32_t need_x = hp->scale_parameter && !carried ? 1 : 0;
     const StatsArgs sa{static_cast<float>(hp->eps1), static_cast<float>(a.b2), static_cast<float>(1.0 - a.b2), need_x,
                        a.b2, 1.0 - a.b2};
     PassTimer pt(s);
@@ -1177,16 +1192,30 @@ int meo_adafactor_shard_stats(const meo_adafactor_hparams* hp, int64_t step, int
         launch_rowstats(1, tab(kListRc1), p->count[kListRc1], sa, s);
         pt.mark(kPassStatsWide);
     }
-    launch_shard_partials(tab(kListShard), p->count[kListShard], partials, need_x, s);
+    launch_shard_partials(tab(kListShard), p->count[kListShard], partials, need_x, carried, s);
     pt.mark(kPassFinalize);
     return launch_status("adafactor shard statistics launch");
 }
 
-int meo_adafactor_shard_apply(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
-                              const meo_shard* sh, const meo_adafactor_state* st, const float* partials, void* ws,
+int meo_adafactor_shard_stats(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                              const meo_shard* sh, const meo_adafactor_state* st, float* partials, void* ws,
                               size_t ws_bytes, void* stream) {
+    return af_shard_stats(hp, step, n, ts, sh, st, partials, -1, ws, ws_bytes, stream);
+}
+
+int meo_adafactor_shard_stats_carry(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                                    const meo_shard* sh, const meo_adafactor_state* st, int32_t param_sumsq_valid,
+                                    float* partials, void* ws, size_t ws_bytes, void* stream) {
+    return af_shard_stats(hp, step, n, ts, sh, st, partials, param_sumsq_valid ? 1 : 0, ws, ws_bytes, stream);
+}
+
+// carry: also leave the shard's sum of squares of its updated rows in param_sumsq.
+static int af_shard_apply(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                   const meo_shard* sh, const meo_adafactor_state* st, const float* partials, bool carry, void* ws,
+                   size_t ws_bytes, void* stream) {
     AfShard a;
-    int rc = af_shard_prepare(hp, step, n, ts, sh, st, partials, ws, ws_bytes, &a);
+    int rc = af_shard_prepare(hp, step, n, ts, sh, st, partials, ws, ws_bytes, &a, carry);
+    carry = carry && hp->scale_parameter;
     if (rc || n == 0 || a.p->n == 0) return rc;
     Plan* p = a.p;
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1200,9 +1229,25 @@ int meo_adafactor_shard_apply(const meo_adafactor_hparams* hp, int64_t step, int
     pt.mark(kPassScalars);
     launch_af_apply(tab(kListAll), p->count[kListAll],
                     AfApplyArgs{static_cast<float>(hp->beta1), static_cast<float>(1.0 - hp->beta1), hp->has_beta1},
-                    p->storage, false, s);
+                    p->storage, carry, s);
     pt.mark(kPassAfApply);
+    if (carry) {
+        launch_sumsq_fold(p->desc, w, p->n, s);
+        pt.mark(kPassSumsqFold);
+    }
     return launch_status("adafactor shard apply launch");
+}
+
+int meo_adafactor_shard_apply(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                              const meo_shard* sh, const meo_adafactor_state* st, const float* partials, void* ws,
+                              size_t ws_bytes, void* stream) {
+    return af_shard_apply(hp, step, n, ts, sh, st, partials, false, ws, ws_bytes, stream);
+}
+
+int meo_adafactor_shard_apply_carry(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                                    const meo_shard* sh, const meo_adafactor_state* st, const float* partials,
+                                    void* ws, size_t ws_bytes, void* stream) {
+    return af_shard_apply(hp, step, n, ts, sh, st, partials, true, ws, ws_bytes, stream);
 }
 
 int meo_lamb_shard_stats(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
@@ -1218,7 +1263,7 @@ int meo_lamb_shard_stats(const meo_lamb_hparams* hp, int64_t step, int32_t n, co
     PassTimer pt(s);
     launch_lamb_moments(Table{p->desc, p->items[kListAll], w}, p->count[kListAll], lamb_args(hp, step), p->storage, s);
     pt.mark(kPassLambMoments);
-    launch_shard_partials(Table{p->desc, p->items[kListShard], w}, p->count[kListShard], partials, 0, s);
+    launch_shard_partials(Table{p->desc, p->items[kListShard], w}, p->count[kListShard], partials, 0, 0, s);
     pt.mark(kPassFinalize);
     return launch_status("lamb shard statistics launch");
 }
@@ -1296,7 +1341,7 @@ int meo_came_shard_stats(const meo_came_hparams* hp, int64_t step, int32_t n, co
         launch_rowstats(1, tab(kListRc1), p->count[kListRc1], sa, s);
         pt.mark(kPassStatsWide);
     }
-    launch_shard_partials(tab(kListShard), p->count[kListShard], partials, 0, s);
+    launch_shard_partials(tab(kListShard), p->count[kListShard], partials, 0, 0, s);
     pt.mark(kPassFinalize);
     return launch_status("came shard statistics launch");
 }

@@ -554,7 +554,9 @@ void launch_lamb_moments(const Table& t, int64_t n, const LambArgs& a, int stora
 void launch_lamb_apply(const Table& t, int64_t n, const LambArgs& a, int storage, hipStream_t s);
 // Row-sharded steps: the shard's partial sums, and their fold (after the caller's
 // all-reduce) into the replicated column statistic.
-void launch_shard_partials(const Table& t, int64_t n, float* partials, int32_t need_x, hipStream_t s);
+// carried (Adafactor): the sum of X^2 comes from each tensor's carried value.
+void launch_shard_partials(const Table& t, int64_t n, float* partials, int32_t need_x, int32_t carried,
+                           hipStream_t s);
 void launch_shard_fold(const Table& t, int64_t n, const float* partials, double beta, hipStream_t s);
 // Zero-fills records (x = first float, y = length) of tensors a rank holds none of.
 void launch_zero_records(const int2* items, int64_t n, float* partials, hipStream_t s);

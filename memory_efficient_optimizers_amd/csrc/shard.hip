@@ -13,8 +13,11 @@
 namespace meo {
 
 // Items: a factored tensor's matrix b and 256-column chunk (b * chunks + chunk); a
-// flat tensor, item 0. Writes the tensor's record (layout in meo.h).
-__global__ __launch_bounds__(kThreads) void k_shard_partials(Table t, float* partials, int32_t need_x) {
+// flat tensor, item 0. Writes the tensor's record (layout in meo.h). `carried`
+// (Adafactor): the record's sum of X^2 is the shard's carried value (TDesc::xsq),
+// which the previous step's apply pass formed from the rows it stored.
+__global__ __launch_bounds__(kThreads) void k_shard_partials(Table t, float* partials, int32_t need_x,
+                                                             int32_t carried) {
     __shared__ double lds[kWaves];
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
@@ -33,6 +36,7 @@ __global__ __launch_bounds__(kThreads) void k_shard_partials(Table t, float* par
         s0 = block_sum_d(s0, lds);
         __syncthreads();
         s1 = block_sum_d(s1, lds);
+        if (carried && d.xsq) s1 = static_cast<double>(ldf(d.xsq));
         if (tid == 0) {
             stf(out, static_cast<float>(s0));
             stf(out + 1, static_cast<float>(s1));
@@ -65,14 +69,16 @@ __global__ __launch_bounds__(kThreads) void k_shard_partials(Table t, float* par
             if (need_x)  // the sum(X^2) chunks ran only then
                 for (int j = tid; j < d.xchunks; j += kThreads) x += static_cast<double>(ldf(ws + d.xpart + j));
             x = block_sum_d(x, lds);
+            if (carried && d.xsq) x = static_cast<double>(ldf(d.xsq));
             if (tid == 0) stf(out + 2 * BW + d.B, static_cast<float>(x));
         }
     }
 }
 
-void launch_shard_partials(const Table& t, int64_t n, float* partials, int32_t need_x, hipStream_t s) {
+void launch_shard_partials(const Table& t, int64_t n, float* partials, int32_t need_x, int32_t carried,
+                           hipStream_t s) {
     if (n > 0) hipLaunchKernelGGL(k_shard_partials, dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, s, t, partials,
-                                  need_x);
+                                  need_x, carried);
 }
 
 // Items: a factored tensor's matrix b and 256-column chunk. From the totals: C_j <-

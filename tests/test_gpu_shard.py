@@ -59,10 +59,17 @@ def _ranges(opt, shape, nranks):
     ("adafactor", {"beta1": 0.9, "weight_decay": 0.1}),
     ("adafactor", {}),
     ("adafactor", {"scale_parameter": False, "beta1": 0.5, "clip_threshold": 0.3}),
+    ("adafactor-carry", {"beta1": 0.9, "weight_decay": 0.1}),
+    ("adafactor-carry", {"warmup_init": True}),
     ("lamb", {"weight_decay": 0.01}),
     ("came", {"lr": 2e-4, "weight_decay": 0.05}),
 ])
 def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
+    """"adafactor-carry": the carry calls, each rank carrying the sum of X^2 of its
+    own shard from the second step on; the ranks' sums add up to the whole
+    parameter's."""
+    carry = opt == "adafactor-carry"
+    opt = "adafactor" if carry else opt
     wl = workloads.custom(f"shard_{opt}", opt, SHAPES, hparams=hp, grad_dtype=torch.bfloat16,
                           grad_scaling="rowcol" if opt != "lamb" else "row")
     full = workloads.init_params(wl, "cuda")
@@ -80,12 +87,18 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
             for key in ("exp_avg_sq_col", "exp_avg_res_col"):  # column statistics are kept whole on every rank
                 if key in st:
                     st[key] = torch.zeros(full[k].shape[:-2] + full[k].shape[-1:], device="cuda")
+            if carry:
+                st["param_sumsq"] = torch.zeros(1, device="cuda")
             sts.append(st)
         ranks.append({"params": ps, "states": sts})
     size = getattr(_lib, f"meo_{opt}_partials_size")(ranks[0]["params"], ranks[0]["params"])
     csize = _lib.meo_came_confidence_size(ranks[0]["params"], ranks[0]["params"]) if opt == "came" else 0
     stats = getattr(_lib, f"meo_{opt}_shard_stats")
     apply = getattr(_lib, f"meo_{opt}_shard_apply")
+    if carry:
+        def stats(hps, t, ps, gs, totals, sts, part, ws):
+            _lib.meo_adafactor_shard_stats_carry(hps, t, ps, gs, totals, sts, t > 1, part, ws)
+        apply = _lib.meo_adafactor_shard_apply_carry
     ox = [to64(p) for p in full]
     ost = [oracle.INIT_STATE[opt](tuple(p.shape), hp) for p in full]
     for t in range(1, 4):
@@ -136,9 +149,14 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
                 else:
                     errs[key] = output_err(key, to64(whole(key)), ost[k][key])
             worst = max(errs, key=errs.get)
-            print(f"  {opt} N={nranks} step {t} {spec.name} {tuple(spec.shape)}: worst {errs[worst]:.3e} ({worst})",
-                  flush=True)
+            print(f"  {opt}{' carry' if carry else ''} N={nranks} step {t} {spec.name} {tuple(spec.shape)}: "
+                  f"worst {errs[worst]:.3e} ({worst})", flush=True)
             assert errs[worst] <= TOL_F32, (t, spec.shape, worst, errs[worst])
+            if carry:  # the ranks' carried sums add up to the whole parameter's sum of squares
+                got = sum(float(rk["states"][k]["param_sumsq"].item())
+                          for rk, (r0, r1) in zip(ranks, ranges[k][0]) if r1 > r0)
+                want = float(np.sum(np.square(ox[k])))
+                assert abs(got - want) <= 1e-5 * want, (t, spec.shape, got, want)
 
 
 def test_came_confidence_record_layout():
@@ -197,3 +215,33 @@ def test_prepared_came_shard_of_the_whole_is_the_whole_step():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert output_err("param", to64(y), to64(x)) <= TOL_F32
+
+
+def test_prepared_adafactor_shard_carry_of_the_whole_is_the_whole_step():
+    """The prepared carry calls on one rank holding everything give the whole-list
+    carry step's parameters and carried sums within the fp32 bar."""
+    wl = workloads.custom("shard1a", "adafactor", [(129, 1024), (300,), (2, 3, 72, 136)], hparams={"beta1": 0.9},
+                          grad_dtype=torch.bfloat16)
+    a = workloads.init_params(wl, "cuda")
+    b = [p.clone() for p in a]
+    scales = workloads.grad_scales(wl, "cuda")
+    hps = _lib.adafactor_hparams(beta1=0.9)
+    sa = [_lib.init_state("adafactor", p, beta1=True) for p in a]
+    sb = [_lib.init_state("adafactor", p, beta1=True) for p in b]
+    for st in sa + sb:
+        st["param_sumsq"] = torch.zeros(1, device="cuda")
+    totals = [129, 300, 72]
+    part = torch.zeros(_lib.meo_adafactor_partials_size(a, a), device="cuda")
+    gs = workloads.grads(wl, 0, scales, "cuda")
+    ws = _lib.workspace(_lib.meo_adafactor_workspace_size(a, gs), "cuda")
+    call = _lib.PreparedShardStep("adafactor", hps, b, gs, totals, sb, part, ws, carry=True)
+    for t in range(1, 5):
+        for g, n in zip(gs, workloads.grads(wl, t - 1, scales, "cuda")):
+            g.copy_(n)
+        _lib.meo_adafactor_step_carry(hps, t, a, gs, sa, t > 1, ws)
+        call.stats(t)
+        call.apply(t)
+    torch.cuda.synchronize()
+    for x, y, s1, s2 in zip(a, b, sa, sb):
+        assert output_err("param", to64(y), to64(x)) <= TOL_F32
+        assert abs(s2["param_sumsq"].item() - s1["param_sumsq"].item()) <= 1e-5 * s1["param_sumsq"].item()
