@@ -384,3 +384,30 @@ def test_binding_rejects_strided_states(lib):
     s["exp_avg_sq"] = torch.zeros(4, 6).T
     with pytest.raises(ValueError):
         _lib._states(_lib.meo_lamb_state, _lib.LAMB_KEYS, [s])
+
+
+def test_carry_calls_check_param_sumsq_first(lib):
+    """The carry entry points refuse a tensor with elements but no param_sumsq
+    (when scale_parameter needs RMS(X)) before touching anything else; an empty
+    tensor needs none, and without scale_parameter none is needed at all (the
+    call then fails on its missing workspace, the next check)."""
+    ps, gs = _mk([(4, 8), (8,), (0, 5)])
+    st = _af_states(ps)
+    for s in st:
+        s["param_sumsq"] = torch.zeros(1)
+    hp = _lib.adafactor_hparams()
+    miss = [dict(s) for s in st]
+    del miss[1]["param_sumsq"]
+    code, msg = _code(_lib.meo_adafactor_step_carry, hp, 1, ps, gs, miss, True, None, 0)
+    assert code == _lib.MEO_ENULL and msg == "tensor 1: param_sumsq is NULL"
+    code, msg = _code(_lib.meo_adafactor_shard_stats_carry, hp, 1, ps, gs, [4, 8, 0], miss, True, None, None, 0)
+    assert code == _lib.MEO_ENULL and msg == "tensor 1: param_sumsq is NULL"
+    code, msg = _code(_lib.meo_adafactor_shard_apply_carry, hp, 1, ps, gs, [4, 8, 0], miss, None, None, 0)
+    assert code == _lib.MEO_ENULL and msg == "tensor 1: param_sumsq is NULL"
+    empty_ok = [dict(s) for s in st]
+    del empty_ok[2]["param_sumsq"]
+    assert _code(_lib.meo_adafactor_step_carry, hp, 1, ps, gs, empty_ok, False, None, 0)[0] == _lib.MEO_EWORKSPACE
+    no_scale = _lib.adafactor_hparams(scale_parameter=False)
+    assert _code(_lib.meo_adafactor_step_carry, no_scale, 1, ps, gs, miss, True, None, 0)[0] == _lib.MEO_EWORKSPACE
+    # the plain step ignores param_sumsq
+    assert _code(_lib.meo_adafactor_step, hp, 1, ps, gs, miss, None, 0)[0] == _lib.MEO_EWORKSPACE
