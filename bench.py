@@ -11,7 +11,9 @@ hipEvents on the stream (synchronised on both sides). One JSON line on stdout:
 
 * ``value``: optimizer-step throughput in parameters per second (whole job).
 * ``hbm``: the step's compulsory bytes (read G once, read and write the parameter
-  and every full-size state once) over the step time, against 8 TB/s.
+  and every full-size state once) over the step time, against 8 TB/s; beside it
+  (``measured_*``) the bytes the step's kernels move by the committed rocprofv3
+  counter record of the whole step (Adafactor workloads), over the same time.
 * ``roofline``: the dominant pass (the apply pass for Adafactor), its algorithmic
   bytes per launch over its average duration, timed with hipEvents that the
   library records between its passes on the same stream during the timed steps.
@@ -136,6 +138,36 @@ def profile_traffic(kernel: str, workload: str):
         with open(os.path.join(here, src), "rb") as f:
             h.update(f.read())
     return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
+def step_traffic(workload: str, passes: dict, steps: int, carry: bool):
+    """HBM bytes per step from the committed whole-step counter record (per-launch
+    bytes of every kernel of the step, rocprofv3 FETCH_SIZE / WRITE_SIZE), weighted
+    by the launches the timed steps made; None without a record, or when the
+    kernels' sources changed since it was taken, or when a timed pass has no entry."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"adafactor_step_{workload.split('_', 1)[1]}_traffic.json")
+    if not workload.startswith("adafactor_") or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("workload") != workload:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(here, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    per = rec["bytes_per_launch"]
+    total = 0.0
+    for name, v in passes.items():
+        key = "adafactor_apply_carry" if (name == "adafactor_apply" and carry) else name
+        if key not in per:
+            return None
+        total += per[key] * v["launches"]
+    return total / steps
 
 
 def flat_views(torch, shapes, dtype, device):
@@ -557,6 +589,9 @@ def main() -> int:
         read = {"ms_per_step": r_total / args.steps, "value": numel / (r_total / args.steps / 1e3),
                 "step_ms": {"min": min(r_ms), "median": sorted(r_ms)[len(r_ms) // 2], "max": max(r_ms)},
                 "passes_ms_per_step": {k: v["ms"] / args.steps for k, v in r_passes.items()}}
+        r_meas = step_traffic(wl.name, r_passes, args.steps, False)
+        read["measured_step_bytes"] = r_meas
+        read["measured_frac"] = None if r_meas is None else r_meas / (read["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBPS
 
     ab = algorithmic_bytes(wl)
     step_gbps = ab["step"] / (ms_step / 1e3) / 1e9
@@ -564,6 +599,7 @@ def main() -> int:
     avg_ms = passes[dominant]["ms"] / passes[dominant]["launches"]
     achieved = ab[dominant] / (avg_ms / 1e3) / 1e9
     traffic = profile_traffic(dominant, wl.name)
+    measured = step_traffic(wl.name, passes, args.steps, carry)
 
     metric = "optimizer-step params/s + achieved HBM GB/s (% peak), " + (
         "7B-shaped Adafactor" if wl.name == "adafactor_llama7b" else wl.name)
@@ -588,7 +624,10 @@ def main() -> int:
                    "param_sumsq": "carry" if carry else "read",
                    "hparams": {k: (list(v) if isinstance(v, tuple) else v) for k, v in hp.items()}},
         "hbm": {"step_bytes": ab["step"], "achieved": step_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": step_gbps / HBM_PEAK_GBPS},
+                "frac": step_gbps / HBM_PEAK_GBPS,
+                "measured_step_bytes": measured,
+                "measured_achieved": None if measured is None else measured / (ms_step / 1e3) / 1e9,
+                "measured_frac": None if measured is None else measured / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBPS},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "bytes_per_launch": ab[dominant], "avg_ms": avg_ms},
