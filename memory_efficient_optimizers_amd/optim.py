@@ -185,6 +185,10 @@ class Adafactor(_MeoOptimizer):
         hp = _lib.adafactor_hparams(**{k: group[k] for k in self._HP})
         if not (self._carry and group["scale_parameter"]):
             _lib.meo_adafactor_step(hp, step, params, grads, states, ws)
+            # the library's writes do not bump the version counter: a plain step
+            # leaves any carried sum of these parameters stale
+            for p in params:
+                self._carried.pop(id(p), None)
             return
         for p, st in zip(params, states):
             if "param_sumsq" not in st:  # e.g. state loaded from a run without the carry

@@ -236,3 +236,30 @@ def test_carry_full_llama7b_sampled():
             assert not bad, (t, names[k], bad)
             assert abs(got - want) / want <= SUMSQ_ORACLE
         del gs
+
+
+def test_front_end_plain_steps_in_between_drop_the_carry():
+    """A group switched to scale_parameter=False for a step (the plain step, whose
+    writes do not bump version counters) and back: the next carry step reads X
+    again, so it equals the plain step on the same parameters and state."""
+    from memory_efficient_optimizers_amd import Adafactor
+    hp = {"beta1": 0.9}
+    wl = workloads.custom("carry_toggle", "adafactor", [(96, 520), (520,)], hparams=hp)
+    scales = workloads.grad_scales(wl, "cuda")
+    ps = [torch.nn.Parameter(p.clone()) for p in workloads.init_params(wl, "cuda")]
+    o = Adafactor(ps, carry_param_sumsq=True, **hp)
+    for t in range(4):
+        gs = workloads.grads(wl, t, scales, "cuda")
+        for p, g in zip(ps, gs):
+            p.grad = g
+        o.param_groups[0]["scale_parameter"] = t != 2
+        if t == 3:
+            x_before = [p.detach().clone() for p in ps]
+            st_before = [{k: v.clone() for k, v in o.state[p].items() if k != "step"} for p in ps]
+        o.step()
+    torch.cuda.synchronize()
+    want = [x.clone() for x in x_before]
+    lib_step("adafactor", lib_hp("adafactor", hp), 4, want, gs, st_before, lib_workspace("adafactor", want, gs))
+    torch.cuda.synchronize()
+    for p, q in zip(ps, want):
+        assert torch.equal(p.detach(), q)
