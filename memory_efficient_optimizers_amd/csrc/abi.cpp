@@ -68,7 +68,7 @@ bool overflow_numel(const meo_tensor& t, int64_t* numel) {
 // alignment of param and grad (which decides the statistics mode), not on states.
 struct Geo {
     int64_t numel = 0;
-    int32_t mode = kFlat, cls = 0, B = 1, H = 1, W = 1, tr = 1, tc = 0, strips = 0, nrc = 0, ncc = 0;
+    int32_t mode = kFlat, cls = 0, B = 1, H = 1, W = 1, tr = 1, tc = 0, strips = 0, srows = 0, nrc = 0, ncc = 0;
     int64_t tiles = 0;  // 2-D tiles (factored) or flat tiles
     int32_t xchunks = 0;
     int64_t rowpart = 0, colpart = 0, sumr = 0, tilepart = 0, xpart = 0, apart = 0, bscal = 0, scal = 0;
@@ -95,7 +95,8 @@ int64_t layout(int op, int32_t n, const meo_tensor* ts, std::vector<Geo>* out) {
                 g.cls = g.W <= kRcMaxCols0 ? 0 : 1;
                 g.tr = static_cast<int32_t>(ceil_div(g.H, kTileRows));
                 g.tc = static_cast<int32_t>(ceil_div(g.W, kTileCols));
-                g.strips = static_cast<int32_t>(ceil_div(g.H, kStripRows));
+                g.srows = op == kOpAdafactor ? kStripRowsAdafactor : kStripRowsCame;
+                g.strips = static_cast<int32_t>(ceil_div(g.H, g.srows));
                 g.tiles = static_cast<int64_t>(g.B) * g.tr * g.tc;
                 g.nrc = static_cast<int32_t>(ceil_div(g.H, kFinChunk));
                 g.ncc = static_cast<int32_t>(ceil_div(g.W, kFinCols));
@@ -542,7 +543,7 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
         if (g.mode != kFlat) vec = vec && (g.W % kVec == 0);
         else vec = vec && (!d.v || aligned16(d.v));
         d.vec = vec;
-        d.tr = g.tr; d.tc = g.tc; d.strips = g.strips;
+        d.tr = g.tr; d.tc = g.tc; d.strips = g.strips; d.srows = g.srows;
         d.nrc = g.nrc; d.ncc = g.ncc;
         if (shards) {
             d.part = poff[k];

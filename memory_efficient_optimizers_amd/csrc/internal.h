@@ -7,7 +7,7 @@
 //     bf16 or two 16-byte fp32 accesses per row), each wave kRowsPerWave rows.
 //   * The first (statistics) pass of a factored tensor whose rows fit a block
 //     ("row-complete" tensors: 16-byte aligned, W % 8 == 0, W <= 12288) uses
-//     strips of kStripRows full rows: the block sees whole rows, so it finishes
+//     strips of full rows (TDesc::srows of them): the block sees whole rows, so it finishes
 //     the row statistic itself and can weight the column sums by it. Other
 //     factored tensors use the 2-D tiles for their statistics too (and then need a
 //     second read of G for the RMS of the update).
@@ -37,7 +37,12 @@ constexpr int kFlatTile = kThreads * kVec * kFlatIters;  // 32768
 constexpr int kFinChunk = 256;                   // rows per finalize block
 constexpr int kFinCols = 64;                     // columns per finalize block
 constexpr int kScalSlots = 8;                    // floats of per-tensor scalars
-constexpr int kStripRows = 64;                   // rows per strip of the row-complete pass
+// Rows per strip of the row-complete pass (TDesc::srows): 128 for Adafactor (half
+// the column partials of 64-row strips; measured 1.6-2.5% faster steps on the 7B
+// list), 64 for CAME.
+constexpr int kStripRowsMax = 128;
+constexpr int kStripRowsAdafactor = 128;
+constexpr int kStripRowsCame = 64;
 // Widest row of each row-complete class (class 0: 256 threads x 2 groups of 8
 // columns; class 1: 512 threads x 3 groups).
 constexpr int kRcMaxCols0 = 256 * 8 * 2;  // 4096
@@ -93,6 +98,7 @@ struct TDesc {
     int32_t vec;      // 16-byte vector accesses are valid
     int32_t tr, tc;   // 2-D tiles per matrix along rows / columns (flat: tr = 1, tc = tiles)
     int32_t strips;   // row-complete strips per matrix
+    int32_t srows;    // rows per row-complete strip
     int32_t nrc, ncc; // finalize chunks per matrix along rows / columns
     int32_t xchunks;  // row-complete: chunks of the parameter for sum(X^2)
     // Row-sharded steps: where the tensor's record starts in the partial-sum buffer

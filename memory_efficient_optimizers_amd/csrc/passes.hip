@@ -236,11 +236,11 @@ __device__ __forceinline__ void strip_batch(const TDesc& d, const StatsArgs& a, 
     }
 }
 
-// One strip of up to kStripRows full rows of matrix b (the sum of X^2 is taken by
+// One strip of up to d.srows full rows of matrix b (the sum of X^2 is taken by
 // k_xnorm). Thread t owns the 8-column groups t,
 // t + NTHR, ..., t + (KMAX-1) NTHR; rows go in batches of RB, two register buffers
 // alternating so that a batch's loads are in flight during the previous one's
-// reduction. `red` holds 2 * NW * RB floats, `rold` kStripRows.
+// reduction. `red` holds 2 * NW * RB floats, `rold` kStripRowsMax.
 template <int NTHR, int KMAX, int RB, bool BF16>
 __device__ void rowstats_strip(const TDesc& d, int lt, float* __restrict__ ws, const StatsArgs& a, float* red,
                                float* rold, float* bsum) {
@@ -249,8 +249,8 @@ __device__ void rowstats_strip(const TDesc& d, int lt, float* __restrict__ ws, c
     const int b = lt / d.strips;
     const int st = lt - b * d.strips;
     StripCtx c;
-    c.row_begin = st * kStripRows;
-    c.row_end = min(c.row_begin + kStripRows, d.H);
+    c.row_begin = st * d.srows;
+    c.row_end = min(c.row_begin + d.srows, d.H);
     c.W = d.W;
     c.ngroups = d.W / kVec;
     c.mat = static_cast<int64_t>(b) * d.H * d.W;
@@ -290,7 +290,7 @@ __device__ void rowstats_strip(const TDesc& d, int lt, float* __restrict__ ws, c
 constexpr int kRb0 = 4, kRb1 = 2;
 
 __global__ __launch_bounds__(256) void k_rowstats0(Table t, StatsArgs a) {
-    __shared__ float red[2 * kWaves * kRb0], rold[kStripRows], bsum[2 * kWaves];
+    __shared__ float red[2 * kWaves * kRb0], rold[kStripRowsMax], bsum[2 * kWaves];
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     if (d.mode == kFlat) stats_flat<256>(d, it.y, t.ws, a, bsum);
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) void k_rowstats0(Table t, StatsArgs a) {
 }
 
 __global__ __launch_bounds__(512) void k_rowstats1(Table t, StatsArgs a) {
-    __shared__ float red[2 * 8 * kRb1], rold[kStripRows], bsum[2 * 8];
+    __shared__ float red[2 * 8 * kRb1], rold[kStripRowsMax], bsum[2 * 8];
     const int2 it = t.items[blockIdx.x];
     const TDesc d = t.desc[it.x];
     if (d.gbf16) rowstats_strip<512, 3, kRb1, true>(d, it.y, t.ws, a, red, rold, bsum);
