@@ -209,10 +209,11 @@ def _sampled_full(wl, sample_idx, steps):
         del gs
 
 
-@pytest.mark.parametrize("name", ["adafactor_llama7b", "adafactor_llama7b_bf16", "adafactor_llama7b_i8"])
+@pytest.mark.parametrize("name", ["adafactor_llama7b", "adafactor_llama7b_bf16", "adafactor_llama7b_i8",
+                                  "came_llama7b", "lamb_llama7b"])
 def test_full_llama7b_sampled(name):
-    """The 7B list (291 tensors, 6.74e9 parameters) in one call per step, with fp32
-    and with bf16 parameter and first-moment storage. Step 1: the embedding, the
+    """The 7B list (291 tensors, 6.74e9 parameters) in one call per step: Adafactor
+    with fp32, bf16 and 8-bit storage, CAME and LAMB. Step 1: the embedding, the
     last gate projection and the final norm checked in full; then three chained
     steps on a q projection and the final norm."""
     wl = workloads.WORKLOADS[name]

@@ -149,6 +149,11 @@ _register(_wl("came_llama_layer", "came", _CAME, llama_layer_specs(),
 _register(_wl("lamb_bert_large", "lamb", _LAMB, bert_specs(),
               torch.float32, 1e-2, "none", 20))
 
+# CAME and LAMB over the same Llama-7B-shaped list as the headline (measurement at
+# that scale; bf16 gradients as in the Adafactor 7B configuration).
+_register(_wl("came_llama7b", "came", _CAME, llama_specs(), torch.bfloat16, 1e-3, "rowcol", 5))
+_register(_wl("lamb_llama7b", "lamb", _LAMB, llama_specs(), torch.bfloat16, 1e-3, "rowcol", 5))
+
 # 16-bit storage: the 7B and one-layer Adafactor configurations with bf16
 # parameters and bf16 first moments.
 _register(dataclasses.replace(WORKLOADS["adafactor_llama7b"], name="adafactor_llama7b_bf16",
