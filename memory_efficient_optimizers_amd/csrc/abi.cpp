@@ -1420,6 +1420,7 @@ struct GaPlan {
     const RDesc* rdesc = nullptr;
     const int2* items[kGaListCount] = {};
     int64_t count[kGaListCount] = {};
+    bool back_direct[2] = {false, false};  // back-projection staged by global_load_lds (right, left)
 };
 std::list<GaPlan*> g_ga_plans;  // most recently used first, under g_mu
 
@@ -1757,6 +1758,13 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
     GaPlan* p = new GaPlan;
     p->key = std::move(key);
     p->device = dev;
+    // Direct staging needs whole contraction blocks and 16-byte rows everywhere.
+    for (int side = 0; side < 2; ++side) {
+        const std::vector<GDesc>& v = side ? left : right;
+        bool ok = true;
+        for (const GDesc& d : v) ok = ok && d.vec && d.r % kGaKb == 0;
+        p->back_direct[side] = ok;
+    }
     if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
         hipMemcpy(p->mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
         if (p->mem) (void)hipFree(p->mem);
@@ -1894,8 +1902,8 @@ int meo_galore_step(const meo_galore_hparams* hp, int64_t step, int32_t n, const
     launch_galore_project(GTable{p->gdesc, p->items[kGaProjR]}, p->count[kGaProjR], a, false, s);
     launch_galore_project(GTable{p->gdesc, p->items[kGaProjL]}, p->count[kGaProjL], a, true, s);
     pt.mark(kPassGaProject);
-    launch_galore_back(GTable{p->gdesc, p->items[kGaBackR]}, p->count[kGaBackR], a, false, s);
-    launch_galore_back(GTable{p->gdesc, p->items[kGaBackL]}, p->count[kGaBackL], a, true, s);
+    launch_galore_back(GTable{p->gdesc, p->items[kGaBackR]}, p->count[kGaBackR], a, false, p->back_direct[0], s);
+    launch_galore_back(GTable{p->gdesc, p->items[kGaBackL]}, p->count[kGaBackL], a, true, p->back_direct[1], s);
     pt.mark(kPassGaBack);
     a.coef = static_cast<float>(hp->lr);
     launch_galore_adamw(Table{p->fdesc, p->items[kGaFlat], nullptr}, p->count[kGaFlat], a, s);

@@ -285,15 +285,47 @@ void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool lef
 constexpr int kBackThreads = kThreads * kGaBackRW;
 constexpr int kBackN = kGaTile * kGaBackRW;  // rows of N per tile
 
-template <bool Left>
-__global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a) {
+// Direct staging: rows of 64 bf16 (128 bytes, unpadded) written straight from
+// global memory into LDS by global_load_lds (no registers), 8 rows per
+// instruction: lane l fills row (l >> 3) of the group at 16-byte slot (l & 7),
+// which holds the row's chunk (l & 7) ^ (row & 7). Reading chunk c of row w at
+// slot c ^ (w & 7) keeps the 8 rows of a fragment read on 8 different slots (no
+// bank conflict), as the padding does for the register path. Rows past the
+// operand's end read its last row: they only reach outputs that are not stored.
+constexpr int kDirectPitch = kGaKb;  // bf16 per LDS row
+template <int ROWS>
+__device__ __forceinline__ void stage_direct(const uint16_t* g, int64_t nrows, int64_t cols, int64_t r0, int k0,
+                                             uint16_t* dst, int wave, int lane) {
+#pragma unroll
+    for (int j = wave; j < ROWS / 8; j += kBackThreads / 64) {
+        const int rr = 8 * j + (lane >> 3);
+        const int64_t row = min(r0 + rr, nrows - 1);
+        const int c = (lane & 7) ^ (rr & 7);
+        const uint16_t* src = g + row * cols + k0 + c * 8;
+        __builtin_amdgcn_global_load_lds((const MEO_GLOBAL void*)src,
+                                         (__attribute__((address_space(3))) void*)(dst + 8 * j * kDirectPitch),
+                                         16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ bfv8 ld_frag_sw(const uint16_t* base, int row, int kk) {
+    return *reinterpret_cast<const bfv8*>(base + row * kDirectPitch + (((kk >> 3) ^ (row & 7)) << 3));
+}
+
+// Direct: operands staged by global_load_lds into an unpadded swizzled arena
+// (48 KB: 3 blocks per CU), for lists whose rank is a multiple of kGaKb; otherwise
+// through registers into a padded arena (55 KB) with the next block's loads in
+// flight during the multiply.
+template <bool Left, bool Direct>
+__global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GTable t, GaArgs a) {
     // one arena: N's planes [kBackN][pitch] twice, then U [256][pitch]; reused by
     // the epilogue exchange (4 kGaBackRW x 8.5 KB)
-    __shared__ __attribute__((aligned(16))) uint16_t arena[(2 * kBackN + kGaWide) * kGaPitch];
-    static_assert((2 * kBackN + kGaWide) * kGaPitch * 2 >= kBackThreads / 64 * kEpWave * 4, "exchange space");
-    uint16_t* sh = arena;                           // N, high plane
-    uint16_t* sl = arena + kBackN * kGaPitch;       // N, low plane
-    uint16_t* su = arena + 2 * kBackN * kGaPitch;   // U rows
+    constexpr int kPitch = Direct ? kDirectPitch : kGaPitch;
+    __shared__ __attribute__((aligned(16))) uint16_t arena[(2 * kBackN + kGaWide) * kPitch];
+    static_assert((2 * kBackN + kGaWide) * kPitch * 2 >= kBackThreads / 64 * kEpWave * 4, "exchange space");
+    uint16_t* sh = arena;                         // N, high plane
+    uint16_t* sl = arena + kBackN * kPitch;       // N, low plane
+    uint16_t* su = arena + 2 * kBackN * kPitch;   // U rows
     const int2 it = t.items[blockIdx.x];
     if (it.x < 0) return;  // an empty item of the XCD-aligned list
     const GDesc d = t.desc[it.x];
@@ -356,9 +388,15 @@ __global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a
             bfv8 fu[2], fh[2], fl[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-                fu[b] = ld_frag(su + (ug * 64 + b * 32 + (lane & 31)) * kGaPitch + kk);
-                fh[b] = ld_frag(sh + (ng * 64 + b * 32 + (lane & 31)) * kGaPitch + kk);
-                fl[b] = ld_frag(sl + (ng * 64 + b * 32 + (lane & 31)) * kGaPitch + kk);
+                if constexpr (Direct) {
+                    fu[b] = ld_frag_sw(su, ug * 64 + b * 32 + (lane & 31), kk);
+                    fh[b] = ld_frag_sw(sh, ng * 64 + b * 32 + (lane & 31), kk);
+                    fl[b] = ld_frag_sw(sl, ng * 64 + b * 32 + (lane & 31), kk);
+                } else {
+                    fu[b] = ld_frag(su + (ug * 64 + b * 32 + (lane & 31)) * kGaPitch + kk);
+                    fh[b] = ld_frag(sh + (ng * 64 + b * 32 + (lane & 31)) * kGaPitch + kk);
+                    fl[b] = ld_frag(sl + (ng * 64 + b * 32 + (lane & 31)) * kGaPitch + kk);
+                }
             }
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib)
@@ -374,11 +412,22 @@ __global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a
                 }
         }
     };
+    const int klast = (d.r - 1) / kGaKb * kGaKb;
+    if constexpr (Direct) {
+        // the rank is a multiple of kGaKb: every contraction block is whole
+        for (int k0 = 0; k0 <= klast; k0 += kGaKb) {
+            stage_direct<kBackN>(d.nh, d.D, d.r, n0, k0, sh, wave, lane);
+            stage_direct<kBackN>(d.nl, d.D, d.r, n0, k0, sl, wave, lane);
+            stage_direct<kGaWide>(d.u, d.d, d.r, u0, k0, su, wave, lane);
+            __syncthreads();  // the loads have landed (each wave waits for its own first)
+            multiply();
+            __syncthreads();
+        }
+    } else {
     fetch(0);
     // All blocks but the last: the next block's loads go out before the multiply.
     // The last one (peeled, so that the parameter registers are live only there
     // and in the epilogue) prefetches the parameter tile instead.
-    const int klast = (d.r - 1) / kGaKb * kGaKb;
     for (int k0 = 0; k0 < klast; k0 += kGaKb) {
         ph.store(sh);
         pl.store(sl);
@@ -395,6 +444,7 @@ __global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a
     prefetch_w();
     multiply();
     __syncthreads();
+    }
     // W <- decay W - coef C, rows of 8 columns per lane (see ep_spill), 16 bytes at
     // a time where rows allow.
     float* lw = reinterpret_cast<float*>(arena) + wave * kEpWave;
@@ -413,7 +463,8 @@ __global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a
             if (d.xbf16) {
                 uint16_t* xp = static_cast<uint16_t*>(d.x) + idx;
                 if (full) {
-                    bf16x8(wpre[ib][q][0], w);
+                    if constexpr (Direct) bf16x8(*gld<u32x4>(xp), w);
+                    else bf16x8(wpre[ib][q][0], w);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
@@ -431,7 +482,8 @@ __global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a
             } else {
                 float* xp = static_cast<float*>(d.x) + idx;
                 if (full) {
-                    const u32x4 x0 = wpre[ib][q][0], x1 = wpre[ib][q][1];
+                    const u32x4 x0 = Direct ? *gld<u32x4>(xp) : wpre[ib][q][0];
+                    const u32x4 x1 = Direct ? *gld<u32x4>(xp + 4) : wpre[ib][q][1];
                     w[0] = __uint_as_float(x0.x); w[1] = __uint_as_float(x0.y);
                     w[2] = __uint_as_float(x0.z); w[3] = __uint_as_float(x0.w);
                     w[4] = __uint_as_float(x1.x); w[5] = __uint_as_float(x1.y);
@@ -455,11 +507,16 @@ __global__ __launch_bounds__(kBackThreads) void k_galore_back(GTable t, GaArgs a
     }
 }
 
-void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, hipStream_t s) {
+void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s) {
     if (n <= 0) return;
     const dim3 grid(static_cast<uint32_t>(n)), block(kBackThreads);
-    if (left) hipLaunchKernelGGL(k_galore_back<true>, grid, block, 0, s, t, a);
-    else hipLaunchKernelGGL(k_galore_back<false>, grid, block, 0, s, t, a);
+    if (left) {
+        if (direct) hipLaunchKernelGGL((k_galore_back<true, true>), grid, block, 0, s, t, a);
+        else hipLaunchKernelGGL((k_galore_back<true, false>), grid, block, 0, s, t, a);
+    } else {
+        if (direct) hipLaunchKernelGGL((k_galore_back<false, true>), grid, block, 0, s, t, a);
+        else hipLaunchKernelGGL((k_galore_back<false, false>), grid, block, 0, s, t, a);
+    }
 }
 
 // ------------------------------------------------------------------ flat AdamW
