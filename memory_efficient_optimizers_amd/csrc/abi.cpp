@@ -1421,6 +1421,7 @@ struct GaPlan {
     const int2* items[kGaListCount] = {};
     int64_t count[kGaListCount] = {};
     bool back_direct[2] = {false, false};  // back-projection staged by global_load_lds (right, left)
+    bool proj_direct = false;              // m >= n projection staged by global_load_lds
 };
 std::list<GaPlan*> g_ga_plans;  // most recently used first, under g_mu
 
@@ -1765,6 +1766,8 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
         for (const GDesc& d : v) ok = ok && d.vec && d.r % kGaKb == 0;
         p->back_direct[side] = ok;
     }
+    p->proj_direct = true;
+    for (const GDesc& d : right) p->proj_direct = p->proj_direct && d.vec && d.d % kGaKb == 0;
     if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
         hipMemcpy(p->mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
         if (p->mem) (void)hipFree(p->mem);
@@ -1899,8 +1902,8 @@ int meo_galore_step(const meo_galore_hparams* hp, int64_t step, int32_t n, const
              static_cast<float>(hp->eps), static_cast<float>(1.0 - hp->lr * hp->weight_decay),
              static_cast<float>(hp->lr * hp->scale)};
     PassTimer pt(s);
-    launch_galore_project(GTable{p->gdesc, p->items[kGaProjR]}, p->count[kGaProjR], a, false, s);
-    launch_galore_project(GTable{p->gdesc, p->items[kGaProjL]}, p->count[kGaProjL], a, true, s);
+    launch_galore_project(GTable{p->gdesc, p->items[kGaProjR]}, p->count[kGaProjR], a, false, p->proj_direct, s);
+    launch_galore_project(GTable{p->gdesc, p->items[kGaProjL]}, p->count[kGaProjL], a, true, false, s);
     pt.mark(kPassGaProject);
     launch_galore_back(GTable{p->gdesc, p->items[kGaBackR]}, p->count[kGaBackR], a, false, p->back_direct[0], s);
     launch_galore_back(GTable{p->gdesc, p->items[kGaBackL]}, p->count[kGaBackL], a, true, p->back_direct[1], s);

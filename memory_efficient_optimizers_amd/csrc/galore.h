@@ -46,7 +46,9 @@ struct GaArgs {
     float coef;                      // lr * scale (projected) or lr (flat)
 };
 
-void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool left, hipStream_t s);
+// direct (m >= n lists only): every tensor has d % kGaKb == 0 and 16-byte rows
+// (vec); its operands are then staged by global_load_lds.
+void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s);
 // direct: every tensor of the list has rank % kGaKb == 0 and 16-byte rows (vec); its
 // operands are then staged by global_load_lds.
 void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s);

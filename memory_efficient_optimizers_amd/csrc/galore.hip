@@ -151,15 +151,49 @@ __device__ __forceinline__ void ep_gather(const float* lw, int lane, int q, floa
 
 // ------------------------------------------------------------------ projection + AdamW
 
-template <bool Left>
+// Direct staging: rows of 64 bf16 (128 bytes, unpadded) written straight from
+// global memory into LDS by global_load_lds (no registers), 8 rows per
+// instruction: lane l fills row (l >> 3) of the group at 16-byte slot (l & 7),
+// which holds the row's chunk (l & 7) ^ (row & 7). Reading chunk c of row w at
+// slot c ^ (w & 7) keeps the 8 rows of a fragment read on 8 different slots (no
+// bank conflict), as the padding does for the register path. Rows past the
+// operand's end read its last row: they only reach outputs that are not stored.
+constexpr int kDirectPitch = kGaKb;  // bf16 per LDS row
+template <int ROWS, int THREADS = kThreads>
+__device__ __forceinline__ void stage_direct(const uint16_t* g, int64_t nrows, int64_t cols, int64_t r0, int k0,
+                                             uint16_t* dst, int wave, int lane) {
+#pragma unroll
+    for (int j = wave; j < ROWS / 8; j += THREADS / 64) {
+        const int rr = 8 * j + (lane >> 3);
+        const int64_t row = min(r0 + rr, nrows - 1);
+        const int c = (lane & 7) ^ (rr & 7);
+        const uint16_t* src = g + row * cols + k0 + c * 8;
+        __builtin_amdgcn_global_load_lds((const MEO_GLOBAL void*)src,
+                                         (__attribute__((address_space(3))) void*)(dst + 8 * j * kDirectPitch),
+                                         16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ bfv8 ld_frag_sw(const uint16_t* base, int row, int kk) {
+    return *reinterpret_cast<const bfv8*>(base + row * kDirectPitch + (((kk >> 3) ^ (row & 7)) << 3));
+}
+
+
+template <bool Left, bool Direct>
 // Tile: kGaProjRows rows of R x all r columns; wave w holds columns 64w .. 64w + 63.
 // With 64-row tiles, 3 waves per SIMD: 13% faster on the 7B list than the 2 that
-// the registers would otherwise allow, with no spills. (The back-projection spills
-// under the same bound.)
-__global__ __launch_bounds__(kThreads, kGaProjRB == 1 ? 3 : 2) void k_galore_project(GTable t, GaArgs a) {
+// the registers would otherwise allow, with no spills. Direct (m >= n lists whose
+// contraction length is a multiple of kGaKb): both operands staged by
+// global_load_lds into an unpadded swizzled arena, no staging registers.
+__global__ __launch_bounds__(kThreads, Direct ? 4 : (kGaProjRB == 1 ? 3 : 2)) void k_galore_project(GTable t,
+                                                                                                   GaArgs a) {
+    static_assert(!(Direct && Left), "the m < n projection reads G transposed through registers");
     constexpr int kRB = 2 * kGaProjRB;  // 32-row blocks of a wave's tile
-    __shared__ __attribute__((aligned(16))) uint16_t sa[kGaProjRows * kGaPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t sb[kGaWide * kGaPitch];
+    constexpr int kPitch = Direct ? kDirectPitch : kGaPitch;
+    __shared__ __attribute__((aligned(16))) uint16_t arena[(kGaProjRows + kGaWide) * kPitch];
+    static_assert((kGaProjRows + kGaWide) * kPitch * 2 >= kWaves * kEpWave * 4, "exchange space");
+    uint16_t* sa = arena;
+    uint16_t* sb = arena + kGaProjRows * kPitch;
     const int2 it = t.items[blockIdx.x];
     const GDesc d = t.desc[it.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -180,34 +214,51 @@ __global__ __launch_bounds__(kThreads, kGaProjRB == 1 ? 3 : 2) void k_galore_pro
         else pa.load(d.g, d.D, d.d, i0, k0, vec);
         pb.load(d.ut, d.r, d.d, 0, k0, vec);
     };
-    fetch(0);
-    for (int64_t k0 = 0; k0 < d.d; k0 += kGaKb) {
-        pa.store(sa);
-        pb.store(sb);
-        __syncthreads();
-        if (k0 + kGaKb < d.d) fetch(k0 + kGaKb);
-        if (active) {
+    auto multiply = [&]() {
+        if (!active) return;
 #pragma unroll
-            for (int ks = 0; ks < kGaKb; ks += 16) {
-                const int kk = ks + 8 * (lane >> 5);
-                bfv8 fa[kRB], fb[2];
+        for (int ks = 0; ks < kGaKb; ks += 16) {
+            const int kk = ks + 8 * (lane >> 5);
+            bfv8 fa[kRB], fb[2];
 #pragma unroll
-                for (int ib = 0; ib < kRB; ++ib) fa[ib] = ld_frag(sa + (ib * 32 + (lane & 31)) * kGaPitch + kk);
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb)
-                    fb[jb] = ld_frag(sb + (wave * 64 + jb * 32 + (lane & 31)) * kGaPitch + kk);
-#pragma unroll
-                for (int ib = 0; ib < kRB; ++ib)
-#pragma unroll
-                    for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma32(fa[ib], fb[jb], acc[ib][jb]);
+            for (int ib = 0; ib < kRB; ++ib) {
+                if constexpr (Direct) fa[ib] = ld_frag_sw(sa, ib * 32 + (lane & 31), kk);
+                else fa[ib] = ld_frag(sa + (ib * 32 + (lane & 31)) * kGaPitch + kk);
             }
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                if constexpr (Direct) fb[jb] = ld_frag_sw(sb, wave * 64 + jb * 32 + (lane & 31), kk);
+                else fb[jb] = ld_frag(sb + (wave * 64 + jb * 32 + (lane & 31)) * kGaPitch + kk);
+            }
+#pragma unroll
+            for (int ib = 0; ib < kRB; ++ib)
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma32(fa[ib], fb[jb], acc[ib][jb]);
         }
-        __syncthreads();
+    };
+    if constexpr (Direct) {
+        for (int64_t k0 = 0; k0 < d.d; k0 += kGaKb) {
+            stage_direct<kGaProjRows>(d.g, d.D, d.d, i0, static_cast<int>(k0), sa, wave, lane);
+            stage_direct<kGaWide>(d.ut, d.r, d.d, 0, static_cast<int>(k0), sb, wave, lane);
+            __syncthreads();  // the loads have landed (each wave waits for its own first)
+            multiply();
+            __syncthreads();
+        }
+    } else {
+        fetch(0);
+        for (int64_t k0 = 0; k0 < d.d; k0 += kGaKb) {
+            pa.store(sa);
+            pb.store(sb);
+            __syncthreads();
+            if (k0 + kGaKb < d.d) fetch(k0 + kGaKb);
+            multiply();
+            __syncthreads();
+        }
     }
     if (!active) return;
     // AdamW on the tile of R, rows of 8 columns per lane (see ep_spill): moments
     // read and written, N's planes written, 16 bytes at a time where rows allow.
-    float* lw = reinterpret_cast<float*>(sb) + wave * kEpWave;
+    float* lw = reinterpret_cast<float*>(arena) + wave * kEpWave;
 #pragma unroll
     for (int ib = 0; ib < kRB; ++ib) {
         ep_spill(acc[ib][0], acc[ib][1], lw, lane);
@@ -268,11 +319,12 @@ __global__ __launch_bounds__(kThreads, kGaProjRB == 1 ? 3 : 2) void k_galore_pro
     }
 }
 
-void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool left, hipStream_t s) {
+void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s) {
     if (n <= 0) return;
     const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
-    if (left) hipLaunchKernelGGL(k_galore_project<true>, grid, block, 0, s, t, a);
-    else hipLaunchKernelGGL(k_galore_project<false>, grid, block, 0, s, t, a);
+    if (left) hipLaunchKernelGGL((k_galore_project<true, false>), grid, block, 0, s, t, a);
+    else if (direct) hipLaunchKernelGGL((k_galore_project<false, true>), grid, block, 0, s, t, a);
+    else hipLaunchKernelGGL((k_galore_project<false, false>), grid, block, 0, s, t, a);
 }
 
 // ------------------------------------------------------------------ back-projection + update
@@ -284,33 +336,6 @@ void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool lef
 // reads 4r / 256 + 2r / (64 kGaBackRW) bytes from L2.
 constexpr int kBackThreads = kThreads * kGaBackRW;
 constexpr int kBackN = kGaTile * kGaBackRW;  // rows of N per tile
-
-// Direct staging: rows of 64 bf16 (128 bytes, unpadded) written straight from
-// global memory into LDS by global_load_lds (no registers), 8 rows per
-// instruction: lane l fills row (l >> 3) of the group at 16-byte slot (l & 7),
-// which holds the row's chunk (l & 7) ^ (row & 7). Reading chunk c of row w at
-// slot c ^ (w & 7) keeps the 8 rows of a fragment read on 8 different slots (no
-// bank conflict), as the padding does for the register path. Rows past the
-// operand's end read its last row: they only reach outputs that are not stored.
-constexpr int kDirectPitch = kGaKb;  // bf16 per LDS row
-template <int ROWS>
-__device__ __forceinline__ void stage_direct(const uint16_t* g, int64_t nrows, int64_t cols, int64_t r0, int k0,
-                                             uint16_t* dst, int wave, int lane) {
-#pragma unroll
-    for (int j = wave; j < ROWS / 8; j += kBackThreads / 64) {
-        const int rr = 8 * j + (lane >> 3);
-        const int64_t row = min(r0 + rr, nrows - 1);
-        const int c = (lane & 7) ^ (rr & 7);
-        const uint16_t* src = g + row * cols + k0 + c * 8;
-        __builtin_amdgcn_global_load_lds((const MEO_GLOBAL void*)src,
-                                         (__attribute__((address_space(3))) void*)(dst + 8 * j * kDirectPitch),
-                                         16, 0, 0);
-    }
-}
-
-__device__ __forceinline__ bfv8 ld_frag_sw(const uint16_t* base, int row, int kk) {
-    return *reinterpret_cast<const bfv8*>(base + row * kDirectPitch + (((kk >> 3) ^ (row & 7)) << 3));
-}
 
 // Direct: operands staged by global_load_lds into an unpadded swizzled arena
 // (48 KB: 3 blocks per CU), for lists whose rank is a multiple of kGaKb; otherwise
@@ -416,9 +441,9 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
     if constexpr (Direct) {
         // the rank is a multiple of kGaKb: every contraction block is whole
         for (int k0 = 0; k0 <= klast; k0 += kGaKb) {
-            stage_direct<kBackN>(d.nh, d.D, d.r, n0, k0, sh, wave, lane);
-            stage_direct<kBackN>(d.nl, d.D, d.r, n0, k0, sl, wave, lane);
-            stage_direct<kGaWide>(d.u, d.d, d.r, u0, k0, su, wave, lane);
+            stage_direct<kBackN, kBackThreads>(d.nh, d.D, d.r, n0, k0, sh, wave, lane);
+            stage_direct<kBackN, kBackThreads>(d.nl, d.D, d.r, n0, k0, sl, wave, lane);
+            stage_direct<kGaWide, kBackThreads>(d.u, d.d, d.r, u0, k0, su, wave, lane);
             __syncthreads();  // the loads have landed (each wave waits for its own first)
             multiply();
             __syncthreads();

@@ -77,6 +77,8 @@ def run_case(shapes, rank, t=5, hp=None, param_dtype=torch.float32, seed=0, chec
     ((300, 136), 40),     # ragged rows, r not a multiple of 32
     ((72, 333), 24),      # ragged, odd columns: element-wise loads
     ((200, 96), 13),      # r not a multiple of 8
+    ((200, 192), 13),     # direct-staged projection: ragged rows, r not a multiple of 8
+    ((1000, 256), 100),   # direct-staged projection: second wave partly past r
     ((40, 24), 256),      # rank clamped to min(m, n)
     ((512, 384), 256),    # full rank-256 tile, several contraction blocks
     ((300, 600), 256),    # m < n at rank 256
