@@ -127,6 +127,31 @@ def test_list_equals_singles():
             assert torch.equal(s1[k][key], s2[k][key])
 
 
+
+def test_direct_staging_equals_register_staging():
+    """The staging path is chosen per list: direct (global_load_lds) when every
+    contraction length of the list is a multiple of 64, through registers otherwise.
+    Both put the same values in LDS and run the same MFMA sequence, so a tensor's
+    step is bitwise the same on either. (256, 128) and (128, 320) at rank 64 take the
+    direct paths alone and the register paths beside (200, 40) and (40, 200), whose
+    rank 40 and contraction length 40 are not multiples of 64."""
+    shapes = [(256, 128), (200, 40), (128, 320), (40, 200)]
+    dev = "cuda"
+    h = _lib.galore_hparams(lr=0.05, rank=64)
+    p1, g1, s1 = workloads.galore_inputs(shapes, 64, 23, device=dev)
+    p2, g2, s2 = workloads.galore_inputs(shapes, 64, 23, device=dev)
+    ws = _lib.workspace(_lib.meo_galore_workspace_size(h, p1, g1), dev)
+    _lib.meo_galore_step(h, 5, p1, g1, s1, ws)
+    for k in (0, 2):
+        wk = _lib.workspace(_lib.meo_galore_workspace_size(h, [p2[k]], [g2[k]]), dev)
+        _lib.meo_galore_step(h, 5, [p2[k]], [g2[k]], [s2[k]], wk)
+    torch.cuda.synchronize()
+    for k in (0, 2):
+        assert not torch.equal(p1[k], workloads.galore_inputs(shapes, 64, 23, device=dev)[0][k])
+        assert torch.equal(p1[k], p2[k])
+        for key in s1[k]:
+            assert torch.equal(s1[k][key], s2[k][key])
+
 # ----------------------------------------------------------------------------- projector refresh
 #
 # The refresh computes the leading r singular vectors by subspace iteration; it
