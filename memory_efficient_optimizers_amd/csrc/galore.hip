@@ -386,6 +386,10 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
     const int64_t wr0 = Left ? r0 + ug * 64 : r0 + ng * 64;
     const int64_t wc0 = Left ? c0 + ng * 64 : c0 + ug * 64;
     const int64_t wcol = wc0 + (lane & 7) * 8;
+    // Direct: only the first 16 rows of the wave's tile (16 VGPRs for fp32), which
+    // is what the registers left at 3 blocks per CU hold without spilling.
+    constexpr int kDirectPreQ = 2;
+    auto pre = [](int ib, int q) { return !Direct || (ib == 0 && q < kDirectPreQ); };
     u32x4 wpre[2][4][2];
     auto prefetch_w = [&]() {
         if (!(d.wvec && wcol + 8 <= d.n)) return;
@@ -394,7 +398,7 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int64_t row = wr0 + ib * 32 + (lane >> 3) + 8 * q;
-                if (row >= d.m) continue;
+                if (!pre(ib, q) || row >= d.m) continue;
                 const int64_t idx = row * d.n + wcol;
                 if (d.xbf16) {
                     wpre[ib][q][0] = *gld<u32x4>(static_cast<const uint16_t*>(d.x) + idx);
@@ -445,6 +449,7 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
             stage_direct<kBackN, kBackThreads>(d.nl, d.D, d.r, n0, k0, sl, wave, lane);
             stage_direct<kGaWide, kBackThreads>(d.u, d.d, d.r, u0, k0, su, wave, lane);
             __syncthreads();  // the loads have landed (each wave waits for its own first)
+            if (k0 == klast) prefetch_w();
             multiply();
             __syncthreads();
         }
@@ -488,8 +493,7 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
             if (d.xbf16) {
                 uint16_t* xp = static_cast<uint16_t*>(d.x) + idx;
                 if (full) {
-                    if constexpr (Direct) bf16x8(*gld<u32x4>(xp), w);
-                    else bf16x8(wpre[ib][q][0], w);
+                    bf16x8(pre(ib, q) ? wpre[ib][q][0] : *gld<u32x4>(xp), w);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
@@ -507,8 +511,8 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
             } else {
                 float* xp = static_cast<float*>(d.x) + idx;
                 if (full) {
-                    const u32x4 x0 = Direct ? *gld<u32x4>(xp) : wpre[ib][q][0];
-                    const u32x4 x1 = Direct ? *gld<u32x4>(xp + 4) : wpre[ib][q][1];
+                    const u32x4 x0 = pre(ib, q) ? wpre[ib][q][0] : *gld<u32x4>(xp);
+                    const u32x4 x1 = pre(ib, q) ? wpre[ib][q][1] : *gld<u32x4>(xp + 4);
                     w[0] = __uint_as_float(x0.x); w[1] = __uint_as_float(x0.y);
                     w[2] = __uint_as_float(x0.z); w[3] = __uint_as_float(x0.w);
                     w[4] = __uint_as_float(x1.x); w[5] = __uint_as_float(x1.y);
