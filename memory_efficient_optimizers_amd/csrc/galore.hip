@@ -480,6 +480,21 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
     float* lw = reinterpret_cast<float*>(arena) + wave * kEpWave;
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
+        // The row groups not prefetched are all loaded before any is stored (a store
+        // may alias a later load as far as the compiler knows).
+        u32x4 wl[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t row = wr0 + ib * 32 + (lane >> 3) + 8 * q;
+            if (pre(ib, q) || !(d.wvec && wcol + 8 <= d.n) || row >= d.m) continue;
+            const int64_t idx = row * d.n + wcol;
+            if (d.xbf16) {
+                wl[q][0] = *gld<u32x4>(static_cast<const uint16_t*>(d.x) + idx);
+            } else {
+                wl[q][0] = *gld<u32x4>(static_cast<const float*>(d.x) + idx);
+                wl[q][1] = *gld<u32x4>(static_cast<const float*>(d.x) + idx + 4);
+            }
+        }
         ep_spill(acc[ib][0], acc[ib][1], lw, lane);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -493,7 +508,7 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
             if (d.xbf16) {
                 uint16_t* xp = static_cast<uint16_t*>(d.x) + idx;
                 if (full) {
-                    bf16x8(pre(ib, q) ? wpre[ib][q][0] : *gld<u32x4>(xp), w);
+                    bf16x8(pre(ib, q) ? wpre[ib][q][0] : wl[q][0], w);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
@@ -511,8 +526,8 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
             } else {
                 float* xp = static_cast<float*>(d.x) + idx;
                 if (full) {
-                    const u32x4 x0 = pre(ib, q) ? wpre[ib][q][0] : *gld<u32x4>(xp);
-                    const u32x4 x1 = pre(ib, q) ? wpre[ib][q][1] : *gld<u32x4>(xp + 4);
+                    const u32x4 x0 = pre(ib, q) ? wpre[ib][q][0] : wl[q][0];
+                    const u32x4 x1 = pre(ib, q) ? wpre[ib][q][1] : wl[q][1];
                     w[0] = __uint_as_float(x0.x); w[1] = __uint_as_float(x0.y);
                     w[2] = __uint_as_float(x0.z); w[3] = __uint_as_float(x0.w);
                     w[4] = __uint_as_float(x1.x); w[5] = __uint_as_float(x1.y);
