@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MEO_VERSION 7
+#define MEO_VERSION 8
 
 /* Return codes. */
 #define MEO_OK          0
@@ -86,7 +86,7 @@ extern "C" {
  * One parameter tensor and its gradient, viewed as [batch, rows, cols]:
  * ndim >= 2 -> rows = size of dim -2, cols = size of dim -1, batch = product of
  * the leading dims; the Adafactor/CAME statistics are factored per matrix
- * (page "Step 3": factored = len(param_shape) >= 2).
+ * (page "Step 3": tensors of two or more dimensions keep factored statistics).
  * ndim 0 or 1 -> batch = rows = 1, cols = numel; full (unfactored) statistic.
  * LAMB ignores the view and treats the tensor as one flat layer.
  */
@@ -469,6 +469,40 @@ int     meo_galore_step(const meo_galore_hparams* hp, int64_t step, int32_t n, c
 int     meo_galore_refresh(const meo_galore_hparams* hp, int32_t n, const meo_tensor* tensors,
                            const meo_galore_state* states, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* ------------------------------------------------------- per-tensor scalars */
+
+/*
+ * For tests and diagnostics. A step call over a list leaves, for every tensor
+ * with elements, 8 float32 per-tensor scalars in the workspace; they can be read
+ * back once the call's work on the stream has completed and before the
+ * workspace is used again (the next call overwrites them). meo_*_scalar_offsets
+ * writes, for each of the n tensors, the offset in floats from the workspace's
+ * start of that tensor's 8 slots, or -1 for a tensor with zero elements; the
+ * offsets depend on the list (shapes and the 16-byte alignment of param and
+ * grad), exactly as the step call lays the workspace out. Host only; MEO_OK,
+ * MEO_ENULL (tensors or offsets NULL with n > 0) or MEO_ESHAPE.
+ *
+ * Slots (from the note after "Step 5" of the Colossal-AI distributed-optimizers
+ * page: RMS clipping and scale_parameter; the "four optimizers" table and the
+ * DistributedLAMB paragraph: the layer-wise trust ratio):
+ *   [0] Adafactor: alpha, the step size rho times max(eps2, RMS(param)) with
+ *       scale_parameter (else rho); CAME: 1
+ *   [1] alpha / kappa (Adafactor, CAME)
+ *   [2] decoupled weight-decay factor: weight_decay * alpha (Adafactor),
+ *       weight_decay * lr (CAME)
+ *   [3] RMS of the unclipped update U = G / sqrt(V_hat) (Adafactor, CAME)
+ *   [4] RMS(param) before the update (Adafactor; written with scale_parameter);
+ *       LAMB: ||param||_2
+ *   [5] LAMB: ||d||_2 of the update direction
+ *   [6] kappa = max(1, RMS(U) / clip_threshold), the clip divisor (Adafactor, CAME)
+ *   [7] LAMB: the trust ratio ||param|| / ||d|| (1 when either norm is 0)
+ * Slots an optimizer does not name hold unspecified values. The row-sharded
+ * calls use the same slots (their values then come from the reduced sums).
+ */
+int meo_adafactor_scalar_offsets(int32_t n, const meo_tensor* tensors, int64_t* offsets);
+int meo_came_scalar_offsets(int32_t n, const meo_tensor* tensors, int64_t* offsets);
+int meo_lamb_scalar_offsets(int32_t n, const meo_tensor* tensors, int64_t* offsets);
 
 /* ----------------------------------------------------------------- utilities */
 

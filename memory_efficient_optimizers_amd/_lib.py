@@ -42,6 +42,7 @@ EXPORTS = [
     "meo_came_shard_apply",
     "meo_galore_defaults", "meo_galore_rank", "meo_galore_workspace_size", "meo_galore_validate",
     "meo_galore_step", "meo_galore_refresh",
+    "meo_adafactor_scalar_offsets", "meo_came_scalar_offsets", "meo_lamb_scalar_offsets",
 ]
 MEO_NUM_PASSES = 17
 
@@ -133,6 +134,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         getattr(lib, f"meo_{opt}_defaults").restype = None
         getattr(lib, f"meo_{opt}_workspace_size").argtypes = [c_int32, T]
         getattr(lib, f"meo_{opt}_workspace_size").restype = c_size_t
+        getattr(lib, f"meo_{opt}_scalar_offsets").argtypes = [c_int32, T, ctypes.POINTER(c_int64)]
+        getattr(lib, f"meo_{opt}_scalar_offsets").restype = ctypes.c_int
         getattr(lib, f"meo_{opt}_validate").argtypes = [ctypes.POINTER(hp), c_int64, c_int32, T,
                                                         ctypes.POINTER(st)]
         getattr(lib, f"meo_{opt}_validate").restype = ctypes.c_int
@@ -349,6 +352,47 @@ def meo_came_workspace_size(params, grads) -> int:
 
 def meo_lamb_workspace_size(params, grads) -> int:
     return int(load().meo_lamb_workspace_size(len(params), _tensors(params, grads)))
+
+
+SCALAR_SLOTS = ("alpha", "coef", "decay", "rms_u", "rms_x", "norm_d", "kappa", "trust")
+
+
+def _scalar_offsets(opt, params, grads):
+    out = (c_int64 * max(len(params), 1))()
+    _check(getattr(load(), f"meo_{opt}_scalar_offsets")(len(params), _tensors(params, grads), out))
+    return [int(out[k]) for k in range(len(params))]
+
+
+def meo_adafactor_scalar_offsets(params, grads):
+    return _scalar_offsets("adafactor", params, grads)
+
+
+def meo_came_scalar_offsets(params, grads):
+    return _scalar_offsets("came", params, grads)
+
+
+def meo_lamb_scalar_offsets(params, grads):
+    return _scalar_offsets("lamb", params, grads)
+
+
+def read_scalars(workspace: torch.Tensor, offsets) -> List[Optional[Dict[str, float]]]:
+    """The per-tensor scalars a completed step left in ``workspace`` (slots named as
+    in SCALAR_SLOTS; None for tensors with zero elements). Synchronises the device."""
+    live = [off for off in offsets if off >= 0]
+    if not live:
+        return [None] * len(offsets)
+    flat = workspace.view(torch.float32)
+    idx = torch.tensor([off + i for off in live for i in range(len(SCALAR_SLOTS))], dtype=torch.int64,
+                       device=flat.device)
+    vals = flat[idx].cpu().tolist()
+    out, j = [], 0
+    for off in offsets:
+        if off < 0:
+            out.append(None)
+            continue
+        out.append(dict(zip(SCALAR_SLOTS, vals[j:j + len(SCALAR_SLOTS)])))
+        j += len(SCALAR_SLOTS)
+    return out
 
 
 def meo_adafactor_validate(hp, step, params, grads, states) -> None:

@@ -397,6 +397,25 @@ int check_tensor_memory(int op, int32_t n, const meo_tensor* ts, const StatePtrs
     return MEO_OK;
 }
 
+// Offsets (floats) of each tensor's scalar slots in the workspace, -1 for tensors
+// with zero elements; the layout the step calls use for the same list.
+int scalar_offsets(int op, int32_t n, const meo_tensor* ts, int64_t* out) {
+    g_err.clear();
+    if (n < 0) return fail(MEO_ESHAPE, "n must be >= 0");
+    if (n == 0) return MEO_OK;
+    if (!ts || !out) return fail(MEO_ENULL, "tensors and offsets must not be NULL");
+    for (int32_t k = 0; k < n; ++k) {
+        int64_t numel = 0;
+        if (ts[k].batch < 0 || ts[k].rows < 0 || ts[k].cols < 0 || overflow_numel(ts[k], &numel) ||
+            (is_factored(op, ts[k]) && (ts[k].batch > kMaxDim || ts[k].rows > kMaxDim || ts[k].cols > kMaxDim)))
+            return fail(MEO_ESHAPE, "tensor " + std::to_string(k) + ": invalid batch/rows/cols");
+    }
+    std::vector<Geo> geo;
+    layout(op, n, ts, &geo);
+    for (int32_t k = 0; k < n; ++k) out[k] = geo[k].numel > 0 ? geo[k].scal : -1;
+    return MEO_OK;
+}
+
 // ----------------------------------------------------------------------------- plan cache
 
 // Item tables of the launches of one call.
@@ -475,37 +494,37 @@ void xcd_order(std::vector<int2>& items, const std::vector<TDesc>& desc) {
     items.swap(out);
 }
 
-// Builds (or finds) the launch table for this list. Returns nullptr with g_err set
-// on a HIP failure.
-// `shards` (row-sharded steps; else null): the whole tensors' sizes, part of the key.
-Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int has_m, int* rc,
-               const meo_shard* shards = nullptr) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        *rc = fail(MEO_EHIP, "hipGetDevice failed");
-        return nullptr;
-    }
+// The key of a list's launch tables: everything they are built from.
+std::vector<uint8_t> plan_key(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int has_m, int dev,
+                              const meo_shard* shards) {
     const size_t nsh = shards ? n * sizeof(meo_shard) : 0;
     std::vector<uint8_t> key(sizeof(int) * 5 + n * (sizeof(meo_tensor) + sizeof(StatePtrs)) + nsh);
-    {
-        uint8_t* w = key.data();
-        const int hdr[5] = {op, n, dev, has_m, shards ? 1 : 0};
-        std::memcpy(w, hdr, sizeof hdr); w += sizeof hdr;
-        std::memcpy(w, ts, n * sizeof(meo_tensor)); w += n * sizeof(meo_tensor);
-        std::memcpy(w, sp, n * sizeof(StatePtrs)); w += n * sizeof(StatePtrs);
-        if (nsh) std::memcpy(w, shards, nsh);
-    }
-    std::lock_guard<std::mutex> lock(g_mu);
-    for (auto it = g_plans.begin(); it != g_plans.end(); ++it) {
-        if ((*it)->key == key) {
-            Plan* p = *it;
-            g_plans.erase(it);
-            g_plans.push_front(p);
-            return p;
-        }
-    }
-    *rc = check_tensor_memory(op, n, ts, sp, has_m, dev);
-    if (*rc) return nullptr;
+    uint8_t* w = key.data();
+    const int hdr[5] = {op, n, dev, has_m, shards ? 1 : 0};
+    std::memcpy(w, hdr, sizeof hdr); w += sizeof hdr;
+    std::memcpy(w, ts, n * sizeof(meo_tensor)); w += n * sizeof(meo_tensor);
+    std::memcpy(w, sp, n * sizeof(StatePtrs)); w += n * sizeof(StatePtrs);
+    if (nsh) std::memcpy(w, shards, nsh);
+    return key;
+}
+
+// The launch tables of one list in host memory: [n TDesc][item tables], each
+// table 256-byte aligned at offs[l] with count[l] items.
+struct HostPlan {
+    std::vector<uint8_t> bytes;
+    size_t offs[kListCount] = {};
+    int64_t count[kListCount] = {};
+    int32_t n = 0;
+    int32_t storage = kStoreF32;
+};
+
+// Builds the launch tables of a list on the host (no device memory is touched or
+// allocated); first checks every pointer of the list against its allocation.
+// `shards` (row-sharded steps; else null): the whole tensors' sizes.
+int build_host_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int has_m, int dev,
+                    const meo_shard* shards, HostPlan* out) {
+    int rc = check_tensor_memory(op, n, ts, sp, has_m, dev);
+    if (rc) return rc;
     std::vector<Geo> geo;
     layout(op, n, ts, &geo);
     std::vector<int64_t> poff, poff2;
@@ -596,35 +615,69 @@ Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int
     for (const TDesc& d : desc) any_i8 = any_i8 || d.mi8;
     if (any_i8) xcd_order(lists[kListAll], desc);
     const int32_t m = static_cast<int32_t>(desc.size());
-    size_t offs[kListCount + 1];
     size_t total = (m * sizeof(TDesc) + 255) / 256 * 256;
     for (int l = 0; l < kListCount; ++l) {
-        offs[l] = total;
+        out->offs[l] = total;
+        out->count[l] = static_cast<int64_t>(lists[l].size());
         total += (lists[l].size() * sizeof(int2) + 255) / 256 * 256;
     }
     total = std::max<size_t>(total, 256);
-    std::vector<uint8_t> host(total, 0);
-    if (m) std::memcpy(host.data(), desc.data(), m * sizeof(TDesc));
+    out->bytes.assign(total, 0);
+    if (m) std::memcpy(out->bytes.data(), desc.data(), m * sizeof(TDesc));
     for (int l = 0; l < kListCount; ++l)
-        if (!lists[l].empty()) std::memcpy(host.data() + offs[l], lists[l].data(), lists[l].size() * sizeof(int2));
+        if (!lists[l].empty())
+            std::memcpy(out->bytes.data() + out->offs[l], lists[l].data(), lists[l].size() * sizeof(int2));
+    out->n = m;
+    out->storage = storage_class(desc);
+    return MEO_OK;
+}
+
+// Points a Plan's tables into device memory holding a HostPlan's bytes.
+void bind_plan(const HostPlan& h, void* dev_bytes, Plan* p) {
+    uint8_t* base = static_cast<uint8_t*>(dev_bytes);
+    p->n = h.n;
+    p->storage = h.storage;
+    p->desc = reinterpret_cast<const TDesc*>(base);
+    for (int l = 0; l < kListCount; ++l) {
+        p->items[l] = reinterpret_cast<const int2*>(base + h.offs[l]);
+        p->count[l] = h.count[l];
+    }
+}
+
+// Builds (or finds) the device-resident launch tables for this list (allocated
+// once per distinct list and cached). Returns nullptr with g_err set on a failure.
+// `shards` (row-sharded steps; else null): the whole tensors' sizes, part of the key.
+Plan* get_plan(int op, int32_t n, const meo_tensor* ts, const StatePtrs* sp, int has_m, int* rc,
+               const meo_shard* shards = nullptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        *rc = fail(MEO_EHIP, "hipGetDevice failed");
+        return nullptr;
+    }
+    std::vector<uint8_t> key = plan_key(op, n, ts, sp, has_m, dev, shards);
+    std::lock_guard<std::mutex> lock(g_mu);
+    for (auto it = g_plans.begin(); it != g_plans.end(); ++it) {
+        if ((*it)->key == key) {
+            Plan* p = *it;
+            g_plans.erase(it);
+            g_plans.push_front(p);
+            return p;
+        }
+    }
+    HostPlan h;
+    *rc = build_host_plan(op, n, ts, sp, has_m, dev, shards, &h);
+    if (*rc) return nullptr;
     Plan* p = new Plan;
     p->key = std::move(key);
     p->device = dev;
-    p->n = m;
-    p->storage = storage_class(desc);
-    if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
-        hipMemcpy(p->mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    if (hipMalloc(&p->mem, h.bytes.size()) != hipSuccess ||
+        hipMemcpy(p->mem, h.bytes.data(), h.bytes.size(), hipMemcpyHostToDevice) != hipSuccess) {
         if (p->mem) (void)hipFree(p->mem);
         delete p;
         *rc = fail(MEO_EHIP, "could not allocate or upload the launch table");
         return nullptr;
     }
-    uint8_t* base = static_cast<uint8_t*>(p->mem);
-    p->desc = reinterpret_cast<const TDesc*>(base);
-    for (int l = 0; l < kListCount; ++l) {
-        p->items[l] = reinterpret_cast<const int2*>(base + offs[l]);
-        p->count[l] = static_cast<int64_t>(lists[l].size());
-    }
+    bind_plan(h, p->mem, p);
     g_plans.push_front(p);
     while (g_plans.size() > kMaxPlans) {
         free_plan(g_plans.back());
@@ -785,6 +838,10 @@ size_t meo_adafactor_workspace_size(int32_t n, const meo_tensor* ts) {
     return static_cast<size_t>(layout(kOpAdafactor, n, ts, nullptr)) * sizeof(float);
 }
 
+int meo_adafactor_scalar_offsets(int32_t n, const meo_tensor* ts, int64_t* offsets) {
+    return scalar_offsets(kOpAdafactor, n, ts, offsets);
+}
+
 int meo_adafactor_validate(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
                            const meo_adafactor_state* st) {
     g_err.clear();
@@ -817,6 +874,9 @@ int check_param_sumsq(int32_t n, const meo_tensor* ts, const meo_adafactor_state
     return MEO_OK;
 }
 
+int adafactor_passes(const meo_adafactor_hparams* hp, int64_t step, int carry, const Plan& plan, float* w,
+                     hipStream_t s);
+
 // carry: -1 plain step; 0 or 1 a step that leaves the updated parameter's sum of
 // squares in each tensor's param_sumsq (1: and takes RMS(X) from it).
 int adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
@@ -837,8 +897,14 @@ int adafactor_step(const meo_adafactor_hparams* hp, int64_t step, int32_t n, con
     Plan* p = get_plan(kOpAdafactor, n, ts, sp.data(), hp->has_beta1, &rc);
     if (!p) return rc;
     if (p->n == 0) return MEO_OK;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    float* w = static_cast<float*>(ws);
+    return adafactor_passes(hp, step, carry, *p, static_cast<float*>(ws), static_cast<hipStream_t>(stream));
+}
+
+// The passes of one Adafactor step over a list whose launch tables are `p` and
+// whose workspace starts at `w`, enqueued on `s`. carry as for adafactor_step.
+int adafactor_passes(const meo_adafactor_hparams* hp, int64_t step, int carry, const Plan& plan, float* w,
+                     hipStream_t s) {
+    const Plan* p = &plan;
     auto tab = [&](int l) { return Table{p->desc, p->items[l], w}; };
 
     const double tt = static_cast<double>(step);
@@ -922,6 +988,10 @@ void meo_came_defaults(meo_came_hparams* hp) {
 size_t meo_came_workspace_size(int32_t n, const meo_tensor* ts) {
     if (n <= 0 || !ts) return 0;
     return static_cast<size_t>(layout(kOpCame, n, ts, nullptr)) * sizeof(float);
+}
+
+int meo_came_scalar_offsets(int32_t n, const meo_tensor* ts, int64_t* offsets) {
+    return scalar_offsets(kOpCame, n, ts, offsets);
 }
 
 int meo_came_validate(const meo_came_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
@@ -1008,6 +1078,10 @@ void meo_lamb_defaults(meo_lamb_hparams* hp) {
 size_t meo_lamb_workspace_size(int32_t n, const meo_tensor* ts) {
     if (n <= 0 || !ts) return 0;
     return static_cast<size_t>(layout(kOpLamb, n, ts, nullptr)) * sizeof(float);
+}
+
+int meo_lamb_scalar_offsets(int32_t n, const meo_tensor* ts, int64_t* offsets) {
+    return scalar_offsets(kOpLamb, n, ts, offsets);
 }
 
 int meo_lamb_validate(const meo_lamb_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,

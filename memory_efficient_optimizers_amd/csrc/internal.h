@@ -48,9 +48,10 @@ constexpr int kStripRowsCame = 64;
 constexpr int kRcMaxCols0 = 256 * 8 * 2;  // 4096
 constexpr int kRcMaxCols1 = 512 * 8 * 3;  // 12288
 
-// Per-tensor scalar slots in the workspace.
+// Per-tensor scalar slots in the workspace (their meaning is part of the C ABI:
+// meo_*_scalar_offsets). LAMB keeps the parameter's norm in kSlotRmsX.
 enum ScalSlot { kSlotAlpha = 0, kSlotCoef = 1, kSlotDecay = 2, kSlotRmsU = 3, kSlotRmsX = 4,
-                kSlotNormD = 5 };
+                kSlotNormD = 5, kSlotKappa = 6, kSlotTrust = 7 };
 
 // Storage class of a launch's parameters and first moments: all fp32, all bf16,
 // fp32 or bf16 parameters with 8-bit first moments, or a mix (then read per tensor

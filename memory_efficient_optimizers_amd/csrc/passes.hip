@@ -557,6 +557,7 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
             stf(bs, static_cast<float>(a.lr * trust));
             stf(scal + kSlotRmsX, static_cast<float>(xn));
             stf(scal + kSlotNormD, static_cast<float>(dn));
+            stf(scal + kSlotTrust, static_cast<float>(trust));
         }
         return;
     }
@@ -617,6 +618,7 @@ __global__ __launch_bounds__(kThreads) void k_scalars(const TDesc* __restrict__ 
         stf(scal + kSlotAlpha, static_cast<float>(alpha));
         stf(scal + kSlotCoef, static_cast<float>(coef));
         stf(scal + kSlotRmsU, static_cast<float>(rms_u));
+        stf(scal + kSlotKappa, static_cast<float>(kappa));
         // Decoupled weight decay: Adafactor scales it by alpha, CAME by lr.
         stf(scal + kSlotDecay, static_cast<float>(a.mode == kScalAdafactor ? a.wd * alpha : a.wd * a.lr));
     }

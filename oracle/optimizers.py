@@ -179,7 +179,8 @@ def _moment_out(m: Array, new: State, bf16: bool, i8: bool) -> Array:
 
 
 def is_factored(shape: Tuple[int, ...]) -> bool:
-    """Page "Step 3": factored = len(param_shape) >= 2."""
+    """Page "Step 3": the statistics are factored for tensors of two or more
+    dimensions, full for the others."""
     return len(shape) >= 2
 
 
@@ -249,9 +250,14 @@ def adafactor_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None, *, e
 
 
 def adafactor_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int, *,
-                          param_bf16: bool = False, exp_avg_bf16: bool = False, exp_avg_i8: bool = False
-                          ) -> Tuple[Array, State]:
-    """One Adafactor step of one tensor; returns (new parameter, new state)."""
+                          param_bf16: bool = False, exp_avg_bf16: bool = False, exp_avg_i8: bool = False,
+                          scalars: Optional[dict] = None) -> Tuple[Array, State]:
+    """One Adafactor step of one tensor; returns (new parameter, new state).
+
+    ``scalars``, if given, receives the step's per-tensor values: ``rho`` (the
+    relative or given step size), ``rms_x`` (with scale_parameter), ``alpha``
+    (the scaled step size), ``rms_u`` (RMS of the unclipped update) and ``kappa``
+    (the clip divisor max(1, RMS(u) / clip_threshold))."""
     h = adafactor_hparams(hp)
     if t < 1:
         raise ValueError("step must be >= 1")
@@ -264,8 +270,12 @@ def adafactor_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], 
     # Learning rate: relative step, scaled by the parameter's RMS before this
     # step's update (reading: the RMS is taken when the rate is computed).
     alpha = adafactor_step_size(h, t)
+    out = {} if scalars is None else scalars
+    out["rho"] = alpha
     if h["scale_parameter"]:
-        alpha *= max(eps2, rms(x))
+        out["rms_x"] = rms(x)
+        alpha *= max(eps2, out["rms_x"])
+    out["alpha"] = alpha
 
     b2 = adafactor_beta2t(h, t)
     q = g * g + eps1  # reading: eps1 enters with the squared gradient
@@ -283,7 +293,9 @@ def adafactor_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], 
         v_hat = v
     u = g / np.sqrt(v_hat)
     # RMS clipping (note after "Step 5"): divide by max(1, RMS(u) / clip_threshold).
-    u = u / max(1.0, rms(u) / h["clip_threshold"])
+    out["rms_u"] = rms(u)
+    out["kappa"] = max(1.0, out["rms_u"] / h["clip_threshold"])
+    u = u / out["kappa"]
     u = alpha * u
     if h["beta1"] is not None:
         # reading: the first moment averages the clipped, lr-scaled update.
@@ -344,9 +356,12 @@ def _factored_estimate(row: Array, col: Array) -> Array:
 
 
 def came_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int, *,
-                     param_bf16: bool = False, exp_avg_bf16: bool = False, exp_avg_i8: bool = False
-                     ) -> Tuple[Array, State]:
-    """One CAME step of one tensor; returns (new parameter, new state)."""
+                     param_bf16: bool = False, exp_avg_bf16: bool = False, exp_avg_i8: bool = False,
+                     scalars: Optional[dict] = None) -> Tuple[Array, State]:
+    """One CAME step of one tensor; returns (new parameter, new state).
+
+    ``scalars``, if given, receives ``rms_u`` (RMS of the unclipped update) and
+    ``kappa`` (the clip divisor)."""
     h = came_hparams(hp)
     if t < 1:
         raise ValueError("step must be >= 1")
@@ -373,7 +388,10 @@ def came_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
         new["exp_avg_sq"] = v
         v_hat = v
     u = g / np.sqrt(v_hat)
-    u = u / max(1.0, rms(u) / h["clip_threshold"])
+    out = {} if scalars is None else scalars
+    out["rms_u"] = rms(u)
+    out["kappa"] = max(1.0, out["rms_u"] / h["clip_threshold"])
+    u = u / out["kappa"]
 
     m = _moment_out(beta1 * _moment_in(state, exp_avg_i8) + (1.0 - beta1) * u, new, exp_avg_bf16, exp_avg_i8)
 
@@ -427,9 +445,12 @@ def lamb_init_state(shape: Tuple[int, ...], hp: Optional[dict] = None, *, exp_av
 
 
 def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: int, *,
-                     param_bf16: bool = False, exp_avg_bf16: bool = False, exp_avg_i8: bool = False
-                     ) -> Tuple[Array, State]:
-    """One LAMB step of one tensor (the whole tensor is one layer for the trust ratio)."""
+                     param_bf16: bool = False, exp_avg_bf16: bool = False, exp_avg_i8: bool = False,
+                     scalars: Optional[dict] = None) -> Tuple[Array, State]:
+    """One LAMB step of one tensor (the whole tensor is one layer for the trust ratio).
+
+    ``scalars``, if given, receives ``x_norm`` and ``d_norm`` (the 2-norms of the
+    parameter and of the update direction) and ``trust`` (the trust ratio)."""
     h = lamb_hparams(hp)
     if t < 1:
         raise ValueError("step must be >= 1")
@@ -452,6 +473,8 @@ def lamb_step_tensor(x: Array, g: Array, state: State, hp: Optional[dict], t: in
     d_norm = float(np.sqrt(np.sum(d * d)))
     # reading: identity scaling of the parameter norm; ratio 1 when either norm is 0.
     trust = x_norm / d_norm if (x_norm > 0.0 and d_norm > 0.0) else 1.0
+    if scalars is not None:
+        scalars.update(x_norm=x_norm, d_norm=d_norm, trust=trust)
     x_new = _stored(x - h["lr"] * trust * d, param_bf16)
     new["exp_avg_sq"] = v
     return x_new, new

@@ -2,6 +2,7 @@
 header declares, and validates arguments (codes and page messages) before any
 device work. No compute call is made, so these run without a GPU: validation
 only inspects pointers, never dereferences them."""
+import ctypes
 import json
 import os
 import re
@@ -411,3 +412,28 @@ def test_carry_calls_check_param_sumsq_first(lib):
     assert _code(_lib.meo_adafactor_step_carry, no_scale, 1, ps, gs, miss, True, None, 0)[0] == _lib.MEO_EWORKSPACE
     # the plain step ignores param_sumsq
     assert _code(_lib.meo_adafactor_step, hp, 1, ps, gs, miss, None, 0)[0] == _lib.MEO_EWORKSPACE
+
+
+@pytest.mark.parametrize("opt", ["adafactor", "came", "lamb"])
+def test_scalar_offsets(lib, opt):
+    """Each tensor with elements gets its own 8 slots inside the workspace the step
+    would use (256-byte aligned, no overlap); empty tensors get -1; bad arguments are
+    refused on the host."""
+    shapes = [(4, 8), (0, 5), (8,), (3, 70, 130), (), (1000, 1)]
+    ps, gs = _mk(shapes)
+    offs = getattr(_lib, f"meo_{opt}_scalar_offsets")(ps, gs)
+    ws_floats = getattr(_lib, f"meo_{opt}_workspace_size")(ps, gs) // 4
+    live = [o for o, s in zip(offs, shapes) if o >= 0]
+    assert [o < 0 for o in offs] == [torch.zeros(s).numel() == 0 for s in shapes]
+    assert all(o % 64 == 0 and o + len(_lib.SCALAR_SLOTS) <= ws_floats for o in live)
+    assert len(set(live)) == len(live)
+    spans = sorted((o, o + len(_lib.SCALAR_SLOTS)) for o in live)
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    fn = getattr(lib, f"meo_{opt}_scalar_offsets")
+    out = (ctypes.c_int64 * 2)()
+    assert fn(-1, None, out) == _lib.MEO_ESHAPE
+    assert fn(2, None, out) == _lib.MEO_ENULL
+    assert fn(0, None, None) == _lib.MEO_OK
+    bad = _lib._tensors(*_mk([(4, 8)]))
+    bad[0].rows = -3
+    assert fn(1, bad, out) == _lib.MEO_ESHAPE

@@ -87,7 +87,7 @@ def test_nan_gradient_stays_in_its_tensor(opt, hp):
     for k in range(1, len(SHAPES)):
         xk, _ = oracle.STEP_TENSOR[opt](run.ox[k], to64(gs[k]), run.ost[k], run.hp, 1)
         assert torch.isfinite(run.params[k]).all()
-        assert output_err("param", to64(run.params[k]), xk) <= TOL_F32
+        assert output_err("param", to64(run.params[k]), xk, x0=run.x0[k]) <= TOL_F32
 
 
 def test_mixed_gradient_dtypes_in_one_call():

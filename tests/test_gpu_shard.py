@@ -21,7 +21,7 @@ import torch
 import oracle
 import workloads
 from memory_efficient_optimizers_amd import _lib
-from tests.harness import TOL_F32, output_err, to64
+from tests.harness import TOL_F32, beta1_of, output_err, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -100,7 +100,9 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
             _lib.meo_adafactor_shard_stats_carry(hps, t, ps, gs, totals, sts, t > 1, part, ws)
         apply = _lib.meo_adafactor_shard_apply_carry
     ox = [to64(p) for p in full]
+    x0 = [x.copy() for x in ox]
     ost = [oracle.INIT_STATE[opt](tuple(p.shape), hp) for p in full]
+    b1 = beta1_of(opt, hp)
     for t in range(1, 4):
         gfull = workloads.grads(wl, t - 1, scales, "cuda")
         parts = []
@@ -126,6 +128,7 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
         for rk in ranks:
             apply(hps, t, rk["params"], rk["grads"], totals, rk["states"], reduced, rk["ws"])
         torch.cuda.synchronize()
+        ost_prev = ost
         ox, ost = oracle.STEP[opt](ox, [to64(g) for g in gfull], ost, hp, t)
         for k, spec in enumerate(wl.specs):
             fac = opt != "lamb" and len(spec.shape) >= 2
@@ -139,7 +142,7 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
                     return torch.cat(pieces, dim=-2)
                 return torch.cat([p.reshape(-1) for p in pieces]).reshape(spec.shape)
 
-            errs = {"param": output_err("param", to64(whole("param")), ox[k])}
+            errs = {"param": output_err("param", to64(whole("param")), ox[k], x0=x0[k])}
             for key in ost[k]:
                 if key in ("exp_avg_sq_col", "exp_avg_res_col"):
                     cols = [rk["states"][k][key] for rk, (r0, r1) in zip(ranks, ranges[k][0]) if r1 > r0]
@@ -147,7 +150,8 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
                         assert torch.equal(c, cols[0]), "ranks disagree on the column statistic"
                     errs[key] = output_err(key, to64(cols[0]), ost[k][key])
                 else:
-                    errs[key] = output_err(key, to64(whole(key)), ost[k][key])
+                    errs[key] = output_err(key, to64(whole(key)), ost[k][key],
+                                           prev=ost_prev[k].get(key) if key == "exp_avg" else None, beta1=b1)
             worst = max(errs, key=errs.get)
             print(f"  {opt}{' carry' if carry else ''} N={nranks} step {t} {spec.name} {tuple(spec.shape)}: "
                   f"worst {errs[worst]:.3e} ({worst})", flush=True)

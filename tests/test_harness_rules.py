@@ -1,8 +1,11 @@
 """CPU checks of the parity bars used by the GPU tests (tests/harness.py): the
 16-bit rules accept the one-step rounding disagreements that near-tie values may
 take, and reject systematic faults planted on the CPU (truncation instead of
-rounding to nearest, a skipped rounding, a wrong value in a tail)."""
+rounding to nearest, a skipped rounding, a wrong value in a tail); the step and
+scalar checks reject faults planted in a float32 replica of the step (a step size
+or clip divisor 0.1% off, LAMB's decay term dropped, its trust ratio 0.1% off)."""
 import numpy as np
+import pytest
 
 import oracle
 from tests.harness import TOL_F32, bar_kind, check_bar
@@ -82,3 +85,36 @@ def test_code_rules():
     shifted = np.clip(codes.astype(np.int16) + (rng.random(codes.size) < 0.2), -127, 127).astype(np.int8)
     assert not check_bar("codes", "exp_avg", (shifted, scales), ref)[0]
     assert not check_bar("codes", "exp_avg", (codes, scales * np.float32(1.03)), ref)[0]
+
+
+# Faults a kernel could make in the step itself, planted in the float32 replica
+# (tests/fp32_replica.py) on the CPU. Each must fail the named check on the weight
+# matrices. The step check dX catches them on its own, except CAME's clip divisor:
+# a factored CAME step M / sqrt(S) does not change when U is scaled (M and sqrt(S)
+# scale alike), so that fault shows in the first moment.
+@pytest.mark.parametrize("case,fault,check", [
+    ("adafactor_defaults", "alpha*1.001", "dx"),
+    ("adafactor_beta1", "alpha*1.001", "dx"),
+    ("adafactor_beta1", "kappa*1.001", "dx"),
+    ("came", "kappa*1.001", "exp_avg"),
+    ("lamb", "no_decay", "dx"),
+    ("lamb", "trust*1.001", "dx"),
+])
+def test_planted_step_faults_fail(case, fault, check):
+    from tests.test_tolerance_floors import CASES, replica_run
+    wl = CASES[case]
+    failed = {}
+    for t, k, res, _, _, _ in replica_run(wl, steps=3, fault=fault):
+        for key, v in res.items():
+            if not v[0]:
+                failed.setdefault(key, set()).add(wl.specs[k].kind)
+    assert "weight" in failed.get(check, ()), (case, fault, failed)
+
+
+def test_correct_replica_passes_planted_fault_cases():
+    """The same three steps without a fault pass every check (the faults above are
+    what fails, not the cases)."""
+    from tests.test_tolerance_floors import CASES, replica_run
+    for case in ("adafactor_defaults", "adafactor_beta1", "came", "lamb"):
+        for t, k, res, _, _, _ in replica_run(CASES[case], steps=3):
+            assert all(v[0] for v in res.values()), (case, t, k, {key: v for key, v in res.items() if not v[0]})
