@@ -47,10 +47,12 @@
  * - `workspace` is device scratch of at least meo_*_workspace_size() bytes,
  *   256-byte aligned, valid only while the enqueued work runs; no value is kept
  *   in it between calls.
- * - The library keeps a small cache of device-side launch tables keyed on the
- *   tensor list (shapes and pointers). Building a table allocates device memory
- *   and copies to it synchronously, once per distinct list;
- *   meo_release_plans() frees the cache.
+ * - The library keeps a cache of device-side launch tables keyed on the tensor
+ *   list (shapes and pointers), up to 64 lists. A call over a list that is not
+ *   cached allocates device memory for its tables (hipMalloc) and copies them
+ *   synchronously; past 64 lists the least recently used table is freed
+ *   (hipFree, which waits for the device). Calls over a cached list allocate
+ *   nothing. meo_release_plans() frees the cache.
  */
 #ifndef MEO_H
 #define MEO_H

@@ -435,7 +435,9 @@ struct Plan {
 
 std::mutex g_mu;
 std::list<Plan*> g_plans;  // most recently used first
-constexpr size_t kMaxPlans = 16;
+// Cached lists per kind (whole-tensor / row-sharded steps, GaLore). Evicting one frees
+// its device memory, which waits for the device.
+constexpr size_t kMaxPlans = 64;
 
 void free_plan(Plan* p) {
     int cur = 0;

@@ -21,7 +21,9 @@ tensor's initial parameter.
   (relative to |b_i|) plus the steps' relative errors, which add up on the scale
   of the accumulated change b - x0. For a weight that change is ~1e-2 of the
   weight; a parameter that starts at zero (a bias) *is* its accumulated change and
-  can cancel to near zero, where only that scale applies.
+  can cancel to near zero, where only that scale applies. GaLore's update has a
+  bar of its own, 1e-4 (bf16 matrix cores, N in two bf16 planes), so its
+  parameter takes 10 RMS(b - x0) there (``step_tol``).
 * the step itself, dX = X_new - X_old on each side (fp32 parameters; the
   library's from its own stored values, the oracle's in fp64):
   max_i max(0, |dXa_i - dXb_i| - s_i) / max(|dXb_i|, 0.1 RMS(dXb)) <= 1e-5, where
@@ -155,16 +157,19 @@ def ema_terms(b, prev, beta: float) -> np.ndarray:
     return np.abs(p) + np.abs(b - p)
 
 
-def output_errs(key: str, a, b, x0=None, prev=None, beta1=None) -> np.ndarray:
+def output_errs(key: str, a, b, x0=None, prev=None, beta1=None, step_tol: float = TOL_F32) -> np.ndarray:
     """Elementwise errors of one fp32 output under its bar (rules above). x0, the
-    initial parameter, sets the parameter's accumulated-change floor; prev and
-    beta1, the first moment's previous value and weight, its terms' floor."""
+    initial parameter, sets the parameter's accumulated-change floor, scaled by
+    step_tol / 1e-5 where the steps carry a bar of their own (GaLore's update,
+    1e-4 on bf16 matrix cores); prev and beta1, the first moment's previous value
+    and weight, its terms' floor."""
     if key in POSITIVE_KEYS:
         return floored_rel_errs(a, b, 0.0)
     if key == "param":
         scale = 0.0
         if x0 is not None:
-            scale = _rms(np.asarray(b, dtype=np.float64).reshape(-1) - np.asarray(x0, dtype=np.float64).reshape(-1))
+            scale = (step_tol / TOL_F32) * _rms(np.asarray(b, dtype=np.float64).reshape(-1)
+                                                - np.asarray(x0, dtype=np.float64).reshape(-1))
         return floored_rel_errs(a, b, FLOOR_PARAM, scale)
     if key == "exp_avg":
         scale = ema_terms(b, prev, beta1) if (prev is not None and beta1 is not None) else 0.0
@@ -277,7 +282,7 @@ def bar_kind(opt: str, hp: dict, storage: dict, key: str) -> str:
     return "f32"
 
 
-def check_bar(kind: str, key: str, a, b, x0=None, prev=None, beta1=None):
+def check_bar(kind: str, key: str, a, b, x0=None, prev=None, beta1=None, step_tol: float = TOL_F32):
     """(ok, max error, elements off the fp32 bar (or codes that differ), elements)
     of one output under its bar. For "codes", a and b are (codes, scales) pairs.
     fp32 bar: x0, the initial parameter, for the parameter's floor; prev and beta1
@@ -295,7 +300,7 @@ def check_bar(kind: str, key: str, a, b, x0=None, prev=None, beta1=None):
         over = int(np.count_nonzero(ca.astype(np.int64) != cb.astype(np.int64)))
         return err <= TOL_BF16 and over <= MAX_SHARE * e.size + MAX_EXTRA, err, over, e.size
     if kind == "f32":
-        e = output_errs(key, a, b, x0, prev, beta1)
+        e = output_errs(key, a, b, x0, prev, beta1, step_tol)
     else:
         e = floored_rel_errs(a, b, 0.0 if key in POSITIVE_KEYS else 1.0)
     err = float(np.max(e)) if e.size else 0.0

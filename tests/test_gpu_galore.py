@@ -56,8 +56,10 @@ def run_case(shapes, rank, t=5, hp=None, param_dtype=torch.float32, seed=0, chec
         checks = [(kind, "param", got_x, want_x),
                   ("f32", "exp_avg", to64(states[k]["exp_avg"]), want_s["exp_avg"]),
                   ("f32", "exp_avg_sq", to64(states[k]["exp_avg_sq"]), want_s["exp_avg_sq"])]
+        b1 = ga.galore_hparams(hpo)["betas"][0]
         for kd, key, a, b in checks:
-            ok, err, over, n = check_bar(kd, key, a, b)
+            ok, err, over, n = check_bar(kd, key, a, b, x0=x0[k], prev=s0[k]["exp_avg"], beta1=b1,
+                                         step_tol=TOL_UPDATE)
             if not ok:
                 bad.append(f"tensor {k} {shape} {key}: err {err:.3g} ({over}/{n} above 1e-5)")
         if param_dtype == torch.float32 and check_update:
@@ -226,7 +228,8 @@ def test_full_llama7b_sampled(param_dtype):
         for kd, key, a, b in [(kind, "param", got_x, want_x),
                               ("f32", "exp_avg", to64(states[k]["exp_avg"]), want_s["exp_avg"]),
                               ("f32", "exp_avg_sq", to64(states[k]["exp_avg_sq"]), want_s["exp_avg_sq"])]:
-            ok, err, over, n = check_bar(kd, key, a, b)
+            ok, err, over, n = check_bar(kd, key, a, b, x0=x0[k], prev=s0[k]["exp_avg"],
+                                         beta1=ga.galore_hparams(hp)["betas"][0], step_tol=TOL_UPDATE)
             print(f"  {names[k]} {key}: worst {err:.3g}", flush=True)
             if not ok:
                 bad.append(f"{names[k]} {key}: err {err:.3g} ({over}/{n} above the bar)")

@@ -145,10 +145,11 @@ def test_rejected_call_changes_nothing():
 
 
 def test_launch_table_cache_eviction():
-    """More distinct tensor lists than the cache holds, revisited: results stay exact."""
+    """More distinct tensor lists than the cache holds (64), revisited: results stay
+    exact."""
     outs = {}
     for rep in range(2):
-        for i in range(20):
+        for i in range(70):
             shape = (8 + i, 64 + 8 * i)
             wl = workloads.custom(f"ev{i}", "adafactor", [shape], hparams={"beta1": 0.9}, seed=i)
             run = Run(wl)
