@@ -52,7 +52,8 @@
  *   cached allocates device memory for its tables (hipMalloc) and copies them
  *   synchronously; past 64 lists the least recently used table is freed
  *   (hipFree, which waits for the device). Calls over a cached list allocate
- *   nothing. meo_release_plans() frees the cache.
+ *   nothing. meo_release_plans() frees the cache. meo_adafactor_step_noalloc
+ *   never allocates.
  */
 #ifndef MEO_H
 #define MEO_H
@@ -211,6 +212,31 @@ int    meo_adafactor_step_carry(const meo_adafactor_hparams* hp, int64_t step, i
                                 const meo_tensor* tensors, const meo_adafactor_state* states,
                                 int32_t param_sumsq_valid, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* The Adafactor step (meo_adafactor_step) for callers that cannot allocate device
+ * memory: code that runs under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. It takes no workspace and calls no hipMalloc, hipFree or
+ * other allocating routine: the launch tables and the workspace of the call live
+ * in a scratch array of MEO_NOALLOC_SCRATCH_BYTES that the library's code object
+ * holds on each GPU it runs on (allocated when the code is loaded on that GPU and
+ * kept until the process ends). The tables are built on the host (cached per
+ * distinct list in host memory) and copied into the scratch on `stream` before the
+ * passes; the same kernels then run in the same order, so the results are those
+ * of meo_adafactor_step, bit for bit.
+ *
+ * Limits: a list whose launch tables and workspace need more than
+ * MEO_NOALLOC_SCRATCH_BYTES is refused (MEO_EWORKSPACE) before anything runs; a
+ * Llama-7B decoder layer needs about 22 MB, the whole 7B list about 0.7 GB (use
+ * meo_adafactor_step for it). Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (on different streams, or from different threads
+ * before the earlier one's work has run) race and must be serialised by the
+ * caller. Nothing in the scratch is carried from one call to the next, and
+ * nothing in it needs to start at zero (every pass writes what a later pass
+ * reads). Arguments, validation, stream semantics and errors are otherwise as for
+ * meo_adafactor_step. */
+#define MEO_NOALLOC_SCRATCH_BYTES (64u << 20)
+int    meo_adafactor_step_noalloc(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
+                                  const meo_tensor* tensors, const meo_adafactor_state* states, void* stream);
 
 /* ----------------------------------------------------------------------- CAME */
 

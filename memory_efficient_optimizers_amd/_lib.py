@@ -43,7 +43,9 @@ EXPORTS = [
     "meo_galore_defaults", "meo_galore_rank", "meo_galore_workspace_size", "meo_galore_validate",
     "meo_galore_step", "meo_galore_refresh",
     "meo_adafactor_scalar_offsets", "meo_came_scalar_offsets", "meo_lamb_scalar_offsets",
+    "meo_adafactor_step_noalloc",
 ]
+MEO_NOALLOC_SCRATCH_BYTES = 64 << 20
 MEO_NUM_PASSES = 17
 
 
@@ -146,6 +148,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                              ctypes.POINTER(meo_adafactor_state), c_int32, c_void_p, c_size_t,
                                              c_void_p]
     lib.meo_adafactor_step_carry.restype = ctypes.c_int
+    lib.meo_adafactor_step_noalloc.argtypes = [ctypes.POINTER(meo_adafactor_hparams), c_int64, c_int32, T,
+                                               ctypes.POINTER(meo_adafactor_state), c_void_p]
+    lib.meo_adafactor_step_noalloc.restype = ctypes.c_int
     S = ctypes.POINTER(meo_shard)
     for opt, hp, st in (("adafactor", meo_adafactor_hparams, meo_adafactor_state),
                         ("lamb", meo_lamb_hparams, meo_lamb_state)):
@@ -426,6 +431,13 @@ def meo_adafactor_step_carry(hp, step, params, grads, states, param_sumsq_valid:
     _check(load().meo_adafactor_step_carry(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
                                            _states(meo_adafactor_state, ADAFACTOR_KEYS, states),
                                            1 if param_sumsq_valid else 0, ws, nb, _stream(stream)))
+
+
+def meo_adafactor_step_noalloc(hp, step, params, grads, states, stream=None) -> None:
+    """meo_adafactor_step without a workspace: the library's per-GPU scratch holds
+    the call's launch tables and workspace (at most MEO_NOALLOC_SCRATCH_BYTES)."""
+    _check(load().meo_adafactor_step_noalloc(ctypes.byref(hp), step, len(params), _tensors(params, grads, states),
+                                             _states(meo_adafactor_state, ADAFACTOR_KEYS, states), _stream(stream)))
 
 
 def meo_came_step(hp, step, params, grads, states, workspace=None, stream=None) -> None:

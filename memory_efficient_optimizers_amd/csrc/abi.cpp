@@ -971,6 +971,90 @@ int meo_adafactor_step_carry(const meo_adafactor_hparams* hp, int64_t step, int3
     return adafactor_step(hp, step, n, ts, st, param_sumsq_valid ? 1 : 0, ws, ws_bytes, stream);
 }
 
+// ----------------------------------------------------------------------------- no-allocation step
+
+// Scratch of meo_adafactor_step_noalloc: one call's launch tables followed by its
+// workspace. A file-scope device array, so the library never allocates it: each
+// GPU that loads this code holds its own copy until the process ends. Host code
+// must not pass the array's name to a kernel (it stands for a host-side shadow);
+// the device address of each GPU's copy comes from hipGetSymbolAddress.
+__device__ __align__(256) unsigned char scratch[MEO_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_na_mu;
+std::vector<void*> g_scratch_ptr;  // per device, filled on the first call on it
+// Host launch tables of recent lists (most recent first), for the no-allocation step.
+std::list<std::pair<std::vector<uint8_t>, HostPlan>> g_na_plans;
+constexpr size_t kMaxNaPlans = 16;
+
+// The device address of this device's scratch (looked up once per device, with the
+// device current). Call with g_na_mu held.
+void* scratch_of(int dev, int* rc) {
+    if (static_cast<size_t>(dev) >= g_scratch_ptr.size()) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            *rc = fail(MEO_EHIP, std::string("hipGetSymbolAddress of the scratch array failed: ") +
+                                     hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int meo_adafactor_step_noalloc(const meo_adafactor_hparams* hp, int64_t step, int32_t n, const meo_tensor* ts,
+                               const meo_adafactor_state* st, void* stream) {
+    int rc = meo_adafactor_validate(hp, step, n, ts, st);
+    if (rc) return rc;
+    if (n == 0) return MEO_OK;
+    const size_t ws_bytes = static_cast<size_t>(layout(kOpAdafactor, n, ts, nullptr)) * sizeof(float);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MEO_EHIP, "hipGetDevice failed");
+    const std::vector<StatePtrs> sp = state_ptrs(kOpAdafactor, n, st);
+    std::vector<uint8_t> key = plan_key(kOpAdafactor, n, ts, sp.data(), hp->has_beta1, dev, nullptr);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_na_mu);
+    auto it = g_na_plans.begin();
+    for (; it != g_na_plans.end(); ++it)
+        if (it->first == key) break;
+    if (it == g_na_plans.end()) {
+        HostPlan h;
+        rc = build_host_plan(kOpAdafactor, n, ts, sp.data(), hp->has_beta1, dev, nullptr, &h);
+        if (rc) return rc;
+        g_na_plans.emplace_front(std::move(key), std::move(h));
+        if (g_na_plans.size() > kMaxNaPlans) g_na_plans.pop_back();
+    } else if (it != g_na_plans.begin()) {
+        g_na_plans.splice(g_na_plans.begin(), g_na_plans, it);
+    }
+    const HostPlan& h = g_na_plans.front().second;
+    const size_t tbytes = (h.bytes.size() + 255) / 256 * 256;
+    if (tbytes + ws_bytes > MEO_NOALLOC_SCRATCH_BYTES)
+        return fail(MEO_EWORKSPACE, "this list needs " + std::to_string(tbytes + ws_bytes) +
+                                        " bytes of scratch (launch tables and workspace); "
+                                        "meo_adafactor_step_noalloc holds at most " +
+                                        std::to_string(static_cast<size_t>(MEO_NOALLOC_SCRATCH_BYTES)) +
+                                        " (meo_adafactor_step takes a workspace of any size)");
+    if (h.n == 0) return MEO_OK;
+    uint8_t* base = static_cast<uint8_t*>(scratch_of(dev, &rc));
+    if (!base) return rc;
+    // The tables go in on the stream, before the passes that read them. The host
+    // bytes stay in the cache; a pageable source is consumed before the call returns.
+    const hipError_t e = hipMemcpyAsync(base, h.bytes.data(), h.bytes.size(), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return fail(MEO_EHIP, std::string("launch table upload: ") + hipGetErrorString(e));
+    Plan view;
+    bind_plan(h, base, &view);
+    return adafactor_passes(hp, step, -1, view, reinterpret_cast<float*>(base + tbytes), s);
+}
+
+}  // extern "C"
+
 // ----------------------------------------------------------------------------- CAME
 
 void meo_came_defaults(meo_came_hparams* hp) {
