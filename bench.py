@@ -17,8 +17,9 @@ hipEvents on the stream (synchronised on both sides). One JSON line on stdout:
 * ``roofline``: the dominant pass (the apply pass for Adafactor), its algorithmic
   bytes per launch over its average duration, timed with hipEvents that the
   library records between its passes on the same stream during the timed steps.
-* ``cpu_baseline``: the fp64 oracle (single-threaded NumPy) on a bounded sample of
-  the same workload, one step, in parameters per second.
+* ``cpu_baseline``: the fp64 oracle stepping the whole list once on the host's
+  cores (one worker process per CPU, at most 16), in parameters per second, with
+  the CPU model, and a bounded single-thread sample beside it.
 
 Adafactor with scale_parameter steps through meo_adafactor_step_carry by default
 (``--param-sumsq carry``): each step's apply pass sums the squares of the
@@ -88,37 +89,94 @@ def algorithmic_bytes(wl) -> dict:
     return tot
 
 
-def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
-    """The fp64 oracle stepping the workload's tensors on the host, one tensor at a
-    time in list order (inputs drawn on the CPU, outside the timing), until about
-    `budget_s` seconds of oracle time: parameters stepped per second."""
+def _oracle_inputs(wl, k):
+    """Tensor k's parameter, gradient (step 0), state and storage flags, drawn on
+    the CPU (the same generators the tests use; not part of any timing)."""
     import torch
     import oracle
     import workloads
-
     from memory_efficient_optimizers_amd.optim import moment_dtype
-    hp = dict(wl.hparams)
-    done, spent, names = 0, 0.0, []
-    for k, spec in enumerate(wl.specs):
-        x = workloads.init_params(wl, "cpu", [k])[0].to(torch.float64).numpy()
-        sc = workloads.grad_scales(wl, "cpu", [k])
-        g = workloads.grads(wl, 0, sc, "cpu", [k])[0].to(torch.float64).numpy()
-        mdt = moment_dtype(wl.optimizer, spec.shape, wl.state_dtype, wl.param_dtype)
-        storage = dict(param_bf16=wl.param_dtype == torch.bfloat16, exp_avg_bf16=mdt == torch.bfloat16,
-                       exp_avg_i8=mdt == torch.int8)
-        st = oracle.INIT_STATE[wl.optimizer](x.shape, hp, exp_avg_i8=storage["exp_avg_i8"])
-        t0 = time.perf_counter()
-        oracle.STEP_TENSOR[wl.optimizer](x, g, st, hp, 1, **storage)
-        spent += time.perf_counter() - t0
+    spec = wl.specs[k]
+    x = workloads.init_params(wl, "cpu", [k])[0].to(torch.float64).numpy()
+    sc = workloads.grad_scales(wl, "cpu", [k])
+    g = workloads.grads(wl, 0, sc, "cpu", [k])[0].to(torch.float64).numpy()
+    mdt = moment_dtype(wl.optimizer, spec.shape, wl.state_dtype, wl.param_dtype)
+    storage = dict(param_bf16=wl.param_dtype == torch.bfloat16, exp_avg_bf16=mdt == torch.bfloat16,
+                   exp_avg_i8=mdt == torch.int8)
+    st = oracle.INIT_STATE[wl.optimizer](x.shape, dict(wl.hparams), exp_avg_i8=storage["exp_avg_i8"])
+    return x, g, st, storage
+
+
+def _oracle_tensor_job(job):
+    """One worker task: draw tensor k's inputs, then time one fp64 oracle step of
+    it. Returns (worker pid, k, elements, oracle seconds)."""
+    import oracle
+    import workloads
+    name, k = job
+    wl = workloads.WORKLOADS[name]
+    x, g, st, storage = _oracle_inputs(wl, k)
+    t0 = time.perf_counter()
+    oracle.STEP_TENSOR[wl.optimizer](x, g, st, dict(wl.hparams), 1, **storage)
+    return os.getpid(), k, x.size, time.perf_counter() - t0
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, single_budget_s: float = 15.0) -> dict:
+    """The fp64 oracle (plain NumPy, as it stands) stepping the workload on the host.
+
+    All cores: every tensor of the list, streamed tensor by tensor (largest first)
+    over one worker process per CPU this process may run on (at most 16, the
+    host share of one GPU); each worker draws a tensor's inputs on the CPU, then
+    times one oracle step of it. ``value`` is the list's parameters over the
+    longest per-worker sum of oracle seconds (the workers run side by side, so
+    the oracle work of the whole list takes that long); ``wall_s`` is the pool's
+    wall time including the draws. Single thread: the first tensors of the list in
+    order, in this process, until about ``single_budget_s`` seconds of oracle
+    time. Run before anything touches the GPU (the workers are fresh processes)."""
+    import multiprocessing
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    jobs = sorted(range(len(wl.specs)), key=lambda k: -wl.specs[k].numel)
+    t0 = time.perf_counter()
+    with multiprocessing.get_context("spawn").Pool(workers) as pool:
+        res = pool.map(_oracle_tensor_job, [(wl.name, k) for k in jobs], chunksize=1)
+    wall = time.perf_counter() - t0
+    per_worker: dict = {}
+    for pid, _, _, dt in res:
+        per_worker[pid] = per_worker.get(pid, 0.0) + dt
+    total = sum(n for _, _, n, _ in res)
+    makespan = max(per_worker.values())
+
+    import oracle
+    done, spent, count = 0, 0.0, 0
+    for k in range(len(wl.specs)):
+        x, g, st, storage = _oracle_inputs(wl, k)
+        t1 = time.perf_counter()
+        oracle.STEP_TENSOR[wl.optimizer](x, g, st, dict(wl.hparams), 1, **storage)
+        spent += time.perf_counter() - t1
         done += x.size
-        names.append(spec.name)
+        count += 1
         del x, g, st
-        if spent > budget_s:
+        if spent > single_budget_s:
             break
-    return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"one fp64 step of the first {len(names)} tensors of the same workload "
-                      f"({done} parameters, '{names[0]}' .. '{names[-1]}'), {spent:.1f} s of oracle time, "
-                      f"single-threaded NumPy"}
+    return {"value": total / makespan, "unit": "params/s", "cores": workers, "kind": "oracle",
+            "cpu": _cpu_model(), "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"one fp64 oracle step of every tensor of the workload ({len(res)} tensors, {total} "
+                      f"parameters), streamed tensor by tensor over {workers} worker processes; oracle seconds "
+                      f"per worker measured (longest {makespan:.1f} s), inputs drawn on the CPU outside them",
+            "wall_s": wall,
+            "single_thread": {"value": done / spent, "unit": "params/s", "cores": 1,
+                              "sample": f"the first {count} tensors of the list ({done} parameters, "
+                                        f"{done / total:.1%} of it), {spent:.1f} s of oracle time"}}
 
 
 def profile_traffic(kernel: str, workload: str):
@@ -181,6 +239,90 @@ def flat_views(torch, shapes, dtype, device):
         o += (n + align - 1) // align * align
     buf = torch.empty(max(o, 1), dtype=dtype, device=device)
     return [buf[a:a + n].view(s) for a, n, s in zip(offs, sizes, shapes)]
+
+
+# Which buffers go to which third of HBM (memory_efficient_optimizers_amd/hbm.py):
+# no pass may write two full-size streams into one third. Adafactor's apply writes
+# the parameter and the first moment; CAME's passes write one each; LAMB's moment
+# pass writes both moments. Index into the groups of chunks, largest first.
+THIRDS = {"adafactor": {"param": 0, "exp_avg": 1, "grad": 2},
+          "came": {"param": 0, "exp_avg": 1, "grad": 2},
+          "lamb": {"exp_avg": 0, "exp_avg_sq": 1, "param": 2, "grad": 2}}
+
+
+def thirds_buffers(torch, _lib, wl, mdts, beta1, dev, same_third_copy=False):
+    """Parameters, gradients and states of the workload placed by HBM third: the
+    device's free memory is taken as 2 GiB chunks, each chunk's third found by the
+    timing probe, and each full-size kind packed into chunks of its own third (the
+    small statistics are ordinary allocations). With ``same_third_copy`` a second
+    first moment is packed into the parameter's third too, to time the layout the
+    placement avoids. Returns (params, grads, states, placement record, extra first
+    moment or None); unused chunks are freed."""
+    from memory_efficient_optimizers_amd import hbm
+    shapes = [s.shape for s in wl.specs]
+    proto = [_lib.state_shapes(wl.optimizer, s, beta1=beta1, i8=m == torch.int8) for s, m in zip(shapes, mdts)]
+    big = {"param": [(k, shapes[k], wl.param_dtype) for k in range(len(shapes))],
+           "grad": [(k, shapes[k], wl.grad_dtype) for k in range(len(shapes))],
+           "exp_avg": [(k, shapes[k], mdts[k]) for k in range(len(shapes)) if "exp_avg" in proto[k]]}
+    if wl.optimizer == "lamb":
+        big["exp_avg_sq"] = [(k, shapes[k], torch.float32) for k in range(len(shapes))]
+    pool = hbm.ChunkPool(torch, dev)
+    groups = pool.classify(_lib)
+    need = {kind: hbm.chunks_needed([math.prod(s) * torch.empty((), dtype=d).element_size() for _, s, d in items])
+            for kind, items in big.items()}
+    plan = THIRDS[wl.optimizer]
+    mode = "thirds"
+    if groups is None or len(groups) < 2:
+        groups, mode = [list(range(len(pool.chunks)))], "allocation order"
+    taken = {g: 0 for g in range(len(groups))}
+    chunk_ids = {}
+    order = sorted(big, key=lambda kind: plan.get(kind, 0))
+    if same_third_copy and "exp_avg" in big:
+        order.append("exp_avg_same_third")
+        need["exp_avg_same_third"] = need["exp_avg"]
+    for kind in order:
+        g = plan.get("exp_avg" if kind == "exp_avg_same_third" else kind, 0)
+        if kind == "exp_avg_same_third":
+            g = plan["param"]
+        g = min(g, len(groups) - 1)
+        if taken[g] + need[kind] > len(groups[g]):  # not enough room in that third: any other
+            g = max(range(len(groups)), key=lambda i: len(groups[i]) - taken[i])
+        chunk_ids[kind] = groups[g][taken[g]:taken[g] + need[kind]]
+        taken[g] += need[kind]
+        if len(chunk_ids[kind]) < need[kind]:
+            raise RuntimeError(f"not enough device memory for the {kind} buffers")
+    views = {kind: pool.views(chunk_ids[kind], [s for _, s, _ in big["exp_avg" if kind == "exp_avg_same_third"
+                                                                    else kind]],
+                              [d for _, _, d in big["exp_avg" if kind == "exp_avg_same_third" else kind]])
+             for kind in chunk_ids}
+    where = {c: k for k, grp in enumerate(groups) for c in grp}
+    record = {"mode": mode, "chunk_gib": hbm.CHUNK // hbm.GiB, "chunks": len(pool.chunks),
+              "groups": [len(g) for g in groups], "probe_apply_ms": pool.probe_ms,
+              "third_of": {kind: sorted({where[c] for c in ids}) for kind, ids in chunk_ids.items()}}
+    pool.release([c for ids in chunk_ids.values() for c in ids])
+    params = [None] * len(shapes)
+    grads = [None] * len(shapes)
+    states = [dict() for _ in shapes]
+    for kind, items in big.items():
+        for (k, _, _), v in zip(items, views[kind]):
+            if kind == "param":
+                params[k] = v
+            elif kind == "grad":
+                grads[k] = v
+            else:
+                states[k][kind] = v
+    for k, st in enumerate(proto):
+        for key, shp in st.items():
+            if key not in states[k]:
+                states[k][key] = torch.zeros(shp, dtype=torch.float32, device=dev)
+        for v in states[k].values():
+            v.zero_()
+    extra = None
+    if "exp_avg_same_third" in views:
+        extra = [None] * len(shapes)
+        for (k, _, _), v in zip(big["exp_avg"], views["exp_avg_same_third"]):
+            extra[k] = v.zero_()
+    return params, grads, states, record, extra
 
 
 def copy_calibration(torch, args) -> int:
@@ -484,8 +626,10 @@ def main() -> int:
     ap.add_argument("--workload", default="adafactor_llama7b",
                     help="a workload of workloads.py, or galore_llama7b / galore_llama7b_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--layout", choices=["flat", "separate"], default="flat",
-                    help="flat: one buffer per kind of tensor (default); separate: one allocation per tensor")
+    ap.add_argument("--layout", choices=["thirds", "flat", "separate"], default="thirds",
+                    help="thirds: each kind of full-size buffer in 2 GiB chunks of its own third of HBM, "
+                         "found by a timing probe (default); flat: one buffer per kind of tensor, in "
+                         "allocation order; separate: one allocation per tensor")
     ap.add_argument("--shard-ranks", type=int, default=0,
                     help="instead of the whole step: time one rank's share of a row-sharded step over N ranks "
                          "(the all-reduces of the partial sums between the calls are not part of it)")
@@ -508,6 +652,13 @@ def main() -> int:
     from memory_efficient_optimizers_amd import _lib
     from memory_efficient_optimizers_amd.optim import moment_dtype
 
+    # The CPU leg first: its worker processes start before this process touches
+    # the GPU.
+    cpu = None
+    if (not args.no_cpu_baseline and not args.copy_calibration and args.workload not in GALORE_WORKLOADS
+            and args.shard_ranks <= 1):
+        cpu = cpu_baseline(workloads.WORKLOADS[args.workload])
+
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
@@ -526,7 +677,14 @@ def main() -> int:
     hp = dict(wl.hparams)
     beta1 = hp.get("beta1") is not None
     mdts = [moment_dtype(wl.optimizer, s.shape, wl.state_dtype, wl.param_dtype) for s in wl.specs]
-    if args.layout == "flat":
+    placement, m_same = None, None
+    if args.layout == "thirds":
+        params, grads, states, placement, m_same = thirds_buffers(
+            torch, _lib, wl, mdts, beta1 or wl.optimizer != "adafactor", dev,
+            same_third_copy=wl.optimizer == "adafactor" and beta1)
+        workloads.init_params(wl, dev, out=params)
+        workloads.grads(wl, 0, workloads.grad_scales(wl, dev), dev, out=grads)
+    elif args.layout == "flat":
         # One flat buffer per kind (parameters, gradients, each state), tensors as
         # 256-byte aligned views, as flat-parameter training frameworks keep them.
         shapes = [s.shape for s in wl.specs]
@@ -593,6 +751,20 @@ def main() -> int:
         read["measured_step_bytes"] = r_meas
         read["measured_frac"] = None if r_meas is None else r_meas / (read["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBPS
 
+    if m_same is not None:
+        # The plain step (RMS(X) read, as read_param_sumsq) with the first moment in
+        # the parameter's third instead: the layout the placement avoids. Its apply
+        # kernel is the plain one, so it stays apart from the carry apply's launches
+        # in a kernel trace.
+        sts2 = [dict(st, exp_avg=m) if m is not None else st for st, m in zip(states, m_same)]
+        t, _, s_total, s_passes = timed(_lib.PreparedStep(wl.optimizer, hps, params, grads, sts2, ws), t)
+        placement["plain_step_exp_avg_in_param_third"] = {
+            "ms_per_step": s_total / args.steps,
+            "apply_ms": s_passes["adafactor_apply"]["ms"] / s_passes["adafactor_apply"]["launches"]}
+        if read is not None:
+            placement["plain_step"] = {"ms_per_step": read["ms_per_step"],
+                                       "apply_ms": read["passes_ms_per_step"]["adafactor_apply"]}
+
     ab = algorithmic_bytes(wl)
     step_gbps = ab["step"] / (ms_step / 1e3) / 1e9
     dominant = max((k for k in passes if k in ab), key=lambda k: passes[k]["ms"])  # the apply pass
@@ -635,8 +807,11 @@ def main() -> int:
     }
     if read is not None:
         out["read_param_sumsq"] = read
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl)
+    if placement is not None:
+        placement["apply_ms"] = avg_ms
+        out["placement"] = placement
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     return 0
 

@@ -520,6 +520,40 @@ struct HostPlan {
     int32_t storage = kStoreF32;
 };
 
+// Deals whole tensors (runs of items with one tensor index) to the 8 XCD queues,
+// largest first onto the least loaded queue, then interleaves the queues so that
+// block i runs on XCD i % 8: every tile of a tensor runs on one XCD, whose L2
+// then fetches that tensor's shared operands once. Empty items (x = -1) pad the
+// shorter queues.
+void xcd_deal(std::vector<int2>& items) {
+    std::vector<std::pair<size_t, size_t>> runs;
+    for (size_t i = 0; i < items.size();) {
+        size_t j = i;
+        while (j < items.size() && items[j].x == items[i].x) ++j;
+        if (items[i].x >= 0) runs.push_back({i, j});
+        i = j;
+    }
+    std::vector<size_t> order(runs.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
+        return runs[a].second - runs[a].first > runs[b].second - runs[b].first;
+    });
+    std::vector<std::vector<int2>> q(kXcds);
+    for (size_t r : order) {
+        size_t best = 0;
+        for (size_t x = 1; x < q.size(); ++x)
+            if (q[x].size() < q[best].size()) best = x;
+        q[best].insert(q[best].end(), items.begin() + runs[r].first, items.begin() + runs[r].second);
+    }
+    size_t longest = 0;
+    for (const auto& v : q) longest = std::max(longest, v.size());
+    std::vector<int2> out;
+    out.reserve(longest * kXcds);
+    for (size_t r = 0; r < longest; ++r)
+        for (int x = 0; x < kXcds; ++x) out.push_back(r < q[x].size() ? q[x][r] : make_int2(-1, -1));
+    items.swap(out);
+}
+
 // Builds the launch tables of a list on the host (no device memory is touched or
 // allocated); first checks every pointer of the list against its allocation.
 // `shards` (row-sharded steps; else null): the whole tensors' sizes.
@@ -1878,27 +1912,26 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
         const int id = static_cast<int>(i);
         const int64_t pt = ceil_div(d.D, kGaProjRows);
         for (int64_t y = 0; y < pt; ++y) lists[is_left ? kGaProjL : kGaProjR].push_back(make_int2(id, static_cast<int>(y)));
-        // Back-projection tiles, XCD-aligned: blocks go to the 8 XCDs in turn, so
-        // the blocks that read one tile of N (a row tile for m >= n, a column tile
-        // for m < n) are placed 8 apart and share one L2. The tensor starts at a
-        // multiple of 8; empty items (x = -1) fill the gaps.
+        // Back-projection tiles, tile rows of N outer and tiles of U inner, so
+        // that consecutive blocks share a tile of N; xcd_deal below then puts the
+        // whole tensor on one XCD.
         std::vector<int2>& L = lists[is_left ? kGaBackL : kGaBackR];
         const int64_t ti_n = is_left ? ceil_div(d.m, kGaWide) : ceil_div(d.m, kGaTile * kGaBackRW);
         const int64_t na = is_left ? d.btj : ti_n;   // tiles of N
         const int64_t nb = is_left ? ti_n : d.btj;   // tiles of U
-        while (L.size() % 8) L.push_back(make_int2(-1, 0));
-        for (int64_t g = 0; g < ceil_div(na, 8); ++g)
-            for (int64_t b = 0; b < nb; ++b)
-                for (int64_t x = 0; x < 8; ++x) {
-                    const int64_t a = 8 * g + x;
-                    if (a >= na) {
-                        L.push_back(make_int2(-1, 0));
-                        continue;
-                    }
-                    const int64_t ti = is_left ? b : a, tj = is_left ? a : b;
-                    L.push_back(make_int2(id, static_cast<int>(ti * d.btj + tj)));
-                }
+        for (int64_t a = 0; a < na; ++a)
+            for (int64_t b = 0; b < nb; ++b) {
+                const int64_t ti = is_left ? b : a, tj = is_left ? a : b;
+                L.push_back(make_int2(id, static_cast<int>(ti * d.btj + tj)));
+            }
     }
+    // Every tile of a tensor on one XCD: its L2 then fetches the tensor's projector
+    // and low-rank arrays once (measured on the 7B list: projection -0.8%,
+    // back-projection -2.4%).
+    xcd_deal(lists[kGaProjR]);
+    xcd_deal(lists[kGaProjL]);
+    xcd_deal(lists[kGaBackR]);
+    xcd_deal(lists[kGaBackL]);
     size_t offs[kGaListCount];
     size_t total = (gd.size() * sizeof(GDesc) + 255) / 256 * 256;
     const size_t foff = total;

@@ -195,6 +195,7 @@ __global__ __launch_bounds__(kThreads, Direct ? 4 : (kGaProjRB == 1 ? 3 : 2)) vo
     uint16_t* sa = arena;
     uint16_t* sb = arena + kGaProjRows * kPitch;
     const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;  // an empty item of the XCD-dealt list (the whole block)
     const GDesc d = t.desc[it.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t i0 = static_cast<int64_t>(it.y) * kGaProjRows;
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
     uint16_t* sl = arena + kBackN * kPitch;       // N, low plane
     uint16_t* su = arena + 2 * kBackN * kPitch;   // U rows
     const int2 it = t.items[blockIdx.x];
-    if (it.x < 0) return;  // an empty item of the XCD-aligned list
+    if (it.x < 0) return;  // an empty item of the XCD-dealt list
     const GDesc d = t.desc[it.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ug = wave & 3, ng = wave >> 2;  // the wave's 64-row groups of U and of N
