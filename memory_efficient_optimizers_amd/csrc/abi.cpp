@@ -1615,7 +1615,7 @@ struct GaPlan {
     const int2* items[kGaListCount] = {};
     int64_t count[kGaListCount] = {};
     bool back_direct[2] = {false, false};  // back-projection staged by global_load_lds (right, left)
-    bool proj_direct = false;              // m >= n projection staged by global_load_lds
+    bool proj_direct[2] = {false, false};  // projection staged by global_load_lds (right, left)
 };
 std::list<GaPlan*> g_ga_plans;  // most recently used first, under g_mu
 
@@ -1906,11 +1906,14 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
     // Right descriptors first, then left; the item tables index that array.
     std::vector<GDesc> gd(right);
     gd.insert(gd.end(), left.begin(), left.end());
+    bool proj_direct[2] = {true, true};  // right, left
+    for (const GDesc& d : right) proj_direct[0] = proj_direct[0] && d.vec && d.d % kGaKb == 0;
+    for (const GDesc& d : left) proj_direct[1] = proj_direct[1] && d.vec && d.d % kGaKb == 0;
     for (size_t i = 0; i < gd.size(); ++i) {
         const GDesc& d = gd[i];
         const bool is_left = i >= right.size();
         const int id = static_cast<int>(i);
-        const int64_t pt = ceil_div(d.D, kGaProjRows);
+        const int64_t pt = ceil_div(d.D, proj_direct[is_left] ? kGaPwRows : kGaProjRows);
         for (int64_t y = 0; y < pt; ++y) lists[is_left ? kGaProjL : kGaProjR].push_back(make_int2(id, static_cast<int>(y)));
         // Back-projection tiles, tile rows of N outer and tiles of U inner, so
         // that consecutive blocks share a tile of N; xcd_deal below then puts the
@@ -1959,8 +1962,8 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
         for (const GDesc& d : v) ok = ok && d.vec && d.r % kGaKb == 0;
         p->back_direct[side] = ok;
     }
-    p->proj_direct = true;
-    for (const GDesc& d : right) p->proj_direct = p->proj_direct && d.vec && d.d % kGaKb == 0;
+    p->proj_direct[0] = proj_direct[0];
+    p->proj_direct[1] = proj_direct[1];
     if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
         hipMemcpy(p->mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
         if (p->mem) (void)hipFree(p->mem);
@@ -2095,8 +2098,8 @@ int meo_galore_step(const meo_galore_hparams* hp, int64_t step, int32_t n, const
              static_cast<float>(hp->eps), static_cast<float>(1.0 - hp->lr * hp->weight_decay),
              static_cast<float>(hp->lr * hp->scale)};
     PassTimer pt(s);
-    launch_galore_project(GTable{p->gdesc, p->items[kGaProjR]}, p->count[kGaProjR], a, false, p->proj_direct, s);
-    launch_galore_project(GTable{p->gdesc, p->items[kGaProjL]}, p->count[kGaProjL], a, true, false, s);
+    launch_galore_project(GTable{p->gdesc, p->items[kGaProjR]}, p->count[kGaProjR], a, false, p->proj_direct[0], s);
+    launch_galore_project(GTable{p->gdesc, p->items[kGaProjL]}, p->count[kGaProjL], a, true, p->proj_direct[1], s);
     pt.mark(kPassGaProject);
     launch_galore_back(GTable{p->gdesc, p->items[kGaBackR]}, p->count[kGaBackR], a, false, p->back_direct[0], s);
     launch_galore_back(GTable{p->gdesc, p->items[kGaBackL]}, p->count[kGaBackL], a, true, p->back_direct[1], s);

@@ -11,6 +11,8 @@ constexpr int kGaPitch = kGaKb + 8;  // bf16 per LDS row (padding against bank c
 constexpr int kGaProjRB = 1;       // projection tile: 64 kGaProjRB rows of R per block
 constexpr int kGaProjRows = kGaTile * kGaProjRB;
 constexpr int kGaBackRW = 1;      // back-projection tile: 64 kGaBackRW rows of N per block
+constexpr int kGaPwRows = 256;    // wide projection (direct lists): rows of R per block
+constexpr int kGaPwThreads = 512; // wide projection: 8 waves
 
 // One projected (2-D, bf16-gradient) tensor. With m >= n (right side) the low-rank
 // arrays are [m][r] and the projector spans the columns' space (d = n); with m < n
@@ -46,8 +48,9 @@ struct GaArgs {
     float coef;                      // lr * scale (projected) or lr (flat)
 };
 
-// direct (m >= n lists only): every tensor has d % kGaKb == 0 and 16-byte rows
-// (vec); its operands are then staged by global_load_lds.
+// direct: every tensor of the list has d % kGaKb == 0 and 16-byte rows (vec); the
+// list's items are then tiles of kGaPwRows rows of R for the wide kernel, whose
+// operands are staged by global_load_lds. Otherwise items are kGaProjRows-row tiles.
 void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s);
 // direct: every tensor of the list has rank % kGaKb == 0 and 16-byte rows (vec); its
 // operands are then staged by global_load_lds.

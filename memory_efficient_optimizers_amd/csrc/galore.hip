@@ -11,10 +11,11 @@
 //
 // so the low-rank arrays are always [max(m, n)][r]. Two kernels per step:
 //
-//   k_galore_project  R = X U with X = G (m >= n) or G^T (m < n), bf16 MFMA with
-//                     fp32 accumulation, one 64-row tile of R per block and the
-//                     whole contraction in the block (no split partials); the
-//                     epilogue runs AdamW on the tile: moments updated in place,
+//   k_galore_project_wide / k_galore_project
+//                     R = X U with X = G (m >= n) or G^T (m < n), bf16 MFMA with
+//                     fp32 accumulation, one 256-row (wide) or 64-row tile of R
+//                     per block and the whole contraction in the block (no split
+//                     partials); the epilogue runs AdamW on the tile: moments updated in place,
 //                     direction N = m_hat / (sqrt(v_hat) + eps) written as two
 //                     bf16 planes (high part and the remainder) so that the back
 //                     projection keeps ~16 significant bits of N on bf16 MFMA.
@@ -24,8 +25,10 @@
 //
 // The projector is kept in bf16 (the gradient's type) both as U [d][r] and as
 // U^T [r][d], so every operand is read with the contraction index contiguous.
-// The only transposed read is G in the m < n projection, which is staged through
-// LDS. Non-projected tensors take a flat AdamW kernel (k_galore_adamw).
+// The only transposed read is G in the m < n projection: the wide kernel stages
+// G's rows as they lie and reads them with the LDS transpose read; the
+// register-staged kernel scatters them transposed into LDS. Non-projected
+// tensors take a flat AdamW kernel (k_galore_adamw).
 #include "galore.h"
 
 #include <type_traits>
@@ -154,11 +157,14 @@ __device__ __forceinline__ void ep_gather(const float* lw, int lane, int q, floa
 // Direct staging: rows of 64 bf16 (128 bytes, unpadded) written straight from
 // global memory into LDS by global_load_lds (no registers), 8 rows per
 // instruction: lane l fills row (l >> 3) of the group at 16-byte slot (l & 7),
-// which holds the row's chunk (l & 7) ^ (row & 7). Reading chunk c of row w at
-// slot c ^ (w & 7) keeps the 8 rows of a fragment read on 8 different slots (no
-// bank conflict), as the padding does for the register path. Rows past the
-// operand's end read its last row: they only reach outputs that are not stored.
+// which holds the row's chunk (l & 7) ^ sw_row(row). A fragment read (16 lanes per
+// LDS cycle on 64 banks: 16 consecutive rows, one chunk each) then finds rows r and
+// r + 8 on different slots as well as the 8 rows of each parity: no bank conflict
+// (with sw_row(r) = r & 7 alone rows r and r + 8 collided, which doubled the LDS
+// cycles of the projection). Rows past the operand's end read its last row: they
+// only reach outputs that are not stored.
 constexpr int kDirectPitch = kGaKb;  // bf16 per LDS row
+__device__ __forceinline__ int sw_row(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 template <int ROWS, int THREADS = kThreads>
 __device__ __forceinline__ void stage_direct(const uint16_t* g, int64_t nrows, int64_t cols, int64_t r0, int k0,
                                              uint16_t* dst, int wave, int lane) {
@@ -166,7 +172,7 @@ __device__ __forceinline__ void stage_direct(const uint16_t* g, int64_t nrows, i
     for (int j = wave; j < ROWS / 8; j += THREADS / 64) {
         const int rr = 8 * j + (lane >> 3);
         const int64_t row = min(r0 + rr, nrows - 1);
-        const int c = (lane & 7) ^ (rr & 7);
+        const int c = (lane & 7) ^ sw_row(rr);
         const uint16_t* src = g + row * cols + k0 + c * 8;
         __builtin_amdgcn_global_load_lds((const MEO_GLOBAL void*)src,
                                          (__attribute__((address_space(3))) void*)(dst + 8 * j * kDirectPitch),
@@ -175,21 +181,68 @@ __device__ __forceinline__ void stage_direct(const uint16_t* g, int64_t nrows, i
 }
 
 __device__ __forceinline__ bfv8 ld_frag_sw(const uint16_t* base, int row, int kk) {
-    return *reinterpret_cast<const bfv8*>(base + row * kDirectPitch + (((kk >> 3) ^ (row & 7)) << 3));
+    return *reinterpret_cast<const bfv8*>(base + row * kDirectPitch + (((kk >> 3) ^ sw_row(row)) << 3));
 }
 
 
-template <bool Left, bool Direct>
-// Tile: kGaProjRows rows of R x all r columns; wave w holds columns 64w .. 64w + 63.
-// With 64-row tiles, 3 waves per SIMD: 13% faster on the 7B list than the 2 that
-// the registers would otherwise allow, with no spills. Direct (m >= n lists whose
-// contraction length is a multiple of kGaKb): both operands staged by
-// global_load_lds into an unpadded swizzled arena, no staging registers.
-__global__ __launch_bounds__(kThreads, Direct ? 4 : (kGaProjRB == 1 ? 3 : 2)) void k_galore_project(GTable t,
-                                                                                                   GaArgs a) {
-    static_assert(!(Direct && Left), "the m < n projection reads G transposed through registers");
+__device__ __forceinline__ void galore_adamw8(const GDesc& d, const GaArgs& a, int64_t row, int col, const float* rv) {
+    float m[8], v[8], nh[8], nl[8];
+    const int64_t idx = row * d.r + col;
+    const bool full = d.rvec && col + 8 <= d.r;
+    if (full) {
+        const f32x4 m0 = *gld<f32x4>(d.em + idx), m1 = *gld<f32x4>(d.em + idx + 4);
+        const f32x4 v0 = *gld<f32x4>(d.ev + idx), v1 = *gld<f32x4>(d.ev + idx + 4);
+        m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w; m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
+        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            m[e] = col + e < d.r ? *gld<float>(d.em + idx + e) : 0.0f;
+            v[e] = col + e < d.r ? *gld<float>(d.ev + idx + e) : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        m[e] = fmaf(a.beta1, m[e], a.omb1 * rv[e]);
+        v[e] = fmaf(a.beta2, v[e], a.omb2 * (rv[e] * rv[e]));
+        const float n = (m[e] * a.inv_bc1) / (sqrtf(v[e] * a.inv_bc2) + a.eps);
+        nh[e] = round_bf16(n);
+        nl[e] = n - nh[e];
+    }
+    if (full) {
+        *gst<f32x4>(d.em + idx) = f32x4{m[0], m[1], m[2], m[3]};
+        *gst<f32x4>(d.em + idx + 4) = f32x4{m[4], m[5], m[6], m[7]};
+        *gst<f32x4>(d.ev + idx) = f32x4{v[0], v[1], v[2], v[3]};
+        *gst<f32x4>(d.ev + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (col + e < d.r) {
+                *gst<float>(d.em + idx + e) = m[e];
+                *gst<float>(d.ev + idx + e) = v[e];
+            }
+    }
+    if (d.vec && col + 8 <= d.r) {  // the planes are 256-byte aligned; rows of r % 8 == 0
+        *gst<u32x4>(d.nh + idx) = pack_bf16x8(nh);
+        *gst<u32x4>(d.nl + idx) = pack_bf16x8(nl);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (col + e < d.r) {
+                *gst<uint16_t>(d.nh + idx + e) = static_cast<uint16_t>(bf16_bits(nh[e]));
+                *gst<uint16_t>(d.nl + idx + e) = static_cast<uint16_t>(bf16_bits(nl[e]));
+            }
+    }
+}
+
+// Register-staged projection, for lists the wide kernel does not take (a
+// contraction length that is not a multiple of kGaKb, or rows without 16-byte
+// alignment). Tile: kGaProjRows rows of R x all r columns; wave w holds columns
+// 64w .. 64w + 63. With 64-row tiles, 3 waves per SIMD.
+template <bool Left>
+__global__ __launch_bounds__(kThreads, kGaProjRB == 1 ? 3 : 2) void k_galore_project(GTable t, GaArgs a) {
     constexpr int kRB = 2 * kGaProjRB;  // 32-row blocks of a wave's tile
-    constexpr int kPitch = Direct ? kDirectPitch : kGaPitch;
+    constexpr int kPitch = kGaPitch;
     __shared__ __attribute__((aligned(16))) uint16_t arena[(kGaProjRows + kGaWide) * kPitch];
     static_assert((kGaProjRows + kGaWide) * kPitch * 2 >= kWaves * kEpWave * 4, "exchange space");
     uint16_t* sa = arena;
@@ -222,39 +275,23 @@ __global__ __launch_bounds__(kThreads, Direct ? 4 : (kGaProjRB == 1 ? 3 : 2)) vo
             const int kk = ks + 8 * (lane >> 5);
             bfv8 fa[kRB], fb[2];
 #pragma unroll
-            for (int ib = 0; ib < kRB; ++ib) {
-                if constexpr (Direct) fa[ib] = ld_frag_sw(sa, ib * 32 + (lane & 31), kk);
-                else fa[ib] = ld_frag(sa + (ib * 32 + (lane & 31)) * kGaPitch + kk);
-            }
+            for (int ib = 0; ib < kRB; ++ib) fa[ib] = ld_frag(sa + (ib * 32 + (lane & 31)) * kGaPitch + kk);
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                if constexpr (Direct) fb[jb] = ld_frag_sw(sb, wave * 64 + jb * 32 + (lane & 31), kk);
-                else fb[jb] = ld_frag(sb + (wave * 64 + jb * 32 + (lane & 31)) * kGaPitch + kk);
-            }
+            for (int jb = 0; jb < 2; ++jb) fb[jb] = ld_frag(sb + (wave * 64 + jb * 32 + (lane & 31)) * kGaPitch + kk);
 #pragma unroll
             for (int ib = 0; ib < kRB; ++ib)
 #pragma unroll
                 for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma32(fa[ib], fb[jb], acc[ib][jb]);
         }
     };
-    if constexpr (Direct) {
-        for (int64_t k0 = 0; k0 < d.d; k0 += kGaKb) {
-            stage_direct<kGaProjRows>(d.g, d.D, d.d, i0, static_cast<int>(k0), sa, wave, lane);
-            stage_direct<kGaWide>(d.ut, d.r, d.d, 0, static_cast<int>(k0), sb, wave, lane);
-            __syncthreads();  // the loads have landed (each wave waits for its own first)
-            multiply();
-            __syncthreads();
-        }
-    } else {
-        fetch(0);
-        for (int64_t k0 = 0; k0 < d.d; k0 += kGaKb) {
-            pa.store(sa);
-            pb.store(sb);
-            __syncthreads();
-            if (k0 + kGaKb < d.d) fetch(k0 + kGaKb);
-            multiply();
-            __syncthreads();
-        }
+    fetch(0);
+    for (int64_t k0 = 0; k0 < d.d; k0 += kGaKb) {
+        pa.store(sa);
+        pb.store(sb);
+        __syncthreads();
+        if (k0 + kGaKb < d.d) fetch(k0 + kGaKb);
+        multiply();
+        __syncthreads();
     }
     if (!active) return;
     // AdamW on the tile of R, rows of 8 columns per lane (see ep_spill): moments
@@ -268,54 +305,161 @@ __global__ __launch_bounds__(kThreads, Direct ? 4 : (kGaProjRB == 1 ? 3 : 2)) vo
             const int64_t row = i0 + ib * 32 + (lane >> 3) + 8 * q;
             const int col = wave * 64 + (lane & 7) * 8;
             if (row >= d.D || col >= d.r) continue;
-            float rv[8], m[8], v[8], nh[8], nl[8];
+            float rv[8];
             ep_gather(lw, lane, q, rv);
-            const int64_t idx = row * d.r + col;
-            const bool full = d.rvec && col + 8 <= d.r;
-            if (full) {
-                const f32x4 m0 = *gld<f32x4>(d.em + idx), m1 = *gld<f32x4>(d.em + idx + 4);
-                const f32x4 v0 = *gld<f32x4>(d.ev + idx), v1 = *gld<f32x4>(d.ev + idx + 4);
-                m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w; m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
-                v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w; v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-            } else {
+            galore_adamw8(d, a, row, col, rv);
+        }
+    }
+}
+
+
+// Wide projection (lists whose contraction length is a multiple of kGaKb and
+// whose rows allow 16-byte loads): a 256-row x r tile of R per block of 8 waves,
+// wave w at rows 128 (w / 4) and columns 64 (w % 4), one block per CU. The G and
+// U^T blocks of one contraction step (64 long) go by global_load_lds into one of
+// two LDS stages (separate arrays, so that the compiler tells the stages apart and
+// waits only for the stage being read): step k + 1 is in flight while step k is
+// multiplied. Every wave issues exactly kPwDma transfers per stage, so waiting
+// until at most kPwDma are outstanding means the older stage has landed. Against
+// the 64-row tile of k_galore_project, each U^T block serves 4x the rows: its L2
+// reads per row drop 4x, and the projection of the Llama-7B-shaped list ran
+// 6.32 -> 5.11 ms (both sides), with bitwise the same results.
+constexpr int kPwDma = 2 * kGaPwRows / 8 / (kGaPwThreads / 64);   // 8
+// One stage: the G block and the U^T block of the contraction step at k0 (64
+// columns of the contraction each), 256 rows each, by global_load_lds.
+//   m >= n: G rows i0 .. i0 + 255 (rows of R), contraction along G's rows: the
+//           swizzled 64-column layout that ld_frag_sw reads.
+//   m < n:  G rows k0 .. k0 + 63 (the contraction runs down G's columns),
+//           columns i0 .. i0 + 255 (rows of R): 64 LDS rows of 256 (512 bytes),
+//           whose 16-byte chunk c sits at position c ^ (4 (row & 3)); instruction j
+//           fills rows 2j and 2j + 1. ld_frag_tr reads it transposed.
+template <bool Left>
+__device__ __forceinline__ void pw_stage(const GDesc& d, int64_t i0, int k0, uint16_t* sa, uint16_t* sb, int wave,
+                                         int lane) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    m[e] = col + e < d.r ? *gld<float>(d.em + idx + e) : 0.0f;
-                    v[e] = col + e < d.r ? *gld<float>(d.ev + idx + e) : 0.0f;
-                }
+    for (int i = 0; i < kGaPwRows / 8 / (kGaPwThreads / 64); ++i) {
+        const int j = wave + i * (kGaPwThreads / 64);
+        const int rr = 8 * j + (lane >> 3);
+        const int c = (lane & 7) ^ sw_row(rr);
+        if constexpr (Left) {
+            const int kr = 2 * j + (lane >> 5);
+            const int64_t cc = min(i0 / 8 + ((lane & 31) ^ ((kr & 3) << 2)), static_cast<int64_t>(d.D) / 8 - 1);
+            __builtin_amdgcn_global_load_lds((const MEO_GLOBAL void*)(d.g + (k0 + kr) * static_cast<int64_t>(d.D) + cc * 8),
+                                             (__attribute__((address_space(3))) void*)(sa + j * 512), 16, 0, 0);
+        } else {
+            const int64_t ra = min(i0 + rr, static_cast<int64_t>(d.D) - 1);
+            __builtin_amdgcn_global_load_lds((const MEO_GLOBAL void*)(d.g + ra * d.d + k0 + c * 8),
+                                             (__attribute__((address_space(3))) void*)(sa + 8 * j * kDirectPitch), 16, 0, 0);
+        }
+        const int64_t rb = min(rr, d.r - 1);
+        __builtin_amdgcn_global_load_lds((const MEO_GLOBAL void*)(d.ut + rb * d.d + k0 + c * 8),
+                                         (__attribute__((address_space(3))) void*)(sb + 8 * j * kDirectPitch), 16, 0, 0);
+    }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// MFMA A fragment of rows r0 .. r0 + 31 of R at contraction offset ks from the
+// transposed G stage (m < n), by LDS transpose reads: within each 16-lane group the
+// read hands lane i the i-th 16-bit element of each of the 4 rows that lanes
+// 4e + (i >> 2) address, so lanes 4e + q point at row kbase + e, columns
+// cbase + 4q .. + 3 and lane i receives column cbase + i at rows kbase .. kbase + 3.
+// Lane l (group g = l >> 4) gets row r0 + (l & 31) at contraction rows
+// ks + 8 (l >> 5) .. + 7, as the MFMA wants; two reads give the 8.
+__device__ __forceinline__ bfv8 ld_frag_tr(const uint16_t* sa, int r0, int ks, int lane) {
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+    const int col = r0 + 16 * (g & 1) + 4 * q;
+    const int kr = ks + 8 * (g >> 1) + e;
+    const int off = (((col >> 3) ^ (e << 2)) << 3) + (col & 7);  // (kr & 3) == e for both reads
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(sa + kr * 256 + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(sa + (kr + 4) * 256 + off));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bfv8, v);
+}
+
+#define MEO_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((n) | (7 << 4) | (15 << 8))
+
+template <bool Left>
+__global__ __launch_bounds__(kGaPwThreads, 1) void k_galore_project_wide(GTable t, GaArgs a) {
+    static_assert(kPwDma == 8, "wait counts below");
+    __shared__ __attribute__((aligned(16))) uint16_t a0[kGaPwRows * kDirectPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t b0[kGaWide * kDirectPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t a1[kGaPwRows * kDirectPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t b1[kGaWide * kDirectPitch];
+    const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;
+    const GDesc d = t.desc[it.x];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rg = wave >> 2, cg = wave & 3;
+    const int64_t i0 = static_cast<int64_t>(it.y) * kGaPwRows;
+    const bool active = cg * 64 < d.r;
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.0f;
+    auto multiply = [&](const uint16_t* sa, const uint16_t* sb) {
+        if (!active) return;
+#pragma unroll
+        for (int ks = 0; ks < kGaKb; ks += 16) {
+            const int kk = ks + 8 * (lane >> 5);
+            bfv8 fa[4], fb[2];
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                if constexpr (Left) fa[ib] = ld_frag_tr(sa, rg * 128 + ib * 32, ks, lane);
+                else fa[ib] = ld_frag_sw(sa, rg * 128 + ib * 32 + (lane & 31), kk);
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                m[e] = fmaf(a.beta1, m[e], a.omb1 * rv[e]);
-                v[e] = fmaf(a.beta2, v[e], a.omb2 * (rv[e] * rv[e]));
-                const float n = (m[e] * a.inv_bc1) / (sqrtf(v[e] * a.inv_bc2) + a.eps);
-                nh[e] = round_bf16(n);
-                nl[e] = n - nh[e];
-            }
-            if (full) {
-                *gst<f32x4>(d.em + idx) = f32x4{m[0], m[1], m[2], m[3]};
-                *gst<f32x4>(d.em + idx + 4) = f32x4{m[4], m[5], m[6], m[7]};
-                *gst<f32x4>(d.ev + idx) = f32x4{v[0], v[1], v[2], v[3]};
-                *gst<f32x4>(d.ev + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
-            } else {
+            for (int jb = 0; jb < 2; ++jb) fb[jb] = ld_frag_sw(sb, cg * 64 + jb * 32 + (lane & 31), kk);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (col + e < d.r) {
-                        *gst<float>(d.em + idx + e) = m[e];
-                        *gst<float>(d.ev + idx + e) = v[e];
-                    }
-            }
-            if (d.vec && col + 8 <= d.r) {  // the planes are 256-byte aligned; rows of r % 8 == 0
-                *gst<u32x4>(d.nh + idx) = pack_bf16x8(nh);
-                *gst<u32x4>(d.nl + idx) = pack_bf16x8(nl);
-            } else {
+            for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (col + e < d.r) {
-                        *gst<uint16_t>(d.nh + idx + e) = static_cast<uint16_t>(bf16_bits(nh[e]));
-                        *gst<uint16_t>(d.nl + idx + e) = static_cast<uint16_t>(bf16_bits(nl[e]));
-                    }
-            }
+                for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma32(fa[ib], fb[jb], acc[ib][jb]);
+        }
+    };
+    // Every stage issues its transfers unconditionally (past the last step it
+    // fetches the last block again), so that each wait below is the same count.
+    const int nk = d.d / kGaKb, last = nk - 1;
+    pw_stage<Left>(d, i0, 0, a0, b0, wave, lane);
+    pw_stage<Left>(d, i0, min(1, last) * kGaKb, a1, b1, wave, lane);
+    MEO_WAIT_VM(8);
+    __builtin_amdgcn_s_barrier();
+    multiply(a0, b0);
+    __builtin_amdgcn_s_barrier();
+    for (int kb = 1; kb < nk; kb += 2) {
+        pw_stage<Left>(d, i0, min(kb + 1, last) * kGaKb, a0, b0, wave, lane);  // stage 1 holds step kb
+        MEO_WAIT_VM(8);
+        __builtin_amdgcn_s_barrier();
+        multiply(a1, b1);
+        __builtin_amdgcn_s_barrier();
+        if (kb + 1 >= nk) break;
+        pw_stage<Left>(d, i0, min(kb + 2, last) * kGaKb, a1, b1, wave, lane);  // stage 0 holds step kb + 1
+        MEO_WAIT_VM(8);
+        __builtin_amdgcn_s_barrier();
+        multiply(a0, b0);
+        __builtin_amdgcn_s_barrier();
+    }
+    MEO_WAIT_VM(0);  // every wave's last, repeated transfers land before the LDS is reused
+    __builtin_amdgcn_s_barrier();
+    if (!active) return;
+    uint16_t* ex = wave < 3 ? a0 : (wave < 6 ? b0 : a1);
+    float* lw = reinterpret_cast<float*>(ex) + (wave % 3) * kEpWave;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+        ep_spill(acc[ib][0], acc[ib][1], lw, lane);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t row = i0 + rg * 128 + ib * 32 + (lane >> 3) + 8 * q;
+            const int col = cg * 64 + (lane & 7) * 8;
+            if (row >= d.D || col >= d.r) continue;
+            float rv[8];
+            ep_gather(lw, lane, q, rv);
+            galore_adamw8(d, a, row, col, rv);
         }
     }
 }
@@ -323,9 +467,10 @@ __global__ __launch_bounds__(kThreads, Direct ? 4 : (kGaProjRB == 1 ? 3 : 2)) vo
 void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s) {
     if (n <= 0) return;
     const dim3 grid(static_cast<uint32_t>(n)), block(kThreads);
-    if (left) hipLaunchKernelGGL((k_galore_project<true, false>), grid, block, 0, s, t, a);
-    else if (direct) hipLaunchKernelGGL((k_galore_project<false, true>), grid, block, 0, s, t, a);
-    else hipLaunchKernelGGL((k_galore_project<false, false>), grid, block, 0, s, t, a);
+    if (direct && left) hipLaunchKernelGGL((k_galore_project_wide<true>), grid, dim3(kGaPwThreads), 0, s, t, a);
+    else if (direct) hipLaunchKernelGGL((k_galore_project_wide<false>), grid, dim3(kGaPwThreads), 0, s, t, a);
+    else if (left) hipLaunchKernelGGL(k_galore_project<true>, grid, block, 0, s, t, a);
+    else hipLaunchKernelGGL(k_galore_project<false>, grid, block, 0, s, t, a);
 }
 
 // ------------------------------------------------------------------ back-projection + update

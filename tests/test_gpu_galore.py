@@ -79,8 +79,12 @@ def run_case(shapes, rank, t=5, hp=None, param_dtype=torch.float32, seed=0, chec
     ((300, 136), 40),     # ragged rows, r not a multiple of 32
     ((72, 333), 24),      # ragged, odd columns: element-wise loads
     ((200, 96), 13),      # r not a multiple of 8
-    ((200, 192), 13),     # direct-staged projection: ragged rows, r not a multiple of 8
-    ((1000, 256), 100),   # direct-staged projection: second wave partly past r
+    ((200, 192), 13),     # wide projection: ragged rows, r not a multiple of 8, 3 contraction steps
+    ((1000, 256), 100),   # wide projection: second column wave partly past r
+    ((300, 64), 64),      # wide projection: a single contraction step
+    ((128, 328), 64),     # m < n wide projection (transpose reads): ragged last tile of 72 rows
+    ((192, 1000), 100),   # m < n wide projection: 3 contraction steps, a wave partly past r
+    ((64, 296), 32),      # m < n wide projection: a single contraction step
     ((40, 24), 256),      # rank clamped to min(m, n)
     ((512, 384), 256),    # full rank-256 tile, several contraction blocks
     ((300, 600), 256),    # m < n at rank 256
@@ -131,12 +135,14 @@ def test_list_equals_singles():
 
 
 def test_direct_staging_equals_register_staging():
-    """The staging path is chosen per list: direct (global_load_lds) when every
-    contraction length of the list is a multiple of 64, through registers otherwise.
-    Both put the same values in LDS and run the same MFMA sequence, so a tensor's
-    step is bitwise the same on either. (256, 128) and (128, 320) at rank 64 take the
-    direct paths alone and the register paths beside (200, 40) and (40, 200), whose
-    rank 40 and contraction length 40 are not multiples of 64."""
+    """The kernels are chosen per list: the wide projection and the direct-staged
+    back-projection (global_load_lds) when every contraction length of the list is
+    a multiple of 64, the register-staged ones otherwise. All feed the MFMAs the
+    same fragments in the same order (the m < n wide projection through LDS
+    transpose reads), so a tensor's step is bitwise the same on either. (256, 128)
+    and (128, 320) at rank 64 take the wide and direct kernels alone and the
+    register-staged ones beside (200, 40) and (40, 200), whose rank 40 and
+    contraction length 40 are not multiples of 64."""
     shapes = [(256, 128), (200, 40), (128, 320), (40, 200)]
     dev = "cuda"
     h = _lib.galore_hparams(lr=0.05, rank=64)
