@@ -403,24 +403,48 @@ __global__ __launch_bounds__(kGaPwThreads, 1) void k_galore_project_wide(GTable 
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[ib][jb][v] = 0.0f;
+    // Fragments of sub-step ks + 16 are read while sub-step ks is multiplied.
     auto multiply = [&](const uint16_t* sa, const uint16_t* sb) {
         if (!active) return;
-#pragma unroll
-        for (int ks = 0; ks < kGaKb; ks += 16) {
+        bfv8 fa[2][4], fb[2][2];
+        auto load = [&](int ks, int buf) {
             const int kk = ks + 8 * (lane >> 5);
-            bfv8 fa[4], fb[2];
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
-                if constexpr (Left) fa[ib] = ld_frag_tr(sa, rg * 128 + ib * 32, ks, lane);
-                else fa[ib] = ld_frag_sw(sa, rg * 128 + ib * 32 + (lane & 31), kk);
+                if constexpr (Left) fa[buf][ib] = ld_frag_tr(sa, rg * 128 + ib * 32, ks, lane);
+                else fa[buf][ib] = ld_frag_sw(sa, rg * 128 + ib * 32 + (lane & 31), kk);
             }
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) fb[jb] = ld_frag_sw(sb, cg * 64 + jb * 32 + (lane & 31), kk);
+            for (int jb = 0; jb < 2; ++jb) fb[buf][jb] = ld_frag_sw(sb, cg * 64 + jb * 32 + (lane & 31), kk);
+        };
+        load(0, 0);
+#pragma unroll
+        for (int s4 = 0; s4 < kGaKb / 16; ++s4) {
+            if (s4 + 1 < kGaKb / 16) load((s4 + 1) * 16, (s4 + 1) & 1);
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-                for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma32(fa[ib], fb[jb], acc[ib][jb]);
+                for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma32(fa[s4 & 1][ib], fb[s4 & 1][jb], acc[ib][jb]);
         }
+        // Schedule (the compiler otherwise waits for each sub-step's reads before its
+        // MFMAs, leaving the SIMD idle): the first sub-step's LDS reads, then each
+        // later sub-step's reads one by one between the 8 MFMAs of the current one
+        // (m < n: 10 reads, two transpose reads per A fragment; the last two follow
+        // the MFMAs). Right side, Llama-7B list: 3.95 -> 3.75 ms.
+        constexpr int kReads = Left ? 10 : 6;
+        constexpr int kPaired = kReads < 8 ? kReads : 8;
+        __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // 0x100: LDS reads
+#pragma unroll
+        for (int s4 = 0; s4 + 1 < kGaKb / 16; ++s4) {
+#pragma unroll
+            for (int r = 0; r < kPaired; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 0x008: MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if (8 > kPaired) __builtin_amdgcn_sched_group_barrier(0x008, 8 - kPaired, 0);
+            if (kReads > kPaired) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kPaired, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
     // Every stage issues its transfers unconditionally (past the last step it
     // fetches the last block again), so that each wait below is the same count.
