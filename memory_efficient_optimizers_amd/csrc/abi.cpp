@@ -1614,7 +1614,7 @@ struct GaPlan {
     const RDesc* rdesc = nullptr;
     const int2* items[kGaListCount] = {};
     int64_t count[kGaListCount] = {};
-    bool back_direct[2] = {false, false};  // back-projection staged by global_load_lds (right, left)
+    int back_mode[2] = {kBackReg, kBackReg};  // back-projection kernel (BackMode), right and left
     bool proj_direct[2] = {false, false};  // projection staged by global_load_lds (right, left)
 };
 std::list<GaPlan*> g_ga_plans;  // most recently used first, under g_mu
@@ -1903,6 +1903,23 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
             for (int64_t i = 0; i < ceil_div(numel, kFlatTile); ++i) lists[kGaFlat].push_back(make_int2(id, static_cast<int>(i)));
         }
     }
+    // Back-projection kernel per side (see BackMode): the U-register kernel when every
+    // rank is a multiple of kGaKb, rows allow 16-byte access and all parameters share
+    // a dtype; its items cover 256 rows of U x up to kUrTiles tiles of N.
+    int back_mode[2] = {kBackReg, kBackReg};
+    for (int side = 0; side < 2; ++side) {
+        const std::vector<GDesc>& v = side ? left : right;
+        bool direct = true, all_f32 = true, all_bf16 = true;
+        for (const GDesc& d : v) {
+            direct = direct && d.vec && d.r % kGaKb == 0;
+            all_f32 = all_f32 && !d.xbf16;
+            all_bf16 = all_bf16 && d.xbf16;
+        }
+        back_mode[side] = !direct ? kBackReg : all_f32 ? kBackUr : all_bf16 ? kBackUrBf16 : kBackDirect;
+    }
+    for (int side = 0; side < 2; ++side)
+        if (back_mode[side] == kBackUr || back_mode[side] == kBackUrBf16)
+            for (GDesc& d : side ? left : right) d.btj = static_cast<int32_t>(ceil_div(ceil_div(d.D, kGaTile), kUrTiles));
     // Right descriptors first, then left; the item tables index that array.
     std::vector<GDesc> gd(right);
     gd.insert(gd.end(), left.begin(), left.end());
@@ -1915,10 +1932,17 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
         const int id = static_cast<int>(i);
         const int64_t pt = ceil_div(d.D, proj_direct[is_left] ? kGaPwRows : kGaProjRows);
         for (int64_t y = 0; y < pt; ++y) lists[is_left ? kGaProjL : kGaProjR].push_back(make_int2(id, static_cast<int>(y)));
+        std::vector<int2>& L = lists[is_left ? kGaBackL : kGaBackR];
+        if (back_mode[is_left] == kBackUr || back_mode[is_left] == kBackUrBf16) {
+            // chunks of N outer, bands of U inner: consecutive items share N's rows
+            const int64_t bands = ceil_div(d.d, kGaWide);
+            for (int64_t c = 0; c < d.btj; ++c)
+                for (int64_t b = 0; b < bands; ++b) L.push_back(make_int2(id, static_cast<int>(b * d.btj + c)));
+            continue;
+        }
         // Back-projection tiles, tile rows of N outer and tiles of U inner, so
         // that consecutive blocks share a tile of N; xcd_deal below then puts the
         // whole tensor on one XCD.
-        std::vector<int2>& L = lists[is_left ? kGaBackL : kGaBackR];
         const int64_t ti_n = is_left ? ceil_div(d.m, kGaWide) : ceil_div(d.m, kGaTile * kGaBackRW);
         const int64_t na = is_left ? d.btj : ti_n;   // tiles of N
         const int64_t nb = is_left ? ti_n : d.btj;   // tiles of U
@@ -1955,13 +1979,8 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
     GaPlan* p = new GaPlan;
     p->key = std::move(key);
     p->device = dev;
-    // Direct staging needs whole contraction blocks and 16-byte rows everywhere.
-    for (int side = 0; side < 2; ++side) {
-        const std::vector<GDesc>& v = side ? left : right;
-        bool ok = true;
-        for (const GDesc& d : v) ok = ok && d.vec && d.r % kGaKb == 0;
-        p->back_direct[side] = ok;
-    }
+    p->back_mode[0] = back_mode[0];
+    p->back_mode[1] = back_mode[1];
     p->proj_direct[0] = proj_direct[0];
     p->proj_direct[1] = proj_direct[1];
     if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
@@ -2101,8 +2120,8 @@ int meo_galore_step(const meo_galore_hparams* hp, int64_t step, int32_t n, const
     launch_galore_project(GTable{p->gdesc, p->items[kGaProjR]}, p->count[kGaProjR], a, false, p->proj_direct[0], s);
     launch_galore_project(GTable{p->gdesc, p->items[kGaProjL]}, p->count[kGaProjL], a, true, p->proj_direct[1], s);
     pt.mark(kPassGaProject);
-    launch_galore_back(GTable{p->gdesc, p->items[kGaBackR]}, p->count[kGaBackR], a, false, p->back_direct[0], s);
-    launch_galore_back(GTable{p->gdesc, p->items[kGaBackL]}, p->count[kGaBackL], a, true, p->back_direct[1], s);
+    launch_galore_back(GTable{p->gdesc, p->items[kGaBackR]}, p->count[kGaBackR], a, false, p->back_mode[0], s);
+    launch_galore_back(GTable{p->gdesc, p->items[kGaBackL]}, p->count[kGaBackL], a, true, p->back_mode[1], s);
     pt.mark(kPassGaBack);
     a.coef = static_cast<float>(hp->lr);
     launch_galore_adamw(Table{p->fdesc, p->items[kGaFlat], nullptr}, p->count[kGaFlat], a, s);

@@ -52,9 +52,14 @@ struct GaArgs {
 // list's items are then tiles of kGaPwRows rows of R for the wide kernel, whose
 // operands are staged by global_load_lds. Otherwise items are kGaProjRows-row tiles.
 void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s);
-// direct: every tensor of the list has rank % kGaKb == 0 and 16-byte rows (vec); its
-// operands are then staged by global_load_lds.
-void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s);
+// Back-projection kernels. kBackReg: operands staged through registers (any list).
+// kBackDirect: 64 x 256 tiles staged by global_load_lds (every rank a multiple of kGaKb,
+// 16-byte rows). kBackUr / kBackUrBf16: as direct, with U held in registers and items of
+// 256 rows of U x up to kUrTiles 64-row tiles of N (item y = band * btj + chunk); every
+// parameter of the list fp32 (kBackUr) or bf16 (kBackUrBf16).
+enum BackMode { kBackReg = 0, kBackDirect = 1, kBackUr = 2, kBackUrBf16 = 3 };
+constexpr int kUrTiles = 64;  // 64-row tiles of N per item of the U-register back-projection
+void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, int mode, hipStream_t s);
 void launch_galore_adamw(const Table& t, int64_t n, const GaArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------------ projector refresh

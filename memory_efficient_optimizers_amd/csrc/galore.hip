@@ -19,9 +19,11 @@
 //                     direction N = m_hat / (sqrt(v_hat) + eps) written as two
 //                     bf16 planes (high part and the remainder) so that the back
 //                     projection keeps ~16 significant bits of N on bf16 MFMA.
-//   k_galore_back     W <- W (1 - lr wd) - lr scale (N U^T or U N^T): two bf16
+//   k_galore_back_ur / k_galore_back
+//                     W <- W (1 - lr wd) - lr scale (N U^T or U N^T): two bf16
 //                     MFMAs per fragment (high and low plane), the parameter tile
-//                     read and written once.
+//                     read and written once; the U-register kernel keeps a 256-row
+//                     block of U in registers and walks up to 64 tiles of N.
 //
 // The projector is kept in bf16 (the gradient's type) both as U [d][r] and as
 // U^T [r][d], so every operand is read with the contraction index contiguous.
@@ -380,7 +382,9 @@ __device__ __forceinline__ bfv8 ld_frag_tr(const uint16_t* sa, int r0, int ks, i
     return __builtin_bit_cast(bfv8, v);
 }
 
-#define MEO_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((n) | (7 << 4) | (15 << 8))
+// s_waitcnt with only the vector-memory count (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maxima).
+#define MEO_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 template <bool Left>
 __global__ __launch_bounds__(kGaPwThreads, 1) void k_galore_project_wide(GTable t, GaArgs a) {
@@ -721,9 +725,276 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
     }
 }
 
-void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s) {
+
+// Back-projection with the U block in registers (lists whose rank is a multiple of
+// kGaKb and whose rows allow 16-byte loads). An item is 256 rows of U (a band of W's
+// columns for m >= n, of its rows for m < n) and up to kUrTiles consecutive 64-row
+// tiles of N. The block's 8 waves (wave w: U rows 32 w, all 64 rows of a tile's N)
+// load their U fragments for the whole rank once, 64 VGPRs; then per tile
+// only N's planes are staged, by global_load_lds, into one of two LDS buffers (64 KB
+// each: rows of 256, chunk c of row w at c ^ (w & 15)), the next tile's while the
+// current one is multiplied. The parameter part of tile i + 1 is loaded right after
+// tile i's stores, so it has tile i + 1's contraction to land; the wait before a tile
+// leaves exactly the newer N stage, those stores and those loads outstanding. Against
+// the direct-staged 64 x 256 tiles (3 blocks per CU, U staged per tile) the L2 bytes
+// staged per tile fall from 192 KB to 64 KB: Llama-7B list, fp32 parameters, 13.55 ->
+// 12.57 ms (bf16 10.2 -> 9.95 ms), results bitwise the same. The parameter stream (one
+// read and one write of W) bounds it: without the MFMAs the m >= n pass takes 8.6 of
+// its 9.8 ms, about the rate of a plain read-write copy.
+constexpr int kUrN = kGaTile;           // rows of N per tile
+constexpr int kUrNDma = 2 * kUrN * (kGaWide / 8) / 64 / 8;  // 16-byte transfers per wave per tile: 8
+// A wave's 32 x 32 exchange block in LDS, unpadded: row r at row r ^ ((r >> 2) & 1), its
+// 16-byte chunk c at chunk c ^ ((r >> 1) & 1), so that neither the accumulator spill
+// (rows r and r + 4 at once) nor the 8-column gather (rows 4k .. 4k + 3) hits a bank twice.
+__device__ __forceinline__ int ur_ex(int r, int col) {
+    return ((r ^ ((r >> 2) & 1)) << 5) + ((((col >> 2) ^ ((r >> 1) & 1))) << 2) + (col & 3);
+}
+
+__device__ __forceinline__ void ur_stage(const GDesc& d, int64_t n0, uint16_t* buf, int wave, int lane) {
+    // instruction j: rows 2j, 2j + 1 of one plane (plane = j / 32), 32 chunks each
+#pragma unroll
+    for (int i = 0; i < kUrNDma; ++i) {
+        const int j = wave + 8 * i;                 // 0 .. 63
+        const int plane = j >> 5, jr = j & 31;
+        const int row = 2 * jr + (lane >> 5);       // 0 .. 63
+        const int c = (lane & 31) ^ (row & 15);     // global chunk held at position lane & 31
+        const int cc = min(c, d.r / 8 - 1);
+        const int64_t grow = min(n0 + row, static_cast<int64_t>(d.D) - 1);
+        const uint16_t* src = (plane ? d.nl : d.nh) + grow * d.r + cc * 8;
+        __builtin_amdgcn_global_load_lds((const MEO_GLOBAL void*)src,
+                                         (__attribute__((address_space(3))) void*)(buf + j * 512), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ bfv8 ur_frag(const uint16_t* plane, int row, int kk) {
+    return *reinterpret_cast<const bfv8*>(plane + row * 256 + ((((kk >> 3) ^ (row & 15))) << 3));
+}
+
+template <bool Left, bool XB>
+__global__ __launch_bounds__(512, 1) void k_galore_back_ur(GTable t, GaArgs a) {
+    static_assert(kUrNDma == 8, "wait counts below");
+    constexpr int kP = XB ? 4 : 8;  // 16-byte parameter loads (and stores) per lane per tile
+    __shared__ __attribute__((aligned(16))) uint16_t nb0[2 * kUrN * 256];
+    __shared__ __attribute__((aligned(16))) uint16_t nb1[2 * kUrN * 256];
+    __shared__ __attribute__((aligned(16))) float exb[8 * 32 * 32];
+    const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;  // an empty item of the XCD-dealt list
+    const GDesc d = t.desc[it.x];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nc = d.btj;  // chunks of kUrTiles tiles per band
+    const int band = it.y / nc, chunk = it.y % nc;
+    const int64_t u0 = static_cast<int64_t>(band) * kGaWide;
+    const int64_t nt0 = static_cast<int64_t>(chunk) * kUrTiles;
+    const int ntiles = static_cast<int>(min<int64_t>(kUrTiles, (d.D + kUrN - 1) / kUrN - nt0));
+    const int nks = d.r / 16;  // 16-wide contraction sub-steps
+    using PT = typename std::conditional<XB, uint16_t, float>::type;
+    PT* const x = static_cast<PT*>(d.x);
+    // U fragments of the wave's 32 rows for the whole rank (64 VGPRs), landed before the
+    // pipeline starts so that no wait inside it has to cover them
+    bfv8 uf[16];
+    {
+        const int64_t row = min(u0 + wave * 32 + (lane & 31), static_cast<int64_t>(d.d) - 1);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const int k = min(ks, nks - 1) * 16 + 8 * (lane >> 5);
+            uf[ks] = __builtin_bit_cast(bfv8, *gld<u32x4>(d.u + row * d.r + k));
+        }
+    }
+    MEO_WAIT_VM(0);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) __asm__ volatile("" : "+v"(uf[ks]));
+    // W cells of the wave: two 32 x 32 blocks (blk: the tile's 32-row halves of N); in
+    // block blk, lane holds rows (lane >> 2) + 16 q (q < 2), columns 8 (lane & 3) .. + 7.
+    auto cell = [&](int64_t n0, int blk, int q, int64_t& row, int64_t& col) {
+        const int r = (lane >> 2) + 16 * q, c = 8 * (lane & 3);
+        if (Left) {  // rows from U, columns from N
+            row = u0 + wave * 32 + r;
+            col = n0 + blk * 32 + c;
+        } else {     // rows from N, columns from U
+            row = n0 + blk * 32 + r;
+            col = u0 + wave * 32 + c;
+        }
+    };
+    u32x4 wp[2][2][2];  // [block][q][16-byte half]
+    // exactly kP loads, rows and columns clamped into the tensor
+    auto load_w = [&](int64_t n0) {
+        if (!d.wvec) return;  // only the exact path (16-byte rows) uses them
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                int64_t row, col;
+                cell(n0, blk, q, row, col);
+                row = min(row, static_cast<int64_t>(d.m) - 1);
+                col = min(col, static_cast<int64_t>(d.n) - 8);
+                const PT* p = x + row * d.n + col;
+                wp[blk][q][0] = *gld<u32x4>(p);
+                if (!XB) wp[blk][q][1] = *gld<u32x4>(p + 4);
+            }
+    };
+    f32x16 acc[2];
+    auto multiply = [&](const uint16_t* buf) {
+        const uint16_t* ph = buf;
+        const uint16_t* pl = buf + kUrN * 256;
+        // The fragment reads are one asm block per sub-step that waits for its own
+        // reads: the compiler cannot tell which stage an LDS read hits, and before a
+        // plain read it would wait for every outstanding transfer, the next stage and
+        // the parameter loads included. The stage read here landed (the wait and the
+        // barrier before the multiply).
+        // One address per sub-step: the low plane is 32 KB on, rows r + 32 are 16 KB on
+        // (same swizzle, since r + 32 = r mod 16).
+        static_assert(kUrN * 256 * 2 == 32768, "plane offset in the reads below");
+        (void)pl;
+        const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ph)) + (lane & 31) * 512;
+        const int sw = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            if (ks >= nks) break;
+            const int kc = 2 * ks + (lane >> 5);  // 16-byte chunk of the row
+            int swv = sw;
+            __asm__ volatile("" : "+v"(swv));  // computed here, not hoisted and spilled
+            const uint32_t addr = base + static_cast<uint32_t>((kc ^ swv) << 4);
+            u32x4 h0, l0, h1, l1;
+            __asm__ volatile(
+                "ds_read_b128 %0, %4\n\t"
+                "ds_read_b128 %1, %4 offset:32768\n\t"
+                "ds_read_b128 %2, %4 offset:16384\n\t"
+                "ds_read_b128 %3, %4 offset:49152\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(h0), "=&v"(l0), "=&v"(h1), "=&v"(l1)
+                : "v"(addr));
+            const bfv8 fh[2] = {__builtin_bit_cast(bfv8, h0), __builtin_bit_cast(bfv8, h1)};
+            const bfv8 fl[2] = {__builtin_bit_cast(bfv8, l0), __builtin_bit_cast(bfv8, l1)};
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                if (Left) {
+                    acc[b] = mfma32(uf[ks], fh[b], acc[b]);
+                    acc[b] = mfma32(uf[ks], fl[b], acc[b]);
+                } else {
+                    acc[b] = mfma32(fh[b], uf[ks], acc[b]);
+                    acc[b] = mfma32(fl[b], uf[ks], acc[b]);
+                }
+            }
+        }
+    };
+    // W <- decay W - coef C for a tile, through the wave's exchange region (one 32 x 32
+    // block at a time, so that each lane ends with 8 consecutive columns of a row).
+    // exact: every cell inside the tensor, exactly kP 16-byte stores; otherwise
+    // element-wise edges and a full wait after them.
+    auto update = [&](int64_t n0, bool exact) {
+        float* lw = exb + wave * (32 * 32);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) lw[ur_ex(acc_row(v, lane), acc_col(lane))] = acc[blk][v];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                float cq[8];
+                {
+                    const int r = (lane >> 2) + 16 * q, c = 8 * (lane & 3);
+                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(lw + ur_ex(r, c));
+                    const f32x4 c1 = *reinterpret_cast<const f32x4*>(lw + ur_ex(r, c + 4));
+                    cq[0] = c0.x; cq[1] = c0.y; cq[2] = c0.z; cq[3] = c0.w;
+                    cq[4] = c1.x; cq[5] = c1.y; cq[6] = c1.z; cq[7] = c1.w;
+                }
+                int64_t row, col;
+                cell(n0, blk, q, row, col);
+                float w[8];
+                if (exact) {
+                    PT* xp = x + row * d.n + col;
+                    if (XB) {
+                        bf16x8(wp[blk][q][0], w);
+                    } else {
+                        const u32x4 x0 = wp[blk][q][0], x1 = wp[blk][q][1];
+                        w[0] = __uint_as_float(x0.x); w[1] = __uint_as_float(x0.y);
+                        w[2] = __uint_as_float(x0.z); w[3] = __uint_as_float(x0.w);
+                        w[4] = __uint_as_float(x1.x); w[5] = __uint_as_float(x1.y);
+                        w[6] = __uint_as_float(x1.z); w[7] = __uint_as_float(x1.w);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = a.decay * w[e] - a.coef * cq[e];
+                    if (XB) {
+                        *gst<u32x4>(xp) = pack_bf16x8(w);
+                    } else {
+                        *gst<f32x4>(xp) = f32x4{w[0], w[1], w[2], w[3]};
+                        *gst<f32x4>(xp + 4) = f32x4{w[4], w[5], w[6], w[7]};
+                    }
+                } else {
+                    if (row >= d.m || col >= d.n) continue;
+                    PT* xp = x + row * d.n + col;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (col + e >= d.n) continue;
+                        const float w0 = XB ? __uint_as_float(static_cast<uint32_t>(*gld<uint16_t>(reinterpret_cast<const uint16_t*>(xp) + e)) << 16)
+                                            : *gld<float>(reinterpret_cast<const float*>(xp) + e);
+                        const float w1 = a.decay * w0 - a.coef * cq[e];
+                        if (XB) *gst<uint16_t>(reinterpret_cast<uint16_t*>(xp) + e) = static_cast<uint16_t>(bf16_bits(w1));
+                        else *gst<float>(reinterpret_cast<float*>(xp) + e) = w1;
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();  // this block's gathers before the next block's spill
+        }
+        if (!exact) MEO_WAIT_VM(0);
+    };
+    auto zero = [&]() {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
+    };
+    // Exact counts need every tile of the item whole and 16-byte parameter rows.
+    const bool exact = d.wvec && (nt0 + ntiles) * kUrN <= d.D && u0 + kGaWide <= d.d;
+    // Tile i uses buffer i & 1; the stage for tile i + 1 goes out before tile i's wait
+    // (past the last tile it stages the last one again, so counts stay fixed). The
+    // wait before a tile leaves, in issue order after that tile's stage: the previous
+    // tile's kP stores, this tile's kP parameter loads and the next stage's 8 transfers
+    // (the first tile: the kP loads and the next stage).
+    const int last = ntiles - 1;
+    ur_stage(d, nt0 * kUrN, nb0, wave, lane);
+    load_w(nt0 * kUrN);
+    ur_stage(d, (nt0 + min(1, last)) * kUrN, nb1, wave, lane);
+    MEO_WAIT_VM(kP + 8);
+    for (int i = 0; i < ntiles; i += 2) {
+        // tile i in nb0 (its stage landed)
+        __builtin_amdgcn_s_barrier();
+        zero();
+        multiply(nb0);
+        __builtin_amdgcn_s_barrier();
+        update((nt0 + i) * kUrN, exact);
+        load_w((nt0 + min(i + 1, last)) * kUrN);
+        if (i + 1 >= ntiles) break;
+        // tile i + 1 in nb1
+        ur_stage(d, (nt0 + min(i + 2, last)) * kUrN, nb0, wave, lane);
+        if (exact) MEO_WAIT_VM(2 * kP + 8);
+        else MEO_WAIT_VM(0);
+        __builtin_amdgcn_s_barrier();
+        zero();
+        multiply(nb1);
+        __builtin_amdgcn_s_barrier();
+        update((nt0 + i + 1) * kUrN, exact);
+        load_w((nt0 + min(i + 2, last)) * kUrN);
+        if (i + 2 >= ntiles) break;
+        ur_stage(d, (nt0 + min(i + 3, last)) * kUrN, nb1, wave, lane);
+        if (exact) MEO_WAIT_VM(2 * kP + 8);
+        else MEO_WAIT_VM(0);
+    }
+    MEO_WAIT_VM(0);
+}
+
+void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, int mode, hipStream_t s) {
     if (n <= 0) return;
     const dim3 grid(static_cast<uint32_t>(n)), block(kBackThreads);
+    const bool direct = mode == kBackDirect;
+    if (mode == kBackUr || mode == kBackUrBf16) {
+        const bool xb = mode == kBackUrBf16;
+        if (left && xb) hipLaunchKernelGGL((k_galore_back_ur<true, true>), grid, dim3(512), 0, s, t, a);
+        else if (left) hipLaunchKernelGGL((k_galore_back_ur<true, false>), grid, dim3(512), 0, s, t, a);
+        else if (xb) hipLaunchKernelGGL((k_galore_back_ur<false, true>), grid, dim3(512), 0, s, t, a);
+        else hipLaunchKernelGGL((k_galore_back_ur<false, false>), grid, dim3(512), 0, s, t, a);
+        return;
+    }
     if (left) {
         if (direct) hipLaunchKernelGGL((k_galore_back<true, true>), grid, block, 0, s, t, a);
         else hipLaunchKernelGGL((k_galore_back<true, false>), grid, block, 0, s, t, a);

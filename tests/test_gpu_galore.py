@@ -135,13 +135,13 @@ def test_list_equals_singles():
 
 
 def test_direct_staging_equals_register_staging():
-    """The kernels are chosen per list: the wide projection and the direct-staged
-    back-projection (global_load_lds) when every contraction length of the list is
-    a multiple of 64, the register-staged ones otherwise. All feed the MFMAs the
-    same fragments in the same order (the m < n wide projection through LDS
-    transpose reads), so a tensor's step is bitwise the same on either. (256, 128)
-    and (128, 320) at rank 64 take the wide and direct kernels alone and the
-    register-staged ones beside (200, 40) and (40, 200), whose rank 40 and
+    """The kernels are chosen per list: the wide projection and the U-register
+    back-projection (operands staged by global_load_lds) when every contraction
+    length of the list is a multiple of 64, the register-staged ones otherwise. All
+    feed the MFMAs the same fragments in the same order (the m < n wide projection
+    through LDS transpose reads), so a tensor's step is bitwise the same on either.
+    (256, 128) and (128, 320) at rank 64 take the wide and U-register kernels alone
+    and the register-staged ones beside (200, 40) and (40, 200), whose rank 40 and
     contraction length 40 are not multiples of 64."""
     shapes = [(256, 128), (200, 40), (128, 320), (40, 200)]
     dev = "cuda"
@@ -159,6 +159,31 @@ def test_direct_staging_equals_register_staging():
         assert torch.equal(p1[k], p2[k])
         for key in s1[k]:
             assert torch.equal(s1[k][key], s2[k][key])
+
+
+def test_mixed_parameter_dtypes_list():
+    """A list whose parameters mix fp32 and bf16 takes the direct-staged back-projection
+    (the U-register kernel is compiled per parameter dtype); each tensor alone takes the
+    U-register kernel. Both run the same MFMA sequence, so the steps agree bitwise."""
+    dev = "cuda"
+    h = _lib.galore_hparams(lr=0.05, rank=64)
+    f_shapes, b_shapes = [(256, 128), (128, 320)], [(192, 256), (256, 192)]
+    runs = []
+    for _ in range(2):
+        pf, gf, sf = workloads.galore_inputs(f_shapes, 64, 31, device=dev)
+        pb, gb, sb = workloads.galore_inputs(b_shapes, 64, 32, param_dtype=torch.bfloat16, device=dev)
+        runs.append((pf + pb, gf + gb, sf + sb))
+    (p1, g1, s1), (p2, g2, s2) = runs
+    ws = _lib.workspace(_lib.meo_galore_workspace_size(h, p1, g1), dev)
+    _lib.meo_galore_step(h, 4, p1, g1, s1, ws)
+    for k in range(len(p2)):
+        wk = _lib.workspace(_lib.meo_galore_workspace_size(h, [p2[k]], [g2[k]]), dev)
+        _lib.meo_galore_step(h, 4, [p2[k]], [g2[k]], [s2[k]], wk)
+    torch.cuda.synchronize()
+    for k in range(len(p1)):
+        assert torch.equal(p1[k], p2[k]), k
+        for key in s1[k]:
+            assert torch.equal(s1[k][key], s2[k][key]), (k, key)
 
 
 def _views(shapes, dtype):
