@@ -161,6 +161,37 @@ def test_direct_staging_equals_register_staging():
             assert torch.equal(s1[k][key], s2[k][key])
 
 
+@pytest.mark.parametrize("pdt,offset", [(torch.float32, 1), (torch.float32, 3), (torch.bfloat16, 5)])
+def test_offset_parameter_views(pdt, offset):
+    """Parameters carved from one buffer at element offsets that keep their dtype's
+    alignment but not 16 bytes (flat-parameter frameworks hand them over so): the
+    back-projection must take its element-wise edges for them. Against the same step on
+    fresh (aligned) parameters: bitwise equal, the same values computed either way."""
+    dev = "cuda"
+    shapes = [(256, 128), (128, 320), (320, 256)]
+    h = _lib.galore_hparams(lr=0.05, rank=64)
+    pa, ga_, sa = workloads.galore_inputs(shapes, 64, 41, param_dtype=pdt, device=dev)
+    pb, gb, sb = workloads.galore_inputs(shapes, 64, 41, param_dtype=pdt, device=dev)
+    sizes = [int(np.prod(sh)) for sh in shapes]
+    buf = torch.zeros(offset + sum(sizes) + 16, dtype=pdt, device=dev)
+    views, o = [], offset
+    for n_, sh, p in zip(sizes, shapes, pb):
+        v = buf[o:o + n_].view(sh)
+        v.copy_(p)
+        views.append(v)
+        o += n_
+    assert all(v.data_ptr() % 16 != 0 for v in views)
+    for params, grads, states in ((pa, ga_, sa), (views, gb, sb)):
+        ws = _lib.workspace(_lib.meo_galore_workspace_size(h, params, grads), dev)
+        _lib.meo_galore_step(h, 3, params, grads, states, ws)
+    torch.cuda.synchronize()
+    for k in range(len(shapes)):
+        assert not torch.equal(pa[k], workloads.galore_inputs(shapes, 64, 41, param_dtype=pdt, device=dev)[0][k])
+        assert torch.equal(pa[k], views[k]), k
+        for key in sa[k]:
+            assert torch.equal(sa[k][key], sb[k][key]), (k, key)
+
+
 def test_mixed_parameter_dtypes_list():
     """A list whose parameters mix fp32 and bf16 takes the direct-staged back-projection
     (the U-register kernel is compiled per parameter dtype); each tensor alone takes the
