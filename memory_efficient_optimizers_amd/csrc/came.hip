@@ -130,7 +130,7 @@ void launch_came_mom(const Table& t, int64_t n, const CameArgs& a, int storage, 
 // lane's 8 elements (one row, since W % 8 == 0) find their row and column from their
 // index. At every batch the block's four waves then load one contiguous 8 KB range
 // per stream, where 64 x 512 tiles load 2 KB pieces of 16 rows; the pass runs about
-// 6% faster so. The arithmetic is the tiled path's, term for term.
+// 5% faster so (Llama-7B list). The arithmetic is the tiled path's, term for term.
 template <int ST, typename I>
 __device__ __forceinline__ void came_apply_range(const TDesc& d, int lt, const float* ws, float decay) {
     const I W = static_cast<I>(d.W), H = static_cast<I>(d.H);
