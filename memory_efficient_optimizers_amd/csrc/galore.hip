@@ -734,13 +734,15 @@ __global__ __launch_bounds__(kBackThreads, Direct ? 3 : 1) void k_galore_back(GT
 // only N's planes are staged, by global_load_lds, into one of two LDS buffers (64 KB
 // each: rows of 256, chunk c of row w at c ^ (w & 15)), the next tile's while the
 // current one is multiplied. The parameter part of tile i + 1 is loaded right after
-// tile i's stores, so it has tile i + 1's contraction to land; the wait before a tile
-// leaves exactly the newer N stage, those stores and those loads outstanding. Against
-// the direct-staged 64 x 256 tiles (3 blocks per CU, U staged per tile) the L2 bytes
-// staged per tile fall from 192 KB to 64 KB: Llama-7B list, fp32 parameters, 13.55 ->
-// 12.57 ms (bf16 10.2 -> 9.95 ms), results bitwise the same. The parameter stream (one
-// read and one write of W) bounds it: without the MFMAs the m >= n pass takes 8.6 of
-// its 9.8 ms, about the rate of a plain read-write copy.
+// tile i's stores and the next stage, so it has tile i + 1's contraction to land; the
+// wait before a tile leaves exactly those stores, that stage and those loads
+// outstanding. Against the direct-staged 64 x 256 tiles (3 blocks per CU, U staged
+// per tile) the L2 bytes staged per tile fall from 192 KB to 64 KB: Llama-7B list,
+// fp32 parameters, 13.55 -> 12.57 ms (bf16 10.2 -> 9.95 ms), results bitwise the
+// same. The parameter stream (one read and one write of W) bounds it: timing-only
+// copies take 10.8 ms with the parameter stream alone in these tiles (5.0 TB/s), and
+// the same with the products but N staged once; each tile's N stage is what the pass
+// spends beyond that.
 constexpr int kUrN = kGaTile;           // rows of N per tile
 constexpr int kUrNDma = 2 * kUrN * (kGaWide / 8) / 64 / 8;  // 16-byte transfers per wave per tile: 8
 // A wave's 32 x 32 exchange block in LDS, unpadded: row r at row r ^ ((r >> 2) & 1), its
@@ -946,15 +948,21 @@ __global__ __launch_bounds__(512, 1) void k_galore_back_ur(GTable t, GaArgs a) {
     };
     // Exact counts need every tile of the item whole and 16-byte parameter rows.
     const bool exact = d.wvec && (nt0 + ntiles) * kUrN <= d.D && u0 + kGaWide <= d.d;
-    // Tile i uses buffer i & 1; the stage for tile i + 1 goes out before tile i's wait
-    // (past the last tile it stages the last one again, so counts stay fixed). The
-    // wait before a tile leaves, in issue order after that tile's stage: the previous
-    // tile's kP stores, this tile's kP parameter loads and the next stage's 8 transfers
-    // (the first tile: the kP loads and the next stage).
+    // Tile i uses buffer i & 1. After tile i's update, the stage for tile i + 2 goes
+    // out (past the last tile it stages the last one again, so counts stay fixed), then
+    // the parameter loads of tile i + 1. So the loads are the newest transfers: the
+    // update of tile i + 1, whose first use of them makes the compiler wait for every
+    // transfer in flight, waits for them and for older ones only, not for a stage
+    // issued after them (with the loads before the stage, that wait covered the stage:
+    // 12.43 -> 12.06 ms for the fp32 back-projection of the Llama-7B list, bf16 9.80
+    // -> 9.35 ms, results bitwise the same). The wait before a tile's products allows
+    // 2 kP + 8 transfers in flight, all issued after that tile's stage: the previous
+    // tile's kP stores, the next stage's 8 transfers and this tile's kP loads (before
+    // the first tile: the next stage's 8 and its kP loads).
     const int last = ntiles - 1;
     ur_stage(d, nt0 * kUrN, nb0, wave, lane);
-    load_w(nt0 * kUrN);
     ur_stage(d, (nt0 + min(1, last)) * kUrN, nb1, wave, lane);
+    load_w(nt0 * kUrN);
     MEO_WAIT_VM(kP + 8);
     for (int i = 0; i < ntiles; i += 2) {
         // tile i in nb0 (its stage landed)
@@ -963,10 +971,10 @@ __global__ __launch_bounds__(512, 1) void k_galore_back_ur(GTable t, GaArgs a) {
         multiply(nb0);
         __builtin_amdgcn_s_barrier();
         update((nt0 + i) * kUrN, exact);
-        load_w((nt0 + min(i + 1, last)) * kUrN);
         if (i + 1 >= ntiles) break;
         // tile i + 1 in nb1
         ur_stage(d, (nt0 + min(i + 2, last)) * kUrN, nb0, wave, lane);
+        load_w((nt0 + i + 1) * kUrN);
         if (exact) MEO_WAIT_VM(2 * kP + 8);
         else MEO_WAIT_VM(0);
         __builtin_amdgcn_s_barrier();
@@ -974,9 +982,9 @@ __global__ __launch_bounds__(512, 1) void k_galore_back_ur(GTable t, GaArgs a) {
         multiply(nb1);
         __builtin_amdgcn_s_barrier();
         update((nt0 + i + 1) * kUrN, exact);
-        load_w((nt0 + min(i + 2, last)) * kUrN);
         if (i + 2 >= ntiles) break;
         ur_stage(d, (nt0 + min(i + 3, last)) * kUrN, nb1, wave, lane);
+        load_w((nt0 + i + 2) * kUrN);
         if (exact) MEO_WAIT_VM(2 * kP + 8);
         else MEO_WAIT_VM(0);
     }
