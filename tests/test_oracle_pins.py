@@ -255,6 +255,41 @@ def test_list_equals_per_tensor(opt):
         assert np.array_equal(px, lx[k])
 
 
+@pytest.mark.parametrize("opt", ["adafactor", "came", "lamb"])
+def test_empty_tensors_leave_the_rest_alone(opt):
+    """An empty tensor has no element to take a statistic, a norm or a step over:
+    a list holding empty tensors steps its other tensors exactly as the list
+    without them does, for three chained steps, and hands the empty ones back with
+    their shapes and their states unchanged (the per-tensor reading of the pages'
+    loop over parameters, which an empty parameter leaves with nothing to update)."""
+    rng = np.random.default_rng(11)
+    hp = {"adafactor": {"beta1": 0.9}, "came": {"lr": 2e-4}, "lamb": {"weight_decay": 0.01}}[opt]
+    full = [(6, 9), (9,), (3, 4, 5)]
+    empty = [(0,), (0, 5), (3, 0), (2, 0, 4)]
+    order = [full[0], empty[0], empty[1], full[1], empty[2], full[2], empty[3]]
+    xs = {s: rng.normal(0, 0.02, s) for s in order}
+    gs = [{s: rng.normal(size=s) for s in order} for _ in range(3)]
+    st_all = [oracle.INIT_STATE[opt](s, hp) for s in order]
+    st_full = [oracle.INIT_STATE[opt](s, hp) for s in full]
+    x_all, x_full = [xs[s] for s in order], [xs[s] for s in full]
+    for t in (1, 2, 3):
+        x_all, st_all = oracle.STEP[opt](x_all, [gs[t - 1][s] for s in order], st_all, hp, t)
+        x_full, st_full = oracle.STEP[opt](x_full, [gs[t - 1][s] for s in full], st_full, hp, t)
+        got = {s: (x, st) for s, x, st in zip(order, x_all, st_all)}
+        for s, x, st in zip(full, x_full, st_full):
+            assert np.array_equal(got[s][0], x)
+            assert got[s][1].keys() == st.keys()
+            for k in st:
+                assert np.array_equal(got[s][1][k], st[k])
+        for s in empty:
+            x, st = got[s]
+            assert x.shape == s
+            init = oracle.INIT_STATE[opt](s, hp)
+            assert st.keys() == init.keys()
+            for k in init:
+                assert np.shape(st[k]) == np.shape(init[k]) and np.array_equal(st[k], init[k])
+
+
 def test_came_rank1_closed_form_over_steps():
     """Constant G with rank-1 G^2: the squared-gradient estimate is
     (1 - beta2^t) G^2, so u = sign(G) / sqrt(1 - beta2^t), RMS clipping brings it
