@@ -958,12 +958,14 @@ __global__ __launch_bounds__(512, 1) void k_galore_back_ur(GTable t, GaArgs a) {
     // -> 9.35 ms, results bitwise the same). The wait before a tile's products allows
     // 2 kP + 8 transfers in flight, all issued after that tile's stage: the previous
     // tile's kP stores, the next stage's 8 transfers and this tile's kP loads (before
-    // the first tile: the next stage's 8 and its kP loads).
+    // the first tile: the next stage's 8 and its kP loads, or no loads where the
+    // parameter rows are not 16-byte aligned and load_w issues none).
     const int last = ntiles - 1;
     ur_stage(d, nt0 * kUrN, nb0, wave, lane);
     ur_stage(d, (nt0 + min(1, last)) * kUrN, nb1, wave, lane);
     load_w(nt0 * kUrN);
-    MEO_WAIT_VM(kP + 8);
+    if (d.wvec) MEO_WAIT_VM(kP + 8);
+    else MEO_WAIT_VM(8);
     for (int i = 0; i < ntiles; i += 2) {
         // tile i in nb0 (its stage landed)
         __builtin_amdgcn_s_barrier();
