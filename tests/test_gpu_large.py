@@ -12,6 +12,7 @@ whole tensor's when no per-tensor scalar depends on the rest of the tensor: the
 statistics and the per-matrix coefficients are per matrix, the clip threshold is
 set out of reach (the clip divisor is 1 on both sides) and Adafactor runs without
 scale_parameter (its step size is then rho_t alone)."""
+import numpy as np
 import pytest
 import torch
 
@@ -88,6 +89,93 @@ def test_tensor_beyond_2_32_elements(opt, hp, store):
                                    ost_prev=so)
                 print("  " + summarize(f"{opt} {store} step {t} matrix {b} (element {b * per})", res), flush=True)
                 assert not failures(res), (t, b, failures(res))
+    finally:
+        del x, g, st, ws
+        torch.cuda.empty_cache()
+
+
+# GaLore over one matrix past 2^32 elements, each side: 65600 x 65536 (m >= n, the
+# projection along the rows' space) and its transpose shape (m < n). Not a refresh
+# step, so the projector is an input: a random orthonormal basis rounded to bf16.
+# The step is independent per row of the gradient on the m >= n side (and per
+# column on the other), so blocks of 256 rows (columns) at elements 0, 2^31 and
+# past 2^32 are stepped by the oracle on their own. A 256 x 65536 block's shorter
+# side is no longer the projected one, so the oracle takes those blocks with
+# reverse_std, which projects the longer side: the same side, the same basis and
+# the same arithmetic as the whole matrix under std.
+#
+# Bars: the contraction runs over d = 65536 here, 16 times the 4096 of the Llama-7B
+# rows the GaLore bars were set on. The matrix cores accumulate the d products in
+# fp32, about sqrt(d / 16) roundings of 2^-24 of the running sum, so the low-rank
+# gradient's error grows as sqrt(d): 1e-5 becomes 4e-5 for the moments and the
+# parameter (x sqrt(65536 / 4096)), 4e-4 for the step dX.
+GA_SCALE = 4.0
+GA_SHAPES = [(65600, 65536), (65536, 65600)]
+GA_BLOCK = 256
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("shape", GA_SHAPES)
+def test_galore_matrix_beyond_2_32_elements(shape):
+    from oracle import galore as ga
+    from tests.harness import TOL_F32, floored_rel_err, output_errs
+    m, n = shape
+    numel = m * n
+    assert numel > (1 << 32)
+    r = 256
+    right = m >= n
+    d, D = (n, m) if right else (m, n)  # projected side, rows of the low-rank arrays
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    need = numel * (4 + 2) + (4 << 30)
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory, {free / 2**30:.0f} GiB free")
+    gen = torch.Generator(device="cuda").manual_seed(2025)
+    x = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).mul_(0.02)
+    g = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16).mul_(1e-3)
+    q, _ = torch.linalg.qr(torch.randn(d, r, generator=gen, device="cuda", dtype=torch.float32))
+    proj = q.to(torch.bfloat16).contiguous()
+    st = {"exp_avg": torch.randn(D, r, generator=gen, device="cuda", dtype=torch.float32).mul_(5e-4),
+          "exp_avg_sq": torch.rand(D, r, generator=gen, device="cuda", dtype=torch.float32).add_(0.5).mul_(1e-6),
+          "projector": proj, "projector_t": proj.t().contiguous()}
+    hp = dict(lr=0.05, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, scale=0.25, rank=r)
+    t = 5  # not a refresh step (update_proj_gap 200)
+    h = _lib.galore_hparams(**hp)
+    ws = _lib.workspace(_lib.meo_galore_workspace_size(h, [x], [g]), "cuda")
+    # blocks of rows (m >= n) or columns (m < n): the first, the one at element 2^31 and the last
+    starts = [0, (1 << 31) // n if right else 32768, (m if right else n) - GA_BLOCK]
+    blk = lambda a, s: a[s:s + GA_BLOCK] if right else a[:, s:s + GA_BLOCK]
+    u64 = to64(proj)
+    before = {s: (to64(blk(x, s)), to64(blk(g, s)), to64(st["exp_avg"][s:s + GA_BLOCK]),
+                  to64(st["exp_avg_sq"][s:s + GA_BLOCK])) for s in starts}
+    pt0 = st["projector_t"].clone()
+    try:
+        print(f"  galore {shape}: one call over {numel} elements", flush=True)
+        _lib.meo_galore_step(h, t, [x], [g], [st], ws)
+        torch.cuda.synchronize()
+        assert torch.equal(st["projector"], proj) and torch.equal(st["projector_t"], pt0)
+        hpo = dict(hp, proj_type="reverse_std")
+        b1 = hp["betas"][0]
+        for s in starts:
+            x0, g0, m0, v0 = before[s]
+            assert ga.galore_side(x0.shape, "reverse_std") == ("right" if right else "left")
+            want_x, want_s = ga.galore_step_tensor(x0, g0, {"exp_avg": m0, "exp_avg_sq": v0, "projector": u64},
+                                                   hpo, t)
+            got_x = to64(blk(x, s))
+            bad = []
+            errs = {}
+            for key, a, b in (("param", got_x, want_x),
+                              ("exp_avg", to64(st["exp_avg"][s:s + GA_BLOCK]), want_s["exp_avg"]),
+                              ("exp_avg_sq", to64(st["exp_avg_sq"][s:s + GA_BLOCK]), want_s["exp_avg_sq"])):
+                errs[key] = float(np.max(output_errs(key, a, b, x0=x0, prev=m0, beta1=b1, step_tol=1e-4)))
+                if errs[key] > GA_SCALE * TOL_F32:
+                    bad.append(f"{key}: err {errs[key]:.3g}")
+            e = floored_rel_err(got_x - x0, want_x - x0)
+            print(f"  galore {shape} block at {s}: update err {e:.2e}; "
+                  + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+            if e > GA_SCALE * 1e-4:
+                bad.append(f"update: err {e:.3g}")
+            assert not bad, (s, bad)
     finally:
         del x, g, st, ws
         torch.cuda.empty_cache()
