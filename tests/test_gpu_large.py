@@ -18,7 +18,8 @@ import torch
 
 import oracle
 from memory_efficient_optimizers_amd import _lib
-from tests.harness import failures, judge_tensor, lib_hp, lib_step, storage_of_tensor, summarize, to64
+from tests.harness import (TOL_F32, check_dx, failures, floored_rel_err, judge_tensor, lib_hp, lib_step,
+                           output_errs, storage_of_tensor, summarize, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,7 +119,6 @@ GA_BLOCK = 256
 @pytest.mark.parametrize("shape", GA_SHAPES)
 def test_galore_matrix_beyond_2_32_elements(shape):
     from oracle import galore as ga
-    from tests.harness import TOL_F32, floored_rel_err, output_errs
     m, n = shape
     numel = m * n
     assert numel > (1 << 32)
@@ -178,4 +178,81 @@ def test_galore_matrix_beyond_2_32_elements(shape):
             assert not bad, (s, bad)
     finally:
         del x, g, st, ws
+        torch.cuda.empty_cache()
+
+
+def _norm64(a: torch.Tensor, b: torch.Tensor = None) -> float:
+    """2-norm of a (or of a - b) in fp64, in chunks of 2^27 elements."""
+    s = 0.0
+    fa = a.reshape(-1)
+    fb = None if b is None else b.reshape(-1)
+    for i in range(0, fa.numel(), 1 << 27):
+        c = fa[i:i + (1 << 27)].double()
+        if fb is not None:
+            c -= fb[i:i + (1 << 27)].double()
+        s += float(torch.dot(c, c))
+    return s ** 0.5
+
+
+@pytest.mark.timeout(600)
+def test_lamb_tensor_beyond_2_32_elements():
+    """LAMB over the same [65537, 256, 256] tensor (one layer for the trust ratio), a
+    mid-run step (t = 3, seeded moments). The trust ratio spans the whole tensor, so
+    a matrix cannot be stepped on its own; two facts pin the step instead.
+    * Every element's direction is local: on each sampled matrix the library's step
+      is its trust ratio times the oracle's direction for that matrix, which the
+      oracle's step on the matrix alone gives as (x - x_new) / (lr * its own ratio).
+      Moments are local and compared directly.
+    * The ratio: the library's ||X|| matches an fp64 reduction of the parameter, and
+      the step's norm is lr ||X|| over the whole tensor (LAMB's update has the norm
+      lr * trust * ||d|| = lr ||X||), from fp64 reductions on the device."""
+    numel = SHAPE[0] * SHAPE[1] * SHAPE[2]
+    per = SHAPE[1] * SHAPE[2]
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    need = numel * (4 + 4 + 2 + 4 + 4) + (4 << 30)  # parameter and its copy, gradient, moments
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory, {free / 2**30:.0f} GiB free")
+    hp = {"lr": 1e-3, "weight_decay": 0.01}
+    t = 3
+    gen = torch.Generator(device="cuda").manual_seed(2026)
+    x = torch.randn(SHAPE, generator=gen, device="cuda", dtype=torch.float32).mul_(0.02)
+    g = torch.randn(SHAPE, generator=gen, device="cuda", dtype=torch.bfloat16).mul_(1e-3)
+    st = _lib.init_state("lamb", x, state_dtype=torch.float32)
+    torch.randn(SHAPE, generator=gen, device="cuda", dtype=torch.float32, out=st["exp_avg"]).mul_(5e-4)
+    torch.rand(SHAPE, generator=gen, device="cuda", dtype=torch.float32, out=st["exp_avg_sq"]).add_(0.5).mul_(1e-6)
+    x0 = x.clone()
+    xn_ref = _norm64(x0)
+    before = {b: (to64(x[b]).reshape(-1), to64(g[b]).reshape(-1), to64(st["exp_avg"][b]).reshape(-1),
+                  to64(st["exp_avg_sq"][b]).reshape(-1)) for b in SAMPLE}
+    hps = lib_hp("lamb", hp)
+    ws = _lib.workspace(_lib.meo_lamb_workspace_size([x], [g]), "cuda")
+    offs = _lib._scalar_offsets("lamb", [x], [g])
+    try:
+        print(f"  lamb step {t}: one call over {numel} elements", flush=True)
+        lib_step("lamb", hps, t, [x], [g], [st], ws)
+        torch.cuda.synchronize()
+        sc = _lib.read_scalars(ws, offs)[0]
+        xn, dn, tau = sc["rms_x"], sc["norm_d"], sc["trust"]
+        dx_norm = _norm64(x, x0)
+        e_xn = abs(xn - xn_ref) / xn_ref
+        e_tau = abs(tau - xn / dn) / tau
+        e_dx = abs(dx_norm - hp["lr"] * xn_ref) / (hp["lr"] * xn_ref)
+        print(f"  lamb: ||X|| {xn:.6e} (fp64 {xn_ref:.6e}, err {e_xn:.1e}); trust {tau:.6e} (err {e_tau:.1e}); "
+              f"||dX|| / (lr ||X||) - 1 = {e_dx:.1e}", flush=True)
+        assert e_xn <= 1e-6 and e_tau <= 1e-6 and e_dx <= 1e-5, (e_xn, e_tau, e_dx)
+        for b in SAMPLE:
+            x0b, gb, mb, vb = before[b]
+            so = {}
+            xo, sto = oracle.STEP_TENSOR["lamb"](x0b, gb, {"exp_avg": mb, "exp_avg_sq": vb}, hp, t, scalars=so)
+            d_o = (x0b - xo) / (hp["lr"] * so["trust"])  # the oracle's direction on this matrix
+            ok, e, over, _, nw = check_dx("f32", to64(x[b]).reshape(-1), x0b, x0b - hp["lr"] * tau * d_o, x0b)
+            em = float(np.max(output_errs("exp_avg", to64(st["exp_avg"][b]).reshape(-1), sto["exp_avg"],
+                                          prev=mb, beta1=0.9)))
+            ev = float(np.max(output_errs("exp_avg_sq", to64(st["exp_avg_sq"][b]).reshape(-1), sto["exp_avg_sq"])))
+            print(f"  lamb matrix {b} (element {b * per}): dX err {e:.2e} (normwise {nw:.1e}), "
+                  f"exp_avg {em:.2e}, exp_avg_sq {ev:.2e}", flush=True)
+            assert ok and em <= TOL_F32 and ev <= TOL_F32, (b, e, over, nw, em, ev)
+    finally:
+        del x, x0, g, st, ws
         torch.cuda.empty_cache()
