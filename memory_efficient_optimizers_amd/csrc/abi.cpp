@@ -1623,6 +1623,7 @@ struct GaPlan {
     int64_t count[kGaListCount] = {};
     int back_mode[2] = {kBackReg, kBackReg};  // back-projection kernel (BackMode), right and left
     bool proj_direct[2] = {false, false};  // projection staged by global_load_lds (right, left)
+    int nright = 0;  // right-side descriptors, first in gdesc
 };
 std::list<GaPlan*> g_ga_plans;  // most recently used first, under g_mu
 
@@ -1938,7 +1939,10 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
         const bool is_left = i >= right.size();
         const int id = static_cast<int>(i);
         const int64_t pt = ceil_div(d.D, proj_direct[is_left] ? kGaPwRows : kGaProjRows);
-        for (int64_t y = 0; y < pt; ++y) lists[is_left ? kGaProjL : kGaProjR].push_back(make_int2(id, static_cast<int>(y)));
+        // both sides direct: one list (kGaProjR) for the mixed kernel
+        const bool one_list = proj_direct[0] && proj_direct[1];
+        for (int64_t y = 0; y < pt; ++y)
+            lists[is_left && !one_list ? kGaProjL : kGaProjR].push_back(make_int2(id, static_cast<int>(y)));
         std::vector<int2>& L = lists[is_left ? kGaBackL : kGaBackR];
         if (back_mode[is_left] == kBackUr || back_mode[is_left] == kBackUrBf16) {
             // chunks of N outer, bands of U inner: consecutive items share N's rows
@@ -1990,6 +1994,7 @@ GaPlan* get_galore_plan(const meo_galore_hparams* hp, int32_t n, const meo_tenso
     p->back_mode[1] = back_mode[1];
     p->proj_direct[0] = proj_direct[0];
     p->proj_direct[1] = proj_direct[1];
+    p->nright = static_cast<int>(right.size());
     if (hipMalloc(&p->mem, host.size()) != hipSuccess ||
         hipMemcpy(p->mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
         if (p->mem) (void)hipFree(p->mem);
@@ -2124,8 +2129,12 @@ int meo_galore_step(const meo_galore_hparams* hp, int64_t step, int32_t n, const
              static_cast<float>(hp->eps), static_cast<float>(1.0 - hp->lr * hp->weight_decay),
              static_cast<float>(hp->lr * hp->scale)};
     PassTimer pt(s);
-    launch_galore_project(GTable{p->gdesc, p->items[kGaProjR]}, p->count[kGaProjR], a, false, p->proj_direct[0], s);
-    launch_galore_project(GTable{p->gdesc, p->items[kGaProjL]}, p->count[kGaProjL], a, true, p->proj_direct[1], s);
+    if (p->proj_direct[0] && p->proj_direct[1]) {
+        launch_galore_project_mixed(GTable{p->gdesc, p->items[kGaProjR]}, p->count[kGaProjR], p->nright, a, s);
+    } else {
+        launch_galore_project(GTable{p->gdesc, p->items[kGaProjR]}, p->count[kGaProjR], a, false, p->proj_direct[0], s);
+        launch_galore_project(GTable{p->gdesc, p->items[kGaProjL]}, p->count[kGaProjL], a, true, p->proj_direct[1], s);
+    }
     pt.mark(kPassGaProject);
     launch_galore_back(GTable{p->gdesc, p->items[kGaBackR]}, p->count[kGaBackR], a, false, p->back_mode[0], s);
     launch_galore_back(GTable{p->gdesc, p->items[kGaBackL]}, p->count[kGaBackL], a, true, p->back_mode[1], s);

@@ -52,6 +52,9 @@ struct GaArgs {
 // list's items are then tiles of kGaPwRows rows of R for the wide kernel, whose
 // operands are staged by global_load_lds. Otherwise items are kGaProjRows-row tiles.
 void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s);
+// The wide tiles of both sides in one launch (every tensor of the list direct); the
+// items index descriptors of either side, the first nright of them right-side ones.
+void launch_galore_project_mixed(const GTable& t, int64_t n, int nright, const GaArgs& a, hipStream_t s);
 // Back-projection kernels. kBackReg: operands staged through registers (any list).
 // kBackDirect: 64 x 256 tiles staged by global_load_lds (every rank a multiple of kGaKb,
 // 16-byte rows). kBackUr / kBackUrBf16: as direct, with U held in registers and items of

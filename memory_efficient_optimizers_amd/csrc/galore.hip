@@ -11,7 +11,7 @@
 //
 // so the low-rank arrays are always [max(m, n)][r]. Two kernels per step:
 //
-//   k_galore_project_wide / k_galore_project
+//   k_galore_project_mixed / k_galore_project_wide / k_galore_project
 //                     R = X U with X = G (m >= n) or G^T (m < n), bf16 MFMA with
 //                     fp32 accumulation, one 256-row (wide) or 64-row tile of R
 //                     per block and the whole contraction in the block (no split
@@ -386,19 +386,15 @@ __device__ __forceinline__ bfv8 ld_frag_tr(const uint16_t* sa, int r0, int ks, i
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maxima).
 #define MEO_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+// One 256-row tile of R (rows i0 ..) of tensor d: the contraction through the two
+// LDS stages (a0/b0, a1/b1: the kernel's own arrays, so that the compiler tells
+// the stages apart), then AdamW on the tile.
 template <bool Left>
-__global__ __launch_bounds__(kGaPwThreads, 1) void k_galore_project_wide(GTable t, GaArgs a) {
+__device__ __forceinline__ void pw_tile(const GDesc& d, int64_t i0, const GaArgs& a, uint16_t* a0, uint16_t* b0,
+                                        uint16_t* a1, uint16_t* b1) {
     static_assert(kPwDma == 8, "wait counts below");
-    __shared__ __attribute__((aligned(16))) uint16_t a0[kGaPwRows * kDirectPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t b0[kGaWide * kDirectPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t a1[kGaPwRows * kDirectPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t b1[kGaWide * kDirectPitch];
-    const int2 it = t.items[blockIdx.x];
-    if (it.x < 0) return;
-    const GDesc d = t.desc[it.x];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rg = wave >> 2, cg = wave & 3;
-    const int64_t i0 = static_cast<int64_t>(it.y) * kGaPwRows;
     const bool active = cg * 64 < d.r;
     f32x16 acc[4][2];
 #pragma unroll
@@ -490,6 +486,40 @@ __global__ __launch_bounds__(kGaPwThreads, 1) void k_galore_project_wide(GTable 
             galore_adamw8(d, a, row, col, rv);
         }
     }
+}
+
+template <bool Left>
+__global__ __launch_bounds__(kGaPwThreads, 1) void k_galore_project_wide(GTable t, GaArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t a0[kGaPwRows * kDirectPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t b0[kGaWide * kDirectPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t a1[kGaPwRows * kDirectPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t b1[kGaWide * kDirectPitch];
+    const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;
+    pw_tile<Left>(t.desc[it.x], static_cast<int64_t>(it.y) * kGaPwRows, a, a0, b0, a1, b1);
+}
+
+// Both sides' tiles in one launch: descriptors [0, nright) are right-side ones (the
+// side follows proj_type, not only the shape). A launch leaves part of its last round
+// of blocks idle; one launch instead of two has one such tail (Llama-7B list at rank
+// 256: 5.05 -> 4.99 ms for the projection, results bitwise the same).
+__global__ __launch_bounds__(kGaPwThreads, 1) void k_galore_project_mixed(GTable t, GaArgs a, int nright) {
+    __shared__ __attribute__((aligned(16))) uint16_t a0[kGaPwRows * kDirectPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t b0[kGaWide * kDirectPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t a1[kGaPwRows * kDirectPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t b1[kGaWide * kDirectPitch];
+    const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;
+    const GDesc d = t.desc[it.x];
+    const int64_t i0 = static_cast<int64_t>(it.y) * kGaPwRows;
+    if (it.x >= nright) pw_tile<true>(d, i0, a, a0, b0, a1, b1);
+    else pw_tile<false>(d, i0, a, a0, b0, a1, b1);
+}
+
+void launch_galore_project_mixed(const GTable& t, int64_t n, int nright, const GaArgs& a, hipStream_t s) {
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_galore_project_mixed, dim3(static_cast<uint32_t>(n)), dim3(kGaPwThreads), 0, s, t, a,
+                       nright);
 }
 
 void launch_galore_project(const GTable& t, int64_t n, const GaArgs& a, bool left, bool direct, hipStream_t s) {
