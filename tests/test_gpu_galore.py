@@ -161,6 +161,30 @@ def test_direct_staging_equals_register_staging():
             assert torch.equal(s1[k][key], s2[k][key])
 
 
+@pytest.mark.parametrize("shapes,direct", [([(256, 128), (40, 200)], 0), ([(200, 40), (128, 320)], 1)],
+                         ids=["right-direct", "left-direct"])
+def test_one_direct_side_equals_singles(shapes, direct):
+    """With only one side of a list direct, the projection launches the wide kernel for
+    that side and the register-staged one for the other; alone, the direct tensor
+    takes the one launch for both sides. Its step is bitwise the same either way."""
+    dev = "cuda"
+    h = _lib.galore_hparams(lr=0.05, rank=64)
+    p1, g1, s1 = workloads.galore_inputs(shapes, 64, 29, device=dev)
+    p2, g2, s2 = workloads.galore_inputs(shapes, 64, 29, device=dev)
+    ws = _lib.workspace(_lib.meo_galore_workspace_size(h, p1, g1), dev)
+    _lib.meo_galore_step(h, 4, p1, g1, s1, ws)
+    for k in range(len(shapes)):
+        wk = _lib.workspace(_lib.meo_galore_workspace_size(h, [p2[k]], [g2[k]]), dev)
+        _lib.meo_galore_step(h, 4, [p2[k]], [g2[k]], [s2[k]], wk)
+    torch.cuda.synchronize()
+    x0 = workloads.galore_inputs(shapes, 64, 29, device=dev)[0]
+    for k in range(len(shapes)):
+        assert not torch.equal(p1[k], x0[k])
+        assert torch.equal(p1[k], p2[k]), (shapes[k], k == direct)
+        for key in s1[k]:
+            assert torch.equal(s1[k][key], s2[k][key]), (shapes[k], key)
+
+
 @pytest.mark.parametrize("pdt,offset", [(torch.float32, 1), (torch.float32, 3), (torch.bfloat16, 5)])
 def test_offset_parameter_views(pdt, offset):
     """Parameters carved from one buffer at element offsets that keep their dtype's
