@@ -55,3 +55,24 @@ def test_more_than_one_gpu_is_refused(argv, env):
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_galore_bytes():
+    """GaLore at rank 256 projects all 226 two-dimensional tensors, each with d = 4096
+    (the shorter side). Projection: G (bf16, 2 bytes per element), both moments read
+    and written and N's two bf16 planes written (20 bytes per element of [D][r]), U^T
+    read (2 per element of [r][d]). Back-projection: W read and written, N's planes
+    and U read once."""
+    specs = workloads.WORKLOADS["adafactor_llama7b"].specs
+    shapes = [s.shape for s in specs]
+    r, d = 256, HID
+    two_d = [s for s in shapes if len(s) == 2]
+    assert len(two_d) == 2 + 7 * LAYERS == 226
+    sum_big = sum(max(s) for s in two_d)
+    assert sum_big == 2 * V + LAYERS * (4 * HID + 3 * MLP)
+    for xb, back in ((4, 56_063_688_704), (2, 29_111_091_200)):
+        b = bench.galore_bytes_flops(shapes, r, xb)
+        assert b["galore_project"] == 2 * P2 + 20 * r * sum_big + 2 * r * d * 226
+        assert b["galore_back"] == 2 * xb * P2 + 4 * r * sum_big + 2 * r * d * 226 == back
+        assert b["flops_back"] == 2 * b["flops_project"] == 4 * r * P2
+        assert b["galore_adamw"] == (2 + 2 * xb + 16) * P1
