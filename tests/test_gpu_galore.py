@@ -572,6 +572,14 @@ def test_step_reverse_std(shape, rank):
     run_case([shape], rank, hp=dict(proj_type="reverse_std"))
 
 
+def test_step_reverse_std_list():
+    """reverse_std over a list with tensors of both sides and both shapes: the tall
+    (256, 128) and (512, 384) are projected on the left, the wide (128, 320) and
+    (192, 448) on the right; with every contraction length a multiple of 64 they share
+    the one projection launch, which takes each tile's side from its descriptor."""
+    run_case([(256, 128), (128, 320), (512, 384), (192, 448)], 64, hp=dict(proj_type="reverse_std"), seed=6)
+
+
 @pytest.mark.parametrize("shape", [(384, 160), (160, 384)])
 def test_refresh_reverse_std(shape):
     dev = "cuda"
