@@ -10,6 +10,7 @@ raises, there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Dict, List, Optional, Sequence
 
@@ -397,6 +398,30 @@ def read_scalars(workspace: torch.Tensor, offsets) -> List[Optional[Dict[str, fl
             continue
         out.append(dict(zip(SCALAR_SLOTS, vals[j:j + len(SCALAR_SLOTS)])))
         j += len(SCALAR_SLOTS)
+    return out
+
+# The per-tensor slots each optimizer writes (include/meo.h, meo_*_scalar_offsets)
+# through which a non-finite gradient shows: RMS(U) and the clip divisor built on
+# it (Adafactor, CAME), the direction's norm and the trust ratio (LAMB, whose
+# direction also holds the decayed parameter, so its norm slot catches a
+# non-finite parameter as well).
+FINITE_CHECK_SLOTS = {"adafactor": ("coef", "rms_u", "kappa"), "came": ("coef", "rms_u", "kappa"),
+                      "lamb": ("rms_x", "norm_d", "trust")}
+
+
+def nonfinite_tensors(optimizer: str, workspace: torch.Tensor, offsets) -> List[int]:
+    """Indices of the tensors whose scalars, left in ``workspace`` by a completed
+    step call, hold a NaN or an infinity, so that the call's update of that tensor is
+    not finite: a NaN or infinite gradient element does that for every optimizer;
+    for Adafactor and CAME so does a factored tensor's element whose square
+    overflows float32 (LAMB's v then turns infinite and that element's direction is
+    0, a finite step). Tensors with zero elements are never listed. Synchronises the
+    device."""
+    slots = FINITE_CHECK_SLOTS[optimizer]
+    out = []
+    for k, sc in enumerate(read_scalars(workspace, offsets)):
+        if sc is not None and not all(math.isfinite(sc[name]) for name in slots):
+            out.append(k)
     return out
 
 

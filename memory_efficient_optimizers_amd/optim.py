@@ -18,6 +18,12 @@ rounded to nearest even when stored. ``state_dtype=torch.int8`` keeps the first
 moment 8-bit group-quantized (128 values per float32 scale, the GaLore section's
 8-bit base and the ms-swift page's quantizer) for every tensor that
 ``moment_dtype`` allows; the others keep it in float32.
+
+Failure detection: with ``check_finite=True`` (Adafactor, CAME, Lamb) each call's
+per-tensor scalars are read back once it completes, and ``nonfinite_params()``
+lists the parameters whose gradient held a NaN or an infinity. The pages speak of
+detecting NaNs and falling back to another optimizer; the fallback is left to the
+caller.
 """
 from __future__ import annotations
 
@@ -53,13 +59,26 @@ def moment_dtype(optimizer: str, shape, requested: Optional[torch.dtype], param_
 class _MeoOptimizer(torch.optim.Optimizer):
     _kind = ""
 
-    def __init__(self, params, defaults, state_dtype: Optional[torch.dtype] = None, min_8bit_size: int = 4096):
+    def __init__(self, params, defaults, state_dtype: Optional[torch.dtype] = None, min_8bit_size: int = 4096,
+                 check_finite: bool = False):
         if state_dtype not in (None, torch.float32, torch.bfloat16, torch.int8):
             raise TypeError("state_dtype must be None, torch.float32, torch.bfloat16 or torch.int8")
         super().__init__(params, defaults)
         self._state_dtype = state_dtype
         self._min_8bit_size = min_8bit_size
         self._workspace: Dict[torch.device, torch.Tensor] = {}
+        self._check_finite = bool(check_finite)
+        self._nonfinite: List[torch.Tensor] = []
+
+    def nonfinite_params(self) -> List[torch.Tensor]:
+        """With ``check_finite=True``: the parameters whose update was not finite in
+        the steps since the last call (a NaN or an infinity in the gradient; see
+        ``_lib.nonfinite_tensors``), in step order, each once per step; from then on
+        their state is not finite either. What to do then (restore a saved state,
+        lower the loss scale, change optimizer) is the caller's choice. Clears the
+        list."""
+        out, self._nonfinite = self._nonfinite, []
+        return out
 
     def _moment_dtype(self, p: torch.Tensor) -> torch.dtype:
         return moment_dtype(self._kind, p.shape, self._state_dtype, p.dtype, self._min_8bit_size)
@@ -120,6 +139,11 @@ class _MeoOptimizer(torch.optim.Optimizer):
                 ws = self._ws(self._wsize(ps, grads), device)
                 with torch.cuda.device(device):
                     self._call(group, step, ps, grads, states, ws)
+                    if self._check_finite:
+                        # read before the next call reuses the workspace (one
+                        # synchronisation per call)
+                        offs = getattr(_lib, f"meo_{self._kind}_scalar_offsets")(ps, grads)
+                        self._nonfinite.extend(ps[k] for k in _lib.nonfinite_tensors(self._kind, ws, offs))
         return loss
 
 
@@ -147,7 +171,7 @@ class Adafactor(_MeoOptimizer):
     def __init__(self, params, lr=None, eps=(1e-30, 1e-3), clip_threshold=1.0, decay_rate=-0.8,
                  beta1=None, weight_decay=0.0, scale_parameter=True, relative_step=True,
                  warmup_init=False, state_dtype=None,
-                 min_8bit_size=4096, carry_param_sumsq=False):
+                 min_8bit_size=4096, carry_param_sumsq=False, check_finite=False):
         if lr is not None and relative_step:
             raise ValueError("Cannot combine manual lr and relative_step=True options")
         if warmup_init and not relative_step:
@@ -155,7 +179,7 @@ class Adafactor(_MeoOptimizer):
         defaults = dict(lr=lr, eps=eps, clip_threshold=clip_threshold, decay_rate=decay_rate,
                         beta1=beta1, weight_decay=weight_decay, scale_parameter=scale_parameter,
                         relative_step=relative_step, warmup_init=warmup_init)
-        super().__init__(params, defaults, state_dtype, min_8bit_size)
+        super().__init__(params, defaults, state_dtype, min_8bit_size, check_finite)
         self._carry = bool(carry_param_sumsq)
         # id(param) -> (version, data_ptr, id of its param_sumsq) after the last carry step
         self._carried: Dict[int, Tuple[int, int, int]] = {}
@@ -210,12 +234,12 @@ class CAME(_MeoOptimizer):
 
     def __init__(self, params, lr=None, eps=(1e-30, 1e-16), clip_threshold=1.0,
                  betas=(0.9, 0.999, 0.9999), weight_decay=0.0, state_dtype=None,
-                 min_8bit_size=4096):
+                 min_8bit_size=4096, check_finite=False):
         if lr is None:
             raise ValueError("CAME requires an explicit lr")
         defaults = dict(lr=lr, eps=eps, clip_threshold=clip_threshold, betas=betas,
                         weight_decay=weight_decay)
-        super().__init__(params, defaults, state_dtype, min_8bit_size)
+        super().__init__(params, defaults, state_dtype, min_8bit_size, check_finite)
 
     def _state_for(self, p, group):
         return _lib.init_state("came", p, state_dtype=self._moment_dtype(p))
@@ -239,7 +263,7 @@ class Lamb(_MeoOptimizer):
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-6, weight_decay=0.0,
                  bias_correction=True, state_dtype=None,
-                 min_8bit_size=4096):
+                 min_8bit_size=4096, check_finite=False):
         if not lr >= 0.0:
             raise ValueError(f"Invalid learning rate: {lr}")
         if not eps >= 0.0:
@@ -249,7 +273,7 @@ class Lamb(_MeoOptimizer):
                 raise ValueError(f"Invalid beta parameter at index {i}: {b}")
         defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay,
                         bias_correction=bias_correction)
-        super().__init__(params, defaults, state_dtype, min_8bit_size)
+        super().__init__(params, defaults, state_dtype, min_8bit_size, check_finite)
 
     def _state_for(self, p, group):
         return _lib.init_state("lamb", p, state_dtype=self._moment_dtype(p))

@@ -1,7 +1,7 @@
 """Behaviour of the library and its torch.optim front ends beyond single-call
-parity: resume from a state_dict, NaN confinement, mixed gradient dtypes, several
-parameter groups, non-default streams, all-or-nothing validation, and the launch
-table cache."""
+parity: resume from a state_dict, NaN confinement and its detection, mixed gradient
+dtypes, several parameter groups, non-default streams, all-or-nothing validation,
+and the launch table cache."""
 import math
 
 import pytest
@@ -88,6 +88,54 @@ def test_nan_gradient_stays_in_its_tensor(opt, hp):
         xk, _ = oracle.STEP_TENSOR[opt](run.ox[k], to64(gs[k]), run.ost[k], run.hp, 1)
         assert torch.isfinite(run.params[k]).all()
         assert output_err("param", to64(run.params[k]), xk, x0=run.x0[k]) <= TOL_F32
+
+
+@pytest.mark.parametrize("cls,hp", [(Adafactor, {"beta1": 0.9}), (Adafactor, {}), (CAME, {"lr": 2e-4}),
+                                    (Lamb, {"weight_decay": 0.01})])
+def test_check_finite_names_the_nonfinite_tensors(cls, hp):
+    """check_finite=True: after a step whose gradients hold a NaN (the 1-D tensor),
+    an infinity (the 3-D one) and a value whose square overflows float32 (the last
+    matrix), nonfinite_params() names exactly the parameters whose step is not
+    finite, in list order: all three for Adafactor and CAME (the infinite square
+    reaches the factored statistics, and V = R C / mean(R) turns NaN), the first two
+    for LAMB (there v turns infinite and that element's direction m / sqrt(v) is 0,
+    so its step stays finite). The others are stepped to finite values. On the next
+    step the named ones hold non-finite states and are named again. A clean run
+    names nothing and steps bit for bit as without the option."""
+    wl, ps = _params()
+    scales = workloads.grad_scales(wl, "cuda")
+    opt = cls(ps, check_finite=True, **hp)
+    gs = workloads.grads(wl, 0, scales, "cuda")
+    gs[1][7] = float("nan")
+    gs[2][1, 3, 5] = float("inf")
+    gs[3][10, 20] = 3e19
+    for p, g in zip(ps, gs):
+        p.grad = g
+    opt.step()
+    named = [1, 2] if cls is Lamb else [1, 2, 3]
+    assert [id(p) for p in opt.nonfinite_params()] == [id(ps[k]) for k in named]
+    for k in range(len(ps)):
+        assert torch.isfinite(ps[k]).all() == (k not in named), k
+    assert opt.nonfinite_params() == []  # the list was cleared
+    for p, g in zip(ps, workloads.grads(wl, 1, scales, "cuda")):
+        p.grad = g
+    opt.step()
+    assert [id(p) for p in opt.nonfinite_params()] == [id(ps[k]) for k in named]
+
+    wl, ps = _params(seed=1)
+    clean = cls(ps, check_finite=True, **hp)
+    plain = cls([torch.nn.Parameter(p.detach().clone()) for p in ps], **hp)
+    for t in range(2):
+        gs = workloads.grads(wl, t, scales, "cuda")
+        for p, q, g in zip(ps, plain.param_groups[0]["params"], gs):
+            p.grad = g.clone()
+            q.grad = g.clone()
+        clean.step()
+        plain.step()
+    assert clean.nonfinite_params() == []
+    assert plain.nonfinite_params() == []
+    for p, q in zip(ps, plain.param_groups[0]["params"]):
+        assert torch.equal(p.detach(), q.detach())  # the check reads, and changes nothing
 
 
 def test_mixed_gradient_dtypes_in_one_call():
