@@ -19,7 +19,6 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import workloads
 from tests.harness import Run, lib_hp, lib_states, lib_step, lib_workspace, list_run, to64
 

@@ -2,15 +2,13 @@
 parity: resume from a state_dict, NaN confinement and its detection, mixed gradient
 dtypes, several parameter groups, non-default streams, all-or-nothing validation,
 and the launch table cache."""
-import math
-
 import pytest
 import torch
 
 import oracle
 import workloads
 from memory_efficient_optimizers_amd import CAME, Adafactor, Lamb, _lib
-from tests.harness import TOL_F32, Run, lib_hp, lib_states, lib_step, lib_workspace, output_err, to64
+from tests.harness import TOL_F32, Run, lib_states, lib_step, lib_workspace, output_err, to64
 
 pytestmark = pytest.mark.gpu
 
