@@ -65,7 +65,13 @@ A systematic fault (truncation instead of rounding to nearest, a wrong dtype, a
 mis-rounded tail) moves most elements and fails the second rule. The step dX is
 held to the same two rules (floored at RMS(dX)) where the parameter is fp32 and
 the first moment bf16 (dX then follows the stored moment); a bf16 parameter's dX
-is not separable from its storage rounding and is not checked on its own.
+is not separable from its storage rounding and is not checked on its own. LAMB's
+step is its per-tensor trust ratio times the direction (the DistributedLAMB
+paragraph: a layer-wise ratio), so one near-tie element of the stored moment moves
+the ratio, and with it every element's step, by the same factor (3e-5 measured on a
+256-element tensor): there the oracle's step is rescaled by the library's ratio over
+its own before the two rules, which then judge the direction, and the ratio is held
+by its scalar bar (TOL_SCALAR_STORAGE).
 
 8-bit first moment. The same near-tie disagreement can move an int8 code by one
 step (code = m / scale rounded, decided on each side's own m). Such a step is
@@ -332,7 +338,13 @@ def judge_arrays(opt: str, hp: dict, storage: dict, out: list, x0, xo_lib=None, 
             lib_x, ref_x = lib, ref
     dk = dx_kind(opt, hp, storage)
     if dk and xo_lib is not None and xo_ref is not None:
-        ok, err, over, n, nw = check_dx(dk, lib_x, xo_lib, ref_x, xo_ref)
+        want_x = ref_x
+        if (opt == "lamb" and dk == "rounded" and lib_scalars is not None and ref_scalars is not None
+                and ref_scalars.get("trust")):
+            # the direction, with the ratio judged below (see the module notes)
+            xo = np.asarray(xo_ref, dtype=np.float64)
+            want_x = xo + (np.asarray(ref_x, dtype=np.float64) - xo) * (lib_scalars["trust"] / ref_scalars["trust"])
+        ok, err, over, n, nw = check_dx(dk, lib_x, xo_lib, want_x, xo_ref)
         res["dx"] = (ok, err, over, n, dk, nw)
     if lib_scalars is not None and ref_scalars is not None:
         stored = any(storage.get(k) for k in ("param_bf16", "exp_avg_bf16", "exp_avg_i8"))

@@ -1,0 +1,81 @@
+"""Seeded random parity sweep (GPU): lists drawn around the kernels' edges, checked
+against the oracle under the usual bars.
+
+Each case draws an optimizer and a valid set of its hyperparameters, 1 to 5 tensors
+(1-D, 2-D or 3-D) whose sides come from the sizes where tiles, vector groups, strips
+and 8-bit groups begin and end (1, 7, 8, 9, 63 .. 65, 127 .. 129, 255 .. 257, 4095 ..
+4097, 12288, 12289, ...), the gradient dtype and scaling, and the storage (fp32 or
+bf16 parameters; fp32, bf16 or 8-bit first moments where the 8-bit rule applies).
+Two chained steps, every output judged after each. The structured tests pin each
+edge on its own; the sweep covers their combinations in one list."""
+import random
+
+import pytest
+import torch
+
+import workloads
+from tests.harness import Run
+
+pytestmark = pytest.mark.gpu
+
+DIMS = [1, 2, 3, 7, 8, 9, 16, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 513, 1000, 1023, 1024, 1025,
+        4095, 4096, 4097, 8192, 12288, 12289]
+MAX_NUMEL = 300_000
+CASES = 160
+
+
+def _shape(rng: random.Random):
+    while True:
+        nd = rng.choices([1, 2, 3], weights=[3, 6, 2])[0]
+        if nd == 1:
+            shape = (rng.choice(DIMS + [5000, 40000, 131072]),)
+        elif nd == 2:
+            shape = (rng.choice(DIMS), rng.choice(DIMS))
+        else:
+            shape = (rng.choice([2, 3]), rng.choice(DIMS[:20]), rng.choice(DIMS))
+        n = 1
+        for d in shape:
+            n *= d
+        if n <= MAX_NUMEL:
+            return shape
+
+
+def _hparams(rng: random.Random, opt: str) -> dict:
+    if opt == "adafactor":
+        hp = {"beta1": rng.choice([None, 0.9, 0.5]), "weight_decay": rng.choice([0.0, 0.1]),
+              "scale_parameter": rng.choice([True, False]), "clip_threshold": rng.choice([1.0, 0.3])}
+        if rng.random() < 0.3:
+            hp.update(relative_step=False, lr=rng.choice([3e-3, 1e-2]))
+        elif rng.random() < 0.3:
+            hp["warmup_init"] = True
+        return hp
+    if opt == "came":
+        return {"lr": rng.choice([2e-4, 1e-3]), "weight_decay": rng.choice([0.0, 0.05]),
+                "clip_threshold": rng.choice([1.0, 0.5])}
+    return {"lr": rng.choice([1e-3, 2e-3]), "weight_decay": rng.choice([0.0, 0.01]),
+            "bias_correction": rng.choice([True, False])}
+
+
+def draw_case(seed: int):
+    rng = random.Random(1000 + seed)
+    opt = rng.choice(["adafactor", "came", "lamb"])
+    hp = _hparams(rng, opt)
+    shapes = [_shape(rng) for _ in range(rng.randint(1, 5))]
+    param_dtype = rng.choice([torch.float32, torch.bfloat16])
+    state_dtype = rng.choice([torch.float32, torch.bfloat16, torch.int8])
+    grad_dtype = rng.choice([torch.float32, torch.bfloat16])
+    scaling = rng.choice(["row", "rowcol", "none"])
+    return opt, hp, shapes, param_dtype, state_dtype, grad_dtype, scaling
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_list(seed):
+    opt, hp, shapes, pdt, sdt, gdt, scaling = draw_case(seed)
+    print(f"sweep case {seed}: {opt} {hp} shapes={shapes} param={pdt} state={sdt} grad={gdt} {scaling}",
+          flush=True)
+    wl = workloads.custom(f"sweep{seed}", opt, shapes, hparams=hp, grad_dtype=gdt, grad_scaling=scaling,
+                          steps=2, seed=seed, param_dtype=pdt, state_dtype=sdt)
+    run = Run(wl, min_8bit_size=1024)
+    for s in range(2):
+        run.step()
+        run.check(f"case {seed} step {s + 1}")

@@ -118,3 +118,39 @@ def test_correct_replica_passes_planted_fault_cases():
     for case in ("adafactor_defaults", "adafactor_beta1", "came", "lamb"):
         for t, k, res, _, _, _ in replica_run(CASES[case], steps=3):
             assert all(v[0] for v in res.values()), (case, t, k, {key: v for key, v in res.items() if not v[0]})
+
+
+def test_lamb_stored_moment_step_is_ratio_times_direction():
+    """LAMB with an fp32 parameter and a bf16 first moment: a near-tie element of the
+    stored moment moves the trust ratio (and so every element's step) by the same
+    small factor, 3e-5 here. The step check compares the direction, the ratio keeps
+    its own bar. Planted faults still fail: a step applied with a ratio 0.1% off the
+    one the library reports, the reported ratio 0.1% off, a wrong direction."""
+    from tests.harness import judge_arrays
+    rng = np.random.default_rng(11)
+    n, lr = 256, 2e-3
+    storage = dict(param_bf16=False, exp_avg_bf16=True, exp_avg_i8=False)
+    assert bar_kind("lamb", {}, storage, "param") == "rounded"
+    xo = rng.normal(0, 0.02, n)
+    d = rng.normal(0, 1, n)
+    tau = np.linalg.norm(xo) / np.linalg.norm(d)
+    x_ref = xo - lr * tau * d
+    ref_sc = {"x_norm": np.linalg.norm(xo), "d_norm": np.linalg.norm(d), "trust": tau}
+
+    def judge(applied, reported, direction=d):
+        x_lib = (xo - lr * applied * direction).astype(np.float32).astype(np.float64)
+        lib_sc = {"rms_x": ref_sc["x_norm"], "norm_d": ref_sc["d_norm"] * tau / reported, "trust": reported}
+        return judge_arrays("lamb", {}, storage, [("param", x_lib, x_ref)], xo, xo, xo, lib_sc, ref_sc)
+
+    near_tie = tau * (1 + 3e-5)
+    res = judge(near_tie, near_tie)
+    assert res["dx"][0] and res["scalar:trust"][0], res
+    assert res["dx"][2] == 0
+    # compared element by element without the rescale, the same step fails
+    from tests.harness import check_dx
+    x_lib = (xo - lr * near_tie * d).astype(np.float32).astype(np.float64)
+    assert not check_dx("rounded", x_lib, xo, x_ref, xo)[0]
+    # faults
+    assert not judge(near_tie * 1.001, near_tie)["dx"][0]
+    assert not judge(tau * 1.001, tau * 1.001)["scalar:trust"][0]
+    assert not judge(tau, tau, d + 0.05 * d.std() * np.sign(xo))["dx"][0]
