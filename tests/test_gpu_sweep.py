@@ -79,3 +79,44 @@ def test_random_list(seed):
     for s in range(2):
         run.step()
         run.check(f"case {seed} step {s + 1}")
+
+
+# GaLore: random lists of projected and flat tensors on either side, any rank (clamped
+# to the shorter side), std or reverse_std, fp32 or bf16 parameters, a step that is
+# not a refresh step (the projector is an input on both sides). lr x scale stays at
+# or under 1e-2, as in the structured tests.
+GALORE_DIMS = [1, 2, 7, 8, 9, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 511, 513, 1024]
+GALORE_CASES = 60
+
+
+def draw_galore_case(seed: int):
+    rng = random.Random(5000 + seed)
+    shapes = []
+    for _ in range(rng.randint(1, 4)):
+        kind = rng.choices(["2d", "1d", "3d"], weights=[7, 2, 1])[0]
+        while True:
+            if kind == "2d":
+                shape = (rng.choice(GALORE_DIMS), rng.choice(GALORE_DIMS))
+            elif kind == "1d":
+                shape = (rng.choice(GALORE_DIMS + [5000]),)
+            else:
+                shape = (2, rng.choice(GALORE_DIMS[:12]), rng.choice(GALORE_DIMS[:12]))
+            n = 1
+            for d in shape:
+                n *= d
+            if n <= 200_000:
+                break
+        shapes.append(shape)
+    rank = rng.choice([4, 8, 13, 32, 64, 100, 256])
+    hp = {"lr": rng.choice([0.01, 0.02]), "weight_decay": rng.choice([0.0, 0.1]),
+          "scale": rng.choice([0.25, 0.5]), "proj_type": rng.choice(["std", "reverse_std"])}
+    pdt = rng.choice([torch.float32, torch.bfloat16])
+    return shapes, rank, hp, pdt, rng.randint(2, 199)
+
+
+@pytest.mark.parametrize("seed", range(GALORE_CASES))
+def test_random_galore_list(seed):
+    from tests.test_gpu_galore import run_case
+    shapes, rank, hp, pdt, t = draw_galore_case(seed)
+    print(f"galore sweep case {seed}: shapes={shapes} rank={rank} {hp} param={pdt} t={t}", flush=True)
+    run_case(shapes, rank, t=t, hp=hp, param_dtype=pdt, seed=100 + seed)

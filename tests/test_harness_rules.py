@@ -154,3 +154,28 @@ def test_lamb_stored_moment_step_is_ratio_times_direction():
     assert not judge(near_tie * 1.001, near_tie)["dx"][0]
     assert not judge(tau * 1.001, tau * 1.001)["scalar:trust"][0]
     assert not judge(tau, tau, d + 0.05 * d.std() * np.sign(xo))["dx"][0]
+
+
+def test_small_update_rule_forgives_storage_only():
+    """The update check (GaLore; the other optimizers' step check alike) forgives one
+    fp32 spacing of the parameter per element: a small update (1.7e-3 of the
+    parameter) stored in fp32 passes at 1e-4, while the same update with its
+    coefficient 0.1% off, or with the decay term dropped, fails."""
+    from tests.harness import dx_errs
+    rng = np.random.default_rng(12)
+    x0 = rng.normal(0, 0.02, 20000)
+    decay, coef = 1 - 1e-3, 2.5e-3
+    c = rng.normal(0, 0.011, x0.size)
+    want = decay * x0 - coef * c
+
+    def worst(got):
+        e, _ = dx_errs(got, x0, want, x0, floor=1.0)
+        return float(np.max(e))
+
+    f32 = lambda v: np.asarray(v, dtype=np.float32).astype(np.float64)
+    stored = f32(f32(decay * f32(x0)) - f32(coef * c))   # the kernel's roundings
+    assert worst(stored) <= 1e-4
+    from tests.harness import floored_rel_err
+    assert floored_rel_err(stored - x0, want - x0) > 1e-4   # the storage rounding alone, unforgiven
+    assert worst(f32(decay * x0 - 1.001 * coef * c)) > 1e-4
+    assert worst(f32(x0 - coef * c)) > 1e-4
