@@ -120,3 +120,25 @@ def test_random_galore_list(seed):
     shapes, rank, hp, pdt, t = draw_galore_case(seed)
     print(f"galore sweep case {seed}: shapes={shapes} rank={rank} {hp} param={pdt} t={t}", flush=True)
     run_case(shapes, rank, t=t, hp=hp, param_dtype=pdt, seed=100 + seed)
+
+
+# Adafactor through the carry entry point (RMS(X) from the previous apply pass's sum
+# of squares): the same random lists, scale_parameter on, three chained steps.
+CARRY_CASES = 40
+
+
+@pytest.mark.parametrize("seed", range(CARRY_CASES))
+def test_random_carry_list(seed):
+    rng = random.Random(9000 + seed)
+    hp = dict(_hparams(rng, "adafactor"), scale_parameter=True)
+    shapes = [_shape(rng) for _ in range(rng.randint(1, 5))]
+    pdt = rng.choice([torch.float32, torch.bfloat16])
+    sdt = rng.choice([torch.float32, torch.bfloat16, torch.int8])
+    gdt = rng.choice([torch.float32, torch.bfloat16])
+    print(f"carry sweep case {seed}: {hp} shapes={shapes} param={pdt} state={sdt} grad={gdt}", flush=True)
+    wl = workloads.custom(f"carry{seed}", "adafactor", shapes, hparams=hp, grad_dtype=gdt, steps=3, seed=seed,
+                          param_dtype=pdt, state_dtype=sdt)
+    run = Run(wl, min_8bit_size=1024, carry=True)
+    for s in range(3):
+        run.step()
+        run.check(f"carry case {seed} step {s + 1}")
