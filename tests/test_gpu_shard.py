@@ -69,9 +69,15 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
     own shard from the second step on; the ranks' sums add up to the whole
     parameter's."""
     carry = opt == "adafactor-carry"
-    opt = "adafactor" if carry else opt
-    wl = workloads.custom(f"shard_{opt}", opt, SHAPES, hparams=hp, grad_dtype=torch.bfloat16,
-                          grad_scaling="rowcol" if opt != "lamb" else "row")
+    check_sharded("adafactor" if carry else opt, hp, SHAPES, nranks, carry)
+
+
+def check_sharded(opt, hp, shapes, nranks, carry=False, steps=3, seed=0):
+    """N ranks' shares of `shapes` stepped `steps` times through the shard calls, the
+    records summed in between; after every step the shares put together must match
+    the oracle's whole-tensor step."""
+    wl = workloads.custom(f"shard_{opt}", opt, shapes, hparams=hp, grad_dtype=torch.bfloat16,
+                          grad_scaling="rowcol" if opt != "lamb" else "row", seed=seed)
     full = workloads.init_params(wl, "cuda")
     scales = workloads.grad_scales(wl, "cuda")
     hps = {"adafactor": _lib.adafactor_hparams, "lamb": _lib.lamb_hparams, "came": _lib.came_hparams}[opt](**hp)
@@ -103,7 +109,7 @@ def test_row_sharded_step_matches_whole_tensor(opt, hp, nranks):
     x0 = [x.copy() for x in ox]
     ost = [oracle.INIT_STATE[opt](tuple(p.shape), hp) for p in full]
     b1 = beta1_of(opt, hp)
-    for t in range(1, 4):
+    for t in range(1, steps + 1):
         gfull = workloads.grads(wl, t - 1, scales, "cuda")
         parts = []
         for r, rk in enumerate(ranks):

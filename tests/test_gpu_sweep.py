@@ -142,3 +142,33 @@ def test_random_carry_list(seed):
     for s in range(3):
         run.step()
         run.check(f"carry case {seed} step {s + 1}")
+
+
+# Row-sharded steps: random lists split over 1 to 13 ranks (some ranks then hold no
+# rows of a small tensor), the records summed in between, the shares put together
+# against the oracle's whole-tensor step (fp32 storage, as the shard calls take).
+# The shard calls take factored tensors whose rows are a multiple of 8 wide and at
+# most 12288 (they refuse others before any launch; the host tests pin that).
+SHARD_CASES = 30
+
+
+@pytest.mark.parametrize("seed", range(SHARD_CASES))
+def test_random_sharded_list(seed):
+    from tests.test_gpu_shard import check_sharded
+    rng = random.Random(12000 + seed)
+    opt = rng.choice(["adafactor", "adafactor-carry", "came", "lamb"])
+    carry = opt == "adafactor-carry"
+    opt = "adafactor" if carry else opt
+    hp = _hparams(rng, opt)
+    if carry:
+        hp["scale_parameter"] = True
+    shapes = []
+    for _ in range(rng.randint(1, 4)):
+        shape = _shape(rng)
+        while opt != "lamb" and len(shape) >= 2 and (shape[-1] % 8 or shape[-1] > 12288):
+            shape = _shape(rng)
+        shapes.append(shape)
+    nranks = rng.choice([1, 2, 3, 5, 8, 13])
+    print(f"shard sweep case {seed}: {opt}{' carry' if carry else ''} {hp} shapes={shapes} ranks={nranks}",
+          flush=True)
+    check_sharded(opt, hp, shapes, nranks, carry, steps=2, seed=seed)
