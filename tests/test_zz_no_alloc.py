@@ -114,3 +114,32 @@ def test_noalloc_refuses_a_list_beyond_its_scratch():
     torch.cuda.synchronize()
     assert all(bool((p == 0.5).all()) for p in ps)
     assert all(not st["exp_avg"].any() and not st["exp_avg_sq_row"].any() for st in sts)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_noalloc_equals_step_on_random_lists(seed):
+    """Random Adafactor lists (the sweep's draws: edge-sized sides, 1-D to 3-D, every
+    storage class, random valid hyperparameters): two steps through the no-allocation
+    entry point give the plain step's bits."""
+    import random
+    from tests.test_gpu_sweep import _hparams, _shape
+    rng = random.Random(15000 + seed)
+    hp = _hparams(rng, "adafactor")
+    shapes = [_shape(rng) for _ in range(rng.randint(1, 5))]
+    pdt = rng.choice([torch.float32, torch.bfloat16])
+    sdt = rng.choice([torch.float32, torch.bfloat16, torch.int8])
+    gdt = rng.choice([torch.float32, torch.bfloat16])
+    print(f"noalloc case {seed}: {hp} shapes={shapes} param={pdt} state={sdt} grad={gdt}", flush=True)
+    wl = workloads.custom(f"na_rand{seed}", "adafactor", shapes, hparams=hp, grad_dtype=gdt, seed=seed,
+                          param_dtype=pdt, state_dtype=sdt)
+    scales = workloads.grad_scales(wl, "cuda")
+    ps = workloads.init_params(wl, "cuda")
+    sts = lib_states("adafactor", ps, hp, sdt, min_8bit_size=1024)
+    ref_ps, ref_sts = _clone(ps, sts)
+    hps = lib_hp("adafactor", hp)
+    for t in (1, 2):
+        gs = workloads.grads(wl, t - 1, scales, "cuda")
+        _lib.meo_adafactor_step(hps, t, ref_ps, gs, ref_sts, lib_workspace("adafactor", ref_ps, gs))
+        _lib.meo_adafactor_step_noalloc(hps, t, ps, gs, sts)
+    torch.cuda.synchronize()
+    _same(ps, sts, ref_ps, ref_sts)
