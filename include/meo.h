@@ -233,7 +233,14 @@ int    meo_adafactor_step_carry(const meo_adafactor_hparams* hp, int64_t step, i
  * caller. Nothing in the scratch is carried from one call to the next, and
  * nothing in it needs to start at zero (every pass writes what a later pass
  * reads). Arguments, validation, stream semantics and errors are otherwise as for
- * meo_adafactor_step. */
+ * meo_adafactor_step.
+ *
+ * Graph capture: the call records no memset. The table upload is a
+ * hipMemcpyAsync whose source is the library's host copy of that list's tables,
+ * kept for the 16 distinct lists this entry point saw last (meo_release_plans
+ * does not drop them). A captured call replays that copy from the same host
+ * memory, so a graph may be replayed only while its list is among those 16.
+ * Capture itself is not exercised by the tests. */
 #define MEO_NOALLOC_SCRATCH_BYTES (64u << 20)
 int    meo_adafactor_step_noalloc(const meo_adafactor_hparams* hp, int64_t step, int32_t n,
                                   const meo_tensor* tensors, const meo_adafactor_state* states, void* stream);
