@@ -59,7 +59,8 @@ void launch_galore_project_mixed(const GTable& t, int64_t n, int nright, const G
 // kBackDirect: 64 x 256 tiles staged by global_load_lds (every rank a multiple of kGaKb,
 // 16-byte rows). kBackUr / kBackUrBf16: as direct, with U held in registers and items of
 // 256 rows of U x up to kUrTiles 64-row tiles of N (item y = band * btj + chunk); every
-// parameter of the list fp32 (kBackUr) or bf16 (kBackUrBf16).
+// parameter of the list fp32 (kBackUr) or bf16 (kBackUrBf16; its m >= n side takes the
+// 4-wave, two-blocks-per-CU kernel with 32-row tiles of N over the same items).
 enum BackMode { kBackReg = 0, kBackDirect = 1, kBackUr = 2, kBackUrBf16 = 3 };
 constexpr int kUrTiles = 64;  // 64-row tiles of N per item of the U-register back-projection
 void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, int mode, hipStream_t s);

@@ -19,11 +19,13 @@
 //                     direction N = m_hat / (sqrt(v_hat) + eps) written as two
 //                     bf16 planes (high part and the remainder) so that the back
 //                     projection keeps ~16 significant bits of N on bf16 MFMA.
-//   k_galore_back_ur / k_galore_back
+//   k_galore_back_ur / k_galore_back_u2 / k_galore_back
 //                     W <- W (1 - lr wd) - lr scale (N U^T or U N^T): two bf16
 //                     MFMAs per fragment (high and low plane), the parameter tile
-//                     read and written once; the U-register kernel keeps a 256-row
-//                     block of U in registers and walks up to 64 tiles of N.
+//                     read and written once; the U-register kernels keep a 256-row
+//                     block of U in registers and walk up to 4096 rows of N
+//                     (k_galore_back_u2: bf16 parameters, m >= n, two 4-wave
+//                     blocks per CU).
 //
 // The projector is kept in bf16 (the gradient's type) both as U [d][r] and as
 // U^T [r][d], so every operand is read with the contraction index contiguous.
@@ -1023,6 +1025,232 @@ __global__ __launch_bounds__(512, 1) void k_galore_back_ur(GTable t, GaArgs a) {
     MEO_WAIT_VM(0);
 }
 
+// m >= n back-projection of bf16 parameters, two blocks per CU. A block of 4 waves
+// holds a 256-row band of U in registers, 64 rows per wave (128 VGPRs), and walks up
+// to kU2Tiles 32-row tiles of N: per tile its two planes are staged (32 KB, two
+// buffers) and each wave multiplies them into a 32 x 64 block of C, so each fragment
+// read serves twice the MFMAs of the 8-wave kernel and half the LDS reads are made.
+// Two such blocks share a CU (2 x 80 KB of LDS). The parameter tile is loaded a
+// tile ahead as there; to fit it beside U in 256 VGPRs, the stage's and the cells'
+// addresses are recomputed per tile (from a lane index the compiler cannot hoist)
+// instead of being held across the loop. Llama-7B list, bf16 parameters, side by
+// side: 9.39-9.46 -> 9.15-9.27 ms, results bitwise the same. With fp32 parameters
+// it gains nothing (12.33 -> 12.30 ms; the parameter stream bounds that pass), and
+// those lists keep k_galore_back_ur.
+constexpr int kU2N = 32;                     // rows of N per tile
+constexpr int kU2Tiles = 2 * kUrTiles;       // tiles per item: the same 4096 rows of N
+constexpr int kU2Dma = 2 * kU2N * (kGaWide / 8) / 256;  // 16-byte transfers per lane per tile: 8
+
+__device__ __forceinline__ void u2_stage(const GDesc& d, int64_t n0, uint16_t* buf, int wave, int lane) {
+    // instruction j: rows 2 jr, 2 jr + 1 of plane j / 16 (jr = j % 16), 32 chunks each
+    __asm__ volatile("" : "+v"(lane));
+#pragma unroll
+    for (int i = 0; i < kU2Dma; ++i) {
+        const int j = wave + 4 * i;                 // 0 .. 31
+        const int plane = j >> 4, jr = j & 15;
+        const int row = 2 * jr + (lane >> 5);       // 0 .. 31
+        const int c = (lane & 31) ^ (row & 15);     // global chunk held at position lane & 31
+        const int cc = min(c, d.r / 8 - 1);
+        const int64_t grow = min(n0 + row, static_cast<int64_t>(d.D) - 1);
+        const uint16_t* src = (plane ? d.nl : d.nh) + grow * d.r + cc * 8;
+        __builtin_amdgcn_global_load_lds((const MEO_GLOBAL void*)src,
+                                         (__attribute__((address_space(3))) void*)(buf + j * 512), 16, 0, 0);
+    }
+}
+
+template <bool XB>
+__global__ __launch_bounds__(256, 2) void k_galore_back_u2(GTable t, GaArgs a) {
+    static_assert(kU2Dma == 8, "wait counts below");
+    constexpr int kP = XB ? 4 : 8;  // 16-byte parameter loads (and stores) per lane per tile
+    __shared__ __attribute__((aligned(16))) uint16_t nb0[2 * kU2N * 256];
+    __shared__ __attribute__((aligned(16))) uint16_t nb1[2 * kU2N * 256];
+    __shared__ __attribute__((aligned(16))) float exb[4 * 32 * 32];
+    const int2 it = t.items[blockIdx.x];
+    if (it.x < 0) return;  // an empty item of the XCD-dealt list
+    const GDesc d = t.desc[it.x];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nc = d.btj;
+    const int band = it.y / nc, chunk = it.y % nc;
+    const int64_t u0 = static_cast<int64_t>(band) * kGaWide;
+    const int64_t nt0 = static_cast<int64_t>(chunk) * kU2Tiles;
+    const int ntiles = static_cast<int>(min<int64_t>(kU2Tiles, (d.D + kU2N - 1) / kU2N - nt0));
+    const int nks = d.r / 16;
+    using PT = typename std::conditional<XB, uint16_t, float>::type;
+    PT* const x = static_cast<PT*>(d.x);
+    bfv8 uf[16][2];
+#pragma unroll
+    for (int ub = 0; ub < 2; ++ub) {
+        const int64_t row = min(u0 + wave * 64 + ub * 32 + (lane & 31), static_cast<int64_t>(d.d) - 1);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const int k = min(ks, nks - 1) * 16 + 8 * (lane >> 5);
+            uf[ks][ub] = __builtin_bit_cast(bfv8, *gld<u32x4>(d.u + row * d.r + k));
+        }
+    }
+    MEO_WAIT_VM(0);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) __asm__ volatile("" : "+v"(uf[ks][0]), "+v"(uf[ks][1]));
+    // W cells of the wave: the 32 tile rows x two 32-column blocks (ub); in block ub,
+    // lane holds rows (lane >> 2) + 16 q (q < 2), columns 8 (lane & 3) .. + 7.
+    auto cell = [&](int64_t n0, int ub, int q, int64_t& row, int64_t& col) {
+        int ln = lane;
+        __asm__ volatile("" : "+v"(ln));
+        row = n0 + (ln >> 2) + 16 * q;
+        col = u0 + wave * 64 + ub * 32 + 8 * (ln & 3);
+    };
+    u32x4 wp[2][2][2];  // [ub][q][16-byte half]
+    auto load_w = [&](int64_t n0) {
+        if (!d.wvec) return;
+#pragma unroll
+        for (int ub = 0; ub < 2; ++ub)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                int64_t row, col;
+                cell(n0, ub, q, row, col);
+                row = min(row, static_cast<int64_t>(d.m) - 1);
+                col = min(col, static_cast<int64_t>(d.n) - 8);
+                const PT* p = x + row * d.n + col;
+                wp[ub][q][0] = *gld<u32x4>(p);
+                if (!XB) wp[ub][q][1] = *gld<u32x4>(p + 4);
+            }
+    };
+    f32x16 acc[2];
+    auto multiply = [&](const uint16_t* buf) {
+        // Fragment reads in asm blocks that wait for their own reads (the compiler
+        // cannot tell which stage an LDS read hits). Two sub-steps per block; the low
+        // plane sits 16 KB after the high one.
+        static_assert(kU2N * 256 * 2 == 16384, "plane offset in the reads below");
+        const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf)) + (lane & 31) * 512;
+        const int sw = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < 16; ks += 2) {
+            if (ks >= nks) break;
+            int swv = sw;
+            __asm__ volatile("" : "+v"(swv));
+            const uint32_t a0 = base + static_cast<uint32_t>(((2 * ks + (lane >> 5)) ^ swv) << 4);
+            const uint32_t a1 = base + static_cast<uint32_t>(((2 * ks + 2 + (lane >> 5)) ^ swv) << 4);
+            u32x4 h0, l0, h1, l1;
+            __asm__ volatile(
+                "ds_read_b128 %0, %4\n\t"
+                "ds_read_b128 %1, %4 offset:16384\n\t"
+                "ds_read_b128 %2, %5\n\t"
+                "ds_read_b128 %3, %5 offset:16384\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(h0), "=&v"(l0), "=&v"(h1), "=&v"(l1)
+                : "v"(a0), "v"(a1));
+            const bfv8 fh0 = __builtin_bit_cast(bfv8, h0), fl0 = __builtin_bit_cast(bfv8, l0);
+            const bfv8 fh1 = __builtin_bit_cast(bfv8, h1), fl1 = __builtin_bit_cast(bfv8, l1);
+#pragma unroll
+            for (int ub = 0; ub < 2; ++ub) {
+                acc[ub] = mfma32(fh0, uf[ks][ub], acc[ub]);
+                acc[ub] = mfma32(fl0, uf[ks][ub], acc[ub]);
+            }
+#pragma unroll
+            for (int ub = 0; ub < 2; ++ub) {
+                acc[ub] = mfma32(fh1, uf[ks + 1][ub], acc[ub]);
+                acc[ub] = mfma32(fl1, uf[ks + 1][ub], acc[ub]);
+            }
+        }
+    };
+    auto update = [&](int64_t n0, bool exact) {
+        int lane = threadIdx.x & 63;
+        __asm__ volatile("" : "+v"(lane));
+        float* lw = exb + wave * (32 * 32);
+#pragma unroll
+        for (int ub = 0; ub < 2; ++ub) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) lw[ur_ex(acc_row(v, lane), acc_col(lane))] = acc[ub][v];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                float cq[8];
+                {
+                    const int r = (lane >> 2) + 16 * q, c = 8 * (lane & 3);
+                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(lw + ur_ex(r, c));
+                    const f32x4 c1 = *reinterpret_cast<const f32x4*>(lw + ur_ex(r, c + 4));
+                    cq[0] = c0.x; cq[1] = c0.y; cq[2] = c0.z; cq[3] = c0.w;
+                    cq[4] = c1.x; cq[5] = c1.y; cq[6] = c1.z; cq[7] = c1.w;
+                }
+                int64_t row, col;
+                cell(n0, ub, q, row, col);
+                float w[8];
+                if (exact) {
+                    PT* xp = x + row * d.n + col;
+                    if (XB) {
+                        bf16x8(wp[ub][q][0], w);
+                    } else {
+                        const u32x4 x0 = wp[ub][q][0], x1 = wp[ub][q][1];
+                        w[0] = __uint_as_float(x0.x); w[1] = __uint_as_float(x0.y);
+                        w[2] = __uint_as_float(x0.z); w[3] = __uint_as_float(x0.w);
+                        w[4] = __uint_as_float(x1.x); w[5] = __uint_as_float(x1.y);
+                        w[6] = __uint_as_float(x1.z); w[7] = __uint_as_float(x1.w);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = a.decay * w[e] - a.coef * cq[e];
+                    if (XB) {
+                        *gst<u32x4>(xp) = pack_bf16x8(w);
+                    } else {
+                        *gst<f32x4>(xp) = f32x4{w[0], w[1], w[2], w[3]};
+                        *gst<f32x4>(xp + 4) = f32x4{w[4], w[5], w[6], w[7]};
+                    }
+                } else {
+                    if (row >= d.m || col >= d.n) continue;
+                    PT* xp = x + row * d.n + col;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (col + e >= d.n) continue;
+                        const float w0 = XB ? __uint_as_float(static_cast<uint32_t>(*gld<uint16_t>(reinterpret_cast<const uint16_t*>(xp) + e)) << 16)
+                                            : *gld<float>(reinterpret_cast<const float*>(xp) + e);
+                        const float w1 = a.decay * w0 - a.coef * cq[e];
+                        if (XB) *gst<uint16_t>(reinterpret_cast<uint16_t*>(xp) + e) = static_cast<uint16_t>(bf16_bits(w1));
+                        else *gst<float>(reinterpret_cast<float*>(xp) + e) = w1;
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        if (!exact) MEO_WAIT_VM(0);
+    };
+    auto zero = [&]() {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
+    };
+    const bool exact = d.wvec && (nt0 + ntiles) * kU2N <= d.D && u0 + kGaWide <= d.d;
+    // The same pipeline and wait counts as the 8-wave kernel (8 stage transfers and kP
+    // parameter loads or stores per lane per tile).
+    const int last = ntiles - 1;
+    u2_stage(d, nt0 * kU2N, nb0, wave, lane);
+    u2_stage(d, (nt0 + min(1, last)) * kU2N, nb1, wave, lane);
+    load_w(nt0 * kU2N);
+    if (d.wvec) MEO_WAIT_VM(kP + 8);
+    else MEO_WAIT_VM(8);
+    for (int i = 0; i < ntiles; i += 2) {
+        __builtin_amdgcn_s_barrier();
+        zero();
+        multiply(nb0);
+        __builtin_amdgcn_s_barrier();
+        update((nt0 + i) * kU2N, exact);
+        if (i + 1 >= ntiles) break;
+        u2_stage(d, (nt0 + min(i + 2, last)) * kU2N, nb0, wave, lane);
+        load_w((nt0 + i + 1) * kU2N);
+        if (exact) MEO_WAIT_VM(2 * kP + 8);
+        else MEO_WAIT_VM(0);
+        __builtin_amdgcn_s_barrier();
+        zero();
+        multiply(nb1);
+        __builtin_amdgcn_s_barrier();
+        update((nt0 + i + 1) * kU2N, exact);
+        if (i + 2 >= ntiles) break;
+        u2_stage(d, (nt0 + min(i + 3, last)) * kU2N, nb1, wave, lane);
+        load_w((nt0 + i + 2) * kU2N);
+        if (exact) MEO_WAIT_VM(2 * kP + 8);
+        else MEO_WAIT_VM(0);
+    }
+    MEO_WAIT_VM(0);
+}
+
 void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, int mode, hipStream_t s) {
     if (n <= 0) return;
     const dim3 grid(static_cast<uint32_t>(n)), block(kBackThreads);
@@ -1031,7 +1259,7 @@ void launch_galore_back(const GTable& t, int64_t n, const GaArgs& a, bool left, 
         const bool xb = mode == kBackUrBf16;
         if (left && xb) hipLaunchKernelGGL((k_galore_back_ur<true, true>), grid, dim3(512), 0, s, t, a);
         else if (left) hipLaunchKernelGGL((k_galore_back_ur<true, false>), grid, dim3(512), 0, s, t, a);
-        else if (xb) hipLaunchKernelGGL((k_galore_back_ur<false, true>), grid, dim3(512), 0, s, t, a);
+        else if (xb) hipLaunchKernelGGL((k_galore_back_u2<true>), grid, dim3(256), 0, s, t, a);
         else hipLaunchKernelGGL((k_galore_back_ur<false, false>), grid, dim3(512), 0, s, t, a);
         return;
     }
