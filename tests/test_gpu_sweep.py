@@ -7,7 +7,12 @@ and 8-bit groups begin and end (1, 7, 8, 9, 63 .. 65, 127 .. 129, 255 .. 257, 40
 4097, 12288, 12289, ...), the gradient dtype and scaling, and the storage (fp32 or
 bf16 parameters; fp32, bf16 or 8-bit first moments where the 8-bit rule applies).
 Two chained steps, every output judged after each. The structured tests pin each
-edge on its own; the sweep covers their combinations in one list."""
+edge on its own; the sweep covers their combinations in one list.
+
+Further parts draw the same way for GaLore's step (projected and flat tensors of
+either side, any rank, std or reverse_std), Adafactor through the carry entry point,
+the row-sharded calls over 1 to 13 ranks, and GaLore's projector refresh against
+the exact SVD."""
 import random
 
 import pytest
